@@ -1,0 +1,392 @@
+"""ALoDLM adaptively looped denoising step -- ORACLE (test infrastructure only).
+
+A plain, slow, float64 CPU implementation of what one denoising step of
+ALoDLM computes, written from the method pages.  It is test infrastructure:
+only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import it.  It shares no code with the HIP library and never reads anything
+the library produced.
+
+Sources (page titles and sections):
+  * "ALoDLM: Adaptively Looped Diffusion Language Models" summary page
+    (paper.rainbus.top, arXiv 2610.04198): section "Core method" (Prelude /
+    Recurrent Core / Coda split, the two heads, lambda = sigmoid(ExitGate(r)),
+    commit iff entropy <= tau, halt when the mean cumulative halt of the
+    unresolved positions reaches q, forced exit at s = K, Eq. 3), section
+    "Method step details" (Algorithm 1 steps 1-5, the cumulative halting
+    update a <- a + (1 - a) lambda, the forced lowest-entropy commit), section
+    "Background" (looped Transformer with shared weights; depth-aware KV
+    cache: matching depth first, deepest available as fallback), section
+    "Limitations" (the cache holds L + (K-1) m buffers, 84 for 8B at K = 4),
+    section "Technical novelty" (10 + 4 x (16 + 10) = 114 layer calls).
+  * the tokendh.com explainer of the same paper: entropy and cumulative-halt
+    thresholds; committed positions feed back their token embedding.
+
+Readings where the pages are silent (both this oracle and the GPU library
+follow them):
+  * layer = Qwen3 block: pre-norm RMSNorm, per-head RMSNorm of q and k, RoPE
+    (rotate-half pairs (i, i + hd/2), base theta), GQA with q head h reading
+    kv head floor(h * Hkv / Hq), softmax scale 1/sqrt(hd), SwiGLU FFN, no biases;
+  * the prefix cache is built causally; Core depth d holds the K/V the
+    prefix produces on its d-th pass through the Core; Prelude and Coda hold
+    one set each, the Coda set computed on the depth-K output;
+  * block rows see every prefix key and every block key (no mask); positions
+    are 0..P-1 for the prefix and P..P+L-1 for the block;
+  * prefix key j is read at depth min(s, d_j) by Core layers in loop s;
+  * readout r = final RMSNorm of the Coda output; both heads read r;
+  * entropy in nats, commit iff H <= tau_ent; token = argmax, ties to the
+    lowest id (greedy decoding replaces the sampling step of Algorithm 1);
+  * a is updated for positions unresolved at the start of the loop; the halt
+    test uses the mean of a over the positions still unresolved after the
+    loop's commits, "reaches" meaning >=; every sequence halts on its own;
+  * Eq. 3 is applied to every block row that is not unresolved: its state is
+    reset to the embedding of its token at the end of every loop;
+  * committed rows keep running through every layer as context;
+  * if a step committed nothing, the unresolved position of lowest entropy at
+    the last loop (ties to the lowest position) commits, recorded as -s_end;
+  * ExitGate is a d -> 1 linear map plus sigmoid.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=F64)
+
+
+def matmul_t(x: np.ndarray, w: np.ndarray, chunk: int = 16384) -> np.ndarray:
+    """x @ w.T in float64 (w stored [out][in]); converted in row chunks of w to bound memory."""
+    x = _f64(x)
+    n_out = w.shape[0]
+    out = np.empty(x.shape[:-1] + (n_out,), dtype=F64)
+    for o in range(0, n_out, chunk):
+        out[..., o:o + chunk] = x @ _f64(w[o:o + chunk]).T
+    return out
+
+
+# ---------------------------------------------------------------------------
+# layer primitives
+# ---------------------------------------------------------------------------
+def rms_norm(x, g, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g over the last axis."""
+    x = _f64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * _f64(g)
+
+
+def rope(x, pos, theta: float) -> np.ndarray:
+    """Rotary embedding, rotate-half convention: pair (i, i + hd/2) turns by pos * theta^(-2i/hd).
+
+    x: [..., n, hd]; pos: [n] integer positions.
+    """
+    x = _f64(x)
+    hd = x.shape[-1]
+    half = hd // 2
+    inv_freq = float(theta) ** (-(np.arange(half, dtype=F64) * 2.0) / hd)
+    ang = np.asarray(pos, dtype=F64)[:, None] * inv_freq[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def attention(q, k, v, allowed: Optional[np.ndarray] = None) -> np.ndarray:
+    """softmax(q k^T / sqrt(hd)) v per query head; q [Hq][n][hd], k and v [Hkv][m][hd].
+
+    Query head h reads kv head floor(h * Hkv / Hq).  ``allowed`` [n][m] masks keys.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Hq, n, hd = q.shape
+    Hkv = k.shape[0]
+    out = np.empty((Hq, n, v.shape[-1]), dtype=F64)
+    for h in range(Hq):
+        kv = (h * Hkv) // Hq
+        s = q[h] @ k[kv].T / math.sqrt(hd)
+        if allowed is not None:
+            s = np.where(allowed, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[h] = p @ v[kv]
+    return out
+
+
+def silu(x) -> np.ndarray:
+    x = _f64(x)
+    return x / (1.0 + np.exp(-x))
+
+
+def layer_forward(x, W: Dict[str, np.ndarray], li: int, dims, eps: float, theta: float, pos,
+                  ctx_k=None, ctx_v=None, causal: bool = False):
+    """One Qwen3-style block over the n rows ``x`` [n][d] of one sequence.
+
+    ctx_k / ctx_v [Hkv][m][hd]: cached (post-RoPE) keys and values that every
+    row sees in addition to the rows' own keys.  ``causal`` restricts the rows'
+    own keys to positions <= the query's.  Returns (new x, k, v) where k and v
+    [Hkv][n][hd] are this call's post-RoPE keys and values of the rows.
+    """
+    p = "layers.%d." % li
+    x = _f64(x)
+    n = x.shape[0]
+    Hq, Hkv, hd, F = dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn
+    h1 = rms_norm(x, W[p + "attn_norm"], eps)
+    qkv = matmul_t(h1, W[p + "wqkv"])
+    q = qkv[:, : Hq * hd].reshape(n, Hq, hd).transpose(1, 0, 2)
+    k = qkv[:, Hq * hd: (Hq + Hkv) * hd].reshape(n, Hkv, hd).transpose(1, 0, 2)
+    v = qkv[:, (Hq + Hkv) * hd:].reshape(n, Hkv, hd).transpose(1, 0, 2)
+    q = rope(rms_norm(q, W[p + "q_norm"], eps), pos, theta)
+    k = rope(rms_norm(k, W[p + "k_norm"], eps), pos, theta)
+    m = 0 if ctx_k is None else ctx_k.shape[1]
+    keys = k if ctx_k is None else np.concatenate([_f64(ctx_k), k], axis=1)
+    vals = v if ctx_v is None else np.concatenate([_f64(ctx_v), v], axis=1)
+    allowed = None
+    if causal:
+        allowed = np.ones((n, m + n), dtype=bool)
+        allowed[:, m:] = np.tril(np.ones((n, n), dtype=bool))
+    a = attention(q, keys, vals, allowed).transpose(1, 0, 2).reshape(n, Hq * hd)
+    x = x + matmul_t(a, W[p + "wo"])
+    h2 = rms_norm(x, W[p + "ffn_norm"], eps)
+    gu = matmul_t(h2, W[p + "w_gate_up"])
+    x = x + matmul_t(silu(gu[:, :F]) * gu[:, F:], W[p + "w_down"])
+    return x, k, v
+
+
+# ---------------------------------------------------------------------------
+# the depth-aware prefix cache
+# ---------------------------------------------------------------------------
+def kv_slot(dims, k_max: int, layer: int, depth: int = 1) -> int:
+    """Cache slot of (layer, loop depth): Prelude and Coda layers hold one set, Core layers k_max."""
+    if layer < dims.n_pre:
+        return layer
+    if layer < dims.n_pre + dims.n_core:
+        return dims.n_pre + (layer - dims.n_pre) * k_max + (depth - 1)
+    return dims.n_pre + dims.n_core * k_max + (layer - dims.n_pre - dims.n_core)
+
+
+def prefill_sequence(ids, W, dims, k_max: int, eps: float, theta: float) -> Dict[int, tuple]:
+    """Depth-aware cache of one prefix: slot -> (K, V) [Hkv][P][hd] (causal prefix)."""
+    ids = np.asarray(ids)
+    P = ids.shape[0]
+    pos = np.arange(P)
+    cache = {}
+    x = _f64(W["embed"][ids])
+    for li in range(dims.n_pre):
+        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True)
+        cache[kv_slot(dims, k_max, li)] = (k, v)
+    for depth in range(1, k_max + 1):
+        for c in range(dims.n_core):
+            li = dims.n_pre + c
+            x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True)
+            cache[kv_slot(dims, k_max, li, depth)] = (k, v)
+    for c in range(dims.n_coda):
+        li = dims.n_pre + dims.n_core + c
+        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True)
+        cache[kv_slot(dims, k_max, li)] = (k, v)
+    return cache
+
+
+def context_for(cache, dims, k_max: int, layer: int, loop: int, avail):
+    """Prefix K/V a block row reads at ``layer`` during loop ``loop`` (1-based).
+
+    Core layers read prefix position j at depth min(loop, avail[j]); Prelude
+    and Coda layers read their single set.
+    """
+    if dims.n_pre <= layer < dims.n_pre + dims.n_core:
+        K0 = cache[kv_slot(dims, k_max, layer, 1)][0]
+        P = K0.shape[1]
+        depth = np.minimum(loop, np.asarray(avail, dtype=np.int64)) if avail is not None else np.full(P, loop)
+        Ks = np.empty(K0.shape, dtype=F64)
+        Vs = np.empty(K0.shape, dtype=F64)
+        for dpt in np.unique(depth):
+            sel = depth == dpt
+            Kd, Vd = cache[kv_slot(dims, k_max, layer, int(dpt))]
+            Ks[:, sel] = _f64(Kd[:, sel])
+            Vs[:, sel] = _f64(Vd[:, sel])
+        return Ks, Vs
+    K, V = cache[kv_slot(dims, k_max, layer)]
+    return _f64(K), _f64(V)
+
+
+# ---------------------------------------------------------------------------
+# the two heads
+# ---------------------------------------------------------------------------
+def readout(r, W_lm, boost_tok=None, boost_val=None):
+    """LMHead over readout rows r [n][d]: logits z = W_lm r (+ planted boost).
+
+    Returns entropy H = -sum p ln p (nats), argmax token (lowest id on ties),
+    log-sum-exp, and the gap between the two largest logits.
+    """
+    z = matmul_t(r, W_lm)
+    n = z.shape[0]
+    if boost_tok is not None:
+        for i in range(n):
+            if boost_tok[i] >= 0:
+                z[i, boost_tok[i]] += float(boost_val[i])
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    S = e.sum(axis=1, keepdims=True)
+    p = e / S
+    logp = (z - m) - np.log(S)          # ln p, exact for every entry (no 0 * ln 0)
+    H = -(p * logp).sum(axis=1)
+    tok = np.argmax(z, axis=1).astype(np.int64)
+    lse = (m + np.log(S))[:, 0]
+    top2 = np.partition(z, z.shape[1] - 2, axis=1)[:, -2:]
+    gap = np.abs(top2[:, 1] - top2[:, 0])
+    return H, tok, lse, gap
+
+
+def exit_gate(r, w, b: float) -> np.ndarray:
+    """Halting probability lambda = sigmoid(w . r + b) per row."""
+    t = _f64(r) @ _f64(w) + float(b)
+    return 1.0 / (1.0 + np.exp(-t))
+
+
+# ---------------------------------------------------------------------------
+# one denoising step of one sequence
+# ---------------------------------------------------------------------------
+def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loops: int, eps: float,
+                          theta: float, tau_ent: float, tau_halt: float, mask_id: int, exit_b: float,
+                          boost_tok=None, boost_val=None, teacher: Optional[dict] = None,
+                          record_hidden: bool = False, counter: Optional[list] = None) -> dict:
+    """Algorithm 1 of the summary page, steps 1-5, for one sequence.
+
+    ``cache``: slot -> (K, V) [Hkv][P][hd]; ``avail``: deepest cached Core depth
+    per prefix position (None = k_max).  ``teacher`` (optional) replaces the
+    decisions by given ones: {"commit_loop": [L], "tokens": [L], "stop_loop": int}.
+    ``counter`` (optional list) receives one entry per layer call.
+    """
+    block_ids = np.asarray(block_ids, dtype=np.int64)
+    L = block_ids.shape[0]
+    P = next(iter(cache.values()))[0].shape[1] if cache else 0
+    pos = P + np.arange(L)
+
+    def run_layer(x, li, loop):
+        if counter is not None:
+            counter.append(li)
+        if cache:
+            ck, cv = context_for(cache, dims, k_max, li, loop, avail)
+        else:
+            ck = cv = None
+        y, _, _ = layer_forward(x, W, li, dims, eps, theta, pos, ck, cv, causal=False)
+        return y
+
+    # step (1): unresolved set, initial loop state, a = 0, C empty
+    U = block_ids == mask_id
+    C = np.zeros(L, dtype=bool)
+    tokens = block_ids.copy()
+    commit_loop = np.zeros(L, dtype=np.int64)
+    a = np.zeros(L, dtype=F64)
+    h = _f64(W["embed"][block_ids])
+    for li in range(dims.n_pre):
+        h = run_layer(h, li, 1)
+
+    loops = []
+    s_end = 0
+    last = None
+    for s in range(1, k_loops + 1):
+        s_end = s
+        # step (2): Core update, Coda readout
+        y = h
+        for c in range(dims.n_core):
+            y = run_layer(y, dims.n_pre + c, s)
+        h_tilde = y
+        g = h_tilde
+        for c in range(dims.n_coda):
+            g = run_layer(g, dims.n_pre + dims.n_core + c, s)
+        r = rms_norm(g, W["final_norm"], eps)
+        rows = np.nonzero(U)[0]
+        H = np.full(L, np.nan)
+        tok = np.full(L, -1, dtype=np.int64)
+        lse = np.full(L, np.nan)
+        gap = np.full(L, np.nan)
+        lam = np.full(L, np.nan)
+        if rows.size:
+            bt = None if boost_tok is None else np.asarray(boost_tok)[rows]
+            bv = None if boost_val is None else np.asarray(boost_val)[rows]
+            H[rows], tok[rows], lse[rows], gap[rows] = readout(r[rows], W["lm_head"], bt, bv)
+            lam[rows] = exit_gate(r[rows], W["exit_w"], exit_b)
+        # step (4), first half: cumulative halting for the positions unresolved at loop start
+        a[rows] = a[rows] + (1.0 - a[rows]) * lam[rows]
+        # step (3): commit
+        if teacher is None:
+            newly = rows[H[rows] <= tau_ent]
+        else:
+            tcl = np.asarray(teacher["commit_loop"])
+            newly = rows[tcl[rows] == s]
+        for i in newly:
+            tokens[i] = tok[i] if teacher is None else int(teacher["tokens"][i])
+            commit_loop[i] = s
+        U[newly] = False
+        C[newly] = True
+        # Eq. 3: every row that is not unresolved re-enters as the embedding of its token
+        h = h_tilde.copy()
+        fixed = np.nonzero(~U)[0]
+        if fixed.size:
+            h[fixed] = _f64(W["embed"][tokens[fixed]])
+        # step (4), second half: stop test on the remaining unresolved positions
+        n_u = int(U.sum())
+        mean_a = float(a[U].mean()) if n_u else float("nan")
+        if teacher is None:
+            stop = n_u == 0 or mean_a >= tau_halt or s == k_loops
+        else:
+            stop = s == int(teacher["stop_loop"])
+        rec = dict(loop=s, rows=rows, H=H, tok=tok, lse=lse, gap=gap, lam=lam, a=a.copy(),
+                   committed=np.array(newly), mean_a=mean_a, n_unresolved=n_u)
+        if record_hidden:
+            rec["h_tilde"] = h_tilde
+            rec["h"] = h.copy()
+            rec["r"] = r
+        loops.append(rec)
+        last = rec
+        if stop:
+            break
+
+    # step (5): forced progress
+    forced = -1
+    forced_gap = float("nan")
+    if not C.any() and U.any() and last is not None:
+        cand = np.nonzero(U)[0]
+        if teacher is None:
+            Hc = last["H"][cand]
+            forced = int(cand[np.argmin(Hc)])
+            srt = np.sort(Hc)
+            forced_gap = float(srt[1] - srt[0]) if srt.size > 1 else float("inf")
+            tokens[forced] = last["tok"][forced]
+        else:
+            tcl = np.asarray(teacher["commit_loop"])
+            hits = cand[tcl[cand] == -s_end]
+            if hits.size:
+                forced = int(hits[0])
+                tokens[forced] = int(teacher["tokens"][forced])
+        if forced >= 0:
+            commit_loop[forced] = -s_end
+            U[forced] = False
+    return dict(tokens=tokens, commit_loop=commit_loop, loops=s_end, records=loops, forced=forced,
+                forced_gap=forced_gap)
+
+
+def readout_commit_group(r, W_lm, embed, exit_w, exit_b: float, tau_ent: float, tau_halt: float,
+                         boost_tok=None, boost_val=None) -> dict:
+    """The readout half of one loop for one group of rows that are all unresolved at loop 1
+    with a = 0 and a loop cap of 1: heads, cumulative halt, commit, forced progress and the
+    Eq. 3 embedding rows of the committed positions."""
+    n = r.shape[0]
+    H, tok, lse, gap = readout(r, W_lm, boost_tok, boost_val)
+    lam = exit_gate(r, exit_w, exit_b)
+    a = lam.copy()                           # a = 0 + (1 - 0) * lambda
+    commit = H <= tau_ent
+    commit_loop = np.where(commit, 1, 0).astype(np.int64)
+    forced = -1
+    if not commit.any() and n:
+        forced = int(np.argmin(H))
+        commit_loop[forced] = -1
+    committed = commit_loop != 0
+    unresolved = ~committed
+    mean_a = float(a[unresolved].mean()) if unresolved.any() else float("nan")
+    emb = np.zeros((n, embed.shape[1]), dtype=F64)
+    emb[committed] = _f64(embed[tok[committed]])
+    return dict(H=H, tok=tok, lse=lse, gap=gap, lam=lam, a=a, commit_loop=commit_loop, forced=forced,
+                mean_a=mean_a, embed_rows=emb)

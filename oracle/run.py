@@ -1,0 +1,89 @@
+"""Drives the oracle over a seeded synthetic workload (test infrastructure only).
+
+Builds the oracle's inputs from the shared seeded generator and runs the
+per-sequence oracle step; nothing here reads GPU results.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional
+
+import numpy as np
+
+from adaptive_looped_denoising_amd import synth
+from oracle import alodlm_oracle as orc
+
+
+def weights(w: synth.Workload, names: Optional[List[str]] = None) -> Dict[str, np.ndarray]:
+    """Workload weights as float32 arrays holding the exact stored values."""
+    return {k: synth.as_f32(v) for k, v in synth.host_weights(w, names).items()}
+
+
+def cache_for(w: synth.Workload, W, b: int, prefix_ids=None) -> Dict[int, tuple]:
+    """Depth-aware prefix cache of sequence b: computed by the oracle's prefill, or the
+    workload's synthetic K/V."""
+    if w.prefix == 0:
+        return {}
+    if w.kv == "synthetic":
+        out = {}
+        for slot in range(w.dims.kv_slots(w.k_max)):
+            K, V = synth.synthetic_kv_seq(w, slot, b)
+            out[slot] = (synth.as_f32(K), synth.as_f32(V))
+        return out
+    ids = synth.prefix_ids(w) if prefix_ids is None else prefix_ids
+    return orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+
+
+def step(w: synth.Workload, W=None, seqs=None, k_loops: Optional[int] = None, teacher=None,
+         record_hidden: bool = False, block_ids=None, boost=None, avail=None, caches=None,
+         exit_b: Optional[float] = None, counter: Optional[list] = None) -> List[dict]:
+    """Oracle denoising step for the listed sequences of the workload."""
+    W = weights(w) if W is None else W
+    seqs = range(w.batch) if seqs is None else seqs
+    bids = synth.block_ids(w) if block_ids is None else block_ids
+    btok, bval = synth.boosts(w) if boost is None else boost
+    av = synth.avail_depth(w) if avail is None else avail
+    pids = synth.prefix_ids(w) if (w.kv == "prefill" and w.prefix) else None
+    out = []
+    for b in seqs:
+        cache = caches[b] if caches is not None else cache_for(w, W, b, pids)
+        res = orc.denoise_step_sequence(
+            bids[b], cache, av[b] if av is not None and w.prefix else None, W, w.dims,
+            k_max=w.k_max, k_loops=w.k_max if k_loops is None else k_loops, eps=w.rms_eps,
+            theta=w.rope_theta, tau_ent=w.tau_ent, tau_halt=w.tau_halt, mask_id=w.mask_id,
+            exit_b=w.exit_bias() if exit_b is None else exit_b, boost_tok=btok[b], boost_val=bval[b],
+            teacher=None if teacher is None else teacher[b], record_hidden=record_hidden, counter=counter)
+        res["seq"] = b
+        out.append(res)
+    return out
+
+
+def teacher_from(results: List[dict]) -> Dict[int, dict]:
+    """Teacher-forcing decisions (commit loops, tokens, stop loop) taken from oracle results."""
+    return {r["seq"]: dict(commit_loop=r["commit_loop"], tokens=r["tokens"], stop_loop=r["loops"])
+            for r in results}
+
+
+def near_decisions(w: synth.Workload, res: dict, ent_tol: float = 1e-2, gap_tol: float = 1e-2,
+                   halt_tol: float = 1e-2) -> List[str]:
+    """Decisions of one oracle sequence that sit within the tolerances of a threshold:
+    |H - tau_ent|, top-2 logit gap of a committed token, |mean a - tau_halt|, forced-commit
+    entropy gap.  A GPU free run may legitimately differ from the oracle only there."""
+    flags = []
+    for rec in res["records"]:
+        rows = rec["rows"]
+        if rows.size:
+            d = np.abs(rec["H"][rows] - w.tau_ent)
+            if (d < ent_tol).any():
+                flags.append("entropy loop %d rows %s" % (rec["loop"], rows[d < ent_tol].tolist()))
+        for i in rec["committed"]:
+            if rec["gap"][i] < gap_tol:
+                flags.append("argmax gap loop %d row %d" % (rec["loop"], i))
+        if rec["n_unresolved"] and abs(rec["mean_a"] - w.tau_halt) < halt_tol:
+            flags.append("halt loop %d" % rec["loop"])
+    if res["forced"] >= 0:
+        last = res["records"][-1]
+        if res["forced_gap"] < ent_tol:
+            flags.append("forced entropy gap")
+        if last["gap"][res["forced"]] < gap_tol:
+            flags.append("forced argmax gap")
+    return flags

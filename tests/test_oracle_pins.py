@@ -1,0 +1,427 @@
+"""Pins of the oracle to facts it does not compute itself: closed forms, textbook identities,
+brute force on tiny inputs, the structural counts printed on the method pages, and an
+independently written straight-line forward.  CPU only."""
+import json
+import math
+import os
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from adaptive_looped_denoising_amd import synth
+from oracle import alodlm_oracle as orc
+from oracle import run
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _tiny(**over):
+    return synth.workload("tiny", **over)
+
+
+def _rand_weights(w, seed=0):
+    """Random weights with non-unit gains (so gains are exercised), float64."""
+    rng = np.random.default_rng(seed)
+    W = {}
+    for s in synth.weight_specs(w):
+        if "const" in s:
+            W[s["name"]] = 1.0 + 0.1 * rng.standard_normal(s["shape"])
+        else:
+            W[s["name"]] = 0.05 * rng.standard_normal(s["shape"])
+    return W
+
+
+# --------------------------------------------------------------------------- generator
+def test_philox_known_answers():
+    for v in _golden("philox4x32_10_kat.json")["vectors"]:
+        out = synth.philox4x32_10([int(x, 16) for x in v["ctr"]], [int(x, 16) for x in v["key"]])
+        assert [int(x) for x in out] == [int(x, 16) for x in v["out"]]
+
+
+def test_generator_ranges_and_layouts():
+    w = _tiny()
+    ids = synth.prefix_ids(w)
+    assert ids.shape == (1, 32) and ids.min() >= 0 and ids.max() < w.dims.vocab
+    tok, val = synth.boosts(w)
+    easy = tok >= 0
+    assert easy.sum() == w.n_easy == 10
+    assert (val[easy] >= 4).all() and (val[easy] < 10).all() and (val[~easy] == 0).all()
+    assert tok.max() <= w.dims.vocab - 2
+    # element ranges are the same numbers whichever slice is asked for
+    full = synth.ih4((1000,), 7, 99, 0.5, "bf16")
+    part = synth.ih4((100,), 7, 99, 0.5, "bf16", start=450)
+    assert np.array_equal(full[450:550], part)
+    w4 = synth.workload("qwen3_8b_long")
+    w4s = replace(w4, batch=2, prefix=64)
+    av = synth.avail_depth(w4s)
+    assert (np.sort(np.unique(av)) == [3, 6]).all() and ((av == 3).sum(axis=1) == 16).all()
+
+
+# --------------------------------------------------------------------------- layer primitives
+def test_rmsnorm_of_constant_vector_is_gain():
+    g = np.linspace(0.5, 2.0, 64)
+    for c in (3.0, -0.25, 1e3):
+        np.testing.assert_allclose(orc.rms_norm(np.full(64, c), g, 0.0), np.sign(c) * g, rtol=1e-14)
+
+
+def test_rope_identity_norm_and_relative_position():
+    rng = np.random.default_rng(1)
+    hd = 32
+    x = rng.standard_normal((3, hd))
+    np.testing.assert_allclose(orc.rope(x, np.zeros(3), 1e6), x, rtol=0, atol=0)
+    y = orc.rope(x, np.array([5, 77, 1000]), 1e4)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    q, k = rng.standard_normal(hd), rng.standard_normal(hd)
+    dots = []
+    for m, n in ((10, 3), (107, 100), (7, 0)):
+        qm = orc.rope(q[None], np.array([m]), 1e4)[0]
+        kn = orc.rope(k[None], np.array([n]), 1e4)[0]
+        dots.append(qm @ kn)
+    np.testing.assert_allclose(dots, dots[0], rtol=1e-12)
+    # rotate-half pairing: a unit vector on coordinate 0 turns into (cos, ..., sin at hd/2)
+    e0 = np.zeros((1, hd)); e0[0, 0] = 1.0
+    r = orc.rope(e0, np.array([2]), 1e6)[0]
+    assert r[0] == pytest.approx(math.cos(2.0)) and r[hd // 2] == pytest.approx(math.sin(2.0))
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((4, 5, 8))
+    k = rng.standard_normal((2, 7, 8))
+    v = rng.standard_normal((2, 7, 8))
+    # GQA with group 2 equals MHA over duplicated kv heads [0, 0, 1, 1]
+    gqa = orc.attention(q, k, v)
+    mha = orc.attention(q, k[[0, 0, 1, 1]], v[[0, 0, 1, 1]])
+    np.testing.assert_allclose(gqa, mha, rtol=1e-14)
+    # identical keys give the mean of the values
+    kk = np.repeat(k[:, :1], 7, axis=1)
+    np.testing.assert_allclose(orc.attention(q, kk, v)[0], np.broadcast_to(v[0].mean(0), (5, 8)), rtol=1e-12)
+    # one visible key returns its value
+    allowed = np.zeros((5, 7), dtype=bool); allowed[:, 3] = True
+    np.testing.assert_allclose(orc.attention(q, k, v, allowed)[1], np.broadcast_to(v[0, 3], (5, 8)), rtol=1e-12)
+
+
+def test_silu_values():
+    assert orc.silu(0.0) == 0.0
+    assert orc.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert orc.silu(-40.0) == pytest.approx(-40.0 * math.exp(-40.0), rel=1e-9)
+
+
+# --------------------------------------------------------------------------- heads
+@pytest.mark.parametrize("V,lnV", [(512, 6.238325), (151936, 11.931215)])
+def test_uniform_readout_entropy_is_log_vocab(V, lnV):
+    r = np.ones((3, 16))
+    H, tok, lse, gap = orc.readout(r, np.zeros((V, 16)))
+    np.testing.assert_allclose(H, math.log(V), rtol=1e-12)
+    assert abs(H[0] - lnV) < 1e-6
+    assert (tok == 0).all() and (gap == 0).all()
+    np.testing.assert_allclose(lse, math.log(V), rtol=1e-12)
+
+
+@pytest.mark.parametrize("beta", [0.0, 1.5, 4.0, 10.0, 20.0])
+def test_two_level_entropy_closed_form(beta):
+    V = 512
+    H, tok, _, _ = orc.readout(np.ones((1, 4)), np.zeros((V, 4)), [37], [beta])
+    e = math.exp(beta)
+    expect = math.log(e + V - 1) - beta * e / (e + V - 1)
+    assert H[0] == pytest.approx(expect, rel=1e-12, abs=1e-13)
+    assert tok[0] == (37 if beta > 0 else 0)
+
+
+def test_readout_brute_force_tiny_vocab():
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        V, d = int(rng.integers(2, 9)), int(rng.integers(1, 5))
+        Wl = rng.standard_normal((V, d))
+        r = rng.standard_normal((4, d))
+        bt = rng.integers(-1, V, size=4)
+        bv = rng.uniform(0, 3, size=4)
+        H, tok, lse, _ = orc.readout(r, Wl, bt, bv)
+        for i in range(4):
+            z = [sum(Wl[t][j] * r[i][j] for j in range(d)) + (bv[i] if t == bt[i] else 0.0) for t in range(V)]
+            Z = sum(math.exp(x) for x in z)
+            ps = [math.exp(x) / Z for x in z]
+            assert H[i] == pytest.approx(-sum(p * math.log(p) for p in ps), rel=1e-10, abs=1e-12)
+            assert lse[i] == pytest.approx(math.log(Z), rel=1e-12)
+            assert tok[i] == max(range(V), key=lambda t: (z[t], -t))
+
+
+def test_argmax_ties_go_to_lowest_id():
+    Wl = np.zeros((6, 2)); Wl[2] = [1, 0]; Wl[4] = [1, 0]
+    _, tok, _, gap = orc.readout(np.array([[1.0, 0.0]]), Wl)
+    assert tok[0] == 2 and gap[0] == 0
+
+
+def test_exit_gate_sigmoid():
+    lam = orc.exit_gate(np.zeros((2, 8)), np.zeros(8), math.log(0.42 / 0.58))
+    np.testing.assert_allclose(lam, 0.42, rtol=1e-14)
+    lam = orc.exit_gate(np.ones((1, 4)), np.array([1.0, -2.0, 0.5, 0.0]), 0.25)
+    assert lam[0] == pytest.approx(1.0 / (1.0 + math.exp(0.25)), rel=1e-14)
+
+
+def test_online_entropy_merge_equals_two_pass():
+    """The streaming (max, S, T) merge a vocabulary-tiled readout uses reproduces H and lse."""
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal(1000) * 3
+    H_ref, _, lse_ref, _ = orc.readout(np.ones((1, 1)), z[:, None])
+    for tile in (1, 7, 64, 333, 1000):
+        M, S, T = -np.inf, 0.0, 0.0
+        for o in range(0, z.size, tile):
+            t = z[o:o + tile]
+            m2 = t.max(); e = np.exp(t - m2); S2 = e.sum(); T2 = ((t - m2) * e).sum()
+            Mn = max(M, m2)
+            e1 = math.exp(M - Mn) if S else 0.0
+            e2 = math.exp(m2 - Mn)
+            T = ((T + (M - Mn) * S) * e1 if S else 0.0) + (T2 + (m2 - Mn) * S2) * e2
+            S = S * e1 + S2 * e2
+            M = Mn
+        assert math.log(S) - T / S == pytest.approx(H_ref[0], rel=1e-12)
+        assert M + math.log(S) == pytest.approx(lse_ref[0], rel=1e-12)
+
+
+# --------------------------------------------------------------------------- cache structure
+def test_kv_slot_count_matches_page():
+    g = _golden("page_constants.json")
+    d8 = synth.QWEN3_8B_DIMS
+    assert (d8.n_pre, d8.n_pre + d8.n_core, d8.n_layers) == (10, 26, 36)
+    assert tuple(g["layer_split_8b"]["value"]["core"]) == (10, 26)
+    K = g["k_loops"]["value"]
+    n_slots = d8.kv_slots(K)
+    assert n_slots == g["kv_buffers_8b_k4"]["value"] == 84
+    assert n_slots == d8.n_layers + (K - 1) * d8.n_core      # L + (K - 1) m
+    assert d8.kv_slots(1) == g["kv_buffers_8b_k4"]["autoregressive_value"]
+    slots = {orc.kv_slot(d8, K, l, dp) for l in range(36) for dp in range(1, K + 1)}
+    assert slots == set(range(84))
+    assert d8.kv_slots(6) == 116
+
+
+def test_prefill_builds_every_slot_and_is_causal():
+    w = _tiny()
+    W = run.weights(w)
+    ids = synth.prefix_ids(w)[0]
+    cache = orc.prefill_sequence(ids, W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+    assert sorted(cache) == list(range(w.dims.kv_slots(w.k_max)))
+    # causal: the cache of the first 10 positions does not depend on later tokens
+    short = orc.prefill_sequence(ids[:10], W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+    for s in cache:
+        np.testing.assert_allclose(cache[s][0][:, :10], short[s][0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(cache[s][1][:, :10], short[s][1], rtol=1e-12, atol=1e-14)
+
+
+def test_depth_select_reads_min_of_loop_and_available_depth():
+    d = synth.TINY_DIMS
+    K, P = 4, 9
+    cache = {}
+    for l in range(d.n_layers):
+        core = d.n_pre <= l < d.n_pre + d.n_core
+        for dp in range(1, (K if core else 1) + 1):
+            s = orc.kv_slot(d, K, l, dp)
+            cache[s] = (np.full((d.n_kv_heads, P, 4), float(dp)), np.full((d.n_kv_heads, P, 4), 10.0 * dp + s))
+    avail = np.array([1, 2, 3, 4, 4, 3, 2, 1, 4])
+    for loop in range(1, K + 1):
+        for l in range(d.n_pre, d.n_pre + d.n_core):
+            Kc, Vc = orc.context_for(cache, d, K, l, loop, avail)
+            expect = np.minimum(loop, avail)
+            assert (Kc[0, :, 0] == expect).all()
+            c = l - d.n_pre
+            assert (Vc[1, :, 2] == 10.0 * expect + d.n_pre + c * K + expect - 1).all()
+        Kp, _ = orc.context_for(cache, d, K, 0, loop, avail)
+        assert (Kp == 1.0).all()
+
+
+def test_layer_call_count_matches_page():
+    g = _golden("page_constants.json")
+    dims = replace(synth.QWEN3_8B_DIMS, vocab=64, d_model=16, n_q_heads=2, n_kv_heads=1, head_dim=8, ffn=16)
+    w = replace(_tiny(), dims=dims, prefix=0, block=4, k_max=4, tau_ent=-1.0, tau_halt=2.0)
+    calls = []
+    res = run.step(w, counter=calls)
+    assert res[0]["loops"] == 4
+    assert len(calls) == g["layer_calls_8b_k4"]["value"] == 114
+    assert 4 * dims.n_layers == g["layer_calls_8b_k4"]["full_stack_value"]
+
+
+# --------------------------------------------------------------------------- step-level pins
+def _straight_line_tokens(w, W, prefix, block):
+    """Independent forward of [prefix ; block] through the whole stack in one pass: prefix rows
+    attend causally, block rows attend to everything.  Returns argmax tokens of the block rows."""
+    D = w.dims
+    Hq, Hkv, hd, F = D.n_q_heads, D.n_kv_heads, D.head_dim, D.ffn
+    ids = np.concatenate([prefix, block])
+    n, P = ids.size, prefix.size
+    pos = np.arange(n, dtype=np.float64)
+    x = np.array(W["embed"], dtype=np.float64)[ids]
+    vis = np.tril(np.ones((n, n), dtype=bool))
+    vis[P:, :] = True
+
+    def norm(t, g):
+        return t * (1.0 / np.sqrt((t ** 2).sum(-1, keepdims=True) / t.shape[-1] + w.rms_eps)) * g
+
+    half = hd // 2
+    freq = np.exp(-np.log(w.rope_theta) * np.arange(0, hd, 2) / hd)
+    cos, sin = np.cos(np.outer(pos, freq)), np.sin(np.outer(pos, freq))
+
+    def rot(t):  # t [n][H][hd]
+        a, b = t[..., :half], t[..., half:]
+        return np.concatenate([a * cos[:, None] - b * sin[:, None], a * sin[:, None] + b * cos[:, None]], -1)
+
+    for l in range(D.n_layers):
+        g = lambda k: np.array(W["layers.%d.%s" % (l, k)], dtype=np.float64)
+        t = norm(x, g("attn_norm"))
+        wq, wk, wv = np.split(g("wqkv"), [Hq * hd, (Hq + Hkv) * hd])
+        q = rot(norm(np.einsum("nd,od->no", t, wq).reshape(n, Hq, hd), g("q_norm")))
+        k = rot(norm(np.einsum("nd,od->no", t, wk).reshape(n, Hkv, hd), g("k_norm")))
+        v = np.einsum("nd,od->no", t, wv).reshape(n, Hkv, hd)
+        k = np.repeat(k, Hq // Hkv, axis=1)
+        v = np.repeat(v, Hq // Hkv, axis=1)
+        sc = np.einsum("qhe,khe->hqk", q, k) / np.sqrt(hd)
+        sc[:, ~vis] = -np.inf
+        pr = np.exp(sc - sc.max(-1, keepdims=True))
+        pr /= pr.sum(-1, keepdims=True)
+        o = np.einsum("hqk,khe->qhe", pr, v).reshape(n, Hq * hd)
+        x = x + o @ g("wo").T
+        t = norm(x, g("ffn_norm"))
+        gate, up = np.split(t @ g("w_gate_up").T, 2, axis=1)
+        x = x + (gate * (1.0 / (1.0 + np.exp(-gate))) * up) @ g("w_down").T
+    r = norm(x[P:], np.array(W["final_norm"], dtype=np.float64))
+    logits = r @ np.array(W["lm_head"], dtype=np.float64).T
+    return logits.argmax(axis=1)
+
+
+def test_all_commit_reduces_to_one_fixed_depth_pass():
+    """tau_ent >= ln V commits every masked row at loop 1: the tokens are the argmax of a plain
+    fixed-depth stack (here with a one-deep cache, where the stack and the loop coincide)."""
+    w = _tiny(k_max=1, tau_ent=math.log(512) + 1.0)
+    W = _rand_weights(w, seed=5)
+    pre = synth.prefix_ids(w)[0]
+    blk = synth.block_ids(w)[0].copy()
+    blk[[1, 4]] = [17, 300]   # two rows already decoded
+    res = run.step(w, W=W, block_ids=blk[None], boost=(np.full((1, 16), -1), np.zeros((1, 16))))
+    expect = _straight_line_tokens(w, W, pre, blk)
+    masked = blk == w.mask_id
+    assert res[0]["loops"] == 1
+    assert (res[0]["commit_loop"][masked] == 1).all() and (res[0]["commit_loop"][~masked] == 0).all()
+    assert np.array_equal(res[0]["tokens"][masked], expect[masked])
+    assert np.array_equal(res[0]["tokens"][~masked], blk[~masked])
+
+
+def test_looping_equals_unrolling():
+    """K loops of the shared Core equal one pass of a stack with the Core unrolled K times."""
+    K = 3
+    w = _tiny(k_max=K, tau_ent=-1.0, tau_halt=2.0)
+    W = _rand_weights(w, seed=6)
+    D = w.dims
+    Du = replace(D, n_core=D.n_core * K)
+    wu = replace(w, dims=Du, k_max=1)
+    Wu = {k: v for k, v in W.items() if not k.startswith("layers.")}
+    src = list(range(D.n_pre)) + [D.n_pre + c for _ in range(K) for c in range(D.n_core)] + \
+        [D.n_pre + D.n_core + c for c in range(D.n_coda)]
+    for lu, l in enumerate(src):
+        for key in ("attn_norm", "wqkv", "q_norm", "k_norm", "wo", "ffn_norm", "w_gate_up", "w_down"):
+            Wu["layers.%d.%s" % (lu, key)] = W["layers.%d.%s" % (l, key)]
+    looped = run.step(w, W=W, record_hidden=True)[0]
+    unrolled = run.step(wu, W=Wu, record_hidden=True)[0]
+    assert looped["loops"] == K and unrolled["loops"] == 1
+    a, b = looped["records"][-1], unrolled["records"][0]
+    np.testing.assert_allclose(a["h_tilde"], b["h_tilde"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(a["H"], b["H"], rtol=1e-11)
+    assert np.array_equal(a["tok"], b["tok"])
+
+
+def test_uniform_depth_when_nothing_commits_and_halting_is_off():
+    w = _tiny(tau_ent=0.0, tau_halt=1.5)
+    res = run.step(w, record_hidden=True)[0]
+    assert res["loops"] == w.k_max
+    for rec in res["records"]:
+        assert rec["committed"].size == 0
+        assert (rec["H"][rec["rows"]] > 0).all()
+    last = res["records"][-1]
+    i = int(np.argmin(last["H"]))
+    assert res["forced"] == i and res["commit_loop"][i] == -w.k_max and res["tokens"][i] == last["tok"][i]
+    assert (np.delete(res["commit_loop"], i) == 0).all()
+
+
+def test_uniform_readout_forces_lowest_position():
+    w = _tiny(tau_ent=0.3)
+    W = run.weights(w)
+    W["lm_head"] = np.zeros_like(W["lm_head"])
+    res = run.step(w, W=W, boost=(np.full((1, 16), -1), np.zeros((1, 16))))[0]
+    for rec in res["records"]:
+        np.testing.assert_allclose(rec["H"], math.log(512), rtol=1e-12)
+    assert res["forced"] == 0 and res["tokens"][0] == 0 and res["commit_loop"][0] == -res["loops"]
+
+
+@pytest.mark.parametrize("lam,tau_halt,s_star", [(0.42, 0.5, 2), (0.42, 0.9, 5), (0.42, 0.3, 1), (0.2, 0.5, 4)])
+def test_halting_closed_form(lam, tau_halt, s_star):
+    K = 6
+    w = _tiny(k_max=K, tau_ent=-1.0, tau_halt=tau_halt)
+    W = run.weights(w)
+    W["exit_w"] = np.zeros_like(W["exit_w"])
+    res = run.step(w, W=W, exit_b=math.log(lam / (1 - lam)))[0]
+    expect = min(K, math.ceil(math.log(1 - tau_halt) / math.log(1 - lam)))
+    assert expect == s_star
+    assert res["loops"] == s_star
+    for rec in res["records"]:
+        np.testing.assert_allclose(rec["a"], 1 - (1 - lam) ** rec["loop"], rtol=1e-12)
+
+
+def test_eq3_committed_rows_are_token_embeddings():
+    w = _tiny(boost_lo=12.0, boost_hi=14.0)
+    W = run.weights(w)
+    res = run.step(w, W=W, record_hidden=True)[0]
+    n_commit = 0
+    for rec in res["records"]:
+        for i in np.nonzero(res["commit_loop"] != 0)[0]:
+            if 0 < res["commit_loop"][i] <= rec["loop"]:
+                assert np.array_equal(rec["h"][i], np.asarray(W["embed"][res["tokens"][i]], dtype=np.float64))
+                n_commit += 1
+        unres = np.nonzero(res["commit_loop"] == 0)[0]
+        assert np.array_equal(rec["h"][unres], rec["h_tilde"][unres])
+    assert n_commit > 0
+
+
+def test_committed_tokens_are_planted_tokens_when_boost_dominates():
+    w = _tiny(boost_lo=20.0, boost_hi=25.0, tau_ent=0.3)
+    res = run.step(w)[0]
+    tok, _ = synth.boosts(w)
+    easy = tok[0] >= 0
+    assert (res["commit_loop"][easy] == 1).all()
+    assert np.array_equal(res["tokens"][easy], tok[0][easy])
+    assert (res["commit_loop"][~easy] <= 0).all()
+
+
+def test_thresholds_are_monotone():
+    """Raising tau commits more rows at loop 1; raising q never runs fewer loops."""
+    base = _tiny(boost_lo=8.0, boost_hi=14.0)
+    W = run.weights(base)
+    first = [int((run.step(replace(base, tau_ent=t), W=W)[0]["commit_loop"] == 1).sum())
+             for t in (0.05, 0.3, 1.0, 3.0)]
+    assert first == sorted(first) and first[-1] > first[0]
+    loops = [run.step(replace(base, tau_ent=0.05, tau_halt=q), W=W)[0]["loops"] for q in (0.1, 0.5, 0.7, 0.95)]
+    assert loops == sorted(loops) and loops[-1] > loops[0]
+
+
+def test_first_loop_halt_mean_near_page_value():
+    g = _golden("page_constants.json")["mean_first_pass_halt"]["value"]
+    w = _tiny()
+    lam = run.step(w)[0]["records"][0]["lam"]
+    assert abs(float(np.nanmean(lam)) - g) < 0.1
+
+
+def test_readout_group_reduces_to_step_rule():
+    rng = np.random.default_rng(8)
+    V, d = 50, 6
+    Wl = rng.standard_normal((V, d))
+    E = rng.standard_normal((V, d))
+    r = rng.standard_normal((5, d))
+    wg = rng.standard_normal(d)
+    out = orc.readout_commit_group(r, Wl, E, wg, 0.1, tau_ent=1e9, tau_halt=0.5)
+    assert (out["commit_loop"] == 1).all()
+    np.testing.assert_array_equal(out["embed_rows"], E[out["tok"]])
+    out = orc.readout_commit_group(r, Wl, E, wg, 0.1, tau_ent=-1.0, tau_halt=0.5)
+    assert out["forced"] == int(np.argmin(out["H"])) and (out["commit_loop"] != 0).sum() == 1
