@@ -1,0 +1,86 @@
+// Device-side helpers shared by the gfx950 kernels of the looped denoising step.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace alodlm {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
+
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+// Round to nearest even (inputs are finite).
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum with a fixed reduction order (deterministic); red holds NT/64 floats.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += red[i];
+  return s;
+}
+
+// Streaming softmax statistics of a set of logits z: m = max z, S = sum e^(z-m),
+// T = sum (z-m) e^(z-m), idx = argmax (lowest index among equal maxima).
+// Entropy = ln S - T/S, log-sum-exp = m + ln S.
+struct SoftStat {
+  float m, S, T;
+  int idx;
+};
+
+__device__ __forceinline__ SoftStat softstat_empty() {
+  SoftStat s;
+  s.m = -INFINITY;
+  s.S = 0.f;
+  s.T = 0.f;
+  s.idx = 0x7FFFFFFF;
+  return s;
+}
+
+__device__ __forceinline__ SoftStat softstat_merge(const SoftStat& a, const SoftStat& b) {
+  if (a.S == 0.f) return b;
+  if (b.S == 0.f) return a;
+  SoftStat r;
+  r.m = fmaxf(a.m, b.m);
+  const float da = a.m - r.m, db = b.m - r.m;
+  const float ea = __expf(da), eb = __expf(db);
+  r.S = a.S * ea + b.S * eb;
+  r.T = (a.T + da * a.S) * ea + (b.T + db * b.S) * eb;
+  r.idx = a.m > b.m ? a.idx : (b.m > a.m ? b.idx : min(a.idx, b.idx));
+  return r;
+}
+
+__device__ __forceinline__ SoftStat softstat_shfl_xor(const SoftStat& s, int o) {
+  SoftStat r;
+  r.m = __shfl_xor(s.m, o, 64);
+  r.S = __shfl_xor(s.S, o, 64);
+  r.T = __shfl_xor(s.T, o, 64);
+  r.idx = __shfl_xor(s.idx, o, 64);
+  return r;
+}
+
+}  // namespace alodlm

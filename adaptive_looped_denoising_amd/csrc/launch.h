@@ -1,0 +1,98 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace alodlm {
+
+enum { DT_BF16 = 0, DT_FP32 = 1 };
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SOFTSTAT = 2, EPI_SWIGLU = 3 };
+
+struct SoftStat;
+
+// GEMM epilogue operands.  STORE: C = acc.  RESID: C = R + acc (fp32, R may alias C).
+// SOFTSTAT: per (row, column tile) softmax statistics of acc + boost into part[row][tile].
+// SWIGLU: act[row][j] = silu(gate_j) * up_j (act in the activation dtype).
+struct GemmEpi {
+  float* C = nullptr;
+  const float* R = nullptr;
+  int ldc = 0;
+  SoftStat* part = nullptr;
+  int n_tiles = 0;
+  const int32_t* btok = nullptr;
+  const float* bval = nullptr;
+  void* act = nullptr;
+  int ld_act = 0;
+};
+
+// Attention operands.  Query rows r = t * rows_per_seq + i of sequence slot t (cache sequence
+// seq_map[t], or t).  Keys: n_cache prefix keys at ck/cv + b*c_sSeq + h*c_sHead + j*c_sPos
+// (+ (min(loop, avail[b*av_stride + j]) - 1) * c_plane for Core layers), then the rows' own
+// keys at sk/sv + (t + s_seq0)*s_sSeq + h*s_sHead + jj*s_sPos (jj <= i when causal).
+struct AttnParams {
+  const void* q = nullptr;  // [n_rows][Hq][hd]
+  void* out = nullptr;      // [n_rows][Hq*hd]
+  int n_rows = 0, rows_per_seq = 1, Hq = 1, Hkv = 1, hd = 0;
+  float scale = 1.f;
+  const void* ck = nullptr;
+  const void* cv = nullptr;
+  int64_t c_sSeq = 0, c_sHead = 0, c_sPos = 0, c_plane = 0;
+  int n_cache = 0;
+  const uint8_t* avail = nullptr;
+  int64_t av_stride = 0;
+  int loop = 1, core = 0;
+  const int32_t* seq_map = nullptr;
+  const void* sk = nullptr;
+  const void* sv = nullptr;
+  int64_t s_sSeq = 0, s_sHead = 0, s_sPos = 0;
+  int n_self = 0, causal = 0, s_seq0 = 0;
+  // fast path scratch: split-KV partials
+  float* part = nullptr;
+  int n_split = 1;
+};
+
+void launch_embed_rows(int dtype, const int32_t* ids, int n_rows, const void* E, int d, int V, float* out,
+                       hipStream_t st);
+void launch_rmsnorm(int dtype, const float* x, int n_rows, int d, const int32_t* rows, const int32_t* n_dev,
+                    const void* g, float eps, void* out, const void* exit_w, float exit_b, float* lam,
+                    hipStream_t st);
+void launch_exit_gate(int dtype, const void* rows, int n_rows, int d, const void* w, float b, float* lam,
+                      hipStream_t st);
+void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_seq, int pos0, int Hq, int Hkv,
+                         int hd, const void* qn, const void* kn, float eps, const float* cosT, const float* sinT,
+                         void* q_out, void* k_out, void* v_out, int64_t sSeq, int64_t sHead, int64_t sPos,
+                         int seq0, hipStream_t st);
+void launch_swiglu(int dtype, const float* gu, int n_rows, int F, void* act, hipStream_t st);
+void launch_softstat_combine(const SoftStat* part, int n_rows, int n_tiles, const int32_t* n_dev, float* H,
+                             float* lse, int32_t* tok, hipStream_t st);
+void launch_step_init(const int32_t* block_ids, int B, int L, int mask_id, uint8_t* U, float* a, int32_t* tokens,
+                      int8_t* cl, int32_t* ncommit, uint8_t* stop, int8_t* loops, int32_t* act, int32_t* src_slot,
+                      hipStream_t st);
+void launch_build_lists(int nb, int L, int B, const int32_t* act_cur, const uint8_t* stop, const uint8_t* U,
+                        const int32_t* ncommit, int32_t* act_next, int32_t* src_slot, int32_t* ro_rows,
+                        int32_t* ro_map, int32_t* cnt, hipStream_t st);
+void launch_commit(int nb, int s, int k_loops, int L, int B, float tau_ent, float tau_halt, const int32_t* act,
+                   uint8_t* U, float* a, const int32_t* ro_map, const float* H, const int32_t* tok, const float* lam,
+                   const float* lse, int32_t* tokens, int8_t* cl, int32_t* ncommit, uint8_t* stop, int8_t* loops,
+                   const int8_t* tf_cl, const int32_t* tf_tok, const int8_t* tf_stop, float* dbg_H, float* dbg_lam,
+                   float* dbg_a, float* dbg_lse, int32_t* dbg_tok, hipStream_t st);
+void launch_reset_compact(int dtype, int nb_upper, const int32_t* cnt, int L, int d, int V, const int32_t* act,
+                          const int32_t* src, const uint8_t* U, const int32_t* tokens, const float* h_old,
+                          const void* E, float* h_new, hipStream_t st);
+void launch_dump_hidden(int nb, int L, int d, int B, int s, const int32_t* act, const float* h, float* out,
+                        hipStream_t st);
+void launch_gather_boosts(const int32_t* ro_rows, const int32_t* n_dev, const int32_t* act, int n_upper, int L,
+                          const int32_t* boost_tok, const float* boost_val, int32_t* btok, float* bval, hipStream_t st);
+void launch_embed_committed(int dtype, const int8_t* cl, const int32_t* tokens, const void* E, int n, int d, int V,
+                            float* out, hipStream_t st);
+
+void launch_gemm_generic(int dtype, int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                         const int32_t* m_dev, const GemmEpi& ep, hipStream_t st);
+void launch_attn_generic(int dtype, const AttnParams& p, hipStream_t st);
+
+void launch_fill_kv_synth(int dtype, void* slot_base, int B, int Hkv, int P, int P_max, int hd, uint32_t seed,
+                          uint32_t tensor, float scale, hipStream_t st);
+void launch_fill_u8(uint8_t* dst, size_t n, uint8_t v, hipStream_t st);
+void launch_copy_avail(uint8_t* dst, const uint8_t* src, size_t n, hipStream_t st);
+
+}  // namespace alodlm

@@ -1,0 +1,647 @@
+// Host runtime and C ABI of the looped denoising step: workspace plan, argument checks,
+// depth-aware prefix-cache build, and the step driver (Prelude once, then per loop the
+// shared Core, the Coda, the two heads, the commit rule, compaction and the Eq. 3 reset).
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/alodlm.h"
+#include "launch.h"
+#include "common.h"
+
+using namespace alodlm;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct Plan {
+  size_t total = 0;
+  // offsets (bytes) into the workspace
+  size_t rope_cos, rope_sin, kcache, vcache, avail;
+  size_t h, h_alt, xn, attn, qkv, q, kself, vself, gu, act;
+  size_t r, lam, H, lse, tok, btok, bval, part;
+  size_t U, a, ro_map, ro_rows, ncommit, stop, seq_loops, act_seq0, act_seq1, src_slot, cnt;
+  size_t attn_part, gemm_part;
+  // sizes
+  int64_t slot_elems = 0;  // elements of one cache slot: B * Hkv * P * hd
+  int n_slots = 0, rows_step = 0, rows_max = 0, prefill_rows = 0, n_vtiles = 0, max_pos = 0;
+  int attn_splits = 0;
+  size_t gemm_part_elems = 0;
+};
+
+size_t esize(int dtype) { return dtype == ALODLM_DTYPE_BF16 ? 2 : 4; }
+
+int check_config(const alodlm_config* c, std::string* err) {
+  char buf[256];
+  auto bad = [&](const char* what) {
+    snprintf(buf, sizeof buf, "invalid config: %s", what);
+    *err = buf;
+    return ALODLM_EINVAL;
+  };
+  if (!c) return bad("null config");
+  if (c->dtype != ALODLM_DTYPE_BF16 && c->dtype != ALODLM_DTYPE_FP32) return bad("dtype");
+  if (c->vocab < 2) return bad("vocab < 2");
+  if (c->d_model < 64 || c->d_model % 64) return bad("d_model must be a positive multiple of 64");
+  if (c->ffn < 64 || c->ffn % 64) return bad("ffn must be a positive multiple of 64");
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 32, 64 or 128");
+  if (c->n_kv_heads < 1 || c->n_q_heads < c->n_kv_heads || c->n_q_heads % c->n_kv_heads)
+    return bad("n_q_heads must be a positive multiple of n_kv_heads");
+  if (c->n_pre < 0 || c->n_coda < 0 || c->n_core < 1) return bad("layer counts");
+  if (c->k_max < 1 || c->k_max > 16) return bad("k_max must be in 1..16");
+  if (c->max_batch < 1 || c->max_batch > 1024) return bad("max_batch must be in 1..1024");
+  if (c->max_block < 1 || c->max_block > 64) return bad("max_block must be in 1..64");
+  if (c->max_prefix < 0) return bad("max_prefix < 0");
+  if (c->max_prefill_rows < 0 || (c->max_prefill_rows > 0 && c->max_prefill_rows < c->max_prefix))
+    return bad("max_prefill_rows must be 0 or >= max_prefix");
+  if (c->mask_id < 0 || c->mask_id >= c->vocab) return bad("mask_id outside [0, vocab)");
+  if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps)) return bad("rms_eps");
+  if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return bad("rope_theta");
+  return ALODLM_OK;
+}
+
+Plan make_plan(const alodlm_config& c) {
+  Plan p;
+  const size_t es = esize(c.dtype);
+  const int64_t B = c.max_batch, P = c.max_prefix, L = c.max_block, d = c.d_model, hd = c.head_dim;
+  const int64_t Hq = c.n_q_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
+  const int64_t qkv_out = (Hq + 2 * Hkv) * hd;
+  p.n_slots = c.n_pre + c.n_core * c.k_max + c.n_coda;
+  p.slot_elems = B * Hkv * P * hd;
+  p.rows_step = (int)(B * L);
+  p.prefill_rows = c.max_prefill_rows > 0 ? c.max_prefill_rows : (int)(B * P);
+  p.rows_max = p.rows_step > p.prefill_rows ? p.rows_step : p.prefill_rows;
+  p.n_vtiles = (int)((V + 63) / 64);
+  p.max_pos = (int)(P + L);
+  p.attn_splits = 16;
+  const int64_t R = p.rows_max, Rs = p.rows_step;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  p.rope_cos = take(sizeof(float) * p.max_pos * (hd / 2));
+  p.rope_sin = take(sizeof(float) * p.max_pos * (hd / 2));
+  p.kcache = take(es * p.slot_elems * p.n_slots);
+  p.vcache = take(es * p.slot_elems * p.n_slots);
+  p.avail = take(B * P);
+  p.h = take(sizeof(float) * R * d);
+  p.h_alt = take(sizeof(float) * R * d);
+  p.xn = take(es * R * d);
+  p.attn = take(es * R * Hq * hd);
+  p.qkv = take(sizeof(float) * R * qkv_out);
+  p.q = take(es * R * Hq * hd);
+  p.kself = take(es * Rs * Hkv * hd);
+  p.vself = take(es * Rs * Hkv * hd);
+  p.gu = take(sizeof(float) * R * 2 * F);
+  p.act = take(es * R * F);
+  p.r = take(es * Rs * d);
+  p.lam = take(sizeof(float) * Rs);
+  p.H = take(sizeof(float) * Rs);
+  p.lse = take(sizeof(float) * Rs);
+  p.tok = take(sizeof(int32_t) * Rs);
+  p.btok = take(sizeof(int32_t) * Rs);
+  p.bval = take(sizeof(float) * Rs);
+  p.part = take(16 * Rs * (size_t)p.n_vtiles);
+  p.U = take(Rs);
+  p.a = take(sizeof(float) * Rs);
+  p.ro_map = take(sizeof(int32_t) * Rs);
+  p.ro_rows = take(sizeof(int32_t) * Rs);
+  p.ncommit = take(sizeof(int32_t) * B);
+  p.stop = take(B);
+  p.seq_loops = take(B);
+  p.act_seq0 = take(sizeof(int32_t) * B);
+  p.act_seq1 = take(sizeof(int32_t) * B);
+  p.src_slot = take(sizeof(int32_t) * B);
+  p.cnt = take(sizeof(int32_t) * 8);
+  p.attn_part = take(sizeof(float) * Rs * Hq * (size_t)p.attn_splits * (hd + 2));
+  p.gemm_part_elems = (size_t)Rs * (size_t)(2 * F > qkv_out ? 2 * F : qkv_out) * 4;
+  p.gemm_part = take(sizeof(float) * p.gemm_part_elems);
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+struct alodlm_ctx {
+  alodlm_config cfg;
+  alodlm_weights w;
+  std::vector<alodlm_layer_weights> layers;
+  Plan plan;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipStream_t st = nullptr;
+  std::string err;
+  // prefix cache state
+  int cache_batch = -1, cache_prefix = -1;
+  // stats of the last step
+  int64_t layer_calls = 0;
+  int32_t loops_run = 0;
+
+  template <typename T>
+  T* at(size_t off) const {
+    return (T*)(ws + off);
+  }
+  int fail(int code, const std::string& m) {
+    err = m;
+    return code;
+  }
+  int hip_check(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ALODLM_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+    return ALODLM_OK;
+  }
+};
+
+namespace {
+
+int dt(const alodlm_ctx* c) { return c->cfg.dtype == ALODLM_DTYPE_BF16 ? DT_BF16 : DT_FP32; }
+
+void* cache_slot(alodlm_ctx* c, bool v, int slot) {
+  const size_t es = esize(c->cfg.dtype);
+  return c->ws + (v ? c->plan.vcache : c->plan.kcache) + es * (size_t)c->plan.slot_elems * slot;
+}
+
+int slot_of(const alodlm_config& c, int layer, int depth) {
+  if (layer < c.n_pre) return layer;
+  if (layer < c.n_pre + c.n_core) return c.n_pre + (layer - c.n_pre) * c.k_max + (depth - 1);
+  return c.n_pre + c.n_core * c.k_max + (layer - c.n_pre - c.n_core);
+}
+
+// GEMM dispatch: C = A . B^T with the given epilogue.
+void gemm(alodlm_ctx* c, int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+          const int32_t* m_dev, const GemmEpi& ep) {
+  launch_gemm_generic(dt(c), epi, A, lda, B, ldb, M, N, K, m_dev, ep, c->st);
+}
+
+void attention(alodlm_ctx* c, const AttnParams& p) { launch_attn_generic(dt(c), p, c->st); }
+
+enum Mode { STEP, PREFILL };
+
+struct LayerCall {
+  Mode mode;
+  const float* x_in;
+  float* x_out;
+  int n_rows, rows_per_seq, pos0;
+  // step: sequence map and loop; prefill: first sequence of the group and depth
+  const int32_t* seq_map;
+  int loop;
+  int seq0, depth;
+  int prefix_len;
+};
+
+// One transformer block over n_rows rows: x_out = block(x_in).  In prefill mode the rows'
+// post-RoPE K/V go straight into the cache slot of (layer, depth) and attention is causal
+// over them; in step mode the rows attend to the prefix cache (depth-selected for Core
+// layers) plus their own block's K/V.
+void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
+  const alodlm_config& g = c->cfg;
+  const alodlm_layer_weights& W = c->layers[li];
+  const Plan& p = c->plan;
+  const int d = g.d_model, hd = g.head_dim, Hq = g.n_q_heads, Hkv = g.n_kv_heads, F = g.ffn;
+  const int qkv_out = (Hq + 2 * Hkv) * hd;
+  const int n = lc.n_rows;
+  const size_t es = esize(g.dtype);
+  (void)es;
+  void* xn = c->at<void>(p.xn);
+  void* attn = c->at<void>(p.attn);
+  float* qkv = c->at<float>(p.qkv);
+  void* q = c->at<void>(p.q);
+  float* gu = c->at<float>(p.gu);
+  void* act = c->at<void>(p.act);
+
+  launch_rmsnorm(dt(c), lc.x_in, n, d, nullptr, nullptr, W.attn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st);
+  GemmEpi e1;
+  e1.C = qkv;
+  e1.ldc = qkv_out;
+  gemm(c, EPI_STORE, xn, d, W.wqkv, d, n, qkv_out, d, nullptr, e1);
+
+  AttnParams ap;
+  ap.q = q;
+  ap.out = attn;
+  ap.n_rows = n;
+  ap.rows_per_seq = lc.rows_per_seq;
+  ap.Hq = Hq;
+  ap.Hkv = Hkv;
+  ap.hd = hd;
+  ap.scale = 1.0f / sqrtf((float)hd);
+  const int64_t Pm = g.max_prefix;
+  if (lc.mode == PREFILL) {
+    const int slot = slot_of(g, li, lc.depth);
+    void* kd = cache_slot(c, false, slot);
+    void* vd = cache_slot(c, true, slot);
+    const int64_t sSeq = (int64_t)Hkv * Pm * hd, sHead = Pm * hd, sPos = hd;
+    launch_qk_norm_rope(dt(c), qkv, n, lc.rows_per_seq, 0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
+                        c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, kd, vd, sSeq, sHead, sPos, lc.seq0,
+                        c->st);
+    ap.n_cache = 0;
+    ap.sk = kd;
+    ap.sv = vd;
+    ap.s_sSeq = sSeq;
+    ap.s_sHead = sHead;
+    ap.s_sPos = sPos;
+    ap.s_seq0 = lc.seq0;
+    ap.n_self = lc.rows_per_seq;
+    ap.causal = 1;
+  } else {
+    void* ks = c->at<void>(p.kself);
+    void* vs = c->at<void>(p.vself);
+    const int64_t sSeq = (int64_t)lc.rows_per_seq * Hkv * hd, sHead = hd, sPos = (int64_t)Hkv * hd;
+    launch_qk_norm_rope(dt(c), qkv, n, lc.rows_per_seq, lc.pos0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
+                        c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, ks, vs, sSeq, sHead, sPos, 0, c->st);
+    const bool core = li >= g.n_pre && li < g.n_pre + g.n_core;
+    const int slot = slot_of(g, li, 1);
+    ap.ck = cache_slot(c, false, slot);
+    ap.cv = cache_slot(c, true, slot);
+    ap.c_sSeq = (int64_t)Hkv * Pm * hd;
+    ap.c_sHead = Pm * hd;
+    ap.c_sPos = hd;
+    ap.c_plane = p.slot_elems;
+    ap.n_cache = lc.prefix_len;
+    ap.avail = c->at<uint8_t>(p.avail);
+    ap.av_stride = lc.prefix_len;
+    ap.loop = lc.loop;
+    ap.core = core;
+    ap.seq_map = lc.seq_map;
+    ap.sk = ks;
+    ap.sv = vs;
+    ap.s_sSeq = sSeq;
+    ap.s_sHead = sHead;
+    ap.s_sPos = sPos;
+    ap.n_self = lc.rows_per_seq;
+    ap.causal = 0;
+  }
+  attention(c, ap);
+
+  GemmEpi e2;
+  e2.C = lc.x_out;
+  e2.R = lc.x_in;
+  e2.ldc = d;
+  gemm(c, EPI_RESID, attn, Hq * hd, W.wo, Hq * hd, n, d, Hq * hd, nullptr, e2);
+
+  launch_rmsnorm(dt(c), lc.x_out, n, d, nullptr, nullptr, W.ffn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st);
+  GemmEpi e3;
+  e3.C = gu;
+  e3.ldc = 2 * F;
+  gemm(c, EPI_STORE, xn, d, W.w_gate_up, d, n, 2 * F, d, nullptr, e3);
+  launch_swiglu(dt(c), gu, n, F, act, c->st);
+  GemmEpi e4;
+  e4.C = lc.x_out;
+  e4.R = lc.x_out;
+  e4.ldc = d;
+  gemm(c, EPI_RESID, act, F, W.w_down, F, n, d, F, nullptr, e4);
+  c->layer_calls += 1;
+}
+
+// LMHead statistics of the readout rows (rows >= *n_dev skipped) then the fixed-order merge.
+void readout_heads(alodlm_ctx* c, const void* rows, int n_upper, const int32_t* n_dev, const int32_t* btok,
+                   const float* bval) {
+  const alodlm_config& g = c->cfg;
+  const Plan& p = c->plan;
+  GemmEpi ep;
+  ep.part = c->at<SoftStat>(p.part);
+  ep.n_tiles = p.n_vtiles;
+  ep.btok = btok;
+  ep.bval = bval;
+  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_upper, g.vocab, g.d_model, n_dev, ep);
+  launch_softstat_combine(c->at<SoftStat>(p.part), n_upper, p.n_vtiles, n_dev, c->at<float>(p.H),
+                          c->at<float>(p.lse), c->at<int32_t>(p.tok), c->st);
+}
+
+bool finite_f(float x) { return isfinite(x) != 0; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+extern "C" {
+
+int alodlm_workspace_bytes(const alodlm_config* cfg, size_t* bytes) {
+  std::string err;
+  int rc = check_config(cfg, &err);
+  if (rc) {
+    g_create_error = err;
+    return rc;
+  }
+  if (!bytes) {
+    g_create_error = "null bytes pointer";
+    return ALODLM_EINVAL;
+  }
+  *bytes = make_plan(*cfg).total;
+  return ALODLM_OK;
+}
+
+int alodlm_kv_slots(const alodlm_config* cfg, int32_t* slots) {
+  std::string err;
+  int rc = check_config(cfg, &err);
+  if (rc) {
+    g_create_error = err;
+    return rc;
+  }
+  if (!slots) return ALODLM_EINVAL;
+  *slots = cfg->n_pre + cfg->n_core * cfg->k_max + cfg->n_coda;
+  return ALODLM_OK;
+}
+
+int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* workspace, size_t ws_bytes,
+                  void* hip_stream, alodlm_ctx** out) {
+  std::string err;
+  int rc = check_config(cfg, &err);
+  if (rc) {
+    g_create_error = err;
+    return rc;
+  }
+  if (!out || !w) {
+    g_create_error = "null weights or output pointer";
+    return ALODLM_EINVAL;
+  }
+  *out = nullptr;
+  const int nl = cfg->n_pre + cfg->n_core + cfg->n_coda;
+  if (!w->embed || !w->lm_head || !w->final_norm || !w->exit_w || !w->layers || !finite_f(w->exit_b)) {
+    g_create_error = "null weight pointer or non-finite exit_b";
+    return ALODLM_EINVAL;
+  }
+  for (int i = 0; i < nl; ++i) {
+    const alodlm_layer_weights& L = w->layers[i];
+    if (!L.attn_norm || !L.wqkv || !L.q_norm || !L.k_norm || !L.wo || !L.ffn_norm || !L.w_gate_up || !L.w_down) {
+      g_create_error = "null pointer in layer " + std::to_string(i);
+      return ALODLM_EINVAL;
+    }
+  }
+  if (!workspace || ((uintptr_t)workspace & 255)) {
+    g_create_error = "workspace null or not 256-byte aligned";
+    return ALODLM_EINVAL;
+  }
+  Plan plan = make_plan(*cfg);
+  if (ws_bytes < plan.total) {
+    g_create_error = "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(plan.total);
+    return ALODLM_ENOMEM;
+  }
+  alodlm_ctx* c = new alodlm_ctx();
+  c->cfg = *cfg;
+  c->w = *w;
+  c->layers.assign(w->layers, w->layers + nl);
+  c->w.layers = c->layers.data();
+  c->plan = plan;
+  c->ws = (char*)workspace;
+  c->ws_bytes = ws_bytes;
+  c->st = (hipStream_t)hip_stream;
+  // RoPE tables, computed in double on the host: angle(pos, i) = pos * theta^(-2i/hd)
+  const int half = cfg->head_dim / 2;
+  std::vector<float> cs((size_t)plan.max_pos * half), sn((size_t)plan.max_pos * half);
+  for (int pos = 0; pos < plan.max_pos; ++pos)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)pos * pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+      cs[(size_t)pos * half + i] = (float)cos(ang);
+      sn[(size_t)pos * half + i] = (float)sin(ang);
+    }
+  hipError_t e1 = hipMemcpyAsync(c->ws + plan.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, c->st);
+  hipError_t e2 = hipMemcpyAsync(c->ws + plan.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, c->st);
+  hipError_t e3 = hipStreamSynchronize(c->st);
+  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
+    g_create_error = std::string("RoPE table upload: ") +
+                     hipGetErrorString(e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3));
+    delete c;
+    return ALODLM_EHIP;
+  }
+  *out = c;
+  return ALODLM_OK;
+}
+
+int alodlm_prefill_kv(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const int32_t* prefix_ids,
+                      const uint8_t* avail_depth) {
+  if (!c) return ALODLM_EINVAL;
+  const alodlm_config& g = c->cfg;
+  if (batch < 1 || batch > g.max_batch) return c->fail(ALODLM_EINVAL, "batch outside 1..max_batch");
+  if (prefix_len < 0 || prefix_len > g.max_prefix) return c->fail(ALODLM_EINVAL, "prefix_len outside 0..max_prefix");
+  if (prefix_len > 0 && !prefix_ids) return c->fail(ALODLM_EINVAL, "null prefix_ids");
+  const Plan& p = c->plan;
+  c->cache_batch = -1;
+  const size_t nav = (size_t)batch * prefix_len;
+  if (avail_depth)
+    launch_copy_avail(c->at<uint8_t>(p.avail), avail_depth, nav, c->st);
+  else
+    launch_fill_u8(c->at<uint8_t>(p.avail), nav, (uint8_t)g.k_max, c->st);
+  if (prefix_len > 0) {
+    const int per = p.prefill_rows / prefix_len;  // sequences per pass (>= 1: prefill_rows >= max_prefix)
+    float* h = c->at<float>(p.h);
+    for (int b0 = 0; b0 < batch; b0 += per) {
+      const int gb = batch - b0 < per ? batch - b0 : per;
+      const int n = gb * prefix_len;
+      launch_embed_rows(dt(c), prefix_ids + (size_t)b0 * prefix_len, n, c->w.embed, g.d_model, g.vocab, h, c->st);
+      LayerCall lc{PREFILL, h, h, n, prefix_len, 0, nullptr, 1, b0, 1, prefix_len};
+      for (int li = 0; li < g.n_pre; ++li) run_layer(c, li, lc);
+      for (int dpt = 1; dpt <= g.k_max; ++dpt) {
+        lc.depth = dpt;
+        for (int ci = 0; ci < g.n_core; ++ci) run_layer(c, g.n_pre + ci, lc);
+      }
+      lc.depth = 1;
+      for (int ci = 0; ci < g.n_coda; ++ci) run_layer(c, g.n_pre + g.n_core + ci, lc);
+    }
+  }
+  int rc = c->hip_check("prefill launch");
+  if (rc) return rc;
+  c->cache_batch = batch;
+  c->cache_prefix = prefix_len;
+  return ALODLM_OK;
+}
+
+int alodlm_prefill_kv_synthetic(alodlm_ctx* c, int32_t batch, int32_t prefix_len, uint32_t seed, float k_scale,
+                                float v_scale, const uint8_t* avail_depth) {
+  if (!c) return ALODLM_EINVAL;
+  const alodlm_config& g = c->cfg;
+  if (batch < 1 || batch > g.max_batch) return c->fail(ALODLM_EINVAL, "batch outside 1..max_batch");
+  if (prefix_len < 0 || prefix_len > g.max_prefix) return c->fail(ALODLM_EINVAL, "prefix_len outside 0..max_prefix");
+  if (!finite_f(k_scale) || !finite_f(v_scale)) return c->fail(ALODLM_EINVAL, "non-finite scale");
+  const Plan& p = c->plan;
+  c->cache_batch = -1;
+  const size_t nav = (size_t)batch * prefix_len;
+  if (avail_depth)
+    launch_copy_avail(c->at<uint8_t>(p.avail), avail_depth, nav, c->st);
+  else
+    launch_fill_u8(c->at<uint8_t>(p.avail), nav, (uint8_t)g.k_max, c->st);
+  for (int s = 0; s < p.n_slots; ++s) {
+    launch_fill_kv_synth(dt(c), cache_slot(c, false, s), batch, g.n_kv_heads, prefix_len, g.max_prefix, g.head_dim,
+                         seed, 0x10000u + 2u * s, k_scale, c->st);
+    launch_fill_kv_synth(dt(c), cache_slot(c, true, s), batch, g.n_kv_heads, prefix_len, g.max_prefix, g.head_dim,
+                         seed, 0x10000u + 2u * s + 1u, v_scale, c->st);
+  }
+  int rc = c->hip_check("synthetic prefill launch");
+  if (rc) return rc;
+  c->cache_batch = batch;
+  c->cache_prefix = prefix_len;
+  return ALODLM_OK;
+}
+
+int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_out* o) {
+  if (!c) return ALODLM_EINVAL;
+  if (!a || !o) return c->fail(ALODLM_EINVAL, "null args or out");
+  const alodlm_config& g = c->cfg;
+  const Plan& p = c->plan;
+  const int B = a->batch, L = a->block_len, K = a->k_loops, d = g.d_model;
+  if (c->cache_batch < 0) return c->fail(ALODLM_ESTATE, "denoise_step before the prefix cache was built");
+  if (B != c->cache_batch) return c->fail(ALODLM_EINVAL, "batch differs from the prefilled batch");
+  if (L < 1 || L > g.max_block) return c->fail(ALODLM_EINVAL, "block_len outside 1..max_block");
+  if (K < 1 || K > g.k_max) return c->fail(ALODLM_EINVAL, "k_loops outside 1..k_max");
+  if (!finite_f(a->tau_ent) || !finite_f(a->tau_halt)) return c->fail(ALODLM_EINVAL, "non-finite threshold");
+  if (!a->block_ids) return c->fail(ALODLM_EINVAL, "null block_ids");
+  if (a->boost_tok && !a->boost_val) return c->fail(ALODLM_EINVAL, "boost_tok without boost_val");
+  const bool tf = (a->flags & ALODLM_STEP_TEACHER_FORCED) != 0;
+  if (tf && (!a->tf_commit_loop || !a->tf_tokens || !a->tf_stop_loop))
+    return c->fail(ALODLM_EINVAL, "teacher-forced step without tf_* arrays");
+  if (!o->tokens || !o->commit_loop || !o->loops) return c->fail(ALODLM_EINVAL, "null output array");
+  const bool dbg = o->entropy || o->lam || o->halt || o->lse || o->argmax;
+  if (dbg && !(o->entropy && o->lam && o->halt && o->lse && o->argmax))
+    return c->fail(ALODLM_EINVAL, "per-loop records must be all given or all null");
+  const int P = c->cache_prefix;
+  hipStream_t st = c->st;
+  c->layer_calls = 0;
+
+  uint8_t* U = c->at<uint8_t>(p.U);
+  float* av = c->at<float>(p.a);
+  int32_t* ncommit = c->at<int32_t>(p.ncommit);
+  uint8_t* stop = c->at<uint8_t>(p.stop);
+  int32_t* act[2] = {c->at<int32_t>(p.act_seq0), c->at<int32_t>(p.act_seq1)};
+  int32_t* src_slot = c->at<int32_t>(p.src_slot);
+  int32_t* ro_rows = c->at<int32_t>(p.ro_rows);
+  int32_t* ro_map = c->at<int32_t>(p.ro_map);
+  int32_t* cnt = c->at<int32_t>(p.cnt);
+  float* h = c->at<float>(p.h);
+  float* h_alt = c->at<float>(p.h_alt);
+
+  if (dbg) {
+    const size_t n = (size_t)K * B * L;
+    hipMemsetAsync(o->entropy, 0xFF, n * 4, st);  // NaN until written
+    hipMemsetAsync(o->lam, 0xFF, n * 4, st);
+    hipMemsetAsync(o->halt, 0xFF, n * 4, st);
+    hipMemsetAsync(o->lse, 0xFF, n * 4, st);
+    hipMemsetAsync(o->argmax, 0xFF, n * 4, st);
+  }
+  launch_step_init(a->block_ids, B, L, g.mask_id, U, av, o->tokens, o->commit_loop, ncommit, stop, o->loops, act[0],
+                   src_slot, st);
+  launch_build_lists(B, L, B, act[0], stop, U, ncommit, act[1], src_slot, ro_rows, ro_map, cnt, st);
+  int cur = 1;
+
+  // Prelude over every block row (slot t = sequence t)
+  launch_embed_rows(dt(c), a->block_ids, B * L, c->w.embed, d, g.vocab, h, st);
+  LayerCall lc{STEP, h, h, B * L, L, P, act[cur], 1, 0, 1, P};
+  for (int li = 0; li < g.n_pre; ++li) run_layer(c, li, lc);
+
+  int nb = B;
+  int32_t host_cnt[3] = {0, 0, 0};
+  int loops_run = 0;
+  for (int s = 1; s <= K && nb > 0; ++s) {
+    loops_run = s;
+    const int n = nb * L;
+    lc.n_rows = n;
+    lc.seq_map = act[cur];
+    lc.loop = s;
+    lc.x_in = h;
+    lc.x_out = h;
+    for (int ci = 0; ci < g.n_core; ++ci) run_layer(c, g.n_pre + ci, lc);
+    if (o->hidden) launch_dump_hidden(nb, L, d, B, s, act[cur], h, o->hidden, st);
+    const float* gsrc = h;
+    if (g.n_coda > 0) {
+      lc.x_in = h;
+      lc.x_out = h_alt;
+      for (int ci = 0; ci < g.n_coda; ++ci) {
+        run_layer(c, g.n_pre + g.n_core + ci, lc);
+        lc.x_in = h_alt;
+      }
+      gsrc = h_alt;
+    }
+    // readout rows r (compact), ExitGate lambda
+    launch_rmsnorm(dt(c), gsrc, n, d, ro_rows, cnt + 1, c->w.final_norm, g.rms_eps, c->at<void>(p.r), c->w.exit_w,
+                   c->w.exit_b, c->at<float>(p.lam), st);
+    // per-readout-row boosts
+    const int32_t* bt = nullptr;
+    const float* bv = nullptr;
+    if (a->boost_tok) {
+      // gather boosts into readout order on the device: boost index = act[t]*L + i for row t*L+i
+      bt = c->at<int32_t>(p.btok);
+      bv = c->at<float>(p.bval);
+      launch_gather_boosts(ro_rows, cnt + 1, act[cur], n, L, a->boost_tok, a->boost_val, c->at<int32_t>(p.btok),
+                           c->at<float>(p.bval), st);
+    }
+    readout_heads(c, c->at<void>(p.r), n, cnt + 1, bt, bv);
+    launch_commit(nb, s, K, L, B, a->tau_ent, a->tau_halt, act[cur], U, av, ro_map, c->at<float>(p.H),
+                  c->at<int32_t>(p.tok), c->at<float>(p.lam), c->at<float>(p.lse), o->tokens, o->commit_loop, ncommit,
+                  stop, o->loops, tf ? a->tf_commit_loop : nullptr, tf ? a->tf_tokens : nullptr,
+                  tf ? a->tf_stop_loop : nullptr, dbg ? o->entropy : nullptr, o->lam, o->halt, o->lse, o->argmax, st);
+    launch_build_lists(nb, L, B, act[cur], stop, U, ncommit, act[cur ^ 1], src_slot, ro_rows, ro_map, cnt, st);
+    launch_reset_compact(dt(c), nb, cnt, L, d, g.vocab, act[cur ^ 1], src_slot, U, o->tokens, h, c->w.embed, h_alt, st);
+    float* t = h;
+    h = h_alt;
+    h_alt = t;
+    cur ^= 1;
+    hipError_t e1 = hipMemcpyAsync(host_cnt, cnt, sizeof(host_cnt), hipMemcpyDeviceToHost, st);
+    hipError_t e2 = hipStreamSynchronize(st);
+    if (e1 != hipSuccess || e2 != hipSuccess)
+      return c->fail(ALODLM_EHIP, std::string("loop status read: ") + hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+    int rc = c->hip_check("step launch");
+    if (rc) return rc;
+    nb = host_cnt[0];
+  }
+  o->n_committed = host_cnt[2];
+  o->loops_run = loops_run;
+  c->loops_run = loops_run;
+  return ALODLM_OK;
+}
+
+int alodlm_readout_commit(alodlm_ctx* c, const void* rows, int32_t n_rows, int32_t group, float tau_ent,
+                          float tau_halt, const int32_t* boost_tok, const float* boost_val, float* entropy, float* lse,
+                          float* lam, float* halt, int32_t* argmax, int32_t* tokens, int8_t* commit_loop,
+                          float* embed_out) {
+  if (!c) return ALODLM_EINVAL;
+  const alodlm_config& g = c->cfg;
+  const Plan& p = c->plan;
+  if (!rows || !entropy || !lse || !lam || !halt || !argmax || !tokens || !commit_loop || !embed_out)
+    return c->fail(ALODLM_EINVAL, "null pointer");
+  if (n_rows < 1 || n_rows > p.rows_step) return c->fail(ALODLM_EINVAL, "n_rows outside 1..max_batch*max_block");
+  if (group < 1 || group > 64 || n_rows % group) return c->fail(ALODLM_EINVAL, "group must be 1..64 and divide n_rows");
+  if (boost_tok && !boost_val) return c->fail(ALODLM_EINVAL, "boost_tok without boost_val");
+  if (!finite_f(tau_ent) || !finite_f(tau_halt)) return c->fail(ALODLM_EINVAL, "non-finite threshold");
+  const int B = n_rows / group, L = group;
+  hipStream_t st = c->st;
+  uint8_t* U = c->at<uint8_t>(p.U);
+  int32_t* act0 = c->at<int32_t>(p.act_seq0);
+  int32_t* act1 = c->at<int32_t>(p.act_seq1);
+  int8_t* seq_loops = c->at<int8_t>(p.seq_loops);
+  launch_step_init(nullptr, B, L, g.mask_id, U, halt, tokens, commit_loop, c->at<int32_t>(p.ncommit),
+                   c->at<uint8_t>(p.stop), seq_loops, act0, c->at<int32_t>(p.src_slot), st);
+  launch_build_lists(B, L, B, act0, c->at<uint8_t>(p.stop), U, c->at<int32_t>(p.ncommit), act1,
+                     c->at<int32_t>(p.src_slot), c->at<int32_t>(p.ro_rows), c->at<int32_t>(p.ro_map),
+                     c->at<int32_t>(p.cnt), st);
+  launch_exit_gate(dt(c), rows, n_rows, g.d_model, c->w.exit_w, c->w.exit_b, lam, st);
+  // LMHead over the given rows (row order = readout order)
+  GemmEpi ep;
+  ep.part = c->at<SoftStat>(p.part);
+  ep.n_tiles = p.n_vtiles;
+  ep.btok = boost_tok;
+  ep.bval = boost_val;
+  launch_gemm_generic(dt(c), EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_rows, g.vocab, g.d_model,
+                      nullptr, ep, st);
+  launch_softstat_combine(c->at<SoftStat>(p.part), n_rows, p.n_vtiles, nullptr, entropy, lse, argmax, st);
+  // one loop of the commit rule (a starts at 0, so a = lambda); per-row records go to the outputs
+  launch_commit(B, 1, 1, L, B, tau_ent, tau_halt, act1, U, halt, c->at<int32_t>(p.ro_map), entropy, argmax, lam, lse,
+                tokens, commit_loop, c->at<int32_t>(p.ncommit), c->at<uint8_t>(p.stop), seq_loops, nullptr, nullptr,
+                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st);
+  launch_embed_committed(dt(c), commit_loop, tokens, c->w.embed, n_rows, g.d_model, g.vocab, embed_out, st);
+  return c->hip_check("readout launch");
+}
+
+int alodlm_last_step_stats(const alodlm_ctx* c, int64_t* layer_calls, int32_t* loops_run) {
+  if (!c) return ALODLM_EINVAL;
+  if (layer_calls) *layer_calls = c->layer_calls;
+  if (loops_run) *loops_run = c->loops_run;
+  return ALODLM_OK;
+}
+
+const char* alodlm_last_error(const alodlm_ctx* c) { return c ? c->err.c_str() : g_create_error.c_str(); }
+
+void alodlm_destroy(alodlm_ctx* c) { delete c; }
+
+}  // extern "C"

@@ -1,0 +1,222 @@
+"""Python-side driver of the HIP library for a seeded workload.
+
+PyTorch provides device memory and the stream; every computation of the step
+runs in libalodlm.so through the ctypes binding.  Weights are uploaded from the
+host generator for small models and filled on the device (same counter-based
+definition) for large ones.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+from . import synth
+
+
+def _dev_tensor_from_storage(arr: np.ndarray, device) -> torch.Tensor:
+    """Upload a host array in storage format (uint16 bf16 bits or float32)."""
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+@dataclass
+class StepResult:
+    tokens: np.ndarray
+    commit_loop: np.ndarray
+    loops: np.ndarray
+    n_committed: int
+    loops_run: int
+    entropy: Optional[np.ndarray] = None
+    lam: Optional[np.ndarray] = None
+    halt: Optional[np.ndarray] = None
+    lse: Optional[np.ndarray] = None
+    argmax: Optional[np.ndarray] = None
+    hidden: Optional[np.ndarray] = None
+
+
+class Engine:
+    def __init__(self, w: synth.Workload, device: str = "cuda", weight_source: Optional[str] = None,
+                 max_prefill_rows: Optional[int] = None, overrides: Optional[Dict[str, np.ndarray]] = None,
+                 exit_b: Optional[float] = None):
+        self.lib = B.load()
+        self.w = w
+        self.device = torch.device(device)
+        self.stream = torch.cuda.current_stream(self.device)
+        D = w.dims
+        self.tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.cdtype = B.DTYPE_BF16 if w.dtype == "bf16" else B.DTYPE_FP32
+        specs = synth.weight_specs(w)
+        n_params = sum(int(np.prod(s["shape"])) for s in specs)
+        if weight_source is None:
+            weight_source = "host" if n_params < 50_000_000 else "device"
+        self.tensors: Dict[str, torch.Tensor] = {}
+        for s in specs:
+            name = s["name"]
+            if overrides and name in overrides:
+                t = _dev_tensor_from_storage(overrides[name], self.device)
+            elif weight_source == "host":
+                t = _dev_tensor_from_storage(synth.gen_tensor(s, w.seed, w.dtype), self.device)
+            else:
+                t = torch.empty(s["shape"], dtype=self.tdtype, device=self.device)
+                if "const" in s:
+                    B.synth_fill(t.data_ptr(), self.cdtype, 0, t.numel(), 0, 0, 0.0, float(s["const"]),
+                                 self.stream.cuda_stream)
+                else:
+                    B.synth_fill(t.data_ptr(), self.cdtype, 0, t.numel(), w.seed, s["tensor"], float(s["scale"]),
+                                 0.0, self.stream.cuda_stream)
+            self.tensors[name] = t
+        self.cfg = B.Config(
+            vocab=D.vocab, d_model=D.d_model, n_q_heads=D.n_q_heads, n_kv_heads=D.n_kv_heads, head_dim=D.head_dim,
+            ffn=D.ffn, n_pre=D.n_pre, n_core=D.n_core, n_coda=D.n_coda, k_max=w.k_max, max_batch=w.batch,
+            max_prefix=w.prefix, max_block=w.block,
+            max_prefill_rows=max_prefill_rows if max_prefill_rows is not None else min(
+                w.batch * w.prefix, max(w.prefix, 8192)),
+            mask_id=w.mask_id, dtype=self.cdtype, rms_eps=w.rms_eps, rope_theta=w.rope_theta)
+        nl = D.n_layers
+        self.layer_arr = (B.LayerWeights * max(nl, 1))()
+        for l in range(nl):
+            p = "layers.%d." % l
+            lw = self.layer_arr[l]
+            for f in ("attn_norm", "wqkv", "q_norm", "k_norm", "wo", "ffn_norm", "w_gate_up", "w_down"):
+                setattr(lw, f, self.tensors[p + f].data_ptr())
+        self.exit_b = w.exit_bias() if exit_b is None else float(exit_b)
+        self.weights = B.Weights(embed=self.tensors["embed"].data_ptr(), lm_head=self.tensors["lm_head"].data_ptr(),
+                                 final_norm=self.tensors["final_norm"].data_ptr(),
+                                 exit_w=self.tensors["exit_w"].data_ptr(), exit_b=self.exit_b,
+                                 layers=self.layer_arr)
+        self.ws_bytes = B.workspace_bytes(self.cfg)
+        self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.ws.data_ptr()
+        self.ws_ptr = (base + 255) & ~255
+        self.ctx = B.create(self.cfg, self.weights, self.ws_ptr, self.ws_bytes, self.stream.cuda_stream)
+        self.kv_slots = B.kv_slots(self.cfg)
+        # step inputs
+        self.block_ids = torch.from_numpy(synth.block_ids(w)).to(self.device)
+        bt, bv = synth.boosts(w)
+        self.boost_tok = torch.from_numpy(bt).to(self.device)
+        self.boost_val = torch.from_numpy(bv).to(self.device)
+        self.avail = torch.from_numpy(synth.avail_depth(w)).to(self.device) if w.prefix else None
+        Bn, L = w.batch, w.block
+        self.out_tokens = torch.empty((Bn, L), dtype=torch.int32, device=self.device)
+        self.out_cl = torch.empty((Bn, L), dtype=torch.int8, device=self.device)
+        self.out_loops = torch.empty((Bn,), dtype=torch.int8, device=self.device)
+
+    # ------------------------------------------------------------------ prefix cache
+    def prefill(self, prefix_ids: Optional[np.ndarray] = None):
+        w = self.w
+        av = _ptr(self.avail)
+        if w.kv == "synthetic":
+            ks, vs = synth.synthetic_kv_scales(w)
+            B.prefill_kv_synthetic(self.ctx, w.batch, w.prefix, w.seed, float(np.float32(ks)), float(np.float32(vs)),
+                                   av)
+        else:
+            ids = synth.prefix_ids(w) if prefix_ids is None else prefix_ids
+            self.prefix_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(self.device)
+            B.prefill_kv(self.ctx, w.batch, w.prefix, _ptr(self.prefix_ids) if w.prefix else 0, av)
+        torch.cuda.synchronize(self.device)
+
+    # ------------------------------------------------------------------ step
+    def make_args(self, tau_ent=None, tau_halt=None, k_loops=None, boost=True, teacher=None, block_ids=None):
+        w = self.w
+        if block_ids is not None:
+            self.block_ids = torch.from_numpy(np.ascontiguousarray(block_ids, dtype=np.int32)).to(self.device)
+        args = B.StepArgs(batch=w.batch, block_len=w.block, block_ids=_ptr(self.block_ids),
+                          tau_ent=w.tau_ent if tau_ent is None else tau_ent,
+                          tau_halt=w.tau_halt if tau_halt is None else tau_halt,
+                          k_loops=w.k_max if k_loops is None else k_loops, flags=0,
+                          boost_tok=_ptr(self.boost_tok) if boost else 0,
+                          boost_val=_ptr(self.boost_val) if boost else 0)
+        if teacher is not None:
+            Bn, L = w.batch, w.block
+            cl = np.zeros((Bn, L), dtype=np.int8)
+            tk = np.zeros((Bn, L), dtype=np.int32)
+            sl = np.zeros((Bn,), dtype=np.int8)
+            for b, t in teacher.items():
+                cl[b] = t["commit_loop"]
+                tk[b] = t["tokens"]
+                sl[b] = t["stop_loop"]
+            self._tf = [torch.from_numpy(x).to(self.device) for x in (cl, tk, sl)]
+            args.flags = B.STEP_TEACHER_FORCED
+            args.tf_commit_loop, args.tf_tokens, args.tf_stop_loop = (t.data_ptr() for t in self._tf)
+        return args
+
+    def make_out(self, k_loops: int, records: bool = False, hidden: bool = False):
+        w = self.w
+        out = B.StepOut(tokens=_ptr(self.out_tokens), commit_loop=_ptr(self.out_cl), loops=_ptr(self.out_loops))
+        self._rec = None
+        if records:
+            shp = (k_loops, w.batch, w.block)
+            self._rec = dict(entropy=torch.empty(shp, dtype=torch.float32, device=self.device),
+                             lam=torch.empty(shp, dtype=torch.float32, device=self.device),
+                             halt=torch.empty(shp, dtype=torch.float32, device=self.device),
+                             lse=torch.empty(shp, dtype=torch.float32, device=self.device),
+                             argmax=torch.empty(shp, dtype=torch.int32, device=self.device))
+            for k, t in self._rec.items():
+                setattr(out, k, t.data_ptr())
+        self._hidden = None
+        if hidden:
+            self._hidden = torch.full((k_loops, w.batch, w.block, w.dims.d_model), float("nan"), dtype=torch.float32,
+                                      device=self.device)
+            out.hidden = self._hidden.data_ptr()
+        return out
+
+    def run(self, args: B.StepArgs, out: B.StepOut):
+        B.denoise_step(self.ctx, args, out)
+
+    def step(self, tau_ent=None, tau_halt=None, k_loops=None, boost=True, teacher=None, records=False,
+             hidden=False, block_ids=None) -> StepResult:
+        args = self.make_args(tau_ent, tau_halt, k_loops, boost, teacher, block_ids)
+        out = self.make_out(args.k_loops, records, hidden)
+        self.run(args, out)
+        torch.cuda.synchronize(self.device)
+        res = StepResult(tokens=self.out_tokens.cpu().numpy(), commit_loop=self.out_cl.cpu().numpy(),
+                         loops=self.out_loops.cpu().numpy(), n_committed=out.n_committed, loops_run=out.loops_run)
+        if self._rec is not None:
+            for k, t in self._rec.items():
+                setattr(res, k, t.cpu().numpy())
+        if self._hidden is not None:
+            res.hidden = self._hidden.cpu().numpy()
+        return res
+
+    def stats(self):
+        return B.last_step_stats(self.ctx)
+
+    # ------------------------------------------------------------------ readout half of a loop
+    def readout_commit(self, rows: torch.Tensor, group: int, tau_ent: float, tau_halt: float,
+                       boost_tok: Optional[torch.Tensor] = None, boost_val: Optional[torch.Tensor] = None) -> dict:
+        n = rows.shape[0]
+        dev = self.device
+        o = dict(entropy=torch.empty(n, dtype=torch.float32, device=dev),
+                 lse=torch.empty(n, dtype=torch.float32, device=dev),
+                 lam=torch.empty(n, dtype=torch.float32, device=dev),
+                 halt=torch.empty(n, dtype=torch.float32, device=dev),
+                 argmax=torch.empty(n, dtype=torch.int32, device=dev),
+                 tokens=torch.empty(n, dtype=torch.int32, device=dev),
+                 commit_loop=torch.empty(n, dtype=torch.int8, device=dev),
+                 embed=torch.empty((n, self.w.dims.d_model), dtype=torch.float32, device=dev))
+        B.readout_commit(self.ctx, rows.data_ptr(), n, group, tau_ent, tau_halt, _ptr(boost_tok), _ptr(boost_val),
+                         o["entropy"].data_ptr(), o["lse"].data_ptr(), o["lam"].data_ptr(), o["halt"].data_ptr(),
+                         o["argmax"].data_ptr(), o["tokens"].data_ptr(), o["commit_loop"].data_ptr(),
+                         o["embed"].data_ptr())
+        return o
+
+    def close(self):
+        if getattr(self, "ctx", 0):
+            B.destroy(self.ctx)
+            self.ctx = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -375,6 +375,7 @@ def readout_rows(n: int, d: int = 4096) -> np.ndarray:
 
 def readout_workload(n_rows: int) -> Workload:
     """The readout microbench as a Workload (8B readout shape, one loop, groups of 32 rows)."""
-    return Workload("readout_%d" % n_rows, QWEN3_8B_DIMS, "bf16", batch=max(1, n_rows // READOUT_GROUP),
+    dims = replace(QWEN3_8B_DIMS, n_pre=0, n_core=1, n_coda=0)   # the heads only need one (unused) layer
+    return Workload("readout_%d" % n_rows, dims, "bf16", batch=max(1, n_rows // READOUT_GROUP),
                     prefix=0, block=min(n_rows, READOUT_GROUP), k_max=1, tau_ent=READOUT_TAU_ENT,
                     tau_halt=READOUT_TAU_HALT, seed=READOUT_SEED)

@@ -1,0 +1,205 @@
+/*
+ * alodlm.h -- C ABI of the ALoDLM adaptively looped denoising step on MI355X (gfx950).
+ *
+ * The operation is one denoising step of an adaptively looped diffusion LM,
+ * as described on the page "ALoDLM: Adaptively Looped Diffusion Language
+ * Models" (summary of arXiv 2610.04198), sections "Core method" and
+ * "Method step details" (Algorithm 1, Eq. 3):
+ *
+ *   h0 = Prelude(x_t) over the block rows; U = masked positions; a = 0; C = {}
+ *   for s = 1..K:
+ *     h~ = Core(h)                       (shared weights; prefix K/V at depth min(s, d_j))
+ *     r  = RMSNorm_final(Coda(h~))
+ *     for i in U: H_i = entropy(softmax(W_lm r_i)), tok_i = argmax, lambda_i = sigmoid(w_g.r_i + b_g),
+ *                 a_i = a_i + (1 - a_i) lambda_i
+ *     commit B = {i in U : H_i <= tau_ent}; U -= B; C += B
+ *     Eq. 3: h_i = Emb(tok_i) for every i not in U, h_i = h~_i otherwise
+ *     stop if U is empty, or mean_{i in U} a_i >= tau_halt, or s = K
+ *   if C is empty: commit the unresolved position of lowest entropy (forced progress)
+ *
+ * The prefix is held in a depth-aware KV cache (same page, sections
+ * "Background" and "Limitations"): Prelude and Coda layers keep one K/V set,
+ * every Core layer keeps one set per loop depth 1..k_max, i.e.
+ * n_pre + n_core * k_max + n_coda slots (84 for the 8B split at K = 4).
+ *
+ * Conventions for every entry point:
+ *   - "device" pointers are HIP device memory on the context's device,
+ *     "host" pointers are ordinary host memory.  Row-major layouts.
+ *   - Nothing is allocated on the device.  Weights and the workspace are
+ *     BORROWED: the caller keeps them alive and unmodified until
+ *     alodlm_destroy().  The context owns only host-side metadata.
+ *   - Return 0 (ALODLM_OK) on success or a negative ALODLM_E* code; on
+ *     error alodlm_last_error() describes it.  Arguments are validated before
+ *     any device work is enqueued, so an EINVAL call has no device effect.
+ *   - All device work runs on the stream given to alodlm_create().  A context
+ *     is not thread-safe; use one context per stream.
+ */
+#ifndef ALODLM_H
+#define ALODLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef ALODLM_API
+#define ALODLM_API __attribute__((visibility("default")))
+#endif
+
+#define ALODLM_OK 0
+#define ALODLM_EINVAL (-1)  /* bad argument (null pointer, size out of range, non-finite threshold) */
+#define ALODLM_ESTATE (-2)  /* call out of order, e.g. a step before the prefix cache was built */
+#define ALODLM_ENOMEM (-3)  /* workspace smaller than alodlm_workspace_bytes() */
+#define ALODLM_EHIP (-4)    /* a HIP runtime call failed; the message names it */
+
+#define ALODLM_DTYPE_BF16 0 /* bf16 weights, KV and GEMM inputs; fp32 accumulate, residual and heads */
+#define ALODLM_DTYPE_FP32 1 /* fp32 everywhere */
+
+/* Model and capacity description. */
+typedef struct alodlm_config {
+  int32_t vocab;        /* V */
+  int32_t d_model;      /* d, multiple of 64 */
+  int32_t n_q_heads;    /* Hq, multiple of n_kv_heads */
+  int32_t n_kv_heads;   /* Hkv */
+  int32_t head_dim;     /* hd: 32, 64 or 128 */
+  int32_t ffn;          /* F, multiple of 64 */
+  int32_t n_pre;        /* Prelude layers (0 allowed) */
+  int32_t n_core;       /* Recurrent Core layers (>= 1), run once per loop with the same weights */
+  int32_t n_coda;       /* Coda layers (0 allowed) */
+  int32_t k_max;        /* loop cap K and number of Core depth planes in the cache, 1..16 */
+  int32_t max_batch;    /* sequences per step */
+  int32_t max_prefix;   /* prefix positions held per sequence */
+  int32_t max_block;    /* block (window) length L, 1..64 */
+  int32_t max_prefill_rows; /* rows one prefill pass may hold (>= max_prefix); 0 = max_batch * max_prefix */
+  int32_t mask_id;      /* token id of [MASK], 0..V-1 */
+  int32_t dtype;        /* ALODLM_DTYPE_* */
+  float rms_eps;        /* RMSNorm epsilon */
+  float rope_theta;     /* RoPE base */
+} alodlm_config;
+
+/* One transformer layer (Qwen3 block).  Device pointers in the config dtype,
+ * linear maps stored [out][in]. */
+typedef struct alodlm_layer_weights {
+  const void* attn_norm;  /* [d] RMSNorm gain before attention */
+  const void* wqkv;       /* [(Hq + 2 Hkv) hd][d]: q rows, then k rows, then v rows */
+  const void* q_norm;     /* [hd] per-head RMSNorm gain of q */
+  const void* k_norm;     /* [hd] per-head RMSNorm gain of k */
+  const void* wo;         /* [d][Hq hd] */
+  const void* ffn_norm;   /* [d] RMSNorm gain before the FFN */
+  const void* w_gate_up;  /* [2F][d]: gate rows 0..F-1, then up rows; FFN = down(silu(gate) * up) */
+  const void* w_down;     /* [d][F] */
+} alodlm_layer_weights;
+
+typedef struct alodlm_weights {
+  const void* embed;       /* [V][d] token embedding (also the Eq. 3 feedback rows) */
+  const void* lm_head;     /* [V][d] LMHead, logits z = lm_head . r */
+  const void* final_norm;  /* [d] RMSNorm gain producing the readout state r */
+  const void* exit_w;      /* [d] ExitGate weight: lambda = sigmoid(exit_w . r + exit_b) */
+  float exit_b;            /* ExitGate bias */
+  const alodlm_layer_weights* layers; /* host array of n_pre + n_core + n_coda entries, in order */
+} alodlm_weights;
+
+typedef struct alodlm_ctx alodlm_ctx;
+
+/* Bytes of device workspace alodlm_create() needs for this config (KV cache, RoPE
+ * tables and step scratch).  Host only; no device work. */
+ALODLM_API int alodlm_workspace_bytes(const alodlm_config* cfg, size_t* bytes);
+
+/* Number of prefix-cache slots: n_pre + n_core * k_max + n_coda. */
+ALODLM_API int alodlm_kv_slots(const alodlm_config* cfg, int32_t* slots);
+
+/* Creates a context.  cfg and w are copied (the layer array too); the device
+ * buffers they point to are borrowed.  workspace: device buffer of ws_bytes >=
+ * alodlm_workspace_bytes(), 256-byte aligned, owned by the caller.  hip_stream:
+ * a hipStream_t (NULL = default stream).  Enqueues the RoPE table upload. */
+ALODLM_API int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* workspace, size_t ws_bytes,
+                  void* hip_stream, alodlm_ctx** out);
+
+/* Builds the depth-aware prefix cache from token ids (summary page, section
+ * "Limitations": the prefill fills every loop depth).  The prefix runs causally
+ * through the Prelude once, through the Core k_max times (depth d = the d-th
+ * pass) and through the Coda once on the depth-k_max output.
+ *   prefix_ids:  device int32 [batch][prefix_len], ids in [0, V)
+ *   avail_depth: device uint8 [batch][prefix_len], deepest Core depth cached for
+ *                each position (1..k_max), used as min(loop, avail) when reading;
+ *                NULL = k_max everywhere.  Copied into the workspace.
+ * batch <= max_batch, 0 <= prefix_len <= max_prefix.  Asynchronous. */
+ALODLM_API int alodlm_prefill_kv(alodlm_ctx* ctx, int32_t batch, int32_t prefix_len, const int32_t* prefix_ids,
+                      const uint8_t* avail_depth);
+
+/* Fills the prefix cache with seeded synthetic K/V instead of computing it (for
+ * long-context measurements).  Element (slot, b, h, j, e) of K is draw
+ * ((b*Hkv + h)*prefix_len + j)*hd + e of Philox4x32-10 stream (seed, 0x10000 + 2*slot)
+ * mapped to the Irwin-Hall(4) value times k_scale (V: stream + 1, v_scale), as
+ * defined in alodlm_synth.h.  avail_depth as in alodlm_prefill_kv.  Asynchronous. */
+ALODLM_API int alodlm_prefill_kv_synthetic(alodlm_ctx* ctx, int32_t batch, int32_t prefix_len, uint32_t seed,
+                                float k_scale, float v_scale, const uint8_t* avail_depth);
+
+#define ALODLM_STEP_TEACHER_FORCED 1u /* take commits, tokens and stop loops from tf_* */
+
+typedef struct alodlm_step_args {
+  int32_t batch;              /* sequences, == the prefilled batch */
+  int32_t block_len;          /* L, <= max_block */
+  const int32_t* block_ids;   /* device [batch][L]: token ids, mask_id = masked (unresolved) */
+  float tau_ent;              /* commit iff entropy (nats) <= tau_ent; finite */
+  float tau_halt;             /* stop when mean cumulative halt of unresolved rows >= tau_halt; finite */
+  int32_t k_loops;            /* loop cap for this step, 1..k_max */
+  uint32_t flags;             /* ALODLM_STEP_* */
+  const int32_t* boost_tok;   /* optional device [batch][L]: planted logit boost token (-1 none) */
+  const float* boost_val;     /* device [batch][L], required with boost_tok: added to that logit */
+  const int8_t* tf_commit_loop; /* teacher-forced only: device [batch][L], loop s (or -s forced) or 0 */
+  const int32_t* tf_tokens;   /* teacher-forced only: device [batch][L], committed token ids */
+  const int8_t* tf_stop_loop; /* teacher-forced only: device [batch], loop at which the sequence stops */
+} alodlm_step_args;
+
+typedef struct alodlm_step_out {
+  int32_t* tokens;       /* device [batch][L]: committed token, block id for rows not masked, else mask_id */
+  int8_t* commit_loop;   /* device [batch][L]: s if committed at loop s, -s if forced at the last loop s, 0 */
+  int8_t* loops;         /* device [batch]: loops run by each sequence */
+  /* optional per-loop records, device [k_loops][batch][L] float (NaN where not read out): */
+  float* entropy;        /* H of rows unresolved at loop start */
+  float* lam;            /* ExitGate lambda */
+  float* halt;           /* cumulative halt a after the update */
+  float* lse;            /* log-sum-exp of the logits */
+  int32_t* argmax;       /* argmax token (-1 where not read out) */
+  float* hidden;         /* optional device [k_loops][batch][L][d]: Core output h~ per loop (fp32) */
+  int32_t n_committed;   /* host: tokens committed by the step, filled on return */
+  int32_t loops_run;     /* host: largest loop count over the batch, filled on return */
+} alodlm_step_out;
+
+/* Runs one denoising step over the prefilled batch.  Enqueues all work on the
+ * context stream and synchronises that stream once per loop to read the number
+ * of sequences still looping (a few bytes), so it returns after the step has
+ * finished.  Idempotent: it never writes the prefix cache. */
+ALODLM_API int alodlm_denoise_step(alodlm_ctx* ctx, const alodlm_step_args* args, alodlm_step_out* out);
+
+/* The readout half of a loop on given readout states: LMHead entropy/argmax,
+ * ExitGate and cumulative halt (a = lambda at loop 1), entropy commit, forced
+ * progress and the Eq. 3 embedding rows, for n_rows rows grouped into sequences of
+ * group rows (all unresolved, loop cap 1).
+ *   rows: device [n_rows][d] readout states r (config dtype); n_rows <= max_batch * max_block,
+ *         group in 1..64 dividing n_rows
+ *   boost_tok/boost_val: optional device [n_rows]
+ * outputs (device): entropy, lse, lam, halt [n_rows] float; argmax, tokens [n_rows] int32;
+ *   commit_loop [n_rows] int8; embed_out [n_rows][d] float (Emb(tok) for committed rows, 0 else).
+ * Asynchronous. */
+ALODLM_API int alodlm_readout_commit(alodlm_ctx* ctx, const void* rows, int32_t n_rows, int32_t group, float tau_ent,
+                          float tau_halt, const int32_t* boost_tok, const float* boost_val, float* entropy,
+                          float* lse, float* lam, float* halt, int32_t* argmax, int32_t* tokens,
+                          int8_t* commit_loop, float* embed_out);
+
+/* Counters of the last step: layer calls launched and loops run (host). */
+ALODLM_API int alodlm_last_step_stats(const alodlm_ctx* ctx, int64_t* layer_calls, int32_t* loops_run);
+
+/* Last error message of the context (or of the last failed create when ctx is NULL). */
+ALODLM_API const char* alodlm_last_error(const alodlm_ctx* ctx);
+
+/* Releases the host-side context.  Frees nothing it did not allocate. */
+ALODLM_API void alodlm_destroy(alodlm_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ALODLM_H */

@@ -12,8 +12,8 @@ Sources (page titles and sections):
     Recurrent Core / Coda split, the two heads, lambda = sigmoid(ExitGate(r)),
     commit iff entropy <= tau, halt when the mean cumulative halt of the
     unresolved positions reaches q, forced exit at s = K, Eq. 3), section
-    "Method step details" (Algorithm 1 steps 1-5, the cumulative halting
-    update a <- a + (1 - a) lambda, the forced lowest-entropy commit), section
+    "Method step details" (Algorithm 1: outer and inner loop, the cumulative
+    halting update a <- a + (1 - a) lambda, the forced lowest-entropy commit), section
     "Background" (looped Transformer with shared weights; depth-aware KV
     cache: matching depth first, deepest available as fallback), section
     "Limitations" (the cache holds L + (K-1) m buffers, 84 for 8B at K = 4),
@@ -251,7 +251,7 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
                           theta: float, tau_ent: float, tau_halt: float, mask_id: int, exit_b: float,
                           boost_tok=None, boost_val=None, teacher: Optional[dict] = None,
                           record_hidden: bool = False, counter: Optional[list] = None) -> dict:
-    """Algorithm 1 of the summary page, steps 1-5, for one sequence.
+    """One inner loop of Algorithm 1 of the summary page (one denoising step), for one sequence.
 
     ``cache``: slot -> (K, V) [Hkv][P][hd]; ``avail``: deepest cached Core depth
     per prefix position (None = k_max).  ``teacher`` (optional) replaces the
@@ -273,7 +273,7 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
         y, _, _ = layer_forward(x, W, li, dims, eps, theta, pos, ck, cv, causal=False)
         return y
 
-    # step (1): unresolved set, initial loop state, a = 0, C empty
+    # start of the step: unresolved set, initial loop state, a = 0, C empty
     U = block_ids == mask_id
     C = np.zeros(L, dtype=bool)
     tokens = block_ids.copy()
@@ -288,7 +288,7 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
     last = None
     for s in range(1, k_loops + 1):
         s_end = s
-        # step (2): Core update, Coda readout
+        # Core update, Coda readout
         y = h
         for c in range(dims.n_core):
             y = run_layer(y, dims.n_pre + c, s)
@@ -308,9 +308,9 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
             bv = None if boost_val is None else np.asarray(boost_val)[rows]
             H[rows], tok[rows], lse[rows], gap[rows] = readout(r[rows], W["lm_head"], bt, bv)
             lam[rows] = exit_gate(r[rows], W["exit_w"], exit_b)
-        # step (4), first half: cumulative halting for the positions unresolved at loop start
+        # cumulative halting for the positions unresolved at loop start
         a[rows] = a[rows] + (1.0 - a[rows]) * lam[rows]
-        # step (3): commit
+        # entropy commit
         if teacher is None:
             newly = rows[H[rows] <= tau_ent]
         else:
@@ -326,7 +326,7 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
         fixed = np.nonzero(~U)[0]
         if fixed.size:
             h[fixed] = _f64(W["embed"][tokens[fixed]])
-        # step (4), second half: stop test on the remaining unresolved positions
+        # stop test on the positions still unresolved
         n_u = int(U.sum())
         mean_a = float(a[U].mean()) if n_u else float("nan")
         if teacher is None:
@@ -344,7 +344,7 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
         if stop:
             break
 
-    # step (5): forced progress
+    # forced progress when the step committed nothing
     forced = -1
     forced_gap = float("nan")
     if not C.any() and U.any() and last is not None:

@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point, and
+rejects bad arguments before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from adaptive_looped_denoising_amd import binding as B
+from adaptive_looped_denoising_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in ("alodlm.h", "alodlm_synth.h"):
+        txt = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"\b(alodlm_[a-z_0-9]+)\s*\(", txt))
+    return names
+
+
+def _cfg(w=None, **over):
+    w = w or synth.workload("qwen3_8b")
+    D = w.dims
+    c = B.Config(vocab=D.vocab, d_model=D.d_model, n_q_heads=D.n_q_heads, n_kv_heads=D.n_kv_heads,
+                 head_dim=D.head_dim, ffn=D.ffn, n_pre=D.n_pre, n_core=D.n_core, n_coda=D.n_coda, k_max=w.k_max,
+                 max_batch=w.batch, max_prefix=w.prefix, max_block=w.block, max_prefill_rows=0, mask_id=w.mask_id,
+                 dtype=B.DTYPE_BF16 if w.dtype == "bf16" else B.DTYPE_FP32, rms_eps=w.rms_eps,
+                 rope_theta=w.rope_theta)
+    for k, v in over.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = B.load()
+    declared = _declared()
+    assert {"alodlm_create", "alodlm_prefill_kv", "alodlm_denoise_step", "alodlm_destroy"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(B.EXPORTS) == declared
+
+
+def test_kv_slot_counts():
+    assert B.kv_slots(_cfg()) == 84                    # 8B split at K = 4
+    assert B.kv_slots(_cfg(synth.workload("qwen3_8b_long"))) == 116
+    assert B.kv_slots(_cfg(synth.workload("tiny"))) == 1 + 2 * 4 + 1
+
+
+def test_workspace_size_covers_the_cache():
+    c = _cfg()
+    n = B.workspace_bytes(c)
+    kv = 2 * 84 * 8 * 8 * 1024 * 128 * 2
+    assert kv < n < kv + 3 * 2 ** 30
+    c4 = _cfg(synth.workload("qwen3_8b_long"), max_prefill_rows=8192)
+    assert B.workspace_bytes(c4) > 2 * 116 * 32 * 8 * 8192 * 128 * 2
+
+
+@pytest.mark.parametrize("field,value", [
+    ("dtype", 7), ("vocab", 1), ("d_model", 100), ("ffn", 0), ("head_dim", 48), ("n_q_heads", 3),
+    ("n_kv_heads", 0), ("n_core", 0), ("n_pre", -1), ("k_max", 0), ("k_max", 17), ("max_batch", 0),
+    ("max_batch", 2000), ("max_block", 65), ("max_block", 0), ("max_prefix", -2), ("max_prefill_rows", 5),
+    ("mask_id", 151936), ("rms_eps", float("nan")), ("rope_theta", 0.0)])
+def test_bad_configs_are_rejected(field, value):
+    with pytest.raises(B.AlodlmError) as e:
+        B.workspace_bytes(_cfg(**{field: value}))
+    assert e.value.code == B.EINVAL
+    assert "invalid config" in str(e.value)
+
+
+def _weights(nl, ptr=0x1000):
+    layers = (B.LayerWeights * nl)()
+    for l in range(nl):
+        for f, _ in B.LayerWeights._fields_:
+            setattr(layers[l], f, ptr)
+    return B.Weights(embed=ptr, lm_head=ptr, final_norm=ptr, exit_w=ptr, exit_b=0.1, layers=layers), layers
+
+
+def test_create_validates_before_device_work():
+    lib = B.load()
+    c = _cfg(synth.workload("tiny"))
+    w, keep = _weights(4)
+    need = B.workspace_bytes(c)
+    out = ctypes.c_void_p(0)
+    # workspace too small
+    rc = lib.alodlm_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(0x10000), need - 1, None,
+                           ctypes.byref(out))
+    assert rc == B.ENOMEM and out.value is None
+    assert b"need" in lib.alodlm_last_error(None)
+    # misaligned workspace
+    rc = lib.alodlm_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(0x10010), need, None, ctypes.byref(out))
+    assert rc == B.EINVAL
+    # a null layer tensor
+    keep[2].wo = None
+    rc = lib.alodlm_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(0x10000), need, None, ctypes.byref(out))
+    assert rc == B.EINVAL and b"layer 2" in lib.alodlm_last_error(None)
+    # non-finite exit bias
+    keep[2].wo = 0x1000
+    w.exit_b = float("inf")
+    rc = lib.alodlm_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(0x10000), need, None, ctypes.byref(out))
+    assert rc == B.EINVAL
+
+
+def test_null_context_calls_fail_cleanly():
+    lib = B.load()
+    assert lib.alodlm_prefill_kv(None, 1, 1, None, None) == B.EINVAL
+    assert lib.alodlm_denoise_step(None, None, None) == B.EINVAL
+    assert lib.alodlm_readout_commit(None, None, 32, 32, 0.5, 0.5, *([None] * 10)) == B.EINVAL
+    assert lib.alodlm_last_step_stats(None, None, None) == B.EINVAL
+    lib.alodlm_destroy(None)
+    assert lib.alodlm_synth_fill(None, 0, 0, 10, 0, 0, 1.0, 0.0, None) == -1

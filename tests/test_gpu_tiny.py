@@ -1,0 +1,139 @@
+"""GPU parity of the whole step on the tiny workload (vocab 512, d 128, 1/2/1 layers) and its
+variants: fp32 and bf16, free-running and teacher-forced, against the fp64 oracle."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from adaptive_looped_denoising_amd import synth
+from oracle import run as orun
+from tests.parity import TOL, compare_decisions, compare_records, log, rel_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _engine(w, **kw):
+    from adaptive_looped_denoising_amd.engine import Engine
+    e = Engine(w, **kw)
+    e.prefill()
+    return e
+
+
+def _check_step(w, gpu_lib, k_loops=None, block_ids=None, overrides=None, oracle_W=None):
+    log("case %s dtype=%s B=%d P=%d L=%d K=%d tau=%.3g q=%.3g" % (w.name, w.dtype, w.batch, w.prefix, w.block,
+                                                                  w.k_max, w.tau_ent, w.tau_halt))
+    e = _engine(w, overrides=overrides)
+    K = w.k_max if k_loops is None else k_loops
+    W = orun.weights(w) if oracle_W is None else oracle_W
+    ores = orun.step(w, W=W, k_loops=K, record_hidden=True, block_ids=block_ids)
+    free = e.step(k_loops=K, records=True, hidden=True, block_ids=block_ids)
+    flagged = compare_decisions(w, ores, free)
+    clean = [r for r in ores if r["seq"] not in flagged]
+    if clean:
+        worst = compare_records(w, clean, free)
+        log("free run worst errors: %s" % worst)
+    tf = e.step(k_loops=K, records=True, hidden=True, teacher=orun.teacher_from(ores), block_ids=block_ids)
+    worst = compare_records(w, ores, tf)
+    log("teacher-forced worst errors: %s" % worst)
+    for r in ores:
+        b = r["seq"]
+        assert np.array_equal(tf.commit_loop[b], r["commit_loop"]) and np.array_equal(tf.tokens[b], r["tokens"])
+        assert tf.loops[b] == r["loops"]
+    n_commit = sum(int((r["commit_loop"] != 0).sum()) for r in ores)
+    assert tf.n_committed == n_commit
+    return e, ores, free
+
+
+def test_device_generator_matches_host(gpu_lib):
+    from adaptive_looped_denoising_amd import binding as B
+    st = torch.cuda.current_stream().cuda_stream
+    for dtype, tdt, code in (("bf16", torch.bfloat16, B.DTYPE_BF16), ("fp32", torch.float32, B.DTYPE_FP32)):
+        for start, n, tensor, scale in ((0, 4097, 5, 0.013), (123456789, 3001, 77, 1.0), (2 ** 33 + 5, 1000, 3, 2.5e-5)):
+            t = torch.empty(n, dtype=tdt, device="cuda")
+            B.synth_fill(t.data_ptr(), code, start, n, 9, tensor, scale, 0.0, st)
+            host = synth.ih4((n,), 9, tensor, scale, dtype, start=start)
+            dev = t.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else t.cpu().numpy()
+            assert np.array_equal(dev, host), (dtype, start)
+
+
+def test_tiny_fp32_step(gpu_lib):
+    w = synth.workload("tiny")
+    e, ores, free = _check_step(w, gpu_lib)
+    calls, loops = e.stats()
+    assert calls == w.dims.n_pre + loops * (w.dims.n_core + w.dims.n_coda)
+
+
+def test_tiny_fp32_commits_by_entropy(gpu_lib):
+    # larger planted boosts so that easy rows commit over several loops
+    w = synth.workload("tiny", boost_lo=8.0, boost_hi=14.0)
+    _, ores, _ = _check_step(w, gpu_lib)
+    assert sum(int((r["commit_loop"] > 0).sum()) for r in ores) > 0
+
+
+def test_tiny_fp32_batch_and_decoded_rows(gpu_lib):
+    w = synth.workload("tiny", batch=3, boost_lo=8.0, boost_hi=14.0, tau_halt=0.7)
+    bids = synth.block_ids(w)
+    bids[1, [0, 5, 9]] = [3, 100, 200]      # rows already decoded before the step
+    bids[2, :] = 7                          # nothing masked in this sequence
+    bids[2, 15] = w.mask_id
+    _check_step(w, gpu_lib, block_ids=bids)
+
+
+def test_tiny_fp32_uniform_depth_and_closed_form_halting(gpu_lib):
+    # nothing commits by entropy and halting is off: every sequence runs k_max loops
+    w = synth.workload("tiny", batch=2, tau_ent=0.0, tau_halt=1.5)
+    _check_step(w, gpu_lib)
+    # ExitGate weight 0: a = 1 - (1 - lambda)^s, stop at s* = 2 for lambda 0.42, q 0.5
+    w2 = synth.workload("tiny", tau_ent=-1.0, tau_halt=0.5)
+    lam = 0.42
+    ov = {"exit_w": np.zeros(w2.dims.d_model, dtype=np.float32)}
+    from adaptive_looped_denoising_amd.engine import Engine
+    e = Engine(w2, overrides=ov, exit_b=float(np.log(lam / (1 - lam))))
+    e.prefill()
+    r = e.step(records=True)
+    assert r.loops[0] == 2
+    np.testing.assert_allclose(r.halt[1, 0], 1 - (1 - lam) ** 2, rtol=1e-5)
+
+
+def test_tiny_fp32_uniform_readout(gpu_lib):
+    w = synth.workload("tiny")
+    from adaptive_looped_denoising_amd.engine import Engine
+    e = Engine(w, overrides={"lm_head": np.zeros((w.dims.vocab, w.dims.d_model), dtype=np.float32)})
+    e.prefill()
+    r = e.step(records=True, boost=False)
+    H = r.entropy[: r.loops_run, 0]
+    np.testing.assert_allclose(H[np.isfinite(H)], np.log(512.0), rtol=1e-6)
+    assert r.commit_loop[0, 0] == -r.loops[0] and r.tokens[0, 0] == 0
+
+
+def test_tiny_bf16_step(gpu_lib):
+    w = replace(synth.workload("tiny", boost_lo=8.0, boost_hi=14.0, batch=2), dtype="bf16", name="tiny_bf16")
+    _check_step(w, gpu_lib)
+
+
+def test_tiny_deterministic(gpu_lib):
+    w = synth.workload("tiny", boost_lo=8.0, boost_hi=14.0)
+    e = _engine(w)
+    a = e.step(records=True, hidden=True)
+    b = e.step(records=True, hidden=True)
+    for k in ("tokens", "commit_loop", "loops", "entropy", "lam", "halt", "lse", "argmax"):
+        assert np.array_equal(getattr(a, k), getattr(b, k), equal_nan=True) if getattr(a, k).dtype.kind == "f" \
+            else np.array_equal(getattr(a, k), getattr(b, k)), k
+    assert np.array_equal(a.hidden, b.hidden, equal_nan=True)
+
+
+def test_tiny_step_errors(gpu_lib):
+    from adaptive_looped_denoising_amd import binding as B
+    from adaptive_looped_denoising_amd.engine import Engine
+    w = synth.workload("tiny")
+    e = Engine(w)
+    with pytest.raises(B.AlodlmError) as ex:   # step before the prefix cache exists
+        e.step()
+    assert ex.value.code == B.ESTATE
+    e.prefill()
+    for kw in (dict(tau_ent=float("nan")), dict(tau_halt=float("inf")), dict(k_loops=0), dict(k_loops=5)):
+        with pytest.raises(B.AlodlmError) as ex:
+            e.step(**kw)
+        assert ex.value.code == B.EINVAL
+    e.step()
