@@ -18,7 +18,9 @@ STEP_TEACHER_FORCED = 1
 
 EXPORTS = ("alodlm_workspace_bytes", "alodlm_kv_slots", "alodlm_create", "alodlm_prefill_kv",
            "alodlm_prefill_kv_synthetic", "alodlm_denoise_step", "alodlm_readout_commit",
-           "alodlm_last_step_stats", "alodlm_last_error", "alodlm_destroy", "alodlm_synth_fill")
+           "alodlm_last_step_stats", "alodlm_last_error", "alodlm_destroy", "alodlm_synth_fill",
+           "alodlm_diag_gemm", "alodlm_diag_timing_enable", "alodlm_diag_timing_read")
+K_CLASSES = ("gemm_gate_up", "gemm_qkv", "gemm_o", "gemm_down", "attention", "lm_head", "norm_rope", "control")
 
 
 class Config(ctypes.Structure):
@@ -85,6 +87,10 @@ def load(path: str = LIB_PATH):
     lib.alodlm_destroy.restype = None
     lib.alodlm_synth_fill.argtypes = [c_void_p, c_int32, c_uint64, c_uint64, c_uint32, c_uint32, c_float, c_float,
                                       c_void_p]
+    lib.alodlm_diag_gemm.argtypes = [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_int32, c_int32, c_void_p]
+    lib.alodlm_diag_timing_enable.argtypes = [c_void_p, c_int32]
+    lib.alodlm_diag_timing_read.argtypes = [c_void_p, c_int32, POINTER(ctypes.c_double), POINTER(c_int64)]
     for name in EXPORTS:
         if name not in ("alodlm_last_error", "alodlm_destroy"):
             getattr(lib, name).restype = c_int32
@@ -159,3 +165,25 @@ def synth_fill(dst_ptr: int, dtype: int, start: int, n: int, seed: int, tensor: 
                                   c_void_p(stream_ptr))
     if rc != 0:
         raise AlodlmError(rc, "alodlm_synth_fill failed")
+
+
+def diag_gemm(epi: int, M: int, N: int, K: int, A_ptr: int, B_ptr: int, C_ptr: int, act_ptr: int, scratch_ptr: int,
+              scratch_floats: int, force_splits: int, force_generic: int, stream_ptr: int):
+    rc = load().alodlm_diag_gemm(epi, M, N, K, c_void_p(A_ptr), c_void_p(B_ptr), c_void_p(C_ptr or None),
+                                 c_void_p(act_ptr or None), c_void_p(scratch_ptr or None), scratch_floats,
+                                 force_splits, force_generic, c_void_p(stream_ptr))
+    if rc != 0:
+        raise AlodlmError(rc, "alodlm_diag_gemm failed")
+
+
+def timing_enable(ctx: int, on: bool):
+    _check(load().alodlm_diag_timing_enable(c_void_p(ctx), 1 if on else 0), c_void_p(ctx))
+
+
+def timing_read(ctx: int) -> dict:
+    out = {}
+    for k, name in enumerate(K_CLASSES):
+        ms, n = ctypes.c_double(0), c_int64(0)
+        _check(load().alodlm_diag_timing_read(c_void_p(ctx), k, ctypes.byref(ms), ctypes.byref(n)), c_void_p(ctx))
+        out[name] = (ms.value, n.value)
+    return out

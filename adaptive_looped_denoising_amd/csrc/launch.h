@@ -86,6 +86,12 @@ void launch_gather_boosts(const int32_t* ro_rows, const int32_t* n_dev, const in
 void launch_embed_committed(int dtype, const int8_t* cl, const int32_t* tokens, const void* E, int n, int d, int V,
                             float* out, hipStream_t st);
 
+bool gemm_mfma_supported(int K, int lda, int ldb);
+// LM-head column tile of the matrix-core path (softmax statistics are kept per tile).
+constexpr int MFMA_TILE_N = 128;
+void launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                      const int32_t* m_dev, const GemmEpi& ep, int F, float* part, size_t part_floats,
+                      int force_splits, hipStream_t st);
 void launch_gemm_generic(int dtype, int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                          const int32_t* m_dev, const GemmEpi& ep, hipStream_t st);
 void launch_attn_generic(int dtype, const AttnParams& p, hipStream_t st);

@@ -2,6 +2,7 @@
 // depth-aware prefix-cache build, and the step driver (Prelude once, then per loop the
 // shared Core, the Coda, the two heads, the commit rule, compaction and the Eq. 3 reset).
 #include <math.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -9,6 +10,7 @@
 #include <vector>
 
 #include "../../include/alodlm.h"
+#include "../../include/alodlm_diag.h"
 #include "launch.h"
 #include "common.h"
 
@@ -119,7 +121,7 @@ Plan make_plan(const alodlm_config& c) {
   p.src_slot = take(sizeof(int32_t) * B);
   p.cnt = take(sizeof(int32_t) * 8);
   p.attn_part = take(sizeof(float) * Rs * Hq * (size_t)p.attn_splits * (hd + 2));
-  p.gemm_part_elems = (size_t)Rs * (size_t)(2 * F > qkv_out ? 2 * F : qkv_out) * 4;
+  p.gemm_part_elems = (size_t)Rs * (size_t)(2 * F > qkv_out ? 2 * F : qkv_out) * 8;
   p.gemm_part = take(sizeof(float) * p.gemm_part_elems);
   p.total = off;
   return p;
@@ -141,6 +143,47 @@ struct alodlm_ctx {
   // stats of the last step
   int64_t layer_calls = 0;
   int32_t loops_run = 0;
+  bool force_generic = false;  // diagnostics: ALODLM_FORCE_GENERIC=1 keeps bf16 on the vector-ALU kernels
+  // diagnostics: per-class kernel timing with event pairs on the context stream
+  bool timing = false;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<int> ev_class;  // class of each recorded pair
+  size_t ev_used = 0;
+  double t_ms[ALODLM_K_CLASSES] = {0};
+  int64_t t_n[ALODLM_K_CLASSES] = {0};
+
+  bool in_step = false;  // timing covers denoising steps only
+  void tic(int cls) {
+    if (!timing || !in_step) return;
+    const size_t i = ev_used * 2;
+    while (ev_pool.size() < i + 2) {
+      hipEvent_t e;
+      hipEventCreate(&e);
+      ev_pool.push_back(e);
+    }
+    ev_class.resize(ev_used + 1);
+    ev_class[ev_used] = cls;
+    hipEventRecord(ev_pool[i], st);
+  }
+  void toc() {
+    if (!timing || !in_step) return;
+    hipEventRecord(ev_pool[ev_used * 2 + 1], st);
+    ++ev_used;
+  }
+  // After a stream synchronisation: fold the recorded pairs into the totals.
+  void fold() {
+    for (size_t k = 0; k < ev_used; ++k) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, ev_pool[2 * k], ev_pool[2 * k + 1]) == hipSuccess) {
+        t_ms[ev_class[k]] += ms;
+        t_n[ev_class[k]] += 1;
+      }
+    }
+    ev_used = 0;
+  }
+  ~alodlm_ctx() {
+    for (hipEvent_t e : ev_pool) hipEventDestroy(e);
+  }
 
   template <typename T>
   T* at(size_t off) const {
@@ -172,10 +215,33 @@ int slot_of(const alodlm_config& c, int layer, int depth) {
   return c.n_pre + c.n_core * c.k_max + (layer - c.n_pre - c.n_core);
 }
 
-// GEMM dispatch: C = A . B^T with the given epilogue.
+bool use_mfma(const alodlm_ctx* c, int K, int lda, int ldb) {
+  return c->cfg.dtype == ALODLM_DTYPE_BF16 && !c->force_generic && gemm_mfma_supported(K, lda, ldb);
+}
+
+// GEMM dispatch: C = A . B^T with the given epilogue (SWIGLU: N = 2F interleaved gate/up).
 void gemm(alodlm_ctx* c, int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
-          const int32_t* m_dev, const GemmEpi& ep) {
+          const int32_t* m_dev, const GemmEpi& ep, int F = 0) {
+  if (use_mfma(c, K, lda, ldb)) {
+    launch_gemm_mfma(epi, A, lda, B, ldb, M, N, K, m_dev, ep, F, c->at<float>(c->plan.gemm_part),
+                     c->plan.gemm_part_elems, 0, c->st);
+    return;
+  }
+  if (epi == EPI_SWIGLU) {  // generic path: both halves in fp32, then silu(gate) * up
+    GemmEpi e;
+    e.C = c->at<float>(c->plan.gu);
+    e.ldc = N;
+    launch_gemm_generic(dt(c), EPI_STORE, A, lda, B, ldb, M, N, K, m_dev, e, c->st);
+    launch_swiglu(dt(c), e.C, M, F, ep.act, c->st);
+    return;
+  }
   launch_gemm_generic(dt(c), epi, A, lda, B, ldb, M, N, K, m_dev, ep, c->st);
+}
+
+// Column tiles of the LM-head softmax statistics for the path the readout takes.
+int lm_tiles(const alodlm_ctx* c) {
+  const int d = c->cfg.d_model;
+  return use_mfma(c, d, d, d) ? (c->cfg.vocab + MFMA_TILE_N - 1) / MFMA_TILE_N : (c->cfg.vocab + 63) / 64;
 }
 
 void attention(alodlm_ctx* c, const AttnParams& p) { launch_attn_generic(dt(c), p, c->st); }
@@ -211,14 +277,17 @@ void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   void* attn = c->at<void>(p.attn);
   float* qkv = c->at<float>(p.qkv);
   void* q = c->at<void>(p.q);
-  float* gu = c->at<float>(p.gu);
   void* act = c->at<void>(p.act);
 
+  c->tic(ALODLM_K_NORM_ROPE);
   launch_rmsnorm(dt(c), lc.x_in, n, d, nullptr, nullptr, W.attn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st);
+  c->toc();
   GemmEpi e1;
   e1.C = qkv;
   e1.ldc = qkv_out;
+  c->tic(ALODLM_K_GEMM_QKV);
   gemm(c, EPI_STORE, xn, d, W.wqkv, d, n, qkv_out, d, nullptr, e1);
+  c->toc();
 
   AttnParams ap;
   ap.q = q;
@@ -235,9 +304,11 @@ void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
     void* kd = cache_slot(c, false, slot);
     void* vd = cache_slot(c, true, slot);
     const int64_t sSeq = (int64_t)Hkv * Pm * hd, sHead = Pm * hd, sPos = hd;
+    c->tic(ALODLM_K_NORM_ROPE);
     launch_qk_norm_rope(dt(c), qkv, n, lc.rows_per_seq, 0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
                         c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, kd, vd, sSeq, sHead, sPos, lc.seq0,
                         c->st);
+    c->toc();
     ap.n_cache = 0;
     ap.sk = kd;
     ap.sv = vd;
@@ -251,8 +322,10 @@ void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
     void* ks = c->at<void>(p.kself);
     void* vs = c->at<void>(p.vself);
     const int64_t sSeq = (int64_t)lc.rows_per_seq * Hkv * hd, sHead = hd, sPos = (int64_t)Hkv * hd;
+    c->tic(ALODLM_K_NORM_ROPE);
     launch_qk_norm_rope(dt(c), qkv, n, lc.rows_per_seq, lc.pos0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
                         c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, ks, vs, sSeq, sHead, sPos, 0, c->st);
+    c->toc();
     const bool core = li >= g.n_pre && li < g.n_pre + g.n_core;
     const int slot = slot_of(g, li, 1);
     ap.ck = cache_slot(c, false, slot);
@@ -275,25 +348,34 @@ void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
     ap.n_self = lc.rows_per_seq;
     ap.causal = 0;
   }
+  c->tic(ALODLM_K_ATTENTION);
   attention(c, ap);
+  c->toc();
 
   GemmEpi e2;
   e2.C = lc.x_out;
   e2.R = lc.x_in;
   e2.ldc = d;
+  c->tic(ALODLM_K_GEMM_O);
   gemm(c, EPI_RESID, attn, Hq * hd, W.wo, Hq * hd, n, d, Hq * hd, nullptr, e2);
+  c->toc();
 
+  c->tic(ALODLM_K_NORM_ROPE);
   launch_rmsnorm(dt(c), lc.x_out, n, d, nullptr, nullptr, W.ffn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st);
+  c->toc();
   GemmEpi e3;
-  e3.C = gu;
-  e3.ldc = 2 * F;
-  gemm(c, EPI_STORE, xn, d, W.w_gate_up, d, n, 2 * F, d, nullptr, e3);
-  launch_swiglu(dt(c), gu, n, F, act, c->st);
+  e3.act = act;
+  e3.ld_act = F;
+  c->tic(ALODLM_K_GEMM_GATE_UP);
+  gemm(c, EPI_SWIGLU, xn, d, W.w_gate_up, d, n, 2 * F, d, nullptr, e3, F);
+  c->toc();
   GemmEpi e4;
   e4.C = lc.x_out;
   e4.R = lc.x_out;
   e4.ldc = d;
+  c->tic(ALODLM_K_GEMM_DOWN);
   gemm(c, EPI_RESID, act, F, W.w_down, F, n, d, F, nullptr, e4);
+  c->toc();
   c->layer_calls += 1;
 }
 
@@ -304,11 +386,11 @@ void readout_heads(alodlm_ctx* c, const void* rows, int n_upper, const int32_t* 
   const Plan& p = c->plan;
   GemmEpi ep;
   ep.part = c->at<SoftStat>(p.part);
-  ep.n_tiles = p.n_vtiles;
+  ep.n_tiles = lm_tiles(c);
   ep.btok = btok;
   ep.bval = bval;
   gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_upper, g.vocab, g.d_model, n_dev, ep);
-  launch_softstat_combine(c->at<SoftStat>(p.part), n_upper, p.n_vtiles, n_dev, c->at<float>(p.H),
+  launch_softstat_combine(c->at<SoftStat>(p.part), n_upper, ep.n_tiles, n_dev, c->at<float>(p.H),
                           c->at<float>(p.lse), c->at<int32_t>(p.tok), c->st);
 }
 
@@ -389,6 +471,8 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
   c->ws = (char*)workspace;
   c->ws_bytes = ws_bytes;
   c->st = (hipStream_t)hip_stream;
+  const char* fg = getenv("ALODLM_FORCE_GENERIC");
+  c->force_generic = fg && fg[0] == '1';
   // RoPE tables, computed in double on the host: angle(pos, i) = pos * theta^(-2i/hd)
   const int half = cfg->head_dim / 2;
   std::vector<float> cs((size_t)plan.max_pos * half), sn((size_t)plan.max_pos * half);
@@ -499,6 +583,11 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
   const int P = c->cache_prefix;
   hipStream_t st = c->st;
   c->layer_calls = 0;
+  struct StepScope {
+    alodlm_ctx* c;
+    explicit StepScope(alodlm_ctx* x) : c(x) { c->in_step = true; c->ev_used = 0; }
+    ~StepScope() { c->in_step = false; c->ev_used = 0; }
+  } scope(c);
 
   uint8_t* U = c->at<uint8_t>(p.U);
   float* av = c->at<float>(p.a);
@@ -554,8 +643,10 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
       gsrc = h_alt;
     }
     // readout rows r (compact), ExitGate lambda
+    c->tic(ALODLM_K_NORM_ROPE);
     launch_rmsnorm(dt(c), gsrc, n, d, ro_rows, cnt + 1, c->w.final_norm, g.rms_eps, c->at<void>(p.r), c->w.exit_w,
                    c->w.exit_b, c->at<float>(p.lam), st);
+    c->toc();
     // per-readout-row boosts
     const int32_t* bt = nullptr;
     const float* bv = nullptr;
@@ -566,13 +657,17 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
       launch_gather_boosts(ro_rows, cnt + 1, act[cur], n, L, a->boost_tok, a->boost_val, c->at<int32_t>(p.btok),
                            c->at<float>(p.bval), st);
     }
+    c->tic(ALODLM_K_LM_HEAD);
     readout_heads(c, c->at<void>(p.r), n, cnt + 1, bt, bv);
+    c->toc();
+    c->tic(ALODLM_K_CONTROL);
     launch_commit(nb, s, K, L, B, a->tau_ent, a->tau_halt, act[cur], U, av, ro_map, c->at<float>(p.H),
                   c->at<int32_t>(p.tok), c->at<float>(p.lam), c->at<float>(p.lse), o->tokens, o->commit_loop, ncommit,
                   stop, o->loops, tf ? a->tf_commit_loop : nullptr, tf ? a->tf_tokens : nullptr,
                   tf ? a->tf_stop_loop : nullptr, dbg ? o->entropy : nullptr, o->lam, o->halt, o->lse, o->argmax, st);
     launch_build_lists(nb, L, B, act[cur], stop, U, ncommit, act[cur ^ 1], src_slot, ro_rows, ro_map, cnt, st);
     launch_reset_compact(dt(c), nb, cnt, L, d, g.vocab, act[cur ^ 1], src_slot, U, o->tokens, h, c->w.embed, h_alt, st);
+    c->toc();
     float* t = h;
     h = h_alt;
     h_alt = t;
@@ -583,6 +678,7 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
       return c->fail(ALODLM_EHIP, std::string("loop status read: ") + hipGetErrorString(e1 != hipSuccess ? e1 : e2));
     int rc = c->hip_check("step launch");
     if (rc) return rc;
+    c->fold();
     nb = host_cnt[0];
   }
   o->n_committed = host_cnt[2];
@@ -619,18 +715,35 @@ int alodlm_readout_commit(alodlm_ctx* c, const void* rows, int32_t n_rows, int32
   // LMHead over the given rows (row order = readout order)
   GemmEpi ep;
   ep.part = c->at<SoftStat>(p.part);
-  ep.n_tiles = p.n_vtiles;
+  ep.n_tiles = lm_tiles(c);
   ep.btok = boost_tok;
   ep.bval = boost_val;
-  launch_gemm_generic(dt(c), EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_rows, g.vocab, g.d_model,
-                      nullptr, ep, st);
-  launch_softstat_combine(c->at<SoftStat>(p.part), n_rows, p.n_vtiles, nullptr, entropy, lse, argmax, st);
+  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_rows, g.vocab, g.d_model, nullptr, ep);
+  launch_softstat_combine(c->at<SoftStat>(p.part), n_rows, ep.n_tiles, nullptr, entropy, lse, argmax, st);
   // one loop of the commit rule (a starts at 0, so a = lambda); per-row records go to the outputs
   launch_commit(B, 1, 1, L, B, tau_ent, tau_halt, act1, U, halt, c->at<int32_t>(p.ro_map), entropy, argmax, lam, lse,
                 tokens, commit_loop, c->at<int32_t>(p.ncommit), c->at<uint8_t>(p.stop), seq_loops, nullptr, nullptr,
                 nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st);
   launch_embed_committed(dt(c), commit_loop, tokens, c->w.embed, n_rows, g.d_model, g.vocab, embed_out, st);
   return c->hip_check("readout launch");
+}
+
+int alodlm_diag_timing_enable(alodlm_ctx* c, int32_t enable) {
+  if (!c) return ALODLM_EINVAL;
+  c->timing = enable != 0;
+  c->ev_used = 0;
+  for (int k = 0; k < ALODLM_K_CLASSES; ++k) {
+    c->t_ms[k] = 0.0;
+    c->t_n[k] = 0;
+  }
+  return ALODLM_OK;
+}
+
+int alodlm_diag_timing_read(const alodlm_ctx* c, int32_t kernel_class, double* ms, int64_t* launches) {
+  if (!c || kernel_class < 0 || kernel_class >= ALODLM_K_CLASSES) return ALODLM_EINVAL;
+  if (ms) *ms = c->t_ms[kernel_class];
+  if (launches) *launches = c->t_n[kernel_class];
+  return ALODLM_OK;
 }
 
 int alodlm_last_step_stats(const alodlm_ctx* c, int64_t* layer_calls, int32_t* loops_run) {

@@ -1,0 +1,162 @@
+#!/usr/bin/env python3
+"""Committed tokens/s of the ALoDLM adaptively looped denoising step at 8B shape on one MI355X.
+
+One "step" is one alodlm_denoise_step over the whole batch: Prelude once, then per loop the
+shared Core, the Coda, the LM-head / ExitGate readout, the commit rule, compaction and the
+Eq. 3 reset, until every sequence halts.  Inputs (random-init weights, prefix ids, planted
+readout boosts) are synthetic and already resident in HBM; the prefix cache is built by
+alodlm_prefill_kv before timing (reported separately as prefill_ms).
+
+Prints one JSON line.  Options: --gpus (1 only), --steps, --warmup, --workload, --no-cpu-baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+from dataclasses import replace
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
+
+
+def progress(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def ffn_gate_up_traffic(w, rows_total, launches):
+    """Algorithmic HBM bytes per gate/up GEMM launch: the [2F][d] bf16 weight read once, the
+    bf16 input rows read once, the bf16 SwiGLU output written once (averaged over launches)."""
+    D = w.dims
+    wbytes = 2 * D.ffn * D.d_model * 2
+    return (launches * wbytes + rows_total * (D.d_model + D.ffn) * 2) / launches
+
+
+def cpu_baseline(w, tau):
+    """The fp64 oracle (as it stands) on a bounded sample: sequence 0 of the same step, over a
+    synthetic prefix cache (the prefill is excluded on both sides)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import run as orun
+    cores = len(os.sched_getaffinity(0))
+    ws = replace(w, kv="synthetic", tau_ent=tau, batch=1)
+    progress("cpu baseline: generating host weights")
+    W = orun.weights(ws)
+    cache = orun.cache_for(ws, W, 0)
+    progress("cpu baseline: oracle step of one sequence on %d cores" % cores)
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        res = orun.step(ws, W=W, seqs=[0], caches={0: cache})
+        el = time.perf_counter() - t0
+    committed = int(np.count_nonzero(res[0]["commit_loop"]))
+    return dict(value=committed / el, unit="committed tokens/s", cores=cores, kind="oracle",
+                sample="sequence 0 of the %s step (1 of %d sequences, %d loops, %d committed), synthetic prefix "
+                       "cache, %.1f s" % (w.name, w.batch, res[0]["loops"], committed, el))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the step has no cross-GPU path (sequences shard by data "
+              "parallelism with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from adaptive_looped_denoising_amd import binding as B
+    from adaptive_looped_denoising_amd import synth
+    from adaptive_looped_denoising_amd.engine import Engine
+
+    w = synth.workload(args.workload)
+    taus = synth.TAU_SWEEP_8B if args.workload == "qwen3_8b" else (w.tau_ent,)
+    progress("workload %s: building engine (device-filled weights)" % w.name)
+    e = Engine(w)
+    torch.cuda.synchronize()
+    progress("prefill")
+    t0 = time.perf_counter()
+    e.prefill()
+    torch.cuda.synchronize()
+    prefill_ms = (time.perf_counter() - t0) * 1e3
+    progress("prefill %.1f ms" % prefill_ms)
+
+    def timed(tau, steps, warmup):
+        a = e.make_args(tau_ent=tau)
+        o = e.make_out(a.k_loops)
+        for _ in range(warmup):
+            e.run(a, o)
+        torch.cuda.synchronize()
+        committed = 0
+        loops = []
+        t = time.perf_counter()
+        for _ in range(steps):
+            e.run(a, o)
+            committed += o.n_committed
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t
+        loops = e.out_loops.cpu().numpy().astype(int).tolist()
+        return dict(tok_s=committed / el, ms_per_step=el / steps * 1e3, committed_per_step=committed / steps,
+                    loops=loops)
+
+    sweep = {}
+    for tau in taus:
+        sweep[str(tau)] = timed(tau, args.steps, args.warmup)
+        progress("tau_ent %.1f: %s" % (tau, sweep[str(tau)]))
+    head = sweep[str(w.tau_ent)]
+
+    # Kernel timing pass: the same steps with HIP event pairs around every kernel class on the
+    # library's stream (the stream every kernel of the step runs on).
+    B.timing_enable(e.ctx, True)
+    prof = timed(w.tau_ent, args.steps, 0)
+    kt = B.timing_read(e.ctx)
+    B.timing_enable(e.ctx, False)
+    loops = prof["loops"]
+    D = w.dims
+    launches = kt["gemm_gate_up"][1]
+    rows_per_step = D.n_pre * w.batch * w.block + (D.n_core + D.n_coda) * w.block * sum(loops)
+    per_launch_ms = kt["gemm_gate_up"][0] / max(launches, 1)
+    traffic = ffn_gate_up_traffic(w, rows_per_step * args.steps, launches)
+    achieved = traffic / (per_launch_ms * 1e-3) / 1e9
+    kernels = {k: dict(ms_per_step=v[0] / args.steps, launches_per_step=v[1] / args.steps) for k, v in kt.items()}
+
+    line = {
+        "metric": "committed tokens/s per GPU, 8B-shape looped denoise; % MFMA peak + % HBM BW",
+        "value": head["tok_s"],
+        "unit": "committed tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and prefix ids, planted readout boosts)",
+        "config": {"workload": "%s: Qwen3-8B dims, batch %d, prefix %d, block %d masked, K_max %d, tau_ent %.1f, "
+                               "tau_halt %.1f" % (w.name, w.batch, w.prefix, w.block, w.k_max, w.tau_ent, w.tau_halt),
+                   "batch": w.batch, "prefix": w.prefix, "block": w.block, "k_max": w.k_max,
+                   "tau_ent": w.tau_ent, "tau_halt": w.tau_halt, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "FFN gate/up GEMM + SwiGLU (k_gemm_mfma, %d rows/launch avg, %.1f us/launch)" % (
+                         rows_per_step / max(launches / args.steps, 1), per_launch_ms * 1e3)},
+        "tau_sweep": sweep,
+        "prefill_ms": prefill_ms,
+        "kernels": kernels,
+        "timing_pass_ms_per_step": prof["ms_per_step"],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, w.tau_ent)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

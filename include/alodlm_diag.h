@@ -1,0 +1,56 @@
+/*
+ * alodlm_diag.h -- kernel-level entry points for unit tests and kernel timing.
+ *
+ * Not part of the method's interface: these expose the library's GEMM dispatcher
+ * (the same tiles, split-K and epilogues the denoising step launches) on caller
+ * buffers, so each kernel can be checked against plain arithmetic and timed at the
+ * step's real shapes.  Device pointers, row-major; nothing is allocated.
+ */
+#ifndef ALODLM_DIAG_H
+#define ALODLM_DIAG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ALODLM_DIAG_STORE 0  /* C[M][N] = A . B^T (fp32) */
+#define ALODLM_DIAG_RESID 1  /* C[M][N] += A . B^T (fp32) */
+#define ALODLM_DIAG_SWIGLU 3 /* B = [2F][K] (gate rows, then up rows); act[M][F] = silu(A.Bg^T) * (A.Bu^T) */
+
+/* bf16 A [M][K], B [N][K] (N = 2F for SWIGLU).  scratch: device fp32 buffer of
+ * scratch_floats for split-K partials (force_splits > 1 needs splits*M*N floats).
+ * force_splits: 0 = the dispatcher's choice.  force_generic != 0 runs the vector-ALU
+ * kernel instead of the matrix-core one.  Asynchronous.  Returns 0 or -1 (bad
+ * arguments, checked before any launch), -4 (launch failed). */
+__attribute__((visibility("default"))) int alodlm_diag_gemm(int32_t epi, int32_t M, int32_t N, int32_t K,
+                                                            const void* A, const void* B, float* C, void* act,
+                                                            float* scratch, size_t scratch_floats,
+                                                            int32_t force_splits, int32_t force_generic,
+                                                            void* hip_stream);
+
+/* Kernel classes timed by alodlm_diag_timing_*. */
+#define ALODLM_K_GEMM_GATE_UP 0 /* FFN gate/up GEMM with the fused SwiGLU epilogue */
+#define ALODLM_K_GEMM_QKV 1
+#define ALODLM_K_GEMM_O 2       /* attention output projection + residual */
+#define ALODLM_K_GEMM_DOWN 3    /* FFN down projection + residual */
+#define ALODLM_K_ATTENTION 4    /* block attention over the depth-aware prefix cache */
+#define ALODLM_K_LM_HEAD 5      /* LM-head readout GEMM + softmax-statistics merge */
+#define ALODLM_K_NORM_ROPE 6    /* RMSNorms, q/k norm + RoPE, ExitGate */
+#define ALODLM_K_CONTROL 7      /* commit rule, list build, Eq. 3 reset, boosts, state init */
+#define ALODLM_K_CLASSES 8
+
+struct alodlm_ctx;
+/* enable != 0: every later denoising step brackets each kernel class with HIP events on the
+ * context stream and accumulates their durations; enable == 0 stops and clears the counters. */
+__attribute__((visibility("default"))) int alodlm_diag_timing_enable(struct alodlm_ctx* ctx, int32_t enable);
+/* Accumulated milliseconds and launch count of a class since timing was enabled. */
+__attribute__((visibility("default"))) int alodlm_diag_timing_read(const struct alodlm_ctx* ctx, int32_t kernel_class,
+                                                                   double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ALODLM_DIAG_H */

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _declared():
     names = set()
-    for h in ("alodlm.h", "alodlm_synth.h"):
+    for h in ("alodlm.h", "alodlm_synth.h", "alodlm_diag.h"):
         txt = open(os.path.join(ROOT, "include", h)).read()
         names |= set(re.findall(r"\b(alodlm_[a-z_0-9]+)\s*\(", txt))
     return names

@@ -1,0 +1,135 @@
+"""Kernel-level GPU checks: the bf16 GEMM family (matrix-core tiles, split-K, epilogues) against
+plain float64 arithmetic, and the fused readout (LM head + ExitGate + commit) against the oracle
+at the 8B LM-head shape."""
+import numpy as np
+import pytest
+import torch
+
+from adaptive_looped_denoising_amd import synth
+from oracle import alodlm_oracle as orc
+from tests.parity import log
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(32, 4096, 2048), (256, 6144, 4096), (200, 1024, 512), (1, 128, 64), (77, 640, 384), (2048, 1024, 4096),
+          (130, 4096, 12288)]
+
+
+def _bf16(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16)
+
+
+def _gemm(epi, A, Bm, C=None, act=None, splits=0, generic=0):
+    from adaptive_looped_denoising_amd import binding as B
+    M, K = A.shape
+    N = Bm.shape[0]
+    scratch = torch.empty(max(8 * M * N, 1), dtype=torch.float32, device="cuda")
+    B.diag_gemm(epi, M, N, K, A.data_ptr(), Bm.data_ptr(), 0 if C is None else C.data_ptr(),
+                0 if act is None else act.data_ptr(), scratch.data_ptr(), scratch.numel(), splits, generic,
+                torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+
+
+def _ref(A, Bm):
+    return A.double().numpy() @ Bm.double().numpy().T
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_store_and_resid(gpu_lib, M, N, K):
+    log("gemm M=%d N=%d K=%d" % (M, N, K))
+    A, Bm = _bf16((M, K), 1), _bf16((N, K), 2, 0.02)
+    ref = _ref(A, Bm)
+    scale = np.sqrt(K) * 0.02
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    _gemm(0, A.cuda(), Bm.cuda(), C=C)
+    err = np.abs(C.cpu().numpy() - ref).max() / scale
+    assert err < 2e-5, err
+    C0 = torch.randn((M, N), generator=torch.Generator().manual_seed(3)).cuda()
+    C1 = C0.clone()
+    _gemm(1, A.cuda(), Bm.cuda(), C=C1)
+    err = np.abs(C1.cpu().numpy() - (C0.cpu().double().numpy() + ref)).max() / scale
+    assert err < 2e-5, err
+
+
+@pytest.mark.parametrize("splits", [2, 4, 8])
+def test_gemm_split_k_matches_single_pass(gpu_lib, splits):
+    M, N, K = 96, 2048, 4096
+    A, Bm = _bf16((M, K), 4).cuda(), _bf16((N, K), 5, 0.02).cuda()
+    C1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    C2 = torch.empty_like(C1)
+    _gemm(0, A, Bm, C=C1, splits=1)
+    _gemm(0, A, Bm, C=C2, splits=splits)
+    ref = _ref(A.cpu(), Bm.cpu())
+    for C in (C1, C2):
+        assert np.abs(C.cpu().numpy() - ref).max() / (np.sqrt(K) * 0.02) < 2e-5
+    # the fixed-order reduction is deterministic
+    C3 = torch.empty_like(C1)
+    _gemm(0, A, Bm, C=C3, splits=splits)
+    assert torch.equal(C2, C3)
+
+
+@pytest.mark.parametrize("M,F,K,splits", [(32, 6144, 2048, 0), (256, 12288, 4096, 0), (50, 384, 128, 0),
+                                          (64, 1024, 4096, 4)])
+def test_gemm_swiglu(gpu_lib, M, F, K, splits):
+    A, Bm = _bf16((M, K), 6), _bf16((2 * F, K), 7, 0.05)
+    act = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    _gemm(3, A.cuda(), Bm.cuda(), act=act, splits=splits)
+    gu = _ref(A, Bm)
+    g, u = gu[:, :F], gu[:, F:]
+    ref = g / (1 + np.exp(-g)) * u
+    got = act.cpu().float().numpy()
+    err = np.abs(got - ref) / (np.abs(ref) + 1e-2 * np.abs(ref).max())
+    assert err.max() < 1.6e-2, err.max()
+
+
+def test_gemm_generic_matches(gpu_lib):
+    M, N, K = 70, 300, 256
+    A, Bm = _bf16((M, K), 8).cuda(), _bf16((N, K), 9, 0.02).cuda()
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    _gemm(0, A, Bm, C=C, generic=1)
+    assert np.abs(C.cpu().numpy() - _ref(A.cpu(), Bm.cpu())).max() / (16 * 0.02) < 2e-5
+
+
+@pytest.mark.parametrize("n_rows", synth.READOUT_ROWS)
+def test_readout_commit_at_8b_vocab(gpu_lib, n_rows):
+    """LM head 4096 x 151936 + ExitGate + commit rule on rows standing for post-RMSNorm states,
+    grouped into sequences of 32; every row of the first group and a row sample of the rest is
+    recomputed by the oracle in float64."""
+    from adaptive_looped_denoising_amd.engine import Engine
+    w = synth.readout_workload(n_rows)
+    log("readout n_rows=%d" % n_rows)
+    e = Engine(w)
+    rows = synth.readout_rows(n_rows)
+    bt, bv = synth.boosts(w)
+    bt, bv = bt.reshape(-1), bv.reshape(-1)
+    rows_d = torch.from_numpy(rows.view(np.int16)).cuda().view(torch.bfloat16)
+    out = e.readout_commit(rows_d, synth.READOUT_GROUP if n_rows >= 32 else n_rows, w.tau_ent, w.tau_halt,
+                           torch.from_numpy(bt).cuda(), torch.from_numpy(bv).cuda())
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    W = {k: synth.as_f32(v) for k, v in synth.host_weights(w, ["lm_head", "embed", "exit_w"]).items()}
+    r = synth.as_f32(rows)
+    group = list(range(min(32, n_rows)))
+    sample = sorted(set(group) | set(range(0, n_rows, max(1, n_rows // 16))))
+    og = orc.readout_commit_group(r[group], W["lm_head"], W["embed"], W["exit_w"], e.exit_b, w.tau_ent,
+                                  w.tau_halt, bt[group], bv[group])
+    H, tok, lse, gap = orc.readout(r[sample], W["lm_head"], bt[sample], bv[sample])
+    lam = orc.exit_gate(r[sample], W["exit_w"], e.exit_b)
+    assert np.abs(got["entropy"][sample] - H).max() < 1e-2
+    assert np.abs(got["lse"][sample] - lse).max() < 1e-3 * np.abs(lse).max()
+    assert np.abs(got["lam"][sample] - lam).max() < 1e-4
+    mism = got["argmax"][sample] != tok
+    assert (gap[mism] < 1e-2).all()
+    # the first group's decisions: commits, forced progress, Eq. 3 rows
+    near = (np.abs(og["H"] - w.tau_ent) < 1e-2).any() or (og["forced"] >= 0 and np.sort(og["H"])[1] -
+                                                           np.sort(og["H"])[0] < 1e-2)
+    if not near:
+        assert np.array_equal(got["commit_loop"][group], og["commit_loop"])
+        committed = og["commit_loop"] != 0
+        assert np.array_equal(got["tokens"][group][committed], og["tok"][committed])
+        np.testing.assert_array_equal(got["embed"][group], og["embed_rows"].astype(np.float32))
+        np.testing.assert_allclose(got["halt"][group], og["a"], atol=1e-4)
+    log("readout n=%d: H err %.2e, commits %d, forced %d" % (n_rows, np.abs(got["entropy"][sample] - H).max(),
+                                                               int((got["commit_loop"] > 0).sum()),
+                                                               int((got["commit_loop"] < 0).sum())))
