@@ -95,6 +95,8 @@ void launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, i
 void launch_gemm_generic(int dtype, int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                          const int32_t* m_dev, const GemmEpi& ep, hipStream_t st);
 void launch_attn_generic(int dtype, const AttnParams& p, hipStream_t st);
+bool attn_mfma_supported(int hd);
+void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st);
 
 void launch_fill_kv_synth(int dtype, void* slot_base, int B, int Hkv, int P, int P_max, int hd, uint32_t seed,
                           uint32_t tensor, float scale, hipStream_t st);

@@ -244,7 +244,15 @@ int lm_tiles(const alodlm_ctx* c) {
   return use_mfma(c, d, d, d) ? (c->cfg.vocab + MFMA_TILE_N - 1) / MFMA_TILE_N : (c->cfg.vocab + 63) / 64;
 }
 
-void attention(alodlm_ctx* c, const AttnParams& p) { launch_attn_generic(dt(c), p, c->st); }
+void attention(alodlm_ctx* c, const AttnParams& p) {
+  if (c->cfg.dtype == ALODLM_DTYPE_BF16 && !c->force_generic && attn_mfma_supported(p.hd)) {
+    AttnParams q = p;
+    q.part = c->at<float>(c->plan.attn_part);
+    launch_attn_mfma(q, c->plan.attn_splits, c->st);
+    return;
+  }
+  launch_attn_generic(dt(c), p, c->st);
+}
 
 enum Mode { STEP, PREFILL };
 

@@ -137,3 +137,36 @@ def test_tiny_step_errors(gpu_lib):
             e.step(**kw)
         assert ex.value.code == B.EINVAL
     e.step()
+
+
+MID_DIMS = synth.Dims(vocab=4096, d_model=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1024, n_pre=2,
+                      n_core=2, n_coda=2)
+
+
+def _mid(**over):
+    base = synth.Workload("mid", MID_DIMS, "bf16", batch=3, prefix=300, block=32, k_max=4, tau_ent=0.6,
+                          tau_halt=0.6, seed=11, boost_lo=10.0, boost_hi=16.0)
+    return replace(base, **over)
+
+
+def test_mid_bf16_prefill_step(gpu_lib):
+    """hd 128, 4 query heads per kv head, ragged prefix (300 = 4 tiles + 44), prefix built by the
+    library's causal prefill."""
+    _check_step(_mid(), gpu_lib)
+
+
+def test_mid_bf16_synthetic_cache_depth_fallback(gpu_lib):
+    """Synthetic depth-aware cache where 25% of prefix positions only hold depths 1..2: loops 3
+    and 4 must fall back to the deepest available depth."""
+    w = _mid(kv="synthetic", short_frac=0.25, short_depth=2, tau_ent=0.0, tau_halt=2.0, prefix=700, batch=2)
+    _check_step(w, gpu_lib)
+
+
+def test_mid_bf16_block_64_and_single_row(gpu_lib):
+    _check_step(_mid(block=64, prefix=130, batch=2), gpu_lib)
+    _check_step(_mid(block=1, prefix=64, batch=4, tau_halt=0.3), gpu_lib)
+
+
+def test_mid_fp32_matches_bf16_structure(gpu_lib):
+    # fp32 mode on the same shapes (generic kernels) at the fp32 tolerance
+    _check_step(_mid(dtype="fp32", prefix=100), gpu_lib)
