@@ -88,7 +88,7 @@ def load(path: str = LIB_PATH):
     lib.alodlm_synth_fill.argtypes = [c_void_p, c_int32, c_uint64, c_uint64, c_uint32, c_uint32, c_float, c_float,
                                       c_void_p]
     lib.alodlm_diag_gemm.argtypes = [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
-                                     c_void_p, c_size_t, c_int32, c_int32, c_void_p]
+                                     c_void_p, c_size_t, c_int32, c_int32, c_int32, c_void_p]
     lib.alodlm_diag_timing_enable.argtypes = [c_void_p, c_int32]
     lib.alodlm_diag_timing_read.argtypes = [c_void_p, c_int32, POINTER(ctypes.c_double), POINTER(c_int64)]
     for name in EXPORTS:
@@ -168,10 +168,10 @@ def synth_fill(dst_ptr: int, dtype: int, start: int, n: int, seed: int, tensor: 
 
 
 def diag_gemm(epi: int, M: int, N: int, K: int, A_ptr: int, B_ptr: int, C_ptr: int, act_ptr: int, scratch_ptr: int,
-              scratch_floats: int, force_splits: int, force_generic: int, stream_ptr: int):
+              scratch_floats: int, force_splits: int, force_generic: int, stream_ptr: int, force_tile: int = -1):
     rc = load().alodlm_diag_gemm(epi, M, N, K, c_void_p(A_ptr), c_void_p(B_ptr), c_void_p(C_ptr or None),
                                  c_void_p(act_ptr or None), c_void_p(scratch_ptr or None), scratch_floats,
-                                 force_splits, force_generic, c_void_p(stream_ptr))
+                                 force_splits, force_generic, force_tile, c_void_p(stream_ptr))
     if rc != 0:
         raise AlodlmError(rc, "alodlm_diag_gemm failed")
 

@@ -27,14 +27,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Address of key j (0-based over prefix keys then own keys) of sequence slot t / cache sequence b.
+// Core layers take the depth plane of prefix key j from sdep[j - dep_base] (staged in LDS).
 __device__ __forceinline__ const bf16_t* akv_row(const AttnParams& p, const void* cbase, const void* sbase, int j,
-                                                 int b, int t, int kvh) {
+                                                 int b, int t, int kvh, const uint8_t* sdep, int dep_base) {
   if (j < p.n_cache) {
     size_t off = (size_t)b * p.c_sSeq + (size_t)kvh * p.c_sHead + (size_t)j * p.c_sPos;
-    if (p.core) {
-      const int dep = max(1, min(p.loop, (int)p.avail[(size_t)b * p.av_stride + j]));
-      off += (size_t)(dep - 1) * p.c_plane;
-    }
+    if (p.core) off += (size_t)sdep[j - dep_base] * p.c_plane;
     return (const bf16_t*)cbase + off;
   }
   const int jj = j - p.n_cache;
@@ -52,8 +50,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
   constexpr int KLD = HD + 8;          // K tile pitch (elements)
   constexpr int VLD = AKT + 4;         // V^T tile pitch (keys)
   constexpr int KROWS = 256 / CPR;     // key rows loaded per pass
+  constexpr int DEPC = 4096;            // depth-plane indices staged per chunk of prefix keys
   __shared__ __attribute__((aligned(16))) bf16_t sK[AKT * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[HD * VLD];
+  __shared__ uint8_t sdep[DEPC];
 
   const int total = n_pairs * n_qblocks * n_splits;
   const int per = (gridDim.x + 7) >> 3;
@@ -108,30 +108,41 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
     lrun[nq] = 0.f;
   }
 
-  for (int k0 = kbeg; k0 < kend; k0 += AKT) {
-    __syncthreads();
-    // K tile: rows k0 .. k0+63, key-major
+  // K/V tile loads are register double-buffered: the next tile's rows are in flight while the
+  // matrix cores work on the current one.
+  constexpr int KP = AKT / KROWS;  // K row passes per thread
+  uint4 kreg[KP], vreg[4];
+  const bool vthread = tid < 16 * CPR;
+  int dep_base = kbeg;
+  auto gload = [&](int k0) {
 #pragma unroll
-    for (int pass = 0; pass < AKT / KROWS; ++pass) {
-      const int r = pass * KROWS + tid / CPR, c = tid % CPR;
-      const int j = k0 + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < kend) v = *(const uint4*)(akv_row(p, p.ck, p.sk, j, b, t, kvh) + c * 8);
-      *(uint4*)&sK[r * KLD + c * 8] = v;
+    for (int pass = 0; pass < KP; ++pass) {
+      const int j = k0 + pass * KROWS + tid / CPR;
+      kreg[pass] = j < kend ? *(const uint4*)(akv_row(p, p.ck, p.sk, j, b, t, kvh, sdep, dep_base) + (tid % CPR) * 8)
+                            : make_uint4(0, 0, 0, 0);
     }
-    // V tile, transposed: thread takes 4 consecutive keys x 8 hd values
-    if (tid < 16 * CPR) {
+    if (vthread) {
       const int kq = tid / CPR, c = tid % CPR;
-      uint4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = k0 + kq * 4 + u;
-        v[u] = j < kend ? *(const uint4*)(akv_row(p, p.cv, p.sv, j, b, t, kvh) + c * 8) : make_uint4(0, 0, 0, 0);
+        vreg[u] = j < kend ? *(const uint4*)(akv_row(p, p.cv, p.sv, j, b, t, kvh, sdep, dep_base) + c * 8)
+                           : make_uint4(0, 0, 0, 0);
       }
-      const bf16_t* e0 = (const bf16_t*)&v[0];
-      const bf16_t* e1 = (const bf16_t*)&v[1];
-      const bf16_t* e2 = (const bf16_t*)&v[2];
-      const bf16_t* e3 = (const bf16_t*)&v[3];
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int pass = 0; pass < KP; ++pass) {
+      const int r = pass * KROWS + tid / CPR, c = tid % CPR;
+      *(uint4*)&sK[r * KLD + c * 8] = kreg[pass];
+    }
+    if (vthread) {  // transpose: 4 consecutive keys x 8 hd values -> 8 rows of V^T
+      const int kq = tid / CPR, c = tid % CPR;
+      const bf16_t* e0 = (const bf16_t*)&vreg[0];
+      const bf16_t* e1 = (const bf16_t*)&vreg[1];
+      const bf16_t* e2 = (const bf16_t*)&vreg[2];
+      const bf16_t* e3 = (const bf16_t*)&vreg[3];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         uint2 w;
@@ -140,7 +151,31 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
         *(uint2*)&sV[(c * 8 + e) * VLD + kq * 4] = w;
       }
     }
+  };
+  // depth plane min(loop, avail[j]) - 1 of the prefix keys [kstart, kstart + DEPC) of this range
+  auto load_dep = [&](int kstart) {
+    const int lim = min(min(kend, p.n_cache), kstart + DEPC);
+    for (int j = kstart + tid; j < lim; j += 256)
+      sdep[j - kstart] = (uint8_t)(max(1, min(p.loop, (int)p.avail[(size_t)b * p.av_stride + j])) - 1);
+  };
+  if (p.core) {
+    load_dep(kbeg);
     __syncthreads();
+  }
+  if (kbeg < kend) gload(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += AKT) {
+    __syncthreads();
+    sstore();
+    __syncthreads();
+    const int kn = k0 + AKT;
+    if (kn < kend) {
+      if (p.core && (kn - dep_base) >= DEPC) {  // next tile starts a new chunk of staged depths
+        dep_base = kn;
+        load_dep(kn);
+        __syncthreads();
+      }
+      gload(kn);
+    }
 
     // S^T = K Q^T : 4 key subtiles x NQ query subtiles
     floatx4 s[4][NQ];
@@ -318,8 +353,9 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st) {
   const int n_tiles = (n_keys + AKT - 1) / AKT;
   int splits = 1;
   if (!p.causal && p.part) {
-    const int want = (512 + n_pairs * n_qblocks - 1) / (n_pairs * n_qblocks);
-    splits = min(min(want, n_tiles), max_splits);
+    // enough blocks to cover the chip once, and at least 4 key tiles per split
+    const int want = (256 + n_pairs * n_qblocks - 1) / (n_pairs * n_qblocks);
+    splits = min(min(want, max(1, n_tiles / 4)), max_splits);
     if (splits < 1) splits = 1;
   }
   const int kps = ((n_tiles + splits - 1) / splits) * AKT;

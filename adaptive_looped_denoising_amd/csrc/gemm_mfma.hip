@@ -11,6 +11,8 @@
 // 16-column groups, output bf16 silu(gate) * up), SOFTSTAT (per-row softmax statistics of the
 // tile for the LM-head readout; logits never leave the chip).  Split-K writes fp32 partials
 // that k_splitk_reduce sums in a fixed order and finishes with the same epilogue.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -30,6 +32,100 @@ __device__ __forceinline__ int swiglu_b_row(int n, int F) {
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool SPLIT>
+__device__ __forceinline__ void gemm_epilogue(floatx4 (&acc)[BM / WM / 16][BN / WN / 16], int m0, int n0, int nt,
+                                              int sp, int Mr, int M, int N, const GemmEpi& ep, int wm, int wn,
+                                              int lane, int tid) {
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  const int rbase = m0 + wm * TM * 16 + 4 * (lane >> 4);
+  const int cbase = n0 + wn * TN * 16 + (lane & 15);
+  if (SPLIT) {
+    float* P = ep.C + (size_t)sp * M * N;
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = rbase + a * 16 + v;
+        if (m >= Mr) continue;
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int n = cbase + b * 16;
+          if (n < N) P[(size_t)m * N + n] = acc[a][b][v];
+        }
+      }
+    return;
+  }
+  if (EPI == EPI_STORE || EPI == EPI_RESID) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = rbase + a * 16 + v;
+        if (m >= Mr) continue;
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int n = cbase + b * 16;
+          if (n >= N) continue;
+          const size_t o = (size_t)m * ep.ldc + n;
+          ep.C[o] = (EPI == EPI_RESID ? ep.R[o] : 0.f) + acc[a][b][v];
+        }
+      }
+  } else if (EPI == EPI_SWIGLU) {
+    bf16_t* act = (bf16_t*)ep.act;
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = rbase + a * 16 + v;
+        if (m >= Mr) continue;
+#pragma unroll
+        for (int b = 0; b < TN; b += 2) {
+          const int n = cbase + b * 16;  // gate column (16-column group of even index)
+          if (n >= N) continue;
+          const int p = (n >> 5) * 16 + (n & 15);
+          const float g = acc[a][b][v], u = acc[a][b + 1][v];
+          act[(size_t)m * ep.ld_act + p] = from_f<bf16_t>(g / (1.0f + __expf(-g)) * u);
+        }
+      }
+  } else if (EPI == EPI_SOFTSTAT) {
+    __shared__ SoftStat red[WN][BM];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rl = wm * TM * 16 + a * 16 + 4 * (lane >> 4) + v;
+        const int m = m0 + rl;
+        const int bt = (m < Mr && ep.btok) ? ep.btok[m] : -1;
+        const float bv = bt >= 0 ? ep.bval[m] : 0.f;
+        SoftStat s = softstat_empty();
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int n = cbase + b * 16;
+          if (n < N) {
+            SoftStat e;
+            e.m = acc[a][b][v] + (n == bt ? bv : 0.f);
+            e.S = 1.f;
+            e.T = 0.f;
+            e.idx = n;
+            s = softstat_merge(s, e);
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) s = softstat_merge(s, softstat_shfl_xor(s, o));
+        if ((lane & 15) == 0) red[wn][rl] = s;
+      }
+    __syncthreads();
+    for (int rl = tid; rl < BM; rl += 256) {
+      const int m = m0 + rl;
+      if (m >= Mr) continue;
+      SoftStat s = red[0][rl];
+#pragma unroll
+      for (int w = 1; w < WN; ++w) s = softstat_merge(s, red[w][rl]);
+      ep.part[(size_t)m * ep.n_tiles + nt] = s;
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, bool SPLIT>
 __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16_t* __restrict__ A, int lda,
                                                    const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
                                                    int k_split, int m_tiles, int n_tiles, int splits,
@@ -38,6 +134,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16_t* __restrict__ A,
   constexpr int A_CH = BM * (GK / 8), B_CH = BN * (GK / 8);
   constexpr int CH = (A_CH + B_CH) / 256;
   static_assert((A_CH + B_CH) % 256 == 0, "tile chunks must divide the block");
+  static_assert(WM * WN == 4 && TM * WM * 16 == BM && TN * WN * 16 == BN, "wave grid must tile the block");
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * GLDK];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * GLDK];
 
@@ -134,94 +231,264 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16_t* __restrict__ A,
     __syncthreads();
   }
 
-  // ---------------------------------------------------------------- epilogues
-  const int rbase = m0 + wm * TM * 16 + 4 * (lane >> 4);
-  const int cbase = n0 + wn * TN * 16 + (lane & 15);
-  if (SPLIT) {
-    float* P = ep.C + (size_t)sp * M * N;
+  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid);
+}
+
+// Pipelined variant: an NS-stage LDS ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane, so one wave instruction
+// fills 8 consecutive 128-byte tile rows).  Up to NS-1 stages are in flight while the matrix cores
+// work on the oldest one.  Row r of a stage keeps its eight 16-byte k-chunks XOR-swizzled
+// (chunk c at slot c ^ (r & 7)) so that the 16 rows a fragment read touches spread over the banks.
+// Rows past M / N load row 0 (never stored).
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt constraining only the vector-memory counter to <= N (gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14], expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int EPI, bool SPLIT>
+__global__ __launch_bounds__(256) void k_gemm_pipe(const bf16_t* __restrict__ A, int lda,
+                                                   const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
+                                                   int k_split, int m_tiles, int n_tiles, int splits,
+                                                   const int32_t* __restrict__ m_dev, GemmEpi ep, int F) {
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  constexpr int ROWS = BM + BN;                 // 128-byte rows per stage
+  constexpr int STAGE = ROWS * 64;              // bf16 elements per stage
+  constexpr int LPW = ROWS / 32;                // load instructions per wave per stage
+  static_assert(ROWS % 32 == 0, "stage rows must split over 4 waves x 8 rows");
+  static_assert(WM * WN == 4 && TM * WM * 16 == BM && TN * WN * 16 == BN, "wave grid must tile the block");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * STAGE];
+
+  const int total = m_tiles * n_tiles * splits;
+  const int per = (gridDim.x + 7) >> 3;
+  const int T = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (T >= total) return;
+  const int mt = T % m_tiles;
+  const int rest = T / m_tiles;
+  const int nt = rest % n_tiles;
+  const int sp = rest / n_tiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+  int Mr = M;
+  if (m_dev) Mr = min(Mr, *m_dev);
+  if (m0 >= Mr) return;
+  const int kb = sp * k_split;
+  const int nk = (min(K, kb + k_split) - kb) / GK;
+
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int wm = wid / WN, wn = wid % WN;
+
+  // this lane's global source row and k-chunk for each of its LPW load instructions
+  const bf16_t* src[LPW];
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = rbase + a * 16 + v;
-        if (m >= Mr) continue;
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const int n = cbase + b * 16;
-          if (n < N) P[(size_t)m * N + n] = acc[a][b][v];
-        }
-      }
-    return;
-  }
-  if (EPI == EPI_STORE || EPI == EPI_RESID) {
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = rbase + a * 16 + v;
-        if (m >= Mr) continue;
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const int n = cbase + b * 16;
-          if (n >= N) continue;
-          const size_t o = (size_t)m * ep.ldc + n;
-          ep.C[o] = (EPI == EPI_RESID ? ep.R[o] : 0.f) + acc[a][b][v];
-        }
-      }
-  } else if (EPI == EPI_SWIGLU) {
-    bf16_t* act = (bf16_t*)ep.act;
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = rbase + a * 16 + v;
-        if (m >= Mr) continue;
-#pragma unroll
-        for (int b = 0; b < TN; b += 2) {
-          const int n = cbase + b * 16;  // gate column (16-column group of even index)
-          if (n >= N) continue;
-          const int p = (n >> 5) * 16 + (n & 15);
-          const float g = acc[a][b][v], u = acc[a][b + 1][v];
-          act[(size_t)m * ep.ld_act + p] = from_f<bf16_t>(g / (1.0f + __expf(-g)) * u);
-        }
-      }
-  } else if (EPI == EPI_SOFTSTAT) {
-    __shared__ SoftStat red[WN][BM];
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rl = wm * TM * 16 + a * 16 + 4 * (lane >> 4) + v;
-        const int m = m0 + rl;
-        const int bt = (m < Mr && ep.btok) ? ep.btok[m] : -1;
-        const float bv = bt >= 0 ? ep.bval[m] : 0.f;
-        SoftStat s = softstat_empty();
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const int n = cbase + b * 16;
-          if (n < N) {
-            SoftStat e;
-            e.m = acc[a][b][v] + (n == bt ? bv : 0.f);
-            e.S = 1.f;
-            e.T = 0.f;
-            e.idx = n;
-            s = softstat_merge(s, e);
-          }
-        }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) s = softstat_merge(s, softstat_shfl_xor(s, o));
-        if ((lane & 15) == 0) red[wn][rl] = s;
-      }
-    __syncthreads();
-    for (int rl = tid; rl < BM; rl += 256) {
-      const int m = m0 + rl;
-      if (m >= Mr) continue;
-      SoftStat s = red[0][rl];
-#pragma unroll
-      for (int w = 1; w < WN; ++w) s = softstat_merge(s, red[w][rl]);
-      ep.part[(size_t)m * ep.n_tiles + nt] = s;
+  for (int j = 0; j < LPW; ++j) {
+    const int rho = (wid * LPW + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (rho & 7);
+    if (rho < BM) {
+      const int gm = m0 + rho;
+      src[j] = A + (size_t)(gm < Mr ? gm : 0) * lda + c * 8;
+    } else {
+      const int gn = n0 + rho - BM;
+      const int ok = gn < N ? gn : 0;
+      const int brow = (EPI == EPI_SWIGLU) ? swiglu_b_row(ok, F) : ok;
+      src[j] = B + (size_t)brow * ldb + c * 8;
     }
   }
+  auto issue = [&](int stage_k, int slot) {
+    bf16_t* base = smem + slot * STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + stage_k), LDS_PTR(base + (wid * LPW + j) * 8 * 64), 16,
+                                       0, 0);
+  };
+
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(kb + s * GK, s);
+
+  const int col = lane & 15, quad = lane >> 4;
+  for (int it = 0; it < nk; ++it) {
+    if (it + NS - 1 <= nk)
+      wait_vmcnt_le<(NS - 2) * LPW>();
+    else
+      wait_vmcnt_le<0>();
+    // Workgroup barrier without the release/acquire fence __syncthreads() carries (the fence
+    // would wait for every load in flight).  This wave's stage-`it` loads are complete (waitcnt
+    // above); after the barrier so are every other wave's, and all reads of the slot refilled
+    // below finished in the previous iteration.  The empty asm keeps the compiler from moving
+    // LDS accesses across the barrier.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (it + NS - 1 < nk) issue(kb + (it + NS - 1) * GK, (it + NS - 1) % NS);
+    const bf16_t* st = smem + (it % NS) * STAGE;
+    // all fragment reads of the stage first, so the second k-chunk's reads overlap the first
+    // chunk's matrix-core work
+    bf16x8_t af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int c = kc * 4 + quad;
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const int r = wm * TM * 16 + a * 16 + col;
+        af[kc][a] = *(const bf16x8_t*)&st[r * 64 + ((c ^ (r & 7)) << 3)];
+      }
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int r = BM + wn * TN * 16 + b * 16 + col;
+        bfr[kc][b] = *(const bf16x8_t*)&st[r * 64 + ((c ^ (r & 7)) << 3)];
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kc][a], bfr[kc][b], acc[a][b], 0, 0, 0);
+  }
+  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid);
+}
+
+// Weight-streaming variant for 65..256 rows: the four waves split the 256 rows (64 each) and all
+// read the same BN weight columns.  Only the shared weight tile goes through LDS (an NS-stage
+// ring of direct global->LDS loads); each wave fetches its own activation fragments straight into
+// registers in the matrix-core operand layout, two stages ahead (they hit L2: every column tile
+// of the GEMM re-reads the same <= 2 MB of activations).  LDS traffic per stage is the weight
+// tile written once and read by four waves.
+template <int BN, int NS, int EPI, bool SPLIT>
+__global__ __launch_bounds__(256) void k_gemm_adirect(const bf16_t* __restrict__ A, int lda,
+                                                      const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
+                                                      int k_split, int m_tiles, int n_tiles, int splits,
+                                                      const int32_t* __restrict__ m_dev, GemmEpi ep, int F) {
+  constexpr int BM = 256, WM = 4, WN = 1, TM = 4, TN = BN / 16;
+  constexpr int STAGE = BN * 64;      // bf16 elements per weight stage
+  constexpr int LPW = BN / 32;        // DMA instructions per wave per stage
+  constexpr int AL = 2 * TM;          // activation loads per lane per stage
+  static_assert(BN % 32 == 0 && NS >= 3, "tile");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * STAGE];
+
+  const int total = m_tiles * n_tiles * splits;
+  const int per = (gridDim.x + 7) >> 3;
+  const int T = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (T >= total) return;
+  const int mt = T % m_tiles;
+  const int rest = T / m_tiles;
+  const int nt = rest % n_tiles;
+  const int sp = rest / n_tiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+  int Mr = M;
+  if (m_dev) Mr = min(Mr, *m_dev);
+  if (m0 >= Mr) return;
+  const int kb = sp * k_split;
+  const int nk = (min(K, kb + k_split) - kb) / GK;
+
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, quad = lane >> 4;
+  const int wm = wid, wn = 0;
+
+  // weight rows this lane DMAs
+  const bf16_t* bsrc[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int rho = (wid * LPW + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (rho & 7);
+    const int gn = n0 + rho;
+    const int ok = gn < N ? gn : 0;
+    const int brow = (EPI == EPI_SWIGLU) ? swiglu_b_row(ok, F) : ok;
+    bsrc[j] = B + (size_t)brow * ldb + c * 8;
+  }
+  auto issue_b = [&](int stage_k, int slot) {
+    bf16_t* base = smem + slot * STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[j] + stage_k), LDS_PTR(base + (wid * LPW + j) * 8 * 64),
+                                       16, 0, 0);
+  };
+  // activation rows of this lane: m0 + 64 wid + 16 a + col, k offset quad * 8 within each 32-chunk
+  const bf16_t* asrc[TM];
+#pragma unroll
+  for (int a = 0; a < TM; ++a) {
+    const int gm = m0 + wid * 64 + a * 16 + col;
+    asrc[a] = A + (size_t)(gm < Mr ? gm : 0) * lda + quad * 8;
+  }
+  uint4 areg[2][AL];
+  auto issue_a = [&](int stage_k, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int a = 0; a < TM; ++a) areg[buf][kc * TM + a] = *(const uint4*)(asrc[a] + stage_k + kc * 32);
+  };
+
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+  // prologue: weights for stages 0..NS-2, activations for stages 0 and 1
+  if (nk > 0) issue_a(kb, std::integral_constant<int, 0>());
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue_b(kb + s * GK, s);
+  if (nk > 1) issue_a(kb + GK, std::integral_constant<int, 1>());
+
+  // One iteration; the activation register buffer is a compile-time index (the loop is unrolled
+  // by two) so the buffers stay in registers.
+  auto step = [&](int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    // In flight, in issue order: ..., A(it+1) [issued end of it-1], B(it+NS-2) ... ; stage `it`
+    // needs B(it) and A(it).  Everything issued after A(it) may stay outstanding: the weight
+    // stages it+1..it+NS-2 plus A(it+1) (issued after B(it) for it >= 1).
+    const int nb_after = min(NS - 2, nk - 1 - it);        // weight stages issued after B(it)
+    const bool a_next = it + 1 < nk;                       // A(it+1) issued after A(it)
+    if (nb_after == NS - 2 && a_next)
+      wait_vmcnt_le<(NS - 2) * LPW + AL>();
+    else if (a_next)
+      wait_vmcnt_le<AL>();
+    else
+      wait_vmcnt_le<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (it + NS - 1 < nk) issue_b(kb + (it + NS - 1) * GK, (it + NS - 1) % NS);
+    const bf16_t* st = smem + (it % NS) * STAGE;
+    bf16x8_t bfr[2][TN];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int c = kc * 4 + quad;
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int r = b * 16 + col;
+        bfr[kc][b] = *(const bf16x8_t*)&st[r * 64 + ((c ^ (r & 7)) << 3)];
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const bf16x8_t af = *(const bf16x8_t*)&areg[buf][kc * TM + a];
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[kc][b], acc[a][b], 0, 0, 0);
+      }
+    if (it + 2 < nk) issue_a(kb + (it + 2) * GK, bufc);
+  };
+  for (int it = 0; it < nk; it += 2) {
+    step(it, std::integral_constant<int, 0>());
+    if (it + 1 < nk) step(it + 1, std::integral_constant<int, 1>());
+  }
+  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid);
 }
 
 // Fixed-order sum of split-K partials [splits][M][N] followed by the epilogue.
@@ -252,6 +519,50 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int NS>
+static void run_pipe(int epi, bool split, dim3 grid, const bf16_t* A, int lda, const bf16_t* B, int ldb, int M,
+                     int N, int K, int k_split, int mt, int nt, int splits, const int32_t* m_dev, const GemmEpi& ep,
+                     int F, hipStream_t st) {
+#define GO(E, S)                                                                                               \
+  k_gemm_pipe<BM, BN, WM, WN, NS, E, S><<<grid, 256, 0, st>>>(A, lda, B, ldb, M, N, K, k_split, mt, nt, splits, \
+                                                              m_dev, ep, F)
+  if (split) {
+    if (epi == EPI_SWIGLU) GO(EPI_SWIGLU, true);
+    else GO(EPI_STORE, true);
+  } else if (epi == EPI_STORE) {
+    GO(EPI_STORE, false);
+  } else if (epi == EPI_RESID) {
+    GO(EPI_RESID, false);
+  } else if (epi == EPI_SWIGLU) {
+    GO(EPI_SWIGLU, false);
+  } else {
+    GO(EPI_SOFTSTAT, false);
+  }
+#undef GO
+}
+
+template <int BN, int NS>
+static void run_adirect(int epi, bool split, dim3 grid, const bf16_t* A, int lda, const bf16_t* B, int ldb, int M,
+                        int N, int K, int k_split, int mt, int nt, int splits, const int32_t* m_dev, const GemmEpi& ep,
+                        int F, hipStream_t st) {
+#define GO(E, S)                                                                                                  \
+  k_gemm_adirect<BN, NS, E, S><<<grid, 256, 0, st>>>(A, lda, B, ldb, M, N, K, k_split, mt, nt, splits, m_dev, ep, \
+                                                     F)
+  if (split) {
+    if (epi == EPI_SWIGLU) GO(EPI_SWIGLU, true);
+    else GO(EPI_STORE, true);
+  } else if (epi == EPI_STORE) {
+    GO(EPI_STORE, false);
+  } else if (epi == EPI_RESID) {
+    GO(EPI_RESID, false);
+  } else if (epi == EPI_SWIGLU) {
+    GO(EPI_SWIGLU, false);
+  } else {
+    GO(EPI_SOFTSTAT, false);
+  }
+#undef GO
+}
+
 template <int BM, int BN, int WM, int WN>
 static void run_tile(int epi, bool split, dim3 grid, const bf16_t* A, int lda, const bf16_t* B, int ldb, int M,
                      int N, int K, int k_split, int mt, int nt, int splits, const int32_t* m_dev, const GemmEpi& ep,
@@ -275,24 +586,74 @@ static void run_tile(int epi, bool split, dim3 grid, const bf16_t* A, int lda, c
 
 bool gemm_mfma_supported(int K, int lda, int ldb) { return K % GK == 0 && lda % 8 == 0 && ldb % 8 == 0 && K > 0; }
 
-int gemm_mfma_tile_n(int M) {
-  (void)M;
-  return 128;
+
+// Tile shapes (BM, BN, waves along M x N).
+struct TileCfg {
+  int bm, bn;
+};
+static const TileCfg kTiles[] = {{32, 128}, {64, 128}, {128, 128}, {256, 64}, {256, 128}, {128, 64}, {64, 64},
+                                 {128, 256},
+                                 // pipelined (LDS ring) variants
+                                 {128, 128}, {64, 128}, {32, 128}, {256, 64}, {64, 64}, {128, 64}, {256, 128},
+                                 {128, 256}, {256, 96}, {256, 128}, {128, 96},
+                                 // activations direct to registers, weights through the LDS ring
+                                 {256, 64}, {256, 96}, {256, 128}, {256, 96}};
+constexpr int kNumTiles = 23;
+
+// Measured choices (MI355X, bf16, K = 2048..12288): rows up to 48 stream the weights with the
+// 32-row pipelined tile; 49..384 rows use the 256-row tiles; more rows use the large tiles.
+// Returns the tile; *splits gets the split-K factor (0 = the generic rule).
+int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
+  *splits = 0;
+  if (M <= 48) {
+    if (epi == EPI_SWIGLU || epi == EPI_SOFTSTAT) {
+      *splits = 1;
+      return 10;
+    }
+    *splits = 4;
+    return N <= 4096 && K <= 4096 ? 12 : 10;
+  }
+  if (M <= 64) return 9;
+  if (M <= 384) {
+    if (epi == EPI_SWIGLU || epi == EPI_SOFTSTAT) {
+      *splits = 1;
+      return 16;
+    }
+    if (K > N) {  // FFN down projection
+      *splits = 4;
+      return 8;
+    }
+    *splits = 2;
+    return 18;
+  }
+  *splits = 1;
+  if (epi == EPI_STORE && N <= 8192) return 16;
+  return 17;
+}
+
+int gemm_mfma_softstat_bn(int M) {
+  int sp;
+  return kTiles[gemm_mfma_auto_tile(EPI_SOFTSTAT, M, 1, 1, &sp)].bn;
 }
 
 // Chooses the tile and split-K, then launches.  For SWIGLU, N = 2F (interleaved gate/up columns)
-// and the output has F columns.  part/part_floats: split-K scratch.
+// and the output has F columns.  part/part_floats: split-K scratch.  force_tile / force_splits
+// (>= 0 / > 0) override the choice.
 void launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                       const int32_t* m_dev, const GemmEpi& ep, int F, float* part, size_t part_floats,
-                      int force_splits, hipStream_t st) {
+                      int force_splits, hipStream_t st, int force_tile) {
   if (M <= 0 || N <= 0) return;
-  const int BM = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
-  const int BN = 128;
+  int auto_splits = 0;
+  const int tile = (force_tile >= 0 && force_tile < kNumTiles) ? force_tile : gemm_mfma_auto_tile(epi, M, N, K,
+                                                                                                  &auto_splits);
+  const int BM = kTiles[tile].bm, BN = kTiles[tile].bn;
   const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
   int splits = 1;
   if (epi != EPI_SOFTSTAT) {
     if (force_splits > 0) {
       splits = force_splits;
+    } else if (auto_splits > 0 && force_tile < 0) {
+      splits = auto_splits;
     } else {
       while (mt * nt * splits < 512 && (K / GK) % (splits * 2) == 0 && K / (splits * 2) >= 512 &&
              (size_t)(splits * 2) * M * N <= part_floats)
@@ -312,12 +673,40 @@ void launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, i
   }
   const bf16_t* a = (const bf16_t*)A;
   const bf16_t* b = (const bf16_t*)B;
-  if (BM == 32)
-    run_tile<32, 128, 1, 4>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, e, F, st);
-  else if (BM == 64)
-    run_tile<64, 128, 2, 2>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, e, F, st);
-  else
-    run_tile<128, 128, 2, 2>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, e, F, st);
+#define T(BM_, BN_, WM_, WN_) \
+  run_tile<BM_, BN_, WM_, WN_>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, e, F, st)
+  switch (tile) {
+    case 0: T(32, 128, 1, 4); break;
+    case 1: T(64, 128, 2, 2); break;
+    case 2: T(128, 128, 2, 2); break;
+    case 3: T(256, 64, 4, 1); break;
+    case 4: T(256, 128, 4, 1); break;
+    case 5: T(128, 64, 2, 2); break;
+    case 6: T(64, 64, 2, 2); break;
+    case 7: T(128, 256, 2, 2); break;
+#define P(BM_, BN_, WM_, WN_, NS_) \
+  run_pipe<BM_, BN_, WM_, WN_, NS_>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, e, F, st)
+    case 8: P(128, 128, 2, 2, 4); break;
+    case 9: P(64, 128, 2, 2, 4); break;
+    case 10: P(32, 128, 1, 4, 6); break;
+    case 11: P(256, 64, 4, 1, 3); break;
+    case 12: P(64, 64, 2, 2, 6); break;
+    case 13: P(128, 64, 2, 2, 4); break;
+    case 14: P(256, 128, 2, 2, 3); break;
+    case 15: P(128, 256, 2, 2, 3); break;
+    case 16: P(256, 96, 4, 1, 3); break;
+    case 17: P(256, 128, 4, 1, 3); break;
+    case 18: P(128, 96, 4, 1, 4); break;
+#undef P
+#define D(BN_, NS_) \
+  run_adirect<BN_, NS_>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, e, F, st)
+    case 19: D(64, 6); break;
+    case 20: D(96, 5); break;
+    case 21: D(128, 4); break;
+    default: D(96, 3); break;
+#undef D
+  }
+#undef T
   if (split) {
     const int NO = epi == EPI_SWIGLU ? N / 2 : N;
     const size_t n = (size_t)M * NO;
@@ -337,7 +726,7 @@ void launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, i
 
 extern "C" int alodlm_diag_gemm(int32_t epi, int32_t M, int32_t N, int32_t K, const void* A, const void* B, float* C,
                                 void* act, float* scratch, size_t scratch_floats, int32_t force_splits,
-                                int32_t force_generic, void* hip_stream) {
+                                int32_t force_generic, int32_t force_tile, void* hip_stream) {
   using namespace alodlm;
   if (M <= 0 || N <= 0 || K <= 0 || !A || !B) return -1;
   if (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_SWIGLU) return -1;
@@ -357,7 +746,7 @@ extern "C" int alodlm_diag_gemm(int32_t epi, int32_t M, int32_t N, int32_t K, co
     launch_gemm_generic(DT_BF16, epi, A, K, B, K, M, N, K, nullptr, ep, st);
   } else {
     launch_gemm_mfma(epi, A, K, B, K, M, N, K, nullptr, ep, N / 2, scratch, scratch ? scratch_floats : 0,
-                     force_splits, st);
+                     force_splits, st, force_tile);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

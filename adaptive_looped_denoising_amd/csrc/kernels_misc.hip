@@ -20,7 +20,36 @@ __global__ __launch_bounds__(256) void k_embed_rows(const int32_t* __restrict__ 
 
 // ---------------------------------------------------------------------------------------------
 // out[r] = x[src(r)] / sqrt(mean(x^2) + eps) * g ; optional ExitGate lambda = sigmoid(w . out + b)
-// computed on the fp32 normalised row.  Rows >= *n_dev (when given) are skipped.
+// computed on the fp32 normalised row.  Rows >= *n_dev (when given) are skipped.  The row stays
+// in registers between the two reductions (16-byte loads, d <= 256 * 4 * RMS_VEC).
+constexpr int RMS_VEC = 8;
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
+  uint2 w;
+  w.x = (uint32_t)from_f<bf16_t>(a) | ((uint32_t)from_f<bf16_t>(b) << 16);
+  w.y = (uint32_t)from_f<bf16_t>(c) | ((uint32_t)from_f<bf16_t>(d) << 16);
+  *(uint2*)p = w;
+}
+template <typename T>
+__device__ __forceinline__ float4 load4(const T* p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p) {
+  return *(const float4*)p;
+}
+template <>
+__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
+  const uint2 w = *(const uint2*)p;
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xFFFF0000u));
+}
+
 template <typename TG, typename TO>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int d,
                                                  const int32_t* __restrict__ rows,
@@ -32,19 +61,30 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
   if (n_dev && r >= *n_dev) return;
   const int src = rows ? rows[r] : r;
   const float* xr = x + (size_t)src * d;
+  float4 v[RMS_VEC];
   float ss = 0.f;
-  for (int e = threadIdx.x; e < d; e += 256) {
-    const float v = xr[e];
-    ss += v * v;
+#pragma unroll
+  for (int i = 0; i < RMS_VEC; ++i) {
+    const int e = (i * 256 + threadIdx.x) * 4;
+    v[i] = e < d ? *(const float4*)(xr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
   }
   ss = block_sum<256>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
   float dot = 0.f;
   TO* o = out + (size_t)r * d;
-  for (int e = threadIdx.x; e < d; e += 256) {
-    const float y = xr[e] * inv * to_f(g[e]);
-    o[e] = from_f<TO>(y);
-    if (exit_w) dot += y * to_f(exit_w[e]);
+#pragma unroll
+  for (int i = 0; i < RMS_VEC; ++i) {
+    const int e = (i * 256 + threadIdx.x) * 4;
+    if (e < d) {
+      const float4 gg = load4<TG>(g + e);
+      const float a = v[i].x * inv * gg.x, b = v[i].y * inv * gg.y, c = v[i].z * inv * gg.z, dd = v[i].w * inv * gg.w;
+      store4<TO>(o + e, a, b, c, dd);
+      if (exit_w) {
+        const float4 ww = load4<TG>(exit_w + e);
+        dot += a * ww.x + b * ww.y + c * ww.z + dd * ww.w;
+      }
+    }
   }
   if (exit_w) {
     dot = block_sum<256>(dot, red);

@@ -87,11 +87,12 @@ void launch_embed_committed(int dtype, const int8_t* cl, const int32_t* tokens, 
                             float* out, hipStream_t st);
 
 bool gemm_mfma_supported(int K, int lda, int ldb);
-// LM-head column tile of the matrix-core path (softmax statistics are kept per tile).
-constexpr int MFMA_TILE_N = 128;
+// Column-tile width the matrix-core dispatcher uses for a SOFTSTAT (LM-head) GEMM of M rows:
+// the softmax statistics are kept per column tile.
+int gemm_mfma_softstat_bn(int M);
 void launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                       const int32_t* m_dev, const GemmEpi& ep, int F, float* part, size_t part_floats,
-                      int force_splits, hipStream_t st);
+                      int force_splits, hipStream_t st, int force_tile = -1);
 void launch_gemm_generic(int dtype, int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                          const int32_t* m_dev, const GemmEpi& ep, hipStream_t st);
 void launch_attn_generic(int dtype, const AttnParams& p, hipStream_t st);

@@ -47,7 +47,8 @@ int check_config(const alodlm_config* c, std::string* err) {
   if (!c) return bad("null config");
   if (c->dtype != ALODLM_DTYPE_BF16 && c->dtype != ALODLM_DTYPE_FP32) return bad("dtype");
   if (c->vocab < 2) return bad("vocab < 2");
-  if (c->d_model < 64 || c->d_model % 64) return bad("d_model must be a positive multiple of 64");
+  if (c->d_model < 64 || c->d_model % 64 || c->d_model > 8192)
+    return bad("d_model must be a multiple of 64 in 64..8192");
   if (c->ffn < 64 || c->ffn % 64) return bad("ffn must be a positive multiple of 64");
   if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 32, 64 or 128");
   if (c->n_kv_heads < 1 || c->n_q_heads < c->n_kv_heads || c->n_q_heads % c->n_kv_heads)
@@ -238,10 +239,11 @@ void gemm(alodlm_ctx* c, int epi, const void* A, int lda, const void* B, int ldb
   launch_gemm_generic(dt(c), epi, A, lda, B, ldb, M, N, K, m_dev, ep, c->st);
 }
 
-// Column tiles of the LM-head softmax statistics for the path the readout takes.
-int lm_tiles(const alodlm_ctx* c) {
+// Column tiles of the LM-head softmax statistics for the path a readout of M rows takes.
+int lm_tiles(const alodlm_ctx* c, int M) {
   const int d = c->cfg.d_model;
-  return use_mfma(c, d, d, d) ? (c->cfg.vocab + MFMA_TILE_N - 1) / MFMA_TILE_N : (c->cfg.vocab + 63) / 64;
+  const int bn = use_mfma(c, d, d, d) ? gemm_mfma_softstat_bn(M) : 64;
+  return (c->cfg.vocab + bn - 1) / bn;
 }
 
 void attention(alodlm_ctx* c, const AttnParams& p) {
@@ -394,7 +396,7 @@ void readout_heads(alodlm_ctx* c, const void* rows, int n_upper, const int32_t* 
   const Plan& p = c->plan;
   GemmEpi ep;
   ep.part = c->at<SoftStat>(p.part);
-  ep.n_tiles = lm_tiles(c);
+  ep.n_tiles = lm_tiles(c, n_upper);
   ep.btok = btok;
   ep.bval = bval;
   gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_upper, g.vocab, g.d_model, n_dev, ep);
@@ -723,7 +725,7 @@ int alodlm_readout_commit(alodlm_ctx* c, const void* rows, int32_t n_rows, int32
   // LMHead over the given rows (row order = readout order)
   GemmEpi ep;
   ep.part = c->at<SoftStat>(p.part);
-  ep.n_tiles = lm_tiles(c);
+  ep.n_tiles = lm_tiles(c, n_rows);
   ep.btok = boost_tok;
   ep.bval = boost_val;
   gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_rows, g.vocab, g.d_model, nullptr, ep);

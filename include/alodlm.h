@@ -60,7 +60,7 @@ extern "C" {
 /* Model and capacity description. */
 typedef struct alodlm_config {
   int32_t vocab;        /* V */
-  int32_t d_model;      /* d, multiple of 64 */
+  int32_t d_model;      /* d, multiple of 64, at most 8192 */
   int32_t n_q_heads;    /* Hq, multiple of n_kv_heads */
   int32_t n_kv_heads;   /* Hkv */
   int32_t head_dim;     /* hd: 32, 64 or 128 */

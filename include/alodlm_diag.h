@@ -23,13 +23,14 @@ extern "C" {
 /* bf16 A [M][K], B [N][K] (N = 2F for SWIGLU).  scratch: device fp32 buffer of
  * scratch_floats for split-K partials (force_splits > 1 needs splits*M*N floats).
  * force_splits: 0 = the dispatcher's choice.  force_generic != 0 runs the vector-ALU
- * kernel instead of the matrix-core one.  Asynchronous.  Returns 0 or -1 (bad
+ * kernel instead of the matrix-core one.  force_tile: -1 = the dispatcher's tile choice, else a
+ * tile index of the matrix-core kernel (0..7; out of range = the dispatcher's choice).  Asynchronous.  Returns 0 or -1 (bad
  * arguments, checked before any launch), -4 (launch failed). */
 __attribute__((visibility("default"))) int alodlm_diag_gemm(int32_t epi, int32_t M, int32_t N, int32_t K,
                                                             const void* A, const void* B, float* C, void* act,
                                                             float* scratch, size_t scratch_floats,
                                                             int32_t force_splits, int32_t force_generic,
-                                                            void* hip_stream);
+                                                            int32_t force_tile, void* hip_stream);
 
 /* Kernel classes timed by alodlm_diag_timing_*. */
 #define ALODLM_K_GEMM_GATE_UP 0 /* FFN gate/up GEMM with the fused SwiGLU epilogue */

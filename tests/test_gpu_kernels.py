@@ -20,14 +20,14 @@ def _bf16(shape, seed, scale=1.0):
     return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16)
 
 
-def _gemm(epi, A, Bm, C=None, act=None, splits=0, generic=0):
+def _gemm(epi, A, Bm, C=None, act=None, splits=0, generic=0, tile=-1):
     from adaptive_looped_denoising_amd import binding as B
     M, K = A.shape
     N = Bm.shape[0]
     scratch = torch.empty(max(8 * M * N, 1), dtype=torch.float32, device="cuda")
     B.diag_gemm(epi, M, N, K, A.data_ptr(), Bm.data_ptr(), 0 if C is None else C.data_ptr(),
                 0 if act is None else act.data_ptr(), scratch.data_ptr(), scratch.numel(), splits, generic,
-                torch.cuda.current_stream().cuda_stream)
+                torch.cuda.current_stream().cuda_stream, tile)
     torch.cuda.synchronize()
 
 
@@ -50,6 +50,25 @@ def test_gemm_store_and_resid(gpu_lib, M, N, K):
     _gemm(1, A.cuda(), Bm.cuda(), C=C1)
     err = np.abs(C1.cpu().numpy() - (C0.cpu().double().numpy() + ref)).max() / scale
     assert err < 2e-5, err
+
+
+@pytest.mark.parametrize("tile", range(23))
+def test_gemm_every_tile(gpu_lib, tile):
+    M, N, K = 300, 1024, 1024
+    A, Bm = _bf16((M, K), 10), _bf16((N, K), 11, 0.02)
+    ref = _ref(A, Bm)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    _gemm(0, A.cuda(), Bm.cuda(), C=C, tile=tile)
+    assert np.abs(C.cpu().numpy() - ref).max() / (np.sqrt(K) * 0.02) < 2e-5
+    F = 512
+    Bg = _bf16((2 * F, K), 12, 0.05)
+    act = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    _gemm(3, A.cuda(), Bg.cuda(), act=act, tile=tile)
+    gu = _ref(A, Bg)
+    g, u = gu[:, :F], gu[:, F:]
+    refa = g / (1 + np.exp(-g)) * u
+    err = np.abs(act.cpu().float().numpy() - refa) / (np.abs(refa) + 1e-2 * np.abs(refa).max())
+    assert err.max() < 1.6e-2
 
 
 @pytest.mark.parametrize("splits", [2, 4, 8])
