@@ -19,7 +19,7 @@ STEP_TEACHER_FORCED = 1
 EXPORTS = ("alodlm_workspace_bytes", "alodlm_kv_slots", "alodlm_create", "alodlm_prefill_kv",
            "alodlm_prefill_kv_synthetic", "alodlm_denoise_step", "alodlm_readout_commit",
            "alodlm_last_step_stats", "alodlm_last_error", "alodlm_destroy", "alodlm_synth_fill",
-           "alodlm_diag_gemm", "alodlm_diag_timing_enable", "alodlm_diag_timing_read")
+           "alodlm_diag_gemm", "alodlm_diag_timing_enable", "alodlm_diag_timing_read", "alodlm_diag_read_kv", "alodlm_diag_buffer_offset")
 K_CLASSES = ("gemm_gate_up", "gemm_qkv", "gemm_o", "gemm_down", "attention", "lm_head", "norm_rope", "control")
 
 
@@ -90,9 +90,12 @@ def load(path: str = LIB_PATH):
     lib.alodlm_diag_gemm.argtypes = [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_int32, c_int32, c_int32, c_void_p]
     lib.alodlm_diag_timing_enable.argtypes = [c_void_p, c_int32]
+    lib.alodlm_diag_buffer_offset.argtypes = [c_void_p, ctypes.c_char_p]
+    lib.alodlm_diag_buffer_offset.restype = c_int64
+    lib.alodlm_diag_read_kv.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]
     lib.alodlm_diag_timing_read.argtypes = [c_void_p, c_int32, POINTER(ctypes.c_double), POINTER(c_int64)]
     for name in EXPORTS:
-        if name not in ("alodlm_last_error", "alodlm_destroy"):
+        if name not in ("alodlm_last_error", "alodlm_destroy", "alodlm_diag_buffer_offset"):
             getattr(lib, name).restype = c_int32
     _lib = lib
     return lib
@@ -187,3 +190,13 @@ def timing_read(ctx: int) -> dict:
         _check(load().alodlm_diag_timing_read(c_void_p(ctx), k, ctypes.byref(ms), ctypes.byref(n)), c_void_p(ctx))
         out[name] = (ms.value, n.value)
     return out
+
+
+def read_kv(ctx: int, slot: int, b: int, j0: int, n: int, dst_k_ptr: int, dst_v_ptr: int):
+    rc = load().alodlm_diag_read_kv(c_void_p(ctx), slot, b, j0, n, c_void_p(dst_k_ptr), c_void_p(dst_v_ptr))
+    if rc != 0:
+        raise AlodlmError(rc, "alodlm_diag_read_kv failed")
+
+
+def buffer_offset(ctx: int, name: str) -> int:
+    return load().alodlm_diag_buffer_offset(c_void_p(ctx), name.encode())

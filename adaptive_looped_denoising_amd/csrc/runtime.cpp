@@ -756,6 +756,37 @@ int alodlm_diag_timing_read(const alodlm_ctx* c, int32_t kernel_class, double* m
   return ALODLM_OK;
 }
 
+int alodlm_diag_read_kv(const alodlm_ctx* c, int32_t slot, int32_t b, int32_t j0, int32_t n, void* dst_k,
+                        void* dst_v) {
+  if (!c || !dst_k || !dst_v) return ALODLM_EINVAL;
+  const alodlm_config& g = c->cfg;
+  if (slot < 0 || slot >= c->plan.n_slots || b < 0 || b >= g.max_batch || j0 < 0 || n < 0 ||
+      j0 + n > g.max_prefix)
+    return ALODLM_EINVAL;
+  const size_t es = esize(g.dtype), hd = g.head_dim;
+  for (int v = 0; v < 2; ++v) {
+    const char* base = c->ws + (v ? c->plan.vcache : c->plan.kcache) + es * (size_t)c->plan.slot_elems * slot;
+    for (int h = 0; h < g.n_kv_heads; ++h) {
+      const char* src = base + es * (((size_t)b * g.n_kv_heads + h) * g.max_prefix + j0) * hd;
+      char* dst = (char*)(v ? dst_v : dst_k) + es * (size_t)h * n * hd;
+      if (hipMemcpyAsync(dst, src, es * n * hd, hipMemcpyDeviceToDevice, c->st) != hipSuccess) return ALODLM_EHIP;
+    }
+  }
+  return ALODLM_OK;
+}
+
+int64_t alodlm_diag_buffer_offset(const alodlm_ctx* c, const char* name) {
+  if (!c || !name) return -1;
+  const Plan& p = c->plan;
+  const struct {
+    const char* n;
+    size_t off;
+  } tab[] = {{"h", p.h}, {"xn", p.xn}, {"attn", p.attn}, {"q", p.q}, {"qkv", p.qkv}, {"act", p.act}, {"r", p.r}};
+  for (const auto& t : tab)
+    if (!strcmp(t.n, name)) return (int64_t)t.off;
+  return -1;
+}
+
 int alodlm_last_step_stats(const alodlm_ctx* c, int64_t* layer_calls, int32_t* loops_run) {
   if (!c) return ALODLM_EINVAL;
   if (layer_calls) *layer_calls = c->layer_calls;

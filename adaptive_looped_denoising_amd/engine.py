@@ -188,6 +188,15 @@ class Engine:
             res.hidden = self._hidden.cpu().numpy()
         return res
 
+    def read_kv(self, slot: int, b: int, j0: int, n: int):
+        """K and V rows of one cache slot and sequence, as float32 numpy arrays [Hkv][n][hd]."""
+        D = self.w.dims
+        k = torch.empty((D.n_kv_heads, n, D.head_dim), dtype=self.tdtype, device=self.device)
+        v = torch.empty_like(k)
+        B.read_kv(self.ctx, slot, b, j0, n, k.data_ptr(), v.data_ptr())
+        torch.cuda.synchronize(self.device)
+        return k.float().cpu().numpy(), v.float().cpu().numpy()
+
     def stats(self):
         return B.last_step_stats(self.ctx)
 

@@ -32,6 +32,18 @@ __attribute__((visibility("default"))) int alodlm_diag_gemm(int32_t epi, int32_t
                                                             int32_t force_splits, int32_t force_generic,
                                                             int32_t force_tile, void* hip_stream);
 
+/* Copies prefix-cache rows back for inspection: K and V of cache slot `slot`, sequence b,
+ * positions j0 .. j0+n-1, every kv head, into dst_k / dst_v (device, config dtype,
+ * [Hkv][n][hd]).  Asynchronous on the context stream.  Returns 0, -1 (bad arguments). */
+__attribute__((visibility("default"))) int alodlm_diag_read_kv(const struct alodlm_ctx* ctx, int32_t slot, int32_t b,
+                                                               int32_t j0, int32_t n, void* dst_k, void* dst_v);
+
+/* Byte offset, within the workspace, of an internal activation buffer, for inspection after a
+ * call: "h" (fp32 residual rows), "xn" (normalised rows), "attn" (attention output), "q",
+ * "qkv" (fp32 projection), "act" (SwiGLU output), "r" (readout rows).  -1 if unknown. */
+__attribute__((visibility("default"))) int64_t alodlm_diag_buffer_offset(const struct alodlm_ctx* ctx,
+                                                                         const char* name);
+
 /* Kernel classes timed by alodlm_diag_timing_*. */
 #define ALODLM_K_GEMM_GATE_UP 0 /* FFN gate/up GEMM with the fused SwiGLU epilogue */
 #define ALODLM_K_GEMM_QKV 1

@@ -59,6 +59,19 @@ def _f64(a) -> np.ndarray:
     return np.asarray(a, dtype=F64)
 
 
+def round_bf16(x) -> np.ndarray:
+    """Round to bfloat16 the way an fp32 pipeline does: to float32 first, then to the nearest
+    bfloat16 (ties to even); returned as float64."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _rnd(x, prec):
+    return round_bf16(x) if prec == "bf16" else x
+
+
 def matmul_t(x: np.ndarray, w: np.ndarray, chunk: int = 16384) -> np.ndarray:
     """x @ w.T in float64 (w stored [out][in]); converted in row chunks of w to bound memory."""
     x = _f64(x)
@@ -120,25 +133,29 @@ def silu(x) -> np.ndarray:
 
 
 def layer_forward(x, W: Dict[str, np.ndarray], li: int, dims, eps: float, theta: float, pos,
-                  ctx_k=None, ctx_v=None, causal: bool = False):
+                  ctx_k=None, ctx_v=None, causal: bool = False, prec=None):
     """One Qwen3-style block over the n rows ``x`` [n][d] of one sequence.
 
     ctx_k / ctx_v [Hkv][m][hd]: cached (post-RoPE) keys and values that every
     row sees in addition to the rows' own keys.  ``causal`` restricts the rows'
     own keys to positions <= the query's.  Returns (new x, k, v) where k and v
     [Hkv][n][hd] are this call's post-RoPE keys and values of the rows.
+
+    ``prec="bf16"`` rounds to bfloat16 where a bf16 pipeline stores values: the
+    normalised inputs of the projections, q / k / v, the attention output and the
+    SwiGLU output (the residual stream stays exact).  Default: exact arithmetic.
     """
     p = "layers.%d." % li
     x = _f64(x)
     n = x.shape[0]
     Hq, Hkv, hd, F = dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn
-    h1 = rms_norm(x, W[p + "attn_norm"], eps)
+    h1 = _rnd(rms_norm(x, W[p + "attn_norm"], eps), prec)
     qkv = matmul_t(h1, W[p + "wqkv"])
     q = qkv[:, : Hq * hd].reshape(n, Hq, hd).transpose(1, 0, 2)
     k = qkv[:, Hq * hd: (Hq + Hkv) * hd].reshape(n, Hkv, hd).transpose(1, 0, 2)
-    v = qkv[:, (Hq + Hkv) * hd:].reshape(n, Hkv, hd).transpose(1, 0, 2)
-    q = rope(rms_norm(q, W[p + "q_norm"], eps), pos, theta)
-    k = rope(rms_norm(k, W[p + "k_norm"], eps), pos, theta)
+    v = _rnd(qkv[:, (Hq + Hkv) * hd:].reshape(n, Hkv, hd).transpose(1, 0, 2), prec)
+    q = _rnd(rope(rms_norm(q, W[p + "q_norm"], eps), pos, theta), prec)
+    k = _rnd(rope(rms_norm(k, W[p + "k_norm"], eps), pos, theta), prec)
     m = 0 if ctx_k is None else ctx_k.shape[1]
     keys = k if ctx_k is None else np.concatenate([_f64(ctx_k), k], axis=1)
     vals = v if ctx_v is None else np.concatenate([_f64(ctx_v), v], axis=1)
@@ -146,11 +163,11 @@ def layer_forward(x, W: Dict[str, np.ndarray], li: int, dims, eps: float, theta:
     if causal:
         allowed = np.ones((n, m + n), dtype=bool)
         allowed[:, m:] = np.tril(np.ones((n, n), dtype=bool))
-    a = attention(q, keys, vals, allowed).transpose(1, 0, 2).reshape(n, Hq * hd)
+    a = _rnd(attention(q, keys, vals, allowed).transpose(1, 0, 2).reshape(n, Hq * hd), prec)
     x = x + matmul_t(a, W[p + "wo"])
-    h2 = rms_norm(x, W[p + "ffn_norm"], eps)
+    h2 = _rnd(rms_norm(x, W[p + "ffn_norm"], eps), prec)
     gu = matmul_t(h2, W[p + "w_gate_up"])
-    x = x + matmul_t(silu(gu[:, :F]) * gu[:, F:], W[p + "w_down"])
+    x = x + matmul_t(_rnd(silu(gu[:, :F]) * gu[:, F:], prec), W[p + "w_down"])
     return x, k, v
 
 
@@ -166,25 +183,31 @@ def kv_slot(dims, k_max: int, layer: int, depth: int = 1) -> int:
     return dims.n_pre + dims.n_core * k_max + (layer - dims.n_pre - dims.n_core)
 
 
-def prefill_sequence(ids, W, dims, k_max: int, eps: float, theta: float) -> Dict[int, tuple]:
-    """Depth-aware cache of one prefix: slot -> (K, V) [Hkv][P][hd] (causal prefix)."""
+def prefill_sequence(ids, W, dims, k_max: int, eps: float, theta: float, progress=None,
+                     prec=None) -> Dict[int, tuple]:
+    """Depth-aware cache of one prefix: slot -> (K, V) [Hkv][P][hd] (causal prefix).
+    ``progress`` (optional) is called with a short text after every layer call."""
     ids = np.asarray(ids)
     P = ids.shape[0]
     pos = np.arange(P)
     cache = {}
     x = _f64(W["embed"][ids])
+
+    def run(li, slot):
+        nonlocal x
+        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True, prec=prec)
+        cache[slot] = (k, v)
+        if progress is not None:
+            progress("prefill layer %d -> slot %d" % (li, slot))
+
     for li in range(dims.n_pre):
-        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True)
-        cache[kv_slot(dims, k_max, li)] = (k, v)
+        run(li, kv_slot(dims, k_max, li))
     for depth in range(1, k_max + 1):
         for c in range(dims.n_core):
-            li = dims.n_pre + c
-            x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True)
-            cache[kv_slot(dims, k_max, li, depth)] = (k, v)
+            run(dims.n_pre + c, kv_slot(dims, k_max, dims.n_pre + c, depth))
     for c in range(dims.n_coda):
         li = dims.n_pre + dims.n_core + c
-        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True)
-        cache[kv_slot(dims, k_max, li)] = (k, v)
+        run(li, kv_slot(dims, k_max, li))
     return cache
 
 
@@ -250,13 +273,16 @@ def exit_gate(r, w, b: float) -> np.ndarray:
 def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loops: int, eps: float,
                           theta: float, tau_ent: float, tau_halt: float, mask_id: int, exit_b: float,
                           boost_tok=None, boost_val=None, teacher: Optional[dict] = None,
-                          record_hidden: bool = False, counter: Optional[list] = None) -> dict:
+                          record_hidden: bool = False, counter: Optional[list] = None, progress=None,
+                          prec=None) -> dict:
     """One inner loop of Algorithm 1 of the summary page (one denoising step), for one sequence.
 
     ``cache``: slot -> (K, V) [Hkv][P][hd]; ``avail``: deepest cached Core depth
     per prefix position (None = k_max).  ``teacher`` (optional) replaces the
     decisions by given ones: {"commit_loop": [L], "tokens": [L], "stop_loop": int}.
-    ``counter`` (optional list) receives one entry per layer call.
+    ``counter`` (optional list) receives one entry per layer call; ``progress`` (optional) is
+    called with a short text after every layer call.  ``prec`` as in layer_forward (the
+    readout rows feeding the LMHead are rounded too; the ExitGate reads them exactly).
     """
     block_ids = np.asarray(block_ids, dtype=np.int64)
     L = block_ids.shape[0]
@@ -270,7 +296,9 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
             ck, cv = context_for(cache, dims, k_max, li, loop, avail)
         else:
             ck = cv = None
-        y, _, _ = layer_forward(x, W, li, dims, eps, theta, pos, ck, cv, causal=False)
+        y, _, _ = layer_forward(x, W, li, dims, eps, theta, pos, ck, cv, causal=False, prec=prec)
+        if progress is not None:
+            progress("step loop %d layer %d" % (loop, li))
         return y
 
     # start of the step: unresolved set, initial loop state, a = 0, C empty
@@ -306,7 +334,7 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
         if rows.size:
             bt = None if boost_tok is None else np.asarray(boost_tok)[rows]
             bv = None if boost_val is None else np.asarray(boost_val)[rows]
-            H[rows], tok[rows], lse[rows], gap[rows] = readout(r[rows], W["lm_head"], bt, bv)
+            H[rows], tok[rows], lse[rows], gap[rows] = readout(_rnd(r[rows], prec), W["lm_head"], bt, bv)
             lam[rows] = exit_gate(r[rows], W["exit_w"], exit_b)
         # cumulative halting for the positions unresolved at loop start
         a[rows] = a[rows] + (1.0 - a[rows]) * lam[rows]

@@ -18,7 +18,7 @@ def weights(w: synth.Workload, names: Optional[List[str]] = None) -> Dict[str, n
     return {k: synth.as_f32(v) for k, v in synth.host_weights(w, names).items()}
 
 
-def cache_for(w: synth.Workload, W, b: int, prefix_ids=None) -> Dict[int, tuple]:
+def cache_for(w: synth.Workload, W, b: int, prefix_ids=None, progress=None, prec=None) -> Dict[int, tuple]:
     """Depth-aware prefix cache of sequence b: computed by the oracle's prefill, or the
     workload's synthetic K/V."""
     if w.prefix == 0:
@@ -30,13 +30,15 @@ def cache_for(w: synth.Workload, W, b: int, prefix_ids=None) -> Dict[int, tuple]
             out[slot] = (synth.as_f32(K), synth.as_f32(V))
         return out
     ids = synth.prefix_ids(w) if prefix_ids is None else prefix_ids
-    return orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+    return orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, progress=progress, prec=prec)
 
 
 def step(w: synth.Workload, W=None, seqs=None, k_loops: Optional[int] = None, teacher=None,
          record_hidden: bool = False, block_ids=None, boost=None, avail=None, caches=None,
-         exit_b: Optional[float] = None, counter: Optional[list] = None) -> List[dict]:
-    """Oracle denoising step for the listed sequences of the workload."""
+         exit_b: Optional[float] = None, counter: Optional[list] = None, progress=None,
+         prec=None) -> List[dict]:
+    """Oracle denoising step for the listed sequences of the workload (``prec`` as in
+    alodlm_oracle.layer_forward)."""
     W = weights(w) if W is None else W
     seqs = range(w.batch) if seqs is None else seqs
     bids = synth.block_ids(w) if block_ids is None else block_ids
@@ -45,13 +47,14 @@ def step(w: synth.Workload, W=None, seqs=None, k_loops: Optional[int] = None, te
     pids = synth.prefix_ids(w) if (w.kv == "prefill" and w.prefix) else None
     out = []
     for b in seqs:
-        cache = caches[b] if caches is not None else cache_for(w, W, b, pids)
+        cache = caches[b] if caches is not None else cache_for(w, W, b, pids, progress, prec)
         res = orc.denoise_step_sequence(
             bids[b], cache, av[b] if av is not None and w.prefix else None, W, w.dims,
             k_max=w.k_max, k_loops=w.k_max if k_loops is None else k_loops, eps=w.rms_eps,
             theta=w.rope_theta, tau_ent=w.tau_ent, tau_halt=w.tau_halt, mask_id=w.mask_id,
             exit_b=w.exit_bias() if exit_b is None else exit_b, boost_tok=btok[b], boost_val=bval[b],
-            teacher=None if teacher is None else teacher[b], record_hidden=record_hidden, counter=counter)
+            teacher=None if teacher is None else teacher[b], record_hidden=record_hidden, counter=counter,
+            progress=progress, prec=prec)
         res["seq"] = b
         out.append(res)
     return out

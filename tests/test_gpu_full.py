@@ -1,0 +1,166 @@
+"""GPU parity at the full workload sizes (1.7B shape, 8B shape, 8B long context), in the launch
+configuration the benchmark times, against the fp64 oracle on sampled outputs:
+
+* prefill: causal attention makes the first positions of the depth-aware cache depend on those
+  positions only, so the oracle recomputes them exactly from the token ids;
+* step: sequences are independent (per-sequence halting), so the oracle recomputes whole
+  sequences of the batch over the seeded synthetic cache.
+"""
+import gc
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from adaptive_looped_denoising_amd import synth
+from oracle import alodlm_oracle as orc
+from oracle import run as orun
+from tests.parity import (CAL_FACTOR, calibrated_tolerances, compare_decisions, compare_records, log, rel_rows,
+                          tol_hidden)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+_W_CACHE = {}
+
+
+def _oracle_weights(w):
+    key = (w.dims, w.seed, w.dtype)
+    if key not in _W_CACHE:
+        _W_CACHE.clear()
+        gc.collect()
+        log("generating host weights for %s" % w.name)
+        _W_CACHE[key] = orun.weights(w)
+    return _W_CACHE[key]
+
+
+def _engine(w):
+    from adaptive_looped_denoising_amd.engine import Engine
+    gc.collect()
+    torch.cuda.empty_cache()
+    e = Engine(w)
+    e.prefill()
+    return e
+
+
+def _slot_errors(e, w, b, n_pos, cache):
+    errs = []
+    for slot in range(w.dims.kv_slots(w.k_max)):
+        gk, gv = e.read_kv(slot, b, 0, n_pos)
+        ok_, ov = cache[slot]
+        e_slot = 0.0
+        for g, o in ((gk, ok_), (gv, ov)):
+            err = rel_rows(g.reshape(-1, w.dims.head_dim), np.asarray(o).reshape(-1, w.dims.head_dim))
+            e_slot = max(e_slot, float(err.max()))
+        errs.append(e_slot)
+    return errs
+
+
+def _layer_depth(w, slot):
+    """Layer calls the prefix has gone through when it produces the K/V of a cache slot."""
+    D = w.dims
+    if slot < D.n_pre:
+        return slot + 1
+    if slot < D.n_pre + D.n_core * w.k_max:
+        c, dpt = divmod(slot - D.n_pre, w.k_max)
+        return D.n_pre + dpt * D.n_core + c + 1
+    return D.n_pre + w.k_max * D.n_core + (slot - D.n_pre - D.n_core * w.k_max) + 1
+
+
+def _check_prefill_prefix(w, n_pos, seqs):
+    """GPU prefill over the full prefix vs the oracle's prefill of the first n_pos tokens:
+    within the bf16 tolerance of the oracle at the pipeline's rounding points, and within a
+    random-walk bound of the exact oracle (first-layer deviation e1 growing as sqrt(depth), x2)."""
+    e = _engine(w)
+    W = _oracle_weights(w)
+    ids = synth.prefix_ids(w)
+    for b in seqs:
+        log("oracle prefill of the first %d positions of sequence %d" % (n_pos, b))
+        c64 = orc.prefill_sequence(ids[b][:n_pos], W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+        e64 = _slot_errors(e, w, b, n_pos, c64)
+        log("seq %d per-slot worst row error: %s" % (b, " ".join("%.4f" % x for x in e64)))
+        c16 = orc.prefill_sequence(ids[b][:n_pos], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, prec="bf16")
+        drift = []
+        for slot in range(len(e64)):
+            d_ = 0.0
+            for o16, o64 in zip(c16[slot], c64[slot]):
+                d_ = max(d_, float(rel_rows(np.asarray(o16).reshape(-1, w.dims.head_dim),
+                                            np.asarray(o64).reshape(-1, w.dims.head_dim)).max()))
+            drift.append(d_)
+        log("seq %d per-slot bf16 drift of the oracle: %s" % (b, " ".join("%.4f" % x for x in drift)))
+        bound = [max(tol_hidden(w.dtype, _layer_depth(w, s)), CAL_FACTOR * drift[s]) for s in range(len(e64))]
+        bad = [i for i, (x, y) in enumerate(zip(e64, bound)) if x > y]
+        assert not bad, "seq %d slots %s beyond the depth tolerance" % (b, bad)
+        log("seq %d worst error / tolerance over slots: %.2f" % (b, max(x / y for x, y in zip(e64, bound))))
+    e.close()
+
+
+def _check_step(w, seqs):
+    e = _engine(w)
+    W = _oracle_weights(w)
+    log("case %s B=%d P=%d L=%d K=%d tau=%.2f q=%.2f, oracle on sequences %s" % (
+        w.name, w.batch, w.prefix, w.block, w.k_max, w.tau_ent, w.tau_halt, list(seqs)))
+    free = e.step(records=True, hidden=True)
+    caches = {}
+    for b in seqs:
+        caches[b] = orun.cache_for(w, W, b)
+    ores = orun.step(w, W=W, seqs=seqs, record_hidden=True, caches=caches,
+                     progress=lambda m: print(m, flush=True) if m.endswith(" 0") else None)
+    o16 = orun.step(w, W=W, seqs=seqs, record_hidden=True, caches=caches, prec="bf16",
+                    teacher=orun.teacher_from(ores))
+    tols = calibrated_tolerances(w, ores, o16)
+    log("tolerances per (sequence, loop): %s" % {k: {n: round(v, 4) for n, v in t.items()} for k, t in tols.items()})
+    flagged = compare_decisions(w, ores, free, tols)
+    clean = [r for r in ores if r["seq"] not in flagged]
+    if clean:
+        log("free run worst errors: %s" % compare_records(w, clean, free, tols=tols))
+    teacher = orun.teacher_from(ores)
+    for b in range(w.batch):   # sequences the oracle did not run keep their own decisions
+        if b not in teacher:
+            teacher[b] = dict(commit_loop=free.commit_loop[b], tokens=free.tokens[b], stop_loop=free.loops[b])
+    tf = e.step(records=True, hidden=True, teacher=teacher)
+    log("teacher-forced worst errors: %s" % compare_records(w, ores, tf, tols=tols))
+    for r in ores:
+        b = r["seq"]
+        assert np.array_equal(tf.commit_loop[b], r["commit_loop"]) and tf.loops[b] == r["loops"]
+    log("GPU commits per sequence %s, loops %s" % ((free.commit_loop != 0).sum(axis=1).tolist(),
+                                                   free.loops.tolist()))
+    return e, ores, free
+
+
+def test_qwen3_1p7b_prefill_first_positions(gpu_lib):
+    _check_prefill_prefix(synth.workload("qwen3_1p7b"), 16, [0])
+
+
+def test_qwen3_1p7b_step(gpu_lib):
+    w = synth.workload("qwen3_1p7b", kv="synthetic")
+    e, _, _ = _check_step(w, [0])
+    e.close()
+
+
+def test_qwen3_8b_prefill_first_positions(gpu_lib):
+    _check_prefill_prefix(synth.workload("qwen3_8b"), 8, [0, 5])
+
+
+def test_qwen3_8b_step_sampled_sequences(gpu_lib):
+    w = synth.workload("qwen3_8b", kv="synthetic")
+    e, _, _ = _check_step(w, [0, 7])
+    # structural pin: with entropy commits and halting off the 8B split runs 10 + 4 x (16 + 10) layers
+    e.step(tau_ent=-1.0, tau_halt=2.0)
+    calls, loops = e.stats()
+    assert loops == 4 and calls == 114
+    e.close()
+
+
+def test_qwen3_8b_step_with_entropy_commits(gpu_lib):
+    # planted boosts strong enough that easy rows commit by entropy at 8B vocabulary size
+    w = synth.workload("qwen3_8b", kv="synthetic", boost_lo=10.0, boost_hi=20.0, tau_ent=0.9)
+    e, ores, free = _check_step(w, [2])
+    assert sum(int((r["commit_loop"] > 0).sum()) for r in ores) > 0
+    e.close()
+
+
+def test_qwen3_8b_long_context_step(gpu_lib):
+    w = synth.workload("qwen3_8b_long")
+    e, _, _ = _check_step(w, [5])
+    e.close()

@@ -425,3 +425,26 @@ def test_readout_group_reduces_to_step_rule():
     np.testing.assert_array_equal(out["embed_rows"], E[out["tok"]])
     out = orc.readout_commit_group(r, Wl, E, wg, 0.1, tau_ent=-1.0, tau_halt=0.5)
     assert out["forced"] == int(np.argmin(out["H"])) and (out["commit_loop"] != 0).sum() == 1
+
+
+def test_bf16_rounding_matches_library_conversion():
+    import torch
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.standard_normal(10000) * 10.0 ** rng.integers(-6, 6, size=10000),
+                        [1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0]])
+    ref = torch.tensor(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.round_bf16(x)
+    assert np.array_equal(got, ref)
+    assert got[-5] == 1.0 and got[-4] == 1.0 and got[-3] == 1.0 + 2 ** -6   # ties to even
+
+
+def test_rounding_points_mode_stays_close_to_exact():
+    """The bf16 rounding-point variant of the step differs from the exact step by bf16 noise only."""
+    w = _tiny(boost_lo=12.0, boost_hi=14.0)
+    W = run.weights(w)
+    a = run.step(w, W=W, record_hidden=True)[0]
+    b = run.step(w, W=W, record_hidden=True, prec="bf16")[0]
+    ra, rb = a["records"][0], b["records"][0]
+    rel = np.linalg.norm(ra["h_tilde"] - rb["h_tilde"], axis=1) / np.linalg.norm(ra["h_tilde"], axis=1)
+    assert 0 < rel.max() < 2e-2
+    assert np.array_equal(a["commit_loop"], b["commit_loop"])
