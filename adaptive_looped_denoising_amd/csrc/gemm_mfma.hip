@@ -615,10 +615,10 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   }
   if (M <= 64) return 9;
   if (M <= 384) {
-    if (epi == EPI_SWIGLU || epi == EPI_SOFTSTAT) {
-      *splits = 1;
-      return 16;
-    }
+    *splits = 1;
+    if (epi == EPI_SOFTSTAT) return 17;  // LM head: the widest weight tile halves activation re-reads
+    if (epi == EPI_SWIGLU) return 16;
+    *splits = 0;
     if (K > N) {  // FFN down projection
       *splits = 4;
       return 8;

@@ -22,6 +22,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
+# HBM bytes per launch of the gate/up GEMM measured with rocprofv3 FETCH_SIZE + WRITE_SIZE (copy-
+# calibrated), for the kernel named here; profiles/gemm_gate_up_swiglu_qwen3_8b_hbm_traffic.md.
+GATE_UP_KERNEL = "k_gemm_pipe<256, 96, 4, 1, 3, 3, false>"
+GATE_UP_TRAFFIC_BYTES = 223.0e6
 
 
 def progress(msg):
@@ -65,6 +69,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (known traffic, for calibrating HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the step has no cross-GPU path (sequences shard by data "
@@ -78,6 +84,12 @@ def main():
 
     w = synth.workload(args.workload)
     taus = synth.TAU_SWEEP_8B if args.workload == "qwen3_8b" else (w.tau_ent,)
+    if args.copy_probe:
+        src = torch.ones(2 ** 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     progress("workload %s: building engine (device-filled weights)" % w.name)
     e = Engine(w)
     torch.cuda.synchronize()
@@ -145,9 +157,11 @@ def main():
                    "batch": w.batch, "prefix": w.prefix, "block": w.block, "k_max": w.k_max,
                    "tau_ent": w.tau_ent, "tau_halt": w.tau_halt, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "FFN gate/up GEMM + SwiGLU (k_gemm_mfma, %d rows/launch avg, %.1f us/launch)" % (
-                         rows_per_step / max(launches / args.steps, 1), per_launch_ms * 1e3)},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": GATE_UP_TRAFFIC_BYTES if w.name == "qwen3_8b" else None,
+                     "kernel": "FFN gate/up GEMM + SwiGLU (%s), %d rows/launch avg, %.1f us/launch, %.1f MB "
+                               "algorithmic per launch" % (GATE_UP_KERNEL, rows_per_step / max(launches / args.steps, 1),
+                                                           per_launch_ms * 1e3, traffic / 1e6)},
         "tau_sweep": sweep,
         "prefill_ms": prefill_ms,
         "kernels": kernels,
