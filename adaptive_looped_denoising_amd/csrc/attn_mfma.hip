@@ -341,21 +341,24 @@ bool attn_mfma_supported(int hd) { return hd == 32 || hd == 64 || hd == 128; }
 
 // p.n_rows / rows_per_seq = sequence slots; p.part must hold n_pairs * rows_q * max_splits * (hd + 2)
 // floats when max_splits > 1.
-void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st) {
+void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int force_splits, int force_qw) {
   if (p.n_rows <= 0) return;
   const int n_seq = p.n_rows / p.rows_per_seq;
   const int n_pairs = n_seq * p.Hkv;
   const int rows_q = (p.Hq / p.Hkv) * p.rows_per_seq;
-  const int QW = rows_q <= 64 ? 16 : 32;
+  // 16 query rows per wave measured faster than 32 at 128 query rows per pair (more blocks in
+  // flight per key range); 32 only where one pair has more than 256 query rows
+  const int QW = (force_qw == 16 || force_qw == 32) ? force_qw : (rows_q <= 256 ? 16 : 32);
   const int QB = 4 * QW;
   const int n_qblocks = (rows_q + QB - 1) / QB;
   const int n_keys = p.n_cache + p.n_self;
   const int n_tiles = (n_keys + AKT - 1) / AKT;
   int splits = 1;
   if (!p.causal && p.part) {
-    // enough blocks to cover the chip once, and at least 4 key tiles per split
-    const int want = (256 + n_pairs * n_qblocks - 1) / (n_pairs * n_qblocks);
-    splits = min(min(want, max(1, n_tiles / 4)), max_splits);
+    // about three resident blocks per compute unit, and at least 3 key tiles per split
+    const int want = (768 + n_pairs * n_qblocks - 1) / (n_pairs * n_qblocks);
+    splits = min(min(want, max(1, (n_tiles + 2) / 3)), max_splits);
+    if (force_splits > 0) splits = min(force_splits, max_splits);
     if (splits < 1) splits = 1;
   }
   const int kps = ((n_tiles + splits - 1) / splits) * AKT;

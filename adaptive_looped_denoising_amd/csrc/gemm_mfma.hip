@@ -639,10 +639,10 @@ int gemm_mfma_softstat_bn(int M) {
 // Chooses the tile and split-K, then launches.  For SWIGLU, N = 2F (interleaved gate/up columns)
 // and the output has F columns.  part/part_floats: split-K scratch.  force_tile / force_splits
 // (>= 0 / > 0) override the choice.
-void launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
-                      const int32_t* m_dev, const GemmEpi& ep, int F, float* part, size_t part_floats,
-                      int force_splits, hipStream_t st, int force_tile) {
-  if (M <= 0 || N <= 0) return;
+int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                     const int32_t* m_dev, const GemmEpi& ep, int F, float* part, size_t part_floats,
+                     int force_splits, hipStream_t st, int force_tile, bool defer_reduce) {
+  if (M <= 0 || N <= 0) return 1;
   int auto_splits = 0;
   const int tile = (force_tile >= 0 && force_tile < kNumTiles) ? force_tile : gemm_mfma_auto_tile(epi, M, N, K,
                                                                                                   &auto_splits);
@@ -707,7 +707,7 @@ void launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, i
 #undef D
   }
 #undef T
-  if (split) {
+  if (split && !(defer_reduce && epi != EPI_SWIGLU)) {
     const int NO = epi == EPI_SWIGLU ? N / 2 : N;
     const size_t n = (size_t)M * NO;
     const unsigned g = (unsigned)((n + 255) / 256);
@@ -717,7 +717,9 @@ void launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, i
       k_splitk_reduce<EPI_RESID><<<g, 256, 0, st>>>(part, splits, M, N, m_dev, ep);
     else
       k_splitk_reduce<EPI_STORE><<<g, 256, 0, st>>>(part, splits, M, N, m_dev, ep);
+    return 1;
   }
+  return splits;
 }
 
 }  // namespace alodlm
@@ -746,7 +748,7 @@ extern "C" int alodlm_diag_gemm(int32_t epi, int32_t M, int32_t N, int32_t K, co
     launch_gemm_generic(DT_BF16, epi, A, K, B, K, M, N, K, nullptr, ep, st);
   } else {
     launch_gemm_mfma(epi, A, K, B, K, M, N, K, nullptr, ep, N / 2, scratch, scratch ? scratch_floats : 0,
-                     force_splits, st, force_tile);
+                     force_splits, st, force_tile, false);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -55,7 +55,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
                                                  const int32_t* __restrict__ rows,
                                                  const int32_t* __restrict__ n_dev, const TG* __restrict__ g,
                                                  float eps, TO* __restrict__ out, const TG* __restrict__ exit_w,
-                                                 float exit_b, float* __restrict__ lam) {
+                                                 float exit_b, float* __restrict__ lam,
+                                                 const float* __restrict__ part, int splits, int n_rows_part,
+                                                 float* __restrict__ x_out) {
   __shared__ float red[4];
   const int r = blockIdx.x;
   if (n_dev && r >= *n_dev) return;
@@ -67,6 +69,21 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
   for (int i = 0; i < RMS_VEC; ++i) {
     const int e = (i * 256 + threadIdx.x) * 4;
     v[i] = e < d ? *(const float4*)(xr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (splits > 1 && e < d) {  // residual + fixed-order sum of the producing GEMM's split-K partials
+      float4 acc = *(const float4*)(part + (size_t)src * d + e);
+      for (int sp = 1; sp < splits; ++sp) {
+        const float4 pp = *(const float4*)(part + ((size_t)sp * n_rows_part + src) * d + e);
+        acc.x += pp.x;
+        acc.y += pp.y;
+        acc.z += pp.z;
+        acc.w += pp.w;
+      }
+      v[i].x += acc.x;
+      v[i].y += acc.y;
+      v[i].z += acc.z;
+      v[i].w += acc.w;
+      *(float4*)(x_out + (size_t)src * d + e) = v[i];
+    }
     ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
   }
   ss = block_sum<256>(ss, red);
@@ -115,7 +132,8 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
                                                       float eps, const float* __restrict__ cosT,
                                                       const float* __restrict__ sinT, TA* __restrict__ q_out,
                                                       TA* __restrict__ k_out, TA* __restrict__ v_out,
-                                                      int64_t sSeq, int64_t sHead, int64_t sPos, int seq0) {
+                                                      int64_t sSeq, int64_t sHead, int64_t sPos, int seq0,
+                                                      int splits) {
   const int NH = Hq + 2 * Hkv;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -123,13 +141,20 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
   const int r = gw / NH, hh = gw % NH;
   const int half = hd >> 1;
   const float* src = qkv + (size_t)r * NH * hd + (size_t)hh * hd;
+  const size_t pstride = (size_t)n_rows * NH * hd;  // split-K partial stride
+  // element e of this head: the projection, or the fixed-order sum of its split-K partials
+  auto val = [&](int e) {
+    float acc = src[e];
+    for (int sp = 1; sp < splits; ++sp) acc += src[sp * pstride + e];
+    return acc;
+  };
   const int jpos = r % rows_per_seq;
   const int pos = pos0 + jpos;
   const size_t kv_off = (size_t)(seq0 + r / rows_per_seq) * sSeq + (size_t)jpos * sPos;
   if (hh >= Hq + Hkv) {  // value head: copy
     const int h = hh - Hq - Hkv;
     TA* dst = v_out + kv_off + (size_t)h * sHead;
-    for (int e = lane; e < hd; e += 64) dst[e] = from_f<TA>(src[e]);
+    for (int e = lane; e < hd; e += 64) dst[e] = from_f<TA>(val(e));
     return;
   }
   const bool is_q = hh < Hq;
@@ -141,8 +166,8 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
     const int p = lane + 64 * t;
     x1[t] = x2[t] = 0.f;
     if (p < half) {
-      x1[t] = src[p];
-      x2[t] = src[p + half];
+      x1[t] = val(p);
+      x2[t] = val(p + half);
       ss += x1[t] * x1[t] + x2[t] * x2[t];
     }
   }
@@ -471,11 +496,11 @@ void launch_embed_rows(int dtype, const int32_t* ids, int n_rows, const void* E,
 
 void launch_rmsnorm(int dtype, const float* x, int n_rows, int d, const int32_t* rows, const int32_t* n_dev,
                     const void* g, float eps, void* out, const void* exit_w, float exit_b, float* lam,
-                    hipStream_t st) {
+                    hipStream_t st, const float* part, int splits, float* x_out) {
   if (n_rows <= 0) return;
   DISPATCH_T(dtype, T,
              k_rmsnorm<T, T><<<n_rows, 256, 0, st>>>(x, d, rows, n_dev, (const T*)g, eps, (T*)out,
-                                                      (const T*)exit_w, exit_b, lam));
+                                                      (const T*)exit_w, exit_b, lam, part, splits, n_rows, x_out));
 }
 
 void launch_exit_gate(int dtype, const void* rows, int n_rows, int d, const void* w, float b, float* lam,
@@ -487,13 +512,13 @@ void launch_exit_gate(int dtype, const void* rows, int n_rows, int d, const void
 void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_seq, int pos0, int Hq, int Hkv,
                          int hd, const void* qn, const void* kn, float eps, const float* cosT,
                          const float* sinT, void* q_out, void* k_out, void* v_out, int64_t sSeq, int64_t sHead,
-                         int64_t sPos, int seq0, hipStream_t st) {
+                         int64_t sPos, int seq0, hipStream_t st, int splits) {
   if (n_rows <= 0) return;
   const int waves = n_rows * (Hq + 2 * Hkv);
   DISPATCH_T(dtype, T,
              k_qk_norm_rope<T, T><<<(waves + 3) / 4, 256, 0, st>>>(
                  qkv, n_rows, rows_per_seq, pos0, Hq, Hkv, hd, (const T*)qn, (const T*)kn, eps, cosT, sinT,
-                 (T*)q_out, (T*)k_out, (T*)v_out, sSeq, sHead, sPos, seq0));
+                 (T*)q_out, (T*)k_out, (T*)v_out, sSeq, sHead, sPos, seq0, splits));
 }
 
 void launch_swiglu(int dtype, const float* gu, int n_rows, int F, void* act, hipStream_t st) {

@@ -53,15 +53,19 @@ struct AttnParams {
 
 void launch_embed_rows(int dtype, const int32_t* ids, int n_rows, const void* E, int d, int V, float* out,
                        hipStream_t st);
+// x rows are x[src] (+ sum of `splits` deferred split-K partials part[s][r][:] when splits > 1,
+// written back to x_out[r]).
 void launch_rmsnorm(int dtype, const float* x, int n_rows, int d, const int32_t* rows, const int32_t* n_dev,
                     const void* g, float eps, void* out, const void* exit_w, float exit_b, float* lam,
-                    hipStream_t st);
+                    hipStream_t st, const float* part = nullptr, int splits = 1, float* x_out = nullptr);
 void launch_exit_gate(int dtype, const void* rows, int n_rows, int d, const void* w, float b, float* lam,
                       hipStream_t st);
+// qkv rows come from `qkv`, or are the sum of `splits` deferred split-K partials [s][row][:] of
+// the projection when splits > 1 (qkv then points at the partials).
 void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_seq, int pos0, int Hq, int Hkv,
                          int hd, const void* qn, const void* kn, float eps, const float* cosT, const float* sinT,
                          void* q_out, void* k_out, void* v_out, int64_t sSeq, int64_t sHead, int64_t sPos,
-                         int seq0, hipStream_t st);
+                         int seq0, hipStream_t st, int splits = 1);
 void launch_swiglu(int dtype, const float* gu, int n_rows, int F, void* act, hipStream_t st);
 void launch_softstat_combine(const SoftStat* part, int n_rows, int n_tiles, const int32_t* n_dev, float* H,
                              float* lse, int32_t* tok, hipStream_t st);
@@ -90,14 +94,17 @@ bool gemm_mfma_supported(int K, int lda, int ldb);
 // Column-tile width the matrix-core dispatcher uses for a SOFTSTAT (LM-head) GEMM of M rows:
 // the softmax statistics are kept per column tile.
 int gemm_mfma_softstat_bn(int M);
-void launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
-                      const int32_t* m_dev, const GemmEpi& ep, int F, float* part, size_t part_floats,
-                      int force_splits, hipStream_t st, int force_tile = -1);
+// Returns the number of split-K partials left unreduced in `part` ([splits][M][N] fp32, plain
+// A.B^T sums) when defer_reduce is set and the GEMM was split (STORE / RESID only), else 1 (the
+// epilogue has been applied).
+int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                     const int32_t* m_dev, const GemmEpi& ep, int F, float* part, size_t part_floats,
+                     int force_splits, hipStream_t st, int force_tile = -1, bool defer_reduce = false);
 void launch_gemm_generic(int dtype, int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                          const int32_t* m_dev, const GemmEpi& ep, hipStream_t st);
 void launch_attn_generic(int dtype, const AttnParams& p, hipStream_t st);
 bool attn_mfma_supported(int hd);
-void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st);
+void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int force_splits = 0, int force_qw = 0);
 
 void launch_fill_kv_synth(int dtype, void* slot_base, int B, int Hkv, int P, int P_max, int hd, uint32_t seed,
                           uint32_t tensor, float scale, hipStream_t st);

@@ -145,6 +145,8 @@ struct alodlm_ctx {
   int64_t layer_calls = 0;
   int32_t loops_run = 0;
   bool force_generic = false;  // diagnostics: ALODLM_FORCE_GENERIC=1 keeps bf16 on the vector-ALU kernels
+  int attn_force_splits = 0;   // diagnostics: ALODLM_ATTN_SPLITS=n fixes the key splits of step attention
+  int attn_force_qw = 0;       // diagnostics: ALODLM_ATTN_QW=16|32 fixes the query rows per wave
   // diagnostics: per-class kernel timing with event pairs on the context stream
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;
@@ -221,12 +223,13 @@ bool use_mfma(const alodlm_ctx* c, int K, int lda, int ldb) {
 }
 
 // GEMM dispatch: C = A . B^T with the given epilogue (SWIGLU: N = 2F interleaved gate/up).
-void gemm(alodlm_ctx* c, int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
-          const int32_t* m_dev, const GemmEpi& ep, int F = 0) {
+// With `defer`, a split-K STORE / RESID GEMM may leave its partials unreduced in the split-K
+// scratch for the consuming kernel; the return value is then the number of partials (else 1).
+int gemm(alodlm_ctx* c, int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+         const int32_t* m_dev, const GemmEpi& ep, int F = 0, bool defer = false) {
   if (use_mfma(c, K, lda, ldb)) {
-    launch_gemm_mfma(epi, A, lda, B, ldb, M, N, K, m_dev, ep, F, c->at<float>(c->plan.gemm_part),
-                     c->plan.gemm_part_elems, 0, c->st);
-    return;
+    return launch_gemm_mfma(epi, A, lda, B, ldb, M, N, K, m_dev, ep, F, c->at<float>(c->plan.gemm_part),
+                            c->plan.gemm_part_elems, 0, c->st, -1, defer);
   }
   if (epi == EPI_SWIGLU) {  // generic path: both halves in fp32, then silu(gate) * up
     GemmEpi e;
@@ -234,9 +237,10 @@ void gemm(alodlm_ctx* c, int epi, const void* A, int lda, const void* B, int ldb
     e.ldc = N;
     launch_gemm_generic(dt(c), EPI_STORE, A, lda, B, ldb, M, N, K, m_dev, e, c->st);
     launch_swiglu(dt(c), e.C, M, F, ep.act, c->st);
-    return;
+    return 1;
   }
   launch_gemm_generic(dt(c), epi, A, lda, B, ldb, M, N, K, m_dev, ep, c->st);
+  return 1;
 }
 
 // Column tiles of the LM-head softmax statistics for the path a readout of M rows takes.
@@ -250,7 +254,7 @@ void attention(alodlm_ctx* c, const AttnParams& p) {
   if (c->cfg.dtype == ALODLM_DTYPE_BF16 && !c->force_generic && attn_mfma_supported(p.hd)) {
     AttnParams q = p;
     q.part = c->at<float>(c->plan.attn_part);
-    launch_attn_mfma(q, c->plan.attn_splits, c->st);
+    launch_attn_mfma(q, c->plan.attn_splits, c->st, c->attn_force_splits, c->attn_force_qw);
     return;
   }
   launch_attn_generic(dt(c), p, c->st);
@@ -296,8 +300,9 @@ void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   e1.C = qkv;
   e1.ldc = qkv_out;
   c->tic(ALODLM_K_GEMM_QKV);
-  gemm(c, EPI_STORE, xn, d, W.wqkv, d, n, qkv_out, d, nullptr, e1);
+  const int qkv_splits = gemm(c, EPI_STORE, xn, d, W.wqkv, d, n, qkv_out, d, nullptr, e1, 0, true);
   c->toc();
+  const float* qkv_src = qkv_splits > 1 ? c->at<float>(p.gemm_part) : qkv;
 
   AttnParams ap;
   ap.q = q;
@@ -315,9 +320,9 @@ void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
     void* vd = cache_slot(c, true, slot);
     const int64_t sSeq = (int64_t)Hkv * Pm * hd, sHead = Pm * hd, sPos = hd;
     c->tic(ALODLM_K_NORM_ROPE);
-    launch_qk_norm_rope(dt(c), qkv, n, lc.rows_per_seq, 0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
+    launch_qk_norm_rope(dt(c), qkv_src, n, lc.rows_per_seq, 0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
                         c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, kd, vd, sSeq, sHead, sPos, lc.seq0,
-                        c->st);
+                        c->st, qkv_splits);
     c->toc();
     ap.n_cache = 0;
     ap.sk = kd;
@@ -333,8 +338,9 @@ void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
     void* vs = c->at<void>(p.vself);
     const int64_t sSeq = (int64_t)lc.rows_per_seq * Hkv * hd, sHead = hd, sPos = (int64_t)Hkv * hd;
     c->tic(ALODLM_K_NORM_ROPE);
-    launch_qk_norm_rope(dt(c), qkv, n, lc.rows_per_seq, lc.pos0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
-                        c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, ks, vs, sSeq, sHead, sPos, 0, c->st);
+    launch_qk_norm_rope(dt(c), qkv_src, n, lc.rows_per_seq, lc.pos0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
+                        c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, ks, vs, sSeq, sHead, sPos, 0, c->st,
+                        qkv_splits);
     c->toc();
     const bool core = li >= g.n_pre && li < g.n_pre + g.n_core;
     const int slot = slot_of(g, li, 1);
@@ -367,11 +373,17 @@ void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   e2.R = lc.x_in;
   e2.ldc = d;
   c->tic(ALODLM_K_GEMM_O);
-  gemm(c, EPI_RESID, attn, Hq * hd, W.wo, Hq * hd, n, d, Hq * hd, nullptr, e2);
+  const int o_splits = gemm(c, EPI_RESID, attn, Hq * hd, W.wo, Hq * hd, n, d, Hq * hd, nullptr, e2, 0, true);
   c->toc();
 
+  // FFN RMSNorm; with deferred O-projection partials it also forms x_out = x_in + sum(partials)
   c->tic(ALODLM_K_NORM_ROPE);
-  launch_rmsnorm(dt(c), lc.x_out, n, d, nullptr, nullptr, W.ffn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st);
+  if (o_splits > 1)
+    launch_rmsnorm(dt(c), lc.x_in, n, d, nullptr, nullptr, W.ffn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st,
+                   c->at<float>(p.gemm_part), o_splits, lc.x_out);
+  else
+    launch_rmsnorm(dt(c), lc.x_out, n, d, nullptr, nullptr, W.ffn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr,
+                   c->st);
   c->toc();
   GemmEpi e3;
   e3.act = act;
@@ -483,6 +495,8 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
   c->st = (hipStream_t)hip_stream;
   const char* fg = getenv("ALODLM_FORCE_GENERIC");
   c->force_generic = fg && fg[0] == '1';
+  if (const char* v = getenv("ALODLM_ATTN_SPLITS")) c->attn_force_splits = atoi(v);
+  if (const char* v = getenv("ALODLM_ATTN_QW")) c->attn_force_qw = atoi(v);
   // RoPE tables, computed in double on the host: angle(pos, i) = pos * theta^(-2i/hd)
   const int half = cfg->head_dim / 2;
   std::vector<float> cs((size_t)plan.max_pos * half), sn((size_t)plan.max_pos * half);
