@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(HERE, "libalodlm.so")
 OK, EINVAL, ESTATE, ENOMEM, EHIP = 0, -1, -2, -3, -4
 DTYPE_BF16, DTYPE_FP32 = 0, 1
 STEP_TEACHER_FORCED = 1
+# diagnostics GEMM epilogues (alodlm_diag.h)
+DIAG_STORE, DIAG_RESID, DIAG_SOFTSTAT, DIAG_SWIGLU = 0, 1, 2, 3
 
 EXPORTS = ("alodlm_workspace_bytes", "alodlm_kv_slots", "alodlm_create", "alodlm_prefill_kv",
            "alodlm_prefill_kv_synthetic", "alodlm_denoise_step", "alodlm_readout_commit",

@@ -34,7 +34,7 @@ __device__ __forceinline__ int swiglu_b_row(int n, int F) {
 template <int BM, int BN, int WM, int WN, int EPI, bool SPLIT>
 __device__ __forceinline__ void gemm_epilogue(floatx4 (&acc)[BM / WM / 16][BN / WN / 16], int m0, int n0, int nt,
                                               int sp, int Mr, int M, int N, const GemmEpi& ep, int wm, int wn,
-                                              int lane, int tid) {
+                                              int lane, int tid, SoftStat* red) {
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   const int rbase = m0 + wm * TM * 16 + 4 * (lane >> 4);
   const int cbase = n0 + wn * TN * 16 + (lane & 15);
@@ -87,7 +87,10 @@ __device__ __forceinline__ void gemm_epilogue(floatx4 (&acc)[BM / WM / 16][BN / 
         }
       }
   } else if (EPI == EPI_SOFTSTAT) {
-    __shared__ SoftStat red[WN][BM];
+    // red (WN * BM entries) lives in the kernel's own operand LDS, reused once every wave is
+    // past its last fragment read: a second LDS object would make the compiler's tracking of
+    // the direct global->LDS loads wait for all of them before every fragment read of the loop.
+    __syncthreads();
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -96,30 +99,46 @@ __device__ __forceinline__ void gemm_epilogue(floatx4 (&acc)[BM / WM / 16][BN / 
         const int m = m0 + rl;
         const int bt = (m < Mr && ep.btok) ? ep.btok[m] : -1;
         const float bv = bt >= 0 ? ep.bval[m] : 0.f;
-        SoftStat s = softstat_empty();
+        // this lane's TN logits of the row: max (first column attaining it), then
+        // S = sum exp(z - max) and T = sum (z - max) exp(z - max), one exponential per logit
+        float z[TN];
+        float mx = -INFINITY;
+        int ix = 0x7FFFFFFF;
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
           const int n = cbase + b * 16;
-          if (n < N) {
-            SoftStat e;
-            e.m = acc[a][b][v] + (n == bt ? bv : 0.f);
-            e.S = 1.f;
-            e.T = 0.f;
-            e.idx = n;
-            s = softstat_merge(s, e);
+          z[b] = n < N ? acc[a][b][v] + (n == bt ? bv : 0.f) : -INFINITY;
+          if (z[b] > mx) {
+            mx = z[b];
+            ix = n;
           }
+        }
+        SoftStat s = softstat_empty();
+        if (ix != 0x7FFFFFFF) {
+          float S = 0.f, Tt = 0.f;
+#pragma unroll
+          for (int b = 0; b < TN; ++b) {
+            const float dz = z[b] - mx;
+            const float e = __expf(dz);  // exp(-inf) = 0 for columns past N
+            S += e;
+            Tt += z[b] > -INFINITY ? dz * e : 0.f;
+          }
+          s.m = mx;
+          s.S = S;
+          s.T = Tt;
+          s.idx = ix;
         }
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) s = softstat_merge(s, softstat_shfl_xor(s, o));
-        if ((lane & 15) == 0) red[wn][rl] = s;
+        if ((lane & 15) == 0) red[wn * BM + rl] = s;
       }
     __syncthreads();
     for (int rl = tid; rl < BM; rl += 256) {
       const int m = m0 + rl;
       if (m >= Mr) continue;
-      SoftStat s = red[0][rl];
+      SoftStat s = red[rl];
 #pragma unroll
-      for (int w = 1; w < WN; ++w) s = softstat_merge(s, red[w][rl]);
+      for (int w = 1; w < WN; ++w) s = softstat_merge(s, red[w * BM + rl]);
       ep.part[(size_t)m * ep.n_tiles + nt] = s;
     }
   }
@@ -231,7 +250,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16_t* __restrict__ A,
     __syncthreads();
   }
 
-  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid);
+  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid, (SoftStat*)&sA[0][0]);
 }
 
 // Pipelined variant: an NS-stage LDS ring filled by direct global->LDS loads
@@ -356,7 +375,149 @@ __global__ __launch_bounds__(256) void k_gemm_pipe(const bf16_t* __restrict__ A,
         for (int b = 0; b < TN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kc][a], bfr[kc][b], acc[a][b], 0, 0, 0);
   }
-  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid);
+  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid, (SoftStat*)smem);
+}
+
+// Dual-ring variant: the activation tile (re-read by every column tile, so it comes from L2) and
+// the weight tile (read once, from HBM) have LDS rings of their own, DA + 1 and DB + 1 stages
+// deep, with DB > DA: weight stages are requested DB iterations ahead, activation stages DA
+// ahead, so more HBM bytes are in flight per compute unit than one shared ring of the same LDS
+// size allows.  Issue order is uniform over virtual iterations j = -DB .. nk - 1: A(j + DA) then
+// B(j + DB), each only if its stage exists; the wait before iteration `it` counts exactly the
+// loads issued after A(it) (the later of the two loads that iteration needs).
+template <int LA, int LB, int DA, int CA = 0, int CB = 0>
+__device__ __forceinline__ void ring2_wait(int ca, int cb) {
+  if (ca == CA && cb == CB) {
+    wait_vmcnt_le<CA * LA + CB * LB>();
+    return;
+  }
+  if constexpr (CB < DA)
+    ring2_wait<LA, LB, DA, CA, CB + 1>(ca, cb);
+  else if constexpr (CA < DA - 1)
+    ring2_wait<LA, LB, DA, CA + 1, 0>(ca, cb);
+  else
+    wait_vmcnt_le<0>();
+}
+
+template <int BM, int BN, int WM, int WN, int DA, int DB, int EPI, bool SPLIT>
+__global__ __launch_bounds__(256) void k_gemm_ring2(const bf16_t* __restrict__ A, int lda,
+                                                    const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
+                                                    int k_split, int m_tiles, int n_tiles, int splits,
+                                                    const int32_t* __restrict__ m_dev, GemmEpi ep, int F) {
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  constexpr int LA = BM / 32, LB = BN / 32;     // load instructions per wave per stage
+  constexpr int SA = BM * 64, SB = BN * 64;     // bf16 elements per stage
+  static_assert(BM % 32 == 0 && BN % 32 == 0 && DA >= 1 && DB >= DA, "ring shape");
+  static_assert(WM * WN == 4 && TM * WM * 16 == BM && TN * WN * 16 == BN, "wave grid must tile the block");
+  // one LDS object for both rings: with two, the compiler's LDS-DMA tracking inserts a full
+  // vector-memory wait before the fragment reads of the second
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[(DA + 1) * SA + (DB + 1) * SB];
+  bf16_t* const sa = smem;
+  bf16_t* const sb = smem + (DA + 1) * SA;
+
+  const int total = m_tiles * n_tiles * splits;
+  const int per = (gridDim.x + 7) >> 3;
+  const int T = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (T >= total) return;
+  const int mt = T % m_tiles;
+  const int rest = T / m_tiles;
+  const int nt = rest % n_tiles;
+  const int sp = rest / n_tiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+  int Mr = M;
+  if (m_dev) Mr = min(Mr, *m_dev);
+  if (m0 >= Mr) return;
+  const int kb = sp * k_split;
+  const int nk = (min(K, kb + k_split) - kb) / GK;
+
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int wm = wid / WN, wn = wid % WN;
+
+  const bf16_t* asrc[LA];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int rho = (wid * LA + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (rho & 7);
+    const int gm = m0 + rho;
+    asrc[j] = A + (size_t)(gm < Mr ? gm : 0) * lda + c * 8;
+  }
+  const bf16_t* bsrc[LB];
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int rho = (wid * LB + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (rho & 7);
+    const int gn = n0 + rho;
+    const int ok = gn < N ? gn : 0;
+    const int brow = (EPI == EPI_SWIGLU) ? swiglu_b_row(ok, F) : ok;
+    bsrc[j] = B + (size_t)brow * ldb + c * 8;
+  }
+  auto issue = [&](int j) {  // virtual iteration j: A(j + DA), then B(j + DB)
+    const int xa = j + DA, xb = j + DB;
+    if (xa >= 0 && xa < nk) {
+      bf16_t* base = sa + (xa % (DA + 1)) * SA;
+      const int k = kb + xa * GK;
+#pragma unroll
+      for (int i = 0; i < LA; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + k), LDS_PTR(base + (wid * LA + i) * 8 * 64), 16, 0, 0);
+    }
+    if (xb < nk) {
+      bf16_t* base = sb + (xb % (DB + 1)) * SB;
+      const int k = kb + xb * GK;
+#pragma unroll
+      for (int i = 0; i < LB; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + k), LDS_PTR(base + (wid * LB + i) * 8 * 64), 16, 0, 0);
+    }
+  };
+
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+  for (int j = -DB; j < 0; ++j) issue(j);
+
+  const int col = lane & 15, quad = lane >> 4;
+  for (int it = 0; it < nk; ++it) {
+    // loads issued after A(it): B of virtual iterations it-DA .. it-1 and A of it-DA+1 .. it-1
+    const int cb = min(max(nk - DB - (it - DA), 0), DA);
+    const int ca = min(max(nk - 1 - it, 0), DA - 1);
+    if (ca == DA - 1 && cb == DA)
+      wait_vmcnt_le<(DA - 1) * LA + DA * LB>();
+    else
+      ring2_wait<LA, LB, DA>(ca, cb);
+    // barrier without the fence of __syncthreads (see k_gemm_pipe): stage `it` has landed for
+    // every wave, and every wave is done reading the slots refilled by issue(it) below.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(it);
+    const bf16_t* ta = sa + (it % (DA + 1)) * SA;
+    const bf16_t* tb = sb + (it % (DB + 1)) * SB;
+    bf16x8_t af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int c = kc * 4 + quad;
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const int r = wm * TM * 16 + a * 16 + col;
+        af[kc][a] = *(const bf16x8_t*)&ta[r * 64 + ((c ^ (r & 7)) << 3)];
+      }
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int r = wn * TN * 16 + b * 16 + col;
+        bfr[kc][b] = *(const bf16x8_t*)&tb[r * 64 + ((c ^ (r & 7)) << 3)];
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kc][a], bfr[kc][b], acc[a][b], 0, 0, 0);
+  }
+  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid, (SoftStat*)smem);
 }
 
 // Weight-streaming variant for 65..256 rows: the four waves split the 256 rows (64 each) and all
@@ -488,7 +649,7 @@ __global__ __launch_bounds__(256) void k_gemm_adirect(const bf16_t* __restrict__
     step(it, std::integral_constant<int, 0>());
     if (it + 1 < nk) step(it + 1, std::integral_constant<int, 1>());
   }
-  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid);
+  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid, (SoftStat*)smem);
 }
 
 // Fixed-order sum of split-K partials [splits][M][N] followed by the epilogue.
@@ -526,6 +687,28 @@ static void run_pipe(int epi, bool split, dim3 grid, const bf16_t* A, int lda, c
 #define GO(E, S)                                                                                               \
   k_gemm_pipe<BM, BN, WM, WN, NS, E, S><<<grid, 256, 0, st>>>(A, lda, B, ldb, M, N, K, k_split, mt, nt, splits, \
                                                               m_dev, ep, F)
+  if (split) {
+    if (epi == EPI_SWIGLU) GO(EPI_SWIGLU, true);
+    else GO(EPI_STORE, true);
+  } else if (epi == EPI_STORE) {
+    GO(EPI_STORE, false);
+  } else if (epi == EPI_RESID) {
+    GO(EPI_RESID, false);
+  } else if (epi == EPI_SWIGLU) {
+    GO(EPI_SWIGLU, false);
+  } else {
+    GO(EPI_SOFTSTAT, false);
+  }
+#undef GO
+}
+
+template <int BM, int BN, int WM, int WN, int DA, int DB>
+static void run_ring2(int epi, bool split, dim3 grid, const bf16_t* A, int lda, const bf16_t* B, int ldb, int M,
+                      int N, int K, int k_split, int mt, int nt, int splits, const int32_t* m_dev, const GemmEpi& ep,
+                      int F, hipStream_t st) {
+#define GO(E, S)                                                                                       \
+  k_gemm_ring2<BM, BN, WM, WN, DA, DB, E, S><<<grid, 256, 0, st>>>(A, lda, B, ldb, M, N, K, k_split, mt, nt, \
+                                                                   splits, m_dev, ep, F)
   if (split) {
     if (epi == EPI_SWIGLU) GO(EPI_SWIGLU, true);
     else GO(EPI_STORE, true);
@@ -597,11 +780,16 @@ static const TileCfg kTiles[] = {{32, 128}, {64, 128}, {128, 128}, {256, 64}, {2
                                  {128, 128}, {64, 128}, {32, 128}, {256, 64}, {64, 64}, {128, 64}, {256, 128},
                                  {128, 256}, {256, 96}, {256, 128}, {128, 96},
                                  // activations direct to registers, weights through the LDS ring
-                                 {256, 64}, {256, 96}, {256, 128}, {256, 96}};
-constexpr int kNumTiles = 23;
+                                 {256, 64}, {256, 96}, {256, 128}, {256, 96},
+                                 {256, 96}, {256, 96}, {256, 128}, {256, 64},
+                                 // dual ring: activation stages DA ahead, weight stages DB ahead
+                                 {256, 96}, {256, 96}, {128, 96}, {128, 96}, {128, 128}, {128, 128}, {32, 128},
+                                 {64, 128}, {256, 64}};
+constexpr int kNumTiles = 36;
 
 // Measured choices (MI355X, bf16, K = 2048..12288): rows up to 48 stream the weights with the
-// 32-row pipelined tile; 49..384 rows use the 256-row tiles; more rows use the large tiles.
+// 32-row pipelined tile; 49..384 rows use 128- or 256-row tiles (the dual-ring ones where they
+// measured faster); more rows use the large tiles.
 // Returns the tile; *splits gets the split-K factor (0 = the generic rule).
 int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   *splits = 0;
@@ -616,14 +804,13 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   if (M <= 64) return 9;
   if (M <= 384) {
     *splits = 1;
-    if (epi == EPI_SOFTSTAT) return 17;  // LM head: the widest weight tile halves activation re-reads
-    if (epi == EPI_SWIGLU) return 16;
-    *splits = 0;
+    if (epi == EPI_SOFTSTAT) return M <= 128 ? 31 : 17;  // LM head: wide weight tiles, few activation re-reads
+    if (epi == EPI_SWIGLU) return M <= 128 ? 18 : 27;
     if (K > N) {  // FFN down projection
       *splits = 4;
-      return 8;
+      return M <= 128 ? 34 : 8;
     }
-    *splits = 2;
+    *splits = M <= 128 ? 4 : 2;
     return 18;
   }
   *splits = 1;
@@ -703,8 +890,26 @@ int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, in
     case 19: D(64, 6); break;
     case 20: D(96, 5); break;
     case 21: D(128, 4); break;
+    case 23: D(96, 8); break;
+    case 24: D(96, 10); break;
+    case 25: D(128, 8); break;
+    case 26: D(64, 12); break;
     default: D(96, 3); break;
 #undef D
+#define R(BM_, BN_, WM_, WN_, DA_, DB_)                                                                        \
+  run_ring2<BM_, BN_, WM_, WN_, DA_, DB_>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, \
+                                         e, F, st)
+    case 27: R(256, 96, 4, 1, 2, 4); break;
+    case 28: R(256, 96, 4, 1, 1, 6); break;
+    case 29: R(128, 96, 4, 1, 2, 6); break;
+    case 30: R(128, 96, 4, 1, 2, 8); break;
+    case 31: R(128, 128, 2, 2, 2, 5); break;
+    case 32: R(128, 128, 2, 2, 1, 6); break;
+    case 33: R(32, 128, 1, 4, 2, 7); break;
+    case 34: R(64, 128, 2, 2, 2, 7); break;
+    case 35: R(256, 64, 4, 1, 2, 6); break;
+#undef R
+
   }
 #undef T
   if (split && !(defer_reduce && epi != EPI_SWIGLU)) {
@@ -731,6 +936,22 @@ extern "C" int alodlm_diag_gemm(int32_t epi, int32_t M, int32_t N, int32_t K, co
                                 int32_t force_generic, int32_t force_tile, void* hip_stream) {
   using namespace alodlm;
   if (M <= 0 || N <= 0 || K <= 0 || !A || !B) return -1;
+  if (epi == EPI_SOFTSTAT) {
+    if (!C || !act || !scratch || force_generic || !gemm_mfma_supported(K, K, K)) return -1;
+    int sp;
+    const int tile = (force_tile >= 0 && force_tile < kNumTiles) ? force_tile : gemm_mfma_auto_tile(epi, M, N, K, &sp);
+    const int n_tiles = (N + kTiles[tile].bn - 1) / kTiles[tile].bn;
+    if ((size_t)4 * M * n_tiles > scratch_floats) return -1;
+    hipStream_t st = (hipStream_t)hip_stream;
+    float* H = C;                 // first M floats, then the M log-sum-exps
+    float* lse = C + M;
+    GemmEpi ep;
+    ep.part = (SoftStat*)scratch;
+    ep.n_tiles = n_tiles;
+    launch_gemm_mfma(epi, A, K, B, K, M, N, K, nullptr, ep, 0, nullptr, 0, 1, st, tile, false);
+    launch_softstat_combine((const SoftStat*)scratch, M, n_tiles, nullptr, H, lse, (int32_t*)act, st);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+  }
   if (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_SWIGLU) return -1;
   if (epi == EPI_SWIGLU && (!act || N % 32)) return -1;
   if (epi != EPI_SWIGLU && !C) return -1;

@@ -681,8 +681,11 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
       launch_gather_boosts(ro_rows, cnt + 1, act[cur], n, L, a->boost_tok, a->boost_val, c->at<int32_t>(p.btok),
                            c->at<float>(p.bval), st);
     }
+    // after loop 1 the host holds the exact readout row count (read back with the loop status),
+    // which picks the LM-head tile; loop 1 uses the bound n
+    const int n_read = (s > 1 && host_cnt[1] > 0 && host_cnt[1] <= n) ? host_cnt[1] : n;
     c->tic(ALODLM_K_LM_HEAD);
-    readout_heads(c, c->at<void>(p.r), n, cnt + 1, bt, bv);
+    readout_heads(c, c->at<void>(p.r), n_read, cnt + 1, bt, bv);
     c->toc();
     c->tic(ALODLM_K_CONTROL);
     launch_commit(nb, s, K, L, B, a->tau_ent, a->tau_halt, act[cur], U, av, ro_map, c->at<float>(p.H),

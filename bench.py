@@ -23,9 +23,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
 # HBM bytes per launch of the gate/up GEMM measured with rocprofv3 FETCH_SIZE + WRITE_SIZE (copy-
-# calibrated), for the kernel named here; profiles/gemm_gate_up_swiglu_qwen3_8b_hbm_traffic.md.
-GATE_UP_KERNEL = "k_gemm_pipe<256, 96, 4, 1, 3, 3, false>"
-GATE_UP_TRAFFIC_BYTES = 223.0e6
+# calibrated), for the kernel named here; None until the counters are taken on this kernel.
+GATE_UP_KERNEL = "k_gemm_ring2<256, 96, 4, 1, 2, 4, 3, false>"
+GATE_UP_TRAFFIC_BYTES = None
 
 
 def progress(msg):
@@ -158,7 +158,7 @@ def main():
                    "tau_ent": w.tau_ent, "tau_halt": w.tau_halt, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": GATE_UP_TRAFFIC_BYTES if w.name == "qwen3_8b" else None,
+                     "traffic": GATE_UP_TRAFFIC_BYTES if w.name == "qwen3_8b" and GATE_UP_TRAFFIC_BYTES else None,
                      "kernel": "FFN gate/up GEMM + SwiGLU (%s), %d rows/launch avg, %.1f us/launch, %.1f MB "
                                "algorithmic per launch" % (GATE_UP_KERNEL, rows_per_step / max(launches / args.steps, 1),
                                                            per_launch_ms * 1e3, traffic / 1e6)},

@@ -19,13 +19,18 @@ extern "C" {
 #define ALODLM_DIAG_STORE 0  /* C[M][N] = A . B^T (fp32) */
 #define ALODLM_DIAG_RESID 1  /* C[M][N] += A . B^T (fp32) */
 #define ALODLM_DIAG_SWIGLU 3 /* B = [2F][K] (gate rows, then up rows); act[M][F] = silu(A.Bg^T) * (A.Bu^T) */
+/* Readout statistics of the logits z = A.B^T over the N columns, the LM-head kernel of the
+ * step: C[M][2] = {entropy of softmax(z), log-sum-exp of z} (fp32) and act = int32 [M]
+ * argmax (lowest column among equal maxima).  scratch holds the per-column-tile partial
+ * statistics: 4 * M * ceil(N / 64) floats cover every tile.  Matrix-core path only. */
+#define ALODLM_DIAG_SOFTSTAT 2
 
 /* bf16 A [M][K], B [N][K] (N = 2F for SWIGLU).  scratch: device fp32 buffer of
  * scratch_floats for split-K partials (force_splits > 1 needs splits*M*N floats).
  * force_splits: 0 = the dispatcher's choice.  force_generic != 0 runs the vector-ALU
  * kernel instead of the matrix-core one.  force_tile: -1 = the dispatcher's tile choice, else a
- * tile index of the matrix-core kernel (0..7; out of range = the dispatcher's choice).  Asynchronous.  Returns 0 or -1 (bad
- * arguments, checked before any launch), -4 (launch failed). */
+ * tile index of the matrix-core kernel (out of range = the dispatcher's choice).  Asynchronous.
+ * Returns 0 or -1 (bad arguments, checked before any launch), -4 (launch failed). */
 __attribute__((visibility("default"))) int alodlm_diag_gemm(int32_t epi, int32_t M, int32_t N, int32_t K,
                                                             const void* A, const void* B, float* C, void* act,
                                                             float* scratch, size_t scratch_floats,

@@ -52,7 +52,7 @@ def test_gemm_store_and_resid(gpu_lib, M, N, K):
     assert err < 2e-5, err
 
 
-@pytest.mark.parametrize("tile", range(23))
+@pytest.mark.parametrize("tile", range(36))
 def test_gemm_every_tile(gpu_lib, tile):
     M, N, K = 300, 1024, 1024
     A, Bm = _bf16((M, K), 10), _bf16((N, K), 11, 0.02)
@@ -69,6 +69,33 @@ def test_gemm_every_tile(gpu_lib, tile):
     refa = g / (1 + np.exp(-g)) * u
     err = np.abs(act.cpu().float().numpy() - refa) / (np.abs(refa) + 1e-2 * np.abs(refa).max())
     assert err.max() < 1.6e-2
+
+
+@pytest.mark.parametrize("tile", range(36))
+def test_softstat_every_tile(gpu_lib, tile):
+    """LM-head readout statistics (entropy, log-sum-exp, argmax over the columns) of every tile,
+    on a ragged shape, against float64 arithmetic on the same bf16 operands."""
+    from adaptive_looped_denoising_amd import binding as B
+    M, N, K = 77, 1000, 256
+    A, Bm = _bf16((M, K), 20), _bf16((N, K), 21, 0.1)
+    z = _ref(A, Bm)
+    zmax = z.max(axis=1, keepdims=True)
+    p = np.exp(z - zmax)
+    S = p.sum(axis=1)
+    lse = zmax[:, 0] + np.log(S)
+    H = lse - (p * z).sum(axis=1) / S
+    out = torch.empty((2, M), dtype=torch.float32, device="cuda")
+    tok = torch.empty(M, dtype=torch.int32, device="cuda")
+    scratch = torch.empty(4 * M * ((N + 63) // 64), dtype=torch.float32, device="cuda")
+    Ad, Bd = A.cuda(), Bm.cuda()  # held until the asynchronous launch has finished
+    B.diag_gemm(B.DIAG_SOFTSTAT, M, N, K, Ad.data_ptr(), Bd.data_ptr(), out.data_ptr(), tok.data_ptr(),
+                scratch.data_ptr(), scratch.numel(), 0, 0, torch.cuda.current_stream().cuda_stream, tile)
+    torch.cuda.synchronize()
+    gH, glse = out.cpu().numpy()
+    assert np.abs(gH - H).max() < 1e-4 and np.abs(glse - lse).max() < 1e-4
+    top2 = np.sort(z, axis=1)[:, -2:]
+    ok = (tok.cpu().numpy() == z.argmax(axis=1)) | (top2[:, 1] - top2[:, 0] < 1e-4)
+    assert ok.all()
 
 
 @pytest.mark.parametrize("splits", [2, 4, 8])
@@ -123,8 +150,8 @@ def test_readout_commit_at_8b_vocab(gpu_lib, n_rows):
     bt, bv = synth.boosts(w)
     bt, bv = bt.reshape(-1), bv.reshape(-1)
     rows_d = torch.from_numpy(rows.view(np.int16)).cuda().view(torch.bfloat16)
-    out = e.readout_commit(rows_d, synth.READOUT_GROUP if n_rows >= 32 else n_rows, w.tau_ent, w.tau_halt,
-                           torch.from_numpy(bt).cuda(), torch.from_numpy(bv).cuda())
+    bt_d, bv_d = torch.from_numpy(bt).cuda(), torch.from_numpy(bv).cuda()  # alive until the launch finishes
+    out = e.readout_commit(rows_d, synth.READOUT_GROUP if n_rows >= 32 else n_rows, w.tau_ent, w.tau_halt, bt_d, bv_d)
     torch.cuda.synchronize()
     got = {k: v.cpu().numpy() for k, v in out.items()}
     W = {k: synth.as_f32(v) for k, v in synth.host_weights(w, ["lm_head", "embed", "exit_w"]).items()}
