@@ -272,13 +272,19 @@ struct LayerCall {
   int loop;
   int seq0, depth;
   int prefix_len;
+  // chaining of the FFN down projection into the next layer: `defer` lets this layer leave its
+  // split-K partials unreduced (the caller guarantees the next launch is run_layer on the same
+  // rows, reading x_out as its x_in); `pend` > 1 says x_in still lacks that many partials, which
+  // the attention RMSNorm adds (in place) before normalising.
+  bool defer = false;
+  int pend = 1;
 };
 
 // One transformer block over n_rows rows: x_out = block(x_in).  In prefill mode the rows'
 // post-RoPE K/V go straight into the cache slot of (layer, depth) and attention is causal
 // over them; in step mode the rows attend to the prefix cache (depth-selected for Core
 // layers) plus their own block's K/V.
-void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
+int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   const alodlm_config& g = c->cfg;
   const alodlm_layer_weights& W = c->layers[li];
   const Plan& p = c->plan;
@@ -294,7 +300,11 @@ void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   void* act = c->at<void>(p.act);
 
   c->tic(ALODLM_K_NORM_ROPE);
-  launch_rmsnorm(dt(c), lc.x_in, n, d, nullptr, nullptr, W.attn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st);
+  if (lc.pend > 1)  // finish the previous layer's down projection: x_in += its partials, in place
+    launch_rmsnorm(dt(c), lc.x_in, n, d, nullptr, nullptr, W.attn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st,
+                   c->at<float>(p.gemm_part), lc.pend, const_cast<float*>(lc.x_in));
+  else
+    launch_rmsnorm(dt(c), lc.x_in, n, d, nullptr, nullptr, W.attn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st);
   c->toc();
   GemmEpi e1;
   e1.C = qkv;
@@ -396,9 +406,10 @@ void run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   e4.R = lc.x_out;
   e4.ldc = d;
   c->tic(ALODLM_K_GEMM_DOWN);
-  gemm(c, EPI_RESID, act, F, W.w_down, F, n, d, F, nullptr, e4);
+  const int down_splits = gemm(c, EPI_RESID, act, F, W.w_down, F, n, d, F, nullptr, e4, 0, lc.defer);
   c->toc();
   c->layer_calls += 1;
+  return down_splits;
 }
 
 // LMHead statistics of the readout rows (rows >= *n_dev skipped) then the fixed-order merge.
@@ -641,7 +652,12 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
   // Prelude over every block row (slot t = sequence t)
   launch_embed_rows(dt(c), a->block_ids, B * L, c->w.embed, d, g.vocab, h, st);
   LayerCall lc{STEP, h, h, B * L, L, P, act[cur], 1, 0, 1, P};
-  for (int li = 0; li < g.n_pre; ++li) run_layer(c, li, lc);
+  // run one layer; `chain`: the next launch is the next layer on this layer's output
+  auto layer = [&](int li, bool chain) {
+    lc.defer = chain;
+    lc.pend = run_layer(c, li, lc);
+  };
+  for (int li = 0; li < g.n_pre; ++li) layer(li, true);  // the first Core layer follows the Prelude
 
   int nb = B;
   int32_t host_cnt[3] = {0, 0, 0};
@@ -654,14 +670,15 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
     lc.loop = s;
     lc.x_in = h;
     lc.x_out = h;
-    for (int ci = 0; ci < g.n_core; ++ci) run_layer(c, g.n_pre + ci, lc);
+    for (int ci = 0; ci < g.n_core; ++ci)
+      layer(g.n_pre + ci, ci + 1 < g.n_core || (g.n_coda > 0 && !o->hidden));
     if (o->hidden) launch_dump_hidden(nb, L, d, B, s, act[cur], h, o->hidden, st);
     const float* gsrc = h;
     if (g.n_coda > 0) {
       lc.x_in = h;
       lc.x_out = h_alt;
       for (int ci = 0; ci < g.n_coda; ++ci) {
-        run_layer(c, g.n_pre + g.n_core + ci, lc);
+        layer(g.n_pre + g.n_core + ci, ci + 1 < g.n_coda);
         lc.x_in = h_alt;
       }
       gsrc = h_alt;
