@@ -1,15 +1,20 @@
 // Block attention over the depth-aware prefix cache on the gfx950 matrix cores (bf16).
 //
-// One workgroup (4 waves) takes one (sequence slot, kv head) pair, a block of QB query rows of
-// that pair -- the G = Hq/Hkv query heads sharing the kv head are packed as rows
-// (position i, head g) -> i*G + g -- and one split of its key range.  Keys are the prefix keys
-// (Core layers read position j at depth min(loop, avail[j]), gathered row by row from the depth
-// planes) followed by the block's own keys.  Per tile of 64 keys:
-//   K tile -> LDS (key-major), V tile -> LDS transposed ([hd][key]);
-//   S^T = K Q^T on the matrix cores (Q held in registers as the B operand), so every lane ends
-//   up with 16 scores of one query column -- the online softmax needs no LDS round trip and the
-//   probabilities are already laid out as the B operand of O^T += V^T P^T;
-//   O^T accumulates in registers (fp32), rescaled by the running-max correction.
+// One workgroup (4 waves) takes one (sequence slot, kv head) pair, a block of QB = 4 * QW query
+// rows of that pair -- the G = Hq/Hkv query heads sharing the kv head are packed as rows
+// (position i, head g) -> i*G + g -- and one split of its key tiles.  Key tiles hold 64 keys of
+// one segment: the prefix keys (the cache slot of the loop's depth plane; the planes are
+// materialised at prefill so that plane s already holds every position at depth
+// min(s, available depth)), then the block's own keys.
+//
+// Both operand tiles stream straight from memory into an NS-stage LDS ring with direct
+// global->LDS loads, no register staging and no transposition:
+//   K tile [64 keys][HD] (hd-contiguous rows), 16-byte chunks XOR-swizzled by row;
+//   V^T tile [HD][64 keys] -- the cache stores V transposed (positions contiguous), which is
+//   the operand layout of the P.V product -- chunks swizzled by (row / 2).
+// S^T = K Q^T on the matrix cores (Q in registers as the B operand), so every lane holds 16
+// scores of one query column: the online softmax needs no LDS round trip and the
+// probabilities are already laid out as the B operand of O^T += V^T P^T.
 // With several key splits, partial (O, max, sum) go to a scratch buffer and k_attn_merge
 // combines them in a fixed order.
 #include "common.h"
@@ -26,34 +31,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)from_f<bf16_t>(lo) | ((uint32_t)from_f<bf16_t>(hi) << 16);
 }
 
-// Address of key j (0-based over prefix keys then own keys) of sequence slot t / cache sequence b.
-// Core layers take the depth plane of prefix key j from sdep[j - dep_base] (staged in LDS).
-__device__ __forceinline__ const bf16_t* akv_row(const AttnParams& p, const void* cbase, const void* sbase, int j,
-                                                 int b, int t, int kvh, const uint8_t* sdep, int dep_base) {
-  if (j < p.n_cache) {
-    size_t off = (size_t)b * p.c_sSeq + (size_t)kvh * p.c_sHead + (size_t)j * p.c_sPos;
-    if (p.core) off += (size_t)sdep[j - dep_base] * p.c_plane;
-    return (const bf16_t*)cbase + off;
-  }
-  const int jj = j - p.n_cache;
-  return (const bf16_t*)sbase + (size_t)(t + p.s_seq0) * p.s_sSeq + (size_t)kvh * p.s_sHead + (size_t)jj * p.s_sPos;
-}
-
-template <int HD, int QW>
+template <int HD, int QW, int NS>
 __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, int n_qblocks, int n_splits,
-                                                   int keys_per_split) {
+                                                   int tiles_per_split) {
   constexpr int QB = 4 * QW;
   constexpr int NQ = QW / 16;
   constexpr int NH = HD / 16;
   constexpr int NC = HD / 32;
-  constexpr int CPR = HD / 8;          // 16-byte chunks per key row
-  constexpr int KLD = HD + 8;          // K tile pitch (elements)
-  constexpr int VLD = AKT + 4;         // V^T tile pitch (keys)
-  constexpr int KROWS = 256 / CPR;     // key rows loaded per pass
-  constexpr int DEPC = 4096;            // depth-plane indices staged per chunk of prefix keys
-  __shared__ __attribute__((aligned(16))) bf16_t sK[AKT * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[HD * VLD];
-  __shared__ uint8_t sdep[DEPC];
+  constexpr int CK = HD / 8;             // 16-byte chunks per K row
+  constexpr int KST = AKT * HD;          // K elements per stage
+  constexpr int STAGE = 2 * AKT * HD;    // K then V^T
+  constexpr int KL = HD / 32;            // K load instructions per wave per stage (1 KB each)
+  constexpr int VL = HD / 32;            // V^T load instructions per wave per stage
+  constexpr int LPW = KL + VL;
+  constexpr int RPI = 1024 / (HD * 2);   // K rows per load instruction
+  static_assert(NS >= 2 && (NS - 2) * LPW < 64, "ring depth");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * STAGE];
 
   const int total = n_pairs * n_qblocks * n_splits;
   const int per = (gridDim.x + 7) >> 3;
@@ -69,14 +62,15 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
 
-  // key range of this block
-  const int n_keys = p.n_cache + p.n_self;
-  int kbeg = sp * keys_per_split;
-  int kend = min(n_keys, kbeg + keys_per_split);
-  if (p.causal) {  // last position of the block's queries bounds the keys it can see
+  // tile range of this block: prefix tiles 0 .. TP-1, then own-key tiles TP .. TP+TS-1
+  const int TP = (p.n_cache + AKT - 1) / AKT;
+  int TE = TP + (p.n_self + AKT - 1) / AKT;
+  if (p.causal) {  // the block's last query position bounds the own keys it can see
     const int last_row = min(rows_q, (qb + 1) * QB) - 1;
-    kend = min(kend, p.n_cache + last_row / G + 1);
+    TE = min(TE, TP + (last_row / G) / AKT + 1);
   }
+  const int tb = sp * tiles_per_split;
+  const int te = min(TE, tb + tiles_per_split);
 
   // Q fragments (B operand): query row rho = qb*QB + wid*QW + nq*16 + col, hd chunk c
   bf16x8_t qf[NQ][NC];
@@ -96,6 +90,45 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
     }
   }
 
+  // segment bases of this (sequence, kv head)
+  const bf16_t* kpre = (const bf16_t*)p.ck + (size_t)b * p.c_kSeq + (size_t)kvh * p.c_kHead;
+  const bf16_t* vpre = (const bf16_t*)p.cv + (size_t)b * p.c_vSeq + (size_t)kvh * p.c_vHead;
+  const bf16_t* kslf = (const bf16_t*)p.sk + (size_t)(t + p.s_seq0) * p.s_kSeq + (size_t)kvh * p.s_kHead;
+  const bf16_t* vslf = (const bf16_t*)p.sv + (size_t)(t + p.s_seq0) * p.s_vSeq + (size_t)kvh * p.s_vHead;
+
+  // lane-constant parts of the DMA addresses
+  int krow[KL], kchunk[KL], vrow[VL], vchunk[VL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) {
+    krow[i] = (wid * KL + i) * RPI + lane / CK;
+    kchunk[i] = (lane % CK) ^ (krow[i] & (CK - 1));
+  }
+#pragma unroll
+  for (int i = 0; i < VL; ++i) {
+    vrow[i] = (wid * VL + i) * 8 + (lane >> 3);
+    vchunk[i] = (lane & 7) ^ ((vrow[i] >> 1) & 7);
+  }
+  auto issue = [&](int tile, int slot) {
+    bf16_t* base = smem + slot * STAGE;
+    const bool pre = tile < TP;
+    const int k0 = pre ? tile * AKT : (tile - TP) * AKT;  // first key of the tile in its segment
+    const int klen = pre ? p.n_cache : p.n_self;
+    const bf16_t* kb = pre ? kpre : kslf;
+    const int64_t kpos = pre ? p.c_kPos : p.s_kPos;
+    const bf16_t* vb = pre ? vpre : vslf;
+    const int64_t vr = pre ? p.c_vRow : p.s_vRow;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int key = min(k0 + krow[i], klen - 1);  // rows past the segment load a valid row (masked)
+      __builtin_amdgcn_global_load_lds((const void*)(kb + (size_t)key * kpos + kchunk[i] * 8),
+                                       LDS_PTR(base + (wid * KL + i) * 512), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VL; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(vb + (size_t)vrow[i] * vr + k0 + vchunk[i] * 8),
+                                       LDS_PTR(base + KST + (wid * VL + i) * 512), 16, 0, 0);
+  };
+
   floatx4 o[NH][NQ];
 #pragma unroll
   for (int h = 0; h < NH; ++h)
@@ -108,74 +141,24 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
     lrun[nq] = 0.f;
   }
 
-  // K/V tile loads are register double-buffered: the next tile's rows are in flight while the
-  // matrix cores work on the current one.
-  constexpr int KP = AKT / KROWS;  // K row passes per thread
-  uint4 kreg[KP], vreg[4];
-  const bool vthread = tid < 16 * CPR;
-  int dep_base = kbeg;
-  auto gload = [&](int k0) {
 #pragma unroll
-    for (int pass = 0; pass < KP; ++pass) {
-      const int j = k0 + pass * KROWS + tid / CPR;
-      kreg[pass] = j < kend ? *(const uint4*)(akv_row(p, p.ck, p.sk, j, b, t, kvh, sdep, dep_base) + (tid % CPR) * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-    if (vthread) {
-      const int kq = tid / CPR, c = tid % CPR;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = k0 + kq * 4 + u;
-        vreg[u] = j < kend ? *(const uint4*)(akv_row(p, p.cv, p.sv, j, b, t, kvh, sdep, dep_base) + c * 8)
-                           : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int pass = 0; pass < KP; ++pass) {
-      const int r = pass * KROWS + tid / CPR, c = tid % CPR;
-      *(uint4*)&sK[r * KLD + c * 8] = kreg[pass];
-    }
-    if (vthread) {  // transpose: 4 consecutive keys x 8 hd values -> 8 rows of V^T
-      const int kq = tid / CPR, c = tid % CPR;
-      const bf16_t* e0 = (const bf16_t*)&vreg[0];
-      const bf16_t* e1 = (const bf16_t*)&vreg[1];
-      const bf16_t* e2 = (const bf16_t*)&vreg[2];
-      const bf16_t* e3 = (const bf16_t*)&vreg[3];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint2 w;
-        w.x = (uint32_t)e0[e] | ((uint32_t)e1[e] << 16);
-        w.y = (uint32_t)e2[e] | ((uint32_t)e3[e] << 16);
-        *(uint2*)&sV[(c * 8 + e) * VLD + kq * 4] = w;
-      }
-    }
-  };
-  // depth plane min(loop, avail[j]) - 1 of the prefix keys [kstart, kstart + DEPC) of this range
-  auto load_dep = [&](int kstart) {
-    const int lim = min(min(kend, p.n_cache), kstart + DEPC);
-    for (int j = kstart + tid; j < lim; j += 256)
-      sdep[j - kstart] = (uint8_t)(max(1, min(p.loop, (int)p.avail[(size_t)b * p.av_stride + j])) - 1);
-  };
-  if (p.core) {
-    load_dep(kbeg);
-    __syncthreads();
-  }
-  if (kbeg < kend) gload(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += AKT) {
-    __syncthreads();
-    sstore();
-    __syncthreads();
-    const int kn = k0 + AKT;
-    if (kn < kend) {
-      if (p.core && (kn - dep_base) >= DEPC) {  // next tile starts a new chunk of staged depths
-        dep_base = kn;
-        load_dep(kn);
-        __syncthreads();
-      }
-      gload(kn);
-    }
+  for (int s = 0; s < NS - 1; ++s)
+    if (tb + s < te) issue(tb + s, s);
+
+  for (int tile = tb; tile < te; ++tile) {
+    const int it = tile - tb;
+    if (tile + NS - 1 <= te)
+      wait_vmcnt_le<(NS - 2) * LPW>();
+    else
+      wait_vmcnt_le<0>();
+    // every wave's loads of this stage have landed, and every wave is done with the slot refilled below
+    lds_barrier();
+    if (tile + NS - 1 < te) issue(tile + NS - 1, (it + NS - 1) % NS);
+    const bf16_t* sK = smem + (it % NS) * STAGE;
+    const bf16_t* sV = sK + KST;
+    const bool pre = tile < TP;
+    const int k0 = pre ? tile * AKT : (tile - TP) * AKT;
+    const int klen = pre ? p.n_cache : p.n_self;
 
     // S^T = K Q^T : 4 key subtiles x NQ query subtiles
     floatx4 s[4][NQ];
@@ -187,7 +170,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t a = *(const bf16x8_t*)&sK[(ks * 16 + col) * KLD + c * 32 + quad * 8];
+        const int r = ks * 16 + col;
+        const bf16x8_t a = *(const bf16x8_t*)&sK[r * HD + (((c * 4 + quad) ^ (r & (CK - 1))) << 3)];
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq) s[ks][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nq][c], s[ks][nq], 0, 0, 0);
       }
@@ -202,9 +186,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int j = k0 + ks * 16 + quad * 4 + v;
-          bool ok = j < kend && qok[nq];
-          if (p.causal) ok = ok && (j < p.n_cache || j - p.n_cache <= qpos[nq]);
+          const int kk = k0 + ks * 16 + quad * 4 + v;  // key within its segment
+          bool ok = kk < klen && qok[nq];
+          if (p.causal && !pre) ok = ok && kk <= qpos[nq];
           const float sc = ok ? s[ks][nq][v] * p.scale : -INFINITY;
           s[ks][nq][v] = sc;
           mx = fmaxf(mx, sc);
@@ -243,16 +227,18 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
     // O^T += V^T P^T ; lane's 8 k-slots are keys 32c2 + 4quad + {0..3} and 32c2 + 16 + 4quad + {0..3}
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
+      const int r = h * 16 + col;
+      const int sw = (r >> 1) & 7;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16_t* vr = &sV[(h * 16 + col) * VLD + c2 * 32 + quad * 4];
+        const int lo = c2 * 32 + quad * 4, hi = lo + 16;  // first keys of the two 8-byte pieces
+        const uint2 a0 = *(const uint2*)&sV[r * AKT + ((((lo >> 3) ^ sw) << 3) | (lo & 7))];
+        const uint2 a1 = *(const uint2*)&sV[r * AKT + ((((hi >> 3) ^ sw) << 3) | (hi & 7))];
         uint4 w;
-        const uint2 lo = *(const uint2*)vr;
-        const uint2 hi = *(const uint2*)(vr + 16);
-        w.x = lo.x;
-        w.y = lo.y;
-        w.z = hi.x;
-        w.w = hi.y;
+        w.x = a0.x;
+        w.y = a0.y;
+        w.z = a1.x;
+        w.w = a1.y;
         const bf16x8_t a = *(bf16x8_t*)&w;
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq) o[h][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[c2][nq], o[h][nq], 0, 0, 0);
@@ -326,10 +312,15 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int n_pairs, i
 }
 
 template <int HD, int QW>
-static void run_attn(const AttnParams& p, int n_pairs, int n_qblocks, int n_splits, int kps, hipStream_t st) {
+static void run_attn(const AttnParams& p, int n_pairs, int n_qblocks, int n_splits, int tps, int ns, hipStream_t st) {
   const int total = n_pairs * n_qblocks * n_splits;
   const int grid = ((total + 7) / 8) * 8;
-  k_attn_mfma<HD, QW><<<grid, 256, 0, st>>>(p, n_pairs, n_qblocks, n_splits, kps);
+  if (ns == 2)
+    k_attn_mfma<HD, QW, 2><<<grid, 256, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+  else if (ns == 4)
+    k_attn_mfma<HD, QW, 4><<<grid, 256, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+  else
+    k_attn_mfma<HD, QW, 3><<<grid, 256, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   if (n_splits > 1) {
     const int rows_q = (p.Hq / p.Hkv) * p.rows_per_seq;
     const int waves = n_pairs * rows_q;
@@ -340,31 +331,33 @@ static void run_attn(const AttnParams& p, int n_pairs, int n_qblocks, int n_spli
 bool attn_mfma_supported(int hd) { return hd == 32 || hd == 64 || hd == 128; }
 
 // p.n_rows / rows_per_seq = sequence slots; p.part must hold n_pairs * rows_q * max_splits * (hd + 2)
-// floats when max_splits > 1.
-void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int force_splits, int force_qw) {
+// floats when max_splits > 1.  Key rows must be 16-byte aligned and V^T rows (c_vRow, s_vRow
+// elements) multiples of 64 elements; n_cache >= 1 or n_self >= 1.
+void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int force_splits, int force_qw,
+                      int force_ns) {
   if (p.n_rows <= 0) return;
   const int n_seq = p.n_rows / p.rows_per_seq;
   const int n_pairs = n_seq * p.Hkv;
   const int rows_q = (p.Hq / p.Hkv) * p.rows_per_seq;
-  // 16 query rows per wave measured faster than 32 at 128 query rows per pair (more blocks in
-  // flight per key range); 32 only where one pair has more than 256 query rows
-  const int QW = (force_qw == 16 || force_qw == 32) ? force_qw : (rows_q <= 256 ? 16 : 32);
+  // measured (8B shape, 128 and 256 query rows per pair): 16 query rows per wave and a
+  // two-stage ring (64 KB of LDS, two blocks per compute unit) beat wider and deeper variants
+  const int QW = (force_qw == 16 || force_qw == 32) ? force_qw : 16;
   const int QB = 4 * QW;
   const int n_qblocks = (rows_q + QB - 1) / QB;
-  const int n_keys = p.n_cache + p.n_self;
-  const int n_tiles = (n_keys + AKT - 1) / AKT;
+  const int n_tiles = (p.n_cache + AKT - 1) / AKT + (p.n_self + AKT - 1) / AKT;
   int splits = 1;
   if (!p.causal && p.part) {
-    // about three resident blocks per compute unit, and at least 3 key tiles per split
-    const int want = (768 + n_pairs * n_qblocks - 1) / (n_pairs * n_qblocks);
-    splits = min(min(want, max(1, (n_tiles + 2) / 3)), max_splits);
+    // about two blocks per compute unit and at least two splits, at least 2 key tiles per split
+    const int want = max(2, (512 + n_pairs * n_qblocks - 1) / (n_pairs * n_qblocks));
+    splits = min(min(want, max(1, n_tiles / 2)), max_splits);
     if (force_splits > 0) splits = min(force_splits, max_splits);
     if (splits < 1) splits = 1;
   }
-  const int kps = ((n_tiles + splits - 1) / splits) * AKT;
-  splits = (n_keys + kps - 1) / kps;
+  const int tps = (n_tiles + splits - 1) / splits;
+  splits = (n_tiles + tps - 1) / tps;
   if (splits < 1) splits = 1;
-#define GO(H, Q) run_attn<H, Q>(p, n_pairs, n_qblocks, splits, kps, st)
+  const int ns = (force_ns >= 2 && force_ns <= 4) ? force_ns : 2;
+#define GO(H, Q) run_attn<H, Q>(p, n_pairs, n_qblocks, splits, tps, ns, st)
   if (p.hd == 128) {
     if (QW == 16) GO(128, 16); else GO(128, 32);
   } else if (p.hd == 64) {

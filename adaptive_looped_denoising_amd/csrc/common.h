@@ -19,6 +19,27 @@ template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) {
   return (bf16_t)(u >> 16);
 }
 
+// LDS address operand of the direct global->LDS loads (each lane's bytes land at M0 + lane * size).
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt constraining only the vector-memory counter to <= N (gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14], expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without the release/acquire fence of __syncthreads() (which would wait for
+// every load in flight, including the prefetched pipeline stages).  Callers order their own
+// memory operations with explicit waits; the empty asm keeps the compiler from moving LDS
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

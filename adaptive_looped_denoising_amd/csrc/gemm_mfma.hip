@@ -259,15 +259,6 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16_t* __restrict__ A,
 // work on the oldest one.  Row r of a stage keeps its eight 16-byte k-chunks XOR-swizzled
 // (chunk c at slot c ^ (r & 7)) so that the 16 rows a fragment read touches spread over the banks.
 // Rows past M / N load row 0 (never stored).
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-// s_waitcnt constraining only the vector-memory counter to <= N (gfx9 encoding: vmcnt in bits
-// [3:0] and [15:14], expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
 
 template <int BM, int BN, int WM, int WN, int NS, int EPI, bool SPLIT>
 __global__ __launch_bounds__(256) void k_gemm_pipe(const bf16_t* __restrict__ A, int lda,

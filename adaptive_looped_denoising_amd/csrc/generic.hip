@@ -108,23 +108,26 @@ void launch_gemm_generic(int dtype, int epi, const void* A, int lda, const void*
 }
 
 // ---------------------------------------------------------------------------------------------
-// Attention of one query row and head per wave: keys are the prefix keys (from the depth-aware
-// cache; Core layers read position j at depth min(loop, avail[j])) followed by the rows' own keys
-// (all of them, or positions <= the query's when causal).  Online softmax over chunks of 64
-// keys: lane j scores key j, then every lane accumulates its head-dim elements.
+// Attention of one query row and head per wave: keys are the prefix keys (the cache slot of the
+// loop's depth plane) followed by the rows' own keys (all of them, or positions <= the query's
+// when causal).  Online softmax over chunks of 64 keys: lane j scores key j, then every lane
+// accumulates its head-dim elements.
 template <typename T>
-__device__ __forceinline__ const T* attn_kv_ptr(const AttnParams& p, const void* cbase, const void* sbase, int j,
-                                                int b, int t, int kvh) {
+__device__ __forceinline__ const T* attn_k_ptr(const AttnParams& p, int j, int b, int t, int kvh) {
+  if (j < p.n_cache) return (const T*)p.ck + (size_t)b * p.c_kSeq + (size_t)kvh * p.c_kHead + (size_t)j * p.c_kPos;
+  const int jj = j - p.n_cache;
+  return (const T*)p.sk + (size_t)(t + p.s_seq0) * p.s_kSeq + (size_t)kvh * p.s_kHead + (size_t)jj * p.s_kPos;
+}
+// element e of value j is at the returned pointer + e * (returned row stride)
+template <typename T>
+__device__ __forceinline__ const T* attn_v_ptr(const AttnParams& p, int j, int b, int t, int kvh, int64_t* row) {
   if (j < p.n_cache) {
-    size_t off = (size_t)b * p.c_sSeq + (size_t)kvh * p.c_sHead + (size_t)j * p.c_sPos;
-    if (p.core) {
-      const int dep = max(1, min(p.loop, (int)p.avail[(size_t)b * p.av_stride + j]));
-      off += (size_t)(dep - 1) * p.c_plane;
-    }
-    return (const T*)cbase + off;
+    *row = p.c_vRow;
+    return (const T*)p.cv + (size_t)b * p.c_vSeq + (size_t)kvh * p.c_vHead + j;
   }
   const int jj = j - p.n_cache;
-  return (const T*)sbase + (size_t)(t + p.s_seq0) * p.s_sSeq + (size_t)kvh * p.s_sHead + (size_t)jj * p.s_sPos;
+  *row = p.s_vRow;
+  return (const T*)p.sv + (size_t)(t + p.s_seq0) * p.s_vSeq + (size_t)kvh * p.s_vHead + jj;
 }
 
 template <typename T>
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(64) void k_attn_generic(AttnParams p) {
     const int j = j0 + lane;
     float sc = -INFINITY;
     if (j < n_keys) {
-      const T* kp = attn_kv_ptr<T>(p, p.ck, p.sk, j, b, t, kvh);
+      const T* kp = attn_k_ptr<T>(p, j, b, t, kvh);
       float dot = 0.f;
       for (int e = 0; e < p.hd; ++e) dot += qs[e] * to_f(kp[e]);
       sc = dot * p.scale;
@@ -158,9 +161,10 @@ __global__ __launch_bounds__(64) void k_attn_generic(AttnParams p) {
     const int nk = min(64, n_keys - j0);
     for (int jj = 0; jj < nk; ++jj) {
       const float pw = __shfl(pj, jj, 64);
-      const T* vp = attn_kv_ptr<T>(p, p.cv, p.sv, j0 + jj, b, t, kvh);
-      if (lane < p.hd) acc0 += pw * to_f(vp[lane]);
-      if (lane + 64 < p.hd) acc1 += pw * to_f(vp[lane + 64]);
+      int64_t vr;
+      const T* vp = attn_v_ptr<T>(p, j0 + jj, b, t, kvh, &vr);
+      if (lane < p.hd) acc0 += pw * to_f(vp[(size_t)lane * vr]);
+      if (lane + 64 < p.hd) acc1 += pw * to_f(vp[(size_t)(lane + 64) * vr]);
     }
     m = mn;
   }

@@ -132,8 +132,8 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
                                                       float eps, const float* __restrict__ cosT,
                                                       const float* __restrict__ sinT, TA* __restrict__ q_out,
                                                       TA* __restrict__ k_out, TA* __restrict__ v_out,
-                                                      int64_t sSeq, int64_t sHead, int64_t sPos, int seq0,
-                                                      int splits) {
+                                                      int64_t kSeq, int64_t kHead, int64_t kPos, int64_t vSeq,
+                                                      int64_t vHead, int64_t vRow, int seq0, int splits) {
   const int NH = Hq + 2 * Hkv;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -150,13 +150,14 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
   };
   const int jpos = r % rows_per_seq;
   const int pos = pos0 + jpos;
-  const size_t kv_off = (size_t)(seq0 + r / rows_per_seq) * sSeq + (size_t)jpos * sPos;
-  if (hh >= Hq + Hkv) {  // value head: copy
+  const size_t seq = (size_t)(seq0 + r / rows_per_seq);
+  if (hh >= Hq + Hkv) {  // value head: copy, transposed (positions contiguous)
     const int h = hh - Hq - Hkv;
-    TA* dst = v_out + kv_off + (size_t)h * sHead;
-    for (int e = lane; e < hd; e += 64) dst[e] = from_f<TA>(val(e));
+    TA* dst = v_out + seq * vSeq + (size_t)h * vHead + jpos;
+    for (int e = lane; e < hd; e += 64) dst[(size_t)e * vRow] = from_f<TA>(val(e));
     return;
   }
+  const size_t kv_off = seq * kSeq + (size_t)jpos * kPos;
   const bool is_q = hh < Hq;
   const TW* g = is_q ? qn : kn;
   float x1[2], x2[2];
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
-  TA* dst = is_q ? q_out + ((size_t)r * Hq + hh) * hd : k_out + kv_off + (size_t)(hh - Hq) * sHead;
+  TA* dst = is_q ? q_out + ((size_t)r * Hq + hh) * hd : k_out + kv_off + (size_t)(hh - Hq) * kHead;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int p = lane + 64 * t;
@@ -511,14 +512,15 @@ void launch_exit_gate(int dtype, const void* rows, int n_rows, int d, const void
 
 void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_seq, int pos0, int Hq, int Hkv,
                          int hd, const void* qn, const void* kn, float eps, const float* cosT,
-                         const float* sinT, void* q_out, void* k_out, void* v_out, int64_t sSeq, int64_t sHead,
-                         int64_t sPos, int seq0, hipStream_t st, int splits) {
+                         const float* sinT, void* q_out, void* k_out, void* v_out, int64_t kSeq, int64_t kHead,
+                         int64_t kPos, int64_t vSeq, int64_t vHead, int64_t vRow, int seq0, hipStream_t st,
+                         int splits) {
   if (n_rows <= 0) return;
   const int waves = n_rows * (Hq + 2 * Hkv);
   DISPATCH_T(dtype, T,
              k_qk_norm_rope<T, T><<<(waves + 3) / 4, 256, 0, st>>>(
                  qkv, n_rows, rows_per_seq, pos0, Hq, Hkv, hd, (const T*)qn, (const T*)kn, eps, cosT, sinT,
-                 (T*)q_out, (T*)k_out, (T*)v_out, sSeq, sHead, sPos, seq0, splits));
+                 (T*)q_out, (T*)k_out, (T*)v_out, kSeq, kHead, kPos, vSeq, vHead, vRow, seq0, splits));
 }
 
 void launch_swiglu(int dtype, const float* gu, int n_rows, int F, void* act, hipStream_t st) {

@@ -29,6 +29,11 @@ struct GemmEpi {
 // seq_map[t], or t).  Keys: n_cache prefix keys at ck/cv + b*c_sSeq + h*c_sHead + j*c_sPos
 // (+ (min(loop, avail[b*av_stride + j]) - 1) * c_plane for Core layers), then the rows' own
 // keys at sk/sv + (t + s_seq0)*s_sSeq + h*s_sHead + jj*s_sPos (jj <= i when causal).
+// Attention operands.  Keys are the prefix keys j < n_cache (cache slot, already the right depth
+// plane) followed by the rows' own keys (n_self of them).  K rows are hd-contiguous:
+// k(j) = base + seq * kSeq + kvh * kHead + j * kPos.  V is stored transposed, positions
+// contiguous: v(j, e) = base + seq * vSeq + kvh * vHead + e * vRow + j, with vRow a multiple of
+// 64 (whole 64-key tiles stay inside a row).
 struct AttnParams {
   const void* q = nullptr;  // [n_rows][Hq][hd]
   void* out = nullptr;      // [n_rows][Hq*hd]
@@ -36,15 +41,12 @@ struct AttnParams {
   float scale = 1.f;
   const void* ck = nullptr;
   const void* cv = nullptr;
-  int64_t c_sSeq = 0, c_sHead = 0, c_sPos = 0, c_plane = 0;
+  int64_t c_kSeq = 0, c_kHead = 0, c_kPos = 0, c_vSeq = 0, c_vHead = 0, c_vRow = 0;
   int n_cache = 0;
-  const uint8_t* avail = nullptr;
-  int64_t av_stride = 0;
-  int loop = 1, core = 0;
-  const int32_t* seq_map = nullptr;
+  const int32_t* seq_map = nullptr;  // sequence slot t -> cache sequence (null: identity)
   const void* sk = nullptr;
   const void* sv = nullptr;
-  int64_t s_sSeq = 0, s_sHead = 0, s_sPos = 0;
+  int64_t s_kSeq = 0, s_kHead = 0, s_kPos = 0, s_vSeq = 0, s_vHead = 0, s_vRow = 0;
   int n_self = 0, causal = 0, s_seq0 = 0;
   // fast path scratch: split-KV partials
   float* part = nullptr;
@@ -62,10 +64,12 @@ void launch_exit_gate(int dtype, const void* rows, int n_rows, int d, const void
                       hipStream_t st);
 // qkv rows come from `qkv`, or are the sum of `splits` deferred split-K partials [s][row][:] of
 // the projection when splits > 1 (qkv then points at the partials).
+// K rows go to k_out + seq * kSeq + kvh * kHead + pos * kPos (hd-contiguous), V transposed to
+// v_out + seq * vSeq + kvh * vHead + e * vRow + pos, seq = seq0 + row / rows_per_seq.
 void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_seq, int pos0, int Hq, int Hkv,
                          int hd, const void* qn, const void* kn, float eps, const float* cosT, const float* sinT,
-                         void* q_out, void* k_out, void* v_out, int64_t sSeq, int64_t sHead, int64_t sPos,
-                         int seq0, hipStream_t st, int splits = 1);
+                         void* q_out, void* k_out, void* v_out, int64_t kSeq, int64_t kHead, int64_t kPos,
+                         int64_t vSeq, int64_t vHead, int64_t vRow, int seq0, hipStream_t st, int splits = 1);
 void launch_swiglu(int dtype, const float* gu, int n_rows, int F, void* act, hipStream_t st);
 void launch_softstat_combine(const SoftStat* part, int n_rows, int n_tiles, const int32_t* n_dev, float* H,
                              float* lse, int32_t* tok, hipStream_t st);
@@ -104,11 +108,23 @@ void launch_gemm_generic(int dtype, int epi, const void* A, int lda, const void*
                          const int32_t* m_dev, const GemmEpi& ep, hipStream_t st);
 void launch_attn_generic(int dtype, const AttnParams& p, hipStream_t st);
 bool attn_mfma_supported(int hd);
-void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int force_splits = 0, int force_qw = 0);
+void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int force_splits = 0, int force_qw = 0,
+                      int force_ns = 0);
 
-void launch_fill_kv_synth(int dtype, void* slot_base, int B, int Hkv, int P, int P_max, int hd, uint32_t seed,
-                          uint32_t tensor, float scale, hipStream_t st);
+// Cache slot fill with the counter-based synthetic values: logical element (b, kvh, j, e) is
+// generator index ((b * Hkv + kvh) * P + j) * hd + e; stored K-layout ([b][kvh][P_pitch][hd]) or,
+// with transposed, V-layout ([b][kvh][hd][P_pitch]).
+void launch_fill_kv_synth(int dtype, void* slot_base, int B, int Hkv, int P, int P_pitch, int hd, uint32_t seed,
+                          uint32_t tensor, float scale, bool transposed, hipStream_t st);
 void launch_fill_u8(uint8_t* dst, size_t n, uint8_t v, hipStream_t st);
 void launch_copy_avail(uint8_t* dst, const uint8_t* src, size_t n, hipStream_t st);
+// Depth planes of one Core layer's cache (plane p = depth p + 1, plane_elems apart): for every
+// position j with avail[b][j] = a_j, plane p takes the values of plane max(1, min(p + 1, a_j)) - 1,
+// so that reading plane s - 1 at loop s gives every key at depth min(s, a_j).
+void launch_materialize_depth(int dtype, void* k_plane0, void* v_plane0, int64_t plane_elems, int k_max, int B,
+                              int Hkv, int P, int P_pitch, int hd, const uint8_t* avail, hipStream_t st);
+// V rows j0 .. j0+n-1 of a transposed cache slot, every kv head, to dst [Hkv][n][hd].
+void launch_read_v_rows(int dtype, const void* slot_base, int b, int Hkv, int P_pitch, int hd, int j0, int n,
+                        void* dst, hipStream_t st);
 
 }  // namespace alodlm

@@ -29,7 +29,10 @@ struct Plan {
   size_t U, a, ro_map, ro_rows, ncommit, stop, seq_loops, act_seq0, act_seq1, src_slot, cnt;
   size_t attn_part, gemm_part;
   // sizes
-  int64_t slot_elems = 0;  // elements of one cache slot: B * Hkv * P * hd
+  // Cache slot: K [B][Hkv][Pp][hd], V transposed [B][Hkv][hd][Pp], Pp = max_prefix rounded up to
+  // 64 (a 64-key tile never leaves a V row).  Own-block V likewise [B][Hkv][hd][Lp].
+  int64_t slot_elems = 0;  // elements of one cache slot: B * Hkv * Pp * hd
+  int64_t Pp = 0, Lp = 0;
   int n_slots = 0, rows_step = 0, rows_max = 0, prefill_rows = 0, n_vtiles = 0, max_pos = 0;
   int attn_splits = 0;
   size_t gemm_part_elems = 0;
@@ -73,7 +76,9 @@ Plan make_plan(const alodlm_config& c) {
   const int64_t Hq = c.n_q_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
   const int64_t qkv_out = (Hq + 2 * Hkv) * hd;
   p.n_slots = c.n_pre + c.n_core * c.k_max + c.n_coda;
-  p.slot_elems = B * Hkv * P * hd;
+  p.Pp = (P + 63) / 64 * 64;
+  p.Lp = (L + 63) / 64 * 64;
+  p.slot_elems = B * Hkv * p.Pp * hd;
   p.rows_step = (int)(B * L);
   p.prefill_rows = c.max_prefill_rows > 0 ? c.max_prefill_rows : (int)(B * P);
   p.rows_max = p.rows_step > p.prefill_rows ? p.rows_step : p.prefill_rows;
@@ -99,7 +104,7 @@ Plan make_plan(const alodlm_config& c) {
   p.qkv = take(sizeof(float) * R * qkv_out);
   p.q = take(es * R * Hq * hd);
   p.kself = take(es * Rs * Hkv * hd);
-  p.vself = take(es * Rs * Hkv * hd);
+  p.vself = take(es * B * Hkv * hd * p.Lp);
   p.gu = take(sizeof(float) * R * 2 * F);
   p.act = take(es * R * F);
   p.r = take(es * Rs * d);
@@ -147,6 +152,7 @@ struct alodlm_ctx {
   bool force_generic = false;  // diagnostics: ALODLM_FORCE_GENERIC=1 keeps bf16 on the vector-ALU kernels
   int attn_force_splits = 0;   // diagnostics: ALODLM_ATTN_SPLITS=n fixes the key splits of step attention
   int attn_force_qw = 0;       // diagnostics: ALODLM_ATTN_QW=16|32 fixes the query rows per wave
+  int attn_force_ns = 0;       // diagnostics: ALODLM_ATTN_NS=2..4 fixes the LDS ring depth
   // diagnostics: per-class kernel timing with event pairs on the context stream
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;
@@ -254,7 +260,7 @@ void attention(alodlm_ctx* c, const AttnParams& p) {
   if (c->cfg.dtype == ALODLM_DTYPE_BF16 && !c->force_generic && attn_mfma_supported(p.hd)) {
     AttnParams q = p;
     q.part = c->at<float>(c->plan.attn_part);
-    launch_attn_mfma(q, c->plan.attn_splits, c->st, c->attn_force_splits, c->attn_force_qw);
+    launch_attn_mfma(q, c->plan.attn_splits, c->st, c->attn_force_splits, c->attn_force_qw, c->attn_force_ns);
     return;
   }
   launch_attn_generic(dt(c), p, c->st);
@@ -323,54 +329,62 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   ap.Hkv = Hkv;
   ap.hd = hd;
   ap.scale = 1.0f / sqrtf((float)hd);
-  const int64_t Pm = g.max_prefix;
+  const int64_t Pp = p.Pp, Lp = p.Lp;
   if (lc.mode == PREFILL) {
     const int slot = slot_of(g, li, lc.depth);
     void* kd = cache_slot(c, false, slot);
     void* vd = cache_slot(c, true, slot);
-    const int64_t sSeq = (int64_t)Hkv * Pm * hd, sHead = Pm * hd, sPos = hd;
+    const int64_t kSeq = (int64_t)Hkv * Pp * hd, kHead = Pp * hd, kPos = hd;
+    const int64_t vSeq = (int64_t)Hkv * hd * Pp, vHead = hd * Pp, vRow = Pp;
     c->tic(ALODLM_K_NORM_ROPE);
     launch_qk_norm_rope(dt(c), qkv_src, n, lc.rows_per_seq, 0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
-                        c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, kd, vd, sSeq, sHead, sPos, lc.seq0,
-                        c->st, qkv_splits);
+                        c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, kd, vd, kSeq, kHead, kPos, vSeq, vHead,
+                        vRow, lc.seq0, c->st, qkv_splits);
     c->toc();
     ap.n_cache = 0;
     ap.sk = kd;
     ap.sv = vd;
-    ap.s_sSeq = sSeq;
-    ap.s_sHead = sHead;
-    ap.s_sPos = sPos;
+    ap.s_kSeq = kSeq;
+    ap.s_kHead = kHead;
+    ap.s_kPos = kPos;
+    ap.s_vSeq = vSeq;
+    ap.s_vHead = vHead;
+    ap.s_vRow = vRow;
     ap.s_seq0 = lc.seq0;
     ap.n_self = lc.rows_per_seq;
     ap.causal = 1;
   } else {
     void* ks = c->at<void>(p.kself);
     void* vs = c->at<void>(p.vself);
-    const int64_t sSeq = (int64_t)lc.rows_per_seq * Hkv * hd, sHead = hd, sPos = (int64_t)Hkv * hd;
+    const int64_t kSeq = (int64_t)lc.rows_per_seq * Hkv * hd, kHead = hd, kPos = (int64_t)Hkv * hd;
+    const int64_t vSeq = (int64_t)Hkv * hd * Lp, vHead = hd * Lp, vRow = Lp;
     c->tic(ALODLM_K_NORM_ROPE);
     launch_qk_norm_rope(dt(c), qkv_src, n, lc.rows_per_seq, lc.pos0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
-                        c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, ks, vs, sSeq, sHead, sPos, 0, c->st,
-                        qkv_splits);
+                        c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, ks, vs, kSeq, kHead, kPos, vSeq, vHead,
+                        vRow, 0, c->st, qkv_splits);
     c->toc();
+    // Core layers read the depth plane of the loop: the planes are materialised after the prefill
+    // (plane s holds every position at depth min(s, available depth))
     const bool core = li >= g.n_pre && li < g.n_pre + g.n_core;
-    const int slot = slot_of(g, li, 1);
+    const int slot = slot_of(g, li, core ? lc.loop : 1);
     ap.ck = cache_slot(c, false, slot);
     ap.cv = cache_slot(c, true, slot);
-    ap.c_sSeq = (int64_t)Hkv * Pm * hd;
-    ap.c_sHead = Pm * hd;
-    ap.c_sPos = hd;
-    ap.c_plane = p.slot_elems;
+    ap.c_kSeq = (int64_t)Hkv * Pp * hd;
+    ap.c_kHead = Pp * hd;
+    ap.c_kPos = hd;
+    ap.c_vSeq = (int64_t)Hkv * hd * Pp;
+    ap.c_vHead = hd * Pp;
+    ap.c_vRow = Pp;
     ap.n_cache = lc.prefix_len;
-    ap.avail = c->at<uint8_t>(p.avail);
-    ap.av_stride = lc.prefix_len;
-    ap.loop = lc.loop;
-    ap.core = core;
     ap.seq_map = lc.seq_map;
     ap.sk = ks;
     ap.sv = vs;
-    ap.s_sSeq = sSeq;
-    ap.s_sHead = sHead;
-    ap.s_sPos = sPos;
+    ap.s_kSeq = kSeq;
+    ap.s_kHead = kHead;
+    ap.s_kPos = kPos;
+    ap.s_vSeq = vSeq;
+    ap.s_vHead = vHead;
+    ap.s_vRow = vRow;
     ap.n_self = lc.rows_per_seq;
     ap.causal = 0;
   }
@@ -508,6 +522,7 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
   c->force_generic = fg && fg[0] == '1';
   if (const char* v = getenv("ALODLM_ATTN_SPLITS")) c->attn_force_splits = atoi(v);
   if (const char* v = getenv("ALODLM_ATTN_QW")) c->attn_force_qw = atoi(v);
+  if (const char* v = getenv("ALODLM_ATTN_NS")) c->attn_force_ns = atoi(v);
   // RoPE tables, computed in double on the host: angle(pos, i) = pos * theta^(-2i/hd)
   const int half = cfg->head_dim / 2;
   std::vector<float> cs((size_t)plan.max_pos * half), sn((size_t)plan.max_pos * half);
@@ -519,6 +534,13 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
     }
   hipError_t e1 = hipMemcpyAsync(c->ws + plan.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, c->st);
   hipError_t e2 = hipMemcpyAsync(c->ws + plan.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, c->st);
+  // V rows are read in whole 64-key tiles whose masked keys get probability 0; their padding must
+  // hold finite values (0 * NaN would poison the sum), so the V cache and own-block V start at zero
+  const size_t es = esize(cfg->dtype);
+  if (e1 == hipSuccess) e1 = hipMemsetAsync(c->ws + plan.vcache, 0, es * plan.slot_elems * plan.n_slots, c->st);
+  if (e1 == hipSuccess)
+    e1 = hipMemsetAsync(c->ws + plan.vself, 0, es * (size_t)cfg->max_batch * cfg->n_kv_heads * cfg->head_dim * plan.Lp,
+                        c->st);
   hipError_t e3 = hipStreamSynchronize(c->st);
   if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
     g_create_error = std::string("RoPE table upload: ") +
@@ -529,6 +551,19 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
   *out = c;
   return ALODLM_OK;
 }
+
+namespace {
+// Fill each Core layer's higher depth planes from its available depth (see launch_materialize_depth).
+void materialize_depths(alodlm_ctx* c, int batch, int prefix_len) {
+  const alodlm_config& g = c->cfg;
+  const Plan& p = c->plan;
+  for (int ci = 0; ci < g.n_core; ++ci) {
+    const int s0 = slot_of(g, g.n_pre + ci, 1);
+    launch_materialize_depth(dt(c), cache_slot(c, false, s0), cache_slot(c, true, s0), p.slot_elems, g.k_max, batch,
+                             g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim, c->at<uint8_t>(p.avail), c->st);
+  }
+}
+}  // namespace
 
 int alodlm_prefill_kv(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const int32_t* prefix_ids,
                       const uint8_t* avail_depth) {
@@ -560,6 +595,7 @@ int alodlm_prefill_kv(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const in
       lc.depth = 1;
       for (int ci = 0; ci < g.n_coda; ++ci) run_layer(c, g.n_pre + g.n_core + ci, lc);
     }
+    materialize_depths(c, batch, prefix_len);
   }
   int rc = c->hip_check("prefill launch");
   if (rc) return rc;
@@ -583,11 +619,12 @@ int alodlm_prefill_kv_synthetic(alodlm_ctx* c, int32_t batch, int32_t prefix_len
   else
     launch_fill_u8(c->at<uint8_t>(p.avail), nav, (uint8_t)g.k_max, c->st);
   for (int s = 0; s < p.n_slots; ++s) {
-    launch_fill_kv_synth(dt(c), cache_slot(c, false, s), batch, g.n_kv_heads, prefix_len, g.max_prefix, g.head_dim,
-                         seed, 0x10000u + 2u * s, k_scale, c->st);
-    launch_fill_kv_synth(dt(c), cache_slot(c, true, s), batch, g.n_kv_heads, prefix_len, g.max_prefix, g.head_dim,
-                         seed, 0x10000u + 2u * s + 1u, v_scale, c->st);
+    launch_fill_kv_synth(dt(c), cache_slot(c, false, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,
+                         seed, 0x10000u + 2u * s, k_scale, false, c->st);
+    launch_fill_kv_synth(dt(c), cache_slot(c, true, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,
+                         seed, 0x10000u + 2u * s + 1u, v_scale, true, c->st);
   }
+  if (prefix_len > 0) materialize_depths(c, batch, prefix_len);
   int rc = c->hip_check("synthetic prefill launch");
   if (rc) return rc;
   c->cache_batch = batch;
@@ -797,16 +834,17 @@ int alodlm_diag_read_kv(const alodlm_ctx* c, int32_t slot, int32_t b, int32_t j0
   if (slot < 0 || slot >= c->plan.n_slots || b < 0 || b >= g.max_batch || j0 < 0 || n < 0 ||
       j0 + n > g.max_prefix)
     return ALODLM_EINVAL;
-  const size_t es = esize(g.dtype), hd = g.head_dim;
-  for (int v = 0; v < 2; ++v) {
-    const char* base = c->ws + (v ? c->plan.vcache : c->plan.kcache) + es * (size_t)c->plan.slot_elems * slot;
-    for (int h = 0; h < g.n_kv_heads; ++h) {
-      const char* src = base + es * (((size_t)b * g.n_kv_heads + h) * g.max_prefix + j0) * hd;
-      char* dst = (char*)(v ? dst_v : dst_k) + es * (size_t)h * n * hd;
-      if (hipMemcpyAsync(dst, src, es * n * hd, hipMemcpyDeviceToDevice, c->st) != hipSuccess) return ALODLM_EHIP;
-    }
+  const size_t es = esize(g.dtype), hd = g.head_dim, Pp = (size_t)c->plan.Pp;
+  const char* kbase = c->ws + c->plan.kcache + es * (size_t)c->plan.slot_elems * slot;
+  for (int h = 0; h < g.n_kv_heads; ++h) {
+    const char* src = kbase + es * (((size_t)b * g.n_kv_heads + h) * Pp + j0) * hd;
+    char* dst = (char*)dst_k + es * (size_t)h * n * hd;
+    if (hipMemcpyAsync(dst, src, es * n * hd, hipMemcpyDeviceToDevice, c->st) != hipSuccess) return ALODLM_EHIP;
   }
-  return ALODLM_OK;
+  const char* vbase = c->ws + c->plan.vcache + es * (size_t)c->plan.slot_elems * slot;
+  launch_read_v_rows(g.dtype == ALODLM_DTYPE_BF16 ? DT_BF16 : DT_FP32, vbase, b, g.n_kv_heads, (int)Pp, (int)hd, j0,
+                     n, dst_v, c->st);
+  return hipGetLastError() == hipSuccess ? ALODLM_OK : ALODLM_EHIP;
 }
 
 int64_t alodlm_diag_buffer_offset(const alodlm_ctx* c, const char* name) {

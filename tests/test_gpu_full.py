@@ -43,6 +43,33 @@ def _engine(w):
     return e
 
 
+def _read_depths(w, b, n_pos):
+    """Cache slot the GPU's slot holds position j from: Core depth slots hold every position at
+    depth min(depth, available depth), the depth a step at that loop reads."""
+    D = w.dims
+    av = synth.avail_depth(w)[b, :n_pos].astype(int)
+    src = {}
+    for slot in range(D.kv_slots(w.k_max)):
+        if D.n_pre <= slot < D.n_pre + D.n_core * w.k_max:
+            c, dp = divmod(slot - D.n_pre, w.k_max)
+            eff = np.maximum(1, np.minimum(dp + 1, av))
+            src[slot] = D.n_pre + c * w.k_max + eff - 1
+        else:
+            src[slot] = np.full(n_pos, slot)
+    return src
+
+
+def _effective(w, b, n_pos, cache):
+    """The oracle cache as the GPU stores it after the prefill (per-position depth selection)."""
+    src = _read_depths(w, b, n_pos)
+    out = {}
+    for slot, rows in src.items():
+        K = np.stack([np.asarray(cache[int(s)][0])[:, j] for j, s in enumerate(rows)], axis=1)
+        V = np.stack([np.asarray(cache[int(s)][1])[:, j] for j, s in enumerate(rows)], axis=1)
+        out[slot] = (K, V)
+    return out
+
+
 def _slot_errors(e, w, b, n_pos, cache):
     errs = []
     for slot in range(w.dims.kv_slots(w.k_max)):
@@ -76,10 +103,12 @@ def _check_prefill_prefix(w, n_pos, seqs):
     ids = synth.prefix_ids(w)
     for b in seqs:
         log("oracle prefill of the first %d positions of sequence %d" % (n_pos, b))
-        c64 = orc.prefill_sequence(ids[b][:n_pos], W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+        c64 = _effective(w, b, n_pos, orc.prefill_sequence(ids[b][:n_pos], W, w.dims, w.k_max, w.rms_eps,
+                                                           w.rope_theta))
         e64 = _slot_errors(e, w, b, n_pos, c64)
         log("seq %d per-slot worst row error: %s" % (b, " ".join("%.4f" % x for x in e64)))
-        c16 = orc.prefill_sequence(ids[b][:n_pos], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, prec="bf16")
+        c16 = _effective(w, b, n_pos, orc.prefill_sequence(ids[b][:n_pos], W, w.dims, w.k_max, w.rms_eps,
+                                                           w.rope_theta, prec="bf16"))
         drift = []
         for slot in range(len(e64)):
             d_ = 0.0
