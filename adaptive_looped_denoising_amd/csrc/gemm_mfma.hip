@@ -260,17 +260,19 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16_t* __restrict__ A,
 // (chunk c at slot c ^ (r & 7)) so that the 16 rows a fragment read touches spread over the banks.
 // Rows past M / N load row 0 (never stored).
 
+// WM x WN waves (4 or 8; with 8, two waves share each SIMD and hide each other's waits).
 template <int BM, int BN, int WM, int WN, int NS, int EPI, bool SPLIT>
-__global__ __launch_bounds__(256) void k_gemm_pipe(const bf16_t* __restrict__ A, int lda,
-                                                   const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
-                                                   int k_split, int m_tiles, int n_tiles, int splits,
-                                                   const int32_t* __restrict__ m_dev, GemmEpi ep, int F) {
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const bf16_t* __restrict__ A, int lda,
+                                                            const bf16_t* __restrict__ B, int ldb, int M, int N,
+                                                            int K, int k_split, int m_tiles, int n_tiles, int splits,
+                                                            const int32_t* __restrict__ m_dev, GemmEpi ep, int F) {
+  constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   constexpr int ROWS = BM + BN;                 // 128-byte rows per stage
   constexpr int STAGE = ROWS * 64;              // bf16 elements per stage
-  constexpr int LPW = ROWS / 32;                // load instructions per wave per stage
-  static_assert(ROWS % 32 == 0, "stage rows must split over 4 waves x 8 rows");
-  static_assert(WM * WN == 4 && TM * WM * 16 == BM && TN * WN * 16 == BN, "wave grid must tile the block");
+  constexpr int LPW = ROWS / (8 * NW);          // load instructions per wave per stage
+  static_assert(ROWS % (8 * NW) == 0, "stage rows must split over the waves x 8 rows");
+  static_assert((NW == 4 || NW == 8) && TM * WM * 16 == BM && TN * WN * 16 == BN, "wave grid must tile the block");
   __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * STAGE];
 
   const int total = m_tiles * n_tiles * splits;
@@ -675,9 +677,9 @@ template <int BM, int BN, int WM, int WN, int NS>
 static void run_pipe(int epi, bool split, dim3 grid, const bf16_t* A, int lda, const bf16_t* B, int ldb, int M,
                      int N, int K, int k_split, int mt, int nt, int splits, const int32_t* m_dev, const GemmEpi& ep,
                      int F, hipStream_t st) {
-#define GO(E, S)                                                                                               \
-  k_gemm_pipe<BM, BN, WM, WN, NS, E, S><<<grid, 256, 0, st>>>(A, lda, B, ldb, M, N, K, k_split, mt, nt, splits, \
-                                                              m_dev, ep, F)
+#define GO(E, S)                                                                                             \
+  k_gemm_pipe<BM, BN, WM, WN, NS, E, S><<<grid, WM * WN * 64, 0, st>>>(A, lda, B, ldb, M, N, K, k_split, mt, nt, \
+                                                                       splits, m_dev, ep, F)
   if (split) {
     if (epi == EPI_SWIGLU) GO(EPI_SWIGLU, true);
     else GO(EPI_STORE, true);
@@ -762,25 +764,34 @@ bool gemm_mfma_supported(int K, int lda, int ldb) { return K % GK == 0 && lda % 
 
 
 // Tile shapes (BM, BN, waves along M x N).
+// Tile shapes: BM, BN and the number of waves along N.  The SwiGLU epilogue pairs gate and up
+// 16-column groups inside one wave, so a single-pass SwiGLU needs an even count of column
+// groups per wave (BN / WN / 16); tiles without it take SwiGLU only with split-K.
 struct TileCfg {
-  int bm, bn;
+  int bm, bn, wn;
 };
-static const TileCfg kTiles[] = {{32, 128}, {64, 128}, {128, 128}, {256, 64}, {256, 128}, {128, 64}, {64, 64},
-                                 {128, 256},
-                                 // pipelined (LDS ring) variants
-                                 {128, 128}, {64, 128}, {32, 128}, {256, 64}, {64, 64}, {128, 64}, {256, 128},
-                                 {128, 256}, {256, 96}, {256, 128}, {128, 96},
-                                 // activations direct to registers, weights through the LDS ring
-                                 {256, 64}, {256, 96}, {256, 128}, {256, 96},
-                                 {256, 96}, {256, 96}, {256, 128}, {256, 64},
-                                 // dual ring: activation stages DA ahead, weight stages DB ahead
-                                 {256, 96}, {256, 96}, {128, 96}, {128, 96}, {128, 128}, {128, 128}, {32, 128},
-                                 {64, 128}, {256, 64}};
-constexpr int kNumTiles = 36;
+static const TileCfg kTiles[] = {
+    {32, 128, 4}, {64, 128, 2}, {128, 128, 2}, {256, 64, 1}, {256, 128, 1}, {128, 64, 2}, {64, 64, 2},
+    {128, 256, 2},
+    // pipelined (LDS ring) variants
+    {128, 128, 2}, {64, 128, 2}, {32, 128, 4}, {256, 64, 1}, {64, 64, 2}, {128, 64, 2}, {256, 128, 2},
+    {128, 256, 2}, {256, 96, 1}, {256, 128, 1}, {128, 96, 1},
+    // activations direct to registers, weights through the LDS ring
+    {256, 64, 1}, {256, 96, 1}, {256, 128, 1}, {256, 96, 1}, {256, 96, 1}, {256, 96, 1}, {256, 128, 1},
+    {256, 64, 1},
+    // dual ring: activation stages DA ahead, weight stages DB ahead
+    {256, 96, 1}, {256, 96, 1}, {128, 96, 1}, {128, 96, 1}, {128, 128, 2}, {128, 128, 2}, {32, 128, 4},
+    {64, 128, 2}, {256, 64, 1},
+    // eight waves (two per SIMD), LDS ring
+    {128, 192, 4}, {256, 128, 2}, {128, 128, 4}, {256, 64, 2}, {64, 192, 4}, {128, 192, 4}, {128, 128, 4},
+    {128, 128, 4}, {128, 256, 4}, {64, 128, 4}, {64, 256, 4}, {128, 192, 2}, {128, 192, 2}};
+constexpr int kNumTiles = 49;
+
+bool swiglu_single_pass_ok(int tile) { return ((kTiles[tile].bn / kTiles[tile].wn / 16) & 1) == 0; }
 
 // Measured choices (MI355X, bf16, K = 2048..12288): rows up to 48 stream the weights with the
-// 32-row pipelined tile; 49..384 rows use 128- or 256-row tiles (the dual-ring ones where they
-// measured faster); more rows use the large tiles.
+// 32-row pipelined tile; 49..384 rows mostly use the eight-wave tiles (two waves per SIMD hide
+// each other's LDS and barrier waits); more rows use the large tiles.
 // Returns the tile; *splits gets the split-K factor (0 = the generic rule).
 int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   *splits = 0;
@@ -792,17 +803,15 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
     *splits = 4;
     return N <= 4096 && K <= 4096 ? 12 : 10;
   }
-  if (M <= 64) return 9;
+  if (M <= 64 && epi == EPI_SOFTSTAT) return 9;
   if (M <= 384) {
     *splits = 1;
-    if (epi == EPI_SOFTSTAT) return M <= 128 ? 31 : 17;  // LM head: wide weight tiles, few activation re-reads
-    if (epi == EPI_SWIGLU) return M <= 128 ? 18 : 27;
-    if (K > N) {  // FFN down projection
-      *splits = 4;
-      return M <= 128 ? 34 : 8;
-    }
-    *splits = M <= 128 ? 4 : 2;
-    return 18;
+    if (epi == EPI_SOFTSTAT) return M <= 128 ? 47 : 37;  // LM head: wide weight tiles, few activation re-reads
+    if (epi == EPI_SWIGLU) return M <= 64 ? 45 : (M <= 128 ? 18 : 47);
+    // projections (QKV, O, FFN down): split-K 4 over the eight-wave tiles
+    *splits = 4;
+    if (M <= 128) return (M <= 64 || N <= 4096) ? 45 : 18;
+    return (N > 4096 && K <= N) ? 36 : 38;
   }
   *splits = 1;
   if (epi == EPI_STORE && N <= 8192) return 16;
@@ -822,8 +831,12 @@ int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, in
                      int force_splits, hipStream_t st, int force_tile, bool defer_reduce) {
   if (M <= 0 || N <= 0) return 1;
   int auto_splits = 0;
-  const int tile = (force_tile >= 0 && force_tile < kNumTiles) ? force_tile : gemm_mfma_auto_tile(epi, M, N, K,
-                                                                                                  &auto_splits);
+  int tile = (force_tile >= 0 && force_tile < kNumTiles) ? force_tile : gemm_mfma_auto_tile(epi, M, N, K,
+                                                                                            &auto_splits);
+  // a single-pass SwiGLU needs gate/up column pairs inside one wave: tiles without them run the
+  // SwiGLU with split-K 2 (epilogue in the fixed-order reduction) or, if K cannot split, on tile 18
+  const bool k_can_split = (K / GK) % 2 == 0 && (size_t)2 * M * N <= part_floats;
+  if (epi == EPI_SWIGLU && !swiglu_single_pass_ok(tile) && !k_can_split) tile = 18;
   const int BM = kTiles[tile].bm, BN = kTiles[tile].bn;
   const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
   int splits = 1;
@@ -838,6 +851,7 @@ int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, in
         splits *= 2;
     }
     if ((size_t)splits * M * N > part_floats || (K / GK) % splits != 0) splits = 1;
+    if (epi == EPI_SWIGLU && splits == 1 && !swiglu_single_pass_ok(tile)) splits = 2;  // k_can_split holds here
   }
   const int k_split = K / splits;
   const int total = mt * nt * splits;
@@ -900,6 +914,22 @@ int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, in
     case 34: R(64, 128, 2, 2, 2, 7); break;
     case 35: R(256, 64, 4, 1, 2, 6); break;
 #undef R
+#define P8(BM_, BN_, WM_, WN_, NS_) \
+  run_pipe<BM_, BN_, WM_, WN_, NS_>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, e, F, st)
+    case 36: P8(128, 192, 2, 4, 3); break;
+    case 37: P8(256, 128, 4, 2, 3); break;
+    case 38: P8(128, 128, 2, 4, 4); break;
+    case 39: P8(256, 64, 4, 2, 3); break;
+    case 40: P8(64, 192, 2, 4, 4); break;
+    case 41: P8(128, 192, 2, 4, 2); break;
+    case 42: P8(128, 128, 2, 4, 2); break;
+    case 43: P8(128, 128, 2, 4, 3); break;
+    case 44: P8(128, 256, 2, 4, 3); break;
+    case 45: P8(64, 128, 2, 4, 4); break;
+    case 46: P8(64, 256, 2, 4, 3); break;
+    case 47: P8(128, 192, 4, 2, 3); break;
+    case 48: P8(128, 192, 4, 2, 2); break;
+#undef P8
 
   }
 #undef T
