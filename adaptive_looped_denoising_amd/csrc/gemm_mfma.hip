@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) void k_gemm_ring2(const bf16_t* __restrict__ A
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   constexpr int LA = BM / 32, LB = BN / 32;     // load instructions per wave per stage
   constexpr int SA = BM * 64, SB = BN * 64;     // bf16 elements per stage
-  static_assert(BM % 32 == 0 && BN % 32 == 0 && DA >= 1 && DB >= DA, "ring shape");
+  static_assert(BM % 32 == 0 && BN % 32 == 0 && DA >= 1 && DB > DA, "ring shape (B of a stage is issued before its A)");
   static_assert(WM * WN == 4 && TM * WM * 16 == BM && TN * WN * 16 == BN, "wave grid must tile the block");
   // one LDS object for both rings: with two, the compiler's LDS-DMA tracking inserts a full
   // vector-memory wait before the fragment reads of the second
@@ -500,6 +500,145 @@ __global__ __launch_bounds__(256) void k_gemm_ring2(const bf16_t* __restrict__ A
       for (int b = 0; b < TN; ++b) {
         const int r = wn * TN * 16 + b * 16 + col;
         bfr[kc][b] = *(const bf16x8_t*)&tb[r * 64 + ((c ^ (r & 7)) << 3)];
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kc][a], bfr[kc][b], acc[a][b], 0, 0, 0);
+  }
+  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid, (SoftStat*)smem);
+}
+
+// Wave-specialised loads: eight waves all compute, but the first half of them fetch only the
+// activation tile (from L2, DA stages ahead) and the second half only the weight tile (from HBM,
+// DB stages ahead).  vmcnt counts a wave's own loads in issue order, so when one wave fetches
+// both streams, waiting for a near activation stage also waits for every weight load issued
+// before it; with one stream per wave each wave waits only on its own, and the weight stream
+// keeps DB stages of HBM latency in flight.
+// vmcnt <= c * L for the runtime count c in 0 .. D-1 (immediate forms)
+template <int L, int D, int C = 0>
+__device__ __forceinline__ void wait_stream(int c) {
+  if (c == C) {
+    wait_vmcnt_le<C * L>();
+    return;
+  }
+  if constexpr (C + 1 < D) wait_stream<L, D, C + 1>(c);
+  else wait_vmcnt_le<0>();
+}
+
+template <int BM, int BN, int WM, int WN, int DA, int DB, int EPI, bool SPLIT>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_ws(const bf16_t* __restrict__ A, int lda,
+                                                          const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
+                                                          int k_split, int m_tiles, int n_tiles, int splits,
+                                                          const int32_t* __restrict__ m_dev, GemmEpi ep, int F) {
+  constexpr int NW = WM * WN;
+  constexpr int HW = NW / 2;                    // waves per stream
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  constexpr int LA = BM / (8 * HW), LB = BN / (8 * HW);  // load instructions per loading wave per stage
+  constexpr int SA = BM * 64, SB = BN * 64;
+  static_assert(NW == 8 && BM % (8 * HW) == 0 && BN % (8 * HW) == 0 && DA >= 1 && DB >= 1, "shape");
+  static_assert(TM * WM * 16 == BM && TN * WN * 16 == BN, "wave grid must tile the block");
+  static_assert((DA - 1) * LA < 64 && (DB - 1) * LB < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[(DA + 1) * SA + (DB + 1) * SB];
+  bf16_t* const sa = smem;
+  bf16_t* const sb = smem + (DA + 1) * SA;
+
+  const int total = m_tiles * n_tiles * splits;
+  const int per = (gridDim.x + 7) >> 3;
+  const int T = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (T >= total) return;
+  const int mt = T % m_tiles;
+  const int rest = T / m_tiles;
+  const int nt = rest % n_tiles;
+  const int sp = rest / n_tiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+  int Mr = M;
+  if (m_dev) Mr = min(Mr, *m_dev);
+  if (m0 >= Mr) return;
+  const int kb = sp * k_split;
+  const int nk = (min(K, kb + k_split) - kb) / GK;
+
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int wm = wid / WN, wn = wid % WN;
+  const bool a_wave = wid < HW;
+  const int lw = a_wave ? wid : wid - HW;       // index among the waves of this stream
+
+  constexpr int LMAX = LA > LB ? LA : LB;
+  const bf16_t* src[LMAX];
+#pragma unroll
+  for (int j = 0; j < LMAX; ++j) {
+    if (a_wave) {
+      const int rho = (lw * LA + (j < LA ? j : 0)) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ (rho & 7);
+      const int gm = m0 + rho;
+      src[j] = A + (size_t)(gm < Mr ? gm : 0) * lda + c * 8;
+    } else {
+      const int rho = (lw * LB + (j < LB ? j : 0)) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ (rho & 7);
+      const int gn = n0 + rho;
+      const int ok = gn < N ? gn : 0;
+      const int brow = (EPI == EPI_SWIGLU) ? swiglu_b_row(ok, F) : ok;
+      src[j] = B + (size_t)brow * ldb + c * 8;
+    }
+  }
+  auto issue = [&](int stage) {  // this wave's share of its stream for k-stage `stage`
+    const int k = kb + stage * GK;
+    if (a_wave) {
+      bf16_t* base = sa + (stage % (DA + 1)) * SA;
+#pragma unroll
+      for (int j = 0; j < LA; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(src[j] + k), LDS_PTR(base + (lw * LA + j) * 512), 16, 0, 0);
+    } else {
+      bf16_t* base = sb + (stage % (DB + 1)) * SB;
+#pragma unroll
+      for (int j = 0; j < LB; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(src[j] + k), LDS_PTR(base + (lw * LB + j) * 512), 16, 0, 0);
+    }
+  };
+
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+  const int depth = a_wave ? DA : DB;
+  for (int s = 0; s < depth && s < nk; ++s) issue(s);
+
+  const int col = lane & 15, quad = lane >> 4;
+  for (int it = 0; it < nk; ++it) {
+    // own loads issued after stage `it`: stages it+1 .. min(it+depth-1, nk-1)
+    const int c = min(max(nk - 1 - it, 0), depth - 1);
+    if (a_wave) {
+      if (c == DA - 1) wait_vmcnt_le<(DA - 1) * LA>();
+      else wait_stream<LA, DA>(c);
+    } else {
+      if (c == DB - 1) wait_vmcnt_le<(DB - 1) * LB>();
+      else wait_stream<LB, DB>(c);
+    }
+    // every wave's share of stage `it` has landed; every wave is done with stage it-1, whose
+    // slots the issue below refills
+    lds_barrier();
+    if (it + depth < nk) issue(it + depth);
+    const bf16_t* ta = sa + (it % (DA + 1)) * SA;
+    const bf16_t* tb = sb + (it % (DB + 1)) * SB;
+    bf16x8_t af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int cc = kc * 4 + quad;
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const int r = wm * TM * 16 + a * 16 + col;
+        af[kc][a] = *(const bf16x8_t*)&ta[r * 64 + ((cc ^ (r & 7)) << 3)];
+      }
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int r = wn * TN * 16 + b * 16 + col;
+        bfr[kc][b] = *(const bf16x8_t*)&tb[r * 64 + ((cc ^ (r & 7)) << 3)];
       }
     }
 #pragma unroll
@@ -717,6 +856,28 @@ static void run_ring2(int epi, bool split, dim3 grid, const bf16_t* A, int lda, 
 #undef GO
 }
 
+template <int BM, int BN, int WM, int WN, int DA, int DB>
+static void run_ws(int epi, bool split, dim3 grid, const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N,
+                   int K, int k_split, int mt, int nt, int splits, const int32_t* m_dev, const GemmEpi& ep, int F,
+                   hipStream_t st) {
+#define GO(E, S)                                                                                             \
+  k_gemm_ws<BM, BN, WM, WN, DA, DB, E, S><<<grid, WM * WN * 64, 0, st>>>(A, lda, B, ldb, M, N, K, k_split, mt, \
+                                                                         nt, splits, m_dev, ep, F)
+  if (split) {
+    if (epi == EPI_SWIGLU) GO(EPI_SWIGLU, true);
+    else GO(EPI_STORE, true);
+  } else if (epi == EPI_STORE) {
+    GO(EPI_STORE, false);
+  } else if (epi == EPI_RESID) {
+    GO(EPI_RESID, false);
+  } else if (epi == EPI_SWIGLU) {
+    GO(EPI_SWIGLU, false);
+  } else {
+    GO(EPI_SOFTSTAT, false);
+  }
+#undef GO
+}
+
 template <int BN, int NS>
 static void run_adirect(int epi, bool split, dim3 grid, const bf16_t* A, int lda, const bf16_t* B, int ldb, int M,
                         int N, int K, int k_split, int mt, int nt, int splits, const int32_t* m_dev, const GemmEpi& ep,
@@ -784,8 +945,10 @@ static const TileCfg kTiles[] = {
     {64, 128, 2}, {256, 64, 1},
     // eight waves (two per SIMD), LDS ring
     {128, 192, 4}, {256, 128, 2}, {128, 128, 4}, {256, 64, 2}, {64, 192, 4}, {128, 192, 4}, {128, 128, 4},
-    {128, 128, 4}, {128, 256, 4}, {64, 128, 4}, {64, 256, 4}, {128, 192, 2}, {128, 192, 2}};
-constexpr int kNumTiles = 49;
+    {128, 128, 4}, {128, 256, 4}, {64, 128, 4}, {64, 256, 4}, {128, 192, 2}, {128, 192, 2},
+    // eight waves, wave-specialised loads (activation stream DA deep, weight stream DB deep)
+    {128, 192, 2}, {128, 192, 2}, {128, 192, 2}, {128, 128, 4}, {128, 128, 4}, {64, 128, 4}, {256, 128, 2}};
+constexpr int kNumTiles = 56;
 
 bool swiglu_single_pass_ok(int tile) { return ((kTiles[tile].bn / kTiles[tile].wn / 16) & 1) == 0; }
 
@@ -929,6 +1092,16 @@ int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, in
     case 46: P8(64, 256, 2, 4, 3); break;
     case 47: P8(128, 192, 4, 2, 3); break;
     case 48: P8(128, 192, 4, 2, 2); break;
+#define W(BM_, BN_, WM_, WN_, DA_, DB_) \
+  run_ws<BM_, BN_, WM_, WN_, DA_, DB_>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, e, F, st)
+    case 49: W(128, 192, 4, 2, 2, 3); break;
+    case 50: W(128, 192, 4, 2, 1, 4); break;
+    case 51: W(128, 192, 4, 2, 2, 2); break;
+    case 52: W(128, 128, 2, 4, 2, 4); break;
+    case 53: W(128, 128, 2, 4, 2, 5); break;
+    case 54: W(64, 128, 2, 4, 2, 6); break;
+    case 55: W(256, 128, 4, 2, 2, 3); break;
+#undef W
 #undef P8
 
   }

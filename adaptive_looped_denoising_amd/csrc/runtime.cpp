@@ -154,6 +154,7 @@ struct alodlm_ctx {
   int attn_force_qw = 0;       // diagnostics: ALODLM_ATTN_QW=16|32 fixes the query rows per wave
   int attn_force_ns = 0;       // diagnostics: ALODLM_ATTN_NS=2..4 fixes the LDS ring depth
   int proj_splits[3] = {0, 0, 0};  // diagnostics: ALODLM_PROJ_SPLITS=q,o,d fixes the QKV / O / down split-K
+  int proj_tiles[4] = {-1, -1, -1, -1};  // diagnostics: ALODLM_PROJ_TILES=q,o,d,gu fixes their GEMM tiles
   // diagnostics: per-class kernel timing with event pairs on the context stream
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;
@@ -233,10 +234,11 @@ bool use_mfma(const alodlm_ctx* c, int K, int lda, int ldb) {
 // With `defer`, a split-K STORE / RESID GEMM may leave its partials unreduced in the split-K
 // scratch for the consuming kernel; the return value is then the number of partials (else 1).
 int gemm(alodlm_ctx* c, int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
-         const int32_t* m_dev, const GemmEpi& ep, int F = 0, bool defer = false, int force_splits = 0) {
+         const int32_t* m_dev, const GemmEpi& ep, int F = 0, bool defer = false, int force_splits = 0,
+         int force_tile = -1) {
   if (use_mfma(c, K, lda, ldb)) {
     return launch_gemm_mfma(epi, A, lda, B, ldb, M, N, K, m_dev, ep, F, c->at<float>(c->plan.gemm_part),
-                            c->plan.gemm_part_elems, force_splits, c->st, -1, defer);
+                            c->plan.gemm_part_elems, force_splits, c->st, force_tile, defer);
   }
   if (epi == EPI_SWIGLU) {  // generic path: both halves in fp32, then silu(gate) * up
     GemmEpi e;
@@ -317,7 +319,8 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   e1.C = qkv;
   e1.ldc = qkv_out;
   c->tic(ALODLM_K_GEMM_QKV);
-  const int qkv_splits = gemm(c, EPI_STORE, xn, d, W.wqkv, d, n, qkv_out, d, nullptr, e1, 0, true, c->proj_splits[0]);
+  const int qkv_splits = gemm(c, EPI_STORE, xn, d, W.wqkv, d, n, qkv_out, d, nullptr, e1, 0, true, c->proj_splits[0],
+                             c->proj_tiles[0]);
   c->toc();
   const float* qkv_src = qkv_splits > 1 ? c->at<float>(p.gemm_part) : qkv;
 
@@ -399,7 +402,8 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   e2.ldc = d;
   c->tic(ALODLM_K_GEMM_O);
   const int o_splits =
-      gemm(c, EPI_RESID, attn, Hq * hd, W.wo, Hq * hd, n, d, Hq * hd, nullptr, e2, 0, true, c->proj_splits[1]);
+      gemm(c, EPI_RESID, attn, Hq * hd, W.wo, Hq * hd, n, d, Hq * hd, nullptr, e2, 0, true, c->proj_splits[1],
+           c->proj_tiles[1]);
   c->toc();
 
   // FFN RMSNorm; with deferred O-projection partials it also forms x_out = x_in + sum(partials)
@@ -415,14 +419,15 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   e3.act = act;
   e3.ld_act = F;
   c->tic(ALODLM_K_GEMM_GATE_UP);
-  gemm(c, EPI_SWIGLU, xn, d, W.w_gate_up, d, n, 2 * F, d, nullptr, e3, F);
+  gemm(c, EPI_SWIGLU, xn, d, W.w_gate_up, d, n, 2 * F, d, nullptr, e3, F, false, 0, c->proj_tiles[3]);
   c->toc();
   GemmEpi e4;
   e4.C = lc.x_out;
   e4.R = lc.x_out;
   e4.ldc = d;
   c->tic(ALODLM_K_GEMM_DOWN);
-  const int down_splits = gemm(c, EPI_RESID, act, F, W.w_down, F, n, d, F, nullptr, e4, 0, lc.defer, c->proj_splits[2]);
+  const int down_splits = gemm(c, EPI_RESID, act, F, W.w_down, F, n, d, F, nullptr, e4, 0, lc.defer, c->proj_splits[2],
+                                c->proj_tiles[2]);
   c->toc();
   c->layer_calls += 1;
   return down_splits;
@@ -527,6 +532,8 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
   if (const char* v = getenv("ALODLM_ATTN_NS")) c->attn_force_ns = atoi(v);
   if (const char* v = getenv("ALODLM_PROJ_SPLITS"))
     sscanf(v, "%d,%d,%d", &c->proj_splits[0], &c->proj_splits[1], &c->proj_splits[2]);
+  if (const char* v = getenv("ALODLM_PROJ_TILES"))
+    sscanf(v, "%d,%d,%d,%d", &c->proj_tiles[0], &c->proj_tiles[1], &c->proj_tiles[2], &c->proj_tiles[3]);
   // RoPE tables, computed in double on the host: angle(pos, i) = pos * theta^(-2i/hd)
   const int half = cfg->head_dim / 2;
   std::vector<float> cs((size_t)plan.max_pos * half), sn((size_t)plan.max_pos * half);
