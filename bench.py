@@ -40,6 +40,40 @@ def ffn_gate_up_traffic(w, rows_total, launches):
     return (launches * wbytes + rows_total * (D.d_model + D.ffn) * 2) / launches
 
 
+def algorithmic_work(w, loops):
+    """Algorithmic HBM bytes and flops per step of each kernel class (what the method must move
+    and compute: weights streamed once per layer call, K/V read once per attention call,
+    activations read and written once; split-K partials and other implementation traffic are
+    not counted).  Rows per loop from the sequences' loop counts; readout rows bounded by the
+    looping rows."""
+    D = w.dims
+    d, hd, F, V = D.d_model, D.head_dim, D.ffn, D.vocab
+    Hq, Hkv = D.n_q_heads, D.n_kv_heads
+    qkv = (Hq + 2 * Hkv) * hd
+    calls = [(w.batch, D.n_pre)] + [(sum(1 for l in loops if l >= s), D.n_core + D.n_coda)
+                                     for s in range(1, max(loops) + 1)]
+    acc = {k: [0.0, 0.0] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention", "lm_head",
+                                   "norm_rope")}
+
+    def add(k, b, f):
+        acc[k][0] += b
+        acc[k][1] += f
+    for s_idx, (nseq, n_calls) in enumerate(calls):
+        R = nseq * w.block
+        for _ in range(n_calls):
+            add("gemm_qkv", d * qkv * 2 + R * d * 2 + R * qkv * 4, 2.0 * R * d * qkv)
+            add("gemm_o", Hq * hd * d * 2 + R * Hq * hd * 2 + R * d * 8, 2.0 * R * Hq * hd * d)
+            add("gemm_gate_up", 2 * F * d * 2 + R * d * 2 + R * F * 2, 4.0 * R * d * F)
+            add("gemm_down", F * d * 2 + R * F * 2 + R * d * 8, 2.0 * R * F * d)
+            add("attention", nseq * Hkv * (w.prefix + w.block) * hd * 4 + R * Hq * hd * 4,
+                4.0 * R * Hq * hd * (w.prefix + w.block))
+            add("norm_rope", R * (d * 12 + qkv * 6), 0.0)
+        if s_idx > 0:
+            add("lm_head", d * V * 2 + R * d * 2, 2.0 * R * d * V)
+            add("norm_rope", R * d * 6, 0.0)
+    return acc
+
+
 def cpu_baseline(w, tau):
     """The fp64 oracle (as it stands) on a bounded sample: sequence 0 of the same step, over a
     synthetic prefix cache (the prefill is excluded on both sides)."""
@@ -137,7 +171,17 @@ def main():
     per_launch_ms = kt["gemm_gate_up"][0] / max(launches, 1)
     traffic = ffn_gate_up_traffic(w, rows_per_step * args.steps, launches)
     achieved = traffic / (per_launch_ms * 1e-3) / 1e9
-    kernels = {k: dict(ms_per_step=v[0] / args.steps, launches_per_step=v[1] / args.steps) for k, v in kt.items()}
+    work = algorithmic_work(w, loops)
+    kernels = {}
+    for k, v in kt.items():
+        ms = v[0] / args.steps
+        ent = dict(ms_per_step=ms, launches_per_step=v[1] / args.steps)
+        if k in work and ms > 0:
+            b, f = work[k]
+            ent.update(alg_bytes_per_step=b, alg_flops_per_step=f, achieved_gbs=b / (ms * 1e-3) / 1e9,
+                       achieved_tflops=f / (ms * 1e-3) / 1e12, hbm_frac=b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       mfma_frac=f / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
+        kernels[k] = ent
 
     line = {
         "metric": "committed tokens/s per GPU, 8B-shape looped denoise; % MFMA peak + % HBM BW",
@@ -164,6 +208,8 @@ def main():
                                                            per_launch_ms * 1e3, traffic / 1e6)},
         "tau_sweep": sweep,
         "prefill_ms": prefill_ms,
+        # per class: event-timed ms (the event pairs add a little time to short kernels, so the
+        # fractions are lower bounds) with algorithmic bytes / flops and their roofline fractions
         "kernels": kernels,
         "timing_pass_ms_per_step": prof["ms_per_step"],
     }
