@@ -31,20 +31,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)from_f<bf16_t>(lo) | ((uint32_t)from_f<bf16_t>(hi) << 16);
 }
 
-template <int HD, int QW, int NS>
-__global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, int n_qblocks, int n_splits,
-                                                   int tiles_per_split) {
-  constexpr int QB = 4 * QW;
+// NW waves per workgroup (4, or 8 for HD >= 64: two waves per SIMD sharing one K/V stream).
+template <int HD, int QW, int NS, int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs, int n_qblocks, int n_splits,
+                                                       int tiles_per_split) {
+  constexpr int QB = NW * QW;
   constexpr int NQ = QW / 16;
   constexpr int NH = HD / 16;
   constexpr int NC = HD / 32;
   constexpr int CK = HD / 8;             // 16-byte chunks per K row
   constexpr int KST = AKT * HD;          // K elements per stage
   constexpr int STAGE = 2 * AKT * HD;    // K then V^T
-  constexpr int KL = HD / 32;            // K load instructions per wave per stage (1 KB each)
-  constexpr int VL = HD / 32;            // V^T load instructions per wave per stage
+  constexpr int KL = HD * 8 / (64 * NW); // K load instructions per wave per stage (1 KB each)
+  constexpr int VL = HD * 8 / (64 * NW); // V^T load instructions per wave per stage
   constexpr int LPW = KL + VL;
   constexpr int RPI = 1024 / (HD * 2);   // K rows per load instruction
+  static_assert(KL >= 1 && KL * NW * 64 == HD * 8, "tile loads must split evenly over the waves");
   static_assert(NS >= 2 && (NS - 2) * LPW < 64, "ring depth");
   __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * STAGE];
 
@@ -193,26 +195,32 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
           s[ks][nq][v] = sc;
           mx = fmaxf(mx, sc);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrun[nq], mx);
-      const float corr = mnew == -INFINITY ? 1.f : __expf(mrun[nq] - mnew);
+      // Raise the column's running max only when some lane saw a larger score: the test is a
+      // wave vote, and the cross-lane max (two crossbar shuffles) runs only then -- after the
+      // first tiles most tiles skip it.  lrun holds this lane's partial sum (its 16 keys of each
+      // tile) against the column's common max; the quads' sums are added once at the end.
+      if (__any(mx > mrun[nq])) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(mrun[nq], mx);
+        const float corr = mrun[nq] == -INFINITY ? 0.f : __expf(mrun[nq] - mnew);
+        lrun[nq] *= corr;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) o[h][nq] *= corr;
+        mrun[nq] = mnew;
+      }
+      const float mref = mrun[nq];
       float sum = 0.f;
       float pv[4][4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float e = mnew == -INFINITY ? 0.f : __expf(s[ks][nq][v] - mnew);
+          const float e = mref == -INFINITY ? 0.f : __expf(s[ks][nq][v] - mref);
           pv[ks][v] = e;
           sum += e;
         }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-      lrun[nq] = lrun[nq] * corr + sum;
-      mrun[nq] = mnew;
-#pragma unroll
-      for (int h = 0; h < NH; ++h) o[h][nq] *= corr;
+      lrun[nq] += sum;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         uint4 w;
@@ -246,6 +254,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnParams p, int n_pairs, in
     }
   }
 
+  // the column's sum over its four quads of lanes
+#pragma unroll
+  for (int nq = 0; nq < NQ; ++nq) {
+    lrun[nq] += __shfl_xor(lrun[nq], 16, 64);
+    lrun[nq] += __shfl_xor(lrun[nq], 32, 64);
+  }
   // write: lane holds query column col of subtile nq, hd rows h*16 + 4*quad + v
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
@@ -311,16 +325,16 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int n_pairs, i
   }
 }
 
-template <int HD, int QW>
+template <int HD, int QW, int NW>
 static void run_attn(const AttnParams& p, int n_pairs, int n_qblocks, int n_splits, int tps, int ns, hipStream_t st) {
   const int total = n_pairs * n_qblocks * n_splits;
   const int grid = ((total + 7) / 8) * 8;
   if (ns == 2)
-    k_attn_mfma<HD, QW, 2><<<grid, 256, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+    k_attn_mfma<HD, QW, 2, NW><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   else if (ns == 4)
-    k_attn_mfma<HD, QW, 4><<<grid, 256, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+    k_attn_mfma<HD, QW, 4, NW><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   else
-    k_attn_mfma<HD, QW, 3><<<grid, 256, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+    k_attn_mfma<HD, QW, 3, NW><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   if (n_splits > 1) {
     const int rows_q = (p.Hq / p.Hkv) * p.rows_per_seq;
     const int waves = n_pairs * rows_q;
@@ -334,7 +348,7 @@ bool attn_mfma_supported(int hd) { return hd == 32 || hd == 64 || hd == 128; }
 // floats when max_splits > 1.  Key rows must be 16-byte aligned and V^T rows (c_vRow, s_vRow
 // elements) multiples of 64 elements; n_cache >= 1 or n_self >= 1.
 void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int force_splits, int force_qw,
-                      int force_ns) {
+                      int force_ns, int force_nw) {
   if (p.n_rows <= 0) return;
   const int n_seq = p.n_rows / p.rows_per_seq;
   const int n_pairs = n_seq * p.Hkv;
@@ -342,7 +356,8 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
   // measured (8B shape, 128 and 256 query rows per pair): 16 query rows per wave and a
   // two-stage ring (64 KB of LDS, two blocks per compute unit) beat wider and deeper variants
   const int QW = (force_qw == 16 || force_qw == 32) ? force_qw : 16;
-  const int QB = 4 * QW;
+  const int NW = (force_nw == 8 && p.hd >= 64) ? 8 : 4;
+  const int QB = NW * QW;
   const int n_qblocks = (rows_q + QB - 1) / QB;
   const int n_tiles = (p.n_cache + AKT - 1) / AKT + (p.n_self + AKT - 1) / AKT;
   int splits = 1;
@@ -357,13 +372,21 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
   splits = (n_tiles + tps - 1) / tps;
   if (splits < 1) splits = 1;
   const int ns = (force_ns >= 2 && force_ns <= 4) ? force_ns : 2;
-#define GO(H, Q) run_attn<H, Q>(p, n_pairs, n_qblocks, splits, tps, ns, st)
+#define GO(H, Q, W) run_attn<H, Q, W>(p, n_pairs, n_qblocks, splits, tps, ns, st)
   if (p.hd == 128) {
-    if (QW == 16) GO(128, 16); else GO(128, 32);
+    if (NW == 8) {
+      if (QW == 16) GO(128, 16, 8); else GO(128, 32, 8);
+    } else {
+      if (QW == 16) GO(128, 16, 4); else GO(128, 32, 4);
+    }
   } else if (p.hd == 64) {
-    if (QW == 16) GO(64, 16); else GO(64, 32);
+    if (NW == 8) {
+      if (QW == 16) GO(64, 16, 8); else GO(64, 32, 8);
+    } else {
+      if (QW == 16) GO(64, 16, 4); else GO(64, 32, 4);
+    }
   } else {
-    if (QW == 16) GO(32, 16); else GO(32, 32);
+    if (QW == 16) GO(32, 16, 4); else GO(32, 32, 4);
   }
 #undef GO
 }

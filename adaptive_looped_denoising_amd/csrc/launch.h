@@ -109,7 +109,7 @@ void launch_gemm_generic(int dtype, int epi, const void* A, int lda, const void*
 void launch_attn_generic(int dtype, const AttnParams& p, hipStream_t st);
 bool attn_mfma_supported(int hd);
 void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int force_splits = 0, int force_qw = 0,
-                      int force_ns = 0);
+                      int force_ns = 0, int force_nw = 0);
 
 // Cache slot fill with the counter-based synthetic values: logical element (b, kvh, j, e) is
 // generator index ((b * Hkv + kvh) * P + j) * hd + e; stored K-layout ([b][kvh][P_pitch][hd]) or,

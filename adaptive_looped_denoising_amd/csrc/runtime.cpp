@@ -153,6 +153,7 @@ struct alodlm_ctx {
   int attn_force_splits = 0;   // diagnostics: ALODLM_ATTN_SPLITS=n fixes the key splits of step attention
   int attn_force_qw = 0;       // diagnostics: ALODLM_ATTN_QW=16|32 fixes the query rows per wave
   int attn_force_ns = 0;       // diagnostics: ALODLM_ATTN_NS=2..4 fixes the LDS ring depth
+  int attn_force_nw = 0;       // diagnostics: ALODLM_ATTN_NW=4|8 fixes the waves per workgroup
   int proj_splits[3] = {0, 0, 0};  // diagnostics: ALODLM_PROJ_SPLITS=q,o,d fixes the QKV / O / down split-K
   int proj_tiles[4] = {-1, -1, -1, -1};  // diagnostics: ALODLM_PROJ_TILES=q,o,d,gu fixes their GEMM tiles
   // diagnostics: per-class kernel timing with event pairs on the context stream
@@ -263,7 +264,8 @@ void attention(alodlm_ctx* c, const AttnParams& p) {
   if (c->cfg.dtype == ALODLM_DTYPE_BF16 && !c->force_generic && attn_mfma_supported(p.hd)) {
     AttnParams q = p;
     q.part = c->at<float>(c->plan.attn_part);
-    launch_attn_mfma(q, c->plan.attn_splits, c->st, c->attn_force_splits, c->attn_force_qw, c->attn_force_ns);
+    launch_attn_mfma(q, c->plan.attn_splits, c->st, c->attn_force_splits, c->attn_force_qw, c->attn_force_ns,
+                     c->attn_force_nw);
     return;
   }
   launch_attn_generic(dt(c), p, c->st);
@@ -530,6 +532,7 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
   if (const char* v = getenv("ALODLM_ATTN_SPLITS")) c->attn_force_splits = atoi(v);
   if (const char* v = getenv("ALODLM_ATTN_QW")) c->attn_force_qw = atoi(v);
   if (const char* v = getenv("ALODLM_ATTN_NS")) c->attn_force_ns = atoi(v);
+  if (const char* v = getenv("ALODLM_ATTN_NW")) c->attn_force_nw = atoi(v);
   if (const char* v = getenv("ALODLM_PROJ_SPLITS"))
     sscanf(v, "%d,%d,%d", &c->proj_splits[0], &c->proj_splits[1], &c->proj_splits[2]);
   if (const char* v = getenv("ALODLM_PROJ_TILES"))
