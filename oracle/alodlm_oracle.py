@@ -34,7 +34,16 @@ follow them):
   * prefix key j is read at depth min(s, d_j) by Core layers in loop s;
   * readout r = final RMSNorm of the Coda output; both heads read r;
   * entropy in nats, commit iff H <= tau_ent; token = argmax, ties to the
-    lowest id (greedy decoding replaces the sampling step of Algorithm 1);
+    lowest id (greedy decoding) by default; in sampling mode the committed
+    token is the draw y ~ p of Algorithm 1 taken by the Gumbel-max rule
+    y = argmax_v (z_v + g_v), g_v = -ln(-ln u_v), with u_v from the
+    counter-based generator Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+    "Parallel random numbers: as easy as 1, 2, 3", SC'11) at counter
+    (v div 4, 64 b + i, s, step), key (seed mod 2^32, seed div 2^32), word
+    v mod 4, u = (floor(x / 2^9) + 1/2) / 2^23 (sequence b, block row i,
+    loop s); the forced commit takes its row's draw of the last loop too;
+    the one-token-per-step mode of the quality tables is tau_ent < 0 (no
+    entropy commit, only the forced one);
   * a is updated for positions unresolved at the start of the loop; the halt
     test uses the mean of a over the positions still unresolved after the
     loop's commits, "reaches" meaning >=; every sequence halts on its own;
@@ -236,11 +245,12 @@ def context_for(cache, dims, k_max: int, layer: int, loop: int, avail):
 # ---------------------------------------------------------------------------
 # the two heads
 # ---------------------------------------------------------------------------
-def readout(r, W_lm, boost_tok=None, boost_val=None):
+def readout(r, W_lm, boost_tok=None, boost_val=None, gumbel=None):
     """LMHead over readout rows r [n][d]: logits z = W_lm r (+ planted boost).
 
     Returns entropy H = -sum p ln p (nats), argmax token (lowest id on ties),
-    log-sum-exp, and the gap between the two largest logits.
+    log-sum-exp, and the gap between the two largest logits; with ``gumbel`` (noise [n][V])
+    also the Gumbel-max draws of the rows and their top-2 gaps of z + g.
     """
     z = matmul_t(r, W_lm)
     n = z.shape[0]
@@ -258,6 +268,9 @@ def readout(r, W_lm, boost_tok=None, boost_val=None):
     lse = (m + np.log(S))[:, 0]
     top2 = np.partition(z, z.shape[1] - 2, axis=1)[:, -2:]
     gap = np.abs(top2[:, 1] - top2[:, 0])
+    if gumbel is not None:
+        stok, sgap = gumbel_sample(z, gumbel)
+        return H, tok, lse, gap, stok, sgap
     return H, tok, lse, gap
 
 
@@ -268,13 +281,64 @@ def exit_gate(r, w, b: float) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# sampling commit: y ~ p by the Gumbel-max rule over counter-based uniforms
+# ---------------------------------------------------------------------------
+_MASK32 = 0xFFFFFFFF
+
+
+def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
+    """Philox4x32 with 10 rounds (Salmon et al., SC'11): each round multiplies counter words 0
+    and 2 by the two Philox constants into 64-bit products, the new words are (high of the
+    second product) ^ c1 ^ k0, (low of the second), (high of the first) ^ c3 ^ k1, (low of the
+    first); the key adds the two Weyl constants between rounds.  Vectorised over counters
+    (uint64 arrays holding 32-bit words)."""
+    c = [np.asarray(x, dtype=np.uint64) & np.uint64(_MASK32) for x in (c0, c1, c2, c3)]
+    k0, k1 = np.uint64(k0 & _MASK32), np.uint64(k1 & _MASK32)
+    m0, m1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)
+    w0, w1 = np.uint64(0x9E3779B9), np.uint64(0xBB67AE85)
+    mask, sh = np.uint64(_MASK32), np.uint64(32)
+    for rnd in range(10):
+        if rnd:
+            k0 = (k0 + w0) & mask
+            k1 = (k1 + w1) & mask
+        p0 = c[0] * m0          # < 2^64: exact in uint64
+        p1 = c[2] * m1
+        c = [(p1 >> sh) ^ c[1] ^ k0, p1 & mask, (p0 >> sh) ^ c[3] ^ k1, p0 & mask]
+    return c
+
+
+def gumbel_noise(seed: int, step: int, b: int, i: int, s: int, V: int) -> np.ndarray:
+    """Gumbel noise g_v, v < V, of block row i of sequence b at loop s: uniform
+    u_v = (floor(x_v / 2^9) + 1/2) / 2^23 in (0, 1) from word v mod 4 of Philox4x32-10 at counter
+    (v div 4, 64 b + i, s, step) and key (seed mod 2^32, seed div 2^32); g = -ln(-ln u)."""
+    n = (V + 3) // 4
+    g4 = np.arange(n, dtype=np.uint64)
+    words = philox4x32_10(g4, np.full(n, 64 * b + i), np.full(n, s), np.full(n, step), seed & _MASK32,
+                          (seed >> 32) & _MASK32)
+    x = np.stack(words, axis=1).reshape(-1)[:V]            # word v mod 4 of group v div 4
+    u = ((x >> np.uint64(9)).astype(F64) + 0.5) * 2.0 ** -23
+    return -np.log(-np.log(u))
+
+
+def gumbel_sample(z, g):
+    """Draw y = argmax_v (z_v + g_v) per row (lowest v on ties): with g standard Gumbel noise,
+    P(y = v) = softmax(z)_v.  Returns the draws and the gap between the two largest z + g."""
+    y = _f64(z) + _f64(g)
+    tok = np.argmax(y, axis=1).astype(np.int64)
+    if y.shape[1] < 2:
+        return tok, np.full(y.shape[0], np.inf)
+    top2 = np.partition(y, y.shape[1] - 2, axis=1)[:, -2:]
+    return tok, np.abs(top2[:, 1] - top2[:, 0])
+
+
+# ---------------------------------------------------------------------------
 # one denoising step of one sequence
 # ---------------------------------------------------------------------------
 def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loops: int, eps: float,
                           theta: float, tau_ent: float, tau_halt: float, mask_id: int, exit_b: float,
                           boost_tok=None, boost_val=None, teacher: Optional[dict] = None,
                           record_hidden: bool = False, counter: Optional[list] = None, progress=None,
-                          prec=None) -> dict:
+                          prec=None, sample: Optional[dict] = None) -> dict:
     """One inner loop of Algorithm 1 of the summary page (one denoising step), for one sequence.
 
     ``cache``: slot -> (K, V) [Hkv][P][hd]; ``avail``: deepest cached Core depth
@@ -283,6 +347,8 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
     ``counter`` (optional list) receives one entry per layer call; ``progress`` (optional) is
     called with a short text after every layer call.  ``prec`` as in layer_forward (the
     readout rows feeding the LMHead are rounded too; the ExitGate reads them exactly).
+    ``sample`` (optional) {"seed", "step", "seq"}: commit the Gumbel-max draw of each row
+    (gumbel_noise with this sequence index) instead of its argmax.
     """
     block_ids = np.asarray(block_ids, dtype=np.int64)
     L = block_ids.shape[0]
@@ -331,11 +397,20 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
         lse = np.full(L, np.nan)
         gap = np.full(L, np.nan)
         lam = np.full(L, np.nan)
+        stok = np.full(L, -1, dtype=np.int64)
+        sgap = np.full(L, np.nan)
         if rows.size:
             bt = None if boost_tok is None else np.asarray(boost_tok)[rows]
             bv = None if boost_val is None else np.asarray(boost_val)[rows]
-            H[rows], tok[rows], lse[rows], gap[rows] = readout(_rnd(r[rows], prec), W["lm_head"], bt, bv)
+            if sample is None:
+                H[rows], tok[rows], lse[rows], gap[rows] = readout(_rnd(r[rows], prec), W["lm_head"], bt, bv)
+            else:
+                gn = np.stack([gumbel_noise(sample["seed"], sample["step"], sample["seq"], int(i), s,
+                                            W["lm_head"].shape[0]) for i in rows])
+                H[rows], tok[rows], lse[rows], gap[rows], stok[rows], sgap[rows] = readout(
+                    _rnd(r[rows], prec), W["lm_head"], bt, bv, gumbel=gn)
             lam[rows] = exit_gate(r[rows], W["exit_w"], exit_b)
+        ctok = tok if sample is None else stok   # the token a commit takes
         # cumulative halting for the positions unresolved at loop start
         a[rows] = a[rows] + (1.0 - a[rows]) * lam[rows]
         # entropy commit
@@ -345,7 +420,7 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
             tcl = np.asarray(teacher["commit_loop"])
             newly = rows[tcl[rows] == s]
         for i in newly:
-            tokens[i] = tok[i] if teacher is None else int(teacher["tokens"][i])
+            tokens[i] = ctok[i] if teacher is None else int(teacher["tokens"][i])
             commit_loop[i] = s
         U[newly] = False
         C[newly] = True
@@ -362,7 +437,10 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
         else:
             stop = s == int(teacher["stop_loop"])
         rec = dict(loop=s, rows=rows, H=H, tok=tok, lse=lse, gap=gap, lam=lam, a=a.copy(),
-                   committed=np.array(newly), mean_a=mean_a, n_unresolved=n_u)
+                   committed=np.array(newly), mean_a=mean_a, n_unresolved=n_u, ctok=ctok)
+        if sample is not None:
+            rec["stok"] = stok
+            rec["sgap"] = sgap
         if record_hidden:
             rec["h_tilde"] = h_tilde
             rec["h"] = h.copy()
@@ -382,7 +460,7 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
             forced = int(cand[np.argmin(Hc)])
             srt = np.sort(Hc)
             forced_gap = float(srt[1] - srt[0]) if srt.size > 1 else float("inf")
-            tokens[forced] = last["tok"][forced]
+            tokens[forced] = last["ctok"][forced]
         else:
             tcl = np.asarray(teacher["commit_loop"])
             hits = cand[tcl[cand] == -s_end]

@@ -36,9 +36,9 @@ def cache_for(w: synth.Workload, W, b: int, prefix_ids=None, progress=None, prec
 def step(w: synth.Workload, W=None, seqs=None, k_loops: Optional[int] = None, teacher=None,
          record_hidden: bool = False, block_ids=None, boost=None, avail=None, caches=None,
          exit_b: Optional[float] = None, counter: Optional[list] = None, progress=None,
-         prec=None) -> List[dict]:
+         prec=None, sample: Optional[dict] = None) -> List[dict]:
     """Oracle denoising step for the listed sequences of the workload (``prec`` as in
-    alodlm_oracle.layer_forward)."""
+    alodlm_oracle.layer_forward; ``sample`` = {"seed", "step"} commits Gumbel-max draws)."""
     W = weights(w) if W is None else W
     seqs = range(w.batch) if seqs is None else seqs
     bids = synth.block_ids(w) if block_ids is None else block_ids
@@ -54,7 +54,7 @@ def step(w: synth.Workload, W=None, seqs=None, k_loops: Optional[int] = None, te
             theta=w.rope_theta, tau_ent=w.tau_ent, tau_halt=w.tau_halt, mask_id=w.mask_id,
             exit_b=w.exit_bias() if exit_b is None else exit_b, boost_tok=btok[b], boost_val=bval[b],
             teacher=None if teacher is None else teacher[b], record_hidden=record_hidden, counter=counter,
-            progress=progress, prec=prec)
+            progress=progress, prec=prec, sample=None if sample is None else dict(sample, seq=b))
         res["seq"] = b
         out.append(res)
     return out
@@ -70,23 +70,25 @@ def near_decisions(w: synth.Workload, res: dict, ent_tol: float = 1e-2, gap_tol:
                    halt_tol: float = 1e-2) -> List[str]:
     """Decisions of one oracle sequence that sit within the tolerances of a threshold:
     |H - tau_ent|, top-2 logit gap of a committed token, |mean a - tau_halt|, forced-commit
-    entropy gap.  A GPU free run may legitimately differ from the oracle only there."""
+    entropy gap.  In sampling mode the gap that decides a committed token is the top-2 gap of
+    z + g.  A GPU free run may legitimately differ from the oracle only there."""
     flags = []
     for rec in res["records"]:
         rows = rec["rows"]
+        gap = rec.get("sgap", rec["gap"])
         if rows.size:
             d = np.abs(rec["H"][rows] - w.tau_ent)
             if (d < ent_tol).any():
                 flags.append("entropy loop %d rows %s" % (rec["loop"], rows[d < ent_tol].tolist()))
         for i in rec["committed"]:
-            if rec["gap"][i] < gap_tol:
-                flags.append("argmax gap loop %d row %d" % (rec["loop"], i))
+            if gap[i] < gap_tol:
+                flags.append("token gap loop %d row %d" % (rec["loop"], i))
         if rec["n_unresolved"] and abs(rec["mean_a"] - w.tau_halt) < halt_tol:
             flags.append("halt loop %d" % rec["loop"])
     if res["forced"] >= 0:
         last = res["records"][-1]
         if res["forced_gap"] < ent_tol:
             flags.append("forced entropy gap")
-        if last["gap"][res["forced"]] < gap_tol:
-            flags.append("forced argmax gap")
+        if last.get("sgap", last["gap"])[res["forced"]] < gap_tol:
+            flags.append("forced token gap")
     return flags

@@ -448,3 +448,107 @@ def test_rounding_points_mode_stays_close_to_exact():
     rel = np.linalg.norm(ra["h_tilde"] - rb["h_tilde"], axis=1) / np.linalg.norm(ra["h_tilde"], axis=1)
     assert 0 < rel.max() < 2e-2
     assert np.array_equal(a["commit_loop"], b["commit_loop"])
+
+
+# --------------------------------------------------------------------------- sampling commit
+def test_oracle_philox_known_answers():
+    """The oracle's own Philox4x32-10 (independent of the input generator's) against the published
+    known-answer vectors."""
+    for v in _golden("philox4x32_10_kat.json")["vectors"]:
+        c = [np.array([int(x, 16)]) for x in v["ctr"]]
+        k = [int(x, 16) for x in v["key"]]
+        out = orc.philox4x32_10(*c, *k)
+        assert [int(x[0]) for x in out] == [int(x, 16) for x in v["out"]]
+
+
+def test_gumbel_noise_range_and_counter_layout():
+    """u = (floor(x / 2^9) + 1/2) / 2^23 lies in [2^-24, 1 - 2^-24], so g = -ln(-ln u) lies in
+    [-ln(-ln 2^-24), -ln(-ln(1 - 2^-24))]; the noise of vocabulary id v is word v mod 4 of the
+    block at counter v div 4, so a prefix of the vocabulary draws the same numbers."""
+    g = orc.gumbel_noise(0x1234567890ABCDEF, 3, 2, 5, 1, 50001)
+    lo = -math.log(-math.log(2.0 ** -24))
+    hi = -math.log(-math.log1p(-2.0 ** -24))
+    assert g.min() >= lo - 1e-12 and g.max() <= hi + 1e-12
+    np.testing.assert_array_equal(orc.gumbel_noise(0x1234567890ABCDEF, 3, 2, 5, 1, 13), g[:13])
+    # scalar definition through the input generator's separately written Philox, at ids that
+    # cover every word of a block
+    seed = 0x1234567890ABCDEF
+    for v in (0, 1, 2, 3, 4, 7, 4097, 50000):
+        x = int(synth.philox4x32_10([v // 4, 64 * 2 + 5, 1, 3], [seed & 0xFFFFFFFF, seed >> 32])[v % 4])
+        u = ((x >> 9) + 0.5) / 2.0 ** 23
+        assert g[v] == pytest.approx(-math.log(-math.log(u)), rel=1e-13, abs=1e-13)
+    # standard Gumbel moments: mean = Euler-Mascheroni constant, variance = pi^2 / 6
+    assert abs(g.mean() - 0.5772156649) < 4 * math.sqrt(math.pi ** 2 / 6 / g.size)
+    assert abs(g.var() - math.pi ** 2 / 6) < 0.05
+    # every counter word matters: another row, loop, step or seed gives other noise
+    for other in (orc.gumbel_noise(0x1234567890ABCDEF, 3, 2, 6, 1, 64), orc.gumbel_noise(0x1234567890ABCDEF, 3, 3, 5, 1, 64),
+                  orc.gumbel_noise(0x1234567890ABCDEF, 3, 2, 5, 2, 64), orc.gumbel_noise(0x1234567890ABCDEF, 4, 2, 5, 1, 64),
+                  orc.gumbel_noise(0x1234567890ABCDEE, 3, 2, 5, 1, 64), orc.gumbel_noise(0x0234567890ABCDEF, 3, 2, 5, 1, 64)):
+        assert not np.array_equal(other, g[:64])
+
+
+def test_gumbel_max_draws_follow_the_softmax():
+    """argmax(z + g) over independent noise draws token v with probability softmax(z)_v: the
+    empirical frequencies of 60000 draws sit within 4.5 standard errors of the softmax."""
+    z = np.array([0.0, 1.0, 2.5, -1.0, 0.5, 2.0, -3.0])
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    n_i, n_s = 64, 6
+    counts = np.zeros(z.size)
+    n = 0
+    for step in range(160):
+        for b in range(1):
+            for s in range(1, n_s + 1):
+                G = np.stack([orc.gumbel_noise(99, step, b, i, s, z.size) for i in range(n_i)])
+                tok, _ = orc.gumbel_sample(np.broadcast_to(z, G.shape), G)
+                counts += np.bincount(tok, minlength=z.size)
+                n += n_i
+    f = counts / n
+    se = np.sqrt(p * (1 - p) / n)
+    assert (np.abs(f - p) < 4.5 * se).all(), (f, p)
+
+
+def test_gumbel_sample_limits():
+    """A logit 20 above every other always wins (the noise spans less than 20); equal logits draw
+    every id; equal z + g goes to the lowest id."""
+    V = 300
+    z = np.zeros((40, V))
+    z[:, 123] = 20.0
+    G = np.stack([orc.gumbel_noise(5, 0, 0, i, 1, V) for i in range(40)])
+    tok, gap = orc.gumbel_sample(z, G)
+    assert (tok == 123).all() and (gap > 0).all()
+    tok, _ = orc.gumbel_sample(np.zeros((40, V)), G)
+    assert len(set(tok.tolist())) > 30
+    t2, gap2 = orc.gumbel_sample(np.array([[1.0, 0.5, 1.0]]), np.array([[0.0, 0.5, 0.0]]))
+    assert t2[0] == 0 and gap2[0] == 0
+
+
+def test_sampled_step_equals_greedy_when_the_boost_dominates():
+    """With planted boosts far above the noise span, every draw is the argmax, so the sampled step
+    takes the greedy step's decisions exactly; with ordinary boosts it draws other tokens."""
+    w = _tiny(boost_lo=30.0, boost_hi=34.0, tau_ent=0.3, batch=2)
+    W = run.weights(w)
+    g = run.step(w, W=W)
+    s = run.step(w, W=W, sample=dict(seed=7, step=0))
+    for a, b in zip(g, s):
+        assert np.array_equal(a["tokens"], b["tokens"]) and np.array_equal(a["commit_loop"], b["commit_loop"])
+        for ra, rb in zip(a["records"], b["records"]):
+            rows = ra["rows"]
+            assert np.array_equal(rb["stok"][rows][ra["H"][rows] < 1e-3], ra["tok"][rows][ra["H"][rows] < 1e-3])
+    # near-uniform readout: draws differ from the argmax, commits take the draws
+    w2 = _tiny(tau_ent=100.0)
+    r2 = run.step(w2, sample=dict(seed=11, step=1))[0]
+    rec = r2["records"][0]
+    rows = rec["rows"]
+    assert (r2["commit_loop"][rows] == 1).all()
+    assert np.array_equal(r2["tokens"][rows], rec["stok"][rows])
+    assert (rec["stok"][rows] != rec["tok"][rows]).sum() > rows.size // 2
+
+
+def test_sampled_forced_commit_takes_the_draw():
+    w = _tiny(tau_ent=-1.0, tau_halt=1.5)
+    res = run.step(w, sample=dict(seed=3, step=2))[0]
+    last = res["records"][-1]
+    i = res["forced"]
+    assert i == int(np.argmin(last["H"])) and res["tokens"][i] == last["stok"][i]
+    assert res["commit_loop"][i] == -w.k_max
