@@ -14,14 +14,15 @@ LIB_PATH = os.path.join(HERE, "libalodlm.so")
 
 OK, EINVAL, ESTATE, ENOMEM, EHIP = 0, -1, -2, -3, -4
 DTYPE_BF16, DTYPE_FP32 = 0, 1
-STEP_TEACHER_FORCED = 1
+STEP_TEACHER_FORCED, STEP_SAMPLE = 1, 2
 # diagnostics GEMM epilogues (alodlm_diag.h)
 DIAG_STORE, DIAG_RESID, DIAG_SOFTSTAT, DIAG_SWIGLU = 0, 1, 2, 3
 
 EXPORTS = ("alodlm_workspace_bytes", "alodlm_kv_slots", "alodlm_create", "alodlm_prefill_kv",
            "alodlm_prefill_kv_synthetic", "alodlm_denoise_step", "alodlm_readout_commit",
            "alodlm_last_step_stats", "alodlm_last_error", "alodlm_destroy", "alodlm_synth_fill",
-           "alodlm_diag_gemm", "alodlm_diag_timing_enable", "alodlm_diag_timing_read", "alodlm_diag_read_kv", "alodlm_diag_buffer_offset")
+           "alodlm_diag_gemm", "alodlm_diag_timing_enable", "alodlm_diag_timing_read", "alodlm_diag_read_kv", "alodlm_diag_buffer_offset",
+           "alodlm_diag_readout_sample")
 K_CLASSES = ("gemm_gate_up", "gemm_qkv", "gemm_o", "gemm_down", "attention", "lm_head", "norm_rope", "control")
 
 
@@ -46,13 +47,13 @@ class StepArgs(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("block_len", c_int32), ("block_ids", c_void_p), ("tau_ent", c_float),
                 ("tau_halt", c_float), ("k_loops", c_int32), ("flags", c_uint32), ("boost_tok", c_void_p),
                 ("boost_val", c_void_p), ("tf_commit_loop", c_void_p), ("tf_tokens", c_void_p),
-                ("tf_stop_loop", c_void_p)]
+                ("tf_stop_loop", c_void_p), ("sample_seed", c_uint64), ("sample_step", c_uint32)]
 
 
 class StepOut(ctypes.Structure):
     _fields_ = [("tokens", c_void_p), ("commit_loop", c_void_p), ("loops", c_void_p), ("entropy", c_void_p),
                 ("lam", c_void_p), ("halt", c_void_p), ("lse", c_void_p), ("argmax", c_void_p),
-                ("hidden", c_void_p), ("n_committed", c_int32), ("loops_run", c_int32)]
+                ("hidden", c_void_p), ("n_committed", c_int32), ("loops_run", c_int32), ("sampled", c_void_p)]
 
 
 class AlodlmError(RuntimeError):
@@ -91,6 +92,9 @@ def load(path: str = LIB_PATH):
                                       c_void_p]
     lib.alodlm_diag_gemm.argtypes = [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_int32, c_int32, c_int32, c_void_p]
+    lib.alodlm_diag_readout_sample.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_uint64,
+                                               c_uint32, c_uint32, c_void_p, c_void_p, c_size_t, c_int32, c_int32,
+                                               c_void_p]
     lib.alodlm_diag_timing_enable.argtypes = [c_void_p, c_int32]
     lib.alodlm_diag_buffer_offset.argtypes = [c_void_p, ctypes.c_char_p]
     lib.alodlm_diag_buffer_offset.restype = c_int64
@@ -179,6 +183,16 @@ def diag_gemm(epi: int, M: int, N: int, K: int, A_ptr: int, B_ptr: int, C_ptr: i
                                  force_splits, force_generic, force_tile, c_void_p(stream_ptr))
     if rc != 0:
         raise AlodlmError(rc, "alodlm_diag_gemm failed")
+
+
+def diag_readout_sample(M: int, N: int, K: int, A_ptr: int, B_ptr: int, row_key_ptr: int, seed: int, c2: int, c3: int,
+                        tok_ptr: int, scratch_ptr: int, scratch_floats: int, force_generic: int, stream_ptr: int,
+                        force_tile: int = -1):
+    rc = load().alodlm_diag_readout_sample(M, N, K, c_void_p(A_ptr), c_void_p(B_ptr), c_void_p(row_key_ptr), seed, c2,
+                                           c3, c_void_p(tok_ptr), c_void_p(scratch_ptr), scratch_floats,
+                                           force_generic, force_tile, c_void_p(stream_ptr))
+    if rc != 0:
+        raise AlodlmError(rc, "alodlm_diag_readout_sample failed")
 
 
 def timing_enable(ctx: int, on: bool):

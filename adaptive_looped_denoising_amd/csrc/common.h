@@ -95,6 +95,63 @@ __device__ __forceinline__ SoftStat softstat_merge(const SoftStat& a, const Soft
   return r;
 }
 
+// Gumbel-max draw of a set of logits: the largest z + g (g Gumbel noise) and its column,
+// lowest column among equal values; an empty set has g = -inf and idx = INT_MAX.  The struct is
+// the stored form; in registers the pair is kept as two scalars and merged with gstat_take
+// (merging struct copies lets the compiler select between their addresses, i.e. put them in
+// scratch memory).
+struct GStat {
+  float g;
+  int idx;
+};
+
+// (g, idx) <- the better of (g, idx) and (og, oidx).
+__device__ __forceinline__ void gstat_take(float& g, int& idx, float og, int oidx) {
+  const bool tb = og > g || (og == g && oidx < idx);
+  g = tb ? og : g;
+  idx = tb ? oidx : idx;
+}
+
+// Merge of (g, idx) across the lanes of groups of 2 * o_max lanes (xor butterflies 1 .. o_max).
+template <int O_MAX>
+__device__ __forceinline__ void gstat_reduce_xor(float& g, int& idx) {
+#pragma unroll
+  for (int o = 1; o <= O_MAX; o <<= 1) {
+    const float og = __shfl_xor(g, o, 64);
+    const int oi = __shfl_xor(idx, o, 64);
+    gstat_take(g, idx, og, oi);
+  }
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC'11) on counter (c0, c1, c2, c3), in place,
+// with key (k0, k1): ten rounds of two 32x32->64 multiplies by the Philox constants, the key
+// bumped by the Weyl constants between rounds.  Scalar words (no array) so that callers can pick
+// words with selects without the compiler placing them in scratch memory.
+__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0,
+                                              uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// Gumbel noise of one 32-bit draw x: u = (floor(x / 2^9) + 1/2) / 2^23 (exact in fp32, inside
+// (0, 1)), g = -ln(-ln u).
+__device__ __forceinline__ float gumbel_of(uint32_t x) {
+  const float u = ((float)(x >> 9) + 0.5f) * 1.1920928955078125e-07f;
+  return -logf(-logf(u));
+}
+
+
 __device__ __forceinline__ SoftStat softstat_shfl_xor(const SoftStat& s, int o) {
   SoftStat r;
   r.m = __shfl_xor(s.m, o, 64);

@@ -90,9 +90,12 @@ __device__ __forceinline__ void gemm_epilogue(floatx4 (&acc)[BM / WM / 16][BN / 
     // red (WN * BM entries) lives in the kernel's own operand LDS, reused once every wave is
     // past its last fragment read: a second LDS object would make the compiler's tracking of
     // the direct global->LDS loads wait for all of them before every fragment read of the loop.
+    // With sampling, gred (WN * BM draws) follows red in the same LDS.
+    GStat* gred = (GStat*)(red + WN * BM);
+    const bool smp = ep.smp.part != nullptr;
     __syncthreads();
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+    for (int a = 0; a < TM; ++a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int rl = wm * TM * 16 + a * 16 + 4 * (lane >> 4) + v;
@@ -132,6 +135,62 @@ __device__ __forceinline__ void gemm_epilogue(floatx4 (&acc)[BM / WM / 16][BN / 
         for (int o = 1; o < 16; o <<= 1) s = softstat_merge(s, softstat_shfl_xor(s, o));
         if ((lane & 15) == 0) red[wn * BM + rl] = s;
       }
+    }
+    if (smp) {
+      // Gumbel-max draws, one 16-row block at a time (few extra registers beside the
+      // accumulators): lane q of each group of four lanes (four consecutive columns, the same four
+      // rows) draws one Philox block for row q, i.e. that row's noise of the four columns; a 4x4
+      // transpose over the group hands every lane its own column's noise for its four rows.
+      const int q = lane & 3;
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const int r0 = m0 + wm * TM * 16 + a * 16 + 4 * (lane >> 4);
+        const uint32_t rk = r0 + q < Mr ? (uint32_t)ep.smp.row_key[r0 + q] : 0u;
+        int btv[4];
+        float bvv[4], gg[4];
+        int gi[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          btv[v] = (r0 + v < Mr && ep.btok) ? ep.btok[r0 + v] : -1;
+          bvv[v] = btv[v] >= 0 ? ep.bval[r0 + v] : 0.f;
+          gg[v] = -INFINITY;
+          gi[v] = 0x7FFFFFFF;
+        }
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          uint32_t c0 = (uint32_t)((n0 + wn * TN * 16 + b * 16 + (lane & 12)) >> 2), c1 = rk, c2 = ep.smp.c2,
+                   c3 = ep.smp.c3;
+          philox4x32_10(c0, c1, c2, c3, ep.smp.k0, ep.smp.k1);
+          float g[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            // round k: every lane sends its word (q + k) mod 4 and receives, from the lane that drew
+            // row (q - k) mod 4, that row's word q (this lane's column)
+            const int sw = (q + k) & 3;
+            const uint32_t w = (sw & 2) ? ((sw & 1) ? c3 : c2) : ((sw & 1) ? c1 : c0);
+            const uint32_t got = k == 0 ? w : (uint32_t)__shfl((int)w, (lane & ~3) | ((q - k) & 3), 64);
+            const float gv = gumbel_of(got);
+            const int row = (q - k) & 3;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (row == v) g[v] = gv;
+          }
+          const int n = cbase + b * 16;  // ascending over b, so ties keep the lowest column
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float y = acc[a][b][v] + (n == btv[v] ? bvv[v] : 0.f) + g[v];
+            const bool tk = n < N && y > gg[v];
+            gg[v] = tk ? y : gg[v];
+            gi[v] = tk ? n : gi[v];
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          gstat_reduce_xor<8>(gg[v], gi[v]);
+          if ((lane & 15) == 0) gred[wn * BM + wm * TM * 16 + a * 16 + 4 * (lane >> 4) + v] = GStat{gg[v], gi[v]};
+        }
+      }
+    }
     __syncthreads();
     for (int rl = tid; rl < BM; rl += 256) {
       const int m = m0 + rl;
@@ -140,6 +199,13 @@ __device__ __forceinline__ void gemm_epilogue(floatx4 (&acc)[BM / WM / 16][BN / 
 #pragma unroll
       for (int w = 1; w < WN; ++w) s = softstat_merge(s, red[w * BM + rl]);
       ep.part[(size_t)m * ep.n_tiles + nt] = s;
+      if (smp) {
+        float gg = gred[rl].g;
+        int gi = gred[rl].idx;
+#pragma unroll
+        for (int w = 1; w < WN; ++w) gstat_take(gg, gi, gred[w * BM + rl].g, gred[w * BM + rl].idx);
+        ep.smp.part[(size_t)m * ep.n_tiles + nt] = GStat{gg, gi};
+      }
     }
   }
 }
@@ -1143,7 +1209,8 @@ extern "C" int alodlm_diag_gemm(int32_t epi, int32_t M, int32_t N, int32_t K, co
     ep.part = (SoftStat*)scratch;
     ep.n_tiles = n_tiles;
     launch_gemm_mfma(epi, A, K, B, K, M, N, K, nullptr, ep, 0, nullptr, 0, 1, st, tile, false);
-    launch_softstat_combine((const SoftStat*)scratch, M, n_tiles, nullptr, H, lse, (int32_t*)act, st);
+    launch_softstat_combine((const SoftStat*)scratch, M, n_tiles, nullptr, H, lse, (int32_t*)act, nullptr, nullptr,
+                            st);
     return hipGetLastError() == hipSuccess ? 0 : -4;
   }
   if (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_SWIGLU) return -1;
@@ -1165,5 +1232,40 @@ extern "C" int alodlm_diag_gemm(int32_t epi, int32_t M, int32_t N, int32_t K, co
     launch_gemm_mfma(epi, A, K, B, K, M, N, K, nullptr, ep, N / 2, scratch, scratch ? scratch_floats : 0,
                      force_splits, st, force_tile, false);
   }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+extern "C" int alodlm_diag_readout_sample(int32_t M, int32_t N, int32_t K, const void* A, const void* B,
+                                          const int32_t* row_key, uint64_t seed, uint32_t c2, uint32_t c3,
+                                          int32_t* tok, float* scratch, size_t scratch_floats,
+                                          int32_t force_generic, int32_t force_tile, void* hip_stream) {
+  using namespace alodlm;
+  if (M <= 0 || N <= 0 || K <= 0 || !A || !B || !row_key || !tok || !scratch) return -1;
+  const bool mfma = !force_generic && gemm_mfma_supported(K, K, K);
+  int sp;
+  const int tile = !mfma ? -1
+                         : ((force_tile >= 0 && force_tile < kNumTiles) ? force_tile
+                                                                        : gemm_mfma_auto_tile(EPI_SOFTSTAT, M, N, K, &sp));
+  const int bn = mfma ? kTiles[tile].bn : 64;
+  const int n_tiles = (N + bn - 1) / bn;
+  const size_t need = (size_t)6 * M * n_tiles + (size_t)3 * M;
+  if (need > scratch_floats) return -1;
+  hipStream_t st = (hipStream_t)hip_stream;
+  GemmEpi ep;
+  ep.part = (SoftStat*)scratch;
+  ep.n_tiles = n_tiles;
+  ep.smp.part = (GStat*)(scratch + (size_t)4 * M * n_tiles);
+  ep.smp.row_key = row_key;
+  ep.smp.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  ep.smp.k1 = (uint32_t)(seed >> 32);
+  ep.smp.c2 = c2;
+  ep.smp.c3 = c3;
+  if (mfma)
+    launch_gemm_mfma(EPI_SOFTSTAT, A, K, B, K, M, N, K, nullptr, ep, 0, nullptr, 0, 1, st, tile, false);
+  else
+    launch_gemm_generic(DT_BF16, EPI_SOFTSTAT, A, K, B, K, M, N, K, nullptr, ep, st);
+  float* H = scratch + (size_t)6 * M * n_tiles;
+  launch_softstat_combine((const SoftStat*)scratch, M, n_tiles, nullptr, H, H + M, (int32_t*)(H + 2 * M), ep.smp.part,
+                          tok, st);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -70,6 +70,25 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const TA* __restrict__ A, 
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) s = softstat_merge(s, softstat_shfl_xor(s, o));
       if (tx == 0 && m < Mr) ep.part[(size_t)m * ep.n_tiles + blockIdx.x] = s;
+      if (ep.smp.part) {
+        // this thread's four consecutive columns are the four words of one Philox block
+        uint32_t c0 = (uint32_t)((n0 + tx * 4) >> 2), c1 = m < Mr ? (uint32_t)ep.smp.row_key[m] : 0u, c2 = ep.smp.c2,
+                 c3 = ep.smp.c3;
+        philox4x32_10(c0, c1, c2, c3, ep.smp.k0, ep.smp.k1);
+        const uint32_t words[4] = {c0, c1, c2, c3};
+        float gg = -INFINITY;
+        int gi = 0x7FFFFFFF;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + tx * 4 + j;
+          const float y = acc[i][j] + (n == bt ? bv : 0.f) + gumbel_of(words[j]);
+          const bool tk = n < N && y > gg;
+          gg = tk ? y : gg;
+          gi = tk ? n : gi;
+        }
+        gstat_reduce_xor<8>(gg, gi);
+        if (tx == 0 && m < Mr) ep.smp.part[(size_t)m * ep.n_tiles + blockIdx.x] = GStat{gg, gi};
+      }
     }
     return;
   }

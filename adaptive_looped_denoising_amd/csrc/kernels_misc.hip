@@ -203,10 +203,12 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ gu, in
 // ---------------------------------------------------------------------------------------------
 // Merge the per-tile softmax statistics of each readout row in a fixed order:
 // entropy H = ln S - T/S, lse = m + ln S, token = argmax.
+// With gpart, also the Gumbel-max draw: the largest z + g over the tiles (lowest column on ties).
 __global__ __launch_bounds__(64) void k_softstat_combine(const SoftStat* __restrict__ part, int n_tiles,
                                                          const int32_t* __restrict__ n_dev,
                                                          float* __restrict__ H, float* __restrict__ lse,
-                                                         int32_t* __restrict__ tok) {
+                                                         int32_t* __restrict__ tok, const GStat* __restrict__ gpart,
+                                                         int32_t* __restrict__ stok) {
   const int r = blockIdx.x;
   if (n_dev && r >= *n_dev) return;
   const SoftStat* p = part + (size_t)r * n_tiles;
@@ -219,6 +221,14 @@ __global__ __launch_bounds__(64) void k_softstat_combine(const SoftStat* __restr
     H[r] = lS - s.T / s.S;
     lse[r] = s.m + lS;
     tok[r] = s.idx;
+  }
+  if (gpart) {
+    const GStat* q = gpart + (size_t)r * n_tiles;
+    float gg = -INFINITY;
+    int gi = 0x7FFFFFFF;
+    for (int t = threadIdx.x; t < n_tiles; t += 64) gstat_take(gg, gi, q[t].g, q[t].idx);
+    gstat_reduce_xor<32>(gg, gi);
+    if (threadIdx.x == 0) stok[r] = gi;
   }
 }
 
@@ -319,6 +329,7 @@ __global__ __launch_bounds__(64) void k_commit(int s, int k_loops, int L, int B,
                                                const int32_t* __restrict__ act, uint8_t* __restrict__ U,
                                                float* __restrict__ a, const int32_t* __restrict__ ro_map,
                                                const float* __restrict__ H, const int32_t* __restrict__ tok,
+                                               const int32_t* __restrict__ stok,
                                                const float* __restrict__ lam, const float* __restrict__ lse,
                                                int32_t* __restrict__ tokens, int8_t* __restrict__ cl,
                                                int32_t* __restrict__ ncommit, uint8_t* __restrict__ stop,
@@ -326,26 +337,28 @@ __global__ __launch_bounds__(64) void k_commit(int s, int k_loops, int L, int B,
                                                const int32_t* __restrict__ tf_tok,
                                                const int8_t* __restrict__ tf_stop, float* __restrict__ dbg_H,
                                                float* __restrict__ dbg_lam, float* __restrict__ dbg_a,
-                                               float* __restrict__ dbg_lse, int32_t* __restrict__ dbg_tok) {
+                                               float* __restrict__ dbg_lse, int32_t* __restrict__ dbg_tok,
+                                               int32_t* __restrict__ dbg_stok) {
   const int b = act[blockIdx.x];
   const int i = threadIdx.x;
   const bool in = i < L;
   const int idx = b * L + i;
   const bool u = in && U[idx];
   float h = NAN, lm = NAN, ls = NAN;
-  int tk = -1;
+  int tk = -1, sk = -1;
   float av = in ? a[idx] : 0.f;
   if (u) {
     const int k = ro_map[idx];
     h = H[k];
     tk = tok[k];
+    sk = stok ? stok[k] : tk;
     lm = lam[k];
     ls = lse[k];
     av = av + (1.0f - av) * lm;
     a[idx] = av;
   }
   bool commit;
-  int ctok = tk;
+  int ctok = sk;  // the committed token: the draw in sampling mode, else the argmax
   if (tf_cl) {
     commit = u && tf_cl[idx] == s;
     if (u) ctok = tf_tok[idx];
@@ -409,6 +422,7 @@ __global__ __launch_bounds__(64) void k_commit(int s, int k_loops, int L, int B,
     dbg_a[o] = u ? av : NAN;
     dbg_lse[o] = ls;
     dbg_tok[o] = u ? tk : -1;
+    if (dbg_stok) dbg_stok[o] = u ? sk : -1;
   }
 }
 
@@ -449,17 +463,22 @@ __global__ __launch_bounds__(256) void k_dump_hidden(int nb, int L, int d, int B
   for (int e = threadIdx.x; e < d; e += 256) dst[e] = s_[e];
 }
 
-// Boost of readout row k: the (sequence, row) it stands for is act[r / L], r % L with r = ro_rows[k].
-__global__ void k_gather_boosts(const int32_t* __restrict__ ro_rows, const int32_t* __restrict__ n_dev,
-                                const int32_t* __restrict__ act, int n_upper, int L,
-                                const int32_t* __restrict__ boost_tok, const float* __restrict__ boost_val,
-                                int32_t* __restrict__ btok, float* __restrict__ bval) {
+// Readout row k stands for sequence act[r / L], block row r % L with r = ro_rows[k]: gathers its
+// boost and writes its sampling row key 64 * sequence + row.
+__global__ void k_gather_rows(const int32_t* __restrict__ ro_rows, const int32_t* __restrict__ n_dev,
+                              const int32_t* __restrict__ act, int n_upper, int L,
+                              const int32_t* __restrict__ boost_tok, const float* __restrict__ boost_val,
+                              int32_t* __restrict__ btok, float* __restrict__ bval, int32_t* __restrict__ rkey) {
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= n_upper || k >= *n_dev) return;
   const int r = ro_rows[k];
-  const int src = act[r / L] * L + r % L;
-  btok[k] = boost_tok[src];
-  bval[k] = boost_val[src];
+  const int b = act[r / L], i = r % L;
+  const int src = b * L + i;
+  if (boost_tok) {
+    btok[k] = boost_tok[src];
+    bval[k] = boost_val[src];
+  }
+  if (rkey) rkey[k] = 64 * b + i;
 }
 
 // embed_out[k] = committed(k) ? Emb[tokens[k]] : 0
@@ -530,9 +549,9 @@ void launch_swiglu(int dtype, const float* gu, int n_rows, int F, void* act, hip
 }
 
 void launch_softstat_combine(const SoftStat* part, int n_rows, int n_tiles, const int32_t* n_dev, float* H,
-                             float* lse, int32_t* tok, hipStream_t st) {
+                             float* lse, int32_t* tok, const GStat* gpart, int32_t* stok, hipStream_t st) {
   if (n_rows <= 0) return;
-  k_softstat_combine<<<n_rows, 64, 0, st>>>(part, n_tiles, n_dev, H, lse, tok);
+  k_softstat_combine<<<n_rows, 64, 0, st>>>(part, n_tiles, n_dev, H, lse, tok, gpart, stok);
 }
 
 void launch_step_init(const int32_t* block_ids, int B, int L, int mask_id, uint8_t* U, float* a,
@@ -552,13 +571,14 @@ void launch_build_lists(int nb, int L, int B, const int32_t* act_cur, const uint
 
 void launch_commit(int nb, int s, int k_loops, int L, int B, float tau_ent, float tau_halt, const int32_t* act,
                    uint8_t* U, float* a, const int32_t* ro_map, const float* H, const int32_t* tok,
-                   const float* lam, const float* lse, int32_t* tokens, int8_t* cl, int32_t* ncommit,
-                   uint8_t* stop, int8_t* loops, const int8_t* tf_cl, const int32_t* tf_tok, const int8_t* tf_stop,
-                   float* dbg_H, float* dbg_lam, float* dbg_a, float* dbg_lse, int32_t* dbg_tok, hipStream_t st) {
+                   const int32_t* stok, const float* lam, const float* lse, int32_t* tokens, int8_t* cl,
+                   int32_t* ncommit, uint8_t* stop, int8_t* loops, const int8_t* tf_cl, const int32_t* tf_tok,
+                   const int8_t* tf_stop, float* dbg_H, float* dbg_lam, float* dbg_a, float* dbg_lse,
+                   int32_t* dbg_tok, int32_t* dbg_stok, hipStream_t st) {
   if (nb <= 0) return;
-  k_commit<<<nb, 64, 0, st>>>(s, k_loops, L, B, tau_ent, tau_halt, act, U, a, ro_map, H, tok, lam, lse, tokens,
-                              cl, ncommit, stop, loops, tf_cl, tf_tok, tf_stop, dbg_H, dbg_lam, dbg_a, dbg_lse,
-                              dbg_tok);
+  k_commit<<<nb, 64, 0, st>>>(s, k_loops, L, B, tau_ent, tau_halt, act, U, a, ro_map, H, tok, stok, lam, lse,
+                              tokens, cl, ncommit, stop, loops, tf_cl, tf_tok, tf_stop, dbg_H, dbg_lam, dbg_a,
+                              dbg_lse, dbg_tok, dbg_stok);
 }
 
 void launch_reset_compact(int dtype, int nb_upper, const int32_t* cnt, int L, int d, int V, const int32_t* act,
@@ -576,11 +596,12 @@ void launch_dump_hidden(int nb, int L, int d, int B, int s, const int32_t* act, 
   k_dump_hidden<<<nb * L, 256, 0, st>>>(nb, L, d, B, s, act, h, out);
 }
 
-void launch_gather_boosts(const int32_t* ro_rows, const int32_t* n_dev, const int32_t* act, int n_upper, int L,
-                          const int32_t* boost_tok, const float* boost_val, int32_t* btok, float* bval, hipStream_t st) {
-  if (n_upper <= 0) return;
-  k_gather_boosts<<<(n_upper + 255) / 256, 256, 0, st>>>(ro_rows, n_dev, act, n_upper, L, boost_tok, boost_val, btok,
-                                                          bval);
+void launch_gather_rows(const int32_t* ro_rows, const int32_t* n_dev, const int32_t* act, int n_upper, int L,
+                        const int32_t* boost_tok, const float* boost_val, int32_t* btok, float* bval, int32_t* rkey,
+                        hipStream_t st) {
+  if (n_upper <= 0 || (!boost_tok && !rkey)) return;
+  k_gather_rows<<<(n_upper + 255) / 256, 256, 0, st>>>(ro_rows, n_dev, act, n_upper, L, boost_tok, boost_val, btok,
+                                                        bval, rkey);
 }
 
 void launch_embed_committed(int dtype, const int8_t* cl, const int32_t* tokens, const void* E, int n, int d, int V,

@@ -9,6 +9,16 @@ enum { DT_BF16 = 0, DT_FP32 = 1 };
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SOFTSTAT = 2, EPI_SWIGLU = 3 };
 
 struct SoftStat;
+struct GStat;
+
+// Sampling parameters of a readout: Philox key and counter words 2 and 3; row_key[m] is counter
+// word 1 of readout row m (64 * sequence + block row).  Word 0 is the column divided by 4 and
+// column mod 4 picks the output word.
+struct SampleParams {
+  const int32_t* row_key = nullptr;
+  GStat* part = nullptr;  // [rows][column tiles] partial draws
+  uint32_t k0 = 0, k1 = 0, c2 = 0, c3 = 0;
+};
 
 // GEMM epilogue operands.  STORE: C = acc.  RESID: C = R + acc (fp32, R may alias C).
 // SOFTSTAT: per (row, column tile) softmax statistics of acc + boost into part[row][tile].
@@ -23,6 +33,7 @@ struct GemmEpi {
   const float* bval = nullptr;
   void* act = nullptr;
   int ld_act = 0;
+  SampleParams smp;  // SOFTSTAT with smp.part: also the Gumbel-max draw of each row and tile
 };
 
 // Attention operands.  Query rows r = t * rows_per_seq + i of sequence slot t (cache sequence
@@ -71,26 +82,32 @@ void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_s
                          void* q_out, void* k_out, void* v_out, int64_t kSeq, int64_t kHead, int64_t kPos,
                          int64_t vSeq, int64_t vHead, int64_t vRow, int seq0, hipStream_t st, int splits = 1);
 void launch_swiglu(int dtype, const float* gu, int n_rows, int F, void* act, hipStream_t st);
+// gpart (optional): partial Gumbel-max draws merged into stok (the sampled token of each row).
 void launch_softstat_combine(const SoftStat* part, int n_rows, int n_tiles, const int32_t* n_dev, float* H,
-                             float* lse, int32_t* tok, hipStream_t st);
+                             float* lse, int32_t* tok, const GStat* gpart, int32_t* stok, hipStream_t st);
 void launch_step_init(const int32_t* block_ids, int B, int L, int mask_id, uint8_t* U, float* a, int32_t* tokens,
                       int8_t* cl, int32_t* ncommit, uint8_t* stop, int8_t* loops, int32_t* act, int32_t* src_slot,
                       hipStream_t st);
 void launch_build_lists(int nb, int L, int B, const int32_t* act_cur, const uint8_t* stop, const uint8_t* U,
                         const int32_t* ncommit, int32_t* act_next, int32_t* src_slot, int32_t* ro_rows,
                         int32_t* ro_map, int32_t* cnt, hipStream_t st);
+// stok (optional): sampled token per readout row, committed instead of the argmax tok.
 void launch_commit(int nb, int s, int k_loops, int L, int B, float tau_ent, float tau_halt, const int32_t* act,
-                   uint8_t* U, float* a, const int32_t* ro_map, const float* H, const int32_t* tok, const float* lam,
-                   const float* lse, int32_t* tokens, int8_t* cl, int32_t* ncommit, uint8_t* stop, int8_t* loops,
-                   const int8_t* tf_cl, const int32_t* tf_tok, const int8_t* tf_stop, float* dbg_H, float* dbg_lam,
-                   float* dbg_a, float* dbg_lse, int32_t* dbg_tok, hipStream_t st);
+                   uint8_t* U, float* a, const int32_t* ro_map, const float* H, const int32_t* tok,
+                   const int32_t* stok, const float* lam, const float* lse, int32_t* tokens, int8_t* cl,
+                   int32_t* ncommit, uint8_t* stop, int8_t* loops, const int8_t* tf_cl, const int32_t* tf_tok,
+                   const int8_t* tf_stop, float* dbg_H, float* dbg_lam, float* dbg_a, float* dbg_lse,
+                   int32_t* dbg_tok, int32_t* dbg_stok, hipStream_t st);
 void launch_reset_compact(int dtype, int nb_upper, const int32_t* cnt, int L, int d, int V, const int32_t* act,
                           const int32_t* src, const uint8_t* U, const int32_t* tokens, const float* h_old,
                           const void* E, float* h_new, hipStream_t st);
 void launch_dump_hidden(int nb, int L, int d, int B, int s, const int32_t* act, const float* h, float* out,
                         hipStream_t st);
-void launch_gather_boosts(const int32_t* ro_rows, const int32_t* n_dev, const int32_t* act, int n_upper, int L,
-                          const int32_t* boost_tok, const float* boost_val, int32_t* btok, float* bval, hipStream_t st);
+// Per readout row k (sequence b, block row i): its boost (when boost_tok is given) and its
+// sampling row key 64 * b + i (when rkey is given).
+void launch_gather_rows(const int32_t* ro_rows, const int32_t* n_dev, const int32_t* act, int n_upper, int L,
+                        const int32_t* boost_tok, const float* boost_val, int32_t* btok, float* bval, int32_t* rkey,
+                        hipStream_t st);
 void launch_embed_committed(int dtype, const int8_t* cl, const int32_t* tokens, const void* E, int n, int d, int V,
                             float* out, hipStream_t st);
 

@@ -25,7 +25,7 @@ struct Plan {
   // offsets (bytes) into the workspace
   size_t rope_cos, rope_sin, kcache, vcache, avail;
   size_t h, h_alt, xn, attn, qkv, q, kself, vself, gu, act;
-  size_t r, lam, H, lse, tok, btok, bval, part;
+  size_t r, lam, H, lse, tok, btok, bval, part, gpart, rkey, stok;
   size_t U, a, ro_map, ro_rows, ncommit, stop, seq_loops, act_seq0, act_seq1, src_slot, cnt;
   size_t attn_part, gemm_part;
   // sizes
@@ -115,6 +115,9 @@ Plan make_plan(const alodlm_config& c) {
   p.btok = take(sizeof(int32_t) * Rs);
   p.bval = take(sizeof(float) * Rs);
   p.part = take(16 * Rs * (size_t)p.n_vtiles);
+  p.gpart = take(8 * Rs * (size_t)p.n_vtiles);
+  p.rkey = take(sizeof(int32_t) * Rs);
+  p.stok = take(sizeof(int32_t) * Rs);
   p.U = take(Rs);
   p.a = take(sizeof(float) * Rs);
   p.ro_map = take(sizeof(int32_t) * Rs);
@@ -435,9 +438,10 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   return down_splits;
 }
 
-// LMHead statistics of the readout rows (rows >= *n_dev skipped) then the fixed-order merge.
+// LMHead statistics of the readout rows (rows >= *n_dev skipped) then the fixed-order merge; with
+// smp also the Gumbel-max draw of each row (into the stok buffer).
 void readout_heads(alodlm_ctx* c, const void* rows, int n_upper, const int32_t* n_dev, const int32_t* btok,
-                   const float* bval) {
+                   const float* bval, const SampleParams* smp) {
   const alodlm_config& g = c->cfg;
   const Plan& p = c->plan;
   GemmEpi ep;
@@ -445,9 +449,14 @@ void readout_heads(alodlm_ctx* c, const void* rows, int n_upper, const int32_t* 
   ep.n_tiles = lm_tiles(c, n_upper);
   ep.btok = btok;
   ep.bval = bval;
+  if (smp) {
+    ep.smp = *smp;
+    ep.smp.part = c->at<GStat>(p.gpart);
+  }
   gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_upper, g.vocab, g.d_model, n_dev, ep);
   launch_softstat_combine(c->at<SoftStat>(p.part), n_upper, ep.n_tiles, n_dev, c->at<float>(p.H),
-                          c->at<float>(p.lse), c->at<int32_t>(p.tok), c->st);
+                          c->at<float>(p.lse), c->at<int32_t>(p.tok), smp ? ep.smp.part : nullptr,
+                          smp ? c->at<int32_t>(p.stok) : nullptr, c->st);
 }
 
 bool finite_f(float x) { return isfinite(x) != 0; }
@@ -666,6 +675,10 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
   const bool dbg = o->entropy || o->lam || o->halt || o->lse || o->argmax;
   if (dbg && !(o->entropy && o->lam && o->halt && o->lse && o->argmax))
     return c->fail(ALODLM_EINVAL, "per-loop records must be all given or all null");
+  const bool smp = (a->flags & ALODLM_STEP_SAMPLE) != 0;
+  if (o->sampled && !(smp && dbg))
+    return c->fail(ALODLM_EINVAL, "the sampled record needs ALODLM_STEP_SAMPLE and the other per-loop records");
+  if (a->flags & ~(ALODLM_STEP_TEACHER_FORCED | ALODLM_STEP_SAMPLE)) return c->fail(ALODLM_EINVAL, "unknown flags");
   const int P = c->cache_prefix;
   hipStream_t st = c->st;
   c->layer_calls = 0;
@@ -694,6 +707,7 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
     hipMemsetAsync(o->halt, 0xFF, n * 4, st);
     hipMemsetAsync(o->lse, 0xFF, n * 4, st);
     hipMemsetAsync(o->argmax, 0xFF, n * 4, st);
+    if (o->sampled) hipMemsetAsync(o->sampled, 0xFF, n * 4, st);  // -1 until written
   }
   launch_step_init(a->block_ids, B, L, g.mask_id, U, av, o->tokens, o->commit_loop, ncommit, stop, o->loops, act[0],
                    src_slot, st);
@@ -739,27 +753,36 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
     launch_rmsnorm(dt(c), gsrc, n, d, ro_rows, cnt + 1, c->w.final_norm, g.rms_eps, c->at<void>(p.r), c->w.exit_w,
                    c->w.exit_b, c->at<float>(p.lam), st);
     c->toc();
-    // per-readout-row boosts
+    // per-readout-row boosts and sampling row keys, gathered into readout order on the device
+    // (row t*L+i of the compact list is sequence act[t], block row i)
     const int32_t* bt = nullptr;
     const float* bv = nullptr;
     if (a->boost_tok) {
-      // gather boosts into readout order on the device: boost index = act[t]*L + i for row t*L+i
       bt = c->at<int32_t>(p.btok);
       bv = c->at<float>(p.bval);
-      launch_gather_boosts(ro_rows, cnt + 1, act[cur], n, L, a->boost_tok, a->boost_val, c->at<int32_t>(p.btok),
-                           c->at<float>(p.bval), st);
+    }
+    launch_gather_rows(ro_rows, cnt + 1, act[cur], n, L, a->boost_tok, a->boost_val, c->at<int32_t>(p.btok),
+                       c->at<float>(p.bval), smp ? c->at<int32_t>(p.rkey) : nullptr, st);
+    SampleParams sp;
+    if (smp) {
+      sp.row_key = c->at<int32_t>(p.rkey);
+      sp.k0 = (uint32_t)(a->sample_seed & 0xFFFFFFFFu);
+      sp.k1 = (uint32_t)(a->sample_seed >> 32);
+      sp.c2 = (uint32_t)s;
+      sp.c3 = a->sample_step;
     }
     // after loop 1 the host holds the exact readout row count (read back with the loop status),
     // which picks the LM-head tile; loop 1 uses the bound n
     const int n_read = (s > 1 && host_cnt[1] > 0 && host_cnt[1] <= n) ? host_cnt[1] : n;
     c->tic(ALODLM_K_LM_HEAD);
-    readout_heads(c, c->at<void>(p.r), n_read, cnt + 1, bt, bv);
+    readout_heads(c, c->at<void>(p.r), n_read, cnt + 1, bt, bv, smp ? &sp : nullptr);
     c->toc();
     c->tic(ALODLM_K_CONTROL);
     launch_commit(nb, s, K, L, B, a->tau_ent, a->tau_halt, act[cur], U, av, ro_map, c->at<float>(p.H),
-                  c->at<int32_t>(p.tok), c->at<float>(p.lam), c->at<float>(p.lse), o->tokens, o->commit_loop, ncommit,
-                  stop, o->loops, tf ? a->tf_commit_loop : nullptr, tf ? a->tf_tokens : nullptr,
-                  tf ? a->tf_stop_loop : nullptr, dbg ? o->entropy : nullptr, o->lam, o->halt, o->lse, o->argmax, st);
+                  c->at<int32_t>(p.tok), smp ? c->at<int32_t>(p.stok) : nullptr, c->at<float>(p.lam),
+                  c->at<float>(p.lse), o->tokens, o->commit_loop, ncommit, stop, o->loops,
+                  tf ? a->tf_commit_loop : nullptr, tf ? a->tf_tokens : nullptr, tf ? a->tf_stop_loop : nullptr,
+                  dbg ? o->entropy : nullptr, o->lam, o->halt, o->lse, o->argmax, o->sampled, st);
     launch_build_lists(nb, L, B, act[cur], stop, U, ncommit, act[cur ^ 1], src_slot, ro_rows, ro_map, cnt, st);
     launch_reset_compact(dt(c), nb, cnt, L, d, g.vocab, act[cur ^ 1], src_slot, U, o->tokens, h, c->w.embed, h_alt, st);
     c->toc();
@@ -814,11 +837,12 @@ int alodlm_readout_commit(alodlm_ctx* c, const void* rows, int32_t n_rows, int32
   ep.btok = boost_tok;
   ep.bval = boost_val;
   gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_rows, g.vocab, g.d_model, nullptr, ep);
-  launch_softstat_combine(c->at<SoftStat>(p.part), n_rows, ep.n_tiles, nullptr, entropy, lse, argmax, st);
+  launch_softstat_combine(c->at<SoftStat>(p.part), n_rows, ep.n_tiles, nullptr, entropy, lse, argmax, nullptr, nullptr,
+                          st);
   // one loop of the commit rule (a starts at 0, so a = lambda); per-row records go to the outputs
-  launch_commit(B, 1, 1, L, B, tau_ent, tau_halt, act1, U, halt, c->at<int32_t>(p.ro_map), entropy, argmax, lam, lse,
-                tokens, commit_loop, c->at<int32_t>(p.ncommit), c->at<uint8_t>(p.stop), seq_loops, nullptr, nullptr,
-                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st);
+  launch_commit(B, 1, 1, L, B, tau_ent, tau_halt, act1, U, halt, c->at<int32_t>(p.ro_map), entropy, argmax, nullptr,
+                lam, lse, tokens, commit_loop, c->at<int32_t>(p.ncommit), c->at<uint8_t>(p.stop), seq_loops, nullptr,
+                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st);
   launch_embed_committed(dt(c), commit_loop, tokens, c->w.embed, n_rows, g.d_model, g.vocab, embed_out, st);
   return c->hip_check("readout launch");
 }

@@ -7,28 +7,12 @@
 
 namespace alodlm {
 
-__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
-    c[1] = (uint32_t)p1;
-    c[3] = (uint32_t)p0;
-    c[0] = n0;
-    c[2] = n2;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
-}
-
 __device__ __forceinline__ float ih4_value(uint64_t i, uint32_t seed, uint32_t tensor, float scale) {
   const uint64_t n = i >> 1;
-  uint32_t c[4] = {(uint32_t)n, (uint32_t)(n >> 32), 0u, 0u};
-  philox4x32_10(c, seed, tensor);
-  const uint32_t a = (i & 1) ? c[2] : c[0];
-  const uint32_t b = (i & 1) ? c[3] : c[1];
+  uint32_t c0 = (uint32_t)n, c1 = (uint32_t)(n >> 32), c2 = 0u, c3 = 0u;
+  philox4x32_10(c0, c1, c2, c3, seed, tensor);
+  const uint32_t a = (i & 1) ? c2 : c0;
+  const uint32_t b = (i & 1) ? c3 : c1;
   const int32_t z = (int32_t)((a & 0xFFFFu) + (a >> 16) + (b & 0xFFFFu) + (b >> 16)) - 131070;
   return __fmul_rn((float)z, scale);
 }

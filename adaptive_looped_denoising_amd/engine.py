@@ -41,6 +41,7 @@ class StepResult:
     halt: Optional[np.ndarray] = None
     lse: Optional[np.ndarray] = None
     argmax: Optional[np.ndarray] = None
+    sampled: Optional[np.ndarray] = None
     hidden: Optional[np.ndarray] = None
 
 
@@ -126,7 +127,9 @@ class Engine:
         torch.cuda.synchronize(self.device)
 
     # ------------------------------------------------------------------ step
-    def make_args(self, tau_ent=None, tau_halt=None, k_loops=None, boost=True, teacher=None, block_ids=None):
+    def make_args(self, tau_ent=None, tau_halt=None, k_loops=None, boost=True, teacher=None, block_ids=None,
+                  sample=None):
+        """``sample``: {"seed", "step"} commits Gumbel-max draws (ALODLM_STEP_SAMPLE)."""
         w = self.w
         if block_ids is not None:
             self.block_ids = torch.from_numpy(np.ascontiguousarray(block_ids, dtype=np.int32)).to(self.device)
@@ -148,9 +151,13 @@ class Engine:
             self._tf = [torch.from_numpy(x).to(self.device) for x in (cl, tk, sl)]
             args.flags = B.STEP_TEACHER_FORCED
             args.tf_commit_loop, args.tf_tokens, args.tf_stop_loop = (t.data_ptr() for t in self._tf)
+        if sample is not None:
+            args.flags |= B.STEP_SAMPLE
+            args.sample_seed = int(sample["seed"])
+            args.sample_step = int(sample["step"])
         return args
 
-    def make_out(self, k_loops: int, records: bool = False, hidden: bool = False):
+    def make_out(self, k_loops: int, records: bool = False, hidden: bool = False, sampled: bool = False):
         w = self.w
         out = B.StepOut(tokens=_ptr(self.out_tokens), commit_loop=_ptr(self.out_cl), loops=_ptr(self.out_loops))
         self._rec = None
@@ -161,6 +168,8 @@ class Engine:
                              halt=torch.empty(shp, dtype=torch.float32, device=self.device),
                              lse=torch.empty(shp, dtype=torch.float32, device=self.device),
                              argmax=torch.empty(shp, dtype=torch.int32, device=self.device))
+            if sampled:
+                self._rec["sampled"] = torch.empty(shp, dtype=torch.int32, device=self.device)
             for k, t in self._rec.items():
                 setattr(out, k, t.data_ptr())
         self._hidden = None
@@ -174,9 +183,9 @@ class Engine:
         B.denoise_step(self.ctx, args, out)
 
     def step(self, tau_ent=None, tau_halt=None, k_loops=None, boost=True, teacher=None, records=False,
-             hidden=False, block_ids=None) -> StepResult:
-        args = self.make_args(tau_ent, tau_halt, k_loops, boost, teacher, block_ids)
-        out = self.make_out(args.k_loops, records, hidden)
+             hidden=False, block_ids=None, sample=None) -> StepResult:
+        args = self.make_args(tau_ent, tau_halt, k_loops, boost, teacher, block_ids, sample)
+        out = self.make_out(args.k_loops, records, hidden, sampled=sample is not None)
         self.run(args, out)
         torch.cuda.synchronize(self.device)
         res = StepResult(tokens=self.out_tokens.cpu().numpy(), commit_loop=self.out_cl.cpu().numpy(),

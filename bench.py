@@ -134,8 +134,8 @@ def main():
     prefill_ms = (time.perf_counter() - t0) * 1e3
     progress("prefill %.1f ms" % prefill_ms)
 
-    def timed(tau, steps, warmup):
-        a = e.make_args(tau_ent=tau)
+    def timed(tau, steps, warmup, sample=None):
+        a = e.make_args(tau_ent=tau, sample=sample)
         o = e.make_out(a.k_loops)
         for _ in range(warmup):
             e.run(a, o)
@@ -172,6 +172,18 @@ def main():
     traffic = ffn_gate_up_traffic(w, rows_per_step * args.steps, launches)
     achieved = traffic / (per_launch_ms * 1e-3) / 1e9
     work = algorithmic_work(w, loops)
+    # Sampled commits (Gumbel-max draws in the LM-head epilogue): the same step and timing pass
+    # with ALODLM_STEP_SAMPLE, reported beside the greedy headline.
+    samp = timed(w.tau_ent, args.steps, 1, sample=dict(seed=2024, step=0))
+    B.timing_enable(e.ctx, True)
+    samp_prof = timed(w.tau_ent, args.steps, 0, sample=dict(seed=2024, step=0))
+    skt = B.timing_read(e.ctx)
+    B.timing_enable(e.ctx, False)
+    progress("sampled commits: %s" % samp)
+    sampled = dict(tok_s=samp["tok_s"], ms_per_step=samp["ms_per_step"], committed_per_step=samp["committed_per_step"],
+                   lm_head_ms_per_step=skt["lm_head"][0] / args.steps,
+                   lm_head_ms_per_step_greedy=kt["lm_head"][0] / args.steps,
+                   timing_pass_ms_per_step=samp_prof["ms_per_step"])
     kernels = {}
     for k, v in kt.items():
         ms = v[0] / args.steps
@@ -207,6 +219,7 @@ def main():
                                "algorithmic per launch" % (GATE_UP_KERNEL, rows_per_step / max(launches / args.steps, 1),
                                                            per_launch_ms * 1e3, traffic / 1e6)},
         "tau_sweep": sweep,
+        "sampled_commits": sampled,
         "prefill_ms": prefill_ms,
         # per class: event-timed ms (the event pairs add a little time to short kernels, so the
         # fractions are lower bounds) with algorithmic bytes / flops and their roofline fractions

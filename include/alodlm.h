@@ -138,6 +138,18 @@ ALODLM_API int alodlm_prefill_kv_synthetic(alodlm_ctx* ctx, int32_t batch, int32
                                 float k_scale, float v_scale, const uint8_t* avail_depth);
 
 #define ALODLM_STEP_TEACHER_FORCED 1u /* take commits, tokens and stop loops from tf_* */
+/* Sampled commits (same page, section "Method step details", Algorithm 1 step 3: a committed
+ * position takes a draw y ~ p of its readout distribution).  Without this flag the committed
+ * token is the argmax (greedy).  With it, the token of readout row i of sequence b at loop s is
+ * the Gumbel-max draw
+ *     y = argmax_v (z_v + g_v)   (lowest v on ties),   g_v = -ln(-ln u_v),
+ *     u_v = (floor(x_v / 2^9) + 1/2) / 2^23,
+ * where z_v is the logit (with the planted boost) and x_v is word (v mod 4) of Philox4x32-10
+ * (Salmon, Moraes, Dror, Shaw, SC'11) at counter (v div 4, 64 b + i, s, sample_step) under key
+ * (sample_seed mod 2^32, sample_seed div 2^32).  b is the sequence's index in the batch and i its
+ * block row.  Entropy, commit test, halting and the argmax record are unchanged; a forced commit
+ * takes its row's draw of the last loop.  The same (seed, step) replays the same draws. */
+#define ALODLM_STEP_SAMPLE 2u
 
 typedef struct alodlm_step_args {
   int32_t batch;              /* sequences, == the prefilled batch */
@@ -152,6 +164,8 @@ typedef struct alodlm_step_args {
   const int8_t* tf_commit_loop; /* teacher-forced only: device [batch][L], loop s (or -s forced) or 0 */
   const int32_t* tf_tokens;   /* teacher-forced only: device [batch][L], committed token ids */
   const int8_t* tf_stop_loop; /* teacher-forced only: device [batch], loop at which the sequence stops */
+  uint64_t sample_seed;       /* ALODLM_STEP_SAMPLE: Philox key of the draws */
+  uint32_t sample_step;       /* ALODLM_STEP_SAMPLE: fourth counter word, e.g. the index of the denoising step */
 } alodlm_step_args;
 
 typedef struct alodlm_step_out {
@@ -167,6 +181,8 @@ typedef struct alodlm_step_out {
   float* hidden;         /* optional device [k_loops][batch][L][d]: Core output h~ per loop (fp32) */
   int32_t n_committed;   /* host: tokens committed by the step, filled on return */
   int32_t loops_run;     /* host: largest loop count over the batch, filled on return */
+  int32_t* sampled;      /* optional device [k_loops][batch][L]: the draw of each read-out row (-1 where
+                            not read out); needs ALODLM_STEP_SAMPLE and the per-loop records above */
 } alodlm_step_out;
 
 /* Runs one denoising step over the prefilled batch.  Enqueues all work on the

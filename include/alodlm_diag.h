@@ -37,6 +37,19 @@ __attribute__((visibility("default"))) int alodlm_diag_gemm(int32_t epi, int32_t
                                                             int32_t force_splits, int32_t force_generic,
                                                             int32_t force_tile, void* hip_stream);
 
+/* Gumbel-max draws of the logits z = A.B^T (bf16 A [M][K], B [N][K]) through the step's LM-head
+ * kernel: tok[m] = argmax_n (z[m][n] + g), g the Gumbel noise of ALODLM_STEP_SAMPLE in alodlm.h
+ * with counter (n div 4, row_key[m], c2, c3) and key (seed mod 2^32, seed div 2^32).  row_key:
+ * device int32 [M]; tok: device int32 [M].  scratch: device floats, at least 6 * M * ceil(N / 64)
+ * + 3 * M.  force_generic, force_tile as in alodlm_diag_gemm.  Asynchronous.  Returns 0, -1 (bad
+ * arguments, checked before any launch) or -4 (launch failed). */
+__attribute__((visibility("default"))) int alodlm_diag_readout_sample(int32_t M, int32_t N, int32_t K, const void* A,
+                                                                      const void* B, const int32_t* row_key,
+                                                                      uint64_t seed, uint32_t c2, uint32_t c3,
+                                                                      int32_t* tok, float* scratch,
+                                                                      size_t scratch_floats, int32_t force_generic,
+                                                                      int32_t force_tile, void* hip_stream);
+
 /* Copies prefix-cache rows back for inspection: K and V of cache slot `slot`, sequence b,
  * positions j0 .. j0+n-1, every kv head, into dst_k / dst_v (device, config dtype,
  * [Hkv][n][hd]).  After a prefill the Core depth slot of depth p holds position j at depth

@@ -119,6 +119,12 @@ def compare_records(w: synth.Workload, oracle_res: List[dict], gpu, check_hidden
                 if mism.any():  # only allowed where the oracle's top-2 gap is within the flag tolerance
                     assert (rec["gap"][rows][mism] < tol["gap"]).all(), "seq %d loop %d argmax mismatch" % (b, s + 1)
                     worst["tok_mismatch"] += int(mism.sum())
+                if "stok" in rec and getattr(gpu, "sampled", None) is not None:
+                    mism = gpu.sampled[s, b, rows] != rec["stok"][rows]
+                    if mism.any():  # the draw may differ only where the top-2 gap of z + g is within tolerance
+                        assert (rec["sgap"][rows][mism] < tol["gap"]).all(), "seq %d loop %d draw mismatch" % (
+                            b, s + 1)
+                        worst["tok_mismatch"] += int(mism.sum())
             if check_hidden and gpu.hidden is not None and "h_tilde" in rec:
                 e = rel_rows(gpu.hidden[s, b], rec["h_tilde"])
                 worst["hidden"] = max(worst["hidden"], float(e.max()))

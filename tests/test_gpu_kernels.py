@@ -98,6 +98,34 @@ def test_softstat_every_tile(gpu_lib, tile):
     assert ok.all()
 
 
+@pytest.mark.parametrize("tile", list(range(56)) + ["generic"])
+def test_readout_sample_every_tile(gpu_lib, tile):
+    """Gumbel-max draws of the LM-head kernel (every tile and the vector-ALU path), on a ragged
+    shape, against argmax(z + g) with z in float64 on the same bf16 operands and g the oracle's own
+    noise at the same counters.  A draw may differ only where the top two of z + g are within the
+    fp32 accumulation error."""
+    from adaptive_looped_denoising_amd import binding as B
+    M, N, K = 77, 1000, 256
+    seed, loop, step = 0x0123456789ABCDEF, 3, 41
+    A, Bm = _bf16((M, K), 22), _bf16((N, K), 23, 0.1)
+    z = _ref(A, Bm)
+    bi = [(m // 50 + 1, (7 * m) % 50) for m in range(M)]
+    G = np.stack([orc.gumbel_noise(seed, step, b, i, loop, N) for b, i in bi])
+    want, gap = orc.gumbel_sample(z, G)
+    rk = torch.tensor([64 * b + i for b, i in bi], dtype=torch.int32, device="cuda")
+    tok = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    scratch = torch.empty(6 * M * ((N + 63) // 64) + 3 * M, dtype=torch.float32, device="cuda")
+    Ad, Bd = A.cuda(), Bm.cuda()  # held until the asynchronous launch has finished
+    B.diag_readout_sample(M, N, K, Ad.data_ptr(), Bd.data_ptr(), rk.data_ptr(), seed, loop, step, tok.data_ptr(),
+                          scratch.data_ptr(), scratch.numel(), 1 if tile == "generic" else 0,
+                          torch.cuda.current_stream().cuda_stream, -1 if tile == "generic" else tile)
+    torch.cuda.synchronize()
+    got = tok.cpu().numpy()
+    ok = (got == want) | (gap < 1e-4)
+    assert ok.all(), (np.nonzero(~ok)[0][:8], got[~ok][:8], want[~ok][:8])
+    assert (got != z.argmax(axis=1)).sum() > M // 4   # the draws are not the argmax
+
+
 @pytest.mark.parametrize("splits", [2, 4, 8])
 def test_gemm_split_k_matches_single_pass(gpu_lib, splits):
     M, N, K = 96, 2048, 4096

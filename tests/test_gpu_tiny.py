@@ -20,25 +20,26 @@ def _engine(w, **kw):
     return e
 
 
-def _check_step(w, gpu_lib, k_loops=None, block_ids=None, overrides=None, oracle_W=None):
-    log("case %s dtype=%s B=%d P=%d L=%d K=%d tau=%.3g q=%.3g" % (w.name, w.dtype, w.batch, w.prefix, w.block,
-                                                                  w.k_max, w.tau_ent, w.tau_halt))
+def _check_step(w, gpu_lib, k_loops=None, block_ids=None, overrides=None, oracle_W=None, sample=None):
+    log("case %s dtype=%s B=%d P=%d L=%d K=%d tau=%.3g q=%.3g sample=%s" % (
+        w.name, w.dtype, w.batch, w.prefix, w.block, w.k_max, w.tau_ent, w.tau_halt, sample))
     e = _engine(w, overrides=overrides)
     K = w.k_max if k_loops is None else k_loops
     W = orun.weights(w) if oracle_W is None else oracle_W
-    ores = orun.step(w, W=W, k_loops=K, record_hidden=True, block_ids=block_ids)
+    ores = orun.step(w, W=W, k_loops=K, record_hidden=True, block_ids=block_ids, sample=sample)
     tols = None
     if w.dtype == "bf16":  # bf16 drift of this input: the oracle at the pipeline's rounding points
         o16 = orun.step(w, W=W, k_loops=K, record_hidden=True, block_ids=block_ids, prec="bf16",
                         teacher=orun.teacher_from(ores))
         tols = calibrated_tolerances(w, ores, o16)
-    free = e.step(k_loops=K, records=True, hidden=True, block_ids=block_ids)
+    free = e.step(k_loops=K, records=True, hidden=True, block_ids=block_ids, sample=sample)
     flagged = compare_decisions(w, ores, free, tols)
     clean = [r for r in ores if r["seq"] not in flagged]
     if clean:
         worst = compare_records(w, clean, free, tols=tols)
         log("free run worst errors: %s" % worst)
-    tf = e.step(k_loops=K, records=True, hidden=True, teacher=orun.teacher_from(ores), block_ids=block_ids)
+    tf = e.step(k_loops=K, records=True, hidden=True, teacher=orun.teacher_from(ores), block_ids=block_ids,
+                sample=sample)
     worst = compare_records(w, ores, tf, tols=tols)
     log("teacher-forced worst errors: %s" % worst)
     for r in ores:
@@ -117,6 +118,44 @@ def test_tiny_bf16_step(gpu_lib):
     _check_step(w, gpu_lib)
 
 
+SAMPLE = dict(seed=0x5EED0000CAFE1234, step=9)
+
+
+def test_tiny_fp32_sampled_commits(gpu_lib):
+    """Sampled commits (Gumbel-max draws at the documented counters) against the oracle's own
+    generator: a high entropy threshold commits most rows at loop 1 with draws that mostly differ
+    from the argmax; a negative one leaves only the forced commit, which takes its draw."""
+    w = synth.workload("tiny", batch=3, tau_ent=4.0, tau_halt=0.9)
+    _, ores, free = _check_step(w, gpu_lib, sample=SAMPLE)
+    rec = ores[0]["records"][0]
+    assert (rec["stok"][rec["rows"]] != rec["tok"][rec["rows"]]).sum() > 4
+    w2 = synth.workload("tiny", batch=2, tau_ent=-1.0, tau_halt=0.6)
+    _, ores2, _ = _check_step(w2, gpu_lib, sample=dict(seed=77, step=1))
+    assert all(r["forced"] >= 0 for r in ores2)
+
+
+def test_tiny_sampled_replay_and_steps(gpu_lib):
+    """The same (seed, step) replays bit for bit; another step index draws other tokens."""
+    w = synth.workload("tiny", batch=2, tau_ent=4.0)
+    e = _engine(w)
+    a = e.step(records=True, sample=dict(seed=5, step=0))
+    b = e.step(records=True, sample=dict(seed=5, step=0))
+    c = e.step(records=True, sample=dict(seed=5, step=1))
+    assert np.array_equal(a.tokens, b.tokens) and np.array_equal(a.sampled, b.sampled)
+    assert not np.array_equal(a.sampled, c.sampled)
+    from adaptive_looped_denoising_amd import binding as B
+    out = e.make_out(w.k_max)          # a sampled record without the sampled flag is refused
+    out.sampled = e.out_tokens.data_ptr()
+    with pytest.raises(B.AlodlmError) as ex:
+        e.run(e.make_args(), out)
+    assert ex.value.code == B.EINVAL
+
+
+def test_tiny_bf16_sampled_step(gpu_lib):
+    w = replace(synth.workload("tiny", batch=2, tau_ent=5.8), dtype="bf16", name="tiny_bf16")
+    _check_step(w, gpu_lib, sample=SAMPLE)
+
+
 def test_tiny_deterministic(gpu_lib):
     w = synth.workload("tiny", boost_lo=8.0, boost_hi=14.0)
     e = _engine(w)
@@ -170,6 +209,11 @@ def test_mid_bf16_synthetic_cache_depth_fallback(gpu_lib):
 def test_mid_bf16_block_64_and_single_row(gpu_lib):
     _check_step(_mid(block=64, prefix=130, batch=2), gpu_lib)
     _check_step(_mid(block=1, prefix=64, batch=4, tau_halt=0.3), gpu_lib)
+
+
+def test_mid_bf16_sampled_step(gpu_lib):
+    """Sampled commits through the matrix-core LM-head tiles (vocab 4096, hd 128)."""
+    _check_step(_mid(tau_ent=7.0, boost_lo=3.0, boost_hi=8.0), gpu_lib, sample=SAMPLE)
 
 
 def test_mid_fp32_matches_bf16_structure(gpu_lib):
