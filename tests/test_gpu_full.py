@@ -124,16 +124,16 @@ def _check_prefill_prefix(w, n_pos, seqs):
     e.close()
 
 
-def _check_step(w, seqs):
+def _check_step(w, seqs, sample=None):
     e = _engine(w)
     W = _oracle_weights(w)
-    log("case %s B=%d P=%d L=%d K=%d tau=%.2f q=%.2f, oracle on sequences %s" % (
-        w.name, w.batch, w.prefix, w.block, w.k_max, w.tau_ent, w.tau_halt, list(seqs)))
-    free = e.step(records=True, hidden=True)
+    log("case %s B=%d P=%d L=%d K=%d tau=%.2f q=%.2f sample=%s, oracle on sequences %s" % (
+        w.name, w.batch, w.prefix, w.block, w.k_max, w.tau_ent, w.tau_halt, sample, list(seqs)))
+    free = e.step(records=True, hidden=True, sample=sample)
     caches = {}
     for b in seqs:
         caches[b] = orun.cache_for(w, W, b)
-    ores = orun.step(w, W=W, seqs=seqs, record_hidden=True, caches=caches,
+    ores = orun.step(w, W=W, seqs=seqs, record_hidden=True, caches=caches, sample=sample,
                      progress=lambda m: print(m, flush=True) if m.endswith(" 0") else None)
     o16 = orun.step(w, W=W, seqs=seqs, record_hidden=True, caches=caches, prec="bf16",
                     teacher=orun.teacher_from(ores))
@@ -147,7 +147,7 @@ def _check_step(w, seqs):
     for b in range(w.batch):   # sequences the oracle did not run keep their own decisions
         if b not in teacher:
             teacher[b] = dict(commit_loop=free.commit_loop[b], tokens=free.tokens[b], stop_loop=free.loops[b])
-    tf = e.step(records=True, hidden=True, teacher=teacher)
+    tf = e.step(records=True, hidden=True, teacher=teacher, sample=sample)
     log("teacher-forced worst errors: %s" % compare_records(w, ores, tf, tols=tols))
     for r in ores:
         b = r["seq"]
@@ -186,6 +186,16 @@ def test_qwen3_8b_step_with_entropy_commits(gpu_lib):
     w = synth.workload("qwen3_8b", kv="synthetic", boost_lo=10.0, boost_hi=20.0, tau_ent=0.9)
     e, ores, free = _check_step(w, [2])
     assert sum(int((r["commit_loop"] > 0).sum()) for r in ores) > 0
+    e.close()
+
+
+def test_qwen3_8b_sampled_commits(gpu_lib):
+    """Sampled commits at the 8B vocabulary (151936 Gumbel-max candidates per row) in the benchmark's
+    launch configuration: draws, commit schedule and tokens against the oracle's own generator."""
+    w = synth.workload("qwen3_8b", kv="synthetic", boost_lo=10.0, boost_hi=20.0, tau_ent=0.9)
+    e, ores, free = _check_step(w, [3], sample=dict(seed=0xA11CE5EED, step=17))
+    assert sum(int((r["commit_loop"] > 0).sum()) for r in ores) > 0
+    assert free.sampled is not None and (free.sampled[0] >= 0).sum() > 0
     e.close()
 
 
