@@ -52,7 +52,19 @@ follow them):
   * committed rows keep running through every layer as context;
   * if a step committed nothing, the unresolved position of lowest entropy at
     the last loop (ties to the lowest position) commits, recorded as -s_end;
-  * ExitGate is a d -> 1 linear map plus sigmoid.
+  * ExitGate is a d -> 1 linear map plus sigmoid;
+  * a sequence whose block has no masked position runs no loop (loops = 0):
+    the outer loop of Algorithm 1 ends once no [MASK] remains;
+  * outer loop: denoising steps over a block until no position is masked,
+    each step starting from the Prelude of the block with every committed
+    token written in; denoising step t (1-based) of a block draws its samples
+    with counter word 3 = step0 + t - 1;
+  * a finished block joins the depth-aware cache the way the prefill builds
+    it: its positions go through the Prelude once, the Core once per depth
+    d = 1..k_max and the Coda once on the depth-k_max output, causally among
+    themselves, reading the cached positions as a step does (Core position j
+    at depth min(d, avail_j)); they are cached at every depth.  With every
+    cached position at full depth this is the prefill of the longer prefix.
 """
 from __future__ import annotations
 
@@ -242,6 +254,45 @@ def context_for(cache, dims, k_max: int, layer: int, loop: int, avail):
     return _f64(K), _f64(V)
 
 
+def extend_sequence(cache, avail, new_ids, W, dims, k_max: int, eps: float, theta: float, prec=None):
+    """Appends positions (a finished block) to the depth-aware cache of one sequence.
+
+    The new positions (ids ``new_ids``, positions P.. after the P cached ones) run through the
+    Prelude once, the Core once per depth d = 1..k_max and the Coda once on the depth-k_max
+    output, causally among themselves; cached position j is read as a step reads it (Core depth
+    min(d, avail_j)).  Returns the longer cache (slot -> (K, V) [Hkv][P + n][hd]) and its
+    available depths (the new positions at every depth)."""
+    new_ids = np.asarray(new_ids)
+    n = new_ids.shape[0]
+    P = next(iter(cache.values()))[0].shape[1] if cache else 0
+    pos = P + np.arange(n)
+    x = _f64(W["embed"][new_ids])
+    new = {}
+
+    def run(li, depth):
+        nonlocal x
+        ck, cv = context_for(cache, dims, k_max, li, depth, avail) if cache else (None, None)
+        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, ck, cv, causal=True, prec=prec)
+        new[kv_slot(dims, k_max, li, depth)] = (k, v)
+
+    for li in range(dims.n_pre):
+        run(li, 1)
+    for depth in range(1, k_max + 1):
+        for c in range(dims.n_core):
+            run(dims.n_pre + c, depth)
+    for c in range(dims.n_coda):
+        run(dims.n_pre + dims.n_core + c, 1)
+    out = {}
+    for slot, (k, v) in new.items():
+        if cache:
+            out[slot] = (np.concatenate([_f64(cache[slot][0]), k], axis=1),
+                         np.concatenate([_f64(cache[slot][1]), v], axis=1))
+        else:
+            out[slot] = (k, v)
+    av0 = np.full(P, k_max, dtype=np.int64) if avail is None else np.asarray(avail, dtype=np.int64)
+    return out, np.concatenate([av0, np.full(n, k_max, dtype=np.int64)])
+
+
 # ---------------------------------------------------------------------------
 # the two heads
 # ---------------------------------------------------------------------------
@@ -372,6 +423,8 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
     C = np.zeros(L, dtype=bool)
     tokens = block_ids.copy()
     commit_loop = np.zeros(L, dtype=np.int64)
+    if not U.any():   # nothing to denoise: no loop runs
+        return dict(tokens=tokens, commit_loop=commit_loop, loops=0, records=[], forced=-1, forced_gap=float("nan"))
     a = np.zeros(L, dtype=F64)
     h = _f64(W["embed"][block_ids])
     for li in range(dims.n_pre):
@@ -472,6 +525,33 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
             U[forced] = False
     return dict(tokens=tokens, commit_loop=commit_loop, loops=s_end, records=loops, forced=forced,
                 forced_gap=forced_gap)
+
+
+def denoise_block_sequence(block_ids, cache, avail, W, dims, *, max_steps: Optional[int] = None,
+                           sample: Optional[dict] = None, mask_id: int, **step_kw) -> dict:
+    """Outer loop of Algorithm 1 over one sequence's block: denoising steps until no position is
+    masked (or ``max_steps``), each starting from the block with the committed tokens written in.
+    Every step commits at least one position (forced progress), so a block of L positions takes
+    at most L steps.  ``sample`` {"seed", "step0"}: step t draws with counter word 3 = step0 + t - 1.
+    ``step_kw``: the remaining arguments of denoise_step_sequence.  Returns the final ids, per
+    position the step (1-based, 0 = not committed) and the loop of its commit, the number of
+    steps and each step's result."""
+    ids = np.asarray(block_ids, dtype=np.int64).copy()
+    L = ids.shape[0]
+    commit_step = np.zeros(L, dtype=np.int64)
+    commit_loop = np.zeros(L, dtype=np.int64)
+    results = []
+    while (ids == mask_id).any() and (max_steps is None or len(results) < max_steps):
+        t = len(results) + 1
+        smp = None if sample is None else dict(seed=sample["seed"], step=sample["step0"] + t - 1,
+                                               seq=sample["seq"])
+        res = denoise_step_sequence(ids, cache, avail, W, dims, mask_id=mask_id, sample=smp, **step_kw)
+        newly = res["commit_loop"] != 0
+        commit_step[newly] = t
+        commit_loop[newly] = res["commit_loop"][newly]
+        ids = np.asarray(res["tokens"], dtype=np.int64).copy()
+        results.append(res)
+    return dict(tokens=ids, commit_step=commit_step, commit_loop=commit_loop, steps=len(results), results=results)
 
 
 def readout_commit_group(r, W_lm, embed, exit_w, exit_b: float, tau_ent: float, tau_halt: float,

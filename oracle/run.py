@@ -60,6 +60,35 @@ def step(w: synth.Workload, W=None, seqs=None, k_loops: Optional[int] = None, te
     return out
 
 
+def step_kwargs(w: synth.Workload, k_loops: Optional[int] = None, exit_b: Optional[float] = None) -> dict:
+    """Keyword arguments of the oracle step for the workload's model and thresholds."""
+    return dict(k_max=w.k_max, k_loops=w.k_max if k_loops is None else k_loops, eps=w.rms_eps,
+                theta=w.rope_theta, tau_ent=w.tau_ent, tau_halt=w.tau_halt,
+                exit_b=w.exit_bias() if exit_b is None else exit_b)
+
+
+def denoise_block(w: synth.Workload, W=None, seqs=None, block_ids=None, boost=None, caches=None, avail=None,
+                  sample: Optional[dict] = None, max_steps: Optional[int] = None, prec=None) -> List[dict]:
+    """Oracle outer loop (steps until no mask) for the listed sequences of the workload
+    (``sample`` = {"seed", "step0"})."""
+    W = weights(w) if W is None else W
+    seqs = range(w.batch) if seqs is None else seqs
+    bids = synth.block_ids(w) if block_ids is None else block_ids
+    btok, bval = synth.boosts(w) if boost is None else boost
+    av = synth.avail_depth(w) if avail is None else avail
+    pids = synth.prefix_ids(w) if (w.kv == "prefill" and w.prefix) else None
+    out = []
+    for b in seqs:
+        cache = caches[b] if caches is not None else cache_for(w, W, b, pids, None, prec)
+        res = orc.denoise_block_sequence(
+            bids[b], cache, av[b] if av is not None and w.prefix else None, W, w.dims, max_steps=max_steps,
+            sample=None if sample is None else dict(sample, seq=b), mask_id=w.mask_id, boost_tok=btok[b],
+            boost_val=bval[b], prec=prec, **step_kwargs(w))
+        res["seq"] = b
+        out.append(res)
+    return out
+
+
 def teacher_from(results: List[dict]) -> Dict[int, dict]:
     """Teacher-forcing decisions (commit loops, tokens, stop loop) taken from oracle results."""
     return {r["seq"]: dict(commit_loop=r["commit_loop"], tokens=r["tokens"], stop_loop=r["loops"])

@@ -552,3 +552,94 @@ def test_sampled_forced_commit_takes_the_draw():
     i = res["forced"]
     assert i == int(np.argmin(last["H"])) and res["tokens"][i] == last["stok"][i]
     assert res["commit_loop"][i] == -w.k_max
+
+
+# --------------------------------------------------------------------------- outer loop and cache growth
+def test_extend_equals_prefill_of_the_longer_prefix():
+    """By causality, appending positions to a full-depth cache gives the prefill of the longer
+    prefix, whether appended at once, in pieces, or onto an empty cache."""
+    w = _tiny()
+    W = _rand_weights(w)
+    ids = np.random.default_rng(5).integers(0, w.dims.vocab, size=20)
+    kw = dict(dims=w.dims, k_max=w.k_max, eps=w.rms_eps, theta=w.rope_theta)
+    full = orc.prefill_sequence(ids, W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+    part = orc.prefill_sequence(ids[:12], W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+    one, av1 = orc.extend_sequence(part, None, ids[12:], W, **kw)
+    two, _ = orc.extend_sequence(part, None, ids[12:15], W, **kw)
+    two, av2 = orc.extend_sequence(two, None, ids[15:], W, **kw)
+    empty, _ = orc.extend_sequence({}, None, ids[:8], W, **kw)
+    ref8 = orc.prefill_sequence(ids[:8], W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+    assert sorted(one) == sorted(full) and (av1 == w.k_max).all() and av2.shape == (20,)
+    for slot in full:
+        for a, b, c in zip(one[slot], two[slot], full[slot]):
+            np.testing.assert_allclose(a, c, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(b, c, rtol=1e-11, atol=1e-12)
+        for a, c in zip(empty[slot], ref8[slot]):
+            np.testing.assert_allclose(a, c, rtol=1e-11, atol=1e-12)
+
+
+def test_extend_reads_cached_positions_at_their_available_depth():
+    """Cached positions with available depth 1 are read at depth 1 by every Core pass of the
+    appended positions: the same as a cache whose deeper Core slots hold the depth-1 values."""
+    w = _tiny()
+    W = _rand_weights(w, seed=2)
+    D = w.dims
+    ids = np.random.default_rng(6).integers(0, D.vocab, size=14)
+    kw = dict(dims=D, k_max=w.k_max, eps=w.rms_eps, theta=w.rope_theta)
+    cache = orc.prefill_sequence(ids[:10], W, D, w.k_max, w.rms_eps, w.rope_theta)
+    flat = dict(cache)
+    for c in range(D.n_core):
+        for dpt in range(2, w.k_max + 1):
+            flat[orc.kv_slot(D, w.k_max, D.n_pre + c, dpt)] = cache[orc.kv_slot(D, w.k_max, D.n_pre + c, 1)]
+    a, _ = orc.extend_sequence(cache, np.ones(10, dtype=int), ids[10:], W, **kw)
+    b, _ = orc.extend_sequence(flat, None, ids[10:], W, **kw)
+    c, _ = orc.extend_sequence(cache, None, ids[10:], W, **kw)
+    deep = orc.kv_slot(D, w.k_max, D.n_pre, w.k_max)
+    for slot in a:
+        np.testing.assert_allclose(a[slot][0][:, 10:], b[slot][0][:, 10:], rtol=1e-11, atol=1e-12)
+    assert not np.allclose(a[deep][0][:, 10:], c[deep][0][:, 10:])
+
+
+def test_outer_loop_resolves_every_mask():
+    w = _tiny(boost_lo=8.0, boost_hi=14.0, batch=2)
+    bids = synth.block_ids(w)
+    bids[1, [2, 3, 9]] = [11, 12, 13]
+    res = run.denoise_block(w, block_ids=bids)
+    for r in res:
+        b = r["seq"]
+        masked = bids[b] == w.mask_id
+        assert (r["tokens"] != w.mask_id).all() and np.array_equal(r["tokens"][~masked], bids[b][~masked])
+        assert (r["commit_step"][masked] >= 1).all() and (r["commit_step"][~masked] == 0).all()
+        assert 1 <= r["steps"] <= masked.sum()
+        assert all(int((st["commit_loop"] != 0).sum()) >= 1 for st in r["results"])
+        assert r["steps"] < masked.sum()          # entropy commits: several tokens in some step
+    # the first step is the plain step
+    first = run.step(w, block_ids=bids)
+    for r, f in zip(res, first):
+        assert np.array_equal(r["results"][0]["tokens"], f["tokens"])
+
+
+def test_one_token_per_step_mode():
+    """tau_ent < 0 commits nothing by entropy, so every step commits exactly its forced token: a
+    block with n masks takes n steps, one position each."""
+    w = _tiny(tau_ent=-1.0, tau_halt=0.5)
+    r = run.denoise_block(w)[0]
+    masked = synth.block_ids(w)[0] == w.mask_id
+    n = int(masked.sum())
+    assert r["steps"] == n
+    assert sorted(r["commit_step"][masked].tolist()) == list(range(1, n + 1))
+    assert (r["commit_loop"][masked] < 0).all()
+
+
+def test_no_mask_no_loop_and_sampled_steps_advance_the_counter():
+    w = _tiny(tau_ent=4.0)
+    full = synth.block_ids(w)
+    full[:] = 5
+    r = run.step(w, block_ids=full)[0]
+    assert r["loops"] == 0 and r["records"] == [] and (r["commit_loop"] == 0).all()
+    assert run.denoise_block(w, block_ids=full)[0]["steps"] == 0
+    blk = run.denoise_block(w, sample=dict(seed=9, step0=5))[0]
+    assert blk["steps"] >= 2
+    ids1 = np.asarray(blk["results"][0]["tokens"])
+    again = run.step(w, block_ids=ids1[None, :], sample=dict(seed=9, step=6))[0]
+    assert np.array_equal(again["tokens"], blk["results"][1]["tokens"])
