@@ -19,7 +19,8 @@ STEP_TEACHER_FORCED, STEP_SAMPLE = 1, 2
 DIAG_STORE, DIAG_RESID, DIAG_SOFTSTAT, DIAG_SWIGLU = 0, 1, 2, 3
 
 EXPORTS = ("alodlm_workspace_bytes", "alodlm_kv_slots", "alodlm_create", "alodlm_prefill_kv",
-           "alodlm_prefill_kv_synthetic", "alodlm_denoise_step", "alodlm_readout_commit",
+           "alodlm_prefill_kv_synthetic", "alodlm_extend_kv", "alodlm_denoise_step", "alodlm_denoise_block",
+           "alodlm_readout_commit",
            "alodlm_last_step_stats", "alodlm_last_error", "alodlm_destroy", "alodlm_synth_fill",
            "alodlm_diag_gemm", "alodlm_diag_timing_enable", "alodlm_diag_timing_read", "alodlm_diag_read_kv", "alodlm_diag_buffer_offset",
            "alodlm_diag_readout_sample")
@@ -56,6 +57,15 @@ class StepOut(ctypes.Structure):
                 ("hidden", c_void_p), ("n_committed", c_int32), ("loops_run", c_int32), ("sampled", c_void_p)]
 
 
+class BlockArgs(ctypes.Structure):
+    _fields_ = [("step", StepArgs), ("max_steps", c_int32), ("append", c_int32)]
+
+
+class BlockOut(ctypes.Structure):
+    _fields_ = [("tokens", c_void_p), ("commit_step", c_void_p), ("commit_loop", c_void_p), ("n_steps", c_int32),
+                ("n_committed", c_int32)]
+
+
 class AlodlmError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__("alodlm error %d: %s" % (code, msg))
@@ -80,6 +90,8 @@ def load(path: str = LIB_PATH):
     lib.alodlm_prefill_kv.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p]
     lib.alodlm_prefill_kv_synthetic.argtypes = [c_void_p, c_int32, c_int32, c_uint32, c_float, c_float, c_void_p]
     lib.alodlm_denoise_step.argtypes = [c_void_p, P(StepArgs), P(StepOut)]
+    lib.alodlm_extend_kv.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p]
+    lib.alodlm_denoise_block.argtypes = [c_void_p, P(BlockArgs), P(BlockOut)]
     lib.alodlm_readout_commit.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_float, c_float, c_void_p,
                                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                           c_void_p, c_void_p]
@@ -145,6 +157,15 @@ def prefill_kv_synthetic(ctx: int, batch: int, prefix_len: int, seed: int, k_sca
 
 def denoise_step(ctx: int, args: StepArgs, out: StepOut):
     _check(load().alodlm_denoise_step(c_void_p(ctx), ctypes.byref(args), ctypes.byref(out)), c_void_p(ctx))
+
+
+def extend_kv(ctx: int, batch: int, n_new: int, new_ids_ptr: int, avail_ptr: int = 0):
+    _check(load().alodlm_extend_kv(c_void_p(ctx), batch, n_new, c_void_p(new_ids_ptr), c_void_p(avail_ptr or None)),
+           c_void_p(ctx))
+
+
+def denoise_block(ctx: int, args: BlockArgs, out: BlockOut):
+    _check(load().alodlm_denoise_block(c_void_p(ctx), ctypes.byref(args), ctypes.byref(out)), c_void_p(ctx))
 
 
 def readout_commit(ctx: int, rows_ptr: int, n_rows: int, group: int, tau_ent: float, tau_halt: float,

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
   int TE = TP + (p.n_self + AKT - 1) / AKT;
   if (p.causal) {  // the block's last query position bounds the own keys it can see
     const int last_row = min(rows_q, (qb + 1) * QB) - 1;
-    TE = min(TE, TP + (last_row / G) / AKT + 1);
+    TE = min(TE, TP + (last_row / G + p.causal_off) / AKT + 1);
   }
   const int tb = sp * tiles_per_split;
   const int te = min(TE, tb + tiles_per_split);
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
         for (int v = 0; v < 4; ++v) {
           const int kk = k0 + ks * 16 + quad * 4 + v;  // key within its segment
           bool ok = kk < klen && qok[nq];
-          if (p.causal && !pre) ok = ok && kk <= qpos[nq];
+          if (p.causal && !pre) ok = ok && kk <= qpos[nq] + p.causal_off;
           const float sc = ok ? s[ks][nq][v] * p.scale : -INFINITY;
           s[ks][nq][v] = sc;
           mx = fmaxf(mx, sc);

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(64) void k_attn_generic(AttnParams p) {
   const T* q = (const T*)p.q + ((size_t)r * p.Hq + h) * p.hd;
   for (int e = lane; e < p.hd; e += 64) qs[e] = to_f(q[e]);
   __syncthreads();
-  const int n_keys = p.n_cache + (p.causal ? (i + 1) : p.n_self);
+  const int n_keys = p.n_cache + (p.causal ? min(i + 1 + p.causal_off, p.n_self) : p.n_self);
   float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int j0 = 0; j0 < n_keys; j0 += 64) {
     const int j = j0 + lane;

@@ -276,9 +276,9 @@ __global__ __launch_bounds__(1024) void k_build_lists(int nb, int L, int B, cons
   int alive = 0, nrows = 0, b = -1;
   if (t < nb) {
     b = act_cur[t];
-    alive = !stop[b];
-    if (alive)
+    if (!stop[b])
       for (int i = 0; i < L; ++i) nrows += U[b * L + i];
+    alive = nrows > 0;  // a sequence with nothing unresolved runs no (further) loop
   }
   int nc = 0;
   for (int bb = t; bb < B; bb += 1024) nc += ncommit[bb];
@@ -481,6 +481,39 @@ __global__ void k_gather_rows(const int32_t* __restrict__ ro_rows, const int32_t
   if (rkey) rkey[k] = 64 * b + i;
 }
 
+// Outer loop over a block.  k_block_init: working ids = block ids, commit records cleared and
+// cnt[0] = masked positions (one block, fixed-order sum).
+__global__ __launch_bounds__(1024) void k_block_init(const int32_t* __restrict__ block_ids, int n, int mask_id,
+                                                     int32_t* __restrict__ ids, int16_t* __restrict__ commit_step,
+                                                     int8_t* __restrict__ commit_loop, int32_t* __restrict__ cnt) {
+  __shared__ float red[16];
+  int m = 0;
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    const int id = block_ids[i];
+    ids[i] = id;
+    commit_step[i] = 0;
+    commit_loop[i] = 0;
+    m += id == mask_id;
+  }
+  const float s = block_sum<1024>((float)m, red);
+  if (threadIdx.x == 0) cnt[0] = (int32_t)s;
+}
+
+// After step t of the outer loop: positions the step committed record (t, its commit loop); the
+// working ids become the step's output (committed tokens written in, mask_id where unresolved).
+__global__ void k_block_merge(int n, int t, const int32_t* __restrict__ step_tok, const int8_t* __restrict__ step_cl,
+                              int32_t* __restrict__ ids, int16_t* __restrict__ commit_step,
+                              int8_t* __restrict__ commit_loop) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int8_t cl = step_cl[i];
+  if (cl != 0) {
+    commit_step[i] = (int16_t)t;
+    commit_loop[i] = cl;
+  }
+  ids[i] = step_tok[i];
+}
+
 // embed_out[k] = committed(k) ? Emb[tokens[k]] : 0
 template <typename T>
 __global__ __launch_bounds__(256) void k_embed_committed(const int8_t* __restrict__ cl,
@@ -602,6 +635,16 @@ void launch_gather_rows(const int32_t* ro_rows, const int32_t* n_dev, const int3
   if (n_upper <= 0 || (!boost_tok && !rkey)) return;
   k_gather_rows<<<(n_upper + 255) / 256, 256, 0, st>>>(ro_rows, n_dev, act, n_upper, L, boost_tok, boost_val, btok,
                                                         bval, rkey);
+}
+
+void launch_block_init(const int32_t* block_ids, int n, int mask_id, int32_t* ids, int16_t* commit_step,
+                       int8_t* commit_loop, int32_t* cnt, hipStream_t st) {
+  k_block_init<<<1, 1024, 0, st>>>(block_ids, n, mask_id, ids, commit_step, commit_loop, cnt);
+}
+
+void launch_block_merge(int n, int t, const int32_t* step_tok, const int8_t* step_cl, int32_t* ids,
+                        int16_t* commit_step, int8_t* commit_loop, hipStream_t st) {
+  if (n > 0) k_block_merge<<<(n + 255) / 256, 256, 0, st>>>(n, t, step_tok, step_cl, ids, commit_step, commit_loop);
 }
 
 void launch_embed_committed(int dtype, const int8_t* cl, const int32_t* tokens, const void* E, int n, int d, int V,

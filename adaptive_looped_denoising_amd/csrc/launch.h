@@ -58,7 +58,9 @@ struct AttnParams {
   const void* sk = nullptr;
   const void* sv = nullptr;
   int64_t s_kSeq = 0, s_kHead = 0, s_kPos = 0, s_vSeq = 0, s_vHead = 0, s_vRow = 0;
-  int n_self = 0, causal = 0, s_seq0 = 0;
+  // causal: query row i sees own key jj iff jj <= i + causal_off (rows appended after
+  // causal_off own keys that are already in place)
+  int n_self = 0, causal = 0, s_seq0 = 0, causal_off = 0;
   // fast path scratch: split-KV partials
   float* part = nullptr;
   int n_split = 1;
@@ -108,6 +110,12 @@ void launch_dump_hidden(int nb, int L, int d, int B, int s, const int32_t* act, 
 void launch_gather_rows(const int32_t* ro_rows, const int32_t* n_dev, const int32_t* act, int n_upper, int L,
                         const int32_t* boost_tok, const float* boost_val, int32_t* btok, float* bval, int32_t* rkey,
                         hipStream_t st);
+// Outer loop over a block: init copies the block ids, clears the commit records and counts the
+// masked positions into cnt[0]; merge records step t's commits and takes its output ids.
+void launch_block_init(const int32_t* block_ids, int n, int mask_id, int32_t* ids, int16_t* commit_step,
+                       int8_t* commit_loop, int32_t* cnt, hipStream_t st);
+void launch_block_merge(int n, int t, const int32_t* step_tok, const int8_t* step_cl, int32_t* ids,
+                        int16_t* commit_step, int8_t* commit_loop, hipStream_t st);
 void launch_embed_committed(int dtype, const int8_t* cl, const int32_t* tokens, const void* E, int n, int d, int V,
                             float* out, hipStream_t st);
 
@@ -133,13 +141,15 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
 // with transposed, V-layout ([b][kvh][hd][P_pitch]).
 void launch_fill_kv_synth(int dtype, void* slot_base, int B, int Hkv, int P, int P_pitch, int hd, uint32_t seed,
                           uint32_t tensor, float scale, bool transposed, hipStream_t st);
-void launch_fill_u8(uint8_t* dst, size_t n, uint8_t v, hipStream_t st);
-void launch_copy_avail(uint8_t* dst, const uint8_t* src, size_t n, hipStream_t st);
+// Available-depth table [B][pitch]: positions j0 .. j0+n-1 of each sequence from src [B][n], or
+// the value v when src is null.
+void launch_set_avail(uint8_t* dst, int pitch, int j0, int B, int n, const uint8_t* src, uint8_t v, hipStream_t st);
 // Depth planes of one Core layer's cache (plane p = depth p + 1, plane_elems apart): for every
 // position j with avail[b][j] = a_j, plane p takes the values of plane max(1, min(p + 1, a_j)) - 1,
 // so that reading plane s - 1 at loop s gives every key at depth min(s, a_j).
 void launch_materialize_depth(int dtype, void* k_plane0, void* v_plane0, int64_t plane_elems, int k_max, int B,
-                              int Hkv, int P, int P_pitch, int hd, const uint8_t* avail, hipStream_t st);
+                              int Hkv, int j0, int n_pos, int P_pitch, int hd, const uint8_t* avail, int av_pitch,
+                              hipStream_t st);
 // V rows j0 .. j0+n-1 of a transposed cache slot, every kv head, to dst [Hkv][n][hd].
 void launch_read_v_rows(int dtype, const void* slot_base, int b, int Hkv, int P_pitch, int hd, int j0, int n,
                         void* dst, hipStream_t st);

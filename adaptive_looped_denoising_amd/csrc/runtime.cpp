@@ -28,6 +28,7 @@ struct Plan {
   size_t r, lam, H, lse, tok, btok, bval, part, gpart, rkey, stok;
   size_t U, a, ro_map, ro_rows, ncommit, stop, seq_loops, act_seq0, act_seq1, src_slot, cnt;
   size_t attn_part, gemm_part;
+  size_t blk_ids, blk_tok, blk_cl, blk_loops, blk_cnt;  // outer loop over a block
   // sizes
   // Cache slot: K [B][Hkv][Pp][hd], V transposed [B][Hkv][hd][Pp], Pp = max_prefix rounded up to
   // 64 (a 64-key tile never leaves a V row).  Own-block V likewise [B][Hkv][hd][Lp].
@@ -35,6 +36,7 @@ struct Plan {
   int64_t Pp = 0, Lp = 0;
   int n_slots = 0, rows_step = 0, rows_max = 0, prefill_rows = 0, n_vtiles = 0, max_pos = 0;
   int attn_splits = 0;
+  int av_pitch = 1;  // row pitch of the available-depth table [B][av_pitch]
   size_t gemm_part_elems = 0;
 };
 
@@ -96,7 +98,8 @@ Plan make_plan(const alodlm_config& c) {
   p.rope_sin = take(sizeof(float) * p.max_pos * (hd / 2));
   p.kcache = take(es * p.slot_elems * p.n_slots);
   p.vcache = take(es * p.slot_elems * p.n_slots);
-  p.avail = take(B * P);
+  p.av_pitch = P > 0 ? (int)P : 1;
+  p.avail = take(B * p.av_pitch);
   p.h = take(sizeof(float) * R * d);
   p.h_alt = take(sizeof(float) * R * d);
   p.xn = take(es * R * d);
@@ -132,6 +135,11 @@ Plan make_plan(const alodlm_config& c) {
   p.attn_part = take(sizeof(float) * Rs * Hq * (size_t)p.attn_splits * (hd + 2));
   p.gemm_part_elems = (size_t)Rs * (size_t)(2 * F > qkv_out ? 2 * F : qkv_out) * 8;
   p.gemm_part = take(sizeof(float) * p.gemm_part_elems);
+  p.blk_ids = take(sizeof(int32_t) * Rs);
+  p.blk_tok = take(sizeof(int32_t) * Rs);
+  p.blk_cl = take(Rs);
+  p.blk_loops = take(B);
+  p.blk_cnt = take(sizeof(int32_t) * 4);
   p.total = off;
   return p;
 }
@@ -340,15 +348,20 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   ap.scale = 1.0f / sqrtf((float)hd);
   const int64_t Pp = p.Pp, Lp = p.Lp;
   if (lc.mode == PREFILL) {
+    // rows are positions pos0 .. pos0 + rows_per_seq - 1 of each sequence: their post-RoPE K/V go
+    // into the slot right after the pos0 positions already there, and they attend causally to
+    // all of them (pos0 = 0 for a prefill from scratch, the cached length when a block is appended)
     const int slot = slot_of(g, li, lc.depth);
     void* kd = cache_slot(c, false, slot);
     void* vd = cache_slot(c, true, slot);
     const int64_t kSeq = (int64_t)Hkv * Pp * hd, kHead = Pp * hd, kPos = hd;
     const int64_t vSeq = (int64_t)Hkv * hd * Pp, vHead = hd * Pp, vRow = Pp;
+    const size_t es_ = esize(g.dtype);
     c->tic(ALODLM_K_NORM_ROPE);
-    launch_qk_norm_rope(dt(c), qkv_src, n, lc.rows_per_seq, 0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
-                        c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, kd, vd, kSeq, kHead, kPos, vSeq, vHead,
-                        vRow, lc.seq0, c->st, qkv_splits);
+    launch_qk_norm_rope(dt(c), qkv_src, n, lc.rows_per_seq, lc.pos0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
+                        c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q,
+                        (char*)kd + (size_t)lc.pos0 * kPos * es_, (char*)vd + (size_t)lc.pos0 * es_, kSeq, kHead,
+                        kPos, vSeq, vHead, vRow, lc.seq0, c->st, qkv_splits);
     c->toc();
     ap.n_cache = 0;
     ap.sk = kd;
@@ -360,8 +373,9 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
     ap.s_vHead = vHead;
     ap.s_vRow = vRow;
     ap.s_seq0 = lc.seq0;
-    ap.n_self = lc.rows_per_seq;
+    ap.n_self = lc.pos0 + lc.rows_per_seq;
     ap.causal = 1;
+    ap.causal_off = lc.pos0;
   } else {
     void* ks = c->at<void>(p.kself);
     void* vs = c->at<void>(p.vself);
@@ -576,14 +590,15 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
 }
 
 namespace {
-// Fill each Core layer's higher depth planes from its available depth (see launch_materialize_depth).
-void materialize_depths(alodlm_ctx* c, int batch, int prefix_len) {
+// Fill each Core layer's higher depth planes of positions j0 .. j0+n-1 from their available depth
+// (see launch_materialize_depth).
+void materialize_depths(alodlm_ctx* c, int batch, int j0, int n) {
   const alodlm_config& g = c->cfg;
   const Plan& p = c->plan;
   for (int ci = 0; ci < g.n_core; ++ci) {
     const int s0 = slot_of(g, g.n_pre + ci, 1);
     launch_materialize_depth(dt(c), cache_slot(c, false, s0), cache_slot(c, true, s0), p.slot_elems, g.k_max, batch,
-                             g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim, c->at<uint8_t>(p.avail), c->st);
+                             g.n_kv_heads, j0, n, (int)p.Pp, g.head_dim, c->at<uint8_t>(p.avail), p.av_pitch, c->st);
   }
 }
 }  // namespace
@@ -597,11 +612,7 @@ int alodlm_prefill_kv(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const in
   if (prefix_len > 0 && !prefix_ids) return c->fail(ALODLM_EINVAL, "null prefix_ids");
   const Plan& p = c->plan;
   c->cache_batch = -1;
-  const size_t nav = (size_t)batch * prefix_len;
-  if (avail_depth)
-    launch_copy_avail(c->at<uint8_t>(p.avail), avail_depth, nav, c->st);
-  else
-    launch_fill_u8(c->at<uint8_t>(p.avail), nav, (uint8_t)g.k_max, c->st);
+  launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, avail_depth, (uint8_t)g.k_max, c->st);
   if (prefix_len > 0) {
     const int per = p.prefill_rows / prefix_len;  // sequences per pass (>= 1: prefill_rows >= max_prefix)
     float* h = c->at<float>(p.h);
@@ -618,7 +629,7 @@ int alodlm_prefill_kv(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const in
       lc.depth = 1;
       for (int ci = 0; ci < g.n_coda; ++ci) run_layer(c, g.n_pre + g.n_core + ci, lc);
     }
-    materialize_depths(c, batch, prefix_len);
+    materialize_depths(c, batch, 0, prefix_len);
   }
   int rc = c->hip_check("prefill launch");
   if (rc) return rc;
@@ -636,22 +647,52 @@ int alodlm_prefill_kv_synthetic(alodlm_ctx* c, int32_t batch, int32_t prefix_len
   if (!finite_f(k_scale) || !finite_f(v_scale)) return c->fail(ALODLM_EINVAL, "non-finite scale");
   const Plan& p = c->plan;
   c->cache_batch = -1;
-  const size_t nav = (size_t)batch * prefix_len;
-  if (avail_depth)
-    launch_copy_avail(c->at<uint8_t>(p.avail), avail_depth, nav, c->st);
-  else
-    launch_fill_u8(c->at<uint8_t>(p.avail), nav, (uint8_t)g.k_max, c->st);
+  launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, avail_depth, (uint8_t)g.k_max, c->st);
   for (int s = 0; s < p.n_slots; ++s) {
     launch_fill_kv_synth(dt(c), cache_slot(c, false, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,
                          seed, 0x10000u + 2u * s, k_scale, false, c->st);
     launch_fill_kv_synth(dt(c), cache_slot(c, true, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,
                          seed, 0x10000u + 2u * s + 1u, v_scale, true, c->st);
   }
-  if (prefix_len > 0) materialize_depths(c, batch, prefix_len);
+  if (prefix_len > 0) materialize_depths(c, batch, 0, prefix_len);
   int rc = c->hip_check("synthetic prefill launch");
   if (rc) return rc;
   c->cache_batch = batch;
   c->cache_prefix = prefix_len;
+  return ALODLM_OK;
+}
+
+int alodlm_extend_kv(alodlm_ctx* c, int32_t batch, int32_t n_new, const int32_t* new_ids,
+                     const uint8_t* avail_new) {
+  if (!c) return ALODLM_EINVAL;
+  const alodlm_config& g = c->cfg;
+  if (c->cache_batch < 0) return c->fail(ALODLM_ESTATE, "extend before the prefix cache was built");
+  if (batch != c->cache_batch) return c->fail(ALODLM_EINVAL, "batch differs from the cached batch");
+  const int P0 = c->cache_prefix;
+  if (n_new < 1 || n_new > g.max_prefix - P0)
+    return c->fail(ALODLM_EINVAL, "n_new outside 1 .. max_prefix - cached length");
+  if (!new_ids) return c->fail(ALODLM_EINVAL, "null new_ids");
+  const Plan& p = c->plan;
+  const int per = p.prefill_rows / n_new;  // >= 1: prefill_rows >= max_prefix >= n_new
+  float* h = c->at<float>(p.h);
+  for (int b0 = 0; b0 < batch; b0 += per) {
+    const int gb = batch - b0 < per ? batch - b0 : per;
+    const int n = gb * n_new;
+    launch_embed_rows(dt(c), new_ids + (size_t)b0 * n_new, n, c->w.embed, g.d_model, g.vocab, h, c->st);
+    LayerCall lc{PREFILL, h, h, n, n_new, P0, nullptr, 1, b0, 1, P0 + n_new};
+    for (int li = 0; li < g.n_pre; ++li) run_layer(c, li, lc);
+    for (int dpt = 1; dpt <= g.k_max; ++dpt) {
+      lc.depth = dpt;
+      for (int ci = 0; ci < g.n_core; ++ci) run_layer(c, g.n_pre + ci, lc);
+    }
+    lc.depth = 1;
+    for (int ci = 0; ci < g.n_coda; ++ci) run_layer(c, g.n_pre + g.n_core + ci, lc);
+  }
+  launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, P0, batch, n_new, avail_new, (uint8_t)g.k_max, c->st);
+  if (avail_new) materialize_depths(c, batch, P0, n_new);
+  int rc = c->hip_check("extend launch");
+  if (rc) return rc;
+  c->cache_prefix = P0 + n_new;
   return ALODLM_OK;
 }
 
@@ -803,6 +844,60 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
   o->loops_run = loops_run;
   c->loops_run = loops_run;
   return ALODLM_OK;
+}
+
+int alodlm_denoise_block(alodlm_ctx* c, const alodlm_block_args* a, alodlm_block_out* o) {
+  if (!c) return ALODLM_EINVAL;
+  if (!a || !o) return c->fail(ALODLM_EINVAL, "null args or out");
+  if (!o->tokens || !o->commit_step || !o->commit_loop) return c->fail(ALODLM_EINVAL, "null output array");
+  const alodlm_config& g = c->cfg;
+  const Plan& p = c->plan;
+  const int B = a->step.batch, L = a->step.block_len;
+  if (a->step.flags & ALODLM_STEP_TEACHER_FORCED) return c->fail(ALODLM_EINVAL, "teacher forcing in the outer loop");
+  if (c->cache_batch < 0) return c->fail(ALODLM_ESTATE, "denoise_block before the prefix cache was built");
+  if (B != c->cache_batch) return c->fail(ALODLM_EINVAL, "batch differs from the prefilled batch");
+  if (L < 1 || L > g.max_block) return c->fail(ALODLM_EINVAL, "block_len outside 1..max_block");
+  if (!a->step.block_ids) return c->fail(ALODLM_EINVAL, "null block_ids");
+  if (a->max_steps < 0) return c->fail(ALODLM_EINVAL, "max_steps < 0");
+  const int max_steps = a->max_steps == 0 ? L : a->max_steps;
+  if (a->append && (max_steps < L || L > g.max_prefix - c->cache_prefix))
+    return c->fail(ALODLM_EINVAL, "append needs max_steps 0 or >= block_len and room for block_len positions");
+  hipStream_t st = c->st;
+  const int n = B * L;
+  int32_t* ids = c->at<int32_t>(p.blk_ids);
+  int32_t* cnt = c->at<int32_t>(p.blk_cnt);
+  launch_block_init(a->step.block_ids, n, g.mask_id, ids, o->commit_step, o->commit_loop, cnt, st);
+  int32_t masked = 0;
+  hipError_t e1 = hipMemcpyAsync(&masked, cnt, sizeof(masked), hipMemcpyDeviceToHost, st);
+  hipError_t e2 = hipStreamSynchronize(st);
+  if (e1 != hipSuccess || e2 != hipSuccess)
+    return c->fail(ALODLM_EHIP, std::string("mask count read: ") + hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+  int steps = 0, committed = 0;
+  while (masked - committed > 0 && steps < max_steps) {
+    ++steps;
+    alodlm_step_args sa = a->step;
+    sa.block_ids = ids;
+    sa.sample_step = a->step.sample_step + (uint32_t)(steps - 1);
+    alodlm_step_out so;
+    memset(&so, 0, sizeof(so));
+    so.tokens = c->at<int32_t>(p.blk_tok);
+    so.commit_loop = c->at<int8_t>(p.blk_cl);
+    so.loops = c->at<int8_t>(p.blk_loops);
+    int rc = alodlm_denoise_step(c, &sa, &so);
+    if (rc) return rc;
+    launch_block_merge(n, steps, so.tokens, so.commit_loop, ids, o->commit_step, o->commit_loop, st);
+    committed += so.n_committed;
+    if (so.n_committed < 1) return c->fail(ALODLM_ESTATE, "internal: an outer-loop step committed nothing");
+  }
+  if (hipMemcpyAsync(o->tokens, ids, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return c->fail(ALODLM_EHIP, "block tokens copy");
+  o->n_steps = steps;
+  o->n_committed = committed;
+  if (a->append) {
+    int rc = alodlm_extend_kv(c, B, L, ids, nullptr);
+    if (rc) return rc;
+  }
+  return c->hip_check("block launch");
 }
 
 int alodlm_readout_commit(alodlm_ctx* c, const void* rows, int32_t n_rows, int32_t group, float tau_ent,

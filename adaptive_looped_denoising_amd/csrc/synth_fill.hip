@@ -58,16 +58,17 @@ void launch_fill_kv_synth(int dtype, void* slot_base, int B, int Hkv, int P, int
 // value into every plane above the position's available depth.
 template <typename T>
 __global__ __launch_bounds__(256) void k_materialize_depth(T* __restrict__ k0, T* __restrict__ v0,
-                                                           int64_t plane_elems, int k_max, int B, int Hkv, int P,
-                                                           int P_pitch, int hd, const uint8_t* __restrict__ avail) {
-  const uint64_t n = (uint64_t)B * Hkv * P * hd;
+                                                           int64_t plane_elems, int k_max, int B, int Hkv, int j0,
+                                                           int n_pos, int P_pitch, int hd,
+                                                           const uint8_t* __restrict__ avail, int av_pitch) {
+  const uint64_t n = (uint64_t)B * Hkv * n_pos * hd;
   const uint64_t stride = (uint64_t)gridDim.x * 256;
   for (uint64_t k = (uint64_t)blockIdx.x * 256 + threadIdx.x; k < n; k += stride) {
     const uint64_t e = k % hd;
-    const uint64_t j = (k / hd) % P;
-    const uint64_t bh = k / ((uint64_t)hd * P);
+    const uint64_t j = j0 + (k / hd) % n_pos;
+    const uint64_t bh = k / ((uint64_t)hd * n_pos);
     const int b = (int)(bh / Hkv);
-    const int a = max(1, min(k_max, (int)avail[(size_t)b * P + j]));
+    const int a = max(1, min(k_max, (int)avail[(size_t)b * av_pitch + j]));
     if (a >= k_max) continue;
     const uint64_t ok = (bh * P_pitch + j) * hd + e;      // K layout
     const uint64_t ov = (bh * hd + e) * P_pitch + j;      // transposed V layout
@@ -81,16 +82,17 @@ __global__ __launch_bounds__(256) void k_materialize_depth(T* __restrict__ k0, T
 }
 
 void launch_materialize_depth(int dtype, void* k_plane0, void* v_plane0, int64_t plane_elems, int k_max, int B,
-                              int Hkv, int P, int P_pitch, int hd, const uint8_t* avail, hipStream_t st) {
-  const uint64_t n = (uint64_t)B * Hkv * P * hd;
+                              int Hkv, int j0, int n_pos, int P_pitch, int hd, const uint8_t* avail, int av_pitch,
+                              hipStream_t st) {
+  const uint64_t n = (uint64_t)B * Hkv * n_pos * hd;
   if (!n || k_max < 2) return;
   const unsigned grid = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
   if (dtype == DT_BF16)
     k_materialize_depth<bf16_t><<<grid, 256, 0, st>>>((bf16_t*)k_plane0, (bf16_t*)v_plane0, plane_elems, k_max, B,
-                                                      Hkv, P, P_pitch, hd, avail);
+                                                      Hkv, j0, n_pos, P_pitch, hd, avail, av_pitch);
   else
     k_materialize_depth<float><<<grid, 256, 0, st>>>((float*)k_plane0, (float*)v_plane0, plane_elems, k_max, B, Hkv,
-                                                     P, P_pitch, hd, avail);
+                                                     j0, n_pos, P_pitch, hd, avail, av_pitch);
 }
 
 template <typename T>
@@ -120,15 +122,16 @@ __global__ void k_fill_u8(uint8_t* dst, size_t n, uint8_t v) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) dst[i] = v;
 }
-__global__ void k_copy_u8(uint8_t* dst, const uint8_t* src, size_t n) {
+// dst[b * pitch + j0 + j] = src ? src[b * n + j] : v for b < B, j < n
+__global__ void k_set_avail(uint8_t* dst, int pitch, int j0, int B, int n, const uint8_t* src, uint8_t v) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) dst[i] = src[i];
+  if (i >= (size_t)B * n) return;
+  const size_t b = i / n, j = i % n;
+  dst[b * pitch + j0 + j] = src ? src[i] : v;
 }
-void launch_fill_u8(uint8_t* dst, size_t n, uint8_t v, hipStream_t st) {
-  if (n) k_fill_u8<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(dst, n, v);
-}
-void launch_copy_avail(uint8_t* dst, const uint8_t* src, size_t n, hipStream_t st) {
-  if (n) k_copy_u8<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(dst, src, n);
+void launch_set_avail(uint8_t* dst, int pitch, int j0, int B, int n, const uint8_t* src, uint8_t v, hipStream_t st) {
+  const size_t total = (size_t)B * n;
+  if (total) k_set_avail<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(dst, pitch, j0, B, n, src, v);
 }
 
 }  // namespace alodlm

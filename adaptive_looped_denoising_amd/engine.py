@@ -48,7 +48,9 @@ class StepResult:
 class Engine:
     def __init__(self, w: synth.Workload, device: str = "cuda", weight_source: Optional[str] = None,
                  max_prefill_rows: Optional[int] = None, overrides: Optional[Dict[str, np.ndarray]] = None,
-                 exit_b: Optional[float] = None):
+                 exit_b: Optional[float] = None, max_prefix: Optional[int] = None):
+        """``max_prefix``: cache capacity per sequence (default the workload's prefix; larger to
+        append blocks)."""
         self.lib = B.load()
         self.w = w
         self.device = torch.device(device)
@@ -79,7 +81,7 @@ class Engine:
         self.cfg = B.Config(
             vocab=D.vocab, d_model=D.d_model, n_q_heads=D.n_q_heads, n_kv_heads=D.n_kv_heads, head_dim=D.head_dim,
             ffn=D.ffn, n_pre=D.n_pre, n_core=D.n_core, n_coda=D.n_coda, k_max=w.k_max, max_batch=w.batch,
-            max_prefix=w.prefix, max_block=w.block,
+            max_prefix=max(w.prefix, max_prefix or 0), max_block=w.block,
             max_prefill_rows=max_prefill_rows if max_prefill_rows is not None else min(
                 w.batch * w.prefix, max(w.prefix, 8192)),
             mask_id=w.mask_id, dtype=self.cdtype, rms_eps=w.rms_eps, rope_theta=w.rope_theta)
@@ -195,6 +197,36 @@ class Engine:
                 setattr(res, k, t.cpu().numpy())
         if self._hidden is not None:
             res.hidden = self._hidden.cpu().numpy()
+        return res
+
+    # ------------------------------------------------------------------ outer loop, cache growth
+    def extend(self, new_ids: np.ndarray, avail: Optional[np.ndarray] = None):
+        """Appends positions (ids [batch][n]) to every sequence's prefix cache."""
+        ids = torch.from_numpy(np.ascontiguousarray(new_ids, dtype=np.int32)).to(self.device)
+        av = None if avail is None else torch.from_numpy(np.ascontiguousarray(avail, dtype=np.uint8)).to(self.device)
+        B.extend_kv(self.ctx, ids.shape[0], ids.shape[1], ids.data_ptr(), _ptr(av))
+        torch.cuda.synchronize(self.device)
+
+    def make_block(self, tau_ent=None, tau_halt=None, k_loops=None, boost=True, block_ids=None, sample=None,
+                   max_steps=0, append=False):
+        w = self.w
+        step = self.make_args(tau_ent, tau_halt, k_loops, boost, None, block_ids, sample)
+        args = B.BlockArgs(step=step, max_steps=max_steps, append=1 if append else 0)
+        self._blk = dict(tokens=torch.empty((w.batch, w.block), dtype=torch.int32, device=self.device),
+                         commit_step=torch.empty((w.batch, w.block), dtype=torch.int16, device=self.device),
+                         commit_loop=torch.empty((w.batch, w.block), dtype=torch.int8, device=self.device))
+        out = B.BlockOut(tokens=self._blk["tokens"].data_ptr(), commit_step=self._blk["commit_step"].data_ptr(),
+                         commit_loop=self._blk["commit_loop"].data_ptr())
+        return args, out
+
+    def denoise_block(self, **kw) -> dict:
+        """Outer loop: steps until no mask in the block (``sample`` = {"seed", "step"}: first step's
+        counter); returns final tokens, per-position commit step and loop, steps and commits."""
+        args, out = self.make_block(**kw)
+        B.denoise_block(self.ctx, args, out)
+        torch.cuda.synchronize(self.device)
+        res = {k: v.cpu().numpy() for k, v in self._blk.items()}
+        res.update(n_steps=out.n_steps, n_committed=out.n_committed)
         return res
 
     def read_kv(self, slot: int, b: int, j0: int, n: int):

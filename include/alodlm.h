@@ -191,6 +191,47 @@ typedef struct alodlm_step_out {
  * finished.  Idempotent: it never writes the prefix cache. */
 ALODLM_API int alodlm_denoise_step(alodlm_ctx* ctx, const alodlm_step_args* args, alodlm_step_out* out);
 
+/* Appends n_new positions to every sequence's prefix cache: a finished block joins the prefix
+ * (same page, section "Method step details", Algorithm 1 step 5: committed tokens are written
+ * into the sequence before the next denoising step).  The new positions run through the stack the
+ * way alodlm_prefill_kv builds the cache -- Prelude once, the Core once per depth 1..k_max, the
+ * Coda once on the depth-k_max output -- causally among themselves and attending to every cached
+ * position as a step reads it (Core depth min(d, available depth)).  With every cached position at
+ * full depth the cache equals the prefill of the longer prefix.
+ *   new_ids:   device int32 [batch][n_new], ids in [0, V)
+ *   avail_new: device uint8 [batch][n_new], deepest Core depth kept for the new positions, or
+ *              NULL (k_max).
+ * batch == the cached batch; 1 <= n_new and cached length + n_new <= max_prefix, else EINVAL;
+ * before any prefill, ESTATE.  Asynchronous. */
+ALODLM_API int alodlm_extend_kv(alodlm_ctx* ctx, int32_t batch, int32_t n_new, const int32_t* new_ids,
+                                const uint8_t* avail_new);
+
+/* Outer loop of Algorithm 1 over one block (same page, section "Method step details", steps 1
+ * and 5): denoising steps until no position of the block is masked, each step starting from the
+ * block with the previous steps' committed tokens written in.  Every step commits at least one
+ * token of every sequence that still has a masked position (forced progress) and a sequence
+ * with none runs no loop, so a block of L positions takes at most L steps. */
+typedef struct alodlm_block_args {
+  alodlm_step_args step;  /* the first step's arguments: block_ids = the starting block; TEACHER_FORCED is
+                             not allowed; with ALODLM_STEP_SAMPLE, step t (1-based) uses
+                             sample_step + t - 1 */
+  int32_t max_steps;      /* cap on steps, >= 0; 0 = block_len (always enough to finish) */
+  int32_t append;         /* != 0: append the finished block to the cache (alodlm_extend_kv); needs
+                             max_steps 0 or >= block_len and room for block_len more positions */
+} alodlm_block_args;
+
+typedef struct alodlm_block_out {
+  int32_t* tokens;        /* device [batch][L]: final ids (mask_id where still masked) */
+  int16_t* commit_step;   /* device [batch][L]: step (1-based) that committed the position, 0 if none */
+  int8_t* commit_loop;    /* device [batch][L]: that commit's loop within its step (s, or -s forced) */
+  int32_t n_steps;        /* host: steps run */
+  int32_t n_committed;    /* host: tokens committed over all steps */
+} alodlm_block_out;
+
+/* Runs the outer loop; reads the step's commit count back once per step (alodlm_denoise_step
+ * already synchronises per loop).  Returns after the last step (and the append) is enqueued. */
+ALODLM_API int alodlm_denoise_block(alodlm_ctx* ctx, const alodlm_block_args* args, alodlm_block_out* out);
+
 /* The readout half of a loop on given readout states: LMHead entropy/argmax,
  * ExitGate and cumulative halt (a = lambda at loop 1), entropy commit, forced
  * progress and the Eq. 3 embedding rows, for n_rows rows grouped into sequences of
