@@ -125,7 +125,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     progress("workload %s: building engine (device-filled weights)" % w.name)
-    e = Engine(w)
+    e = Engine(w, max_prefix=w.prefix + w.block)   # room to append the decoded block at the end
     torch.cuda.synchronize()
     progress("prefill")
     t0 = time.perf_counter()
@@ -184,6 +184,21 @@ def main():
                    lm_head_ms_per_step=skt["lm_head"][0] / args.steps,
                    lm_head_ms_per_step_greedy=kt["lm_head"][0] / args.steps,
                    timing_pass_ms_per_step=samp_prof["ms_per_step"])
+    # Outer loop: the whole block decoded (steps until no [MASK]), then appended to the cache
+    # (the cache grows by one block, so this runs last).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    blk = e.denoise_block(tau_ent=w.tau_ent)
+    blk_s = time.perf_counter() - t0
+    masked = int((synth.block_ids(w) == w.mask_id).sum())
+    t0 = time.perf_counter()
+    e.extend(blk["tokens"])
+    ext_s = time.perf_counter() - t0
+    outer = dict(masked_tokens=masked, committed=blk["n_committed"], steps=blk["n_steps"], ms=blk_s * 1e3,
+                 tok_s=blk["n_committed"] / blk_s, append_ms=ext_s * 1e3,
+                 append_rows_per_s=w.batch * w.block / ext_s,
+                 append_layer_calls=D.n_pre + w.k_max * D.n_core + D.n_coda)
+    progress("outer loop: %s" % outer)
     kernels = {}
     for k, v in kt.items():
         ms = v[0] / args.steps
@@ -220,6 +235,7 @@ def main():
                                                            per_launch_ms * 1e3, traffic / 1e6)},
         "tau_sweep": sweep,
         "sampled_commits": sampled,
+        "outer_loop": outer,
         "prefill_ms": prefill_ms,
         # per class: event-timed ms (the event pairs add a little time to short kernels, so the
         # fractions are lower bounds) with algorithmic bytes / flops and their roofline fractions
