@@ -59,6 +59,12 @@ follow them):
     each step starting from the Prelude of the block with every committed
     token written in; denoising step t (1-based) of a block draws its samples
     with counter word 3 = step0 + t - 1;
+  * depth-on-demand prefill (the "Limitations" section's remedy for the
+    first-token latency): the prefix is first built to a depth D0 < K, the
+    Coda set on the depth-D0 output, every position available at depth D0;
+    deepening continues the Core passes from the saved depth-D0 output and
+    rebuilds the Coda set on the deeper output (so the result equals a
+    prefill built to that depth directly);
   * a finished block joins the depth-aware cache the way the prefill builds
     it: its positions go through the Prelude once, the Core once per depth
     d = 1..k_max and the Coda once on the depth-k_max output, causally among
@@ -205,12 +211,18 @@ def kv_slot(dims, k_max: int, layer: int, depth: int = 1) -> int:
 
 
 def prefill_sequence(ids, W, dims, k_max: int, eps: float, theta: float, progress=None,
-                     prec=None) -> Dict[int, tuple]:
+                     prec=None, depth: Optional[int] = None, state: bool = False):
     """Depth-aware cache of one prefix: slot -> (K, V) [Hkv][P][hd] (causal prefix).
-    ``progress`` (optional) is called with a short text after every layer call."""
+    ``progress`` (optional) is called with a short text after every layer call.
+
+    ``depth`` (default k_max): build the Core only to this depth, the Coda set on the
+    depth-``depth`` output (depth-on-demand prefill; every position's available depth is then
+    ``depth``).  ``state``: also return the prefix's Core output at that depth, from which
+    deepen_sequence continues."""
     ids = np.asarray(ids)
     P = ids.shape[0]
     pos = np.arange(P)
+    depth = k_max if depth is None else depth
     cache = {}
     x = _f64(W["embed"][ids])
 
@@ -223,13 +235,36 @@ def prefill_sequence(ids, W, dims, k_max: int, eps: float, theta: float, progres
 
     for li in range(dims.n_pre):
         run(li, kv_slot(dims, k_max, li))
-    for depth in range(1, k_max + 1):
+    for dpt in range(1, depth + 1):
         for c in range(dims.n_core):
-            run(dims.n_pre + c, kv_slot(dims, k_max, dims.n_pre + c, depth))
+            run(dims.n_pre + c, kv_slot(dims, k_max, dims.n_pre + c, dpt))
+    core_out = x
     for c in range(dims.n_coda):
         li = dims.n_pre + dims.n_core + c
         run(li, kv_slot(dims, k_max, li))
-    return cache
+    return (cache, core_out) if state else cache
+
+
+def deepen_sequence(cache, core_out, W, dims, k_max: int, eps: float, theta: float, depth_from: int,
+                    depth_to: int, prec=None):
+    """Depth-on-demand: continue a prefix built to ``depth_from`` (its Core output ``core_out``)
+    with the Core passes depth_from+1 .. depth_to, then rebuild the Coda set on the deeper output.
+    Returns the deeper cache and Core output; equals the prefill built to ``depth_to`` directly."""
+    P = core_out.shape[0]
+    pos = np.arange(P)
+    out = dict(cache)
+    x = _f64(core_out)
+    for dpt in range(depth_from + 1, depth_to + 1):
+        for c in range(dims.n_core):
+            li = dims.n_pre + c
+            x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True, prec=prec)
+            out[kv_slot(dims, k_max, li, dpt)] = (k, v)
+    core = x
+    for c in range(dims.n_coda):
+        li = dims.n_pre + dims.n_core + c
+        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True, prec=prec)
+        out[kv_slot(dims, k_max, li)] = (k, v)
+    return out, core
 
 
 def context_for(cache, dims, k_max: int, layer: int, loop: int, avail):

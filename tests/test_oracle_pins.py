@@ -643,3 +643,30 @@ def test_no_mask_no_loop_and_sampled_steps_advance_the_counter():
     ids1 = np.asarray(blk["results"][0]["tokens"])
     again = run.step(w, block_ids=ids1[None, :], sample=dict(seed=9, step=6))[0]
     assert np.array_equal(again["tokens"], blk["results"][1]["tokens"])
+
+
+def test_depth_on_demand_prefill_then_deepen_equals_full_prefill():
+    """Building depth 1 first and deepening later gives the full-depth cache; before deepening,
+    a step reads the deeper Core planes at depth 1."""
+    w = _tiny()
+    W = _rand_weights(w, seed=3)
+    D = w.dims
+    ids = np.random.default_rng(7).integers(0, D.vocab, size=18)
+    args = (W, D, w.k_max, w.rms_eps, w.rope_theta)
+    full = orc.prefill_sequence(ids, *args)
+    c1, s1 = orc.prefill_sequence(ids, *args, depth=1, state=True)
+    assert sorted(c1) == sorted(set(range(D.n_pre)) | {orc.kv_slot(D, w.k_max, D.n_pre + c, 1) for c in range(D.n_core)}
+                                | {orc.kv_slot(D, w.k_max, D.n_pre + D.n_core + c) for c in range(D.n_coda)})
+    c2, s2 = orc.deepen_sequence(c1, s1, *args, depth_from=1, depth_to=2)
+    c4, _ = orc.deepen_sequence(c2, s2, *args, depth_from=2, depth_to=w.k_max)
+    assert sorted(c4) == sorted(full)
+    for slot in full:
+        for a, b in zip(c4[slot], full[slot]):
+            np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
+    c2d = orc.prefill_sequence(ids, *args, depth=2)
+    for slot in c2d:
+        for a, b in zip(c2[slot], c2d[slot]):
+            np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
+    # the Coda set of a shallow build comes from the shallow output
+    coda = orc.kv_slot(D, w.k_max, D.n_pre + D.n_core)
+    assert not np.allclose(c1[coda][0], full[coda][0])
