@@ -19,7 +19,7 @@ STEP_TEACHER_FORCED, STEP_SAMPLE = 1, 2
 DIAG_STORE, DIAG_RESID, DIAG_SOFTSTAT, DIAG_SWIGLU = 0, 1, 2, 3
 
 EXPORTS = ("alodlm_workspace_bytes", "alodlm_kv_slots", "alodlm_create", "alodlm_prefill_kv",
-           "alodlm_prefill_kv_synthetic", "alodlm_extend_kv", "alodlm_denoise_step", "alodlm_denoise_block",
+           "alodlm_prefill_kv_synthetic", "alodlm_prefill_kv_depth", "alodlm_deepen_kv", "alodlm_extend_kv", "alodlm_denoise_step", "alodlm_denoise_block",
            "alodlm_readout_commit",
            "alodlm_last_step_stats", "alodlm_last_error", "alodlm_destroy", "alodlm_synth_fill",
            "alodlm_diag_gemm", "alodlm_diag_timing_enable", "alodlm_diag_timing_read", "alodlm_diag_read_kv", "alodlm_diag_buffer_offset",
@@ -31,7 +31,7 @@ class Config(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "vocab", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "n_pre", "n_core", "n_coda", "k_max",
         "max_batch", "max_prefix", "max_block", "max_prefill_rows", "mask_id", "dtype")] + \
-        [("rms_eps", c_float), ("rope_theta", c_float)]
+        [("rms_eps", c_float), ("rope_theta", c_float), ("depth_on_demand", c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -91,6 +91,8 @@ def load(path: str = LIB_PATH):
     lib.alodlm_prefill_kv_synthetic.argtypes = [c_void_p, c_int32, c_int32, c_uint32, c_float, c_float, c_void_p]
     lib.alodlm_denoise_step.argtypes = [c_void_p, P(StepArgs), P(StepOut)]
     lib.alodlm_extend_kv.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p]
+    lib.alodlm_prefill_kv_depth.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_int32]
+    lib.alodlm_deepen_kv.argtypes = [c_void_p, c_int32]
     lib.alodlm_denoise_block.argtypes = [c_void_p, P(BlockArgs), P(BlockOut)]
     lib.alodlm_readout_commit.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_float, c_float, c_void_p,
                                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -157,6 +159,15 @@ def prefill_kv_synthetic(ctx: int, batch: int, prefix_len: int, seed: int, k_sca
 
 def denoise_step(ctx: int, args: StepArgs, out: StepOut):
     _check(load().alodlm_denoise_step(c_void_p(ctx), ctypes.byref(args), ctypes.byref(out)), c_void_p(ctx))
+
+
+def prefill_kv_depth(ctx: int, batch: int, prefix_len: int, prefix_ids_ptr: int, depth: int):
+    _check(load().alodlm_prefill_kv_depth(c_void_p(ctx), batch, prefix_len, c_void_p(prefix_ids_ptr), depth),
+           c_void_p(ctx))
+
+
+def deepen_kv(ctx: int, depth: int):
+    _check(load().alodlm_deepen_kv(c_void_p(ctx), depth), c_void_p(ctx))
 
 
 def extend_kv(ctx: int, batch: int, n_new: int, new_ids_ptr: int, avail_ptr: int = 0):

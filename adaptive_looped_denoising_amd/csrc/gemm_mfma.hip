@@ -1019,8 +1019,8 @@ constexpr int kNumTiles = 56;
 bool swiglu_single_pass_ok(int tile) { return ((kTiles[tile].bn / kTiles[tile].wn / 16) & 1) == 0; }
 
 // Measured choices (MI355X, bf16, K = 2048..12288): rows up to 48 stream the weights with the
-// 32-row pipelined tile; 49..384 rows mostly use the eight-wave tiles (two waves per SIMD hide
-// each other's LDS and barrier waits); more rows use the large tiles.
+// 32-row pipelined tile; more rows use the eight-wave tiles (two waves per SIMD hide each other's
+// LDS and barrier waits), with split-K up to 384 rows.
 // Returns the tile; *splits gets the split-K factor (0 = the generic rule).
 int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   *splits = 0;
@@ -1042,9 +1042,15 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
     if (M <= 128) return (M <= 64 || N <= 4096) ? 45 : 18;
     return (N > 4096 && K <= N) ? 36 : 38;
   }
+  // more rows (long-context steps, prefill): single pass over the eight-wave tiles, measured at
+  // 512 / 1024 / 2048 / 8192 rows on the 8B projections
   *splits = 1;
-  if (epi == EPI_STORE && N <= 8192) return 16;
-  return 17;
+  if (epi == EPI_SOFTSTAT) return 17;
+  if (M >= 4096) return 44;
+  if (M >= 1536) return epi == EPI_STORE ? 47 : 37;
+  if (epi == EPI_SWIGLU) return M >= 768 ? 44 : 47;
+  if (epi == EPI_STORE) return M >= 768 ? 47 : 38;
+  return 38;
 }
 
 int gemm_mfma_softstat_bn(int M) {

@@ -29,6 +29,7 @@ struct Plan {
   size_t U, a, ro_map, ro_rows, ncommit, stop, seq_loops, act_seq0, act_seq1, src_slot, cnt;
   size_t attn_part, gemm_part;
   size_t blk_ids, blk_tok, blk_cl, blk_loops, blk_cnt;  // outer loop over a block
+  size_t pstate;  // depth-on-demand: the prefix's Core output [B][P][d] fp32 (0 bytes without it)
   // sizes
   // Cache slot: K [B][Hkv][Pp][hd], V transposed [B][Hkv][hd][Pp], Pp = max_prefix rounded up to
   // 64 (a 64-key tile never leaves a V row).  Own-block V likewise [B][Hkv][hd][Lp].
@@ -68,6 +69,7 @@ int check_config(const alodlm_config* c, std::string* err) {
   if (c->mask_id < 0 || c->mask_id >= c->vocab) return bad("mask_id outside [0, vocab)");
   if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps)) return bad("rms_eps");
   if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return bad("rope_theta");
+  if (c->depth_on_demand != 0 && c->depth_on_demand != 1) return bad("depth_on_demand must be 0 or 1");
   return ALODLM_OK;
 }
 
@@ -140,6 +142,7 @@ Plan make_plan(const alodlm_config& c) {
   p.blk_cl = take(Rs);
   p.blk_loops = take(B);
   p.blk_cnt = take(sizeof(int32_t) * 4);
+  p.pstate = take(c.depth_on_demand ? sizeof(float) * B * P * d : 0);
   p.total = off;
   return p;
 }
@@ -157,6 +160,8 @@ struct alodlm_ctx {
   std::string err;
   // prefix cache state
   int cache_batch = -1, cache_prefix = -1;
+  int built_depth = -1;  // depth-on-demand: Core depth the prefix state holds (-1: no state)
+  int state_prefix = -1; // prefix length the saved state covers
   // stats of the last step
   int64_t layer_calls = 0;
   int32_t loops_run = 0;
@@ -603,38 +608,111 @@ void materialize_depths(alodlm_ctx* c, int batch, int j0, int n) {
 }
 }  // namespace
 
-int alodlm_prefill_kv(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const int32_t* prefix_ids,
-                      const uint8_t* avail_depth) {
-  if (!c) return ALODLM_EINVAL;
+namespace {
+// Prefill passes over the prefix of every sequence, in groups of sequences that fit the prefill
+// rows: Prelude, Core depths 1..depth (each pass writing its depth slot), Coda on the
+// depth-`depth` output.  With `save`, the Core output at that depth is kept in the prefill
+// state buffer (depth-on-demand).
+void prefill_passes(alodlm_ctx* c, int batch, int prefix_len, const int32_t* prefix_ids, int depth, bool save) {
+  const alodlm_config& g = c->cfg;
+  const Plan& p = c->plan;
+  const int per = p.prefill_rows / prefix_len;  // sequences per pass (>= 1: prefill_rows >= max_prefix)
+  float* h = c->at<float>(p.h);
+  for (int b0 = 0; b0 < batch; b0 += per) {
+    const int gb = batch - b0 < per ? batch - b0 : per;
+    const int n = gb * prefix_len;
+    launch_embed_rows(dt(c), prefix_ids + (size_t)b0 * prefix_len, n, c->w.embed, g.d_model, g.vocab, h, c->st);
+    LayerCall lc{PREFILL, h, h, n, prefix_len, 0, nullptr, 1, b0, 1, prefix_len};
+    for (int li = 0; li < g.n_pre; ++li) run_layer(c, li, lc);
+    for (int dpt = 1; dpt <= depth; ++dpt) {
+      lc.depth = dpt;
+      for (int ci = 0; ci < g.n_core; ++ci) run_layer(c, g.n_pre + ci, lc);
+    }
+    if (save)
+      hipMemcpyAsync(c->at<float>(p.pstate) + (size_t)b0 * prefix_len * g.d_model, h,
+                     sizeof(float) * (size_t)n * g.d_model, hipMemcpyDeviceToDevice, c->st);
+    lc.depth = 1;
+    for (int ci = 0; ci < g.n_coda; ++ci) run_layer(c, g.n_pre + g.n_core + ci, lc);
+  }
+}
+
+int prefill_common(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const int32_t* prefix_ids,
+                   const uint8_t* avail_depth, int depth) {
   const alodlm_config& g = c->cfg;
   if (batch < 1 || batch > g.max_batch) return c->fail(ALODLM_EINVAL, "batch outside 1..max_batch");
   if (prefix_len < 0 || prefix_len > g.max_prefix) return c->fail(ALODLM_EINVAL, "prefix_len outside 0..max_prefix");
   if (prefix_len > 0 && !prefix_ids) return c->fail(ALODLM_EINVAL, "null prefix_ids");
   const Plan& p = c->plan;
   c->cache_batch = -1;
-  launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, avail_depth, (uint8_t)g.k_max, c->st);
+  c->built_depth = -1;
+  if (depth == g.k_max)
+    launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, avail_depth, (uint8_t)g.k_max, c->st);
+  else
+    launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, nullptr, (uint8_t)depth, c->st);
+  const bool save = g.depth_on_demand != 0;
   if (prefix_len > 0) {
-    const int per = p.prefill_rows / prefix_len;  // sequences per pass (>= 1: prefill_rows >= max_prefix)
-    float* h = c->at<float>(p.h);
-    for (int b0 = 0; b0 < batch; b0 += per) {
-      const int gb = batch - b0 < per ? batch - b0 : per;
-      const int n = gb * prefix_len;
-      launch_embed_rows(dt(c), prefix_ids + (size_t)b0 * prefix_len, n, c->w.embed, g.d_model, g.vocab, h, c->st);
-      LayerCall lc{PREFILL, h, h, n, prefix_len, 0, nullptr, 1, b0, 1, prefix_len};
-      for (int li = 0; li < g.n_pre; ++li) run_layer(c, li, lc);
-      for (int dpt = 1; dpt <= g.k_max; ++dpt) {
-        lc.depth = dpt;
-        for (int ci = 0; ci < g.n_core; ++ci) run_layer(c, g.n_pre + ci, lc);
-      }
-      lc.depth = 1;
-      for (int ci = 0; ci < g.n_coda; ++ci) run_layer(c, g.n_pre + g.n_core + ci, lc);
-    }
+    prefill_passes(c, batch, prefix_len, prefix_ids, depth, save);
     materialize_depths(c, batch, 0, prefix_len);
   }
   int rc = c->hip_check("prefill launch");
   if (rc) return rc;
   c->cache_batch = batch;
   c->cache_prefix = prefix_len;
+  if (save) {
+    c->built_depth = depth;
+    c->state_prefix = prefix_len;
+  }
+  return ALODLM_OK;
+}
+}  // namespace
+
+int alodlm_prefill_kv(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const int32_t* prefix_ids,
+                      const uint8_t* avail_depth) {
+  if (!c) return ALODLM_EINVAL;
+  return prefill_common(c, batch, prefix_len, prefix_ids, avail_depth, c->cfg.k_max);
+}
+
+int alodlm_prefill_kv_depth(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const int32_t* prefix_ids,
+                            int32_t depth) {
+  if (!c) return ALODLM_EINVAL;
+  if (!c->cfg.depth_on_demand) return c->fail(ALODLM_EINVAL, "config without depth_on_demand");
+  if (depth < 1 || depth > c->cfg.k_max) return c->fail(ALODLM_EINVAL, "depth outside 1..k_max");
+  return prefill_common(c, batch, prefix_len, prefix_ids, nullptr, depth);
+}
+
+int alodlm_deepen_kv(alodlm_ctx* c, int32_t depth) {
+  if (!c) return ALODLM_EINVAL;
+  const alodlm_config& g = c->cfg;
+  if (!g.depth_on_demand) return c->fail(ALODLM_EINVAL, "config without depth_on_demand");
+  if (c->cache_batch < 0 || c->built_depth < 1 || c->cache_prefix != c->state_prefix)
+    return c->fail(ALODLM_ESTATE, "deepen needs a cache built by alodlm_prefill_kv_depth and not grown since");
+  if (depth <= c->built_depth || depth > g.k_max)
+    return c->fail(ALODLM_EINVAL, "depth must exceed the built depth and be at most k_max");
+  const Plan& p = c->plan;
+  const int batch = c->cache_batch, P = c->cache_prefix, d0 = c->built_depth;
+  if (P > 0) {
+    const int per = p.prefill_rows / P;
+    float* h = c->at<float>(p.h);
+    for (int b0 = 0; b0 < batch; b0 += per) {
+      const int gb = batch - b0 < per ? batch - b0 : per;
+      const int n = gb * P;
+      float* st_rows = c->at<float>(p.pstate) + (size_t)b0 * P * g.d_model;
+      hipMemcpyAsync(h, st_rows, sizeof(float) * (size_t)n * g.d_model, hipMemcpyDeviceToDevice, c->st);
+      LayerCall lc{PREFILL, h, h, n, P, 0, nullptr, 1, b0, 1, P};
+      for (int dpt = d0 + 1; dpt <= depth; ++dpt) {
+        lc.depth = dpt;
+        for (int ci = 0; ci < g.n_core; ++ci) run_layer(c, g.n_pre + ci, lc);
+      }
+      hipMemcpyAsync(st_rows, h, sizeof(float) * (size_t)n * g.d_model, hipMemcpyDeviceToDevice, c->st);
+      lc.depth = 1;
+      for (int ci = 0; ci < g.n_coda; ++ci) run_layer(c, g.n_pre + g.n_core + ci, lc);
+    }
+    launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, P, nullptr, (uint8_t)depth, c->st);
+    materialize_depths(c, batch, 0, P);
+  }
+  int rc = c->hip_check("deepen launch");
+  if (rc) return rc;
+  c->built_depth = depth;
   return ALODLM_OK;
 }
 
@@ -647,6 +725,7 @@ int alodlm_prefill_kv_synthetic(alodlm_ctx* c, int32_t batch, int32_t prefix_len
   if (!finite_f(k_scale) || !finite_f(v_scale)) return c->fail(ALODLM_EINVAL, "non-finite scale");
   const Plan& p = c->plan;
   c->cache_batch = -1;
+  c->built_depth = -1;
   launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, avail_depth, (uint8_t)g.k_max, c->st);
   for (int s = 0; s < p.n_slots; ++s) {
     launch_fill_kv_synth(dt(c), cache_slot(c, false, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,

@@ -48,9 +48,9 @@ class StepResult:
 class Engine:
     def __init__(self, w: synth.Workload, device: str = "cuda", weight_source: Optional[str] = None,
                  max_prefill_rows: Optional[int] = None, overrides: Optional[Dict[str, np.ndarray]] = None,
-                 exit_b: Optional[float] = None, max_prefix: Optional[int] = None):
+                 exit_b: Optional[float] = None, max_prefix: Optional[int] = None, depth_on_demand: bool = False):
         """``max_prefix``: cache capacity per sequence (default the workload's prefix; larger to
-        append blocks)."""
+        append blocks).  ``depth_on_demand``: keep the prefix state for depth-by-depth builds."""
         self.lib = B.load()
         self.w = w
         self.device = torch.device(device)
@@ -84,7 +84,8 @@ class Engine:
             max_prefix=max(w.prefix, max_prefix or 0), max_block=w.block,
             max_prefill_rows=max_prefill_rows if max_prefill_rows is not None else min(
                 w.batch * w.prefix, max(w.prefix, 8192)),
-            mask_id=w.mask_id, dtype=self.cdtype, rms_eps=w.rms_eps, rope_theta=w.rope_theta)
+            mask_id=w.mask_id, dtype=self.cdtype, rms_eps=w.rms_eps, rope_theta=w.rope_theta,
+            depth_on_demand=1 if depth_on_demand else 0)
         nl = D.n_layers
         self.layer_arr = (B.LayerWeights * max(nl, 1))()
         for l in range(nl):
@@ -115,10 +116,15 @@ class Engine:
         self.out_loops = torch.empty((Bn,), dtype=torch.int8, device=self.device)
 
     # ------------------------------------------------------------------ prefix cache
-    def prefill(self, prefix_ids: Optional[np.ndarray] = None):
+    def prefill(self, prefix_ids: Optional[np.ndarray] = None, depth: Optional[int] = None):
+        """Builds the prefix cache; ``depth``: depth-on-demand build to that Core depth."""
         w = self.w
         av = _ptr(self.avail)
-        if w.kv == "synthetic":
+        if depth is not None:
+            ids = synth.prefix_ids(w) if prefix_ids is None else prefix_ids
+            self.prefix_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(self.device)
+            B.prefill_kv_depth(self.ctx, w.batch, w.prefix, _ptr(self.prefix_ids) if w.prefix else 0, depth)
+        elif w.kv == "synthetic":
             ks, vs = synth.synthetic_kv_scales(w)
             B.prefill_kv_synthetic(self.ctx, w.batch, w.prefix, w.seed, float(np.float32(ks)), float(np.float32(vs)),
                                    av)
@@ -198,6 +204,10 @@ class Engine:
         if self._hidden is not None:
             res.hidden = self._hidden.cpu().numpy()
         return res
+
+    def deepen(self, depth: int):
+        B.deepen_kv(self.ctx, depth)
+        torch.cuda.synchronize(self.device)
 
     # ------------------------------------------------------------------ outer loop, cache growth
     def extend(self, new_ids: np.ndarray, avail: Optional[np.ndarray] = None):

@@ -77,6 +77,9 @@ typedef struct alodlm_config {
   int32_t dtype;        /* ALODLM_DTYPE_* */
   float rms_eps;        /* RMSNorm epsilon */
   float rope_theta;     /* RoPE base */
+  int32_t depth_on_demand; /* 1: the workspace also keeps the prefix's Core output
+                              ([max_batch][max_prefix][d] fp32) so that alodlm_prefill_kv_depth /
+                              alodlm_deepen_kv can build the cache depth by depth; 0: not */
 } alodlm_config;
 
 /* One transformer layer (Qwen3 block).  Device pointers in the config dtype,
@@ -128,6 +131,24 @@ ALODLM_API int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, 
  * batch <= max_batch, 0 <= prefix_len <= max_prefix.  Asynchronous. */
 ALODLM_API int alodlm_prefill_kv(alodlm_ctx* ctx, int32_t batch, int32_t prefix_len, const int32_t* prefix_ids,
                       const uint8_t* avail_depth);
+
+/* Depth-on-demand prefill (same page, section "Limitations": the first-token latency of building
+ * every depth, remedied by building depth 1 first and the deeper depths only when loops need
+ * them).  Builds the Core planes of depths 1..depth only and the Prelude and Coda sets, the Coda
+ * on the depth-`depth` output; every position's available depth is `depth`, so steps read the
+ * deeper Core planes at `depth` (the fallback rule).  Keeps the prefix's Core output for
+ * alodlm_deepen_kv.  Needs cfg.depth_on_demand (else EINVAL); 1 <= depth <= k_max.
+ * alodlm_prefill_kv on such a context also keeps that state (at depth k_max).  Asynchronous. */
+ALODLM_API int alodlm_prefill_kv_depth(alodlm_ctx* ctx, int32_t batch, int32_t prefix_len, const int32_t* prefix_ids,
+                                       int32_t depth);
+
+/* Continues a depth-on-demand cache to a greater depth: the Core passes from the built depth + 1
+ * to `depth` over the saved Core output, then the Coda set rebuilt on the deeper output; every
+ * position becomes available at `depth`.  The result equals alodlm_prefill_kv_depth(.., depth).
+ * ESTATE unless the cache came from alodlm_prefill_kv_depth / alodlm_prefill_kv on a
+ * depth_on_demand context and has not grown since; EINVAL unless built depth < depth <= k_max.
+ * Asynchronous. */
+ALODLM_API int alodlm_deepen_kv(alodlm_ctx* ctx, int32_t depth);
 
 /* Fills the prefix cache with seeded synthetic K/V instead of computing it (for
  * long-context measurements).  Element (slot, b, h, j, e) of K is draw

@@ -170,3 +170,68 @@ def test_mid_bf16_outer_loop(gpu_lib):
                                                    [[int((s["commit_loop"] != 0).sum()) for s in r["results"]]
                                                     for r in ores]))
     _check_block(w, e, ores, g)
+
+
+def _planes_at(w, cache, built):
+    """The cache as the GPU holds it after a build to depth `built`: Core planes deeper than
+    `built` hold the depth-`built` values (every position's available depth)."""
+    D = w.dims
+    out = {}
+    for slot in range(D.kv_slots(w.k_max)):
+        if D.n_pre <= slot < D.n_pre + D.n_core * w.k_max:
+            c, dp = divmod(slot - D.n_pre, w.k_max)
+            out[slot] = cache[orc.kv_slot(D, w.k_max, D.n_pre + c, min(dp + 1, built))]
+        else:
+            out[slot] = cache[slot]
+    return out
+
+
+def test_tiny_fp32_depth_on_demand_prefill(gpu_lib):
+    """Depth 1 first (steps read the deeper planes at depth 1), then deepened to 3 and to K: the
+    cache and the steps match the oracle at every stage, and the final cache is the full prefill."""
+    from adaptive_looped_denoising_amd import binding as B
+    from adaptive_looped_denoising_amd.engine import Engine
+    w = synth.workload("tiny", batch=2, boost_lo=8.0, boost_hi=14.0)
+    e = Engine(w, depth_on_demand=True, max_prefix=w.prefix + 8)
+    e.prefill(depth=1)
+    W = orun.weights(w)
+    ids = synth.prefix_ids(w)
+    args = (W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+    for built in (1, 3, w.k_max):
+        if built > 1:
+            e.deepen(built)
+        caches = {b: orc.prefill_sequence(ids[b], *args, depth=built) for b in range(w.batch)}
+        for b in range(w.batch):
+            _check_cache(e, w, b, 0, w.prefix, _planes_at(w, caches[b], built))
+        av = np.full((w.batch, w.prefix), built, dtype=np.int64)
+        ores = orun.step(w, W=W, caches=caches, avail=av, record_hidden=True)
+        g = e.step(records=True, hidden=True)
+        for r in ores:
+            b = r["seq"]
+            assert np.array_equal(g.commit_loop[b], r["commit_loop"]) and np.array_equal(g.tokens[b], r["tokens"])
+            for rec in r["records"]:
+                assert rel_rows(g.hidden[rec["loop"] - 1, b], rec["h_tilde"]).max() < 1e-4
+        log("built depth %d: cache and step match" % built)
+    with pytest.raises(B.AlodlmError) as ex:        # nothing deeper to build
+        e.deepen(w.k_max)
+    assert ex.value.code == B.EINVAL
+    e.extend(np.zeros((w.batch, 4), dtype=np.int32))
+    e.prefill(depth=2)                               # a fresh depth-2 build after the cache grew
+    e.extend(np.zeros((w.batch, 4), dtype=np.int32))
+    with pytest.raises(B.AlodlmError) as ex:        # the saved state no longer covers the cache
+        e.deepen(3)
+    assert ex.value.code == B.ESTATE
+
+
+def test_mid_bf16_depth_on_demand_prefill(gpu_lib):
+    from adaptive_looped_denoising_amd.engine import Engine
+    w = _mid(prefix=130, batch=2)
+    e = Engine(w, depth_on_demand=True)
+    e.prefill(depth=2)
+    e.deepen(w.k_max)
+    W = orun.weights(w)
+    ids = synth.prefix_ids(w)
+    for b in range(w.batch):
+        ref = orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+        ref16 = orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, prec="bf16")
+        log("seq %d worst/tol %.3f" % (b, _check_cache(e, w, b, 0, w.prefix, ref, ref16)))
