@@ -50,17 +50,20 @@ __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
                      __uint_as_float(w.y & 0xFFFF0000u));
 }
 
-template <typename TG, typename TO>
+// SPLITS (compile time, 0 = runtime `splits`): the number of deferred split-K partials to add, so
+// that every partial load of the row can be in flight at once.
+template <typename TG, typename TO, int SPLITS>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int d,
                                                  const int32_t* __restrict__ rows,
                                                  const int32_t* __restrict__ n_dev, const TG* __restrict__ g,
                                                  float eps, TO* __restrict__ out, const TG* __restrict__ exit_w,
                                                  float exit_b, float* __restrict__ lam,
-                                                 const float* __restrict__ part, int splits, int n_rows_part,
+                                                 const float* __restrict__ part, int splits_rt, int n_rows_part,
                                                  float* __restrict__ x_out) {
   __shared__ float red[4];
   const int r = blockIdx.x;
   if (n_dev && r >= *n_dev) return;
+  const int splits = SPLITS > 0 ? SPLITS : splits_rt;
   const int src = rows ? rows[r] : r;
   const float* xr = x + (size_t)src * d;
   float4 v[RMS_VEC];
@@ -69,14 +72,35 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
   for (int i = 0; i < RMS_VEC; ++i) {
     const int e = (i * 256 + threadIdx.x) * 4;
     v[i] = e < d ? *(const float4*)(xr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-    if (splits > 1 && e < d) {  // residual + fixed-order sum of the producing GEMM's split-K partials
-      float4 acc = *(const float4*)(part + (size_t)src * d + e);
-      for (int sp = 1; sp < splits; ++sp) {
-        const float4 pp = *(const float4*)(part + ((size_t)sp * n_rows_part + src) * d + e);
-        acc.x += pp.x;
-        acc.y += pp.y;
-        acc.z += pp.z;
-        acc.w += pp.w;
+  }
+  if (splits > 1) {  // residual + fixed-order sum of the producing GEMM's split-K partials
+#pragma unroll
+    for (int i = 0; i < RMS_VEC; ++i) {
+      const int e = (i * 256 + threadIdx.x) * 4;
+      if (e >= d) continue;
+      float4 pp[SPLITS > 0 ? SPLITS : 1];
+      float4 acc;
+      if (SPLITS > 0) {
+#pragma unroll
+        for (int sp = 0; sp < (SPLITS > 0 ? SPLITS : 1); ++sp)
+          pp[sp] = *(const float4*)(part + ((size_t)sp * n_rows_part + src) * d + e);
+        acc = pp[0];
+#pragma unroll
+        for (int sp = 1; sp < (SPLITS > 0 ? SPLITS : 1); ++sp) {
+          acc.x += pp[sp].x;
+          acc.y += pp[sp].y;
+          acc.z += pp[sp].z;
+          acc.w += pp[sp].w;
+        }
+      } else {
+        acc = *(const float4*)(part + (size_t)src * d + e);
+        for (int sp = 1; sp < splits; ++sp) {
+          const float4 q = *(const float4*)(part + ((size_t)sp * n_rows_part + src) * d + e);
+          acc.x += q.x;
+          acc.y += q.y;
+          acc.z += q.z;
+          acc.w += q.w;
+        }
       }
       v[i].x += acc.x;
       v[i].y += acc.y;
@@ -84,8 +108,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
       v[i].w += acc.w;
       *(float4*)(x_out + (size_t)src * d + e) = v[i];
     }
-    ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
   }
+#pragma unroll
+  for (int i = 0; i < RMS_VEC; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
   ss = block_sum<256>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
   float dot = 0.f;
@@ -125,7 +150,8 @@ __global__ __launch_bounds__(256) void k_exit_gate(const T* __restrict__ rows, i
 // Per-head RMSNorm of q and k, rotary embedding (rotate-half pairs (p, p + hd/2)), and the
 // layout change of q/k/v.  One wave per (row, head); lane p owns the pair (p, p + hd/2).
 // K/V element (row r, kv head h, e) goes to kv + (seq0 + r / n)*sSeq + h*sHead + (r % n)*sPos + e.
-template <typename TW, typename TA>
+// SPLITS (compile time, 0 = runtime `splits`): split-K partials of the projection to add.
+template <typename TW, typename TA, int SPLITS>
 __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ qkv, int n_rows, int rows_per_seq,
                                                       int pos0, int Hq, int Hkv, int hd,
                                                       const TW* __restrict__ qn, const TW* __restrict__ kn,
@@ -133,7 +159,8 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
                                                       const float* __restrict__ sinT, TA* __restrict__ q_out,
                                                       TA* __restrict__ k_out, TA* __restrict__ v_out,
                                                       int64_t kSeq, int64_t kHead, int64_t kPos, int64_t vSeq,
-                                                      int64_t vHead, int64_t vRow, int seq0, int splits) {
+                                                      int64_t vHead, int64_t vRow, int seq0, int splits_rt) {
+  const int splits = SPLITS > 0 ? SPLITS : splits_rt;
   const int NH = Hq + 2 * Hkv;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -145,7 +172,12 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
   // element e of this head: the projection, or the fixed-order sum of its split-K partials
   auto val = [&](int e) {
     float acc = src[e];
-    for (int sp = 1; sp < splits; ++sp) acc += src[sp * pstride + e];
+    if (SPLITS > 0) {
+#pragma unroll
+      for (int sp = 1; sp < SPLITS; ++sp) acc += src[sp * pstride + e];
+    } else {
+      for (int sp = 1; sp < splits; ++sp) acc += src[sp * pstride + e];
+    }
     return acc;
   };
   const int jpos = r % rows_per_seq;
@@ -551,9 +583,20 @@ void launch_rmsnorm(int dtype, const float* x, int n_rows, int d, const int32_t*
                     const void* g, float eps, void* out, const void* exit_w, float exit_b, float* lam,
                     hipStream_t st, const float* part, int splits, float* x_out) {
   if (n_rows <= 0) return;
-  DISPATCH_T(dtype, T,
-             k_rmsnorm<T, T><<<n_rows, 256, 0, st>>>(x, d, rows, n_dev, (const T*)g, eps, (T*)out,
-                                                      (const T*)exit_w, exit_b, lam, part, splits, n_rows, x_out));
+#define RMS_GO(S)                                                                                              \
+  DISPATCH_T(dtype, T,                                                                                         \
+             k_rmsnorm<T, T, S><<<n_rows, 256, 0, st>>>(x, d, rows, n_dev, (const T*)g, eps, (T*)out,          \
+                                                         (const T*)exit_w, exit_b, lam, part, splits, n_rows, x_out))
+  if (splits <= 1) {
+    RMS_GO(1);
+  } else if (splits == 2) {
+    RMS_GO(2);
+  } else if (splits == 4) {
+    RMS_GO(4);
+  } else {
+    RMS_GO(0);
+  }
+#undef RMS_GO
 }
 
 void launch_exit_gate(int dtype, const void* rows, int n_rows, int d, const void* w, float b, float* lam,
@@ -569,10 +612,21 @@ void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_s
                          int splits) {
   if (n_rows <= 0) return;
   const int waves = n_rows * (Hq + 2 * Hkv);
-  DISPATCH_T(dtype, T,
-             k_qk_norm_rope<T, T><<<(waves + 3) / 4, 256, 0, st>>>(
-                 qkv, n_rows, rows_per_seq, pos0, Hq, Hkv, hd, (const T*)qn, (const T*)kn, eps, cosT, sinT,
-                 (T*)q_out, (T*)k_out, (T*)v_out, kSeq, kHead, kPos, vSeq, vHead, vRow, seq0, splits));
+#define QKR_GO(S)                                                                                 \
+  DISPATCH_T(dtype, T,                                                                            \
+             k_qk_norm_rope<T, T, S><<<(waves + 3) / 4, 256, 0, st>>>(                            \
+                 qkv, n_rows, rows_per_seq, pos0, Hq, Hkv, hd, (const T*)qn, (const T*)kn, eps, cosT, sinT, \
+                 (T*)q_out, (T*)k_out, (T*)v_out, kSeq, kHead, kPos, vSeq, vHead, vRow, seq0, splits))
+  if (splits <= 1) {
+    QKR_GO(1);
+  } else if (splits == 2) {
+    QKR_GO(2);
+  } else if (splits == 4) {
+    QKR_GO(4);
+  } else {
+    QKR_GO(0);
+  }
+#undef QKR_GO
 }
 
 void launch_swiglu(int dtype, const float* gu, int n_rows, int F, void* act, hipStream_t st) {
