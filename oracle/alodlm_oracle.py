@@ -65,6 +65,11 @@ follow them):
     deepening continues the Core passes from the saved depth-D0 output and
     rebuilds the Coda set on the deeper output (so the result equals a
     prefill built to that depth directly);
+  * compressed depth buffers (the "Limitations" section's remedy for the
+    memory of the per-depth cache): keys and values -- the cached ones and
+    a block's own -- may be stored in the OCP FP8 E4M3 format, rounded once
+    from the float32 projection result (nearest, ties to even, saturating
+    at +-448); attention then reads those values;
   * a finished block joins the depth-aware cache the way the prefill builds
     it: its positions go through the Prelude once, the Core once per depth
     d = 1..k_max and the Coda once on the depth-k_max output, causally among
@@ -97,6 +102,30 @@ def round_bf16(x) -> np.ndarray:
 
 def _rnd(x, prec):
     return round_bf16(x) if prec == "bf16" else x
+
+
+FP8_MAX = 448.0  # largest finite OCP FP8 E4M3 value (1.75 * 2^8)
+
+
+def round_fp8_e4m3(x) -> np.ndarray:
+    """Round to the OCP FP8 E4M3 format (sign, 4 exponent bits with bias 7, 3 fraction bits,
+    subnormals, no infinities, largest finite 448) the way a pipeline computing in float32 stores
+    it: to float32 first, then to the nearest E4M3 value with ties to even, saturating at +-448.
+    Returned as float64."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    a = np.abs(f)
+    _, ex = np.frexp(a)                       # a = m * 2^ex, m in [0.5, 1): floor(log2 a) = ex - 1
+    e = np.maximum(ex - 1, -6)                # binade exponent; below 2^-6 the subnormal spacing
+    q = np.ldexp(1.0, e - 3)                  # spacing of E4M3 values in that binade
+    r = np.round(a / q) * q                   # a / q is exact (power-of-two scale); numpy rounds half to even
+    r = np.minimum(r, FP8_MAX)
+    return np.where(a == 0.0, 0.0, np.copysign(r, f))
+
+
+def _kv_round(x, prec, kv):
+    """Storage rounding of post-RoPE keys / values: E4M3 straight from the exact value when the K/V
+    format is fp8 (the pipeline converts its float32 result once), else as ``prec``."""
+    return round_fp8_e4m3(x) if kv == "fp8" else _rnd(x, prec)
 
 
 def matmul_t(x: np.ndarray, w: np.ndarray, chunk: int = 16384) -> np.ndarray:
@@ -160,7 +189,7 @@ def silu(x) -> np.ndarray:
 
 
 def layer_forward(x, W: Dict[str, np.ndarray], li: int, dims, eps: float, theta: float, pos,
-                  ctx_k=None, ctx_v=None, causal: bool = False, prec=None):
+                  ctx_k=None, ctx_v=None, causal: bool = False, prec=None, kv=None):
     """One Qwen3-style block over the n rows ``x`` [n][d] of one sequence.
 
     ctx_k / ctx_v [Hkv][m][hd]: cached (post-RoPE) keys and values that every
@@ -171,6 +200,7 @@ def layer_forward(x, W: Dict[str, np.ndarray], li: int, dims, eps: float, theta:
     ``prec="bf16"`` rounds to bfloat16 where a bf16 pipeline stores values: the
     normalised inputs of the projections, q / k / v, the attention output and the
     SwiGLU output (the residual stream stays exact).  Default: exact arithmetic.
+    ``kv="fp8"``: keys and values are stored (and attended to) in FP8 E4M3.
     """
     p = "layers.%d." % li
     x = _f64(x)
@@ -180,9 +210,9 @@ def layer_forward(x, W: Dict[str, np.ndarray], li: int, dims, eps: float, theta:
     qkv = matmul_t(h1, W[p + "wqkv"])
     q = qkv[:, : Hq * hd].reshape(n, Hq, hd).transpose(1, 0, 2)
     k = qkv[:, Hq * hd: (Hq + Hkv) * hd].reshape(n, Hkv, hd).transpose(1, 0, 2)
-    v = _rnd(qkv[:, (Hq + Hkv) * hd:].reshape(n, Hkv, hd).transpose(1, 0, 2), prec)
+    v = _kv_round(qkv[:, (Hq + Hkv) * hd:].reshape(n, Hkv, hd).transpose(1, 0, 2), prec, kv)
     q = _rnd(rope(rms_norm(q, W[p + "q_norm"], eps), pos, theta), prec)
-    k = _rnd(rope(rms_norm(k, W[p + "k_norm"], eps), pos, theta), prec)
+    k = _kv_round(rope(rms_norm(k, W[p + "k_norm"], eps), pos, theta), prec, kv)
     m = 0 if ctx_k is None else ctx_k.shape[1]
     keys = k if ctx_k is None else np.concatenate([_f64(ctx_k), k], axis=1)
     vals = v if ctx_v is None else np.concatenate([_f64(ctx_v), v], axis=1)
@@ -211,14 +241,14 @@ def kv_slot(dims, k_max: int, layer: int, depth: int = 1) -> int:
 
 
 def prefill_sequence(ids, W, dims, k_max: int, eps: float, theta: float, progress=None,
-                     prec=None, depth: Optional[int] = None, state: bool = False):
+                     prec=None, depth: Optional[int] = None, state: bool = False, kv=None):
     """Depth-aware cache of one prefix: slot -> (K, V) [Hkv][P][hd] (causal prefix).
     ``progress`` (optional) is called with a short text after every layer call.
 
     ``depth`` (default k_max): build the Core only to this depth, the Coda set on the
     depth-``depth`` output (depth-on-demand prefill; every position's available depth is then
     ``depth``).  ``state``: also return the prefix's Core output at that depth, from which
-    deepen_sequence continues."""
+    deepen_sequence continues.  ``kv`` as in layer_forward."""
     ids = np.asarray(ids)
     P = ids.shape[0]
     pos = np.arange(P)
@@ -228,7 +258,7 @@ def prefill_sequence(ids, W, dims, k_max: int, eps: float, theta: float, progres
 
     def run(li, slot):
         nonlocal x
-        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True, prec=prec)
+        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True, prec=prec, kv=kv)
         cache[slot] = (k, v)
         if progress is not None:
             progress("prefill layer %d -> slot %d" % (li, slot))
@@ -246,7 +276,7 @@ def prefill_sequence(ids, W, dims, k_max: int, eps: float, theta: float, progres
 
 
 def deepen_sequence(cache, core_out, W, dims, k_max: int, eps: float, theta: float, depth_from: int,
-                    depth_to: int, prec=None):
+                    depth_to: int, prec=None, kv=None):
     """Depth-on-demand: continue a prefix built to ``depth_from`` (its Core output ``core_out``)
     with the Core passes depth_from+1 .. depth_to, then rebuild the Coda set on the deeper output.
     Returns the deeper cache and Core output; equals the prefill built to ``depth_to`` directly."""
@@ -257,12 +287,12 @@ def deepen_sequence(cache, core_out, W, dims, k_max: int, eps: float, theta: flo
     for dpt in range(depth_from + 1, depth_to + 1):
         for c in range(dims.n_core):
             li = dims.n_pre + c
-            x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True, prec=prec)
+            x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True, prec=prec, kv=kv)
             out[kv_slot(dims, k_max, li, dpt)] = (k, v)
     core = x
     for c in range(dims.n_coda):
         li = dims.n_pre + dims.n_core + c
-        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True, prec=prec)
+        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, causal=True, prec=prec, kv=kv)
         out[kv_slot(dims, k_max, li)] = (k, v)
     return out, core
 
@@ -289,7 +319,8 @@ def context_for(cache, dims, k_max: int, layer: int, loop: int, avail):
     return _f64(K), _f64(V)
 
 
-def extend_sequence(cache, avail, new_ids, W, dims, k_max: int, eps: float, theta: float, prec=None):
+def extend_sequence(cache, avail, new_ids, W, dims, k_max: int, eps: float, theta: float, prec=None,
+                    kv=None):
     """Appends positions (a finished block) to the depth-aware cache of one sequence.
 
     The new positions (ids ``new_ids``, positions P.. after the P cached ones) run through the
@@ -307,7 +338,7 @@ def extend_sequence(cache, avail, new_ids, W, dims, k_max: int, eps: float, thet
     def run(li, depth):
         nonlocal x
         ck, cv = context_for(cache, dims, k_max, li, depth, avail) if cache else (None, None)
-        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, ck, cv, causal=True, prec=prec)
+        x, k, v = layer_forward(x, W, li, dims, eps, theta, pos, ck, cv, causal=True, prec=prec, kv=kv)
         new[kv_slot(dims, k_max, li, depth)] = (k, v)
 
     for li in range(dims.n_pre):
@@ -424,7 +455,7 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
                           theta: float, tau_ent: float, tau_halt: float, mask_id: int, exit_b: float,
                           boost_tok=None, boost_val=None, teacher: Optional[dict] = None,
                           record_hidden: bool = False, counter: Optional[list] = None, progress=None,
-                          prec=None, sample: Optional[dict] = None) -> dict:
+                          prec=None, sample: Optional[dict] = None, kv=None) -> dict:
     """One inner loop of Algorithm 1 of the summary page (one denoising step), for one sequence.
 
     ``cache``: slot -> (K, V) [Hkv][P][hd]; ``avail``: deepest cached Core depth
@@ -434,7 +465,8 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
     called with a short text after every layer call.  ``prec`` as in layer_forward (the
     readout rows feeding the LMHead are rounded too; the ExitGate reads them exactly).
     ``sample`` (optional) {"seed", "step", "seq"}: commit the Gumbel-max draw of each row
-    (gumbel_noise with this sequence index) instead of its argmax.
+    (gumbel_noise with this sequence index) instead of its argmax.  ``kv="fp8"``: the rows' own keys
+    and values are stored in FP8 E4M3 like the cache's.
     """
     block_ids = np.asarray(block_ids, dtype=np.int64)
     L = block_ids.shape[0]
@@ -448,7 +480,7 @@ def denoise_step_sequence(block_ids, cache, avail, W, dims, *, k_max: int, k_loo
             ck, cv = context_for(cache, dims, k_max, li, loop, avail)
         else:
             ck = cv = None
-        y, _, _ = layer_forward(x, W, li, dims, eps, theta, pos, ck, cv, causal=False, prec=prec)
+        y, _, _ = layer_forward(x, W, li, dims, eps, theta, pos, ck, cv, causal=False, prec=prec, kv=kv)
         if progress is not None:
             progress("step loop %d layer %d" % (loop, li))
         return y

@@ -5,6 +5,7 @@ per-sequence oracle step; nothing here reads GPU results.
 """
 from __future__ import annotations
 
+from dataclasses import replace
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -18,19 +19,29 @@ def weights(w: synth.Workload, names: Optional[List[str]] = None) -> Dict[str, n
     return {k: synth.as_f32(v) for k, v in synth.host_weights(w, names).items()}
 
 
+def kv_format(w: synth.Workload):
+    """The oracle's K/V storage option for the workload: "fp8" or None (the model dtype)."""
+    return "fp8" if w.kv_dtype == "fp8" else None
+
+
 def cache_for(w: synth.Workload, W, b: int, prefix_ids=None, progress=None, prec=None) -> Dict[int, tuple]:
     """Depth-aware prefix cache of sequence b: computed by the oracle's prefill, or the
-    workload's synthetic K/V."""
+    workload's synthetic K/V (with fp8 K/V: the float32 draws rounded by the oracle's E4M3)."""
     if w.prefix == 0:
         return {}
     if w.kv == "synthetic":
         out = {}
         for slot in range(w.dims.kv_slots(w.k_max)):
-            K, V = synth.synthetic_kv_seq(w, slot, b)
-            out[slot] = (synth.as_f32(K), synth.as_f32(V))
+            if kv_format(w) == "fp8":
+                K, V = synth.synthetic_kv_seq(replace(w, dtype="fp32"), slot, b)
+                out[slot] = (orc.round_fp8_e4m3(K), orc.round_fp8_e4m3(V))
+            else:
+                K, V = synth.synthetic_kv_seq(w, slot, b)
+                out[slot] = (synth.as_f32(K), synth.as_f32(V))
         return out
     ids = synth.prefix_ids(w) if prefix_ids is None else prefix_ids
-    return orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, progress=progress, prec=prec)
+    return orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, progress=progress, prec=prec,
+                                kv=kv_format(w))
 
 
 def step(w: synth.Workload, W=None, seqs=None, k_loops: Optional[int] = None, teacher=None,
@@ -54,7 +65,7 @@ def step(w: synth.Workload, W=None, seqs=None, k_loops: Optional[int] = None, te
             theta=w.rope_theta, tau_ent=w.tau_ent, tau_halt=w.tau_halt, mask_id=w.mask_id,
             exit_b=w.exit_bias() if exit_b is None else exit_b, boost_tok=btok[b], boost_val=bval[b],
             teacher=None if teacher is None else teacher[b], record_hidden=record_hidden, counter=counter,
-            progress=progress, prec=prec, sample=None if sample is None else dict(sample, seq=b))
+            progress=progress, prec=prec, sample=None if sample is None else dict(sample, seq=b), kv=kv_format(w))
         res["seq"] = b
         out.append(res)
     return out
@@ -83,7 +94,7 @@ def denoise_block(w: synth.Workload, W=None, seqs=None, block_ids=None, boost=No
         res = orc.denoise_block_sequence(
             bids[b], cache, av[b] if av is not None and w.prefix else None, W, w.dims, max_steps=max_steps,
             sample=None if sample is None else dict(sample, seq=b), mask_id=w.mask_id, boost_tok=btok[b],
-            boost_val=bval[b], prec=prec, **step_kwargs(w))
+            boost_val=bval[b], prec=prec, kv=kv_format(w), **step_kwargs(w))
         res["seq"] = b
         out.append(res)
     return out

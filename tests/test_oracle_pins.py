@@ -8,6 +8,7 @@ from dataclasses import replace
 
 import numpy as np
 import pytest
+import torch
 
 from adaptive_looped_denoising_amd import synth
 from oracle import alodlm_oracle as orc
@@ -670,3 +671,64 @@ def test_depth_on_demand_prefill_then_deepen_equals_full_prefill():
     # the Coda set of a shallow build comes from the shallow output
     coda = orc.kv_slot(D, w.k_max, D.n_pre + D.n_core)
     assert not np.allclose(c1[coda][0], full[coda][0])
+
+
+# --------------------------------------------------------------------------- fp8 K/V storage
+def _e4m3_table():
+    """Every finite OCP FP8 E4M3 value from the format definition: sign, 4 exponent bits (bias 7),
+    3 fraction bits; exponent field 0 is subnormal (f/8 * 2^-6); code S.1111.111 is NaN."""
+    vals = []
+    for code in range(256):
+        s, e, f = code >> 7, (code >> 3) & 15, code & 7
+        if e == 15 and f == 7:
+            continue
+        v = (f / 8.0) * 2.0 ** -6 if e == 0 else (1 + f / 8.0) * 2.0 ** (e - 7)
+        vals.append(-v if s else v)
+    return np.array(sorted(set(vals)))
+
+
+def test_fp8_rounding_fixed_points_and_range():
+    t = _e4m3_table()
+    assert t.max() == 448.0 and t.min() == -448.0 and np.min(t[t > 0]) == 2.0 ** -9 and t.size == 253
+    np.testing.assert_array_equal(orc.round_fp8_e4m3(t), t)
+    x = np.random.default_rng(11).uniform(-500, 500, 20000) * np.random.default_rng(12).choice(
+        [1.0, 1e-1, 1e-2, 1e-3], 20000)
+    r = orc.round_fp8_e4m3(x)
+    assert np.isin(r, t).all()
+    # nearest representable value (ties resolved below)
+    idx = np.searchsorted(t, x)
+    lo, hi = t[np.clip(idx - 1, 0, t.size - 1)], t[np.clip(idx, 0, t.size - 1)]
+    best = np.where(np.abs(x - lo) <= np.abs(x - hi), lo, hi)
+    inside = np.abs(x) <= 448.0
+    tie = np.abs(np.abs(x - lo) - np.abs(x - hi)) < 1e-12
+    assert (r[inside & ~tie] == best[inside & ~tie]).all()
+    assert (orc.round_fp8_e4m3(np.array([460.0, 1000.0, -1e6])) == [448.0, 448.0, -448.0]).all()
+
+
+def test_fp8_rounding_matches_library_conversion():
+    """Against torch's float32 -> float8_e4m3fn conversion (round to nearest even) inside the finite
+    range, including every midpoint between neighbouring values (ties to the even code)."""
+    t = _e4m3_table()
+    mids = (t[1:] + t[:-1]) / 2
+    x = np.concatenate([mids, np.random.default_rng(13).normal(0, 3, 50000), t])
+    x = x[np.abs(x) <= 448.0].astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.round_fp8_e4m3(x), lib)
+
+
+def test_fp8_cache_holds_e4m3_values_and_changes_little():
+    w = _tiny(dtype="bf16")
+    W = run.weights(w)
+    ids = synth.prefix_ids(w)[0]
+    c8 = orc.prefill_sequence(ids, W, w.dims, w.k_max, w.rms_eps, w.rope_theta, kv="fp8")
+    c = orc.prefill_sequence(ids, W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
+    for slot in c:
+        for a8, a in zip(c8[slot], c[slot]):
+            np.testing.assert_array_equal(orc.round_fp8_e4m3(a8), a8)
+            rel = np.linalg.norm(a8 - a) / np.linalg.norm(a)
+            assert 1e-4 < rel < 0.08
+    r8 = run.step(replace(w, kv_dtype="fp8"), W=W)[0]
+    r = run.step(w, W=W)[0]
+    h8 = r8["records"][0]["H"][r8["records"][0]["rows"]]
+    h = r["records"][0]["H"][r["records"][0]["rows"]]
+    assert 0 < np.abs(h8 - h).max() < 0.1
