@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libalodlm.so")
 
 OK, EINVAL, ESTATE, ENOMEM, EHIP = 0, -1, -2, -3, -4
 DTYPE_BF16, DTYPE_FP32 = 0, 1
+KV_SAME, KV_FP8 = 0, 2
 STEP_TEACHER_FORCED, STEP_SAMPLE = 1, 2
 # diagnostics GEMM epilogues (alodlm_diag.h)
 DIAG_STORE, DIAG_RESID, DIAG_SOFTSTAT, DIAG_SWIGLU = 0, 1, 2, 3
@@ -31,7 +32,7 @@ class Config(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "vocab", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "n_pre", "n_core", "n_coda", "k_max",
         "max_batch", "max_prefix", "max_block", "max_prefill_rows", "mask_id", "dtype")] + \
-        [("rms_eps", c_float), ("rope_theta", c_float), ("depth_on_demand", c_int32)]
+        [("rms_eps", c_float), ("rope_theta", c_float), ("depth_on_demand", c_int32), ("kv_dtype", c_int32)]
 
 
 class LayerWeights(ctypes.Structure):

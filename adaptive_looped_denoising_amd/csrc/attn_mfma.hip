@@ -17,6 +17,10 @@
 // probabilities are already laid out as the B operand of O^T += V^T P^T.
 // With several key splits, partial (O, max, sum) go to a scratch buffer and k_attn_merge
 // combines them in a fixed order.
+// F8: keys and values are stored in FP8 E4M3 (half the bytes).  The fp8 tiles stream into the
+// LDS ring unswizzled; once a stage has landed, the workgroup converts it (exactly: every E4M3
+// value is a bf16 value) into one bf16 working tile in the layout above, and the matrix-core
+// code is unchanged.
 #include "common.h"
 #include "launch.h"
 
@@ -31,8 +35,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)from_f<bf16_t>(lo) | ((uint32_t)from_f<bf16_t>(hi) << 16);
 }
 
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// Two E4M3 bytes of w (the low half when HI is false, else the high half) as two bf16 (exact:
+// bf16 keeps 7 fraction bits).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  const float2v f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
+}
+
+// 16 E4M3 values -> two groups of 8 bf16 (elements 0..7, 8..15).
+__device__ __forceinline__ void fp8x16_to_bf16(const uint4 in, uint4& lo, uint4& hi) {
+  lo.x = fp8x2_to_bf16x2<false>(in.x);
+  lo.y = fp8x2_to_bf16x2<true>(in.x);
+  lo.z = fp8x2_to_bf16x2<false>(in.y);
+  lo.w = fp8x2_to_bf16x2<true>(in.y);
+  hi.x = fp8x2_to_bf16x2<false>(in.z);
+  hi.y = fp8x2_to_bf16x2<true>(in.z);
+  hi.z = fp8x2_to_bf16x2<false>(in.w);
+  hi.w = fp8x2_to_bf16x2<true>(in.w);
+}
+
 // NW waves per workgroup (4, or 8 for HD >= 64: two waves per SIMD sharing one K/V stream).
-template <int HD, int QW, int NS, int NW>
+template <int HD, int QW, int NS, int NW, bool F8>
 __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs, int n_qblocks, int n_splits,
                                                        int tiles_per_split) {
   constexpr int QB = NW * QW;
@@ -42,13 +68,19 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
   constexpr int CK = HD / 8;             // 16-byte chunks per K row
   constexpr int KST = AKT * HD;          // K elements per stage
   constexpr int STAGE = 2 * AKT * HD;    // K then V^T
-  constexpr int KL = HD * 8 / (64 * NW); // K load instructions per wave per stage (1 KB each)
-  constexpr int VL = HD * 8 / (64 * NW); // V^T load instructions per wave per stage
+  constexpr int KL = HD * 8 / (64 * NW) / (F8 ? 2 : 1); // K load instructions per wave per stage (1 KB each)
+  constexpr int VL = KL;                                 // V^T load instructions per wave per stage
   constexpr int LPW = KL + VL;
   constexpr int RPI = 1024 / (HD * 2);   // K rows per load instruction
-  static_assert(KL >= 1 && KL * NW * 64 == HD * 8, "tile loads must split evenly over the waves");
+  constexpr int CK8 = HD / 16;           // fp8: 16-byte chunks per K row
+  constexpr int STAGE8 = 2 * AKT * HD;   // fp8: bytes per ring stage (K then V^T)
+  static_assert(KL >= 1 && KL * NW * 64 * (F8 ? 2 : 1) == HD * 8, "tile loads must split evenly over the waves");
   static_assert(NS >= 2 && (NS - 2) * LPW < 64, "ring depth");
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * STAGE];
+  // bf16: NS stages; fp8: NS fp8 stages, then the bf16 working tile
+  constexpr int SMEM = F8 ? NS * STAGE8 / 2 + STAGE : NS * STAGE;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM];
+  char* const ring8 = (char*)smem;
+  bf16_t* const work = smem + (F8 ? NS * STAGE8 / 2 : 0);
 
   const int total = n_pairs * n_qblocks * n_splits;
   const int per = (gridDim.x + 7) >> 3;
@@ -97,6 +129,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
   const bf16_t* vpre = (const bf16_t*)p.cv + (size_t)b * p.c_vSeq + (size_t)kvh * p.c_vHead;
   const bf16_t* kslf = (const bf16_t*)p.sk + (size_t)(t + p.s_seq0) * p.s_kSeq + (size_t)kvh * p.s_kHead;
   const bf16_t* vslf = (const bf16_t*)p.sv + (size_t)(t + p.s_seq0) * p.s_vSeq + (size_t)kvh * p.s_vHead;
+  // the same bases for one-byte (fp8) elements
+  const char* kpre8 = (const char*)p.ck + (size_t)b * p.c_kSeq + (size_t)kvh * p.c_kHead;
+  const char* vpre8 = (const char*)p.cv + (size_t)b * p.c_vSeq + (size_t)kvh * p.c_vHead;
+  const char* kslf8 = (const char*)p.sk + (size_t)(t + p.s_seq0) * p.s_kSeq + (size_t)kvh * p.s_kHead;
+  const char* vslf8 = (const char*)p.sv + (size_t)(t + p.s_seq0) * p.s_vSeq + (size_t)kvh * p.s_vHead;
 
   // lane-constant parts of the DMA addresses
   int krow[KL], kchunk[KL], vrow[VL], vchunk[VL];
@@ -111,6 +148,32 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
     vchunk[i] = (lane & 7) ^ ((vrow[i] >> 1) & 7);
   }
   auto issue = [&](int tile, int slot) {
+    if (F8) {
+      // fp8 chunks land unswizzled: K chunk q = (key row q / CK8, 16 hd elements q % CK8), then
+      // V^T chunk q = (hd row q / 4, 16 keys q % 4)
+      char* base8 = ring8 + slot * STAGE8;
+      const bool pre = tile < TP;
+      const int k0 = pre ? tile * AKT : (tile - TP) * AKT;
+      const int klen = pre ? p.n_cache : p.n_self;
+      const char* kb = pre ? kpre8 : kslf8;
+      const int64_t kpos = pre ? p.c_kPos : p.s_kPos;
+      const char* vb = pre ? vpre8 : vslf8;
+      const int64_t vr = pre ? p.c_vRow : p.s_vRow;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        const int q = (wid * KL + i) * 64 + lane;
+        const int key = min(k0 + q / CK8, klen - 1);  // rows past the segment load a valid row (masked)
+        __builtin_amdgcn_global_load_lds((const void*)(kb + (size_t)key * kpos + (q % CK8) * 16),
+                                         LDS_PTR(base8 + (wid * KL + i) * 1024), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int q = (wid * VL + i) * 64 + lane;
+        __builtin_amdgcn_global_load_lds((const void*)(vb + (size_t)(q >> 2) * vr + k0 + (q & 3) * 16),
+                                         LDS_PTR(base8 + AKT * HD + (wid * VL + i) * 1024), 16, 0, 0);
+      }
+      return;
+    }
     bf16_t* base = smem + slot * STAGE;
     const bool pre = tile < TP;
     const int k0 = pre ? tile * AKT : (tile - TP) * AKT;  // first key of the tile in its segment
@@ -154,10 +217,33 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
     else
       wait_vmcnt_le<0>();
     // every wave's loads of this stage have landed, and every wave is done with the slot refilled below
+    // (and, with fp8, with the working tile)
     lds_barrier();
     if (tile + NS - 1 < te) issue(tile + NS - 1, (it + NS - 1) % NS);
-    const bf16_t* sK = smem + (it % NS) * STAGE;
+    const bf16_t* sK = F8 ? work : smem + (it % NS) * STAGE;
     const bf16_t* sV = sK + KST;
+    if (F8) {  // convert the landed fp8 stage into the swizzled bf16 working tile
+      const char* s8 = ring8 + (it % NS) * STAGE8;
+      bf16_t* wK = work;
+      bf16_t* wV = work + KST;
+      for (int q = tid; q < AKT * CK8; q += NW * 64) {
+        const uint4 in = *(const uint4*)(s8 + q * 16);
+        uint4 lo, hi;
+        fp8x16_to_bf16(in, lo, hi);
+        const int r = q / CK8, c = 2 * (q % CK8);
+        *(uint4*)&wK[r * HD + ((c ^ (r & (CK - 1))) << 3)] = lo;
+        *(uint4*)&wK[r * HD + (((c + 1) ^ (r & (CK - 1))) << 3)] = hi;
+      }
+      for (int q = tid; q < HD * 4; q += NW * 64) {
+        const uint4 in = *(const uint4*)(s8 + AKT * HD + q * 16);
+        uint4 lo, hi;
+        fp8x16_to_bf16(in, lo, hi);
+        const int e = q >> 2, c = 2 * (q & 3), sw = (e >> 1) & 7;
+        *(uint4*)&wV[e * AKT + ((c ^ sw) << 3)] = lo;
+        *(uint4*)&wV[e * AKT + (((c + 1) ^ sw) << 3)] = hi;
+      }
+      lds_barrier_lds_only();
+    }
     const bool pre = tile < TP;
     const int k0 = pre ? tile * AKT : (tile - TP) * AKT;
     const int klen = pre ? p.n_cache : p.n_self;
@@ -325,16 +411,16 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int n_pairs, i
   }
 }
 
-template <int HD, int QW, int NW>
+template <int HD, int QW, int NW, bool F8>
 static void run_attn(const AttnParams& p, int n_pairs, int n_qblocks, int n_splits, int tps, int ns, hipStream_t st) {
   const int total = n_pairs * n_qblocks * n_splits;
   const int grid = ((total + 7) / 8) * 8;
   if (ns == 2)
-    k_attn_mfma<HD, QW, 2, NW><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+    k_attn_mfma<HD, QW, 2, NW, F8><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   else if (ns == 4)
-    k_attn_mfma<HD, QW, 4, NW><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+    k_attn_mfma<HD, QW, 4, NW, F8><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   else
-    k_attn_mfma<HD, QW, 3, NW><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+    k_attn_mfma<HD, QW, 3, NW, F8><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   if (n_splits > 1) {
     const int rows_q = (p.Hq / p.Hkv) * p.rows_per_seq;
     const int waves = n_pairs * rows_q;
@@ -356,7 +442,7 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
   // measured (8B shape, 128 and 256 query rows per pair): 16 query rows per wave and a
   // two-stage ring (64 KB of LDS, two blocks per compute unit) beat wider and deeper variants
   const int QW = (force_qw == 16 || force_qw == 32) ? force_qw : 16;
-  const int NW = (force_nw == 8 && p.hd >= 64) ? 8 : 4;
+  const int NW = (force_nw == 8 && p.hd >= (p.kv8 ? 128 : 64)) ? 8 : 4;
   const int QB = NW * QW;
   const int n_qblocks = (rows_q + QB - 1) / QB;
   const int n_tiles = (p.n_cache + AKT - 1) / AKT + (p.n_self + AKT - 1) / AKT;
@@ -372,7 +458,20 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
   splits = (n_tiles + tps - 1) / tps;
   if (splits < 1) splits = 1;
   const int ns = (force_ns >= 2 && force_ns <= 4) ? force_ns : 2;
-#define GO(H, Q, W) run_attn<H, Q, W>(p, n_pairs, n_qblocks, splits, tps, ns, st)
+#define GO(H, Q, W) run_attn<H, Q, W, false>(p, n_pairs, n_qblocks, splits, tps, ns, st)
+#define GO8(H, Q, W) run_attn<H, Q, W, true>(p, n_pairs, n_qblocks, splits, tps, ns, st)
+  if (p.kv8) {  // fp8 keys and values (head sizes 64 and 128)
+    if (p.hd == 128) {
+      if (NW == 8) {
+        if (QW == 16) GO8(128, 16, 8); else GO8(128, 32, 8);
+      } else {
+        if (QW == 16) GO8(128, 16, 4); else GO8(128, 32, 4);
+      }
+    } else {
+      if (QW == 16) GO8(64, 16, 4); else GO8(64, 32, 4);
+    }
+    return;
+  }
   if (p.hd == 128) {
     if (NW == 8) {
       if (QW == 16) GO(128, 16, 8); else GO(128, 32, 8);
@@ -389,6 +488,7 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
     if (QW == 16) GO(32, 16, 4); else GO(32, 32, 4);
   }
 #undef GO
+#undef GO8
 }
 
 }  // namespace alodlm

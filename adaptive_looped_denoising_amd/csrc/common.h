@@ -19,6 +19,20 @@ template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) {
   return (bf16_t)(u >> 16);
 }
 
+// OCP FP8 E4M3 storage byte (sign, 4 exponent bits with bias 7, 3 fraction bits, largest finite
+// 448).  Conversion from float: saturate to +-448, then the hardware's round to nearest even.
+struct fp8_t {
+  uint8_t b;
+};
+template <> __device__ __forceinline__ fp8_t from_f<fp8_t>(float v) {
+  const float c = __builtin_amdgcn_fmed3f(v, 448.0f, -448.0f);
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false);
+  fp8_t r;
+  r.b = (uint8_t)(w & 0xFF);
+  return r;
+}
+__device__ __forceinline__ float to_f(fp8_t v) { return __builtin_amdgcn_cvt_f32_fp8((int)v.b, 0); }
+
 // LDS address operand of the direct global->LDS loads (each lane's bytes land at M0 + lane * size).
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -36,6 +50,16 @@ __device__ __forceinline__ void wait_vmcnt_le() {
 // accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier once this wave's LDS accesses have completed (a wait on the LDS counter only:
+// vector-memory loads in flight, such as prefetched stages, stay in flight).  gfx9 s_waitcnt
+// encoding: vmcnt and expcnt at their maxima, lgkmcnt = 0.
+__device__ __forceinline__ void lds_barrier_lds_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

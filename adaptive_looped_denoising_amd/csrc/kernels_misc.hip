@@ -151,13 +151,14 @@ __global__ __launch_bounds__(256) void k_exit_gate(const T* __restrict__ rows, i
 // layout change of q/k/v.  One wave per (row, head); lane p owns the pair (p, p + hd/2).
 // K/V element (row r, kv head h, e) goes to kv + (seq0 + r / n)*sSeq + h*sHead + (r % n)*sPos + e.
 // SPLITS (compile time, 0 = runtime `splits`): split-K partials of the projection to add.
-template <typename TW, typename TA, int SPLITS>
+// TKV: storage type of the keys and values (the activation type, or FP8 E4M3).
+template <typename TW, typename TA, typename TKV, int SPLITS>
 __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ qkv, int n_rows, int rows_per_seq,
                                                       int pos0, int Hq, int Hkv, int hd,
                                                       const TW* __restrict__ qn, const TW* __restrict__ kn,
                                                       float eps, const float* __restrict__ cosT,
                                                       const float* __restrict__ sinT, TA* __restrict__ q_out,
-                                                      TA* __restrict__ k_out, TA* __restrict__ v_out,
+                                                      TKV* __restrict__ k_out, TKV* __restrict__ v_out,
                                                       int64_t kSeq, int64_t kHead, int64_t kPos, int64_t vSeq,
                                                       int64_t vHead, int64_t vRow, int seq0, int splits_rt) {
   const int splits = SPLITS > 0 ? SPLITS : splits_rt;
@@ -185,8 +186,8 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
   const size_t seq = (size_t)(seq0 + r / rows_per_seq);
   if (hh >= Hq + Hkv) {  // value head: copy, transposed (positions contiguous)
     const int h = hh - Hq - Hkv;
-    TA* dst = v_out + seq * vSeq + (size_t)h * vHead + jpos;
-    for (int e = lane; e < hd; e += 64) dst[(size_t)e * vRow] = from_f<TA>(val(e));
+    TKV* dst = v_out + seq * vSeq + (size_t)h * vHead + jpos;
+    for (int e = lane; e < hd; e += 64) dst[(size_t)e * vRow] = from_f<TKV>(val(e));
     return;
   }
   const size_t kv_off = seq * kSeq + (size_t)jpos * kPos;
@@ -206,7 +207,8 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
-  TA* dst = is_q ? q_out + ((size_t)r * Hq + hh) * hd : k_out + kv_off + (size_t)(hh - Hq) * kHead;
+  TA* dq = q_out + ((size_t)r * Hq + hh) * hd;
+  TKV* dk = k_out + kv_off + (size_t)(hh - Hq) * kHead;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int p = lane + 64 * t;
@@ -214,8 +216,14 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
       const float a = x1[t] * inv * to_f(g[p]);
       const float b = x2[t] * inv * to_f(g[p + half]);
       const float c = cosT[(size_t)pos * half + p], s = sinT[(size_t)pos * half + p];
-      dst[p] = from_f<TA>(a * c - b * s);
-      dst[p + half] = from_f<TA>(b * c + a * s);
+      const float lo = a * c - b * s, hi = b * c + a * s;
+      if (is_q) {
+        dq[p] = from_f<TA>(lo);
+        dq[p + half] = from_f<TA>(hi);
+      } else {
+        dk[p] = from_f<TKV>(lo);
+        dk[p + half] = from_f<TKV>(hi);
+      }
     }
   }
 }
@@ -609,14 +617,19 @@ void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_s
                          int hd, const void* qn, const void* kn, float eps, const float* cosT,
                          const float* sinT, void* q_out, void* k_out, void* v_out, int64_t kSeq, int64_t kHead,
                          int64_t kPos, int64_t vSeq, int64_t vHead, int64_t vRow, int seq0, hipStream_t st,
-                         int splits) {
+                         int splits, int kv_type) {
   if (n_rows <= 0) return;
   const int waves = n_rows * (Hq + 2 * Hkv);
-#define QKR_GO(S)                                                                                 \
-  DISPATCH_T(dtype, T,                                                                            \
-             k_qk_norm_rope<T, T, S><<<(waves + 3) / 4, 256, 0, st>>>(                            \
-                 qkv, n_rows, rows_per_seq, pos0, Hq, Hkv, hd, (const T*)qn, (const T*)kn, eps, cosT, sinT, \
-                 (T*)q_out, (T*)k_out, (T*)v_out, kSeq, kHead, kPos, vSeq, vHead, vRow, seq0, splits))
+#define QKR_LAUNCH(T, TKV, S)                                                                      \
+  k_qk_norm_rope<T, T, TKV, S><<<(waves + 3) / 4, 256, 0, st>>>(                                 \
+      qkv, n_rows, rows_per_seq, pos0, Hq, Hkv, hd, (const T*)qn, (const T*)kn, eps, cosT, sinT, (T*)q_out, \
+      (TKV*)k_out, (TKV*)v_out, kSeq, kHead, kPos, vSeq, vHead, vRow, seq0, splits)
+#define QKR_GO(S)                                   \
+  if (kv_type == DT_FP8) {                          \
+    QKR_LAUNCH(bf16_t, fp8_t, S);                   \
+  } else {                                          \
+    DISPATCH_T(dtype, T, QKR_LAUNCH(T, T, S));      \
+  }
   if (splits <= 1) {
     QKR_GO(1);
   } else if (splits == 2) {
@@ -627,6 +640,7 @@ void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_s
     QKR_GO(0);
   }
 #undef QKR_GO
+#undef QKR_LAUNCH
 }
 
 void launch_swiglu(int dtype, const float* gu, int n_rows, int F, void* act, hipStream_t st) {

@@ -5,7 +5,7 @@
 
 namespace alodlm {
 
-enum { DT_BF16 = 0, DT_FP32 = 1 };
+enum { DT_BF16 = 0, DT_FP32 = 1, DT_FP8 = 2 };  // DT_FP8: K/V storage only (OCP E4M3)
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SOFTSTAT = 2, EPI_SWIGLU = 3 };
 
 struct SoftStat;
@@ -61,6 +61,7 @@ struct AttnParams {
   // causal: query row i sees own key jj iff jj <= i + causal_off (rows appended after
   // causal_off own keys that are already in place)
   int n_self = 0, causal = 0, s_seq0 = 0, causal_off = 0;
+  int kv8 = 0;  // keys and values (cache and own) stored in FP8 E4M3 (matrix-core path, hd 64 / 128)
   // fast path scratch: split-KV partials
   float* part = nullptr;
   int n_split = 1;
@@ -82,7 +83,7 @@ void launch_exit_gate(int dtype, const void* rows, int n_rows, int d, const void
 void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_seq, int pos0, int Hq, int Hkv,
                          int hd, const void* qn, const void* kn, float eps, const float* cosT, const float* sinT,
                          void* q_out, void* k_out, void* v_out, int64_t kSeq, int64_t kHead, int64_t kPos,
-                         int64_t vSeq, int64_t vHead, int64_t vRow, int seq0, hipStream_t st, int splits = 1);
+                         int64_t vSeq, int64_t vHead, int64_t vRow, int seq0, hipStream_t st, int splits = 1, int kv_type = -1);
 void launch_swiglu(int dtype, const float* gu, int n_rows, int F, void* act, hipStream_t st);
 // gpart (optional): partial Gumbel-max draws merged into stok (the sampled token of each row).
 void launch_softstat_combine(const SoftStat* part, int n_rows, int n_tiles, const int32_t* n_dev, float* H,

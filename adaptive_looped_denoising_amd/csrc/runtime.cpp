@@ -42,6 +42,8 @@ struct Plan {
 };
 
 size_t esize(int dtype) { return dtype == ALODLM_DTYPE_BF16 ? 2 : 4; }
+// bytes per stored key / value element
+size_t kv_esize(const alodlm_config& c) { return c.kv_dtype == ALODLM_KV_FP8 ? 1 : esize(c.dtype); }
 
 int check_config(const alodlm_config* c, std::string* err) {
   char buf[256];
@@ -70,6 +72,9 @@ int check_config(const alodlm_config* c, std::string* err) {
   if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps)) return bad("rms_eps");
   if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return bad("rope_theta");
   if (c->depth_on_demand != 0 && c->depth_on_demand != 1) return bad("depth_on_demand must be 0 or 1");
+  if (c->kv_dtype != ALODLM_KV_SAME && c->kv_dtype != ALODLM_KV_FP8) return bad("kv_dtype");
+  if (c->kv_dtype == ALODLM_KV_FP8 && (c->dtype != ALODLM_DTYPE_BF16 || (c->head_dim != 64 && c->head_dim != 128)))
+    return bad("fp8 keys and values need the bf16 dtype and head_dim 64 or 128");
   return ALODLM_OK;
 }
 
@@ -98,8 +103,9 @@ Plan make_plan(const alodlm_config& c) {
   };
   p.rope_cos = take(sizeof(float) * p.max_pos * (hd / 2));
   p.rope_sin = take(sizeof(float) * p.max_pos * (hd / 2));
-  p.kcache = take(es * p.slot_elems * p.n_slots);
-  p.vcache = take(es * p.slot_elems * p.n_slots);
+  const size_t kes = kv_esize(c);
+  p.kcache = take(kes * p.slot_elems * p.n_slots);
+  p.vcache = take(kes * p.slot_elems * p.n_slots);
   p.av_pitch = P > 0 ? (int)P : 1;
   p.avail = take(B * p.av_pitch);
   p.h = take(sizeof(float) * R * d);
@@ -108,8 +114,8 @@ Plan make_plan(const alodlm_config& c) {
   p.attn = take(es * R * Hq * hd);
   p.qkv = take(sizeof(float) * R * qkv_out);
   p.q = take(es * R * Hq * hd);
-  p.kself = take(es * Rs * Hkv * hd);
-  p.vself = take(es * B * Hkv * hd * p.Lp);
+  p.kself = take(kes * Rs * Hkv * hd);
+  p.vself = take(kes * B * Hkv * hd * p.Lp);
   p.gu = take(sizeof(float) * R * 2 * F);
   p.act = take(es * R * F);
   p.r = take(es * Rs * d);
@@ -233,9 +239,11 @@ namespace {
 int dt(const alodlm_ctx* c) { return c->cfg.dtype == ALODLM_DTYPE_BF16 ? DT_BF16 : DT_FP32; }
 
 void* cache_slot(alodlm_ctx* c, bool v, int slot) {
-  const size_t es = esize(c->cfg.dtype);
-  return c->ws + (v ? c->plan.vcache : c->plan.kcache) + es * (size_t)c->plan.slot_elems * slot;
+  return c->ws + (v ? c->plan.vcache : c->plan.kcache) + kv_esize(c->cfg) * (size_t)c->plan.slot_elems * slot;
 }
+
+// storage type of keys and values (DT_FP8, or the model dtype)
+int kvt(const alodlm_ctx* c) { return c->cfg.kv_dtype == ALODLM_KV_FP8 ? DT_FP8 : dt(c); }
 
 int slot_of(const alodlm_config& c, int layer, int depth) {
   if (layer < c.n_pre) return layer;
@@ -277,8 +285,10 @@ int lm_tiles(const alodlm_ctx* c, int M) {
 }
 
 void attention(alodlm_ctx* c, const AttnParams& p) {
-  if (c->cfg.dtype == ALODLM_DTYPE_BF16 && !c->force_generic && attn_mfma_supported(p.hd)) {
+  const bool kv8 = c->cfg.kv_dtype == ALODLM_KV_FP8;  // fp8 keys and values: matrix-core path only
+  if (c->cfg.dtype == ALODLM_DTYPE_BF16 && (kv8 || !c->force_generic) && attn_mfma_supported(p.hd)) {
     AttnParams q = p;
+    q.kv8 = kv8 ? 1 : 0;
     q.part = c->at<float>(c->plan.attn_part);
     launch_attn_mfma(q, c->plan.attn_splits, c->st, c->attn_force_splits, c->attn_force_qw, c->attn_force_ns,
                      c->attn_force_nw);
@@ -361,12 +371,12 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
     void* vd = cache_slot(c, true, slot);
     const int64_t kSeq = (int64_t)Hkv * Pp * hd, kHead = Pp * hd, kPos = hd;
     const int64_t vSeq = (int64_t)Hkv * hd * Pp, vHead = hd * Pp, vRow = Pp;
-    const size_t es_ = esize(g.dtype);
+    const size_t es_ = kv_esize(g);
     c->tic(ALODLM_K_NORM_ROPE);
     launch_qk_norm_rope(dt(c), qkv_src, n, lc.rows_per_seq, lc.pos0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
                         c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q,
                         (char*)kd + (size_t)lc.pos0 * kPos * es_, (char*)vd + (size_t)lc.pos0 * es_, kSeq, kHead,
-                        kPos, vSeq, vHead, vRow, lc.seq0, c->st, qkv_splits);
+                        kPos, vSeq, vHead, vRow, lc.seq0, c->st, qkv_splits, kvt(c));
     c->toc();
     ap.n_cache = 0;
     ap.sk = kd;
@@ -389,7 +399,7 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
     c->tic(ALODLM_K_NORM_ROPE);
     launch_qk_norm_rope(dt(c), qkv_src, n, lc.rows_per_seq, lc.pos0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
                         c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q, ks, vs, kSeq, kHead, kPos, vSeq, vHead,
-                        vRow, 0, c->st, qkv_splits);
+                        vRow, 0, c->st, qkv_splits, kvt(c));
     c->toc();
     // Core layers read the depth plane of the loop: the planes are materialised after the prefill
     // (plane s holds every position at depth min(s, available depth))
@@ -578,7 +588,7 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
   hipError_t e2 = hipMemcpyAsync(c->ws + plan.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, c->st);
   // V rows are read in whole 64-key tiles whose masked keys get probability 0; their padding must
   // hold finite values (0 * NaN would poison the sum), so the V cache and own-block V start at zero
-  const size_t es = esize(cfg->dtype);
+  const size_t es = kv_esize(*cfg);
   if (e1 == hipSuccess) e1 = hipMemsetAsync(c->ws + plan.vcache, 0, es * plan.slot_elems * plan.n_slots, c->st);
   if (e1 == hipSuccess)
     e1 = hipMemsetAsync(c->ws + plan.vself, 0, es * (size_t)cfg->max_batch * cfg->n_kv_heads * cfg->head_dim * plan.Lp,
@@ -602,7 +612,7 @@ void materialize_depths(alodlm_ctx* c, int batch, int j0, int n) {
   const Plan& p = c->plan;
   for (int ci = 0; ci < g.n_core; ++ci) {
     const int s0 = slot_of(g, g.n_pre + ci, 1);
-    launch_materialize_depth(dt(c), cache_slot(c, false, s0), cache_slot(c, true, s0), p.slot_elems, g.k_max, batch,
+    launch_materialize_depth(kvt(c), cache_slot(c, false, s0), cache_slot(c, true, s0), p.slot_elems, g.k_max, batch,
                              g.n_kv_heads, j0, n, (int)p.Pp, g.head_dim, c->at<uint8_t>(p.avail), p.av_pitch, c->st);
   }
 }
@@ -728,9 +738,9 @@ int alodlm_prefill_kv_synthetic(alodlm_ctx* c, int32_t batch, int32_t prefix_len
   c->built_depth = -1;
   launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, avail_depth, (uint8_t)g.k_max, c->st);
   for (int s = 0; s < p.n_slots; ++s) {
-    launch_fill_kv_synth(dt(c), cache_slot(c, false, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,
+    launch_fill_kv_synth(kvt(c), cache_slot(c, false, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,
                          seed, 0x10000u + 2u * s, k_scale, false, c->st);
-    launch_fill_kv_synth(dt(c), cache_slot(c, true, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,
+    launch_fill_kv_synth(kvt(c), cache_slot(c, true, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,
                          seed, 0x10000u + 2u * s + 1u, v_scale, true, c->st);
   }
   if (prefix_len > 0) materialize_depths(c, batch, 0, prefix_len);
@@ -1046,7 +1056,7 @@ int alodlm_diag_read_kv(const alodlm_ctx* c, int32_t slot, int32_t b, int32_t j0
   if (slot < 0 || slot >= c->plan.n_slots || b < 0 || b >= g.max_batch || j0 < 0 || n < 0 ||
       j0 + n > g.max_prefix)
     return ALODLM_EINVAL;
-  const size_t es = esize(g.dtype), hd = g.head_dim, Pp = (size_t)c->plan.Pp;
+  const size_t es = kv_esize(g), hd = g.head_dim, Pp = (size_t)c->plan.Pp;
   const char* kbase = c->ws + c->plan.kcache + es * (size_t)c->plan.slot_elems * slot;
   for (int h = 0; h < g.n_kv_heads; ++h) {
     const char* src = kbase + es * (((size_t)b * g.n_kv_heads + h) * Pp + j0) * hd;
@@ -1054,7 +1064,8 @@ int alodlm_diag_read_kv(const alodlm_ctx* c, int32_t slot, int32_t b, int32_t j0
     if (hipMemcpyAsync(dst, src, es * n * hd, hipMemcpyDeviceToDevice, c->st) != hipSuccess) return ALODLM_EHIP;
   }
   const char* vbase = c->ws + c->plan.vcache + es * (size_t)c->plan.slot_elems * slot;
-  launch_read_v_rows(g.dtype == ALODLM_DTYPE_BF16 ? DT_BF16 : DT_FP32, vbase, b, g.n_kv_heads, (int)Pp, (int)hd, j0,
+  launch_read_v_rows(g.kv_dtype == ALODLM_KV_FP8 ? DT_FP8 : (g.dtype == ALODLM_DTYPE_BF16 ? DT_BF16 : DT_FP32), vbase, b,
+                     g.n_kv_heads, (int)Pp, (int)hd, j0,
                      n, dst_v, c->st);
   return hipGetLastError() == hipSuccess ? ALODLM_OK : ALODLM_EHIP;
 }

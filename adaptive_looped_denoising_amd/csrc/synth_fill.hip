@@ -46,7 +46,10 @@ void launch_fill_kv_synth(int dtype, void* slot_base, int B, int Hkv, int P, int
   const uint64_t n = (uint64_t)B * Hkv * P * hd;
   if (!n) return;
   const unsigned grid = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
-  if (dtype == DT_BF16)
+  if (dtype == DT_FP8)  // the float32 draw rounded once to E4M3
+    k_fill_kv_synth<fp8_t><<<grid, 256, 0, st>>>((fp8_t*)slot_base, B, Hkv, P, P_pitch, hd, seed, tensor, scale,
+                                                 transposed ? 1 : 0);
+  else if (dtype == DT_BF16)
     k_fill_kv_synth<bf16_t><<<grid, 256, 0, st>>>((bf16_t*)slot_base, B, Hkv, P, P_pitch, hd, seed, tensor, scale,
                                                   transposed ? 1 : 0);
   else
@@ -87,7 +90,10 @@ void launch_materialize_depth(int dtype, void* k_plane0, void* v_plane0, int64_t
   const uint64_t n = (uint64_t)B * Hkv * n_pos * hd;
   if (!n || k_max < 2) return;
   const unsigned grid = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
-  if (dtype == DT_BF16)
+  if (dtype == DT_FP8)
+    k_materialize_depth<fp8_t><<<grid, 256, 0, st>>>((fp8_t*)k_plane0, (fp8_t*)v_plane0, plane_elems, k_max, B,
+                                                     Hkv, j0, n_pos, P_pitch, hd, avail, av_pitch);
+  else if (dtype == DT_BF16)
     k_materialize_depth<bf16_t><<<grid, 256, 0, st>>>((bf16_t*)k_plane0, (bf16_t*)v_plane0, plane_elems, k_max, B,
                                                       Hkv, j0, n_pos, P_pitch, hd, avail, av_pitch);
   else
@@ -112,7 +118,9 @@ void launch_read_v_rows(int dtype, const void* slot_base, int b, int Hkv, int P_
   const size_t total = (size_t)Hkv * n * hd;
   if (!total) return;
   const unsigned grid = (unsigned)((total + 255) / 256);
-  if (dtype == DT_BF16)
+  if (dtype == DT_FP8)
+    k_read_v_rows<fp8_t><<<grid, 256, 0, st>>>((const fp8_t*)slot_base, b, Hkv, P_pitch, hd, j0, n, (fp8_t*)dst);
+  else if (dtype == DT_BF16)
     k_read_v_rows<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)slot_base, b, Hkv, P_pitch, hd, j0, n, (bf16_t*)dst);
   else
     k_read_v_rows<float><<<grid, 256, 0, st>>>((const float*)slot_base, b, Hkv, P_pitch, hd, j0, n, (float*)dst);

@@ -85,7 +85,7 @@ class Engine:
             max_prefill_rows=max_prefill_rows if max_prefill_rows is not None else min(
                 w.batch * w.prefix, max(w.prefix, 8192)),
             mask_id=w.mask_id, dtype=self.cdtype, rms_eps=w.rms_eps, rope_theta=w.rope_theta,
-            depth_on_demand=1 if depth_on_demand else 0)
+            depth_on_demand=1 if depth_on_demand else 0, kv_dtype=B.KV_FP8 if w.kv_dtype == "fp8" else B.KV_SAME)
         nl = D.n_layers
         self.layer_arr = (B.LayerWeights * max(nl, 1))()
         for l in range(nl):
@@ -240,13 +240,15 @@ class Engine:
         return res
 
     def read_kv(self, slot: int, b: int, j0: int, n: int):
-        """K and V rows of one cache slot and sequence, as float32 numpy arrays [Hkv][n][hd]."""
+        """K and V rows of one cache slot and sequence, as float32 numpy arrays [Hkv][n][hd] (fp8
+        storage decoded by torch's float8_e4m3fn)."""
         D = self.w.dims
-        k = torch.empty((D.n_kv_heads, n, D.head_dim), dtype=self.tdtype, device=self.device)
+        kdt = torch.float8_e4m3fn if self.w.kv_dtype == "fp8" else self.tdtype
+        k = torch.empty((D.n_kv_heads, n, D.head_dim), dtype=kdt, device=self.device)
         v = torch.empty_like(k)
         B.read_kv(self.ctx, slot, b, j0, n, k.data_ptr(), v.data_ptr())
         torch.cuda.synchronize(self.device)
-        return k.float().cpu().numpy(), v.float().cpu().numpy()
+        return k.cpu().float().numpy(), v.cpu().float().numpy()
 
     def stats(self):
         return B.last_step_stats(self.ctx)

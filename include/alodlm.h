@@ -57,6 +57,14 @@ extern "C" {
 #define ALODLM_DTYPE_BF16 0 /* bf16 weights, KV and GEMM inputs; fp32 accumulate, residual and heads */
 #define ALODLM_DTYPE_FP32 1 /* fp32 everywhere */
 
+/* Storage of keys and values (prefix cache and a block's own).  FP8: the OCP FP8 E4M3 format
+ * (sign, 4 exponent bits with bias 7, 3 fraction bits, largest finite 448), rounded once from the
+ * float32 result to nearest even, saturating; half the bytes of bf16 -- the compressed depth
+ * buffers of the page "ALoDLM: Adaptively Looped Diffusion Language Models", section
+ * "Limitations".  FP8 needs the bf16 dtype and head_dim 64 or 128. */
+#define ALODLM_KV_SAME 0    /* keys and values in the config dtype */
+#define ALODLM_KV_FP8 2
+
 /* Model and capacity description. */
 typedef struct alodlm_config {
   int32_t vocab;        /* V */
@@ -80,6 +88,7 @@ typedef struct alodlm_config {
   int32_t depth_on_demand; /* 1: the workspace also keeps the prefix's Core output
                               ([max_batch][max_prefix][d] fp32) so that alodlm_prefill_kv_depth /
                               alodlm_deepen_kv can build the cache depth by depth; 0: not */
+  int32_t kv_dtype;     /* ALODLM_KV_SAME or ALODLM_KV_FP8 */
 } alodlm_config;
 
 /* One transformer layer (Qwen3 block).  Device pointers in the config dtype,
