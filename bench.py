@@ -145,21 +145,22 @@ def main():
     progress("prefill %.1f ms (depth 1 first: %.1f ms, then deepening to %d: %.1f ms)" % (
         prefill_ms, prefill_d1_ms, w.k_max, deepen_ms))
 
-    def timed(tau, steps, warmup, sample=None):
-        a = e.make_args(tau_ent=tau, sample=sample)
-        o = e.make_out(a.k_loops)
+    def timed(tau, steps, warmup, sample=None, engine=None):
+        e_ = e if engine is None else engine
+        a = e_.make_args(tau_ent=tau, sample=sample)
+        o = e_.make_out(a.k_loops)
         for _ in range(warmup):
-            e.run(a, o)
+            e_.run(a, o)
         torch.cuda.synchronize()
         committed = 0
         loops = []
         t = time.perf_counter()
         for _ in range(steps):
-            e.run(a, o)
+            e_.run(a, o)
             committed += o.n_committed
         torch.cuda.synchronize()
         el = time.perf_counter() - t
-        loops = e.out_loops.cpu().numpy().astype(int).tolist()
+        loops = e_.out_loops.cpu().numpy().astype(int).tolist()
         return dict(tok_s=committed / el, ms_per_step=el / steps * 1e3, committed_per_step=committed / steps,
                     loops=loops)
 
@@ -210,6 +211,26 @@ def main():
                  append_rows_per_s=w.batch * w.block / ext_s,
                  append_layer_calls=D.n_pre + w.k_max * D.n_core + D.n_coda)
     progress("outer loop: %s" % outer)
+    # fp8 (E4M3) keys and values: the same step on a second engine whose cache and own-block K/V
+    # are stored in one byte per element
+    e.close()
+    del e
+    torch.cuda.empty_cache()
+    progress("fp8 K/V engine")
+    e8 = Engine(replace(w, kv_dtype="fp8"))
+    e8.prefill()
+    f8 = timed(w.tau_ent, args.steps, args.warmup, engine=e8)
+    B.timing_enable(e8.ctx, True)
+    timed(w.tau_ent, args.steps, 0, engine=e8)
+    kt8 = B.timing_read(e8.ctx)
+    B.timing_enable(e8.ctx, False)
+    kv_bytes = 2 * D.kv_slots(w.k_max) * w.batch * w.prefix * D.n_kv_heads * D.head_dim
+    kv_fp8 = dict(tok_s=f8["tok_s"], ms_per_step=f8["ms_per_step"], committed_per_step=f8["committed_per_step"],
+                  attention_ms_per_step=kt8["attention"][0] / args.steps,
+                  attention_ms_per_step_bf16=kt["attention"][0] / args.steps,
+                  cache_bytes=kv_bytes, cache_bytes_bf16=2 * kv_bytes)
+    progress("fp8 K/V: %s" % kv_fp8)
+    e8.close()
     kernels = {}
     for k, v in kt.items():
         ms = v[0] / args.steps
@@ -247,6 +268,7 @@ def main():
         "tau_sweep": sweep,
         "sampled_commits": sampled,
         "outer_loop": outer,
+        "kv_fp8": kv_fp8,
         "prefill_ms": prefill_ms,
         "prefill_depth_on_demand": {"depth1_ms": prefill_d1_ms, "deepen_to_kmax_ms": deepen_ms,
                                     "prefix_tokens": w.batch * w.prefix},

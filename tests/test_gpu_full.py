@@ -199,6 +199,13 @@ def test_qwen3_8b_sampled_commits(gpu_lib):
     e.close()
 
 
+def test_qwen3_8b_fp8_kv_step(gpu_lib):
+    """fp8 (E4M3) keys and values at the 8B shape over the synthetic cache."""
+    w = synth.workload("qwen3_8b", kv="synthetic", kv_dtype="fp8")
+    e, _, _ = _check_step(w, [1])
+    e.close()
+
+
 def test_qwen3_8b_long_context_step(gpu_lib):
     w = synth.workload("qwen3_8b_long")
     e, _, _ = _check_step(w, [5])
