@@ -83,7 +83,7 @@ class Engine:
             ffn=D.ffn, n_pre=D.n_pre, n_core=D.n_core, n_coda=D.n_coda, k_max=w.k_max, max_batch=w.batch,
             max_prefix=max(w.prefix, max_prefix or 0), max_block=w.block,
             max_prefill_rows=max_prefill_rows if max_prefill_rows is not None else min(
-                w.batch * w.prefix, max(w.prefix, 8192)),
+                w.batch * max(w.prefix, max_prefix or 0), max(w.prefix, max_prefix or 0, 8192)),
             mask_id=w.mask_id, dtype=self.cdtype, rms_eps=w.rms_eps, rope_theta=w.rope_theta,
             depth_on_demand=1 if depth_on_demand else 0, kv_dtype=B.KV_FP8 if w.kv_dtype == "fp8" else B.KV_SAME)
         nl = D.n_layers
