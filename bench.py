@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="report the step (headline, tau sweep, kernel classes) only: no depth-on-demand prefill, "
+                         "sampled commits, outer loop or fp8 K/V sections (for profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (known traffic, for calibrating HBM counters)")
     args = ap.parse_args()
@@ -130,19 +133,21 @@ def main():
     torch.cuda.synchronize()
     # first-token latency: the depth-on-demand build (depth 1), its deepening to K, then the full
     # prefill that the timed steps use
-    e.prefill(depth=1)   # warm-up (first launches of every prefill kernel)
-    t0 = time.perf_counter()
-    e.prefill(depth=1)
-    prefill_d1_ms = (time.perf_counter() - t0) * 1e3
-    t0 = time.perf_counter()
-    e.deepen(w.k_max)
-    deepen_ms = (time.perf_counter() - t0) * 1e3
+    prefill_d1_ms = deepen_ms = None
+    if not args.step_only:
+        e.prefill(depth=1)   # warm-up (first launches of every prefill kernel)
+        t0 = time.perf_counter()
+        e.prefill(depth=1)
+        prefill_d1_ms = (time.perf_counter() - t0) * 1e3
+        t0 = time.perf_counter()
+        e.deepen(w.k_max)
+        deepen_ms = (time.perf_counter() - t0) * 1e3
     progress("prefill")
     t0 = time.perf_counter()
     e.prefill()
     torch.cuda.synchronize()
     prefill_ms = (time.perf_counter() - t0) * 1e3
-    progress("prefill %.1f ms (depth 1 first: %.1f ms, then deepening to %d: %.1f ms)" % (
+    progress("prefill %.1f ms (depth 1 first: %s ms, then deepening to %d: %s ms)" % (
         prefill_ms, prefill_d1_ms, w.k_max, deepen_ms))
 
     def timed(tau, steps, warmup, sample=None, engine=None):
@@ -184,53 +189,55 @@ def main():
     traffic = ffn_gate_up_traffic(w, rows_per_step * args.steps, launches)
     achieved = traffic / (per_launch_ms * 1e-3) / 1e9
     work = algorithmic_work(w, loops)
-    # Sampled commits (Gumbel-max draws in the LM-head epilogue): the same step and timing pass
-    # with ALODLM_STEP_SAMPLE, reported beside the greedy headline.
-    samp = timed(w.tau_ent, args.steps, 1, sample=dict(seed=2024, step=0))
-    B.timing_enable(e.ctx, True)
-    samp_prof = timed(w.tau_ent, args.steps, 0, sample=dict(seed=2024, step=0))
-    skt = B.timing_read(e.ctx)
-    B.timing_enable(e.ctx, False)
-    progress("sampled commits: %s" % samp)
-    sampled = dict(tok_s=samp["tok_s"], ms_per_step=samp["ms_per_step"], committed_per_step=samp["committed_per_step"],
-                   lm_head_ms_per_step=skt["lm_head"][0] / args.steps,
-                   lm_head_ms_per_step_greedy=kt["lm_head"][0] / args.steps,
-                   timing_pass_ms_per_step=samp_prof["ms_per_step"])
-    # Outer loop: the whole block decoded (steps until no [MASK]), then appended to the cache
-    # (the cache grows by one block, so this runs last).
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    blk = e.denoise_block(tau_ent=w.tau_ent)
-    blk_s = time.perf_counter() - t0
-    masked = int((synth.block_ids(w) == w.mask_id).sum())
-    t0 = time.perf_counter()
-    e.extend(blk["tokens"])
-    ext_s = time.perf_counter() - t0
-    outer = dict(masked_tokens=masked, committed=blk["n_committed"], steps=blk["n_steps"], ms=blk_s * 1e3,
-                 tok_s=blk["n_committed"] / blk_s, append_ms=ext_s * 1e3,
-                 append_rows_per_s=w.batch * w.block / ext_s,
-                 append_layer_calls=D.n_pre + w.k_max * D.n_core + D.n_coda)
-    progress("outer loop: %s" % outer)
-    # fp8 (E4M3) keys and values: the same step on a second engine whose cache and own-block K/V
-    # are stored in one byte per element
-    e.close()
-    del e
-    torch.cuda.empty_cache()
-    progress("fp8 K/V engine")
-    e8 = Engine(replace(w, kv_dtype="fp8"))
-    e8.prefill()
-    f8 = timed(w.tau_ent, args.steps, args.warmup, engine=e8)
-    B.timing_enable(e8.ctx, True)
-    timed(w.tau_ent, args.steps, 0, engine=e8)
-    kt8 = B.timing_read(e8.ctx)
-    B.timing_enable(e8.ctx, False)
-    kv_bytes = 2 * D.kv_slots(w.k_max) * w.batch * w.prefix * D.n_kv_heads * D.head_dim
-    kv_fp8 = dict(tok_s=f8["tok_s"], ms_per_step=f8["ms_per_step"], committed_per_step=f8["committed_per_step"],
-                  attention_ms_per_step=kt8["attention"][0] / args.steps,
-                  attention_ms_per_step_bf16=kt["attention"][0] / args.steps,
-                  cache_bytes=kv_bytes, cache_bytes_bf16=2 * kv_bytes)
-    progress("fp8 K/V: %s" % kv_fp8)
-    e8.close()
+    sampled = outer = kv_fp8 = None
+    if not args.step_only:
+        # Sampled commits (Gumbel-max draws in the LM-head epilogue): the same step and timing pass
+        # with ALODLM_STEP_SAMPLE, reported beside the greedy headline.
+        samp = timed(w.tau_ent, args.steps, 1, sample=dict(seed=2024, step=0))
+        B.timing_enable(e.ctx, True)
+        samp_prof = timed(w.tau_ent, args.steps, 0, sample=dict(seed=2024, step=0))
+        skt = B.timing_read(e.ctx)
+        B.timing_enable(e.ctx, False)
+        progress("sampled commits: %s" % samp)
+        sampled = dict(tok_s=samp["tok_s"], ms_per_step=samp["ms_per_step"], committed_per_step=samp["committed_per_step"],
+                       lm_head_ms_per_step=skt["lm_head"][0] / args.steps,
+                       lm_head_ms_per_step_greedy=kt["lm_head"][0] / args.steps,
+                       timing_pass_ms_per_step=samp_prof["ms_per_step"])
+        # Outer loop: the whole block decoded (steps until no [MASK]), then appended to the cache
+        # (the cache grows by one block, so this runs last).
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        blk = e.denoise_block(tau_ent=w.tau_ent)
+        blk_s = time.perf_counter() - t0
+        masked = int((synth.block_ids(w) == w.mask_id).sum())
+        t0 = time.perf_counter()
+        e.extend(blk["tokens"])
+        ext_s = time.perf_counter() - t0
+        outer = dict(masked_tokens=masked, committed=blk["n_committed"], steps=blk["n_steps"], ms=blk_s * 1e3,
+                     tok_s=blk["n_committed"] / blk_s, append_ms=ext_s * 1e3,
+                     append_rows_per_s=w.batch * w.block / ext_s,
+                     append_layer_calls=D.n_pre + w.k_max * D.n_core + D.n_coda)
+        progress("outer loop: %s" % outer)
+        # fp8 (E4M3) keys and values: the same step on a second engine whose cache and own-block K/V
+        # are stored in one byte per element
+        e.close()
+        del e
+        torch.cuda.empty_cache()
+        progress("fp8 K/V engine")
+        e8 = Engine(replace(w, kv_dtype="fp8"))
+        e8.prefill()
+        f8 = timed(w.tau_ent, args.steps, args.warmup, engine=e8)
+        B.timing_enable(e8.ctx, True)
+        timed(w.tau_ent, args.steps, 0, engine=e8)
+        kt8 = B.timing_read(e8.ctx)
+        B.timing_enable(e8.ctx, False)
+        kv_bytes = 2 * D.kv_slots(w.k_max) * w.batch * w.prefix * D.n_kv_heads * D.head_dim
+        kv_fp8 = dict(tok_s=f8["tok_s"], ms_per_step=f8["ms_per_step"], committed_per_step=f8["committed_per_step"],
+                      attention_ms_per_step=kt8["attention"][0] / args.steps,
+                      attention_ms_per_step_bf16=kt["attention"][0] / args.steps,
+                      cache_bytes=kv_bytes, cache_bytes_bf16=2 * kv_bytes)
+        progress("fp8 K/V: %s" % kv_fp8)
+        e8.close()
     kernels = {}
     for k, v in kt.items():
         ms = v[0] / args.steps
@@ -270,8 +277,8 @@ def main():
         "outer_loop": outer,
         "kv_fp8": kv_fp8,
         "prefill_ms": prefill_ms,
-        "prefill_depth_on_demand": {"depth1_ms": prefill_d1_ms, "deepen_to_kmax_ms": deepen_ms,
-                                    "prefix_tokens": w.batch * w.prefix},
+        "prefill_depth_on_demand": None if args.step_only else {
+            "depth1_ms": prefill_d1_ms, "deepen_to_kmax_ms": deepen_ms, "prefix_tokens": w.batch * w.prefix},
         # per class: event-timed ms (the event pairs add a little time to short kernels, so the
         # fractions are lower bounds) with algorithmic bytes / flops and their roofline fractions
         "kernels": kernels,
