@@ -1013,8 +1013,10 @@ static const TileCfg kTiles[] = {
     {128, 192, 4}, {256, 128, 2}, {128, 128, 4}, {256, 64, 2}, {64, 192, 4}, {128, 192, 4}, {128, 128, 4},
     {128, 128, 4}, {128, 256, 4}, {64, 128, 4}, {64, 256, 4}, {128, 192, 2}, {128, 192, 2},
     // eight waves, wave-specialised loads (activation stream DA deep, weight stream DB deep)
-    {128, 192, 2}, {128, 192, 2}, {128, 192, 2}, {128, 128, 4}, {128, 128, 4}, {64, 128, 4}, {256, 128, 2}};
-constexpr int kNumTiles = 56;
+    {128, 192, 2}, {128, 192, 2}, {128, 192, 2}, {128, 128, 4}, {128, 128, 4}, {64, 128, 4}, {256, 128, 2},
+    // eight waves, deeper LDS ring
+    {128, 192, 2}, {128, 128, 4}, {128, 192, 4}};
+constexpr int kNumTiles = 59;
 
 bool swiglu_single_pass_ok(int tile) { return ((kTiles[tile].bn / kTiles[tile].wn / 16) & 1) == 0; }
 
@@ -1036,7 +1038,7 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   if (M <= 384) {
     *splits = 1;
     if (epi == EPI_SOFTSTAT) return M <= 128 ? 47 : 37;  // LM head: wide weight tiles, few activation re-reads
-    if (epi == EPI_SWIGLU) return M <= 64 ? 45 : (M <= 128 ? 18 : 47);
+    if (epi == EPI_SWIGLU) return M <= 64 ? 45 : (M <= 128 ? 18 : 56);
     // projections (QKV, O, FFN down): split-K 4 over the eight-wave tiles
     *splits = 4;
     if (M <= 128) return (M <= 64 || N <= 4096) ? 45 : 18;
@@ -1174,6 +1176,10 @@ int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, in
     case 54: W(64, 128, 2, 4, 2, 6); break;
     case 55: W(256, 128, 4, 2, 2, 3); break;
 #undef W
+    // four and five stages: the full 160 KB of LDS
+    case 56: P8(128, 192, 4, 2, 4); break;
+    case 57: P8(128, 128, 2, 4, 5); break;
+    case 58: P8(128, 192, 2, 4, 4); break;
 #undef P8
 
   }

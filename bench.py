@@ -24,7 +24,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
 # HBM bytes per launch of the gate/up GEMM measured with rocprofv3 FETCH_SIZE + WRITE_SIZE (copy-
 # calibrated), for the kernel named here; None until the counters are taken on this kernel.
-GATE_UP_KERNEL = "k_gemm_pipe<128, 192, 4, 2, 3, 3, false>"
+GATE_UP_KERNEL = "k_gemm_pipe<128, 192, 4, 2, 4, 3, false>"
 GATE_UP_TRAFFIC_BYTES = 222.8e6
 
 
