@@ -3,6 +3,7 @@ rejects bad arguments before any device work."""
 import ctypes
 import os
 import re
+from dataclasses import replace
 
 import pytest
 
@@ -61,12 +62,28 @@ def test_workspace_size_covers_the_cache():
     ("dtype", 7), ("vocab", 1), ("d_model", 100), ("ffn", 0), ("head_dim", 48), ("n_q_heads", 3),
     ("n_kv_heads", 0), ("n_core", 0), ("n_pre", -1), ("k_max", 0), ("k_max", 17), ("max_batch", 0),
     ("max_batch", 2000), ("max_block", 65), ("max_block", 0), ("max_prefix", -2), ("max_prefill_rows", 5),
-    ("mask_id", 151936), ("rms_eps", float("nan")), ("rope_theta", 0.0)])
+    ("mask_id", 151936), ("rms_eps", float("nan")), ("rope_theta", 0.0), ("depth_on_demand", 2),
+    ("kv_dtype", 1), ("kv_dtype", 3)])
 def test_bad_configs_are_rejected(field, value):
     with pytest.raises(B.AlodlmError) as e:
         B.workspace_bytes(_cfg(**{field: value}))
     assert e.value.code == B.EINVAL
     assert "invalid config" in str(e.value)
+
+
+def test_fp8_kv_config_rules_and_workspace():
+    """fp8 keys and values need the bf16 dtype and head_dim 64 or 128, and halve the cache bytes;
+    depth-on-demand adds the prefix state [max_batch][max_prefix][d] fp32."""
+    for w in (synth.workload("tiny"), replace(synth.workload("tiny"), dtype="bf16")):   # hd 32 / fp32
+        with pytest.raises(B.AlodlmError) as e:
+            B.workspace_bytes(_cfg(w, kv_dtype=B.KV_FP8))
+        assert e.value.code == B.EINVAL
+    base = B.workspace_bytes(_cfg())
+    f8 = B.workspace_bytes(_cfg(kv_dtype=B.KV_FP8))
+    kv = 2 * 84 * 8 * 8 * 1024 * 128 * 2
+    assert abs((base - f8) - kv / 2) < 64 * 2 ** 20      # the cache (and own-block K/V) at one byte
+    dod = B.workspace_bytes(_cfg(depth_on_demand=1))
+    assert abs((dod - base) - 8 * 1024 * 4096 * 4) < 2 ** 20
 
 
 def _weights(nl, ptr=0x1000):
@@ -108,5 +125,11 @@ def test_null_context_calls_fail_cleanly():
     assert lib.alodlm_denoise_step(None, None, None) == B.EINVAL
     assert lib.alodlm_readout_commit(None, None, 32, 32, 0.5, 0.5, *([None] * 10)) == B.EINVAL
     assert lib.alodlm_last_step_stats(None, None, None) == B.EINVAL
+    assert lib.alodlm_extend_kv(None, 1, 1, None, None) == B.EINVAL
+    assert lib.alodlm_denoise_block(None, None, None) == B.EINVAL
+    assert lib.alodlm_prefill_kv_depth(None, 1, 1, None, 1) == B.EINVAL
+    assert lib.alodlm_deepen_kv(None, 2) == B.EINVAL
     lib.alodlm_destroy(None)
     assert lib.alodlm_synth_fill(None, 0, 0, 10, 0, 0, 1.0, 0.0, None) == -1
+    # diagnostics entry: bad shapes and null operands are rejected before any launch
+    assert lib.alodlm_diag_readout_sample(0, 10, 64, None, None, None, 1, 1, 1, None, None, 0, 0, -1, None) == -1
