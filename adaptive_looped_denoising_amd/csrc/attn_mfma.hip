@@ -1,7 +1,7 @@
 // Block attention over the depth-aware prefix cache on the gfx950 matrix cores (bf16).
 //
-// One workgroup (4 waves) takes one (sequence slot, kv head) pair, a block of QB = 4 * QW query
-// rows of that pair -- the G = Hq/Hkv query heads sharing the kv head are packed as rows
+// One workgroup (NW = 4 or 8 waves) takes one (sequence slot, kv head) pair, a block of
+// QB = NW * QW query rows of that pair -- the G = Hq/Hkv query heads sharing the kv head are packed as rows
 // (position i, head g) -> i*G + g -- and one split of its key tiles.  Key tiles hold 64 keys of
 // one segment: the prefix keys (the cache slot of the loop's depth plane; the planes are
 // materialised at prefill so that plane s already holds every position at depth

@@ -1,16 +1,22 @@
 // bf16 GEMM on the gfx950 matrix cores: C[m][n] = sum_k A[m][k] B[n][k] with A, B row-major bf16
 // (both K-contiguous), fp32 accumulation in v_mfma_f32_16x16x32_bf16.
 //
-// Block = 4 waves; tile BM x BN x 64 staged through LDS (double buffer, rows padded by 16 bytes
-// so the 16-byte fragment reads of a wave hit distinct banks).  Tiles are numbered so that the
-// blocks the dispatcher sends to one XCD (block ids congruent mod 8) are consecutive tiles with the
-// row tile varying fastest: the few row tiles that share a weight column tile run on the same
-// XCD at about the same time and find it in that XCD's L2.
+// Kernel families (tile table kTiles, chosen per shape by gemm_mfma_auto_tile):
+//   k_gemm_mfma   4 waves, BM x BN x 64 tiles double-buffered through padded LDS rows;
+//   k_gemm_pipe   4 or 8 waves (two per SIMD), an NS-stage LDS ring filled by direct
+//                 global->LDS loads with XOR-swizzled 16-byte chunks, explicit vmcnt waits;
+//   k_gemm_adirect activations straight to registers, weights through the LDS ring;
+//   k_gemm_ring2  separate activation / weight ring depths;
+//   k_gemm_ws     wave-specialised loads (half the waves fetch activations, half weights).
+// Tiles are numbered so that the blocks the dispatcher sends to one XCD (block ids congruent
+// mod 8) are consecutive tiles with the row tile varying fastest: the few row tiles that share
+// a weight column tile run on the same XCD at about the same time and find it in its L2.
 //
 // Epilogues: STORE (fp32), RESID (fp32 C = R + acc), SWIGLU (gate/up rows interleaved in
 // 16-column groups, output bf16 silu(gate) * up), SOFTSTAT (per-row softmax statistics of the
-// tile for the LM-head readout; logits never leave the chip).  Split-K writes fp32 partials
-// that k_splitk_reduce sums in a fixed order and finishes with the same epilogue.
+// tile for the LM-head readout, optionally with the Gumbel-max draw; logits never leave the
+// chip).  Split-K writes fp32 partials that k_splitk_reduce sums in a fixed order and finishes
+// with the same epilogue, or that the consuming kernel sums (deferred reduction).
 #include <type_traits>
 
 #include "common.h"

@@ -1,6 +1,7 @@
 // Host runtime and C ABI of the looped denoising step: workspace plan, argument checks,
-// depth-aware prefix-cache build, and the step driver (Prelude once, then per loop the
-// shared Core, the Coda, the two heads, the commit rule, compaction and the Eq. 3 reset).
+// depth-aware prefix-cache build (full, depth by depth, or grown by a finished block), the
+// step driver (Prelude once, then per loop the shared Core, the Coda, the two heads, the
+// commit rule, compaction and the Eq. 3 reset) and the outer loop over a block.
 #include <math.h>
 #include <stdlib.h>
 #include <stdio.h>
