@@ -59,12 +59,12 @@ class StepOut(ctypes.Structure):
 
 
 class BlockArgs(ctypes.Structure):
-    _fields_ = [("step", StepArgs), ("max_steps", c_int32), ("append", c_int32)]
+    _fields_ = [("step", StepArgs), ("max_steps", c_int32), ("append", c_int32), ("deepen", c_int32)]
 
 
 class BlockOut(ctypes.Structure):
     _fields_ = [("tokens", c_void_p), ("commit_step", c_void_p), ("commit_loop", c_void_p), ("n_steps", c_int32),
-                ("n_committed", c_int32)]
+                ("n_committed", c_int32), ("built_depth", c_int32)]
 
 
 class AlodlmError(RuntimeError):

@@ -952,6 +952,7 @@ int alodlm_denoise_block(alodlm_ctx* c, const alodlm_block_args* a, alodlm_block
   const int max_steps = a->max_steps == 0 ? L : a->max_steps;
   if (a->append && (max_steps < L || L > g.max_prefix - c->cache_prefix))
     return c->fail(ALODLM_EINVAL, "append needs max_steps 0 or >= block_len and room for block_len positions");
+  if (a->deepen && !g.depth_on_demand) return c->fail(ALODLM_EINVAL, "deepen needs cfg.depth_on_demand");
   hipStream_t st = c->st;
   const int n = B * L;
   int32_t* ids = c->at<int32_t>(p.blk_ids);
@@ -978,11 +979,17 @@ int alodlm_denoise_block(alodlm_ctx* c, const alodlm_block_args* a, alodlm_block
     launch_block_merge(n, steps, so.tokens, so.commit_loop, ids, o->commit_step, o->commit_loop, st);
     committed += so.n_committed;
     if (so.n_committed < 1) return c->fail(ALODLM_ESTATE, "internal: an outer-loop step committed nothing");
+    // depth on demand: a loop ran past the built depth, so build up to that depth for the next step
+    if (a->deepen && c->built_depth > 0 && c->state_prefix == c->cache_prefix && so.loops_run > c->built_depth) {
+      rc = alodlm_deepen_kv(c, so.loops_run);
+      if (rc) return rc;
+    }
   }
   if (hipMemcpyAsync(o->tokens, ids, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, st) != hipSuccess)
     return c->fail(ALODLM_EHIP, "block tokens copy");
   o->n_steps = steps;
   o->n_committed = committed;
+  o->built_depth = c->built_depth;
   if (a->append) {
     int rc = alodlm_extend_kv(c, B, L, ids, nullptr);
     if (rc) return rc;

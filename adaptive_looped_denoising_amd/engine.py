@@ -218,10 +218,10 @@ class Engine:
         torch.cuda.synchronize(self.device)
 
     def make_block(self, tau_ent=None, tau_halt=None, k_loops=None, boost=True, block_ids=None, sample=None,
-                   max_steps=0, append=False):
+                   max_steps=0, append=False, deepen=False):
         w = self.w
         step = self.make_args(tau_ent, tau_halt, k_loops, boost, None, block_ids, sample)
-        args = B.BlockArgs(step=step, max_steps=max_steps, append=1 if append else 0)
+        args = B.BlockArgs(step=step, max_steps=max_steps, append=1 if append else 0, deepen=1 if deepen else 0)
         self._blk = dict(tokens=torch.empty((w.batch, w.block), dtype=torch.int32, device=self.device),
                          commit_step=torch.empty((w.batch, w.block), dtype=torch.int16, device=self.device),
                          commit_loop=torch.empty((w.batch, w.block), dtype=torch.int8, device=self.device))
@@ -236,7 +236,7 @@ class Engine:
         B.denoise_block(self.ctx, args, out)
         torch.cuda.synchronize(self.device)
         res = {k: v.cpu().numpy() for k, v in self._blk.items()}
-        res.update(n_steps=out.n_steps, n_committed=out.n_committed)
+        res.update(n_steps=out.n_steps, n_committed=out.n_committed, built_depth=out.built_depth)
         return res
 
     def read_kv(self, slot: int, b: int, j0: int, n: int):

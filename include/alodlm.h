@@ -248,6 +248,10 @@ typedef struct alodlm_block_args {
   int32_t max_steps;      /* cap on steps, >= 0; 0 = block_len (always enough to finish) */
   int32_t append;         /* != 0: append the finished block to the cache (alodlm_extend_kv); needs
                              max_steps 0 or >= block_len and room for block_len more positions */
+  int32_t deepen;         /* != 0 (depth-on-demand caches, cfg.depth_on_demand): after a step whose loop
+                             count over the batch exceeds the cache's built depth, deepen the cache
+                             to that loop count (alodlm_deepen_kv) before the next step -- deeper
+                             depths are built only once some loop needs them */
 } alodlm_block_args;
 
 typedef struct alodlm_block_out {
@@ -256,6 +260,8 @@ typedef struct alodlm_block_out {
   int8_t* commit_loop;    /* device [batch][L]: that commit's loop within its step (s, or -s forced) */
   int32_t n_steps;        /* host: steps run */
   int32_t n_committed;    /* host: tokens committed over all steps */
+  int32_t built_depth;    /* host: the cache's built Core depth at the end (-1 without a depth-on-demand
+                             build) */
 } alodlm_block_out;
 
 /* Runs the outer loop; reads the step's commit count back once per step (alodlm_denoise_step

@@ -100,6 +100,51 @@ def denoise_block(w: synth.Workload, W=None, seqs=None, block_ids=None, boost=No
     return out
 
 
+def denoise_block_on_demand(w: synth.Workload, depth0: int, W=None, sample: Optional[dict] = None,
+                            prec=None) -> dict:
+    """Oracle outer loop over the whole batch with a depth-on-demand cache: every prefix built to
+    depth0; after a step whose loop count over the batch exceeds the built depth, every cache is
+    deepened to that loop count before the next step (``sample`` = {"seed", "step0"})."""
+    W = weights(w) if W is None else W
+    D = w.dims
+    pids = synth.prefix_ids(w)
+    btok, bval = synth.boosts(w)
+    caches, states = {}, {}
+    for b in range(w.batch):
+        caches[b], states[b] = orc.prefill_sequence(pids[b], W, D, w.k_max, w.rms_eps, w.rope_theta, prec=prec,
+                                                    depth=depth0, state=True, kv=kv_format(w))
+    built = depth0
+    ids = {b: np.asarray(synth.block_ids(w)[b], dtype=np.int64).copy() for b in range(w.batch)}
+    commit_step = {b: np.zeros(w.block, dtype=np.int64) for b in range(w.batch)}
+    commit_loop = {b: np.zeros(w.block, dtype=np.int64) for b in range(w.batch)}
+    results, depths = [], []
+    t = 0
+    while any((ids[b] == w.mask_id).any() for b in range(w.batch)):
+        t += 1
+        loops_max = 0
+        for b in range(w.batch):
+            if not (ids[b] == w.mask_id).any():
+                continue
+            smp = None if sample is None else dict(seed=sample["seed"], step=sample["step0"] + t - 1, seq=b)
+            res = orc.denoise_step_sequence(ids[b], caches[b], np.full(w.prefix, built), W, D, mask_id=w.mask_id,
+                                            boost_tok=btok[b], boost_val=bval[b], prec=prec, sample=smp,
+                                            kv=kv_format(w), **step_kwargs(w))
+            newly = res["commit_loop"] != 0
+            commit_step[b][newly] = t
+            commit_loop[b][newly] = res["commit_loop"][newly]
+            ids[b] = np.asarray(res["tokens"], dtype=np.int64).copy()
+            loops_max = max(loops_max, res["loops"])
+            results.append((t, b, res))
+        if loops_max > built:
+            for b in range(w.batch):
+                caches[b], states[b] = orc.deepen_sequence(caches[b], states[b], W, D, w.k_max, w.rms_eps,
+                                                           w.rope_theta, built, loops_max, prec=prec, kv=kv_format(w))
+            built = loops_max
+        depths.append(built)
+    return dict(tokens=ids, commit_step=commit_step, commit_loop=commit_loop, steps=t, built_depth=built,
+                depth_after_step=depths, results=results)
+
+
 def teacher_from(results: List[dict]) -> Dict[int, dict]:
     """Teacher-forcing decisions (commit loops, tokens, stop loop) taken from oracle results."""
     return {r["seq"]: dict(commit_loop=r["commit_loop"], tokens=r["tokens"], stop_loop=r["loops"])

@@ -235,3 +235,30 @@ def test_mid_bf16_depth_on_demand_prefill(gpu_lib):
         ref = orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta)
         ref16 = orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, prec="bf16")
         log("seq %d worst/tol %.3f" % (b, _check_cache(e, w, b, 0, w.prefix, ref, ref16)))
+
+
+def test_tiny_fp32_outer_loop_deepens_on_demand(gpu_lib):
+    """Depth-on-demand end to end: the prefix is built to depth 1; the first step runs 3 loops, so
+    the cache is deepened to 3 before the second step.  Decisions, commit steps and the final cache
+    match the oracle running the same batch policy.  Near-ties are taken at 1e-5 nats (the fp32
+    path's entropy error on this workload is below 1e-6)."""
+    from adaptive_looped_denoising_amd.engine import Engine
+    w = synth.workload("tiny", batch=2, boost_lo=8.0, boost_hi=14.0, tau_ent=0.8, tau_halt=0.6)
+    e = Engine(w, depth_on_demand=True)
+    e.prefill(depth=1)
+    g = e.denoise_block(deepen=True)
+    r = orun.denoise_block_on_demand(w, 1)
+    log("oracle depth after each step %s, GPU built depth %d" % (r["depth_after_step"], g["built_depth"]))
+    assert g["built_depth"] == r["built_depth"] == 3 and g["n_steps"] == r["steps"]
+    flags = [f for (_, _, res) in r["results"]
+             for f in orun.near_decisions(w, res, ent_tol=1e-5, gap_tol=1e-5, halt_tol=1e-5)]
+    assert not flags, flags
+    for b in range(w.batch):
+        assert np.array_equal(g["tokens"][b], r["tokens"][b])
+        assert np.array_equal(g["commit_step"][b], r["commit_step"][b])
+        assert np.array_equal(g["commit_loop"][b], r["commit_loop"][b])
+    W = orun.weights(w)
+    ids = synth.prefix_ids(w)
+    for b in range(w.batch):
+        ref = orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, depth=3)
+        _check_cache(e, w, b, 0, w.prefix, _planes_at(w, ref, 3))
