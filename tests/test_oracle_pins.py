@@ -732,3 +732,19 @@ def test_fp8_cache_holds_e4m3_values_and_changes_little():
     h8 = r8["records"][0]["H"][r8["records"][0]["rows"]]
     h = r["records"][0]["H"][r["records"][0]["rows"]]
     assert 0 < np.abs(h8 - h).max() < 0.1
+
+
+def test_batch_depth_on_demand_policy_reduces_to_the_plain_outer_loop():
+    """Built to full depth, the on-demand policy never deepens and equals the per-sequence outer loop;
+    built to depth 1 it deepens to the first step's loop count."""
+    w = _tiny(batch=2, boost_lo=8.0, boost_hi=14.0, tau_ent=0.8, tau_halt=0.6)
+    W = run.weights(w)
+    full = run.denoise_block_on_demand(w, w.k_max, W=W)
+    plain = run.denoise_block(w, W=W)
+    assert full["depth_after_step"] == [w.k_max] * full["steps"]
+    for r in plain:
+        b = r["seq"]
+        assert np.array_equal(full["tokens"][b], r["tokens"]) and np.array_equal(full["commit_step"][b], r["commit_step"])
+    od = run.denoise_block_on_demand(w, 1, W=W)
+    first = max(res["loops"] for (t, _, res) in od["results"] if t == 1)
+    assert od["depth_after_step"][0] == max(1, first) and od["built_depth"] == max(od["depth_after_step"])
