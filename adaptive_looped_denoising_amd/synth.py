@@ -175,6 +175,7 @@ class Workload:
     short_frac: float = 0.0  # fraction of prefix positions whose cache stops at short_depth
     short_depth: int = 0
     kv_dtype: str = "same"  # K/V storage: "same" (the model dtype) or "fp8" (OCP E4M3)
+    cache_depths: int = 0   # Core depths kept in the cache (0: all k_max)
     weight_std: float = 0.02
     halt_target: float = 0.42
     rms_eps: float = 1e-6

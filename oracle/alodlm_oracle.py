@@ -75,7 +75,17 @@ follow them):
     d = 1..k_max and the Coda once on the depth-k_max output, causally among
     themselves, reading the cached positions as a step does (Core position j
     at depth min(d, avail_j)); they are cached at every depth.  With every
-    cached position at full depth this is the prefill of the longer prefix.
+    cached position at full depth this is the prefill of the longer prefix;
+  * depth eviction (the "Limitations" section's other memory remedy, dropping
+    low-value depth buffers): a cache keeping depths 1..D holds the sets the
+    full build computes for the Prelude, the Coda and Core depths 1..D, and
+    drops the deeper Core sets; every position's available depth becomes
+    min(avail_j, D), so the deepest-available fallback serves deeper loops.
+    The value of a depth is taken to fall with the depth (the deeper sets go
+    first), since loops past the first few are the rare ones.  A block that
+    joins such a cache still runs all k_max Core passes (the Coda set needs
+    the depth-k_max output), reading the cached positions at min(d, avail_j),
+    and keeps depths 1..D of its own positions.
 """
 from __future__ import annotations
 
@@ -297,6 +307,22 @@ def deepen_sequence(cache, core_out, W, dims, k_max: int, eps: float, theta: flo
     return out, core
 
 
+def evict_depths(cache, avail, dims, k_max: int, keep: int, P: int):
+    """Depth eviction: keep the Prelude and Coda sets and Core depths 1..``keep`` of a depth-aware
+    cache of P positions, drop the deeper Core sets, and clip every available depth to ``keep``
+    (``avail`` None: every position at k_max).  Returns the smaller cache and the clipped depths;
+    a Core layer in loop s then reads position j at depth min(s, avail_j, keep)."""
+    out = {}
+    for li in range(dims.n_pre + dims.n_core + dims.n_coda):
+        core = dims.n_pre <= li < dims.n_pre + dims.n_core
+        for dpt in (range(1, keep + 1) if core else (1,)):
+            slot = kv_slot(dims, k_max, li, dpt)
+            if slot in cache:
+                out[slot] = cache[slot]
+    av = np.full(P, k_max, dtype=np.int64) if avail is None else np.asarray(avail, dtype=np.int64)
+    return out, np.minimum(av, keep)
+
+
 def context_for(cache, dims, k_max: int, layer: int, loop: int, avail):
     """Prefix K/V a block row reads at ``layer`` during loop ``loop`` (1-based).
 
@@ -320,14 +346,17 @@ def context_for(cache, dims, k_max: int, layer: int, loop: int, avail):
 
 
 def extend_sequence(cache, avail, new_ids, W, dims, k_max: int, eps: float, theta: float, prec=None,
-                    kv=None):
+                    kv=None, keep: Optional[int] = None):
     """Appends positions (a finished block) to the depth-aware cache of one sequence.
 
     The new positions (ids ``new_ids``, positions P.. after the P cached ones) run through the
     Prelude once, the Core once per depth d = 1..k_max and the Coda once on the depth-k_max
     output, causally among themselves; cached position j is read as a step reads it (Core depth
     min(d, avail_j)).  Returns the longer cache (slot -> (K, V) [Hkv][P + n][hd]) and its
-    available depths (the new positions at every depth)."""
+    available depths (the new positions at every depth).  ``keep`` < k_max: the cache holds
+    depths 1..keep only (evict_depths); the new positions' deeper Core sets are dropped after
+    use and their available depth is keep."""
+    keep = k_max if keep is None else keep
     new_ids = np.asarray(new_ids)
     n = new_ids.shape[0]
     P = next(iter(cache.values()))[0].shape[1] if cache else 0
@@ -349,6 +378,9 @@ def extend_sequence(cache, avail, new_ids, W, dims, k_max: int, eps: float, thet
     for c in range(dims.n_coda):
         run(dims.n_pre + dims.n_core + c, 1)
     out = {}
+    for li in range(dims.n_pre, dims.n_pre + dims.n_core):
+        for dpt in range(keep + 1, k_max + 1):
+            del new[kv_slot(dims, k_max, li, dpt)]
     for slot, (k, v) in new.items():
         if cache:
             out[slot] = (np.concatenate([_f64(cache[slot][0]), k], axis=1),
@@ -356,7 +388,7 @@ def extend_sequence(cache, avail, new_ids, W, dims, k_max: int, eps: float, thet
         else:
             out[slot] = (k, v)
     av0 = np.full(P, k_max, dtype=np.int64) if avail is None else np.asarray(avail, dtype=np.int64)
-    return out, np.concatenate([av0, np.full(n, k_max, dtype=np.int64)])
+    return out, np.concatenate([av0, np.full(n, keep, dtype=np.int64)])
 
 
 # ---------------------------------------------------------------------------

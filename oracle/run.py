@@ -24,9 +24,24 @@ def kv_format(w: synth.Workload):
     return "fp8" if w.kv_dtype == "fp8" else None
 
 
+def keep_depths(w: synth.Workload) -> int:
+    """Core depths the workload's cache keeps (depth eviction below k_max)."""
+    return w.cache_depths or w.k_max
+
+
+def avail_for(w: synth.Workload, av_b):
+    """Available depths a step reads for one sequence: the supplied ones, clipped by eviction."""
+    if not w.prefix:
+        return None
+    if keep_depths(w) == w.k_max:
+        return av_b
+    return orc.evict_depths({}, av_b, w.dims, w.k_max, keep_depths(w), w.prefix)[1]
+
+
 def cache_for(w: synth.Workload, W, b: int, prefix_ids=None, progress=None, prec=None) -> Dict[int, tuple]:
     """Depth-aware prefix cache of sequence b: computed by the oracle's prefill, or the
-    workload's synthetic K/V (with fp8 K/V: the float32 draws rounded by the oracle's E4M3)."""
+    workload's synthetic K/V (with fp8 K/V: the float32 draws rounded by the oracle's E4M3);
+    with depth eviction, the Core sets deeper than the kept depths are dropped."""
     if w.prefix == 0:
         return {}
     if w.kv == "synthetic":
@@ -38,10 +53,13 @@ def cache_for(w: synth.Workload, W, b: int, prefix_ids=None, progress=None, prec
             else:
                 K, V = synth.synthetic_kv_seq(w, slot, b)
                 out[slot] = (synth.as_f32(K), synth.as_f32(V))
-        return out
-    ids = synth.prefix_ids(w) if prefix_ids is None else prefix_ids
-    return orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, progress=progress, prec=prec,
-                                kv=kv_format(w))
+    else:
+        ids = synth.prefix_ids(w) if prefix_ids is None else prefix_ids
+        out = orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, progress=progress,
+                                   prec=prec, kv=kv_format(w))
+    if keep_depths(w) < w.k_max:
+        out = orc.evict_depths(out, None, w.dims, w.k_max, keep_depths(w), w.prefix)[0]
+    return out
 
 
 def step(w: synth.Workload, W=None, seqs=None, k_loops: Optional[int] = None, teacher=None,
@@ -60,7 +78,7 @@ def step(w: synth.Workload, W=None, seqs=None, k_loops: Optional[int] = None, te
     for b in seqs:
         cache = caches[b] if caches is not None else cache_for(w, W, b, pids, progress, prec)
         res = orc.denoise_step_sequence(
-            bids[b], cache, av[b] if av is not None and w.prefix else None, W, w.dims,
+            bids[b], cache, avail_for(w, av[b] if av is not None else None), W, w.dims,
             k_max=w.k_max, k_loops=w.k_max if k_loops is None else k_loops, eps=w.rms_eps,
             theta=w.rope_theta, tau_ent=w.tau_ent, tau_halt=w.tau_halt, mask_id=w.mask_id,
             exit_b=w.exit_bias() if exit_b is None else exit_b, boost_tok=btok[b], boost_val=bval[b],
@@ -92,7 +110,7 @@ def denoise_block(w: synth.Workload, W=None, seqs=None, block_ids=None, boost=No
     for b in seqs:
         cache = caches[b] if caches is not None else cache_for(w, W, b, pids, None, prec)
         res = orc.denoise_block_sequence(
-            bids[b], cache, av[b] if av is not None and w.prefix else None, W, w.dims, max_steps=max_steps,
+            bids[b], cache, avail_for(w, av[b] if av is not None else None), W, w.dims, max_steps=max_steps,
             sample=None if sample is None else dict(sample, seq=b), mask_id=w.mask_id, boost_tok=btok[b],
             boost_val=bval[b], prec=prec, kv=kv_format(w), **step_kwargs(w))
         res["seq"] = b

@@ -748,3 +748,79 @@ def test_batch_depth_on_demand_policy_reduces_to_the_plain_outer_loop():
     od = run.denoise_block_on_demand(w, 1, W=W)
     first = max(res["loops"] for (t, _, res) in od["results"] if t == 1)
     assert od["depth_after_step"][0] == max(1, first) and od["built_depth"] == max(od["depth_after_step"])
+
+
+# --------------------------------------------------------------------------- depth eviction
+def test_evict_depths_buffer_counts_match_page():
+    """Keeping one Core depth leaves the autoregressive model's buffer count, keeping all K the
+    page's 84; the kept sets are the Prelude, the Coda and Core depths 1..D; depths are clipped."""
+    g = _golden("page_constants.json")
+    d8 = synth.QWEN3_8B_DIMS
+    K = g["k_loops"]["value"]
+    full = {s: (s, s) for s in range(d8.kv_slots(K))}
+    for D, n in ((1, g["kv_buffers_8b_k4"]["autoregressive_value"]), (K, g["kv_buffers_8b_k4"]["value"]),
+                 (2, d8.n_layers + d8.n_core)):
+        kept, av = orc.evict_depths(full, None, d8, K, D, 5)
+        assert len(kept) == n == d8.kv_slots(D)
+        assert set(kept) == {orc.kv_slot(d8, K, l, dp) for l in range(d8.n_layers)
+                             for dp in range(1, (D if d8.n_pre <= l < d8.n_pre + d8.n_core else 1) + 1)}
+        assert all(kept[s] == full[s] for s in kept) and (av == D).all()
+    _, av = orc.evict_depths({}, np.array([1, 2, 3, 4, 4]), d8, K, 2, 5)
+    assert av.tolist() == [1, 2, 2, 2, 2]
+
+
+def test_step_on_evicted_cache_reads_the_deepest_kept_depth():
+    """With one depth kept, a step equals the step on a full cache whose every Core plane holds
+    the depth-1 sets (the fallback written out by hand); it differs from the full-depth step once
+    a loop runs past depth 1."""
+    w = _tiny(tau_ent=0.3, tau_halt=0.9)
+    W = run.weights(w)
+    D = w.dims
+    cache = run.cache_for(w, W, 0)
+    flat = dict(cache)
+    for c in range(D.n_core):
+        for dpt in range(2, w.k_max + 1):
+            flat[orc.kv_slot(D, w.k_max, D.n_pre + c, dpt)] = cache[orc.kv_slot(D, w.k_max, D.n_pre + c, 1)]
+    w1 = replace(w, cache_depths=1)
+    ev = run.cache_for(w1, W, 0)
+    assert len(ev) == D.kv_slots(1)
+    r_ev = run.step(w1, W=W, seqs=[0], record_hidden=True)[0]
+    r_flat = run.step(w, W=W, seqs=[0], caches={0: flat}, record_hidden=True)[0]
+    r_full = run.step(w, W=W, seqs=[0], record_hidden=True)[0]
+    assert r_ev["loops"] >= 2 and r_ev["loops"] == r_flat["loops"]
+    for a, b in zip(r_ev["records"], r_flat["records"]):
+        np.testing.assert_allclose(a["h_tilde"], b["h_tilde"], rtol=1e-12, atol=1e-13)
+    assert not np.allclose(r_ev["records"][1]["h_tilde"], r_full["records"][1]["h_tilde"])
+    np.testing.assert_allclose(r_ev["records"][0]["h_tilde"], r_full["records"][0]["h_tilde"], rtol=1e-12,
+                               atol=1e-13)
+
+
+def test_extend_on_evicted_cache():
+    """Appending to a cache that keeps D depths: the new positions' Prelude and Core depth 1..D sets
+    equal those of the full-cache extension (those passes read cached positions at depth <= D
+    either way) while the Coda set differs; with every cached position at depth <= D, extending
+    then evicting equals evicting then extending."""
+    w = _tiny()
+    W = _rand_weights(w, seed=4)
+    D = w.dims
+    ids = np.random.default_rng(8).integers(0, D.vocab, size=16)
+    kw = dict(dims=D, k_max=w.k_max, eps=w.rms_eps, theta=w.rope_theta)
+    cache = orc.prefill_sequence(ids[:11], W, D, w.k_max, w.rms_eps, w.rope_theta)
+    ev, av = orc.evict_depths(cache, None, D, w.k_max, 2, 11)
+    a, av_a = orc.extend_sequence(ev, av, ids[11:], W, keep=2, **kw)
+    b, _ = orc.extend_sequence(cache, None, ids[11:], W, **kw)
+    assert sorted(a) == sorted(ev) and av_a.tolist() == [2] * 16
+    coda = orc.kv_slot(D, w.k_max, D.n_pre + D.n_core)
+    for slot in a:
+        same = np.allclose(a[slot][0][:, 11:], b[slot][0][:, 11:], rtol=1e-11, atol=1e-12)
+        assert same == (slot < coda), slot
+    # every cached position at depth <= 2: eviction commutes with the extension
+    shallow = np.array([1, 2] * 5 + [2])
+    ev2, av2 = orc.evict_depths(cache, shallow, D, w.k_max, 2, 11)
+    c, _ = orc.extend_sequence(ev2, av2, ids[11:], W, keep=2, **kw)
+    full2, avf = orc.extend_sequence(cache, shallow, ids[11:], W, **kw)
+    d_, _ = orc.evict_depths(full2, avf, D, w.k_max, 2, 16)
+    assert sorted(c) == sorted(d_)
+    for slot in c:
+        for x, y in zip(c[slot], d_[slot]):
+            np.testing.assert_allclose(x, y, rtol=1e-11, atol=1e-12)
