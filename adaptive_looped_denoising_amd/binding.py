@@ -32,7 +32,8 @@ class Config(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "vocab", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "n_pre", "n_core", "n_coda", "k_max",
         "max_batch", "max_prefix", "max_block", "max_prefill_rows", "mask_id", "dtype")] + \
-        [("rms_eps", c_float), ("rope_theta", c_float), ("depth_on_demand", c_int32), ("kv_dtype", c_int32)]
+        [("rms_eps", c_float), ("rope_theta", c_float), ("depth_on_demand", c_int32), ("kv_dtype", c_int32),
+         ("cache_depths", c_int32)]
 
 
 class LayerWeights(ctypes.Structure):

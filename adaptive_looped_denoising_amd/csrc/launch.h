@@ -143,8 +143,9 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
 void launch_fill_kv_synth(int dtype, void* slot_base, int B, int Hkv, int P, int P_pitch, int hd, uint32_t seed,
                           uint32_t tensor, float scale, bool transposed, hipStream_t st);
 // Available-depth table [B][pitch]: positions j0 .. j0+n-1 of each sequence from src [B][n], or
-// the value v when src is null.
-void launch_set_avail(uint8_t* dst, int pitch, int j0, int B, int n, const uint8_t* src, uint8_t v, hipStream_t st);
+// the value v when src is null, clipped to cap (the Core depths the cache keeps).
+void launch_set_avail(uint8_t* dst, int pitch, int j0, int B, int n, const uint8_t* src, uint8_t v, uint8_t cap,
+                      hipStream_t st);
 // Depth planes of one Core layer's cache (plane p = depth p + 1, plane_elems apart): for every
 // position j with avail[b][j] = a_j, plane p takes the values of plane max(1, min(p + 1, a_j)) - 1,
 // so that reading plane s - 1 at loop s gives every key at depth min(s, a_j).

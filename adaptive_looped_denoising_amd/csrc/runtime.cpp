@@ -37,12 +37,17 @@ struct Plan {
   int64_t slot_elems = 0;  // elements of one cache slot: B * Hkv * Pp * hd
   int64_t Pp = 0, Lp = 0;
   int n_slots = 0, rows_step = 0, rows_max = 0, prefill_rows = 0, n_vtiles = 0, max_pos = 0;
+  // depth eviction: the extra plane the Core passes of evicted depths write (-1: none), and the
+  // planes allocated (n_slots, plus that one)
+  int scratch_slot = -1, alloc_slots = 0;
   int attn_splits = 0;
   int av_pitch = 1;  // row pitch of the available-depth table [B][av_pitch]
   size_t gemm_part_elems = 0;
 };
 
 size_t esize(int dtype) { return dtype == ALODLM_DTYPE_BF16 ? 2 : 4; }
+// Core depth planes kept in the cache (depth eviction: the first cache_depths depths)
+int kept_depths(const alodlm_config& c) { return c.cache_depths > 0 ? c.cache_depths : c.k_max; }
 // bytes per stored key / value element
 size_t kv_esize(const alodlm_config& c) { return c.kv_dtype == ALODLM_KV_FP8 ? 1 : esize(c.dtype); }
 
@@ -74,6 +79,9 @@ int check_config(const alodlm_config* c, std::string* err) {
   if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return bad("rope_theta");
   if (c->depth_on_demand != 0 && c->depth_on_demand != 1) return bad("depth_on_demand must be 0 or 1");
   if (c->kv_dtype != ALODLM_KV_SAME && c->kv_dtype != ALODLM_KV_FP8) return bad("kv_dtype");
+  if (c->cache_depths < 0 || c->cache_depths > c->k_max) return bad("cache_depths must be in 0..k_max");
+  if (c->depth_on_demand && c->cache_depths > 0 && c->cache_depths < c->k_max)
+    return bad("depth_on_demand needs every depth kept (cache_depths 0 or k_max)");
   if (c->kv_dtype == ALODLM_KV_FP8 && (c->dtype != ALODLM_DTYPE_BF16 || (c->head_dim != 64 && c->head_dim != 128)))
     return bad("fp8 keys and values need the bf16 dtype and head_dim 64 or 128");
   return ALODLM_OK;
@@ -85,7 +93,10 @@ Plan make_plan(const alodlm_config& c) {
   const int64_t B = c.max_batch, P = c.max_prefix, L = c.max_block, d = c.d_model, hd = c.head_dim;
   const int64_t Hq = c.n_q_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
   const int64_t qkv_out = (Hq + 2 * Hkv) * hd;
-  p.n_slots = c.n_pre + c.n_core * c.k_max + c.n_coda;
+  const int Dk = kept_depths(c);
+  p.n_slots = c.n_pre + c.n_core * Dk + c.n_coda;
+  p.scratch_slot = Dk < c.k_max ? p.n_slots : -1;
+  p.alloc_slots = p.n_slots + (Dk < c.k_max ? 1 : 0);
   p.Pp = (P + 63) / 64 * 64;
   p.Lp = (L + 63) / 64 * 64;
   p.slot_elems = B * Hkv * p.Pp * hd;
@@ -105,8 +116,8 @@ Plan make_plan(const alodlm_config& c) {
   p.rope_cos = take(sizeof(float) * p.max_pos * (hd / 2));
   p.rope_sin = take(sizeof(float) * p.max_pos * (hd / 2));
   const size_t kes = kv_esize(c);
-  p.kcache = take(kes * p.slot_elems * p.n_slots);
-  p.vcache = take(kes * p.slot_elems * p.n_slots);
+  p.kcache = take(kes * p.slot_elems * p.alloc_slots);
+  p.vcache = take(kes * p.slot_elems * p.alloc_slots);
   p.av_pitch = P > 0 ? (int)P : 1;
   p.avail = take(B * p.av_pitch);
   p.h = take(sizeof(float) * R * d);
@@ -246,10 +257,23 @@ void* cache_slot(alodlm_ctx* c, bool v, int slot) {
 // storage type of keys and values (DT_FP8, or the model dtype)
 int kvt(const alodlm_ctx* c) { return c->cfg.kv_dtype == ALODLM_KV_FP8 ? DT_FP8 : dt(c); }
 
+// Stored slot of (layer, loop depth); a Core depth beyond the kept ones reads the deepest kept.
 int slot_of(const alodlm_config& c, int layer, int depth) {
+  const int Dk = kept_depths(c);
   if (layer < c.n_pre) return layer;
-  if (layer < c.n_pre + c.n_core) return c.n_pre + (layer - c.n_pre) * c.k_max + (depth - 1);
-  return c.n_pre + c.n_core * c.k_max + (layer - c.n_pre - c.n_core);
+  if (layer < c.n_pre + c.n_core) return c.n_pre + (layer - c.n_pre) * Dk + ((depth < Dk ? depth : Dk) - 1);
+  return c.n_pre + c.n_core * Dk + (layer - c.n_pre - c.n_core);
+}
+
+// Slot index of a stored slot in the layout that keeps every depth (the synthetic cache's streams)
+int full_slot(const alodlm_config& c, int slot) {
+  const int Dk = kept_depths(c);
+  if (slot < c.n_pre) return slot;
+  if (slot < c.n_pre + c.n_core * Dk) {
+    const int ci = (slot - c.n_pre) / Dk, d = (slot - c.n_pre) % Dk;
+    return c.n_pre + ci * c.k_max + d;
+  }
+  return slot + c.n_core * (c.k_max - Dk);
 }
 
 bool use_mfma(const alodlm_ctx* c, int K, int lda, int ldb) {
@@ -366,8 +390,15 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   if (lc.mode == PREFILL) {
     // rows are positions pos0 .. pos0 + rows_per_seq - 1 of each sequence: their post-RoPE K/V go
     // into the slot right after the pos0 positions already there, and they attend causally to
-    // all of them (pos0 = 0 for a prefill from scratch, the cached length when a block is appended)
-    const int slot = slot_of(g, li, lc.depth);
+    // all of them (pos0 = 0 for a prefill from scratch, the cached length when a block is appended).
+    // A Core pass of an evicted depth works in the scratch plane (its keys are needed only by
+    // itself).
+    // A Core pass of an evicted depth keeps its rows' keys in the scratch plane (from position 0)
+    // and reads the positions already there from the deepest kept plane.
+    const bool core_l = li >= g.n_pre && li < g.n_pre + g.n_core;
+    const bool evicted = core_l && lc.depth > kept_depths(g);
+    const int slot = evicted ? p.scratch_slot : slot_of(g, li, lc.depth);
+    const int at = evicted ? 0 : lc.pos0;  // position of the first row in the written plane
     void* kd = cache_slot(c, false, slot);
     void* vd = cache_slot(c, true, slot);
     const int64_t kSeq = (int64_t)Hkv * Pp * hd, kHead = Pp * hd, kPos = hd;
@@ -376,10 +407,22 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
     c->tic(ALODLM_K_NORM_ROPE);
     launch_qk_norm_rope(dt(c), qkv_src, n, lc.rows_per_seq, lc.pos0, Hq, Hkv, hd, W.q_norm, W.k_norm, g.rms_eps,
                         c->at<float>(p.rope_cos), c->at<float>(p.rope_sin), q,
-                        (char*)kd + (size_t)lc.pos0 * kPos * es_, (char*)vd + (size_t)lc.pos0 * es_, kSeq, kHead,
+                        (char*)kd + (size_t)at * kPos * es_, (char*)vd + (size_t)at * es_, kSeq, kHead,
                         kPos, vSeq, vHead, vRow, lc.seq0, c->st, qkv_splits, kvt(c));
     c->toc();
     ap.n_cache = 0;
+    if (evicted && lc.pos0 > 0) {
+      const int ks = slot_of(g, li, kept_depths(g));
+      ap.ck = (const char*)cache_slot(c, false, ks) + (size_t)lc.seq0 * kSeq * es_;
+      ap.cv = (const char*)cache_slot(c, true, ks) + (size_t)lc.seq0 * vSeq * es_;
+      ap.c_kSeq = kSeq;
+      ap.c_kHead = kHead;
+      ap.c_kPos = kPos;
+      ap.c_vSeq = vSeq;
+      ap.c_vHead = vHead;
+      ap.c_vRow = vRow;
+      ap.n_cache = lc.pos0;
+    }
     ap.sk = kd;
     ap.sv = vd;
     ap.s_kSeq = kSeq;
@@ -389,9 +432,9 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
     ap.s_vHead = vHead;
     ap.s_vRow = vRow;
     ap.s_seq0 = lc.seq0;
-    ap.n_self = lc.pos0 + lc.rows_per_seq;
+    ap.n_self = at + lc.rows_per_seq;
     ap.causal = 1;
-    ap.causal_off = lc.pos0;
+    ap.causal_off = at;
   } else {
     void* ks = c->at<void>(p.kself);
     void* vs = c->at<void>(p.vself);
@@ -519,7 +562,7 @@ int alodlm_kv_slots(const alodlm_config* cfg, int32_t* slots) {
     return rc;
   }
   if (!slots) return ALODLM_EINVAL;
-  *slots = cfg->n_pre + cfg->n_core * cfg->k_max + cfg->n_coda;
+  *slots = cfg->n_pre + cfg->n_core * kept_depths(*cfg) + cfg->n_coda;
   return ALODLM_OK;
 }
 
@@ -590,7 +633,7 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
   // V rows are read in whole 64-key tiles whose masked keys get probability 0; their padding must
   // hold finite values (0 * NaN would poison the sum), so the V cache and own-block V start at zero
   const size_t es = kv_esize(*cfg);
-  if (e1 == hipSuccess) e1 = hipMemsetAsync(c->ws + plan.vcache, 0, es * plan.slot_elems * plan.n_slots, c->st);
+  if (e1 == hipSuccess) e1 = hipMemsetAsync(c->ws + plan.vcache, 0, es * plan.slot_elems * plan.alloc_slots, c->st);
   if (e1 == hipSuccess)
     e1 = hipMemsetAsync(c->ws + plan.vself, 0, es * (size_t)cfg->max_batch * cfg->n_kv_heads * cfg->head_dim * plan.Lp,
                         c->st);
@@ -613,7 +656,7 @@ void materialize_depths(alodlm_ctx* c, int batch, int j0, int n) {
   const Plan& p = c->plan;
   for (int ci = 0; ci < g.n_core; ++ci) {
     const int s0 = slot_of(g, g.n_pre + ci, 1);
-    launch_materialize_depth(kvt(c), cache_slot(c, false, s0), cache_slot(c, true, s0), p.slot_elems, g.k_max, batch,
+    launch_materialize_depth(kvt(c), cache_slot(c, false, s0), cache_slot(c, true, s0), p.slot_elems, kept_depths(g), batch,
                              g.n_kv_heads, j0, n, (int)p.Pp, g.head_dim, c->at<uint8_t>(p.avail), p.av_pitch, c->st);
   }
 }
@@ -657,9 +700,9 @@ int prefill_common(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const int32
   c->cache_batch = -1;
   c->built_depth = -1;
   if (depth == g.k_max)
-    launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, avail_depth, (uint8_t)g.k_max, c->st);
+    launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, avail_depth, (uint8_t)g.k_max, (uint8_t)kept_depths(g), c->st);
   else
-    launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, nullptr, (uint8_t)depth, c->st);
+    launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, nullptr, (uint8_t)depth, (uint8_t)kept_depths(g), c->st);
   const bool save = g.depth_on_demand != 0;
   if (prefix_len > 0) {
     prefill_passes(c, batch, prefix_len, prefix_ids, depth, save);
@@ -718,7 +761,7 @@ int alodlm_deepen_kv(alodlm_ctx* c, int32_t depth) {
       lc.depth = 1;
       for (int ci = 0; ci < g.n_coda; ++ci) run_layer(c, g.n_pre + g.n_core + ci, lc);
     }
-    launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, P, nullptr, (uint8_t)depth, c->st);
+    launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, P, nullptr, (uint8_t)depth, (uint8_t)kept_depths(g), c->st);
     materialize_depths(c, batch, 0, P);
   }
   int rc = c->hip_check("deepen launch");
@@ -737,12 +780,12 @@ int alodlm_prefill_kv_synthetic(alodlm_ctx* c, int32_t batch, int32_t prefix_len
   const Plan& p = c->plan;
   c->cache_batch = -1;
   c->built_depth = -1;
-  launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, avail_depth, (uint8_t)g.k_max, c->st);
+  launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, 0, batch, prefix_len, avail_depth, (uint8_t)g.k_max, (uint8_t)kept_depths(g), c->st);
   for (int s = 0; s < p.n_slots; ++s) {
     launch_fill_kv_synth(kvt(c), cache_slot(c, false, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,
-                         seed, 0x10000u + 2u * s, k_scale, false, c->st);
+                         seed, 0x10000u + 2u * full_slot(g, s), k_scale, false, c->st);
     launch_fill_kv_synth(kvt(c), cache_slot(c, true, s), batch, g.n_kv_heads, prefix_len, (int)p.Pp, g.head_dim,
-                         seed, 0x10000u + 2u * s + 1u, v_scale, true, c->st);
+                         seed, 0x10000u + 2u * full_slot(g, s) + 1u, v_scale, true, c->st);
   }
   if (prefix_len > 0) materialize_depths(c, batch, 0, prefix_len);
   int rc = c->hip_check("synthetic prefill launch");
@@ -778,7 +821,7 @@ int alodlm_extend_kv(alodlm_ctx* c, int32_t batch, int32_t n_new, const int32_t*
     lc.depth = 1;
     for (int ci = 0; ci < g.n_coda; ++ci) run_layer(c, g.n_pre + g.n_core + ci, lc);
   }
-  launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, P0, batch, n_new, avail_new, (uint8_t)g.k_max, c->st);
+  launch_set_avail(c->at<uint8_t>(p.avail), p.av_pitch, P0, batch, n_new, avail_new, (uint8_t)g.k_max, (uint8_t)kept_depths(g), c->st);
   if (avail_new) materialize_depths(c, batch, P0, n_new);
   int rc = c->hip_check("extend launch");
   if (rc) return rc;

@@ -130,16 +130,19 @@ __global__ void k_fill_u8(uint8_t* dst, size_t n, uint8_t v) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) dst[i] = v;
 }
-// dst[b * pitch + j0 + j] = src ? src[b * n + j] : v for b < B, j < n
-__global__ void k_set_avail(uint8_t* dst, int pitch, int j0, int B, int n, const uint8_t* src, uint8_t v) {
+// dst[b * pitch + j0 + j] = min(src ? src[b * n + j] : v, cap) for b < B, j < n
+__global__ void k_set_avail(uint8_t* dst, int pitch, int j0, int B, int n, const uint8_t* src, uint8_t v,
+                            uint8_t cap) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (size_t)B * n) return;
   const size_t b = i / n, j = i % n;
-  dst[b * pitch + j0 + j] = src ? src[i] : v;
+  const uint8_t a = src ? src[i] : v;
+  dst[b * pitch + j0 + j] = a < cap ? a : cap;
 }
-void launch_set_avail(uint8_t* dst, int pitch, int j0, int B, int n, const uint8_t* src, uint8_t v, hipStream_t st) {
+void launch_set_avail(uint8_t* dst, int pitch, int j0, int B, int n, const uint8_t* src, uint8_t v, uint8_t cap,
+                      hipStream_t st) {
   const size_t total = (size_t)B * n;
-  if (total) k_set_avail<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(dst, pitch, j0, B, n, src, v);
+  if (total) k_set_avail<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(dst, pitch, j0, B, n, src, v, cap);
 }
 
 }  // namespace alodlm

@@ -85,7 +85,8 @@ class Engine:
             max_prefill_rows=max_prefill_rows if max_prefill_rows is not None else min(
                 w.batch * max(w.prefix, max_prefix or 0), max(w.prefix, max_prefix or 0, 8192)),
             mask_id=w.mask_id, dtype=self.cdtype, rms_eps=w.rms_eps, rope_theta=w.rope_theta,
-            depth_on_demand=1 if depth_on_demand else 0, kv_dtype=B.KV_FP8 if w.kv_dtype == "fp8" else B.KV_SAME)
+            depth_on_demand=1 if depth_on_demand else 0, kv_dtype=B.KV_FP8 if w.kv_dtype == "fp8" else B.KV_SAME,
+            cache_depths=w.cache_depths)
         nl = D.n_layers
         self.layer_arr = (B.LayerWeights * max(nl, 1))()
         for l in range(nl):

@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step-only", action="store_true",
                     help="report the step (headline, tau sweep, kernel classes) only: no depth-on-demand prefill, "
-                         "sampled commits, outer loop or fp8 K/V sections (for profiling runs)")
+                         "sampled commits, outer loop, fp8 K/V or depth eviction sections (for profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (known traffic, for calibrating HBM counters)")
     args = ap.parse_args()
@@ -189,7 +189,9 @@ def main():
     traffic = ffn_gate_up_traffic(w, rows_per_step * args.steps, launches)
     achieved = traffic / (per_launch_ms * 1e-3) / 1e9
     work = algorithmic_work(w, loops)
-    sampled = outer = kv_fp8 = None
+    # the headline step's decisions (every timed step takes the same ones), for the eviction section
+    tok_full, cl_full = e.out_tokens.cpu().numpy(), e.out_cl.cpu().numpy()
+    sampled = outer = kv_fp8 = kv_evict = None
     if not args.step_only:
         # Sampled commits (Gumbel-max draws in the LM-head epilogue): the same step and timing pass
         # with ALODLM_STEP_SAMPLE, reported beside the greedy headline.
@@ -238,6 +240,31 @@ def main():
                       cache_bytes=kv_bytes, cache_bytes_bf16=2 * kv_bytes)
         progress("fp8 K/V: %s" % kv_fp8)
         e8.close()
+        del e8
+        # Depth eviction: engines whose cache keeps Core depths 1..D only (loops past D read depth D),
+        # with the cache bytes they hold and the share of positions both steps commit that get the
+        # same token as on the full-depth cache
+        kv_evict = {}
+        plane = 2 * w.batch * w.prefix * D.n_kv_heads * D.head_dim * 2      # K and V of one slot, bf16
+        for keep in (2, 1):
+            torch.cuda.empty_cache()
+            ev = Engine(replace(w, cache_depths=keep))
+            ev.prefill()
+            t0 = time.perf_counter()
+            ev.prefill()
+            torch.cuda.synchronize()
+            pf_ms = (time.perf_counter() - t0) * 1e3
+            fe = timed(w.tau_ent, args.steps, args.warmup, engine=ev)
+            tok, cl = ev.out_tokens.cpu().numpy(), ev.out_cl.cpu().numpy()
+            both = (cl != 0) & (cl_full != 0)
+            kv_evict["keep_%d" % keep] = dict(
+                tok_s=fe["tok_s"], ms_per_step=fe["ms_per_step"], committed_per_step=fe["committed_per_step"],
+                loops=fe["loops"], prefill_ms=pf_ms, cache_bytes=plane * (D.kv_slots(keep) + 1),
+                cache_bytes_full=plane * D.kv_slots(w.k_max),
+                token_agreement=float((tok[both] == tok_full[both]).mean()) if both.any() else None)
+            progress("depth eviction, %d kept: %s" % (keep, kv_evict["keep_%d" % keep]))
+            ev.close()
+            del ev
     kernels = {}
     for k, v in kt.items():
         ms = v[0] / args.steps
@@ -276,6 +303,7 @@ def main():
         "sampled_commits": sampled,
         "outer_loop": outer,
         "kv_fp8": kv_fp8,
+        "kv_evict": kv_evict,
         "prefill_ms": prefill_ms,
         "prefill_depth_on_demand": None if args.step_only else {
             "depth1_ms": prefill_d1_ms, "deepen_to_kmax_ms": deepen_ms, "prefix_tokens": w.batch * w.prefix},

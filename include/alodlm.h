@@ -20,7 +20,8 @@
  * The prefix is held in a depth-aware KV cache (same page, sections
  * "Background" and "Limitations"): Prelude and Coda layers keep one K/V set,
  * every Core layer keeps one set per loop depth 1..k_max, i.e.
- * n_pre + n_core * k_max + n_coda slots (84 for the 8B split at K = 4).
+ * n_pre + n_core * k_max + n_coda slots (84 for the 8B split at K = 4), or
+ * only depths 1..cache_depths of the Core under depth eviction.
  *
  * Conventions for every entry point:
  *   - "device" pointers are HIP device memory on the context's device,
@@ -89,6 +90,14 @@ typedef struct alodlm_config {
                               ([max_batch][max_prefix][d] fp32) so that alodlm_prefill_kv_depth /
                               alodlm_deepen_kv can build the cache depth by depth; 0: not */
   int32_t kv_dtype;     /* ALODLM_KV_SAME or ALODLM_KV_FP8 */
+  int32_t cache_depths; /* depth eviction (summary page, section "Limitations": the memory of the
+                           per-depth buffers, remedied by dropping low-value depths): the cache
+                           keeps Core depths 1..cache_depths only, so every available depth is
+                           clipped to it and deeper loops read the deepest kept plane (the
+                           fallback rule); 0 = every depth (k_max).  0..k_max; with
+                           depth_on_demand only 0 or k_max.  The prefill still runs all k_max
+                           Core passes (the Coda set is built on the depth-k_max output), the
+                           deeper ones in one extra scratch plane. */
 } alodlm_config;
 
 /* One transformer layer (Qwen3 block).  Device pointers in the config dtype,
@@ -119,7 +128,9 @@ typedef struct alodlm_ctx alodlm_ctx;
  * tables and step scratch).  Host only; no device work. */
 ALODLM_API int alodlm_workspace_bytes(const alodlm_config* cfg, size_t* bytes);
 
-/* Number of prefix-cache slots: n_pre + n_core * k_max + n_coda. */
+/* Number of prefix-cache slots: n_pre + n_core * D + n_coda, D = the kept depths (cache_depths,
+ * or k_max when 0).  Slot order: Prelude layers, then each Core layer's depths 1..D, then the
+ * Coda layers. */
 ALODLM_API int alodlm_kv_slots(const alodlm_config* cfg, int32_t* slots);
 
 /* Creates a context.  cfg and w are copied (the layer array too); the device
@@ -163,7 +174,9 @@ ALODLM_API int alodlm_deepen_kv(alodlm_ctx* ctx, int32_t depth);
  * long-context measurements).  Element (slot, b, h, j, e) of K is draw
  * ((b*Hkv + h)*prefix_len + j)*hd + e of Philox4x32-10 stream (seed, 0x10000 + 2*slot)
  * mapped to the Irwin-Hall(4) value times k_scale (V: stream + 1, v_scale), as
- * defined in alodlm_synth.h.  avail_depth as in alodlm_prefill_kv.  Asynchronous. */
+ * defined in alodlm_synth.h; `slot` numbers the slots of the cache that keeps every depth (with
+ * cache_depths below k_max, the kept slots take the draws they have there).  avail_depth as in
+ * alodlm_prefill_kv (clipped to the kept depths).  Asynchronous. */
 ALODLM_API int alodlm_prefill_kv_synthetic(alodlm_ctx* ctx, int32_t batch, int32_t prefix_len, uint32_t seed,
                                 float k_scale, float v_scale, const uint8_t* avail_depth);
 
@@ -233,6 +246,8 @@ ALODLM_API int alodlm_denoise_step(alodlm_ctx* ctx, const alodlm_step_args* args
  *              NULL (k_max).
  * batch == the cached batch; 1 <= n_new and cached length + n_new <= max_prefix, else EINVAL;
  * before any prefill, ESTATE.  Asynchronous. */
+/* With cache_depths below k_max the new positions still run all k_max Core passes, reading cached
+ * positions at the deepest kept depth min(d, available depth), and keep depths 1..cache_depths. */
 ALODLM_API int alodlm_extend_kv(alodlm_ctx* ctx, int32_t batch, int32_t n_new, const int32_t* new_ids,
                                 const uint8_t* avail_new);
 

@@ -52,8 +52,9 @@ __attribute__((visibility("default"))) int alodlm_diag_readout_sample(int32_t M,
 
 /* Copies prefix-cache rows back for inspection: K and V of cache slot `slot`, sequence b,
  * positions j0 .. j0+n-1, every kv head, into dst_k / dst_v (device, config dtype,
- * [Hkv][n][hd]).  After a prefill the Core depth slot of depth p holds position j at depth
- * min(p, available depth of j): the values a loop-p step reads.  Asynchronous on the context
+ * [Hkv][n][hd]; the slot numbering of alodlm_kv_slots).  After a prefill the Core depth slot of
+ * depth p holds position j at depth min(p, available depth of j): the values a loop-p step reads.
+ * With fp8 K/V the copies are the stored E4M3 bytes.  Asynchronous on the context
  * stream.  Returns 0, -1 (bad arguments), -4 (launch failed). */
 __attribute__((visibility("default"))) int alodlm_diag_read_kv(const struct alodlm_ctx* ctx, int32_t slot, int32_t b,
                                                                int32_t j0, int32_t n, void* dst_k, void* dst_v);

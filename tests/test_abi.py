@@ -86,6 +86,27 @@ def test_fp8_kv_config_rules_and_workspace():
     assert abs((dod - base) - 8 * 1024 * 4096 * 4) < 2 ** 20
 
 
+def test_depth_eviction_config_rules_and_workspace():
+    """cache_depths D in 0..k_max keeps Core depths 1..D: n_pre + n_core * D + n_coda slots plus one
+    scratch plane for the deeper passes; with depth-on-demand only 0 or k_max."""
+    for bad in (-1, 5):
+        with pytest.raises(B.AlodlmError) as e:
+            B.workspace_bytes(_cfg(cache_depths=bad))
+        assert e.value.code == B.EINVAL
+    for D in (1, 2, 3):
+        with pytest.raises(B.AlodlmError) as e:
+            B.workspace_bytes(_cfg(cache_depths=D, depth_on_demand=1))
+        assert e.value.code == B.EINVAL
+    assert B.workspace_bytes(_cfg(cache_depths=4, depth_on_demand=1)) == B.workspace_bytes(_cfg(depth_on_demand=1))
+    base = B.workspace_bytes(_cfg())
+    assert B.kv_slots(_cfg()) == B.kv_slots(_cfg(cache_depths=4)) == 84 and B.workspace_bytes(_cfg(cache_depths=4)) == base
+    plane = 2 * 8 * 8 * 1024 * 128 * 2          # K and V of one slot: B * Hkv * P * hd bf16
+    for D in (1, 2, 3):
+        assert B.kv_slots(_cfg(cache_depths=D)) == 36 + 16 * (D - 1)
+        saved = base - B.workspace_bytes(_cfg(cache_depths=D))
+        assert saved == (16 * (4 - D) - 1) * plane
+
+
 def _weights(nl, ptr=0x1000):
     layers = (B.LayerWeights * nl)()
     for l in range(nl):
