@@ -7,7 +7,9 @@
 //                 global->LDS loads with XOR-swizzled 16-byte chunks, explicit vmcnt waits;
 //   k_gemm_adirect activations straight to registers, weights through the LDS ring;
 //   k_gemm_ring2  separate activation / weight ring depths;
-//   k_gemm_ws     wave-specialised loads (half the waves fetch activations, half weights).
+//   k_gemm_ws     wave-specialised loads (half the waves fetch activations, half weights);
+//   k_gemm_wide   eight 64-row waves over 256-row tiles, 32-deep stages, each stage's fragments
+//                 read while the matrix cores work on the previous one (many rows).
 // Tiles are numbered so that the blocks the dispatcher sends to one XCD (block ids congruent
 // mod 8) are consecutive tiles with the row tile varying fastest: the few row tiles that share
 // a weight column tile run on the same XCD at about the same time and find it in its L2.
@@ -441,6 +443,156 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const bf16_t* __rest
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kc][a], bfr[kc][b], acc[a][b], 0, 0, 0);
   }
   gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid, (SoftStat*)smem);
+}
+
+// Wide tiles for many rows (prefill, long-context steps), where the matrix cores rather than the
+// weight stream bound the GEMM.  Eight waves hold 64 x (BN / 2) accumulator tiles each, so every
+// 16-byte fragment read from LDS feeds (TM * TN) / (TM + TN) MFMAs, about twice the reuse of the
+// 128-row tiles.  Stages are 32 deep in K (64-byte rows, four 16-byte chunks, chunk c of row r at
+// slot c ^ ((r >> 2) & 3): the 16 rows one fragment read touches cover all banks once), so
+// NS stages of a 256 x 256 tile fit in LDS with NS - 2 stages of load latency cover.  Each
+// stage's fragments are read into one of two register sets while the matrix cores work on the
+// other stage's; the reads are retired with explicit LDS-counter waits one stage later (the
+// compiler's own waits treat the direct-to-LDS loads as unordered with the fragment reads and
+// would wait for the reads just issued as well).  The stage requested in iteration it
+// overwrites the slot of stage it - 1, whose fragments every wave has retired before arriving
+// at iteration it's barrier.
+constexpr int WK = 32;  // K per stage of the wide tiles
+
+template <int BM, int BN, int WM, int WN, int NS, int EPI, bool SPLIT>
+__device__ __forceinline__ void gemm_wide_body(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B,
+                                               int ldb, int M, int N, int K, int k_split, int m_tiles, int n_tiles,
+                                               int splits, const int32_t* __restrict__ m_dev, const GemmEpi& ep,
+                                               int F, bf16_t* smem) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  constexpr int ROWS = BM + BN;                 // 64-byte rows per stage
+  constexpr int STAGE = ROWS * WK;              // bf16 elements per stage
+  constexpr int LPW = ROWS / (16 * NW);         // load instructions per wave per stage
+  static_assert(TM * WM * 16 == BM && TN * WN * 16 == BN && ROWS % (16 * NW) == 0, "waves must tile the block");
+  static_assert(NS >= 3, "fragment prefetch needs three or more stages");
+
+  const int total = m_tiles * n_tiles * splits;
+  const int per = (gridDim.x + 7) >> 3;
+  const int T = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (T >= total) return;
+  const int mt = T % m_tiles;
+  const int rest = T / m_tiles;
+  const int nt = rest % n_tiles;
+  const int sp = rest / n_tiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+  int Mr = M;
+  if (m_dev) Mr = min(Mr, *m_dev);
+  if (m0 >= Mr) return;
+  const int kb = sp * k_split;
+  const int nk = (min(K, kb + k_split) - kb) / WK;
+
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int wm = wid / WN, wn = wid % WN;
+
+  // load instruction j of this wave fills stage rows (wid * LPW + j) * 16 .. + 15; this lane's
+  // 16 bytes land at row rho, slot lane & 3, and hold global chunk (lane & 3) ^ ((rho >> 2) & 3)
+  const bf16_t* src[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int rho = (wid * LPW + j) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((rho >> 2) & 3);
+    if (rho < BM) {
+      const int gm = m0 + rho;
+      src[j] = A + (size_t)(gm < Mr ? gm : 0) * lda + c * 8;
+    } else {
+      const int gn = n0 + rho - BM;
+      const int ok = gn < N ? gn : 0;
+      const int brow = (EPI == EPI_SWIGLU) ? swiglu_b_row(ok, F) : ok;
+      src[j] = B + (size_t)brow * ldb + c * 8;
+    }
+  }
+  auto issue = [&](int stage_k, int slot) {
+    bf16_t* base = smem + slot * STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + stage_k), LDS_PTR(base + (wid * LPW + j) * 16 * WK), 16,
+                                       0, 0);
+  };
+
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(kb + s * WK, s);
+
+  const int col = lane & 15, quad = lane >> 4;
+  auto read = [&](int slot, bf16x8_t (&fa)[TM], bf16x8_t (&fb)[TN]) {
+    const bf16_t* st = smem + slot * STAGE;
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      const int r = wm * TM * 16 + a * 16 + col;
+      fa[a] = *(const bf16x8_t*)&st[r * WK + ((quad ^ ((r >> 2) & 3)) << 3)];
+    }
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      const int r = BM + wn * TN * 16 + b * 16 + col;
+      fb[b] = *(const bf16x8_t*)&st[r * WK + ((quad ^ ((r >> 2) & 3)) << 3)];
+    }
+  };
+  auto mma = [&](bf16x8_t (&fa)[TM], bf16x8_t (&fb)[TN]) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+  };
+  // Iteration it: make stage it + 1 visible, request stage it + NS - 1, retire stage it's
+  // fragment reads, read stage it + 1's into the other register set (unconditionally: in the
+  // last iteration the slot read is one no load writes any more, into registers nobody uses),
+  // then multiply stage it.
+  auto step = [&](int it, bf16x8_t (&ca)[TM], bf16x8_t (&cb)[TN], bf16x8_t (&na)[TM], bf16x8_t (&nb)[TN]) {
+    if (it + 1 < nk) {
+      if (it + NS - 2 <= nk - 1)
+        wait_vmcnt_le<(NS - 3) * LPW>();
+      else
+        wait_vmcnt_le<0>();
+      lds_barrier();
+      if (it + NS - 1 < nk) issue(kb + (it + NS - 1) * WK, (it + NS - 1) % NS);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
+    read((it + 1) % NS, na, nb);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(ca, cb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  if (nk > 0) {
+    if (NS - 2 <= nk - 1)
+      wait_vmcnt_le<(NS - 2) * LPW>();
+    else
+      wait_vmcnt_le<0>();
+    lds_barrier();
+    read(0, fa0, fb0);
+  }
+  for (int it = 0; it < nk; it += 2) {
+    step(it, fa0, fb0, fa1, fb1);
+    if (it + 1 < nk) step(it + 1, fa1, fb1, fa0, fb0);
+  }
+  gemm_epilogue<BM, BN, WM, WN, EPI, SPLIT>(acc, m0, n0, nt, sp, Mr, M, N, ep, wm, wn, lane, tid, (SoftStat*)smem);
+}
+
+// Eight waves (two per SIMD), 64-row wave tiles.
+template <int BM, int BN, int NS, int EPI, bool SPLIT>
+__global__ __launch_bounds__(512) void k_gemm_wide(const bf16_t* __restrict__ A, int lda,
+                                                   const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
+                                                   int k_split, int m_tiles, int n_tiles, int splits,
+                                                   const int32_t* __restrict__ m_dev, GemmEpi ep, int F) {
+  constexpr int WM = BM / 64;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * (BM + BN) * WK];
+  gemm_wide_body<BM, BN, WM, 8 / WM, NS, EPI, SPLIT>(A, lda, B, ldb, M, N, K, k_split, m_tiles, n_tiles, splits,
+                                                     m_dev, ep, F, smem);
 }
 
 // Dual-ring variant: the activation tile (re-read by every column tile, so it comes from L2) and
@@ -906,6 +1058,27 @@ static void run_pipe(int epi, bool split, dim3 grid, const bf16_t* A, int lda, c
 #undef GO
 }
 
+template <int BM, int BN, int NS>
+static void run_wide(int epi, bool split, dim3 grid, const bf16_t* A, int lda, const bf16_t* B, int ldb, int M,
+                     int N, int K, int k_split, int mt, int nt, int splits, const int32_t* m_dev, const GemmEpi& ep,
+                     int F, hipStream_t st) {
+#define GO(E, S)                                                                                                \
+  k_gemm_wide<BM, BN, NS, E, S><<<grid, 512, 0, st>>>(A, lda, B, ldb, M, N, K, k_split, mt, nt, splits, m_dev, ep, F)
+  if (split) {
+    if (epi == EPI_SWIGLU) GO(EPI_SWIGLU, true);
+    else GO(EPI_STORE, true);
+  } else if (epi == EPI_STORE) {
+    GO(EPI_STORE, false);
+  } else if (epi == EPI_RESID) {
+    GO(EPI_RESID, false);
+  } else if (epi == EPI_SWIGLU) {
+    GO(EPI_SWIGLU, false);
+  } else {
+    GO(EPI_SOFTSTAT, false);
+  }
+#undef GO
+}
+
 template <int BM, int BN, int WM, int WN, int DA, int DB>
 static void run_ring2(int epi, bool split, dim3 grid, const bf16_t* A, int lda, const bf16_t* B, int ldb, int M,
                       int N, int K, int k_split, int mt, int nt, int splits, const int32_t* m_dev, const GemmEpi& ep,
@@ -1021,8 +1194,10 @@ static const TileCfg kTiles[] = {
     // eight waves, wave-specialised loads (activation stream DA deep, weight stream DB deep)
     {128, 192, 2}, {128, 192, 2}, {128, 192, 2}, {128, 128, 4}, {128, 128, 4}, {64, 128, 4}, {256, 128, 2},
     // eight waves, deeper LDS ring
-    {128, 192, 2}, {128, 128, 4}, {128, 192, 4}};
-constexpr int kNumTiles = 59;
+    {128, 192, 2}, {128, 128, 4}, {128, 192, 4},
+    // wide tiles (many rows): eight 64-row waves, 32-deep stages, fragments prefetched
+    {256, 256, 2}, {256, 256, 2}, {256, 128, 2}, {128, 256, 4}, {256, 256, 2}};
+constexpr int kNumTiles = 64;
 
 bool swiglu_single_pass_ok(int tile) { return ((kTiles[tile].bn / kTiles[tile].wn / 16) & 1) == 0; }
 
@@ -1054,8 +1229,10 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   // 512 / 1024 / 2048 / 8192 rows on the 8B projections
   *splits = 1;
   if (epi == EPI_SOFTSTAT) return 17;
-  if (M >= 4096) return 44;
-  if (M >= 1536) return epi == EPI_STORE ? 47 : 37;
+  // wide eight-wave tiles where the matrix cores bound the GEMM: every projection at >= 4096
+  // rows (8192-row prefill: gate/up 1.84 -> 1.60 ms, down 0.94 -> 0.85), gate/up from 1536
+  if (M >= 4096) return 59;
+  if (M >= 1536) return epi == EPI_SWIGLU ? 60 : (epi == EPI_STORE ? 47 : 37);
   if (epi == EPI_SWIGLU) return M >= 768 ? 44 : 47;
   if (epi == EPI_STORE) return M >= 768 ? 47 : 38;
   return 38;
@@ -1187,6 +1364,14 @@ int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, in
     case 57: P8(128, 128, 2, 4, 5); break;
     case 58: P8(128, 192, 2, 4, 4); break;
 #undef P8
+#define WD(BM_, BN_, NS_) \
+  run_wide<BM_, BN_, NS_>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, e, F, st)
+    case 59: WD(256, 256, 4); break;
+    case 60: WD(256, 256, 5); break;
+    case 61: WD(256, 128, 6); break;
+    case 62: WD(128, 256, 6); break;
+    case 63: WD(256, 256, 3); break;
+#undef WD
 
   }
 #undef T

@@ -52,7 +52,7 @@ def test_gemm_store_and_resid(gpu_lib, M, N, K):
     assert err < 2e-5, err
 
 
-@pytest.mark.parametrize("tile", range(59))
+@pytest.mark.parametrize("tile", range(64))
 def test_gemm_every_tile(gpu_lib, tile):
     M, N, K = 300, 1024, 1024
     A, Bm = _bf16((M, K), 10), _bf16((N, K), 11, 0.02)
@@ -71,7 +71,7 @@ def test_gemm_every_tile(gpu_lib, tile):
     assert err.max() < 1.6e-2
 
 
-@pytest.mark.parametrize("tile", range(59))
+@pytest.mark.parametrize("tile", range(64))
 def test_softstat_every_tile(gpu_lib, tile):
     """LM-head readout statistics (entropy, log-sum-exp, argmax over the columns) of every tile,
     on a ragged shape, against float64 arithmetic on the same bf16 operands."""
@@ -98,7 +98,7 @@ def test_softstat_every_tile(gpu_lib, tile):
     assert ok.all()
 
 
-@pytest.mark.parametrize("tile", list(range(59)) + ["generic"])
+@pytest.mark.parametrize("tile", list(range(64)) + ["generic"])
 def test_readout_sample_every_tile(gpu_lib, tile):
     """Gumbel-max draws of the LM-head kernel (every tile and the vector-ALU path), on a ragged
     shape, against argmax(z + g) with z in float64 on the same bf16 operands and g the oracle's own
