@@ -31,11 +31,15 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int AKT = 64;  // keys per tile
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)from_f<bf16_t>(lo) | ((uint32_t)from_f<bf16_t>(hi) << 16);
-}
-
 typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Two floats as two bf16 (round to nearest even) in one 32-bit word, lo in the low half: one
+// packed conversion instruction on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const float2v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+}
 
 // Two E4M3 bytes of w (the low half when HI is false, else the high half) as two bf16 (exact:
 // bf16 keeps 7 fraction bits).
@@ -123,6 +127,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
       qf[nq][c] = *(bf16x8_t*)&v;
     }
   }
+
+  const float scale2 = p.scale * 1.44269504088896341f;  // softmax scale times log2(e)
 
   // segment bases of this (sequence, kv head)
   const bf16_t* kpre = (const bf16_t*)p.ck + (size_t)b * p.c_kSeq + (size_t)kvh * p.c_kHead;
@@ -265,22 +271,37 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
       }
     }
 
-    // online softmax per query column; probabilities packed as the B operand of the PV product
+    // Online softmax per query column in base-2 units: scores times scale * log2(e), so each
+    // probability is one hardware exp2.  Masking runs only on tiles that need it (the segment's
+    // last tile, or own keys under a causal mask); rows past the block (qok false) need none:
+    // their query is zero, and their column is never written.
+    const bool full = k0 + AKT <= klen && !(p.causal && !pre);
     bf16x8_t pb[2][NQ];
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
       float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int kk = k0 + ks * 16 + quad * 4 + v;  // key within its segment
-          bool ok = kk < klen && qok[nq];
-          if (p.causal && !pre) ok = ok && kk <= qpos[nq] + p.causal_off;
-          const float sc = ok ? s[ks][nq][v] * p.scale : -INFINITY;
-          s[ks][nq][v] = sc;
-          mx = fmaxf(mx, sc);
-        }
+          for (int v = 0; v < 4; ++v) {
+            const float sc = s[ks][nq][v] * scale2;
+            s[ks][nq][v] = sc;
+            mx = fmaxf(mx, sc);
+          }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int kk = k0 + ks * 16 + quad * 4 + v;  // key within its segment
+            bool ok = kk < klen;
+            if (p.causal && !pre) ok = ok && kk <= qpos[nq] + p.causal_off;
+            const float sc = ok ? s[ks][nq][v] * scale2 : -INFINITY;
+            s[ks][nq][v] = sc;
+            mx = fmaxf(mx, sc);
+          }
+      }
       // Raise the column's running max only when some lane saw a larger score: the test is a
       // wave vote, and the cross-lane max (two crossbar shuffles) runs only then -- after the
       // first tiles most tiles skip it.  lrun holds this lane's partial sum (its 16 keys of each
@@ -289,20 +310,20 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mnew = fmaxf(mrun[nq], mx);
-        const float corr = mrun[nq] == -INFINITY ? 0.f : __expf(mrun[nq] - mnew);
+        const float corr = __builtin_amdgcn_exp2f(mrun[nq] - mnew);  // 0 while mrun is -inf
         lrun[nq] *= corr;
 #pragma unroll
         for (int h = 0; h < NH; ++h) o[h][nq] *= corr;
         mrun[nq] = mnew;
       }
-      const float mref = mrun[nq];
+      const float mref = mrun[nq] == -INFINITY ? 0.f : mrun[nq];  // masked scores give exp2(-inf) = 0
       float sum = 0.f;
       float pv[4][4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float e = mref == -INFINITY ? 0.f : __expf(s[ks][nq][v] - mref);
+          const float e = __builtin_amdgcn_exp2f(s[ks][nq][v] - mref);
           pv[ks][v] = e;
           sum += e;
         }
@@ -367,7 +388,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
 #pragma unroll
       for (int h = 0; h < NH; ++h) *(float4*)&part[h * 16 + quad * 4] = make_float4(o[h][nq][0], o[h][nq][1], o[h][nq][2], o[h][nq][3]);
       if (quad == 0) {
-        part[HD] = mrun[nq];
+        part[HD] = mrun[nq] * 0.69314718055994531f;  // base-2 running max back in natural units
         part[HD + 1] = lrun[nq];
       }
     }
