@@ -9,12 +9,15 @@
 //
 // Both operand tiles stream straight from memory into an NS-stage LDS ring with direct
 // global->LDS loads, no register staging and no transposition:
-//   K tile [64 keys][HD] (hd-contiguous rows), 16-byte chunks XOR-swizzled by row;
+//   K tile [64 keys][HD] (hd-contiguous rows), 16-byte chunks XOR-swizzled by row (kswz);
 //   V^T tile [HD][64 keys] -- the cache stores V transposed (positions contiguous), which is
 //   the operand layout of the P.V product -- chunks swizzled by (row / 2).
 // S^T = K Q^T on the matrix cores (Q in registers as the B operand), so every lane holds 16
 // scores of one query column: the online softmax needs no LDS round trip and the
-// probabilities are already laid out as the B operand of O^T += V^T P^T.
+// probabilities are already laid out as the B operand of O^T += V^T P^T.  The rows of each
+// 16-key S product are a permutation of the tile's keys chosen so that the 8 probabilities a
+// lane feeds one P.V product are 8 consecutive keys: each V^T fragment is then one 16-byte
+// chunk of a row.
 // With several key splits, partial (O, max, sum) go to a scratch buffer and k_attn_merge
 // combines them in a fixed order.
 // F8: keys and values are stored in FP8 E4M3 (half the bytes).  The fp8 tiles stream into the
@@ -30,6 +33,20 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int AKT = 64;  // keys per tile
+
+// Key of row i (0..15) of the ks-th 16-row S product: subtiles 2c and 2c+1 interleave the keys
+// of 32-key group c in blocks of four, so lane quad q (rows 4q .. 4q+3) of the pair holds keys
+// 32c + 8q .. 32c + 8q + 7.
+__device__ __forceinline__ int s_key(int ks, int i) { return (ks >> 1) * 32 + (i >> 2) * 8 + (ks & 1) * 4 + (i & 3); }
+
+// K-tile chunk swizzle: the 16 key rows one S fragment read touches (b + {0..3, 8..11, 16..19,
+// 24..27}) fall in distinct LDS banks.
+template <int HD>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (HD == 128) return (r & 3) | (((r >> 3) & 3) << 2);
+  else if constexpr (HD == 64) return ((r >> 1) & 1) | (((r >> 3) & 3) << 1);
+  else return (r >> 3) & 3;
+}
 
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -146,7 +163,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
 #pragma unroll
   for (int i = 0; i < KL; ++i) {
     krow[i] = (wid * KL + i) * RPI + lane / CK;
-    kchunk[i] = (lane % CK) ^ (krow[i] & (CK - 1));
+    kchunk[i] = (lane % CK) ^ kswz<HD>(krow[i]);
   }
 #pragma unroll
   for (int i = 0; i < VL; ++i) {
@@ -237,8 +254,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
         uint4 lo, hi;
         fp8x16_to_bf16(in, lo, hi);
         const int r = q / CK8, c = 2 * (q % CK8);
-        *(uint4*)&wK[r * HD + ((c ^ (r & (CK - 1))) << 3)] = lo;
-        *(uint4*)&wK[r * HD + (((c + 1) ^ (r & (CK - 1))) << 3)] = hi;
+        *(uint4*)&wK[r * HD + ((c ^ kswz<HD>(r)) << 3)] = lo;
+        *(uint4*)&wK[r * HD + (((c + 1) ^ kswz<HD>(r)) << 3)] = hi;
       }
       for (int q = tid; q < HD * 4; q += NW * 64) {
         const uint4 in = *(const uint4*)(s8 + AKT * HD + q * 16);
@@ -264,8 +281,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int r = ks * 16 + col;
-        const bf16x8_t a = *(const bf16x8_t*)&sK[r * HD + (((c * 4 + quad) ^ (r & (CK - 1))) << 3)];
+        const int r = s_key(ks, col);
+        const bf16x8_t a = *(const bf16x8_t*)&sK[r * HD + (((c * 4 + quad) ^ kswz<HD>(r)) << 3)];
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq) s[ks][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nq][c], s[ks][nq], 0, 0, 0);
       }
@@ -279,29 +296,27 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
     bf16x8_t pb[2][NQ];
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
+      // raw scores; masked ones become -inf (exp2 of -inf is 0)
       float mx = -INFINITY;
       if (full) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float sc = s[ks][nq][v] * scale2;
-            s[ks][nq][v] = sc;
-            mx = fmaxf(mx, sc);
-          }
+          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[ks][nq][v]);
       } else {
+        const int lim = (p.causal && !pre) ? qpos[nq] + p.causal_off : klen;  // last visible own key
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int kk = k0 + ks * 16 + quad * 4 + v;  // key within its segment
-            bool ok = kk < klen;
-            if (p.causal && !pre) ok = ok && kk <= qpos[nq] + p.causal_off;
-            const float sc = ok ? s[ks][nq][v] * scale2 : -INFINITY;
+            const int kk = k0 + s_key(ks, quad * 4 + v);  // key within its segment
+            const bool ok = (kk < klen) & (kk <= lim);
+            const float sc = ok ? s[ks][nq][v] : -INFINITY;
             s[ks][nq][v] = sc;
             mx = fmaxf(mx, sc);
           }
       }
+      mx *= scale2;  // the scale is positive: the max of the scaled scores
       // Raise the column's running max only when some lane saw a larger score: the test is a
       // wave vote, and the cross-lane max (two crossbar shuffles) runs only then -- after the
       // first tiles most tiles skip it.  lrun holds this lane's partial sum (its 16 keys of each
@@ -323,7 +338,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float e = __builtin_amdgcn_exp2f(s[ks][nq][v] - mref);
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[ks][nq][v], scale2, -mref));
           pv[ks][v] = e;
           sum += e;
         }
@@ -339,22 +354,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
       }
     }
 
-    // O^T += V^T P^T ; lane's 8 k-slots are keys 32c2 + 4quad + {0..3} and 32c2 + 16 + 4quad + {0..3}
+    // O^T += V^T P^T ; lane's 8 k-slots are keys 32c2 + 8quad + {0..7}: one 16-byte chunk
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const int r = h * 16 + col;
       const int sw = (r >> 1) & 7;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const int lo = c2 * 32 + quad * 4, hi = lo + 16;  // first keys of the two 8-byte pieces
-        const uint2 a0 = *(const uint2*)&sV[r * AKT + ((((lo >> 3) ^ sw) << 3) | (lo & 7))];
-        const uint2 a1 = *(const uint2*)&sV[r * AKT + ((((hi >> 3) ^ sw) << 3) | (hi & 7))];
-        uint4 w;
-        w.x = a0.x;
-        w.y = a0.y;
-        w.z = a1.x;
-        w.w = a1.y;
-        const bf16x8_t a = *(bf16x8_t*)&w;
+        const bf16x8_t a = *(const bf16x8_t*)&sV[r * AKT + (((c2 * 4 + quad) ^ sw) << 3)];
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq) o[h][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[c2][nq], o[h][nq], 0, 0, 0);
       }
