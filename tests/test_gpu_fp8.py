@@ -119,3 +119,9 @@ def test_mid_fp8_outer_loop_and_append(gpu_lib):
         ref = orc.prefill_sequence(ids, W, w.dims, w.k_max, w.rms_eps, w.rope_theta, kv="fp8")
         ref16 = orc.prefill_sequence(ids, W, w.dims, w.k_max, w.rms_eps, w.rope_theta, kv="fp8", prec="bf16")
         log("seq %d grown cache worst/tol %.3f" % (b, _check_cache(e, w, b, w.prefix + w.block, ref, ref16)))
+
+
+def test_mid_fp8_head_dim_64(gpu_lib):
+    """fp8 K/V at hd 64: the conversion pass into the 64-wide working tile and its swizzle."""
+    dims = replace(MID_DIMS, head_dim=64, n_q_heads=8, n_kv_heads=1)
+    _check_step(replace(_mid(prefix=200, batch=2), dims=dims))

@@ -216,6 +216,16 @@ def test_mid_bf16_sampled_step(gpu_lib):
     _check_step(_mid(tau_ent=7.0, boost_lo=3.0, boost_hi=8.0), gpu_lib, sample=SAMPLE)
 
 
+def test_mid_bf16_head_dim_64(gpu_lib):
+    """hd 64 (the matrix-core attention's 64-wide K rows and their chunk swizzle), 8 query heads
+    per kv head, ragged prefix, prefix built by the causal prefill; then a synthetic depth-fallback
+    cache."""
+    dims = replace(MID_DIMS, head_dim=64, n_q_heads=8, n_kv_heads=1)
+    _check_step(replace(_mid(prefix=200, batch=2), dims=dims), gpu_lib)
+    _check_step(replace(_mid(kv="synthetic", short_frac=0.25, short_depth=2, tau_ent=0.0, tau_halt=2.0, prefix=260,
+                             batch=2), dims=dims), gpu_lib)
+
+
 def test_mid_fp32_matches_bf16_structure(gpu_lib):
     # fp32 mode on the same shapes (generic kernels) at the fp32 tolerance
     _check_step(_mid(dtype="fp32", prefix=100), gpu_lib)
