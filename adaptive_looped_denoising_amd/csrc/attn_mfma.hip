@@ -271,22 +271,53 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
     const int k0 = pre ? tile * AKT : (tile - TP) * AKT;
     const int klen = pre ? p.n_cache : p.n_self;
 
-    // S^T = K Q^T : 4 key subtiles x NQ query subtiles
+    // S^T = K Q^T : 4 key subtiles x NQ query subtiles, hd chunk by hd chunk.  Each chunk's K
+    // fragments are read one chunk ahead of its MFMAs, into the other register set, and retired by
+    // an explicit LDS-counter wait (the compiler's own waits treat the direct-to-LDS loads as
+    // unordered with these reads and would also wait for the reads just issued).
     floatx4 s[4][NQ];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int nq = 0; nq < NQ; ++nq) s[ks][nq] = (floatx4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    auto read_k = [&](int c, bf16x8_t (&f)[4]) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int r = s_key(ks, col);
-        const bf16x8_t a = *(const bf16x8_t*)&sK[r * HD + (((c * 4 + quad) ^ kswz<HD>(r)) << 3)];
-#pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) s[ks][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nq][c], s[ks][nq], 0, 0, 0);
+        f[ks] = *(const bf16x8_t*)&sK[r * HD + (((c * 4 + quad) ^ kswz<HD>(r)) << 3)];
       }
+    };
+    bf16x8_t kf[2][4];
+    read_k(0, kf[0]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + 1 < NC) read_k(c + 1, kf[(c + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq)
+          s[ks][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c & 1][ks], qf[nq][c], s[ks][nq], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first V^T fragments are read while the softmax runs
+    constexpr int HG = NH >= 2 ? 2 : 1;  // hd row blocks per V^T read group
+    auto read_v = [&](int g, bf16x8_t (&f)[HG][2]) {
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const int r = (g * HG + hh) * 16 + col;
+        const int sw = (r >> 1) & 7;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) f[hh][c2] = *(const bf16x8_t*)&sV[r * AKT + (((c2 * 4 + quad) ^ sw) << 3)];
+      }
+    };
+    bf16x8_t vf[2][HG][2];
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(0, vf[0]);
+    __builtin_amdgcn_sched_barrier(0);
 
     // Online softmax per query column in base-2 units: scores times scale * log2(e), so each
     // probability is one hardware exp2.  Masking runs only on tiles that need it (the segment's
@@ -354,17 +385,23 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
       }
     }
 
-    // O^T += V^T P^T ; lane's 8 k-slots are keys 32c2 + 8quad + {0..7}: one 16-byte chunk
+    // O^T += V^T P^T ; lane's 8 k-slots are keys 32c2 + 8quad + {0..7}: one 16-byte chunk.  V^T
+    // fragments are read one group of hd row blocks ahead of their MFMAs.
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const int r = h * 16 + col;
-      const int sw = (r >> 1) & 7;
+    for (int g = 0; g < NH / HG; ++g) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g + 1 < NH / HG) read_v(g + 1, vf[(g + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8_t a = *(const bf16x8_t*)&sV[r * AKT + (((c2 * 4 + quad) ^ sw) << 3)];
+      for (int hh = 0; hh < HG; ++hh)
 #pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) o[h][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[c2][nq], o[h][nq], 0, 0, 0);
-      }
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int nq = 0; nq < NQ; ++nq)
+            o[g * HG + hh][nq] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[g & 1][hh][c2], pb[c2][nq], o[g * HG + hh][nq], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
