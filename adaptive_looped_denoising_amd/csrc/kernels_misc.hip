@@ -148,11 +148,17 @@ __global__ __launch_bounds__(256) void k_exit_gate(const T* __restrict__ rows, i
 
 // ---------------------------------------------------------------------------------------------
 // Per-head RMSNorm of q and k, rotary embedding (rotate-half pairs (p, p + hd/2)), and the
-// layout change of q/k/v.  One wave per (row, head); lane p owns the pair (p, p + hd/2).
-// K/V element (row r, kv head h, e) goes to kv + (seq0 + r / n)*sSeq + h*sHead + (r % n)*sPos + e.
+// layout change of q/k/v.  Blocks 0 .. qk_blocks-1: each wave takes QK_PER_WAVE consecutive
+// (row, q or k head) items (4 for prefill-sized row counts, whose waves would otherwise each wait
+// on one round trip, 1 for a step's few rows); lane p owns the pair (p, p + hd/2); K element (row r, kv head h, e) goes to
+// k_out + (seq0 + r / n)*kSeq + h*kHead + (r % n)*kPos + e.  The remaining blocks transpose the
+// value heads: one block per (sequence, kv head, chunk of up to 64 positions, 32 of the hd
+// elements) stages the chunk in LDS and writes each V^T row v_out + seq*vSeq + h*vHead +
+// e*vRow + position as one contiguous run (a wave per (row, head) would scatter 2-byte writes
+// vRow apart).
 // SPLITS (compile time, 0 = runtime `splits`): split-K partials of the projection to add.
 // TKV: storage type of the keys and values (the activation type, or FP8 E4M3).
-template <typename TW, typename TA, typename TKV, int SPLITS>
+template <typename TW, typename TA, typename TKV, int SPLITS, int QK_PER_WAVE>
 __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ qkv, int n_rows, int rows_per_seq,
                                                       int pos0, int Hq, int Hkv, int hd,
                                                       const TW* __restrict__ qn, const TW* __restrict__ kn,
@@ -160,18 +166,14 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
                                                       const float* __restrict__ sinT, TA* __restrict__ q_out,
                                                       TKV* __restrict__ k_out, TKV* __restrict__ v_out,
                                                       int64_t kSeq, int64_t kHead, int64_t kPos, int64_t vSeq,
-                                                      int64_t vHead, int64_t vRow, int seq0, int splits_rt) {
+                                                      int64_t vHead, int64_t vRow, int seq0, int splits_rt,
+                                                      int qk_blocks) {
   const int splits = SPLITS > 0 ? SPLITS : splits_rt;
   const int NH = Hq + 2 * Hkv;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (gw >= n_rows * NH) return;
-  const int r = gw / NH, hh = gw % NH;
-  const int half = hd >> 1;
-  const float* src = qkv + (size_t)r * NH * hd + (size_t)hh * hd;
   const size_t pstride = (size_t)n_rows * NH * hd;  // split-K partial stride
-  // element e of this head: the projection, or the fixed-order sum of its split-K partials
-  auto val = [&](int e) {
+  // element e of head hh of row r: the projection, or the fixed-order sum of its split-K partials
+  auto head_val = [&](int r, int hh, int e) {
+    const float* src = qkv + (size_t)r * NH * hd + (size_t)hh * hd;
     float acc = src[e];
     if (SPLITS > 0) {
 #pragma unroll
@@ -181,48 +183,82 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const float* __restrict__ 
     }
     return acc;
   };
-  const int jpos = r % rows_per_seq;
-  const int pos = pos0 + jpos;
-  const size_t seq = (size_t)(seq0 + r / rows_per_seq);
-  if (hh >= Hq + Hkv) {  // value head: copy, transposed (positions contiguous)
-    const int h = hh - Hq - Hkv;
-    TKV* dst = v_out + seq * vSeq + (size_t)h * vHead + jpos;
-    for (int e = lane; e < hd; e += 64) dst[(size_t)e * vRow] = from_f<TKV>(val(e));
+  if ((int)blockIdx.x >= qk_blocks) {  // value heads, transposed through LDS
+    __shared__ float tile[32][65];
+    const int chunks = (rows_per_seq + 63) / 64, slices = hd / 32;
+    int vb = blockIdx.x - qk_blocks;
+    const int sl = vb % slices;
+    vb /= slices;
+    const int ch = vb % chunks, h = (vb / chunks) % Hkv, sq = vb / (chunks * Hkv);
+    const int j0 = ch * 64, n = min(64, rows_per_seq - j0);
+    const int r0 = sq * rows_per_seq + j0, e0 = sl * 32;
+    for (int i = threadIdx.x; i < n * 32; i += 256) {
+      const int j = i >> 5, e = i & 31;
+      tile[e][j] = head_val(r0 + j, Hq + Hkv + h, e0 + e);
+    }
+    __syncthreads();
+    TKV* dst = v_out + (size_t)(seq0 + sq) * vSeq + (size_t)h * vHead + (size_t)e0 * vRow + j0;
+    for (int i = threadIdx.x; i < n * 32; i += 256) {
+      const int e = i / n, j = i % n;
+      dst[(size_t)e * vRow + j] = from_f<TKV>(tile[e][j]);
+    }
     return;
   }
-  const size_t kv_off = seq * kSeq + (size_t)jpos * kPos;
-  const bool is_q = hh < Hq;
-  const TW* g = is_q ? qn : kn;
-  float x1[2], x2[2];
-  float ss = 0.f;
+  // q/k heads: each wave takes QK_PER_WAVE consecutive (row, head) items and issues the loads of
+  // all of them before using any (one item per wave leaves each wave waiting on one round trip)
+  const int NQK = Hq + Hkv;
+  const int lane = threadIdx.x & 63;
+  const int item0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * QK_PER_WAVE;
+  const int n_items = n_rows * NQK;
+  if (item0 >= n_items) return;
+  const int half = hd >> 1;
+  float x1[QK_PER_WAVE][2], x2[QK_PER_WAVE][2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int p = lane + 64 * t;
-    x1[t] = x2[t] = 0.f;
-    if (p < half) {
-      x1[t] = val(p);
-      x2[t] = val(p + half);
-      ss += x1[t] * x1[t] + x2[t] * x2[t];
+  for (int k = 0; k < QK_PER_WAVE; ++k) {
+    const int it = min(item0 + k, n_items - 1);
+    const int r = it / NQK, hh = it % NQK;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int p = lane + 64 * t;
+      x1[k][t] = x2[k][t] = 0.f;
+      if (p < half) {
+        x1[k][t] = head_val(r, hh, p);
+        x2[k][t] = head_val(r, hh, p + half);
+      }
     }
   }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
-  TA* dq = q_out + ((size_t)r * Hq + hh) * hd;
-  TKV* dk = k_out + kv_off + (size_t)(hh - Hq) * kHead;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int p = lane + 64 * t;
-    if (p < half) {
-      const float a = x1[t] * inv * to_f(g[p]);
-      const float b = x2[t] * inv * to_f(g[p + half]);
-      const float c = cosT[(size_t)pos * half + p], s = sinT[(size_t)pos * half + p];
-      const float lo = a * c - b * s, hi = b * c + a * s;
-      if (is_q) {
-        dq[p] = from_f<TA>(lo);
-        dq[p + half] = from_f<TA>(hi);
-      } else {
-        dk[p] = from_f<TKV>(lo);
-        dk[p + half] = from_f<TKV>(hi);
+  for (int k = 0; k < QK_PER_WAVE; ++k) {
+    if (item0 + k >= n_items) break;
+    const int r = (item0 + k) / NQK, hh = (item0 + k) % NQK;
+    const int jpos = r % rows_per_seq;
+    const int pos = pos0 + jpos;
+    const size_t seq = (size_t)(seq0 + r / rows_per_seq);
+    const size_t kv_off = seq * kSeq + (size_t)jpos * kPos;
+    const bool is_q = hh < Hq;
+    const TW* g = is_q ? qn : kn;
+    float ss = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) ss += x1[k][t] * x1[k][t] + x2[k][t] * x2[k][t];
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
+    TA* dq = q_out + ((size_t)r * Hq + hh) * hd;
+    TKV* dk = k_out + kv_off + (size_t)(hh - Hq) * kHead;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int p = lane + 64 * t;
+      if (p < half) {
+        const float a = x1[k][t] * inv * to_f(g[p]);
+        const float b = x2[k][t] * inv * to_f(g[p + half]);
+        const float c = cosT[(size_t)pos * half + p], s = sinT[(size_t)pos * half + p];
+        const float lo = a * c - b * s, hi = b * c + a * s;
+        if (is_q) {
+          dq[p] = from_f<TA>(lo);
+          dq[p + half] = from_f<TA>(hi);
+        } else {
+          dk[p] = from_f<TKV>(lo);
+          dk[p + half] = from_f<TKV>(hi);
+        }
       }
     }
   }
@@ -619,11 +655,19 @@ void launch_qk_norm_rope(int dtype, const float* qkv, int n_rows, int rows_per_s
                          int64_t kPos, int64_t vSeq, int64_t vHead, int64_t vRow, int seq0, hipStream_t st,
                          int splits, int kv_type) {
   if (n_rows <= 0) return;
-  const int waves = n_rows * (Hq + 2 * Hkv);
-#define QKR_LAUNCH(T, TKV, S)                                                                      \
-  k_qk_norm_rope<T, T, TKV, S><<<(waves + 3) / 4, 256, 0, st>>>(                                 \
-      qkv, n_rows, rows_per_seq, pos0, Hq, Hkv, hd, (const T*)qn, (const T*)kn, eps, cosT, sinT, (T*)q_out, \
-      (TKV*)k_out, (TKV*)v_out, kSeq, kHead, kPos, vSeq, vHead, vRow, seq0, splits)
+  // q/k heads: one wave each; value heads: one block per (sequence, kv head, 64-position chunk)
+  const int per_wave = n_rows >= 2048 ? 4 : 1;
+  const int qk_blocks = (n_rows * (Hq + Hkv) + 4 * per_wave - 1) / (4 * per_wave);
+  const int v_blocks = (n_rows / rows_per_seq) * Hkv * ((rows_per_seq + 63) / 64) * (hd / 32);
+#define QKR_LAUNCH(T, TKV, S)                                                                             \
+  if (per_wave == 4)                                                                                      \
+    k_qk_norm_rope<T, T, TKV, S, 4><<<qk_blocks + v_blocks, 256, 0, st>>>(                                \
+        qkv, n_rows, rows_per_seq, pos0, Hq, Hkv, hd, (const T*)qn, (const T*)kn, eps, cosT, sinT, (T*)q_out, \
+        (TKV*)k_out, (TKV*)v_out, kSeq, kHead, kPos, vSeq, vHead, vRow, seq0, splits, qk_blocks);          \
+  else                                                                                                    \
+    k_qk_norm_rope<T, T, TKV, S, 1><<<qk_blocks + v_blocks, 256, 0, st>>>(                                \
+        qkv, n_rows, rows_per_seq, pos0, Hq, Hkv, hd, (const T*)qn, (const T*)kn, eps, cosT, sinT, (T*)q_out, \
+        (TKV*)k_out, (TKV*)v_out, kSeq, kHead, kPos, vSeq, vHead, vRow, seq0, splits, qk_blocks)
 #define QKR_GO(S)                                   \
   if (kv_type == DT_FP8) {                          \
     QKR_LAUNCH(bf16_t, fp8_t, S);                   \
