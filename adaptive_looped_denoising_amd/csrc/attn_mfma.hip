@@ -504,16 +504,18 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
   const int n_seq = p.n_rows / p.rows_per_seq;
   const int n_pairs = n_seq * p.Hkv;
   const int rows_q = (p.Hq / p.Hkv) * p.rows_per_seq;
-  // Measured.  8B shape (128 query rows per pair, 17 key tiles): 16 query rows per wave, four
-  // waves, a two-stage ring (64 KB of LDS, two blocks per compute unit) and at least two key
-  // splits beat wider and deeper variants.  Long prefixes (>= 64 key tiles, >= 256 query rows
-  // per pair): one eight-wave block per pair covering all its query rows (32 per wave; 16 with
-  // fp8 K/V), so each key tile is streamed once per pair, and no key split when the pairs
-  // alone fill the chip (8192-key prefix: 113 -> 83 ms of attention per step).
+  // Measured.  8B shape (128 query rows per pair, 17 key tiles): one eight-wave block of 16-row
+  // waves per pair, a two-stage ring and about one block per compute unit through key splits
+  // beat four-wave blocks, wider waves and deeper rings.  Long prefixes (>= 64 key tiles,
+  // >= 256 query rows per pair): one eight-wave block per pair covering all its query rows (32
+  // per wave; 16 with fp8 K/V), so each key tile is streamed once per pair, and no key split
+  // when the pairs alone fill the chip (8192-key prefix: 113 -> 83 ms of attention per step).
   const int n_tiles = (p.n_cache + AKT - 1) / AKT + (p.n_self + AKT - 1) / AKT;
   const bool long_kv = p.hd >= (p.kv8 ? 128 : 64) && rows_q >= 256 && n_tiles >= 64;
+  // >= 128 query rows per pair: eight 16-row waves share each K/V stream (8B step: 2.12 -> 1.94 ms)
+  const bool wide_q = p.hd >= (p.kv8 ? 128 : 64) && rows_q >= 128;
   const int QW = (force_qw == 16 || force_qw == 32) ? force_qw : (long_kv && !p.kv8 ? 32 : 16);
-  const int NW = ((force_nw == 8 || (force_nw == 0 && long_kv)) && p.hd >= (p.kv8 ? 128 : 64)) ? 8 : 4;
+  const int NW = ((force_nw == 8 || (force_nw == 0 && (long_kv || wide_q))) && p.hd >= (p.kv8 ? 128 : 64)) ? 8 : 4;
   const int QB = NW * QW;
   const int n_qblocks = (rows_q + QB - 1) / QB;
   int splits = 1;
@@ -521,7 +523,8 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
     // long: enough splits for about one block per compute unit; else about two blocks per
     // compute unit and at least two splits, at least 2 key tiles per split
     const int blocks = n_pairs * n_qblocks;
-    const int want = long_kv ? max(1, (256 + blocks - 1) / blocks) : max(2, (512 + blocks - 1) / blocks);
+    const int want = long_kv ? max(1, (256 + blocks - 1) / blocks)
+                             : (NW == 8 ? max(2, (256 + blocks - 1) / blocks) : max(2, (512 + blocks - 1) / blocks));
     splits = min(min(want, max(1, n_tiles / 2)), max_splits);
     if (force_splits > 0) splits = min(force_splits, max_splits);
     if (splits < 1) splits = 1;
