@@ -204,3 +204,19 @@ def test_mid_bf16_evicted_extend(gpu_lib):
         ref = _stored(w, ref_c, ref_a)
         ref16 = [(K, V) for K, V, _ in _stored(w, ref16_c, ref_a)]
         log("seq %d new rows worst/tol %.3f" % (b, _check_cache(e, w, b, w.prefix, 40, ref, ref16)))
+
+
+def test_mid_fp8_evicted_step_and_cache(gpu_lib):
+    """Both compressions of the depth buffers at once: fp8 K/V in a cache keeping two depths."""
+    w = _mid(kv_dtype="fp8", prefix=130, tau_ent=0.0, tau_halt=2.0)
+    e, ores = _check_step_bf16(w)
+    assert max(r["loops"] for r in ores) == w.k_max
+    W = orun.weights(w)
+    ids = synth.prefix_ids(w)
+    for b in range(w.batch):
+        a = orun.avail_for(w, synth.avail_depth(w)[b])
+        full = orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, kv="fp8")
+        full16 = orc.prefill_sequence(ids[b], W, w.dims, w.k_max, w.rms_eps, w.rope_theta, kv="fp8", prec="bf16")
+        ref = _stored(w, orc.evict_depths(full, None, w.dims, w.k_max, 2, w.prefix)[0], a)
+        ref16 = [(K, V) for K, V, _ in _stored(w, orc.evict_depths(full16, None, w.dims, w.k_max, 2, w.prefix)[0], a)]
+        log("seq %d cache worst/tol %.3f" % (b, _check_cache(e, w, b, 0, w.prefix, ref, ref16)))
