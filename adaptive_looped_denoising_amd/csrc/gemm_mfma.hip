@@ -334,6 +334,24 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const bf16_t* __restrict__ A,
 // (chunk c at slot c ^ (r & 7)) so that the 16 rows a fragment read touches spread over the banks.
 // Rows past M / N load row 0 (never stored).
 
+// Grouped tile order for many row tiles: consecutive tile numbers walk GM row tiles, then the
+// next column tile, so the 32 workgroups an XCD holds at a time cover GM row panels and 32/GM
+// column panels (12 distinct panels for GM = 8) instead of 32 row panels and one column panel:
+// each panel's K-slice is then read from the XCD's L2 by several workgroups rather than from
+// the memory-side cache by one.  With fewer than GM row tiles this is the plain row-fastest order.
+__device__ __forceinline__ void grouped_tile(int T, int m_tiles, int n_tiles, int& mt, int& nt, int& sp) {
+  constexpr int GM = 8;
+  const int mn = m_tiles * n_tiles;
+  sp = T / mn;
+  const int t = T % mn;
+  const int group = t / (GM * n_tiles);
+  const int first = group * GM;
+  const int gm = min(m_tiles - first, GM);
+  const int w = t % (GM * n_tiles);
+  mt = first + w % gm;
+  nt = w / gm;
+}
+
 // WM x WN waves (4 or 8; with 8, two waves share each SIMD and hide each other's waits).
 template <int BM, int BN, int WM, int WN, int NS, int EPI, bool SPLIT>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const bf16_t* __restrict__ A, int lda,
@@ -353,10 +371,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const bf16_t* __rest
   const int per = (gridDim.x + 7) >> 3;
   const int T = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (T >= total) return;
-  const int mt = T % m_tiles;
-  const int rest = T / m_tiles;
-  const int nt = rest % n_tiles;
-  const int sp = rest / n_tiles;
+  int mt, nt, sp;
+  grouped_tile(T, m_tiles, n_tiles, mt, nt, sp);
   const int m0 = mt * BM, n0 = nt * BN;
   int Mr = M;
   if (m_dev) Mr = min(Mr, *m_dev);
@@ -476,10 +492,8 @@ __device__ __forceinline__ void gemm_wide_body(const bf16_t* __restrict__ A, int
   const int per = (gridDim.x + 7) >> 3;
   const int T = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (T >= total) return;
-  const int mt = T % m_tiles;
-  const int rest = T / m_tiles;
-  const int nt = rest % n_tiles;
-  const int sp = rest / n_tiles;
+  int mt, nt, sp;
+  grouped_tile(T, m_tiles, n_tiles, mt, nt, sp);
   const int m0 = mt * BM, n0 = nt * BN;
   int Mr = M;
   if (m_dev) Mr = min(Mr, *m_dev);
@@ -1230,8 +1244,8 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   *splits = 1;
   if (epi == EPI_SOFTSTAT) return 17;
   // wide eight-wave tiles where the matrix cores bound the GEMM: every projection at >= 4096
-  // rows (8192-row prefill: gate/up 1.84 -> 1.60 ms, down 0.94 -> 0.85), gate/up from 1536
-  if (M >= 4096) return 59;
+  // rows (8192-row prefill: gate/up 1.84 -> 1.50 ms, down 0.94 -> 0.83), gate/up from 1536
+  if (M >= 4096) return 60;
   if (M >= 1536) return epi == EPI_SWIGLU ? 60 : (epi == EPI_STORE ? 47 : 37);
   if (epi == EPI_SWIGLU) return M >= 768 ? 44 : 47;
   if (epi == EPI_STORE) return M >= 768 ? 47 : 38;
