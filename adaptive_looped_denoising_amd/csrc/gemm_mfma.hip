@@ -1232,7 +1232,9 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   if (M <= 64 && epi == EPI_SOFTSTAT) return 9;
   if (M <= 384) {
     *splits = 1;
-    if (epi == EPI_SOFTSTAT) return M <= 128 ? 47 : 37;  // LM head: wide weight tiles, few activation re-reads
+    // LM head: 128-row tiles up to 128 rows, then the 256 x 256 wide tile (one row tile, each
+    // weight tile read once: 256 rows 473 -> 424 us)
+    if (epi == EPI_SOFTSTAT) return M <= 128 ? 47 : 59;
     if (epi == EPI_SWIGLU) return M <= 64 ? 45 : (M <= 128 ? 18 : 56);
     // projections (QKV, O, FFN down): split-K 4 over the eight-wave tiles
     *splits = 4;
@@ -1242,7 +1244,7 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   // more rows (long-context steps, prefill): single pass over the eight-wave tiles, measured at
   // 512 / 1024 / 2048 / 8192 rows on the 8B projections
   *splits = 1;
-  if (epi == EPI_SOFTSTAT) return 17;
+  if (epi == EPI_SOFTSTAT) return 59;  // 2048 rows: 3.24 -> 2.50 ms
   // wide eight-wave tiles where the matrix cores bound the GEMM: every projection at >= 4096
   // rows (8192-row prefill: gate/up 1.84 -> 1.50 ms, down 0.94 -> 0.83), gate/up from 1536
   if (M >= 4096) return 60;
