@@ -226,6 +226,12 @@ def test_mid_bf16_head_dim_64(gpu_lib):
                              batch=2), dims=dims), gpu_lib)
 
 
+def test_empty_prefix(gpu_lib):
+    """No cached prefix (a first block): every layer attends to the block's own keys only."""
+    _check_step(synth.workload("tiny", prefix=0, batch=2, boost_lo=8.0, boost_hi=14.0), gpu_lib)
+    _check_step(_mid(prefix=0, batch=2), gpu_lib)
+
+
 def test_mid_fp32_matches_bf16_structure(gpu_lib):
     # fp32 mode on the same shapes (generic kernels) at the fp32 tolerance
     _check_step(_mid(dtype="fp32", prefix=100), gpu_lib)
