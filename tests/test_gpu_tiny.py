@@ -226,6 +226,13 @@ def test_mid_bf16_head_dim_64(gpu_lib):
                              batch=2), dims=dims), gpu_lib)
 
 
+def test_loop_caps_1_and_16(gpu_lib):
+    """The smallest and largest loop caps: one loop (every sequence stops at once; the forced
+    commit) and sixteen loops with halting off (sixteen Core depth planes in the cache)."""
+    _check_step(synth.workload("tiny", k_max=1, batch=2), gpu_lib)
+    _check_step(synth.workload("tiny", k_max=16, tau_ent=0.0, tau_halt=2.0, batch=2, prefix=40), gpu_lib)
+
+
 def test_empty_prefix(gpu_lib):
     """No cached prefix (a first block): every layer attends to the block's own keys only."""
     _check_step(synth.workload("tiny", prefix=0, batch=2, boost_lo=8.0, boost_hi=14.0), gpu_lib)
