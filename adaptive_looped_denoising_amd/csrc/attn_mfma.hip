@@ -451,18 +451,45 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int n_pairs, i
   const int t = pair / p.Hkv, kvh = pair % p.Hkv;
   const int i = rho / G, g = rho % G;
   const float* part = p.part + ((size_t)pair * rows_q + rho) * n_splits * (HD + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part[s * (HD + 2) + HD]);
-  float L = 0.f, acc[(HD + 63) / 64];
+  // up to MS splits: every partial is loaded before any is combined (one memory round trip)
+  constexpr int MS = 8, NU = (HD + 63) / 64;
+  float ms_[MS], ls_[MS], vs_[MS][NU];
 #pragma unroll
-  for (int u = 0; u < (HD + 63) / 64; ++u) acc[u] = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
+  for (int s = 0; s < MS; ++s) {
+    if (s < n_splits) {
+      const float* ps = part + s * (HD + 2);
+      ms_[s] = ps[HD];
+      ls_[s] = ps[HD + 1];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int e = lane + 64 * u;
+        vs_[s][u] = e < HD ? ps[e] : 0.f;
+      }
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < MS; ++s)
+    if (s < n_splits) M = fmaxf(M, ms_[s]);
+  for (int s = MS; s < n_splits; ++s) M = fmaxf(M, part[s * (HD + 2) + HD]);
+  float L = 0.f, acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc[u] = 0.f;
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    if (s < n_splits) {
+      const float f = ms_[s] == -INFINITY ? 0.f : __expf(ms_[s] - M);
+      L += f * ls_[s];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) acc[u] += f * vs_[s][u];
+    }
+  }
+  for (int s = MS; s < n_splits; ++s) {  // splits past MS, straight from memory
     const float* ps = part + s * (HD + 2);
-    const float ms = ps[HD];
-    const float f = ms == -INFINITY ? 0.f : __expf(ms - M);
+    const float f = ps[HD] == -INFINITY ? 0.f : __expf(ps[HD] - M);
     L += f * ps[HD + 1];
 #pragma unroll
-    for (int u = 0; u < (HD + 63) / 64; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int e = lane + 64 * u;
       if (e < HD) acc[u] += f * ps[e];
     }
