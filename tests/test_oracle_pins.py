@@ -248,9 +248,10 @@ def test_layer_call_count_matches_page():
 
 
 # --------------------------------------------------------------------------- step-level pins
-def _straight_line_tokens(w, W, prefix, block):
+def _straight_line_readout(w, W, prefix, block):
     """Independent forward of [prefix ; block] through the whole stack in one pass: prefix rows
-    attend causally, block rows attend to everything.  Returns argmax tokens of the block rows."""
+    attend causally, block rows attend to everything.  Returns the block rows' readout rows
+    (final RMSNorm of the last layer's output) and their logits."""
     D = w.dims
     Hq, Hkv, hd, F = D.n_q_heads, D.n_kv_heads, D.head_dim, D.ffn
     ids = np.concatenate([prefix, block])
@@ -290,8 +291,7 @@ def _straight_line_tokens(w, W, prefix, block):
         gate, up = np.split(t @ g("w_gate_up").T, 2, axis=1)
         x = x + (gate * (1.0 / (1.0 + np.exp(-gate))) * up) @ g("w_down").T
     r = norm(x[P:], np.array(W["final_norm"], dtype=np.float64))
-    logits = r @ np.array(W["lm_head"], dtype=np.float64).T
-    return logits.argmax(axis=1)
+    return r, r @ np.array(W["lm_head"], dtype=np.float64).T
 
 
 def test_all_commit_reduces_to_one_fixed_depth_pass():
@@ -302,10 +302,18 @@ def test_all_commit_reduces_to_one_fixed_depth_pass():
     pre = synth.prefix_ids(w)[0]
     blk = synth.block_ids(w)[0].copy()
     blk[[1, 4]] = [17, 300]   # two rows already decoded
-    res = run.step(w, W=W, block_ids=blk[None], boost=(np.full((1, 16), -1), np.zeros((1, 16))))
-    expect = _straight_line_tokens(w, W, pre, blk)
+    res = run.step(w, W=W, block_ids=blk[None], boost=(np.full((1, 16), -1), np.zeros((1, 16))),
+                   record_hidden=True)
+    r_ref, z_ref = _straight_line_readout(w, W, pre, blk)
+    expect = z_ref.argmax(axis=1)
     masked = blk == w.mask_id
     assert res[0]["loops"] == 1
+    # the readout rows agree to rounding, and so do the entropies of the masked rows
+    rec = res[0]["records"][0]
+    np.testing.assert_allclose(rec["r"], r_ref, rtol=1e-10, atol=1e-12)
+    p = np.exp(z_ref - z_ref.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(rec["H"][masked], -(p * np.log(p)).sum(axis=1)[masked], rtol=1e-10)
     assert (res[0]["commit_loop"][masked] == 1).all() and (res[0]["commit_loop"][~masked] == 0).all()
     assert np.array_equal(res[0]["tokens"][masked], expect[masked])
     assert np.array_equal(res[0]["tokens"][~masked], blk[~masked])
@@ -357,7 +365,20 @@ def test_uniform_readout_forces_lowest_position():
     assert res["forced"] == 0 and res["tokens"][0] == 0 and res["commit_loop"][0] == -res["loops"]
 
 
-@pytest.mark.parametrize("lam,tau_halt,s_star", [(0.42, 0.5, 2), (0.42, 0.9, 5), (0.42, 0.3, 1), (0.2, 0.5, 4)])
+def test_entropy_equal_to_threshold_commits():
+    """Commit iff H <= tau (inclusive): with a uniform readout every row's entropy is the same
+    value, and a threshold equal to it commits every masked row at loop 1."""
+    w = _tiny()
+    W = run.weights(w)
+    W["lm_head"] = np.zeros_like(W["lm_head"])
+    H0 = float(orc.readout(np.zeros((1, w.dims.d_model)), W["lm_head"])[0][0])
+    res = run.step(replace(w, tau_ent=H0), W=W, boost=(np.full((1, 16), -1), np.zeros((1, 16))))[0]
+    assert res["loops"] == 1 and (res["commit_loop"] == 1).all() and res["forced"] == -1
+    assert (res["tokens"] == 0).all()
+
+
+@pytest.mark.parametrize("lam,tau_halt,s_star", [(0.42, 0.5, 2), (0.42, 0.9, 5), (0.42, 0.3, 1), (0.2, 0.5, 4),
+                                                 (0.5, 0.75, 2)])
 def test_halting_closed_form(lam, tau_halt, s_star):
     K = 6
     w = _tiny(k_max=K, tau_ent=-1.0, tau_halt=tau_halt)
@@ -369,6 +390,22 @@ def test_halting_closed_form(lam, tau_halt, s_star):
     assert res["loops"] == s_star
     for rec in res["records"]:
         np.testing.assert_allclose(rec["a"], 1 - (1 - lam) ** rec["loop"], rtol=1e-12)
+
+
+def test_halting_mean_is_over_unresolved_rows_only():
+    """The stop rule averages a over the positions still unresolved: rows decoded before the step
+    keep a = 0 and do not hold the sequence in the loop (the closed form over U still gives 2)."""
+    lam, K = 0.42, 6
+    w = _tiny(k_max=K, tau_ent=-1.0, tau_halt=0.5)
+    W = run.weights(w)
+    W["exit_w"] = np.zeros_like(W["exit_w"])
+    blk = synth.block_ids(w)[0].copy()
+    blk[:8] = np.arange(5, 13)
+    res = run.step(w, W=W, block_ids=blk[None], exit_b=math.log(lam / (1 - lam)))[0]
+    assert res["loops"] == 2
+    last = res["records"][-1]
+    assert (last["a"][:8] == 0).all()
+    np.testing.assert_allclose(last["mean_a"], 1 - (1 - lam) ** 2, rtol=1e-12)
 
 
 def test_eq3_committed_rows_are_token_embeddings():
