@@ -337,7 +337,11 @@ __global__ void k_step_init(const int32_t* __restrict__ block_ids, int n, int ma
 // (new slot t2 <- old slot t), and the readout rows are their unresolved rows in (slot, row)
 // order.  One block; nb <= 1024 sequences.  Also totals the commits of the whole batch.
 // cnt[0] = sequences still looping, cnt[1] = readout rows, cnt[2] = committed tokens.
-__global__ __launch_bounds__(1024) void k_build_lists(int nb, int L, int B, const int32_t* __restrict__ act_cur,
+// keep_all (the lists of loop 1, whose launches are sized for the whole batch before any count
+// is read back): every sequence keeps its slot, also one with nothing masked, which the commit
+// kernel then stops at loop 1 with 0 loops.
+__global__ __launch_bounds__(1024) void k_build_lists(int nb, int L, int B, int keep_all,
+                                                       const int32_t* __restrict__ act_cur,
                                                        const uint8_t* __restrict__ stop,
                                                        const uint8_t* __restrict__ U,
                                                        const int32_t* __restrict__ ncommit,
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(1024) void k_build_lists(int nb, int L, int B, cons
     b = act_cur[t];
     if (!stop[b])
       for (int i = 0; i < L; ++i) nrows += U[b * L + i];
-    alive = nrows > 0;  // a sequence with nothing unresolved runs no (further) loop
+    alive = keep_all || nrows > 0;  // a sequence with nothing unresolved runs no further loop
   }
   int nc = 0;
   for (int bb = t; bb < B; bb += 1024) nc += ncommit[bb];
@@ -400,7 +404,8 @@ __global__ __launch_bounds__(1024) void k_build_lists(int nb, int L, int B, cons
 // H <= tau_ent (or the teacher's decision); stop iff no row is left unresolved, the mean a of
 // the unresolved rows is >= tau_halt, or s == k_loops (or the teacher's stop loop); a sequence
 // that stops without having committed anything in this step commits its unresolved row of
-// lowest entropy (lowest row on ties), recorded as -s.
+// lowest entropy (lowest row on ties), recorded as -s.  A sequence whose block has no masked
+// row denoises nothing: it stops at once and reports 0 loops.
 __global__ __launch_bounds__(64) void k_commit(int s, int k_loops, int L, int B, float tau_ent, float tau_halt,
                                                const int32_t* __restrict__ act, uint8_t* __restrict__ U,
                                                float* __restrict__ a, const int32_t* __restrict__ ro_map,
@@ -447,6 +452,7 @@ __global__ __launch_bounds__(64) void k_commit(int s, int k_loops, int L, int B,
     U[idx] = 0;
   }
   const unsigned long long cm = __ballot(commit);
+  const bool none = __ballot(u) == 0ull;  // nothing unresolved at loop start: a block without [MASK]
   const bool u2 = u && !commit;
   const unsigned long long um = __ballot(u2);
   const int n_u = __popcll(um);
@@ -454,7 +460,7 @@ __global__ __launch_bounds__(64) void k_commit(int s, int k_loops, int L, int B,
   int nc = ncommit[b] + __popcll(cm);
   bool st;
   if (tf_stop)
-    st = s == (int)tf_stop[b];
+    st = none || s == (int)tf_stop[b];
   else
     st = n_u == 0 || (sum_a / (float)n_u) >= tau_halt || s == k_loops;
   if (st && nc == 0 && n_u > 0) {
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(64) void k_commit(int s, int k_loops, int L, int B,
   if (i == 0) {
     ncommit[b] = nc;
     stop[b] = st;
-    if (st) loops[b] = (int8_t)s;
+    if (st) loops[b] = (int8_t)(none ? 0 : s);
   }
   if (in && dbg_H) {
     const size_t o = (size_t)(s - 1) * B * L + idx;
@@ -708,10 +714,12 @@ void launch_step_init(const int32_t* block_ids, int B, int L, int mask_id, uint8
                                                act, src_slot);
 }
 
-void launch_build_lists(int nb, int L, int B, const int32_t* act_cur, const uint8_t* stop, const uint8_t* U,
+void launch_build_lists(int nb, int L, int B, int keep_all, const int32_t* act_cur, const uint8_t* stop,
+                        const uint8_t* U,
                         const int32_t* ncommit, int32_t* act_next, int32_t* src_slot, int32_t* ro_rows,
                         int32_t* ro_map, int32_t* cnt, hipStream_t st) {
-  k_build_lists<<<1, 1024, 0, st>>>(nb, L, B, act_cur, stop, U, ncommit, act_next, src_slot, ro_rows, ro_map, cnt);
+  k_build_lists<<<1, 1024, 0, st>>>(nb, L, B, keep_all, act_cur, stop, U, ncommit, act_next, src_slot, ro_rows,
+                                     ro_map, cnt);
 }
 
 void launch_commit(int nb, int s, int k_loops, int L, int B, float tau_ent, float tau_halt, const int32_t* act,

@@ -91,8 +91,8 @@ void launch_softstat_combine(const SoftStat* part, int n_rows, int n_tiles, cons
 void launch_step_init(const int32_t* block_ids, int B, int L, int mask_id, uint8_t* U, float* a, int32_t* tokens,
                       int8_t* cl, int32_t* ncommit, uint8_t* stop, int8_t* loops, int32_t* act, int32_t* src_slot,
                       hipStream_t st);
-void launch_build_lists(int nb, int L, int B, const int32_t* act_cur, const uint8_t* stop, const uint8_t* U,
-                        const int32_t* ncommit, int32_t* act_next, int32_t* src_slot, int32_t* ro_rows,
+void launch_build_lists(int nb, int L, int B, int keep_all, const int32_t* act_cur, const uint8_t* stop,
+                        const uint8_t* U, const int32_t* ncommit, int32_t* act_next, int32_t* src_slot, int32_t* ro_rows,
                         int32_t* ro_map, int32_t* cnt, hipStream_t st);
 // stok (optional): sampled token per readout row, committed instead of the argmax tok.
 void launch_commit(int nb, int s, int k_loops, int L, int B, float tau_ent, float tau_halt, const int32_t* act,

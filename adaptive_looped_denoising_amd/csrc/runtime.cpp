@@ -885,7 +885,7 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
   }
   launch_step_init(a->block_ids, B, L, g.mask_id, U, av, o->tokens, o->commit_loop, ncommit, stop, o->loops, act[0],
                    src_slot, st);
-  launch_build_lists(B, L, B, act[0], stop, U, ncommit, act[1], src_slot, ro_rows, ro_map, cnt, st);
+  launch_build_lists(B, L, B, 1, act[0], stop, U, ncommit, act[1], src_slot, ro_rows, ro_map, cnt, st);
   int cur = 1;
 
   // Prelude over every block row (slot t = sequence t)
@@ -957,7 +957,7 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
                   c->at<float>(p.lse), o->tokens, o->commit_loop, ncommit, stop, o->loops,
                   tf ? a->tf_commit_loop : nullptr, tf ? a->tf_tokens : nullptr, tf ? a->tf_stop_loop : nullptr,
                   dbg ? o->entropy : nullptr, o->lam, o->halt, o->lse, o->argmax, o->sampled, st);
-    launch_build_lists(nb, L, B, act[cur], stop, U, ncommit, act[cur ^ 1], src_slot, ro_rows, ro_map, cnt, st);
+    launch_build_lists(nb, L, B, 0, act[cur], stop, U, ncommit, act[cur ^ 1], src_slot, ro_rows, ro_map, cnt, st);
     launch_reset_compact(dt(c), nb, cnt, L, d, g.vocab, act[cur ^ 1], src_slot, U, o->tokens, h, c->w.embed, h_alt, st);
     c->toc();
     float* t = h;
@@ -1061,7 +1061,7 @@ int alodlm_readout_commit(alodlm_ctx* c, const void* rows, int32_t n_rows, int32
   int8_t* seq_loops = c->at<int8_t>(p.seq_loops);
   launch_step_init(nullptr, B, L, g.mask_id, U, halt, tokens, commit_loop, c->at<int32_t>(p.ncommit),
                    c->at<uint8_t>(p.stop), seq_loops, act0, c->at<int32_t>(p.src_slot), st);
-  launch_build_lists(B, L, B, act0, c->at<uint8_t>(p.stop), U, c->at<int32_t>(p.ncommit), act1,
+  launch_build_lists(B, L, B, 1, act0, c->at<uint8_t>(p.stop), U, c->at<int32_t>(p.ncommit), act1,
                      c->at<int32_t>(p.src_slot), c->at<int32_t>(p.ro_rows), c->at<int32_t>(p.ro_map),
                      c->at<int32_t>(p.cnt), st);
   launch_exit_gate(dt(c), rows, n_rows, g.d_model, c->w.exit_w, c->w.exit_b, lam, st);

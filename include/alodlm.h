@@ -214,7 +214,9 @@ typedef struct alodlm_step_args {
 typedef struct alodlm_step_out {
   int32_t* tokens;       /* device [batch][L]: committed token, block id for rows not masked, else mask_id */
   int8_t* commit_loop;   /* device [batch][L]: s if committed at loop s, -s if forced at the last loop s, 0 */
-  int8_t* loops;         /* device [batch]: loops run by each sequence */
+  int8_t* loops;         /* device [batch]: loops run by each sequence; 0 for a block with no masked
+                            row (nothing to denoise: it commits nothing, although its rows still pass
+                            through the first loop's layers with the rest of the batch) */
   /* optional per-loop records, device [k_loops][batch][L] float (NaN where not read out): */
   float* entropy;        /* H of rows unresolved at loop start */
   float* lam;            /* ExitGate lambda */

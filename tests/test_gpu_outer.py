@@ -135,10 +135,15 @@ def test_tiny_fp32_outer_loop(gpu_lib):
     ores = orun.denoise_block(w, block_ids=bids)
     log("steps %s, GPU %d" % ([r["steps"] for r in ores], g["n_steps"]))
     _check_block(w, e, ores, g)
-    # one-token-per-step mode: as many steps as masks
+    # one-token-per-step mode: as many steps as masks; sequence 1 (three rows decoded) finishes
+    # three steps before the others, which keep stepping beside it
     g1 = e.denoise_block(block_ids=bids, tau_ent=-1.0)
     n_mask = (bids == w.mask_id).sum(axis=1)
     assert g1["n_steps"] == n_mask.max() and (g1["commit_loop"][bids == w.mask_id] < 0).all()
+    w1 = replace(w, tau_ent=-1.0)
+    ores1 = orun.denoise_block(w1, block_ids=bids)
+    assert [r["steps"] for r in ores1] == list(n_mask)
+    _check_block(w1, e, ores1, g1)
 
 
 def test_tiny_fp32_outer_loop_sampled_then_append(gpu_lib):

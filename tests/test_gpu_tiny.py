@@ -86,6 +86,49 @@ def test_tiny_fp32_batch_and_decoded_rows(gpu_lib):
     _check_step(w, gpu_lib, block_ids=bids)
 
 
+def test_tiny_fp32_block_without_mask(gpu_lib):
+    # a sequence with nothing masked denoises nothing: no commit, 0 loops (as the oracle)
+    w = synth.workload("tiny", batch=3, boost_lo=8.0, boost_hi=14.0)
+    bids = synth.block_ids(w)
+    bids[1, :] = np.arange(16) + 40
+    _, ores, free = _check_step(w, gpu_lib, block_ids=bids)
+    assert ores[1]["loops"] == 0 and free.loops[1] == 0
+    assert np.array_equal(free.tokens[1], bids[1]) and (free.commit_loop[1] == 0).all()
+    # a whole batch without [MASK]
+    from adaptive_looped_denoising_amd.engine import Engine
+    e = Engine(w)
+    e.prefill()
+    full = np.full_like(bids, 9)
+    r = e.step(block_ids=full)
+    assert (r.loops == 0).all() and r.n_committed == 0 and np.array_equal(r.tokens, full)
+    assert (r.commit_loop == 0).all()
+
+
+def test_tiny_fp32_all_commit_at_loop_one(gpu_lib):
+    # tau_ent above ln V: every masked row commits at loop 1 (tokens = the argmax of one pass)
+    w = synth.workload("tiny", batch=2, tau_ent=float(np.log(512.0)) + 1.0)
+    _, ores, free = _check_step(w, gpu_lib)
+    for r in ores:
+        assert r["loops"] == 1 and (r["commit_loop"] == 1).all()
+    assert (free.loops == 1).all() and (free.commit_loop == 1).all()
+
+
+def test_tiny_fp32_halting_mean_over_unresolved_rows_only(gpu_lib):
+    # rows decoded before the step keep a = 0 and do not enter the stop test's mean
+    lam = 0.42
+    w = synth.workload("tiny", k_max=6, tau_ent=-1.0, tau_halt=0.5)
+    bids = synth.block_ids(w)
+    bids[0, :8] = np.arange(5, 13)
+    from adaptive_looped_denoising_amd.engine import Engine
+    e = Engine(w, overrides={"exit_w": np.zeros(w.dims.d_model, dtype=np.float32)},
+               exit_b=float(np.log(lam / (1 - lam))))
+    e.prefill()
+    r = e.step(block_ids=bids, records=True)
+    assert r.loops[0] == 2
+    np.testing.assert_allclose(r.halt[1, 0, 8:], 1 - (1 - lam) ** 2, rtol=1e-5)
+    assert np.isnan(r.halt[1, 0, :8]).all()
+
+
 def test_tiny_fp32_uniform_depth_and_closed_form_halting(gpu_lib):
     # nothing commits by entropy and halting is off: every sequence runs k_max loops
     w = synth.workload("tiny", batch=2, tau_ent=0.0, tau_halt=1.5)
