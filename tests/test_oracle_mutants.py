@@ -109,6 +109,9 @@ MUTANTS = {
     "gumbel_single_log": (
         "gumbel_noise", "-np.log(-np.log(u))", "-np.log(u)",
         [pins.test_gumbel_noise_range_and_counter_layout, pins.test_gumbel_sample_limits]),
+    "block_without_mask_still_loops": (
+        "denoise_step_sequence", "if not U.any():", "if False:",
+        [pins.test_no_mask_no_loop_and_sampled_steps_advance_the_counter]),
     "eviction_keeps_one_depth_too_many": (
         "evict_depths", "range(1, keep + 1)", "range(1, keep + 2)",
         [pins.test_evict_depths_buffer_counts_match_page]),
