@@ -138,8 +138,11 @@ def compare_decisions(w: synth.Workload, oracle_res: List[dict], gpu, tols: dict
     flagged = []
     for res in oracle_res:
         b = res["seq"]
-        t = tols[(b, res["loops"])] if tols else tolerances(w, loop_depth(w, res["loops"]))
-        flags = orun.near_decisions(w, res, ent_tol=t["H"], gap_tol=t["gap"], halt_tol=t["halt"])
+        if res["loops"] == 0:  # nothing masked: no decision was taken
+            flags = []
+        else:
+            t = tols[(b, res["loops"])] if tols else tolerances(w, loop_depth(w, res["loops"]))
+            flags = orun.near_decisions(w, res, ent_tol=t["H"], gap_tol=t["gap"], halt_tol=t["halt"])
         if flags:
             log("seq %d near decision boundaries: %s" % (b, "; ".join(flags)))
             flagged.append(b)

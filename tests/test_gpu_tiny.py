@@ -254,6 +254,18 @@ def test_mid_bf16_block_64_and_single_row(gpu_lib):
     _check_step(_mid(block=1, prefix=64, batch=4, tau_halt=0.3), gpu_lib)
 
 
+def test_mid_bf16_block_without_mask_between_masked_ones(gpu_lib):
+    """Matrix-core path (hd 128, GQA 4): the middle sequence of three has nothing masked, the
+    last has half its rows decoded; free-running and sampled."""
+    w = _mid(batch=3, prefix=200)
+    bids = synth.block_ids(w)
+    bids[1, :] = np.arange(32) + 100
+    bids[2, ::2] = np.arange(16) + 500
+    _, ores, free = _check_step(w, gpu_lib, block_ids=bids)
+    assert ores[1]["loops"] == 0 and free.loops[1] == 0 and np.array_equal(free.tokens[1], bids[1])
+    _check_step(replace(w, tau_ent=7.0, boost_lo=3.0, boost_hi=8.0), gpu_lib, block_ids=bids, sample=SAMPLE)
+
+
 def test_mid_bf16_sampled_step(gpu_lib):
     """Sampled commits through the matrix-core LM-head tiles (vocab 4096, hd 128)."""
     _check_step(_mid(tau_ent=7.0, boost_lo=3.0, boost_hi=8.0), gpu_lib, sample=SAMPLE)
