@@ -1233,8 +1233,9 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   if (M <= 384) {
     *splits = 1;
     // LM head: 128-row tiles up to 128 rows, then the 256 x 256 wide tile (one row tile, each
-    // weight tile read once: 256 rows 473 -> 424 us)
-    if (epi == EPI_SOFTSTAT) return M <= 128 ? 47 : 59;
+    // weight tile read once: 256 rows 473 -> 424 us); 257..384 rows would take two wide row
+    // tiles, three 128-row ones cost less (288 / 320 / 384 rows: 628 / 781 / 645 -> 553 / 614 / 559 us)
+    if (epi == EPI_SOFTSTAT) return M <= 128 ? 47 : (M <= 256 ? 59 : 44);
     if (epi == EPI_SWIGLU) return M <= 64 ? 45 : (M <= 128 ? 18 : 56);
     // projections (QKV, O, FFN down): split-K 4 over the eight-wave tiles
     *splits = 4;

@@ -98,6 +98,31 @@ def test_softstat_every_tile(gpu_lib, tile):
     assert ok.all()
 
 
+@pytest.mark.parametrize("M", [128, 129, 256, 257, 300, 384, 385])
+def test_softstat_auto_tile_across_row_thresholds(gpu_lib, M):
+    """The readout's automatic tile choice around its row thresholds (128 / 256 / 384)."""
+    from adaptive_looped_denoising_amd import binding as B
+    N, K = 1000, 256
+    A, Bm = _bf16((M, K), 22), _bf16((N, K), 23, 0.1)
+    z = _ref(A, Bm)
+    zmax = z.max(axis=1, keepdims=True)
+    p = np.exp(z - zmax)
+    S = p.sum(axis=1)
+    lse = zmax[:, 0] + np.log(S)
+    H = lse - (p * z).sum(axis=1) / S
+    out = torch.empty((2, M), dtype=torch.float32, device="cuda")
+    tok = torch.empty(M, dtype=torch.int32, device="cuda")
+    scratch = torch.empty(4 * M * ((N + 63) // 64), dtype=torch.float32, device="cuda")
+    Ad, Bd = A.cuda(), Bm.cuda()
+    B.diag_gemm(B.DIAG_SOFTSTAT, M, N, K, Ad.data_ptr(), Bd.data_ptr(), out.data_ptr(), tok.data_ptr(),
+                scratch.data_ptr(), scratch.numel(), 0, 0, torch.cuda.current_stream().cuda_stream, -1)
+    torch.cuda.synchronize()
+    gH, glse = out.cpu().numpy()
+    assert np.abs(gH - H).max() < 1e-4 and np.abs(glse - lse).max() < 1e-4
+    top2 = np.sort(z, axis=1)[:, -2:]
+    assert ((tok.cpu().numpy() == z.argmax(axis=1)) | (top2[:, 1] - top2[:, 0] < 1e-4)).all()
+
+
 @pytest.mark.parametrize("tile", list(range(64)) + ["generic"])
 def test_readout_sample_every_tile(gpu_lib, tile):
     """Gumbel-max draws of the LM-head kernel (every tile and the vector-ALU path), on a ragged
