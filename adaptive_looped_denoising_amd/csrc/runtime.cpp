@@ -176,6 +176,7 @@ struct alodlm_ctx {
   size_t ws_bytes = 0;
   hipStream_t st = nullptr;
   std::string err;
+  bool dev_ready = false;  // RoPE tables uploaded and V padding cleared (first device call)
   // prefix cache state
   int cache_batch = -1, cache_prefix = -1;
   int built_depth = -1;  // depth-on-demand: Core depth the prefix state holds (-1: no state)
@@ -619,7 +620,21 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
     sscanf(v, "%d,%d,%d", &c->proj_splits[0], &c->proj_splits[1], &c->proj_splits[2]);
   if (const char* v = getenv("ALODLM_PROJ_TILES"))
     sscanf(v, "%d,%d,%d,%d", &c->proj_tiles[0], &c->proj_tiles[1], &c->proj_tiles[2], &c->proj_tiles[3]);
-  // RoPE tables, computed in double on the host: angle(pos, i) = pos * theta^(-2i/hd)
+  *out = c;
+  return ALODLM_OK;
+}
+
+namespace {
+// Device set-up of a context, run by the first entry point that enqueues device work (creation
+// itself touches no device, so argument checks of every entry point run without one): the RoPE
+// tables, computed in double on the host (angle(pos, i) = pos * theta^(-2i/hd)), are uploaded,
+// and the V cache and own-block V start at zero -- V rows are read in whole 64-key tiles whose
+// masked keys get probability 0, so their padding must hold finite values (0 * NaN would poison
+// the sum).  Synchronises the stream once.
+int ensure_device(alodlm_ctx* c) {
+  if (c->dev_ready) return ALODLM_OK;
+  const alodlm_config* cfg = &c->cfg;
+  const Plan& plan = c->plan;
   const int half = cfg->head_dim / 2;
   std::vector<float> cs((size_t)plan.max_pos * half), sn((size_t)plan.max_pos * half);
   for (int pos = 0; pos < plan.max_pos; ++pos)
@@ -630,23 +645,19 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
     }
   hipError_t e1 = hipMemcpyAsync(c->ws + plan.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, c->st);
   hipError_t e2 = hipMemcpyAsync(c->ws + plan.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, c->st);
-  // V rows are read in whole 64-key tiles whose masked keys get probability 0; their padding must
-  // hold finite values (0 * NaN would poison the sum), so the V cache and own-block V start at zero
   const size_t es = kv_esize(*cfg);
   if (e1 == hipSuccess) e1 = hipMemsetAsync(c->ws + plan.vcache, 0, es * plan.slot_elems * plan.alloc_slots, c->st);
   if (e1 == hipSuccess)
     e1 = hipMemsetAsync(c->ws + plan.vself, 0, es * (size_t)cfg->max_batch * cfg->n_kv_heads * cfg->head_dim * plan.Lp,
                         c->st);
   hipError_t e3 = hipStreamSynchronize(c->st);
-  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
-    g_create_error = std::string("RoPE table upload: ") +
-                     hipGetErrorString(e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3));
-    delete c;
-    return ALODLM_EHIP;
-  }
-  *out = c;
+  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess)
+    return c->fail(ALODLM_EHIP, std::string("context set-up (RoPE tables, V padding): ") +
+                                    hipGetErrorString(e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3)));
+  c->dev_ready = true;
   return ALODLM_OK;
 }
+}  // namespace
 
 namespace {
 // Fill each Core layer's higher depth planes of positions j0 .. j0+n-1 from their available depth
@@ -696,6 +707,7 @@ int prefill_common(alodlm_ctx* c, int32_t batch, int32_t prefix_len, const int32
   if (batch < 1 || batch > g.max_batch) return c->fail(ALODLM_EINVAL, "batch outside 1..max_batch");
   if (prefix_len < 0 || prefix_len > g.max_prefix) return c->fail(ALODLM_EINVAL, "prefix_len outside 0..max_prefix");
   if (prefix_len > 0 && !prefix_ids) return c->fail(ALODLM_EINVAL, "null prefix_ids");
+  if (int rc0 = ensure_device(c)) return rc0;
   const Plan& p = c->plan;
   c->cache_batch = -1;
   c->built_depth = -1;
@@ -777,6 +789,7 @@ int alodlm_prefill_kv_synthetic(alodlm_ctx* c, int32_t batch, int32_t prefix_len
   if (batch < 1 || batch > g.max_batch) return c->fail(ALODLM_EINVAL, "batch outside 1..max_batch");
   if (prefix_len < 0 || prefix_len > g.max_prefix) return c->fail(ALODLM_EINVAL, "prefix_len outside 0..max_prefix");
   if (!finite_f(k_scale) || !finite_f(v_scale)) return c->fail(ALODLM_EINVAL, "non-finite scale");
+  if (int rc0 = ensure_device(c)) return rc0;
   const Plan& p = c->plan;
   c->cache_batch = -1;
   c->built_depth = -1;
@@ -1051,8 +1064,11 @@ int alodlm_readout_commit(alodlm_ctx* c, const void* rows, int32_t n_rows, int32
     return c->fail(ALODLM_EINVAL, "null pointer");
   if (n_rows < 1 || n_rows > p.rows_step) return c->fail(ALODLM_EINVAL, "n_rows outside 1..max_batch*max_block");
   if (group < 1 || group > 64 || n_rows % group) return c->fail(ALODLM_EINVAL, "group must be 1..64 and divide n_rows");
+  // the per-sequence state (commit counts, stop flags, active lists) holds max_batch sequences
+  if (n_rows / group > g.max_batch) return c->fail(ALODLM_EINVAL, "n_rows / group exceeds max_batch sequences");
   if (boost_tok && !boost_val) return c->fail(ALODLM_EINVAL, "boost_tok without boost_val");
   if (!finite_f(tau_ent) || !finite_f(tau_halt)) return c->fail(ALODLM_EINVAL, "non-finite threshold");
+  if (int rc0 = ensure_device(c)) return rc0;
   const int B = n_rows / group, L = group;
   hipStream_t st = c->st;
   uint8_t* U = c->at<uint8_t>(p.U);
@@ -1107,6 +1123,7 @@ int alodlm_diag_read_kv(const alodlm_ctx* c, int32_t slot, int32_t b, int32_t j0
   if (slot < 0 || slot >= c->plan.n_slots || b < 0 || b >= g.max_batch || j0 < 0 || n < 0 ||
       j0 + n > g.max_prefix)
     return ALODLM_EINVAL;
+  if (ensure_device(const_cast<alodlm_ctx*>(c))) return ALODLM_EHIP;
   const size_t es = kv_esize(g), hd = g.head_dim, Pp = (size_t)c->plan.Pp;
   const char* kbase = c->ws + c->plan.kcache + es * (size_t)c->plan.slot_elems * slot;
   for (int h = 0; h < g.n_kv_heads; ++h) {

@@ -136,7 +136,10 @@ ALODLM_API int alodlm_kv_slots(const alodlm_config* cfg, int32_t* slots);
 /* Creates a context.  cfg and w are copied (the layer array too); the device
  * buffers they point to are borrowed.  workspace: device buffer of ws_bytes >=
  * alodlm_workspace_bytes(), 256-byte aligned, owned by the caller.  hip_stream:
- * a hipStream_t (NULL = default stream).  Enqueues the RoPE table upload. */
+ * a hipStream_t (NULL = default stream).  Host only: no device call is made here.
+ * The first entry point that enqueues device work sets the context up on the
+ * stream (RoPE tables uploaded, the V padding of the cache cleared) and
+ * synchronises the stream once; a HIP failure there returns ALODLM_EHIP. */
 ALODLM_API int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* workspace, size_t ws_bytes,
                   void* hip_stream, alodlm_ctx** out);
 
@@ -290,7 +293,8 @@ ALODLM_API int alodlm_denoise_block(alodlm_ctx* ctx, const alodlm_block_args* ar
  * progress and the Eq. 3 embedding rows, for n_rows rows grouped into sequences of
  * group rows (all unresolved, loop cap 1).
  *   rows: device [n_rows][d] readout states r (config dtype); n_rows <= max_batch * max_block,
- *         group in 1..64 dividing n_rows
+ *         group in 1..64 dividing n_rows, n_rows / group <= max_batch (the per-sequence state
+ *         holds max_batch sequences); else ALODLM_EINVAL
  *   boost_tok/boost_val: optional device [n_rows]
  * outputs (device): entropy, lse, lam, halt [n_rows] float; argmax, tokens [n_rows] int32;
  *   commit_loop [n_rows] int8; embed_out [n_rows][d] float (Emb(tok) for committed rows, 0 else).

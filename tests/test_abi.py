@@ -154,3 +154,61 @@ def test_null_context_calls_fail_cleanly():
     assert lib.alodlm_synth_fill(None, 0, 0, 10, 0, 0, 1.0, 0.0, None) == -1
     # diagnostics entry: bad shapes and null operands are rejected before any launch
     assert lib.alodlm_diag_readout_sample(0, 10, 64, None, None, None, 1, 1, 1, None, None, 0, 0, -1, None) == -1
+
+
+def _fake_ctx(w, **over):
+    """A context over fake device pointers: creation and argument checks touch no device."""
+    lib = B.load()
+    c = _cfg(w, **over)
+    wts, keep = _weights(w.dims.n_layers)
+    need = B.workspace_bytes(c)
+    out = ctypes.c_void_p(0)
+    rc = lib.alodlm_create(ctypes.byref(c), ctypes.byref(wts), ctypes.c_void_p(0x10000), need, None,
+                           ctypes.byref(out))
+    assert rc == B.OK and out.value
+    return lib, out.value, (wts, keep)
+
+
+def test_create_makes_no_device_call_and_calls_validate_first():
+    """Creation is host only, so every entry point's argument checks run here without a device."""
+    w = synth.workload("qwen3_8b")
+    lib, ctx, keep = _fake_ctx(w)
+    try:
+        cx = ctypes.c_void_p(ctx)
+        # a step or an append before any prefill
+        args = B.StepArgs(batch=8, block_len=32, block_ids=0x1000, tau_ent=0.6, tau_halt=0.5, k_loops=4)
+        out = B.StepOut(tokens=0x1000, commit_loop=0x1000, loops=0x1000)
+        assert lib.alodlm_denoise_step(cx, ctypes.byref(args), ctypes.byref(out)) == B.ESTATE
+        assert lib.alodlm_extend_kv(cx, 8, 32, ctypes.c_void_p(0x1000), None) == B.ESTATE
+        assert lib.alodlm_deepen_kv(cx, 2) == B.EINVAL            # not a depth-on-demand config
+        # prefill arguments out of range
+        assert lib.alodlm_prefill_kv(cx, 9, 1024, ctypes.c_void_p(0x1000), None) == B.EINVAL
+        assert lib.alodlm_prefill_kv(cx, 8, 1025, ctypes.c_void_p(0x1000), None) == B.EINVAL
+        assert lib.alodlm_prefill_kv(cx, 8, 1024, None, None) == B.EINVAL
+        assert lib.alodlm_prefill_kv_synthetic(cx, 8, 1024, 1, float("nan"), 1.0, None) == B.EINVAL
+        assert lib.alodlm_prefill_kv_depth(cx, 8, 1024, ctypes.c_void_p(0x1000), 1) == B.EINVAL
+    finally:
+        lib.alodlm_destroy(ctypes.c_void_p(ctx))
+
+
+@pytest.mark.parametrize("n_rows,group,why", [
+    (32, 0, b"group"), (32, 65, b"group"), (96, 64, b"group"), (0, 32, b"n_rows"), (257, 1, b"n_rows"),
+    (256, 16, b"max_batch"), (64, 1, b"max_batch"), (256, 31, b"group")])
+def test_readout_commit_rejects_groups_beyond_the_sequence_state(n_rows, group, why):
+    """The readout entry point's per-sequence state holds max_batch sequences: n_rows / group above
+    that (here max_batch 8, 8 x 32 rows) is rejected before any device work."""
+    w = synth.workload("qwen3_8b")
+    lib, ctx, keep = _fake_ctx(w)
+    try:
+        cx = ctypes.c_void_p(ctx)
+        p = ctypes.c_void_p(0x1000)
+        rc = lib.alodlm_readout_commit(cx, p, n_rows, group, 0.6, 0.5, None, None, *([p] * 8))
+        assert rc == B.EINVAL
+        assert why in lib.alodlm_last_error(cx)
+        # non-finite thresholds and a boost token array without values
+        rc = lib.alodlm_readout_commit(cx, p, 256, 32, float("inf"), 0.5, None, None, *([p] * 8))
+        assert rc == B.EINVAL
+        rc = lib.alodlm_readout_commit(cx, p, 256, 32, 0.6, 0.5, p, None, *([p] * 8))
+        assert rc == B.EINVAL
+    finally:
+        lib.alodlm_destroy(ctypes.c_void_p(ctx))
