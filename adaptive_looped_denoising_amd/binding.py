@@ -21,7 +21,7 @@ DIAG_STORE, DIAG_RESID, DIAG_SOFTSTAT, DIAG_SWIGLU = 0, 1, 2, 3
 
 EXPORTS = ("alodlm_workspace_bytes", "alodlm_kv_slots", "alodlm_create", "alodlm_prefill_kv",
            "alodlm_prefill_kv_synthetic", "alodlm_prefill_kv_depth", "alodlm_deepen_kv", "alodlm_extend_kv", "alodlm_denoise_step", "alodlm_denoise_block",
-           "alodlm_readout_commit",
+           "alodlm_readout_commit", "alodlm_readout_commit_static",
            "alodlm_last_step_stats", "alodlm_last_error", "alodlm_destroy", "alodlm_synth_fill",
            "alodlm_diag_gemm", "alodlm_diag_timing_enable", "alodlm_diag_timing_read", "alodlm_diag_read_kv", "alodlm_diag_buffer_offset",
            "alodlm_diag_readout_sample")
@@ -99,6 +99,7 @@ def load(path: str = LIB_PATH):
     lib.alodlm_readout_commit.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_float, c_float, c_void_p,
                                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                           c_void_p, c_void_p]
+    lib.alodlm_readout_commit_static.argtypes = lib.alodlm_readout_commit.argtypes
     lib.alodlm_last_step_stats.argtypes = [c_void_p, P(c_int64), P(c_int32)]
     lib.alodlm_last_error.argtypes = [c_void_p]
     lib.alodlm_last_error.restype = c_char_p
@@ -189,6 +190,16 @@ def readout_commit(ctx: int, rows_ptr: int, n_rows: int, group: int, tau_ent: fl
                                         c_void_p(entropy), c_void_p(lse), c_void_p(lam), c_void_p(halt),
                                         c_void_p(argmax), c_void_p(tokens), c_void_p(commit_loop),
                                         c_void_p(embed_out)), c_void_p(ctx))
+
+
+def readout_commit_static(ctx: int, rows_ptr: int, n_rows: int, group: int, tau_ent: float, tau_halt: float,
+                          boost_tok_ptr: int, boost_val_ptr: int, entropy: int, lse: int, lam: int, halt: int,
+                          argmax: int, tokens: int, commit_loop: int, embed_out: int):
+    _check(load().alodlm_readout_commit_static(c_void_p(ctx), c_void_p(rows_ptr), n_rows, group, tau_ent, tau_halt,
+                                               c_void_p(boost_tok_ptr or None), c_void_p(boost_val_ptr or None),
+                                               c_void_p(entropy), c_void_p(lse), c_void_p(lam), c_void_p(halt),
+                                               c_void_p(argmax), c_void_p(tokens), c_void_p(commit_loop),
+                                               c_void_p(embed_out)), c_void_p(ctx))
 
 
 def last_step_stats(ctx: int):

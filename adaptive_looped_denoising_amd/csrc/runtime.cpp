@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1053,49 +1054,172 @@ int alodlm_denoise_block(alodlm_ctx* c, const alodlm_block_args* a, alodlm_block
   return c->hip_check("block launch");
 }
 
-int alodlm_readout_commit(alodlm_ctx* c, const void* rows, int32_t n_rows, int32_t group, float tau_ent,
-                          float tau_halt, const int32_t* boost_tok, const float* boost_val, float* entropy, float* lse,
-                          float* lam, float* halt, int32_t* argmax, int32_t* tokens, int8_t* commit_loop,
-                          float* embed_out) {
-  if (!c) return ALODLM_EINVAL;
+}  // extern "C"
+
+namespace {
+// Scratch buffers of one readout (alodlm_readout_commit and its allocation-free variant).
+struct ReadoutScratch {
+  SoftStat* part;  // [n_rows][column tiles] LM-head partial statistics
+  uint8_t* U;      // [n_rows] unresolved flags
+  int32_t *ro_map, *ro_rows;                     // [n_rows]
+  int32_t *act0, *act1, *src_slot, *ncommit;     // [sequences]
+  uint8_t* stop;                                 // [sequences]
+  int8_t* seq_loops;                             // [sequences]
+  int32_t* cnt;                                  // [8]
+};
+
+int readout_check(alodlm_ctx* c, const void* rows, int32_t n_rows, int32_t group, float tau_ent, float tau_halt,
+                  const int32_t* boost_tok, const float* boost_val, float* entropy, float* lse, float* lam, float* halt,
+                  int32_t* argmax, int32_t* tokens, int8_t* commit_loop, float* embed_out) {
   const alodlm_config& g = c->cfg;
-  const Plan& p = c->plan;
   if (!rows || !entropy || !lse || !lam || !halt || !argmax || !tokens || !commit_loop || !embed_out)
     return c->fail(ALODLM_EINVAL, "null pointer");
-  if (n_rows < 1 || n_rows > p.rows_step) return c->fail(ALODLM_EINVAL, "n_rows outside 1..max_batch*max_block");
+  if (n_rows < 1 || n_rows > c->plan.rows_step) return c->fail(ALODLM_EINVAL, "n_rows outside 1..max_batch*max_block");
   if (group < 1 || group > 64 || n_rows % group) return c->fail(ALODLM_EINVAL, "group must be 1..64 and divide n_rows");
   // the per-sequence state (commit counts, stop flags, active lists) holds max_batch sequences
   if (n_rows / group > g.max_batch) return c->fail(ALODLM_EINVAL, "n_rows / group exceeds max_batch sequences");
   if (boost_tok && !boost_val) return c->fail(ALODLM_EINVAL, "boost_tok without boost_val");
   if (!finite_f(tau_ent) || !finite_f(tau_halt)) return c->fail(ALODLM_EINVAL, "non-finite threshold");
-  if (int rc0 = ensure_device(c)) return rc0;
+  return ALODLM_OK;
+}
+
+// The readout half of one loop on given rows: every buffer it writes besides the outputs is in `sc`
+// (launch_step_init sets every entry that is read before it is written).
+int readout_run(alodlm_ctx* c, const ReadoutScratch& sc, const void* rows, int32_t n_rows, int32_t group,
+                float tau_ent, float tau_halt, const int32_t* boost_tok, const float* boost_val, float* entropy,
+                float* lse, float* lam, float* halt, int32_t* argmax, int32_t* tokens, int8_t* commit_loop,
+                float* embed_out) {
+  const alodlm_config& g = c->cfg;
   const int B = n_rows / group, L = group;
   hipStream_t st = c->st;
-  uint8_t* U = c->at<uint8_t>(p.U);
-  int32_t* act0 = c->at<int32_t>(p.act_seq0);
-  int32_t* act1 = c->at<int32_t>(p.act_seq1);
-  int8_t* seq_loops = c->at<int8_t>(p.seq_loops);
-  launch_step_init(nullptr, B, L, g.mask_id, U, halt, tokens, commit_loop, c->at<int32_t>(p.ncommit),
-                   c->at<uint8_t>(p.stop), seq_loops, act0, c->at<int32_t>(p.src_slot), st);
-  launch_build_lists(B, L, B, 1, act0, c->at<uint8_t>(p.stop), U, c->at<int32_t>(p.ncommit), act1,
-                     c->at<int32_t>(p.src_slot), c->at<int32_t>(p.ro_rows), c->at<int32_t>(p.ro_map),
-                     c->at<int32_t>(p.cnt), st);
+  launch_step_init(nullptr, B, L, g.mask_id, sc.U, halt, tokens, commit_loop, sc.ncommit, sc.stop, sc.seq_loops,
+                   sc.act0, sc.src_slot, st);
+  launch_build_lists(B, L, B, 1, sc.act0, sc.stop, sc.U, sc.ncommit, sc.act1, sc.src_slot, sc.ro_rows, sc.ro_map,
+                     sc.cnt, st);
   launch_exit_gate(dt(c), rows, n_rows, g.d_model, c->w.exit_w, c->w.exit_b, lam, st);
   // LMHead over the given rows (row order = readout order)
   GemmEpi ep;
-  ep.part = c->at<SoftStat>(p.part);
+  ep.part = sc.part;
   ep.n_tiles = lm_tiles(c, n_rows);
   ep.btok = boost_tok;
   ep.bval = boost_val;
   gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_rows, g.vocab, g.d_model, nullptr, ep);
-  launch_softstat_combine(c->at<SoftStat>(p.part), n_rows, ep.n_tiles, nullptr, entropy, lse, argmax, nullptr, nullptr,
-                          st);
+  launch_softstat_combine(sc.part, n_rows, ep.n_tiles, nullptr, entropy, lse, argmax, nullptr, nullptr, st);
   // one loop of the commit rule (a starts at 0, so a = lambda); per-row records go to the outputs
-  launch_commit(B, 1, 1, L, B, tau_ent, tau_halt, act1, U, halt, c->at<int32_t>(p.ro_map), entropy, argmax, nullptr,
-                lam, lse, tokens, commit_loop, c->at<int32_t>(p.ncommit), c->at<uint8_t>(p.stop), seq_loops, nullptr,
-                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st);
+  launch_commit(B, 1, 1, L, B, tau_ent, tau_halt, sc.act1, sc.U, halt, sc.ro_map, entropy, argmax, nullptr, lam, lse,
+                tokens, commit_loop, sc.ncommit, sc.stop, sc.seq_loops, nullptr, nullptr, nullptr, nullptr, nullptr,
+                nullptr, nullptr, nullptr, nullptr, st);
   launch_embed_committed(dt(c), commit_loop, tokens, c->w.embed, n_rows, g.d_model, g.vocab, embed_out, st);
   return c->hip_check("readout launch");
+}
+
+constexpr size_t kStaticScratchBytes = (size_t)ALODLM_STATIC_SCRATCH_BYTES;
+}  // namespace
+
+// Scratch of the allocation-free readout (alodlm_readout_commit_static): one array per device,
+// held until the process ends.  Host code never passes the array's name to a kernel (on the host
+// it names a host-side stand-in); it uses the device address looked up once per device.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {nullptr};
+
+// Device address of the current device's array, looked up on the first call on that device.
+int static_scratch(void** out, std::string* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = std::string("hipGetDevice: ") + (e != hipSuccess ? hipGetErrorString(e) : "device index out of range");
+    return ALODLM_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *err = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+      return ALODLM_EHIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return ALODLM_OK;
+}
+
+// Carves the readout scratch for n_rows rows of `group` out of `base` (nullptr: sizes only);
+// returns the bytes used.
+size_t carve_readout(char* base, int n_rows, int group, int n_tiles, ReadoutScratch* sc) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  const size_t B = (size_t)(n_rows / group);
+  sc->part = (SoftStat*)take(sizeof(SoftStat) * (size_t)n_rows * n_tiles);
+  sc->U = (uint8_t*)take((size_t)n_rows);
+  sc->ro_map = (int32_t*)take(sizeof(int32_t) * n_rows);
+  sc->ro_rows = (int32_t*)take(sizeof(int32_t) * n_rows);
+  sc->act0 = (int32_t*)take(sizeof(int32_t) * B);
+  sc->act1 = (int32_t*)take(sizeof(int32_t) * B);
+  sc->src_slot = (int32_t*)take(sizeof(int32_t) * B);
+  sc->ncommit = (int32_t*)take(sizeof(int32_t) * B);
+  sc->stop = (uint8_t*)take(B);
+  sc->seq_loops = (int8_t*)take(B);
+  sc->cnt = (int32_t*)take(sizeof(int32_t) * 8);
+  return off;
+}
+}  // namespace
+
+extern "C" {
+
+int alodlm_readout_commit(alodlm_ctx* c, const void* rows, int32_t n_rows, int32_t group, float tau_ent,
+                          float tau_halt, const int32_t* boost_tok, const float* boost_val, float* entropy, float* lse,
+                          float* lam, float* halt, int32_t* argmax, int32_t* tokens, int8_t* commit_loop,
+                          float* embed_out) {
+  if (!c) return ALODLM_EINVAL;
+  if (int rc = readout_check(c, rows, n_rows, group, tau_ent, tau_halt, boost_tok, boost_val, entropy, lse, lam, halt,
+                             argmax, tokens, commit_loop, embed_out))
+    return rc;
+  if (int rc0 = ensure_device(c)) return rc0;
+  const Plan& p = c->plan;
+  ReadoutScratch sc;
+  sc.part = c->at<SoftStat>(p.part);
+  sc.U = c->at<uint8_t>(p.U);
+  sc.ro_map = c->at<int32_t>(p.ro_map);
+  sc.ro_rows = c->at<int32_t>(p.ro_rows);
+  sc.act0 = c->at<int32_t>(p.act_seq0);
+  sc.act1 = c->at<int32_t>(p.act_seq1);
+  sc.src_slot = c->at<int32_t>(p.src_slot);
+  sc.ncommit = c->at<int32_t>(p.ncommit);
+  sc.stop = c->at<uint8_t>(p.stop);
+  sc.seq_loops = c->at<int8_t>(p.seq_loops);
+  sc.cnt = c->at<int32_t>(p.cnt);
+  return readout_run(c, sc, rows, n_rows, group, tau_ent, tau_halt, boost_tok, boost_val, entropy, lse, lam, halt,
+                     argmax, tokens, commit_loop, embed_out);
+}
+
+int alodlm_readout_commit_static(alodlm_ctx* c, const void* rows, int32_t n_rows, int32_t group, float tau_ent,
+                                 float tau_halt, const int32_t* boost_tok, const float* boost_val, float* entropy,
+                                 float* lse, float* lam, float* halt, int32_t* argmax, int32_t* tokens,
+                                 int8_t* commit_loop, float* embed_out) {
+  if (!c) return ALODLM_EINVAL;
+  if (int rc = readout_check(c, rows, n_rows, group, tau_ent, tau_halt, boost_tok, boost_val, entropy, lse, lam, halt,
+                             argmax, tokens, commit_loop, embed_out))
+    return rc;
+  ReadoutScratch sc;
+  const size_t need = carve_readout(nullptr, n_rows, group, lm_tiles(c, n_rows), &sc);
+  if (need > kStaticScratchBytes)
+    return c->fail(ALODLM_EINVAL, "readout needs " + std::to_string(need) + " bytes of scratch, the fixed array holds " +
+                                      std::to_string(kStaticScratchBytes));
+  void* base = nullptr;
+  std::string err;
+  if (int rc = static_scratch(&base, &err)) return c->fail(rc, err);
+  carve_readout((char*)base, n_rows, group, lm_tiles(c, n_rows), &sc);
+  return readout_run(c, sc, rows, n_rows, group, tau_ent, tau_halt, boost_tok, boost_val, entropy, lse, lam, halt,
+                     argmax, tokens, commit_loop, embed_out);
 }
 
 int alodlm_diag_timing_enable(alodlm_ctx* c, int32_t enable) {

@@ -256,7 +256,9 @@ class Engine:
 
     # ------------------------------------------------------------------ readout half of a loop
     def readout_commit(self, rows: torch.Tensor, group: int, tau_ent: float, tau_halt: float,
-                       boost_tok: Optional[torch.Tensor] = None, boost_val: Optional[torch.Tensor] = None) -> dict:
+                       boost_tok: Optional[torch.Tensor] = None, boost_val: Optional[torch.Tensor] = None,
+                       static_scratch: bool = False) -> dict:
+        """``static_scratch``: the allocation-free entry point (scratch in the library's fixed array)."""
         n = rows.shape[0]
         dev = self.device
         o = dict(entropy=torch.empty(n, dtype=torch.float32, device=dev),
@@ -267,10 +269,10 @@ class Engine:
                  tokens=torch.empty(n, dtype=torch.int32, device=dev),
                  commit_loop=torch.empty(n, dtype=torch.int8, device=dev),
                  embed=torch.empty((n, self.w.dims.d_model), dtype=torch.float32, device=dev))
-        B.readout_commit(self.ctx, rows.data_ptr(), n, group, tau_ent, tau_halt, _ptr(boost_tok), _ptr(boost_val),
-                         o["entropy"].data_ptr(), o["lse"].data_ptr(), o["lam"].data_ptr(), o["halt"].data_ptr(),
-                         o["argmax"].data_ptr(), o["tokens"].data_ptr(), o["commit_loop"].data_ptr(),
-                         o["embed"].data_ptr())
+        fn = B.readout_commit_static if static_scratch else B.readout_commit
+        fn(self.ctx, rows.data_ptr(), n, group, tau_ent, tau_halt, _ptr(boost_tok), _ptr(boost_val),
+           o["entropy"].data_ptr(), o["lse"].data_ptr(), o["lam"].data_ptr(), o["halt"].data_ptr(),
+           o["argmax"].data_ptr(), o["tokens"].data_ptr(), o["commit_loop"].data_ptr(), o["embed"].data_ptr())
         return o
 
     def close(self):

@@ -304,6 +304,29 @@ ALODLM_API int alodlm_readout_commit(alodlm_ctx* ctx, const void* rows, int32_t 
                           float* lse, float* lam, float* halt, int32_t* argmax, int32_t* tokens,
                           int8_t* commit_loop, float* embed_out);
 
+/* Bytes of the fixed scratch array that alodlm_readout_commit_static uses on each device. */
+#define ALODLM_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* Allocation-free variant of alodlm_readout_commit, for callers that cannot allocate device memory
+ * at call time: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, same kernels and the same outputs bit for bit; it does not touch the context's
+ * workspace.  Every scratch buffer (LM-head partial statistics, unresolved flags, sequence lists,
+ * counters) lives in one fixed device array inside the library, ALODLM_STATIC_SCRATCH_BYTES per
+ * device, held by each device the library runs on until the process ends.  A call needs
+ *   16 * n_rows * ceil(V / BN)  (BN = the LM-head column tile: 192 up to 128 rows, else 256)
+ *   + about 9 * n_rows + 18 * (n_rows / group) bytes (each piece rounded up to 256)
+ * and returns ALODLM_EINVAL when that exceeds the array (at V = 151936 about 3500 rows fit).
+ * The array of the current device (hipGetDevice) is used; its address is looked up once per device
+ * on the first call there (a failure returns ALODLM_EHIP).  Calls on one device share the array,
+ * which keeps the last call's contents (every entry a call reads is written by that call first):
+ * calls that overlap on one device, from several streams or threads, race on it.  Makes no
+ * allocation and calls no allocating routine.  Asynchronous on the context's stream. */
+ALODLM_API int alodlm_readout_commit_static(alodlm_ctx* ctx, const void* rows, int32_t n_rows, int32_t group,
+                                            float tau_ent, float tau_halt, const int32_t* boost_tok,
+                                            const float* boost_val, float* entropy, float* lse, float* lam,
+                                            float* halt, int32_t* argmax, int32_t* tokens, int8_t* commit_loop,
+                                            float* embed_out);
+
 /* Counters of the last step: layer calls launched and loops run (host). */
 ALODLM_API int alodlm_last_step_stats(const alodlm_ctx* ctx, int64_t* layer_calls, int32_t* loops_run);
 

@@ -212,3 +212,27 @@ def test_readout_commit_rejects_groups_beyond_the_sequence_state(n_rows, group, 
         assert rc == B.EINVAL
     finally:
         lib.alodlm_destroy(ctypes.c_void_p(ctx))
+
+
+def test_static_readout_validates_and_bounds_its_scratch():
+    """The allocation-free readout takes the same argument checks, and rejects a readout whose
+    scratch would not fit the library's fixed array (checked before any device call)."""
+    w = synth.workload("qwen3_8b")
+    lib, ctx, keep = _fake_ctx(w)
+    p = ctypes.c_void_p(0x1000)
+    try:
+        cx = ctypes.c_void_p(ctx)
+        assert lib.alodlm_readout_commit_static(cx, p, 256, 16, 0.6, 0.5, None, None, *([p] * 8)) == B.EINVAL
+        assert b"max_batch" in lib.alodlm_last_error(cx)
+        assert lib.alodlm_readout_commit_static(cx, None, 256, 32, 0.6, 0.5, None, None, *([p] * 8)) == B.EINVAL
+    finally:
+        lib.alodlm_destroy(ctypes.c_void_p(ctx))
+    # 2048 rows over a 4M-token vocabulary: 16 B x 2048 x 15625 tiles of statistics > 32 MiB
+    big = replace(w, batch=64, dims=replace(w.dims, vocab=4_000_000))
+    lib, ctx, keep = _fake_ctx(big, mask_id=4_000_000 - 1)
+    try:
+        cx = ctypes.c_void_p(ctx)
+        assert lib.alodlm_readout_commit_static(cx, p, 2048, 32, 0.6, 0.5, None, None, *([p] * 8)) == B.EINVAL
+        assert b"scratch" in lib.alodlm_last_error(cx)
+    finally:
+        lib.alodlm_destroy(ctypes.c_void_p(ctx))
