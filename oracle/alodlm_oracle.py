@@ -172,10 +172,13 @@ def rope(x, pos, theta: float) -> np.ndarray:
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
-def attention(q, k, v, allowed: Optional[np.ndarray] = None) -> np.ndarray:
+def attention(q, k, v, allowed: Optional[np.ndarray] = None, prec=None) -> np.ndarray:
     """softmax(q k^T / sqrt(hd)) v per query head; q [Hq][n][hd], k and v [Hkv][m][hd].
 
     Query head h reads kv head floor(h * Hkv / Hq).  ``allowed`` [n][m] masks keys.
+    ``prec="bf16"``: the unnormalised probabilities exp(s - max s) that multiply the values are
+    rounded to bfloat16 (a bf16 pipeline feeds them to its bf16 product with V); the normaliser
+    sums them unrounded.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     Hq, n, hd = q.shape
@@ -188,8 +191,7 @@ def attention(q, k, v, allowed: Optional[np.ndarray] = None) -> np.ndarray:
             s = np.where(allowed, s, -np.inf)
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
-        p = p / p.sum(axis=1, keepdims=True)
-        out[h] = p @ v[kv]
+        out[h] = (_rnd(p, prec) @ v[kv]) / p.sum(axis=1, keepdims=True)
     return out
 
 
@@ -208,8 +210,9 @@ def layer_forward(x, W: Dict[str, np.ndarray], li: int, dims, eps: float, theta:
     [Hkv][n][hd] are this call's post-RoPE keys and values of the rows.
 
     ``prec="bf16"`` rounds to bfloat16 where a bf16 pipeline stores values: the
-    normalised inputs of the projections, q / k / v, the attention output and the
-    SwiGLU output (the residual stream stays exact).  Default: exact arithmetic.
+    normalised inputs of the projections, q / k / v, the attention probabilities that
+    multiply the values, the attention output and the SwiGLU output (the residual stream
+    stays exact).  Default: exact arithmetic.
     ``kv="fp8"``: keys and values are stored (and attended to) in FP8 E4M3.
     """
     p = "layers.%d." % li
@@ -230,7 +233,7 @@ def layer_forward(x, W: Dict[str, np.ndarray], li: int, dims, eps: float, theta:
     if causal:
         allowed = np.ones((n, m + n), dtype=bool)
         allowed[:, m:] = np.tril(np.ones((n, n), dtype=bool))
-    a = _rnd(attention(q, keys, vals, allowed).transpose(1, 0, 2).reshape(n, Hq * hd), prec)
+    a = _rnd(attention(q, keys, vals, allowed, prec).transpose(1, 0, 2).reshape(n, Hq * hd), prec)
     x = x + matmul_t(a, W[p + "wo"])
     h2 = _rnd(rms_norm(x, W[p + "ffn_norm"], eps), prec)
     gu = matmul_t(h2, W[p + "w_gate_up"])

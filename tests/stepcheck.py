@@ -1,0 +1,56 @@
+"""One GPU denoising step against the oracle: free run compared position by position, records
+compared while both runs agree, then a teacher-forced run compared loop by loop (shared by the
+GPU step tests and the smoke check)."""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import run as orun
+from tests.parity import (agreed_loops, calibrated, compare_decisions, compare_records, literal_tolerances, log,
+                          loop_depth, report, tolerances)
+
+
+def check_step(w, e, W=None, seqs=None, caches=None, k_loops=None, block_ids=None, sample=None, name="",
+               teacher_check=True):
+    """Runs the engine's step free and teacher-forced and the oracle on sequences ``seqs``.
+    Returns (oracle results, free GPU result, decision summary per sequence)."""
+    W = orun.weights(w) if W is None else W
+    K = w.k_max if k_loops is None else k_loops
+    log("case %s dtype=%s B=%d P=%d L=%d K=%d tau=%.3g q=%.3g sample=%s seqs=%s" % (
+        name or w.name, w.dtype, w.batch, w.prefix, w.block, K, w.tau_ent, w.tau_halt, sample,
+        "all" if seqs is None else list(seqs)))
+    free = e.step(k_loops=K, records=True, hidden=True, block_ids=block_ids, sample=sample)
+    ores = orun.step(w, W=W, seqs=seqs, k_loops=K, record_hidden=True, block_ids=block_ids, caches=caches,
+                     sample=sample)
+    deep = calibrated(w, loop_depth(w, max([r["loops"] for r in ores] + [1])))
+    o16 = None
+    if deep:   # the oracle's own bf16 drift on this input and these decisions
+        o16 = orun.step(w, W=W, seqs=seqs, k_loops=K, record_hidden=True, block_ids=block_ids, caches=caches,
+                        prec="bf16", teacher=orun.teacher_from(ores), sample=sample)
+    tols = tolerances(w, ores, o16)
+    assert free.n_committed == int((free.commit_loop != 0).sum())
+    dec = compare_decisions(w, ores, free, tols)
+    worst_free = compare_records(w, ores, free, tols, upto=agreed_loops(ores, dec))
+    log("free run: worst errors %s; decisions %s" % (worst_free, dec))
+    worst_tf = None
+    if teacher_check:
+        teacher = orun.teacher_from(ores)
+        for b in range(w.batch):   # sequences the oracle did not run keep the GPU's own decisions
+            if b not in teacher:
+                teacher[b] = dict(commit_loop=free.commit_loop[b], tokens=free.tokens[b], stop_loop=free.loops[b])
+        tf = e.step(k_loops=K, records=True, hidden=True, teacher=teacher, block_ids=block_ids, sample=sample)
+        worst_tf = compare_records(w, ores, tf, tols)
+        for r in ores:
+            b = r["seq"]
+            assert np.array_equal(tf.commit_loop[b], r["commit_loop"]) and np.array_equal(tf.tokens[b], r["tokens"])
+            assert tf.loops[b] == r["loops"]
+        log("teacher-forced: worst errors %s" % worst_tf)
+    worst = {k: max(worst_free.get(k, 0.0), (worst_tf or {}).get(k, 0.0)) for k in ("hidden", "H", "lam", "a", "lse")}
+    depth = max(loop_depth(w, r["loops"]) for r in ores) if any(r["loops"] for r in ores) else 0
+    report(name or w.name, "%s %s B=%d P=%d L=%d K=%d" % (w.name, w.dtype, w.batch, w.prefix, w.block, K), worst,
+           literal_tolerances(w.dtype),
+           dict(layer_calls=depth, tier="calibrated" if deep else "literal",
+                positions_compared_free=sum(d["compared"] for d in dec.values()),
+                sequences_diverged=[b for b, d in dec.items() if d["diverged"] is not None],
+                entropy_commits=int(sum(int((r["commit_loop"] > 0).sum()) for r in ores))))
+    return ores, free, dec

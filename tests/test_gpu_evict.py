@@ -8,8 +8,8 @@ import pytest
 from adaptive_looped_denoising_amd import synth
 from oracle import alodlm_oracle as orc
 from oracle import run as orun
-from tests.parity import CAL_FACTOR, calibrated_tolerances, compare_decisions, compare_records, log, rel_rows, \
-    tol_hidden
+from tests.parity import cache_tolerance, log, rel_rows
+from tests.stepcheck import check_step
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +58,7 @@ def _stored(w, cache, avail):
 
 def _check_cache(e, w, b, j0, n, ref, ref16=None, exact=False):
     """Every stored slot of sequence b, rows j0 .. j0+n-1, against ``ref`` (from _stored): bit-exact,
-    fp32 at 1e-4, or bf16 within the depth model / CAL_FACTOR x the drift of ``ref16``."""
+    or within tests.parity.cache_tolerance (the drift taken from the rounding-point oracle ``ref16``)."""
     assert len(ref) == e.kv_slots == w.dims.kv_slots(orun.keep_depths(w))
     worst = 0.0
     for slot, (K, V, calls) in enumerate(ref):
@@ -69,12 +69,11 @@ def _check_cache(e, w, b, j0, n, ref, ref16=None, exact=False):
                 assert np.array_equal(g, o), "seq %d slot %d" % (b, slot)
                 continue
             err = float(rel_rows(g.reshape(-1, w.dims.head_dim), o.reshape(-1, w.dims.head_dim)).max())
-            if w.dtype == "fp32":
-                tol = 1e-4
-            else:
+            drift = 0.0
+            if w.dtype == "bf16":
                 o16 = ref16[slot][gi][:, j0:j0 + n]
                 drift = float(rel_rows(o16.reshape(-1, w.dims.head_dim), o.reshape(-1, w.dims.head_dim)).max())
-                tol = max(tol_hidden(w.dtype, calls), CAL_FACTOR * drift)
+            tol = cache_tolerance(w.dtype, drift)
             assert err <= tol, "seq %d slot %d rows %d..%d error %.3g > %.3g" % (b, slot, j0, j0 + n, err, tol)
             worst = max(worst, err / tol)
     return worst
@@ -160,17 +159,7 @@ def test_mid_bf16_evicted_synthetic_cache_is_exact(gpu_lib):
 
 def _check_step_bf16(w):
     e = _engine(w)
-    W = orun.weights(w)
-    ores = orun.step(w, W=W, record_hidden=True)
-    o16 = orun.step(w, W=W, record_hidden=True, prec="bf16", teacher=orun.teacher_from(ores))
-    tols = calibrated_tolerances(w, ores, o16)
-    free = e.step(records=True, hidden=True)
-    flagged = compare_decisions(w, ores, free, tols)
-    clean = [r for r in ores if r["seq"] not in flagged]
-    if clean:
-        log("free run worst errors: %s" % compare_records(w, clean, free, tols=tols))
-    tf = e.step(records=True, hidden=True, teacher=orun.teacher_from(ores))
-    log("teacher-forced worst errors: %s" % compare_records(w, ores, tf, tols=tols))
+    ores, _, _ = check_step(w, e, name=w.name + " evicted")
     return e, ores
 
 

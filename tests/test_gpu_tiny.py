@@ -8,7 +8,8 @@ import torch
 
 from adaptive_looped_denoising_amd import synth
 from oracle import run as orun
-from tests.parity import TOL, calibrated_tolerances, compare_decisions, compare_records, log, rel_rows
+from tests.parity import log, rel_rows
+from tests.stepcheck import check_step
 
 pytestmark = pytest.mark.gpu
 
@@ -20,34 +21,9 @@ def _engine(w, **kw):
     return e
 
 
-def _check_step(w, gpu_lib, k_loops=None, block_ids=None, overrides=None, oracle_W=None, sample=None):
-    log("case %s dtype=%s B=%d P=%d L=%d K=%d tau=%.3g q=%.3g sample=%s" % (
-        w.name, w.dtype, w.batch, w.prefix, w.block, w.k_max, w.tau_ent, w.tau_halt, sample))
+def _check_step(w, gpu_lib, k_loops=None, block_ids=None, overrides=None, oracle_W=None, sample=None, name=""):
     e = _engine(w, overrides=overrides)
-    K = w.k_max if k_loops is None else k_loops
-    W = orun.weights(w) if oracle_W is None else oracle_W
-    ores = orun.step(w, W=W, k_loops=K, record_hidden=True, block_ids=block_ids, sample=sample)
-    tols = None
-    if w.dtype == "bf16":  # bf16 drift of this input: the oracle at the pipeline's rounding points
-        o16 = orun.step(w, W=W, k_loops=K, record_hidden=True, block_ids=block_ids, prec="bf16",
-                        teacher=orun.teacher_from(ores))
-        tols = calibrated_tolerances(w, ores, o16)
-    free = e.step(k_loops=K, records=True, hidden=True, block_ids=block_ids, sample=sample)
-    flagged = compare_decisions(w, ores, free, tols)
-    clean = [r for r in ores if r["seq"] not in flagged]
-    if clean:
-        worst = compare_records(w, clean, free, tols=tols)
-        log("free run worst errors: %s" % worst)
-    tf = e.step(k_loops=K, records=True, hidden=True, teacher=orun.teacher_from(ores), block_ids=block_ids,
-                sample=sample)
-    worst = compare_records(w, ores, tf, tols=tols)
-    log("teacher-forced worst errors: %s" % worst)
-    for r in ores:
-        b = r["seq"]
-        assert np.array_equal(tf.commit_loop[b], r["commit_loop"]) and np.array_equal(tf.tokens[b], r["tokens"])
-        assert tf.loops[b] == r["loops"]
-    n_commit = sum(int((r["commit_loop"] != 0).sum()) for r in ores)
-    assert tf.n_committed == n_commit
+    ores, free, dec = check_step(w, e, W=oracle_W, k_loops=k_loops, block_ids=block_ids, sample=sample, name=name)
     return e, ores, free
 
 
@@ -297,3 +273,27 @@ def test_empty_prefix(gpu_lib):
 def test_mid_fp32_matches_bf16_structure(gpu_lib):
     # fp32 mode on the same shapes (generic kernels) at the fp32 tolerance
     _check_step(_mid(dtype="fp32", prefix=100), gpu_lib)
+
+
+def test_split_without_prelude_and_coda(gpu_lib):
+    """The pages' 1.7B layout -- no Prelude, no Coda, the Core loops over the whole stack -- in fp32
+    (literal tolerances) and bf16 on the matrix cores, prefix built by the library's prefill."""
+    dims = replace(synth.TINY_DIMS, n_pre=0, n_core=3, n_coda=0)
+    w = replace(synth.workload("tiny", boost_lo=8.0, boost_hi=14.0, batch=2), dims=dims, name="tiny_0_3_0")
+    e, ores, free = _check_step(w, gpu_lib, name="tiny split 0/3/0 fp32")
+    calls, loops = e.stats()
+    assert calls == loops * 3
+    mdims = replace(MID_DIMS, n_pre=0, n_core=4, n_coda=0)
+    _check_step(replace(_mid(batch=2, prefix=200), dims=mdims, name="mid_0_4_0"), gpu_lib, name="mid split 0/4/0")
+
+
+def test_mid_bf16_step_is_deterministic(gpu_lib):
+    """The matrix-core step run twice (split-K and split-KV partials merged in fixed order): every
+    output, record and hidden row bit for bit."""
+    w = _mid()
+    e = _engine(w)
+    a = e.step(records=True, hidden=True)
+    b = e.step(records=True, hidden=True)
+    for k in ("tokens", "commit_loop", "loops", "entropy", "lam", "halt", "lse", "argmax", "hidden"):
+        x, y = getattr(a, k), getattr(b, k)
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), k

@@ -112,6 +112,29 @@ MUTANTS = {
     "block_without_mask_still_loops": (
         "denoise_step_sequence", "if not U.any():", "if False:",
         [pins.test_no_mask_no_loop_and_sampled_steps_advance_the_counter]),
+    "bf16_residual_stream_rounded": (
+        "layer_forward", "x = x + matmul_t(a, W[p + \"wo\"])", "x = _rnd(x + matmul_t(a, W[p + \"wo\"]), prec)",
+        [lambda: pins.test_bf16_rounding_points_match_an_independent_forward(True)]),
+    "bf16_attention_output_not_rounded": (
+        "layer_forward", "a = _rnd(attention(q, keys, vals, allowed, prec)", "a = (attention(q, keys, vals, allowed, prec)",
+        [lambda: pins.test_bf16_rounding_points_match_an_independent_forward(True)]),
+    "bf16_probabilities_not_rounded": (
+        "attention", "(_rnd(p, prec) @ v[kv])", "(p @ v[kv])",
+        [lambda: pins.test_bf16_rounding_points_match_an_independent_forward(True)]),
+    "bf16_probabilities_rounded_after_normalising": (
+        "attention", "(_rnd(p, prec) @ v[kv]) / p.sum(axis=1, keepdims=True)",
+        "_rnd(p / p.sum(axis=1, keepdims=True), prec) @ v[kv]",
+        [lambda: pins.test_bf16_rounding_points_match_an_independent_forward(True)]),
+    "bf16_swiglu_output_not_rounded": (
+        "layer_forward", "matmul_t(_rnd(silu(gu[:, :F]) * gu[:, F:], prec)", "matmul_t((silu(gu[:, :F]) * gu[:, F:])",
+        [lambda: pins.test_bf16_rounding_points_match_an_independent_forward(True)]),
+    "bf16_readout_rows_not_rounded": (
+        "denoise_step_sequence", "readout(_rnd(r[rows], prec), W[\"lm_head\"], bt, bv)",
+        "readout(r[rows], W[\"lm_head\"], bt, bv)",
+        [lambda: pins.test_bf16_rounding_points_match_an_independent_forward(True)]),
+    "bf16_value_rows_not_rounded": (
+        "layer_forward", "v = _kv_round(qkv[:, (Hq + Hkv) * hd:]", "v = (lambda t, *_: t)(qkv[:, (Hq + Hkv) * hd:]",
+        [lambda: pins.test_bf16_rounding_points_match_an_independent_forward(True)]),
     "eviction_keeps_one_depth_too_many": (
         "evict_depths", "range(1, keep + 1)", "range(1, keep + 2)",
         [pins.test_evict_depths_buffer_counts_match_page]),

@@ -248,10 +248,20 @@ def test_layer_call_count_matches_page():
 
 
 # --------------------------------------------------------------------------- step-level pins
-def _straight_line_readout(w, W, prefix, block):
+def _torch_bf16(t):
+    """torch's own rounding to bfloat16 (through float32, as a float32 pipeline stores it)."""
+    return torch.from_numpy(np.ascontiguousarray(t, dtype=np.float64)).to(torch.float32).to(
+        torch.bfloat16).to(torch.float64).numpy()
+
+
+def _straight_line_readout(w, W, prefix, block, bf16=False):
     """Independent forward of [prefix ; block] through the whole stack in one pass: prefix rows
     attend causally, block rows attend to everything.  Returns the block rows' readout rows
-    (final RMSNorm of the last layer's output) and their logits."""
+    (final RMSNorm of the last layer's output) and their logits.  ``bf16``: values are rounded to
+    bfloat16 (by torch) at the rounding points a bf16 pipeline has -- the normalised projection
+    inputs, q and k after RoPE, v, the unnormalised attention probabilities that multiply v, the
+    attention output, the SwiGLU output and the readout rows feeding the LM head; the residual
+    stream, the softmax normaliser and the readout rows themselves stay exact."""
     D = w.dims
     Hq, Hkv, hd, F = D.n_q_heads, D.n_kv_heads, D.head_dim, D.ffn
     ids = np.concatenate([prefix, block])
@@ -272,32 +282,43 @@ def _straight_line_readout(w, W, prefix, block):
         a, b = t[..., :half], t[..., half:]
         return np.concatenate([a * cos[:, None] - b * sin[:, None], a * sin[:, None] + b * cos[:, None]], -1)
 
+    rb = _torch_bf16 if bf16 else (lambda t: t)
     for l in range(D.n_layers):
         g = lambda k: np.array(W["layers.%d.%s" % (l, k)], dtype=np.float64)
-        t = norm(x, g("attn_norm"))
+        t = rb(norm(x, g("attn_norm")))
         wq, wk, wv = np.split(g("wqkv"), [Hq * hd, (Hq + Hkv) * hd])
-        q = rot(norm(np.einsum("nd,od->no", t, wq).reshape(n, Hq, hd), g("q_norm")))
-        k = rot(norm(np.einsum("nd,od->no", t, wk).reshape(n, Hkv, hd), g("k_norm")))
-        v = np.einsum("nd,od->no", t, wv).reshape(n, Hkv, hd)
+        q = rb(rot(norm(np.einsum("nd,od->no", t, wq).reshape(n, Hq, hd), g("q_norm"))))
+        k = rb(rot(norm(np.einsum("nd,od->no", t, wk).reshape(n, Hkv, hd), g("k_norm"))))
+        v = rb(np.einsum("nd,od->no", t, wv).reshape(n, Hkv, hd))
         k = np.repeat(k, Hq // Hkv, axis=1)
         v = np.repeat(v, Hq // Hkv, axis=1)
         sc = np.einsum("qhe,khe->hqk", q, k) / np.sqrt(hd)
         sc[:, ~vis] = -np.inf
         pr = np.exp(sc - sc.max(-1, keepdims=True))
-        pr /= pr.sum(-1, keepdims=True)
-        o = np.einsum("hqk,khe->qhe", pr, v).reshape(n, Hq * hd)
+        o = np.einsum("hqk,khe->qhe", rb(pr), v) / pr.sum(-1).transpose(1, 0)[:, :, None]
+        o = rb(o.reshape(n, Hq * hd))
         x = x + o @ g("wo").T
-        t = norm(x, g("ffn_norm"))
+        t = rb(norm(x, g("ffn_norm")))
         gate, up = np.split(t @ g("w_gate_up").T, 2, axis=1)
-        x = x + (gate * (1.0 / (1.0 + np.exp(-gate))) * up) @ g("w_down").T
+        x = x + rb(gate * (1.0 / (1.0 + np.exp(-gate))) * up) @ g("w_down").T
     r = norm(x[P:], np.array(W["final_norm"], dtype=np.float64))
-    return r, r @ np.array(W["lm_head"], dtype=np.float64).T
+    return r, rb(r) @ np.array(W["lm_head"], dtype=np.float64).T
 
 
 def test_all_commit_reduces_to_one_fixed_depth_pass():
     """tau_ent >= ln V commits every masked row at loop 1: the tokens are the argmax of a plain
     fixed-depth stack (here with a one-deep cache, where the stack and the loop coincide)."""
+    _all_commit_case((1, 2, 1))
+
+
+def test_all_commit_reduction_without_prelude_and_coda():
+    """The same reduction for a split whose Core is the whole stack (the pages' 1.7B layout)."""
+    _all_commit_case((0, 4, 0))
+
+
+def _all_commit_case(split):
     w = _tiny(k_max=1, tau_ent=math.log(512) + 1.0)
+    w = replace(w, dims=replace(w.dims, n_pre=split[0], n_core=split[1], n_coda=split[2]))
     W = _rand_weights(w, seed=5)
     pre = synth.prefix_ids(w)[0]
     blk = synth.block_ids(w)[0].copy()
@@ -319,10 +340,41 @@ def test_all_commit_reduces_to_one_fixed_depth_pass():
     assert np.array_equal(res[0]["tokens"][~masked], blk[~masked])
 
 
-def test_looping_equals_unrolling():
-    """K loops of the shared Core equal one pass of a stack with the Core unrolled K times."""
+@pytest.mark.parametrize("gqa", [False, True])
+def test_bf16_rounding_points_match_an_independent_forward(gqa):
+    """The oracle's bf16 rounding-point mode (the drift model of a bf16 pipeline) rounds exactly at
+    the documented points: with every masked row committing at loop 1 it equals the straight-line
+    forward above rounded by torch at those points -- readout rows and entropies to fp64 rounding.
+    A rounding point too many or too few moves them by bf16 noise (about 1e-3), far beyond."""
+    w = _tiny(k_max=1, tau_ent=math.log(512) + 1.0)
+    if not gqa:
+        w = replace(w, dims=replace(w.dims, n_kv_heads=4))
+    W = _rand_weights(w, seed=15)
+    pre = synth.prefix_ids(w)[0]
+    blk = synth.block_ids(w)[0].copy()
+    blk[[2, 9]] = [41, 250]
+    nob = (np.full((1, 16), -1), np.zeros((1, 16)))
+    res = run.step(w, W=W, block_ids=blk[None], boost=nob, record_hidden=True, prec="bf16")
+    exact = run.step(w, W=W, block_ids=blk[None], boost=nob, record_hidden=True)
+    r_ref, z_ref = _straight_line_readout(w, W, pre, blk, bf16=True)
+    rec = res[0]["records"][0]
+    np.testing.assert_allclose(rec["r"], r_ref, rtol=1e-10, atol=1e-12)
+    p = np.exp(z_ref - z_ref.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    masked = blk == w.mask_id
+    np.testing.assert_allclose(rec["H"][masked], -(p * np.log(p)).sum(axis=1)[masked], rtol=1e-10)
+    # and the rounding is real: the exact oracle differs by bf16 noise
+    rel = np.linalg.norm(exact[0]["records"][0]["r"] - rec["r"], axis=1) / np.linalg.norm(rec["r"], axis=1)
+    assert 1e-4 < rel.max() < 2e-2
+
+
+@pytest.mark.parametrize("split", [(1, 2, 1), (0, 3, 0)])
+def test_looping_equals_unrolling(split):
+    """K loops of the shared Core equal one pass of a stack with the Core unrolled K times; also for
+    the pages' 1.7B-style split without Prelude and Coda (the Core loops over the whole stack)."""
     K = 3
     w = _tiny(k_max=K, tau_ent=-1.0, tau_halt=2.0)
+    w = replace(w, dims=replace(w.dims, n_pre=split[0], n_core=split[1], n_coda=split[2]))
     W = _rand_weights(w, seed=6)
     D = w.dims
     Du = replace(D, n_core=D.n_core * K)
@@ -442,6 +494,18 @@ def test_thresholds_are_monotone():
     assert first == sorted(first) and first[-1] > first[0]
     loops = [run.step(replace(base, tau_ent=0.05, tau_halt=q), W=W)[0]["loops"] for q in (0.1, 0.5, 0.7, 0.95)]
     assert loops == sorted(loops) and loops[-1] > loops[0]
+
+
+def test_layer_calls_without_prelude_and_coda():
+    """The pages' 1.7B split (no Prelude, no Coda, Core = all 28 layers): K loops make 28 K layer
+    calls, and the cache holds 28 K depth sets."""
+    dims = replace(synth.QWEN3_8B_DIMS, vocab=64, d_model=16, n_q_heads=2, n_kv_heads=1, head_dim=8, ffn=16,
+                   n_pre=0, n_core=28, n_coda=0)
+    w = replace(_tiny(), dims=dims, prefix=3, block=4, k_max=4, tau_ent=-1.0, tau_halt=2.0)
+    calls = []
+    res = run.step(w, counter=calls)
+    assert res[0]["loops"] == 4 and len(calls) == 4 * 28
+    assert dims.kv_slots(4) == 112 and len(run.cache_for(w, run.weights(w), 0)) == 112
 
 
 def test_first_loop_halt_mean_near_page_value():
@@ -861,3 +925,34 @@ def test_extend_on_evicted_cache():
     for slot in c:
         for x, y in zip(c[slot], d_[slot]):
             np.testing.assert_allclose(x, y, rtol=1e-11, atol=1e-12)
+
+
+def test_near_decision_flags_fire_exactly_inside_their_thresholds():
+    """The flags that exempt an outer-loop sequence from the exact free-run comparison: an entropy
+    within the threshold of tau_ent, a committed token whose top-2 gap is within it, a halting mean
+    within it of tau_halt, a forced commit whose entropy gap or token gap is within it -- and
+    nothing else."""
+    w = _tiny(tau_ent=0.5, tau_halt=0.6)
+    nan = float("nan")
+
+    def rec(H, gap, committed, mean_a, n_u=3):
+        return dict(loop=1, rows=np.arange(4), H=np.asarray(H, float), gap=np.asarray(gap, float),
+                    committed=np.asarray(committed, int), mean_a=mean_a, n_unresolved=n_u)
+
+    def res(r, forced=-1, forced_gap=nan):
+        return dict(records=[r], forced=forced, forced_gap=forced_gap)
+
+    far = rec([3.0, 4.0, 0.2, 5.0], [1.0, 1.0, 0.5, 1.0], [2], 0.3)
+    assert run.near_decisions(w, res(far)) == []
+    for H in (0.495, 0.505, 0.5):
+        assert any("entropy" in f for f in run.near_decisions(w, res(rec([3.0, 4.0, H, 5.0], [1, 1, 1, 1], [], 0.3))))
+    assert run.near_decisions(w, res(rec([3.0, 4.0, 0.48, 5.0], [1, 1, 1, 1], [2], 0.3))) == []
+    assert run.near_decisions(w, res(rec([3.0, 4.0, 0.2, 5.0], [1, 1, 0.005, 1], [2], 0.3))) == [
+        "token gap loop 1 row 2"]
+    assert run.near_decisions(w, res(rec([3.0, 4.0, 0.2, 5.0], [1, 0.005, 1, 1], [2], 0.3))) == []  # row 1 not committed
+    assert run.near_decisions(w, res(rec([3.0, 4.0, 0.2, 5.0], [1, 1, 1, 1], [2], 0.605))) == ["halt loop 1"]
+    assert run.near_decisions(w, res(rec([3.0, 4.0, 0.2, 5.0], [1, 1, 1, 1], [2], 0.605, n_u=0))) == []
+    assert run.near_decisions(w, res(rec([3.0, 4.0, 2.2, 5.0], [1, 1, 1, 1], [], 0.3), forced=2, forced_gap=0.004)) == [
+        "forced entropy gap"]
+    assert run.near_decisions(w, res(rec([3.0, 4.0, 2.2, 5.0], [1, 1, 0.001, 1], [], 0.3), forced=2, forced_gap=0.8)) \
+        == ["forced token gap"]
