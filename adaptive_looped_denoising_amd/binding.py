@@ -24,7 +24,7 @@ EXPORTS = ("alodlm_workspace_bytes", "alodlm_kv_slots", "alodlm_create", "alodlm
            "alodlm_readout_commit", "alodlm_readout_commit_static",
            "alodlm_last_step_stats", "alodlm_last_error", "alodlm_destroy", "alodlm_synth_fill",
            "alodlm_diag_gemm", "alodlm_diag_timing_enable", "alodlm_diag_timing_read", "alodlm_diag_read_kv", "alodlm_diag_buffer_offset",
-           "alodlm_diag_readout_sample")
+           "alodlm_diag_readout_sample", "alodlm_diag_gemm_choice")
 K_CLASSES = ("gemm_gate_up", "gemm_qkv", "gemm_o", "gemm_down", "attention", "lm_head", "norm_rope", "control")
 
 
@@ -33,7 +33,7 @@ class Config(ctypes.Structure):
         "vocab", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "n_pre", "n_core", "n_coda", "k_max",
         "max_batch", "max_prefix", "max_block", "max_prefill_rows", "mask_id", "dtype")] + \
         [("rms_eps", c_float), ("rope_theta", c_float), ("depth_on_demand", c_int32), ("kv_dtype", c_int32),
-         ("cache_depths", c_int32)]
+         ("cache_depths", c_int32), ("weight_row_pad", c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -112,6 +112,8 @@ def load(path: str = LIB_PATH):
     lib.alodlm_diag_readout_sample.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_uint64,
                                                c_uint32, c_uint32, c_void_p, c_void_p, c_size_t, c_int32, c_int32,
                                                c_void_p]
+    lib.alodlm_diag_gemm_choice.argtypes = [c_int32, c_int32, c_int32, c_int32, c_size_t, P(c_int32), P(c_int32),
+                                            c_char_p, c_size_t]
     lib.alodlm_diag_timing_enable.argtypes = [c_void_p, c_int32]
     lib.alodlm_diag_buffer_offset.argtypes = [c_void_p, ctypes.c_char_p]
     lib.alodlm_diag_buffer_offset.restype = c_int64
@@ -238,6 +240,16 @@ def diag_readout_sample(M: int, N: int, K: int, A_ptr: int, B_ptr: int, row_key_
                                            force_generic, force_tile, c_void_p(stream_ptr))
     if rc != 0:
         raise AlodlmError(rc, "alodlm_diag_readout_sample failed")
+
+
+def gemm_choice(epi: int, M: int, N: int, K: int, scratch_floats: int):
+    """(tile, split-K, kernel name) the matrix-core dispatcher takes for the shape."""
+    t, sp = c_int32(0), c_int32(0)
+    buf = ctypes.create_string_buffer(256)
+    rc = load().alodlm_diag_gemm_choice(epi, M, N, K, scratch_floats, ctypes.byref(t), ctypes.byref(sp), buf, 256)
+    if rc != 0:
+        raise AlodlmError(rc, "alodlm_diag_gemm_choice: shape not taken by the matrix cores")
+    return t.value, sp.value, buf.value.decode()
 
 
 def timing_enable(ctx: int, on: bool):

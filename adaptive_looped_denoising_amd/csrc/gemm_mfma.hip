@@ -19,6 +19,8 @@
 // tile for the LM-head readout, optionally with the Gumbel-max draw; logits never leave the
 // chip).  Split-K writes fp32 partials that k_splitk_reduce sums in a fixed order and finishes
 // with the same epilogue, or that the consuming kernel sums (deferred reduction).
+#include <stdio.h>
+
 #include <type_traits>
 
 #include "common.h"
@@ -1260,13 +1262,82 @@ int gemm_mfma_softstat_bn(int M) {
   return kTiles[gemm_mfma_auto_tile(EPI_SOFTSTAT, M, 1, 1, &sp)].bn;
 }
 
-// Chooses the tile and split-K, then launches.  For SWIGLU, N = 2F (interleaved gate/up columns)
-// and the output has F columns.  part/part_floats: split-K scratch.  force_tile / force_splits
-// (>= 0 / > 0) override the choice.
-int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
-                     const int32_t* m_dev, const GemmEpi& ep, int F, float* part, size_t part_floats,
-                     int force_splits, hipStream_t st, int force_tile, bool defer_reduce) {
-  if (M <= 0 || N <= 0) return 1;
+// Kernel and static template arguments of each tile (the names rocprofv3 reports are these with
+// the epilogue and split flag appended).
+struct TileName {
+  const char* kernel;
+  const char* args;
+};
+static const TileName kTileNames[kNumTiles] = {
+    {"k_gemm_mfma", "32, 128, 1, 4"},
+    {"k_gemm_mfma", "64, 128, 2, 2"},
+    {"k_gemm_mfma", "128, 128, 2, 2"},
+    {"k_gemm_mfma", "256, 64, 4, 1"},
+    {"k_gemm_mfma", "256, 128, 4, 1"},
+    {"k_gemm_mfma", "128, 64, 2, 2"},
+    {"k_gemm_mfma", "64, 64, 2, 2"},
+    {"k_gemm_mfma", "128, 256, 2, 2"},
+    {"k_gemm_pipe", "128, 128, 2, 2, 4"},
+    {"k_gemm_pipe", "64, 128, 2, 2, 4"},
+    {"k_gemm_pipe", "32, 128, 1, 4, 6"},
+    {"k_gemm_pipe", "256, 64, 4, 1, 3"},
+    {"k_gemm_pipe", "64, 64, 2, 2, 6"},
+    {"k_gemm_pipe", "128, 64, 2, 2, 4"},
+    {"k_gemm_pipe", "256, 128, 2, 2, 3"},
+    {"k_gemm_pipe", "128, 256, 2, 2, 3"},
+    {"k_gemm_pipe", "256, 96, 4, 1, 3"},
+    {"k_gemm_pipe", "256, 128, 4, 1, 3"},
+    {"k_gemm_pipe", "128, 96, 4, 1, 4"},
+    {"k_gemm_adirect", "64, 6"},
+    {"k_gemm_adirect", "96, 5"},
+    {"k_gemm_adirect", "128, 4"},
+    {"k_gemm_adirect", "96, 3"},
+    {"k_gemm_adirect", "96, 8"},
+    {"k_gemm_adirect", "96, 10"},
+    {"k_gemm_adirect", "128, 8"},
+    {"k_gemm_adirect", "64, 12"},
+    {"k_gemm_ring2", "256, 96, 4, 1, 2, 4"},
+    {"k_gemm_ring2", "256, 96, 4, 1, 1, 6"},
+    {"k_gemm_ring2", "128, 96, 4, 1, 2, 6"},
+    {"k_gemm_ring2", "128, 96, 4, 1, 2, 8"},
+    {"k_gemm_ring2", "128, 128, 2, 2, 2, 5"},
+    {"k_gemm_ring2", "128, 128, 2, 2, 1, 6"},
+    {"k_gemm_ring2", "32, 128, 1, 4, 2, 7"},
+    {"k_gemm_ring2", "64, 128, 2, 2, 2, 7"},
+    {"k_gemm_ring2", "256, 64, 4, 1, 2, 6"},
+    {"k_gemm_pipe", "128, 192, 2, 4, 3"},
+    {"k_gemm_pipe", "256, 128, 4, 2, 3"},
+    {"k_gemm_pipe", "128, 128, 2, 4, 4"},
+    {"k_gemm_pipe", "256, 64, 4, 2, 3"},
+    {"k_gemm_pipe", "64, 192, 2, 4, 4"},
+    {"k_gemm_pipe", "128, 192, 2, 4, 2"},
+    {"k_gemm_pipe", "128, 128, 2, 4, 2"},
+    {"k_gemm_pipe", "128, 128, 2, 4, 3"},
+    {"k_gemm_pipe", "128, 256, 2, 4, 3"},
+    {"k_gemm_pipe", "64, 128, 2, 4, 4"},
+    {"k_gemm_pipe", "64, 256, 2, 4, 3"},
+    {"k_gemm_pipe", "128, 192, 4, 2, 3"},
+    {"k_gemm_pipe", "128, 192, 4, 2, 2"},
+    {"k_gemm_ws", "128, 192, 4, 2, 2, 3"},
+    {"k_gemm_ws", "128, 192, 4, 2, 1, 4"},
+    {"k_gemm_ws", "128, 192, 4, 2, 2, 2"},
+    {"k_gemm_ws", "128, 128, 2, 4, 2, 4"},
+    {"k_gemm_ws", "128, 128, 2, 4, 2, 5"},
+    {"k_gemm_ws", "64, 128, 2, 4, 2, 6"},
+    {"k_gemm_ws", "256, 128, 4, 2, 2, 3"},
+    {"k_gemm_pipe", "128, 192, 4, 2, 4"},
+    {"k_gemm_pipe", "128, 128, 2, 4, 5"},
+    {"k_gemm_pipe", "128, 192, 2, 4, 4"},
+    {"k_gemm_wide", "256, 256, 4"},
+    {"k_gemm_wide", "256, 256, 5"},
+    {"k_gemm_wide", "256, 128, 6"},
+    {"k_gemm_wide", "128, 256, 6"},
+    {"k_gemm_wide", "256, 256, 3"},
+};
+
+// The tile and split-K the dispatcher takes for a shape (see launch_gemm_mfma).
+static void gemm_choose(int epi, int M, int N, int K, size_t part_floats, int force_splits, int force_tile,
+                        int* tile_out, int* splits_out) {
   int auto_splits = 0;
   int tile = (force_tile >= 0 && force_tile < kNumTiles) ? force_tile : gemm_mfma_auto_tile(epi, M, N, K,
                                                                                             &auto_splits);
@@ -1290,6 +1361,21 @@ int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, in
     if ((size_t)splits * M * N > part_floats || (K / GK) % splits != 0) splits = 1;
     if (epi == EPI_SWIGLU && splits == 1 && !swiglu_single_pass_ok(tile)) splits = 2;  // k_can_split holds here
   }
+  *tile_out = tile;
+  *splits_out = splits;
+}
+
+// Chooses the tile and split-K, then launches.  For SWIGLU, N = 2F (interleaved gate/up columns)
+// and the output has F columns.  part/part_floats: split-K scratch.  force_tile / force_splits
+// (>= 0 / > 0) override the choice.
+int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                     const int32_t* m_dev, const GemmEpi& ep, int F, float* part, size_t part_floats,
+                     int force_splits, hipStream_t st, int force_tile, bool defer_reduce) {
+  if (M <= 0 || N <= 0) return 1;
+  int tile, splits;
+  gemm_choose(epi, M, N, K, part_floats, force_splits, force_tile, &tile, &splits);
+  const int BM = kTiles[tile].bm, BN = kTiles[tile].bn;
+  const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
   const int k_split = K / splits;
   const int total = mt * nt * splits;
   const int per = (total + 7) / 8;
@@ -1453,6 +1539,22 @@ extern "C" int alodlm_diag_gemm(int32_t epi, int32_t M, int32_t N, int32_t K, co
                      force_splits, st, force_tile, false);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+extern "C" int alodlm_diag_gemm_choice(int32_t epi, int32_t M, int32_t N, int32_t K, size_t scratch_floats,
+                                       int32_t* tile, int32_t* splits, char* name, size_t name_len) {
+  using namespace alodlm;
+  if (M <= 0 || N <= 0 || K <= 0 || !gemm_mfma_supported(K, K, K) || epi < 0 || epi > 3) return -1;
+  int t, sp;
+  gemm_choose(epi, M, N, K, scratch_floats, 0, -1, &t, &sp);
+  if (tile) *tile = t;
+  if (splits) *splits = sp;
+  if (name && name_len) {
+    // the instantiation the dispatcher launches: split-K STORE / RESID run the plain store epilogue
+    const int e = sp > 1 ? (epi == EPI_SWIGLU ? EPI_SWIGLU : EPI_STORE) : epi;
+    snprintf(name, name_len, "%s<%s, %d, %s>", kTileNames[t].kernel, kTileNames[t].args, e, sp > 1 ? "true" : "false");
+  }
+  return 0;
 }
 
 extern "C" int alodlm_diag_readout_sample(int32_t M, int32_t N, int32_t K, const void* A, const void* B,

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
                                                  float eps, TO* __restrict__ out, const TG* __restrict__ exit_w,
                                                  float exit_b, float* __restrict__ lam,
                                                  const float* __restrict__ part, int splits_rt, int n_rows_part,
-                                                 float* __restrict__ x_out) {
+                                                 float* __restrict__ x_out, int out_ld) {
   __shared__ float red[4];
   const int r = blockIdx.x;
   if (n_dev && r >= *n_dev) return;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
   ss = block_sum<256>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
   float dot = 0.f;
-  TO* o = out + (size_t)r * d;
+  TO* o = out + (size_t)r * out_ld;
 #pragma unroll
   for (int i = 0; i < RMS_VEC; ++i) {
     const int e = (i * 256 + threadIdx.x) * 4;
@@ -631,12 +631,14 @@ void launch_embed_rows(int dtype, const int32_t* ids, int n_rows, const void* E,
 
 void launch_rmsnorm(int dtype, const float* x, int n_rows, int d, const int32_t* rows, const int32_t* n_dev,
                     const void* g, float eps, void* out, const void* exit_w, float exit_b, float* lam,
-                    hipStream_t st, const float* part, int splits, float* x_out) {
+                    hipStream_t st, const float* part, int splits, float* x_out, int out_ld) {
   if (n_rows <= 0) return;
+  if (out_ld <= 0) out_ld = d;
 #define RMS_GO(S)                                                                                              \
   DISPATCH_T(dtype, T,                                                                                         \
              k_rmsnorm<T, T, S><<<n_rows, 256, 0, st>>>(x, d, rows, n_dev, (const T*)g, eps, (T*)out,          \
-                                                         (const T*)exit_w, exit_b, lam, part, splits, n_rows, x_out))
+                                                         (const T*)exit_w, exit_b, lam, part, splits, n_rows, x_out, \
+                                                         out_ld))
   if (splits <= 1) {
     RMS_GO(1);
   } else if (splits == 2) {

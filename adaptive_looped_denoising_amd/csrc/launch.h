@@ -72,10 +72,11 @@ struct AttnParams {
 void launch_embed_rows(int dtype, const int32_t* ids, int n_rows, const void* E, int d, int V, float* out,
                        hipStream_t st);
 // x rows are x[src] (+ sum of `splits` deferred split-K partials part[s][r][:] when splits > 1,
-// written back to x_out[r]).
+// written back to x_out[r]).  Output row r at out + r * out_ld (0: d).
 void launch_rmsnorm(int dtype, const float* x, int n_rows, int d, const int32_t* rows, const int32_t* n_dev,
                     const void* g, float eps, void* out, const void* exit_w, float exit_b, float* lam,
-                    hipStream_t st, const float* part = nullptr, int splits = 1, float* x_out = nullptr);
+                    hipStream_t st, const float* part = nullptr, int splits = 1, float* x_out = nullptr,
+                    int out_ld = 0);
 void launch_exit_gate(int dtype, const void* rows, int n_rows, int d, const void* w, float b, float* lam,
                       hipStream_t st);
 // qkv rows come from `qkv`, or are the sum of `splits` deferred split-K partials [s][row][:] of

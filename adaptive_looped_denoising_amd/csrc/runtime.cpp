@@ -43,6 +43,7 @@ struct Plan {
   int scratch_slot = -1, alloc_slots = 0;
   int attn_splits = 0;
   int av_pitch = 1;  // row pitch of the available-depth table [B][av_pitch]
+  int xn_ld = 0;     // row pitch of the normalised projection inputs
   size_t gemm_part_elems = 0;
 };
 
@@ -85,6 +86,8 @@ int check_config(const alodlm_config* c, std::string* err) {
     return bad("depth_on_demand needs every depth kept (cache_depths 0 or k_max)");
   if (c->kv_dtype == ALODLM_KV_FP8 && (c->dtype != ALODLM_DTYPE_BF16 || (c->head_dim != 64 && c->head_dim != 128)))
     return bad("fp8 keys and values need the bf16 dtype and head_dim 64 or 128");
+  if (c->weight_row_pad < 0 || c->weight_row_pad > 1024 || c->weight_row_pad % 8)
+    return bad("weight_row_pad must be a multiple of 8 in 0..1024");
   return ALODLM_OK;
 }
 
@@ -123,7 +126,8 @@ Plan make_plan(const alodlm_config& c) {
   p.avail = take(B * p.av_pitch);
   p.h = take(sizeof(float) * R * d);
   p.h_alt = take(sizeof(float) * R * d);
-  p.xn = take(es * R * d);
+  p.xn_ld = (int)d + 64;  // padded row pitch: the projections stream 128-byte pieces of many rows
+  p.xn = take(es * R * p.xn_ld);
   p.attn = take(es * R * Hq * hd);
   p.qkv = take(sizeof(float) * R * qkv_out);
   p.q = take(es * R * Hq * hd);
@@ -356,6 +360,7 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   const Plan& p = c->plan;
   const int d = g.d_model, hd = g.head_dim, Hq = g.n_q_heads, Hkv = g.n_kv_heads, F = g.ffn;
   const int qkv_out = (Hq + 2 * Hkv) * hd;
+  const int wp = g.weight_row_pad;  // weight rows are in + wp elements apart
   const int n = lc.n_rows;
   const size_t es = esize(g.dtype);
   (void)es;
@@ -365,18 +370,20 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   void* q = c->at<void>(p.q);
   void* act = c->at<void>(p.act);
 
+  const int xp = p.xn_ld;
   c->tic(ALODLM_K_NORM_ROPE);
   if (lc.pend > 1)  // finish the previous layer's down projection: x_in += its partials, in place
     launch_rmsnorm(dt(c), lc.x_in, n, d, nullptr, nullptr, W.attn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st,
-                   c->at<float>(p.gemm_part), lc.pend, const_cast<float*>(lc.x_in));
+                   c->at<float>(p.gemm_part), lc.pend, const_cast<float*>(lc.x_in), xp);
   else
-    launch_rmsnorm(dt(c), lc.x_in, n, d, nullptr, nullptr, W.attn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st);
+    launch_rmsnorm(dt(c), lc.x_in, n, d, nullptr, nullptr, W.attn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st,
+                   nullptr, 1, nullptr, xp);
   c->toc();
   GemmEpi e1;
   e1.C = qkv;
   e1.ldc = qkv_out;
   c->tic(ALODLM_K_GEMM_QKV);
-  const int qkv_splits = gemm(c, EPI_STORE, xn, d, W.wqkv, d, n, qkv_out, d, nullptr, e1, 0, true, c->proj_splits[0],
+  const int qkv_splits = gemm(c, EPI_STORE, xn, xp, W.wqkv, d + wp, n, qkv_out, d, nullptr, e1, 0, true, c->proj_splits[0],
                              c->proj_tiles[0]);
   c->toc();
   const float* qkv_src = qkv_splits > 1 ? c->at<float>(p.gemm_part) : qkv;
@@ -484,7 +491,7 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   e2.ldc = d;
   c->tic(ALODLM_K_GEMM_O);
   const int o_splits =
-      gemm(c, EPI_RESID, attn, Hq * hd, W.wo, Hq * hd, n, d, Hq * hd, nullptr, e2, 0, true, c->proj_splits[1],
+      gemm(c, EPI_RESID, attn, Hq * hd, W.wo, Hq * hd + wp, n, d, Hq * hd, nullptr, e2, 0, true, c->proj_splits[1],
            c->proj_tiles[1]);
   c->toc();
 
@@ -492,23 +499,23 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
   c->tic(ALODLM_K_NORM_ROPE);
   if (o_splits > 1)
     launch_rmsnorm(dt(c), lc.x_in, n, d, nullptr, nullptr, W.ffn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr, c->st,
-                   c->at<float>(p.gemm_part), o_splits, lc.x_out);
+                   c->at<float>(p.gemm_part), o_splits, lc.x_out, xp);
   else
     launch_rmsnorm(dt(c), lc.x_out, n, d, nullptr, nullptr, W.ffn_norm, g.rms_eps, xn, nullptr, 0.f, nullptr,
-                   c->st);
+                   c->st, nullptr, 1, nullptr, xp);
   c->toc();
   GemmEpi e3;
   e3.act = act;
   e3.ld_act = F;
   c->tic(ALODLM_K_GEMM_GATE_UP);
-  gemm(c, EPI_SWIGLU, xn, d, W.w_gate_up, d, n, 2 * F, d, nullptr, e3, F, false, 0, c->proj_tiles[3]);
+  gemm(c, EPI_SWIGLU, xn, xp, W.w_gate_up, d + wp, n, 2 * F, d, nullptr, e3, F, false, 0, c->proj_tiles[3]);
   c->toc();
   GemmEpi e4;
   e4.C = lc.x_out;
   e4.R = lc.x_out;
   e4.ldc = d;
   c->tic(ALODLM_K_GEMM_DOWN);
-  const int down_splits = gemm(c, EPI_RESID, act, F, W.w_down, F, n, d, F, nullptr, e4, 0, lc.defer, c->proj_splits[2],
+  const int down_splits = gemm(c, EPI_RESID, act, F, W.w_down, F + wp, n, d, F, nullptr, e4, 0, lc.defer, c->proj_splits[2],
                                 c->proj_tiles[2]);
   c->toc();
   c->layer_calls += 1;
@@ -530,7 +537,7 @@ void readout_heads(alodlm_ctx* c, const void* rows, int n_upper, const int32_t* 
     ep.smp = *smp;
     ep.smp.part = c->at<GStat>(p.gpart);
   }
-  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_upper, g.vocab, g.d_model, n_dev, ep);
+  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model + g.weight_row_pad, n_upper, g.vocab, g.d_model, n_dev, ep);
   launch_softstat_combine(c->at<SoftStat>(p.part), n_upper, ep.n_tiles, n_dev, c->at<float>(p.H),
                           c->at<float>(p.lse), c->at<int32_t>(p.tok), smp ? ep.smp.part : nullptr,
                           smp ? c->at<int32_t>(p.stok) : nullptr, c->st);
@@ -1108,7 +1115,7 @@ int readout_run(alodlm_ctx* c, const ReadoutScratch& sc, const void* rows, int32
   ep.n_tiles = lm_tiles(c, n_rows);
   ep.btok = boost_tok;
   ep.bval = boost_val;
-  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model, n_rows, g.vocab, g.d_model, nullptr, ep);
+  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model + g.weight_row_pad, n_rows, g.vocab, g.d_model, nullptr, ep);
   launch_softstat_combine(sc.part, n_rows, ep.n_tiles, nullptr, entropy, lse, argmax, nullptr, nullptr, st);
   // one loop of the commit rule (a starts at 0, so a = lambda); per-row records go to the outputs
   launch_commit(B, 1, 1, L, B, tau_ent, tau_halt, sc.act1, sc.U, halt, sc.ro_map, entropy, argmax, nullptr, lam, lse,

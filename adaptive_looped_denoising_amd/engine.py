@@ -25,6 +25,13 @@ def _dev_tensor_from_storage(arr: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
 
 
+# linear weights the library reads with a row pitch of in + weight_row_pad elements
+PADDED = ("wqkv", "wo", "w_gate_up", "w_down", "lm_head")
+# Default pad of bf16 models: dense 4096-wide bf16 rows are 8 KB apart, which puts the same column
+# of every row a matrix tile streams on the same memory channels; this pad staggers them.
+DEFAULT_WEIGHT_ROW_PAD = 64
+
+
 def _ptr(t: Optional[torch.Tensor]) -> int:
     return 0 if t is None else t.data_ptr()
 
@@ -48,9 +55,12 @@ class StepResult:
 class Engine:
     def __init__(self, w: synth.Workload, device: str = "cuda", weight_source: Optional[str] = None,
                  max_prefill_rows: Optional[int] = None, overrides: Optional[Dict[str, np.ndarray]] = None,
-                 exit_b: Optional[float] = None, max_prefix: Optional[int] = None, depth_on_demand: bool = False):
+                 exit_b: Optional[float] = None, max_prefix: Optional[int] = None, depth_on_demand: bool = False,
+                 weight_row_pad: Optional[int] = None):
         """``max_prefix``: cache capacity per sequence (default the workload's prefix; larger to
-        append blocks).  ``depth_on_demand``: keep the prefix state for depth-by-depth builds."""
+        append blocks).  ``depth_on_demand``: keep the prefix state for depth-by-depth builds.
+        ``weight_row_pad``: elements after every row of the linear weights (default
+        DEFAULT_WEIGHT_ROW_PAD for bf16 models, 0 for fp32)."""
         self.lib = B.load()
         self.w = w
         self.device = torch.device(device)
@@ -62,6 +72,9 @@ class Engine:
         n_params = sum(int(np.prod(s["shape"])) for s in specs)
         if weight_source is None:
             weight_source = "host" if n_params < 50_000_000 else "device"
+        if weight_row_pad is None:
+            weight_row_pad = DEFAULT_WEIGHT_ROW_PAD if w.dtype == "bf16" else 0
+        self.weight_row_pad = weight_row_pad
         self.tensors: Dict[str, torch.Tensor] = {}
         for s in specs:
             name = s["name"]
@@ -77,6 +90,12 @@ class Engine:
                 else:
                     B.synth_fill(t.data_ptr(), self.cdtype, 0, t.numel(), w.seed, s["tensor"], float(s["scale"]),
                                  0.0, self.stream.cuda_stream)
+            if weight_row_pad and name.split(".")[-1] in PADDED:
+                # the library reads these [out][in] with a row pitch of in + weight_row_pad
+                p = torch.zeros((t.shape[0], t.shape[1] + weight_row_pad), dtype=t.dtype, device=self.device)
+                p[:, :t.shape[1]] = t
+                del t
+                t = p
             self.tensors[name] = t
         self.cfg = B.Config(
             vocab=D.vocab, d_model=D.d_model, n_q_heads=D.n_q_heads, n_kv_heads=D.n_kv_heads, head_dim=D.head_dim,
@@ -86,7 +105,7 @@ class Engine:
                 w.batch * max(w.prefix, max_prefix or 0), max(w.prefix, max_prefix or 0, 8192)),
             mask_id=w.mask_id, dtype=self.cdtype, rms_eps=w.rms_eps, rope_theta=w.rope_theta,
             depth_on_demand=1 if depth_on_demand else 0, kv_dtype=B.KV_FP8 if w.kv_dtype == "fp8" else B.KV_SAME,
-            cache_depths=w.cache_depths)
+            cache_depths=w.cache_depths, weight_row_pad=weight_row_pad)
         nl = D.n_layers
         self.layer_arr = (B.LayerWeights * max(nl, 1))()
         for l in range(nl):
@@ -257,11 +276,12 @@ class Engine:
     # ------------------------------------------------------------------ readout half of a loop
     def readout_commit(self, rows: torch.Tensor, group: int, tau_ent: float, tau_halt: float,
                        boost_tok: Optional[torch.Tensor] = None, boost_val: Optional[torch.Tensor] = None,
-                       static_scratch: bool = False) -> dict:
-        """``static_scratch``: the allocation-free entry point (scratch in the library's fixed array)."""
+                       static_scratch: bool = False, out: Optional[dict] = None) -> dict:
+        """``static_scratch``: the allocation-free entry point (scratch in the library's fixed array).
+        ``out``: the output tensors of an earlier call of the same size, reused."""
         n = rows.shape[0]
         dev = self.device
-        o = dict(entropy=torch.empty(n, dtype=torch.float32, device=dev),
+        o = out if out is not None else dict(entropy=torch.empty(n, dtype=torch.float32, device=dev),
                  lse=torch.empty(n, dtype=torch.float32, device=dev),
                  lam=torch.empty(n, dtype=torch.float32, device=dev),
                  halt=torch.empty(n, dtype=torch.float32, device=dev),

@@ -20,6 +20,7 @@ windows) and the explainer page's measured first-pass halting mean of 0.417.
 from __future__ import annotations
 
 import ctypes
+import json
 import math
 import os
 import subprocess
@@ -196,14 +197,46 @@ class Workload:
     def exit_bias(self) -> float:
         """ExitGate bias so that the mean first-loop halt probability is about halt_target.
 
-        A readout row r has unit RMS, so w_g . r spreads as N(0, s^2) with
-        s = weight_std * sqrt(d).  The bias solves E[sigmoid(b + s Z)] = target
-        with the probit approximation of the logistic-normal integral
-        (MacKay 1992): b = logit(target) * sqrt(1 + pi s^2 / 8).
+        The named workloads take the bias stored in exit_bias.json, solved on the realised loop-1
+        readout of their seeded inputs (mean over block rows of sigmoid(w_g . r + b) = 0.42) by the
+        oracle-only script oracle/calibrate_exit_bias.py; the table entry is used only for the
+        inputs it was solved on.  Any other workload (test variants) takes a closed form: a
+        readout row r has unit RMS, so w_g . r spreads as N(0, s^2) with s = weight_std * sqrt(d),
+        and the bias solves E[sigmoid(b + s Z)] = target with the probit approximation of the
+        logistic-normal integral (MacKay 1992): b = logit(target) * sqrt(1 + pi s^2 / 8).
         """
+        ent = _bias_table().get(self.name)
+        if ent is not None and ent.get("inputs") == bias_fingerprint(self) and self.halt_target == _BIAS_TARGET[0]:
+            return float(np.float32(ent["exit_b"]))
         s = self.weight_std * math.sqrt(self.dims.d_model)
         t = self.halt_target
         return float(np.float32(math.log(t / (1.0 - t)) * math.sqrt(1.0 + math.pi * s * s / 8.0)))
+
+
+_BIAS_PATH = os.path.join(_HERE, "exit_bias.json")
+_BIAS = None
+_BIAS_TARGET = [None]
+
+
+def _bias_table() -> dict:
+    global _BIAS
+    if _BIAS is None:
+        _BIAS = {}
+        if os.path.exists(_BIAS_PATH):
+            with open(_BIAS_PATH) as f:
+                data = json.load(f)
+            _BIAS = data.get("bias", {})
+            _BIAS_TARGET[0] = data.get("target")
+    return _BIAS
+
+
+def bias_fingerprint(w: "Workload") -> dict:
+    """The inputs a stored ExitGate bias was solved on (everything the loop-1 readout depends on)."""
+    return dict(dims=[w.dims.vocab, w.dims.d_model, w.dims.n_q_heads, w.dims.n_kv_heads, w.dims.head_dim,
+                      w.dims.ffn, w.dims.n_pre, w.dims.n_core, w.dims.n_coda],
+                dtype=w.dtype, seed=w.seed, batch=w.batch, prefix=w.prefix, block=w.block, kv=w.kv,
+                short_frac=w.short_frac, short_depth=w.short_depth, kv_dtype=w.kv_dtype,
+                weight_std=w.weight_std, rms_eps=w.rms_eps, rope_theta=w.rope_theta)
 
 
 QWEN3_8B_DIMS = Dims(vocab=151936, d_model=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=12288,

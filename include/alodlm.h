@@ -98,10 +98,16 @@ typedef struct alodlm_config {
                            depth_on_demand only 0 or k_max.  The prefill still runs all k_max
                            Core passes (the Coda set is built on the depth-k_max output), the
                            deeper ones in one extra scratch plane. */
+  int32_t weight_row_pad; /* elements after every row of the linear weights (wqkv, wo, w_gate_up,
+                           w_down, lm_head): each is stored [out][in + weight_row_pad], the pad
+                           unread.  0 = dense rows; a multiple of 8 in 0..1024.  With dense
+                           4096-wide bf16 rows (8 KB apart) the same column of every row a
+                           matrix tile streams falls on the same memory channels; a pad staggers
+                           them (measured on the step's projections and LM head). */
 } alodlm_config;
 
 /* One transformer layer (Qwen3 block).  Device pointers in the config dtype,
- * linear maps stored [out][in]. */
+ * linear maps stored [out][in] with a row pitch of in + cfg.weight_row_pad elements. */
 typedef struct alodlm_layer_weights {
   const void* attn_norm;  /* [d] RMSNorm gain before attention */
   const void* wqkv;       /* [(Hq + 2 Hkv) hd][d]: q rows, then k rows, then v rows */
@@ -115,7 +121,7 @@ typedef struct alodlm_layer_weights {
 
 typedef struct alodlm_weights {
   const void* embed;       /* [V][d] token embedding (also the Eq. 3 feedback rows) */
-  const void* lm_head;     /* [V][d] LMHead, logits z = lm_head . r */
+  const void* lm_head;     /* [V][d] LMHead (row pitch d + cfg.weight_row_pad), logits z = lm_head . r */
   const void* final_norm;  /* [d] RMSNorm gain producing the readout state r */
   const void* exit_w;      /* [d] ExitGate weight: lambda = sigmoid(exit_w . r + exit_b) */
   float exit_b;            /* ExitGate bias */

@@ -37,6 +37,15 @@ __attribute__((visibility("default"))) int alodlm_diag_gemm(int32_t epi, int32_t
                                                             int32_t force_splits, int32_t force_generic,
                                                             int32_t force_tile, void* hip_stream);
 
+/* The matrix-core dispatcher's choice for a GEMM of M x N x K with epilogue epi (ALODLM_DIAG_*),
+ * given scratch_floats of split-K scratch (the step has max_batch * max_block * max(2F, qkv) * 8):
+ * tile index, split-K factor and the kernel instantiation's name as rocprofv3 reports it
+ * (NUL-terminated, truncated to name_len).  Host only.  Returns 0, or -1 for a shape the matrix
+ * cores do not take. */
+__attribute__((visibility("default"))) int alodlm_diag_gemm_choice(int32_t epi, int32_t M, int32_t N, int32_t K,
+                                                                   size_t scratch_floats, int32_t* tile,
+                                                                   int32_t* splits, char* name, size_t name_len);
+
 /* Gumbel-max draws of the logits z = A.B^T (bf16 A [M][K], B [N][K]) through the step's LM-head
  * kernel: tok[m] = argmax_n (z[m][n] + g), g the Gumbel noise of ALODLM_STEP_SAMPLE in alodlm.h
  * with counter (n div 4, row_key[m], c2, c3) and key (seed mod 2^32, seed div 2^32).  row_key:
@@ -60,7 +69,7 @@ __attribute__((visibility("default"))) int alodlm_diag_read_kv(const struct alod
                                                                int32_t j0, int32_t n, void* dst_k, void* dst_v);
 
 /* Byte offset, within the workspace, of an internal activation buffer, for inspection after a
- * call: "h" (fp32 residual rows), "xn" (normalised rows), "attn" (attention output), "q",
+ * call: "h" (fp32 residual rows), "xn" (normalised rows, row pitch d + 64), "attn" (attention output), "q",
  * "qkv" (fp32 projection), "act" (SwiGLU output), "r" (readout rows).  -1 if unknown. */
 __attribute__((visibility("default"))) int64_t alodlm_diag_buffer_offset(const struct alodlm_ctx* ctx,
                                                                          const char* name);

@@ -236,3 +236,14 @@ def test_static_readout_validates_and_bounds_its_scratch():
         assert b"scratch" in lib.alodlm_last_error(cx)
     finally:
         lib.alodlm_destroy(ctypes.c_void_p(ctx))
+
+
+@pytest.mark.parametrize("pad,ok", [(0, True), (64, True), (1024, True), (4, False), (-8, False), (1032, False)])
+def test_weight_row_pad_range(pad, ok):
+    """weight_row_pad: a multiple of 8 (16-byte aligned rows for the matrix-core loads) in 0..1024."""
+    if ok:
+        assert B.workspace_bytes(_cfg(weight_row_pad=pad)) > 0
+    else:
+        with pytest.raises(B.AlodlmError) as e:
+            B.workspace_bytes(_cfg(weight_row_pad=pad))
+        assert e.value.code == B.EINVAL

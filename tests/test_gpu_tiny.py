@@ -297,3 +297,18 @@ def test_mid_bf16_step_is_deterministic(gpu_lib):
     for k in ("tokens", "commit_loop", "loops", "entropy", "lam", "halt", "lse", "argmax", "hidden"):
         x, y = getattr(a, k), getattr(b, k)
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), k
+
+
+def test_padded_and_dense_weight_rows_give_the_same_bits(gpu_lib):
+    """The linear weights read with a padded row pitch (cfg.weight_row_pad, the engine's default for
+    bf16) and densely: the same kernels and sums, so the same step bit for bit; the dense run is
+    also checked against the oracle."""
+    w = _mid(batch=2, prefix=130)
+    from adaptive_looped_denoising_amd.engine import DEFAULT_WEIGHT_ROW_PAD
+    assert DEFAULT_WEIGHT_ROW_PAD > 0
+    a = _engine(w).step(records=True, hidden=True)
+    ed = _engine(w, weight_row_pad=0)
+    b = ed.step(records=True, hidden=True)
+    for k in ("tokens", "commit_loop", "loops", "entropy", "lam", "halt", "lse", "argmax", "hidden"):
+        assert np.array_equal(getattr(a, k).view(np.uint8), getattr(b, k).view(np.uint8)), k
+    check_step(w, ed, name="mid dense weight rows")
