@@ -18,8 +18,8 @@
 // 16-key S product are a permutation of the tile's keys chosen so that the 8 probabilities a
 // lane feeds one P.V product are 8 consecutive keys: each V^T fragment is then one 16-byte
 // chunk of a row.
-// With several key splits, partial (O, max, sum) go to a scratch buffer and the last block of
-// each (pair, query block) to finish combines them in a fixed order, in the same launch.
+// With several key splits, partial (O, max, sum) go to a scratch buffer and k_attn_merge
+// combines them in a fixed order.
 // F8: keys and values are stored in FP8 E4M3 (half the bytes).  The fp8 tiles stream into the
 // LDS ring unswizzled; once a stage has landed, the workgroup converts it (exactly: every E4M3
 // value is a bf16 value) into one bf16 working tile in the layout above, and the matrix-core
@@ -437,32 +437,17 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
       }
     }
   }
-  if (n_splits > 1) {
-    // The block of this (pair, query block) that finishes last merges every split's partials, in
-    // split order (so the result does not depend on which block that is): each block publishes its
-    // partials (device-scope fence) before it is counted, and the last one fences again before it
-    // reads them.  It resets the counter for the next launch.  The flag lives in the operand LDS,
-    // whose last reads every wave has passed at the barrier.
-    __threadfence();
-    __syncthreads();
-    int* flag = (int*)smem;
-    int* cnt = p.split_cnt + (size_t)pair * n_qblocks + qb;
-    if (tid == 0) flag[0] = atomicAdd(cnt, 1) == n_splits - 1;
-    __syncthreads();
-    if (!flag[0]) return;
-    __threadfence();
-    const int r_end = min(QB, rows_q - qb * QB);
-    for (int r = wid; r < r_end; r += NW) attn_merge_row<HD>(p, pair, qb * QB + r, n_splits, lane);
-    if (tid == 0) *cnt = 0;
-  }
 }
 
-// Combine the key splits of one (pair, query row rho) in a fixed order (split 0, 1, ...): one
-// wave, lane e holding output elements e and e + 64.
+// Combine the key splits of each (pair, query row) in a fixed order.
 template <int HD>
-__device__ __forceinline__ void attn_merge_row(const AttnParams& p, int pair, int rho, int n_splits, int lane) {
+__global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int n_pairs, int n_splits) {
   const int G = p.Hq / p.Hkv;
   const int rows_q = G * p.rows_per_seq;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= n_pairs * rows_q) return;
+  const int pair = w / rows_q, rho = w % rows_q;
   const int t = pair / p.Hkv, kvh = pair % p.Hkv;
   const int i = rho / G, g = rho % G;
   const float* part = p.part + ((size_t)pair * rows_q + rho) * n_splits * (HD + 2);
@@ -512,7 +497,7 @@ __device__ __forceinline__ void attn_merge_row(const AttnParams& p, int pair, in
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   bf16_t* out = (bf16_t*)p.out + (size_t)(t * p.rows_per_seq + i) * p.Hq * HD + (size_t)(kvh * G + g) * HD;
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
+  for (int u = 0; u < (HD + 63) / 64; ++u) {
     const int e = lane + 64 * u;
     if (e < HD) out[e] = from_f<bf16_t>(acc[u] * inv);
   }
@@ -528,13 +513,17 @@ static void run_attn(const AttnParams& p, int n_pairs, int n_qblocks, int n_spli
     k_attn_mfma<HD, QW, 4, NW, F8><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   else
     k_attn_mfma<HD, QW, 3, NW, F8><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+  if (n_splits > 1) {
+    const int rows_q = (p.Hq / p.Hkv) * p.rows_per_seq;
+    const int waves = n_pairs * rows_q;
+    k_attn_merge<HD><<<(waves + 3) / 4, 256, 0, st>>>(p, n_pairs, n_splits);
+  }
 }
 
 bool attn_mfma_supported(int hd) { return hd == 32 || hd == 64 || hd == 128; }
 
 // p.n_rows / rows_per_seq = sequence slots; p.part must hold n_pairs * rows_q * max_splits * (hd + 2)
-// floats when max_splits > 1, and p.split_cnt n_pairs * rows_q zeroed counters (the merging block
-// leaves each at zero).  Key rows must be 16-byte aligned and V^T rows (c_vRow, s_vRow
+// floats when max_splits > 1.  Key rows must be 16-byte aligned and V^T rows (c_vRow, s_vRow
 // elements) multiples of 64 elements; n_cache >= 1 or n_self >= 1.
 void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int force_splits, int force_qw,
                       int force_ns, int force_nw) {
@@ -557,7 +546,7 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
   const int QB = NW * QW;
   const int n_qblocks = (rows_q + QB - 1) / QB;
   int splits = 1;
-  if (!p.causal && p.part && p.split_cnt) {
+  if (!p.causal && p.part) {
     // long: enough splits for about one block per compute unit; else about two blocks per
     // compute unit and at least two splits, at least 2 key tiles per split
     const int blocks = n_pairs * n_qblocks;

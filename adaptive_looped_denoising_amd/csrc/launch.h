@@ -62,10 +62,8 @@ struct AttnParams {
   // causal_off own keys that are already in place)
   int n_self = 0, causal = 0, s_seq0 = 0, causal_off = 0;
   int kv8 = 0;  // keys and values (cache and own) stored in FP8 E4M3 (matrix-core path, hd 64 / 128)
-  // fast path scratch: split-KV partials, and one counter per (pair, query block), zero between
-  // launches, through which the last block to finish finds out that it merges
+  // fast path scratch: split-KV partials
   float* part = nullptr;
-  int* split_cnt = nullptr;
   int n_split = 1;
 };
 

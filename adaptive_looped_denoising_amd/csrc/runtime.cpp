@@ -29,7 +29,7 @@ struct Plan {
   size_t h, h_alt, xn, attn, qkv, q, kself, vself, gu, act;
   size_t r, lam, H, lse, tok, btok, bval, part, gpart, rkey, stok;
   size_t U, a, ro_map, ro_rows, ncommit, stop, seq_loops, act_seq0, act_seq1, src_slot, cnt;
-  size_t attn_part, attn_cnt, gemm_part;
+  size_t attn_part, gemm_part;
   size_t blk_ids, blk_tok, blk_cl, blk_loops, blk_cnt;  // outer loop over a block
   size_t pstate;  // depth-on-demand: the prefix's Core output [B][P][d] fp32 (0 bytes without it)
   // sizes
@@ -158,7 +158,6 @@ Plan make_plan(const alodlm_config& c) {
   p.src_slot = take(sizeof(int32_t) * B);
   p.cnt = take(sizeof(int32_t) * 8);
   p.attn_part = take(sizeof(float) * Rs * Hq * (size_t)p.attn_splits * (hd + 2));
-  p.attn_cnt = take(sizeof(int32_t) * Rs * Hq);  // >= (sequence, kv head) pairs x query blocks
   p.gemm_part_elems = (size_t)Rs * (size_t)(2 * F > qkv_out ? 2 * F : qkv_out) * 8;
   p.gemm_part = take(sizeof(float) * p.gemm_part_elems);
   p.blk_ids = take(sizeof(int32_t) * Rs);
@@ -322,7 +321,6 @@ void attention(alodlm_ctx* c, const AttnParams& p) {
     AttnParams q = p;
     q.kv8 = kv8 ? 1 : 0;
     q.part = c->at<float>(c->plan.attn_part);
-    q.split_cnt = c->at<int>(c->plan.attn_cnt);
     launch_attn_mfma(q, c->plan.attn_splits, c->st, c->attn_force_splits, c->attn_force_qw, c->attn_force_ns,
                      c->attn_force_nw);
     return;
@@ -660,9 +658,6 @@ int ensure_device(alodlm_ctx* c) {
   if (e1 == hipSuccess)
     e1 = hipMemsetAsync(c->ws + plan.vself, 0, es * (size_t)cfg->max_batch * cfg->n_kv_heads * cfg->head_dim * plan.Lp,
                         c->st);
-  // the attention split counters start at zero (each launch leaves them at zero)
-  if (e1 == hipSuccess)
-    e1 = hipMemsetAsync(c->ws + plan.attn_cnt, 0, sizeof(int32_t) * (size_t)plan.rows_step * cfg->n_q_heads, c->st);
   hipError_t e3 = hipStreamSynchronize(c->st);
   if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess)
     return c->fail(ALODLM_EHIP, std::string("context set-up (RoPE tables, V padding): ") +
