@@ -1257,8 +1257,9 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   return 38;
 }
 
-int gemm_mfma_softstat_bn(int M) {
+int gemm_mfma_softstat_bn(int M, int force_tile) {
   int sp;
+  if (force_tile >= 0 && force_tile < kNumTiles) return kTiles[force_tile].bn;
   return kTiles[gemm_mfma_auto_tile(EPI_SOFTSTAT, M, 1, 1, &sp)].bn;
 }
 

@@ -124,7 +124,7 @@ void launch_embed_committed(int dtype, const int8_t* cl, const int32_t* tokens, 
 bool gemm_mfma_supported(int K, int lda, int ldb);
 // Column-tile width the matrix-core dispatcher uses for a SOFTSTAT (LM-head) GEMM of M rows:
 // the softmax statistics are kept per column tile.
-int gemm_mfma_softstat_bn(int M);
+int gemm_mfma_softstat_bn(int M, int force_tile = -1);
 // Returns the number of split-K partials left unreduced in `part` ([splits][M][N] fp32, plain
 // A.B^T sums) when defer_reduce is set and the GEMM was split (STORE / RESID only), else 1 (the
 // epilogue has been applied).

@@ -196,6 +196,7 @@ struct alodlm_ctx {
   int attn_force_nw = 0;       // diagnostics: ALODLM_ATTN_NW=4|8 fixes the waves per workgroup
   int proj_splits[3] = {0, 0, 0};  // diagnostics: ALODLM_PROJ_SPLITS=q,o,d fixes the QKV / O / down split-K
   int proj_tiles[4] = {-1, -1, -1, -1};  // diagnostics: ALODLM_PROJ_TILES=q,o,d,gu fixes their GEMM tiles
+  int lm_tile = -1;            // diagnostics: ALODLM_LM_TILE=t fixes the LM-head readout's GEMM tile
   // diagnostics: per-class kernel timing with event pairs on the context stream
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;
@@ -311,7 +312,7 @@ int gemm(alodlm_ctx* c, int epi, const void* A, int lda, const void* B, int ldb,
 // Column tiles of the LM-head softmax statistics for the path a readout of M rows takes.
 int lm_tiles(const alodlm_ctx* c, int M) {
   const int d = c->cfg.d_model;
-  const int bn = use_mfma(c, d, d, d) ? gemm_mfma_softstat_bn(M) : 64;
+  const int bn = use_mfma(c, d, d, d) ? gemm_mfma_softstat_bn(M, c->lm_tile) : 64;
   return (c->cfg.vocab + bn - 1) / bn;
 }
 
@@ -535,7 +536,8 @@ void readout_heads(alodlm_ctx* c, const void* rows, int n_upper, const int32_t* 
     ep.smp = *smp;
     ep.smp.part = c->at<GStat>(p.gpart);
   }
-  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model + g.weight_row_pad, n_upper, g.vocab, g.d_model, n_dev, ep);
+  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model + g.weight_row_pad, n_upper, g.vocab, g.d_model, n_dev, ep,
+       0, false, 0, c->lm_tile);
   launch_softstat_combine(c->at<SoftStat>(p.part), n_upper, ep.n_tiles, n_dev, c->at<float>(p.H),
                           c->at<float>(p.lse), c->at<int32_t>(p.tok), smp ? ep.smp.part : nullptr,
                           smp ? c->at<int32_t>(p.stok) : nullptr, c->st);
@@ -628,6 +630,7 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
     sscanf(v, "%d,%d,%d", &c->proj_splits[0], &c->proj_splits[1], &c->proj_splits[2]);
   if (const char* v = getenv("ALODLM_PROJ_TILES"))
     sscanf(v, "%d,%d,%d,%d", &c->proj_tiles[0], &c->proj_tiles[1], &c->proj_tiles[2], &c->proj_tiles[3]);
+  if (const char* v = getenv("ALODLM_LM_TILE")) c->lm_tile = atoi(v);
   *out = c;
   return ALODLM_OK;
 }
@@ -1110,7 +1113,8 @@ int readout_run(alodlm_ctx* c, const ReadoutScratch& sc, const void* rows, int32
   ep.n_tiles = lm_tiles(c, n_rows);
   ep.btok = boost_tok;
   ep.bval = boost_val;
-  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model + g.weight_row_pad, n_rows, g.vocab, g.d_model, nullptr, ep);
+  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model + g.weight_row_pad, n_rows, g.vocab, g.d_model, nullptr,
+       ep, 0, false, 0, c->lm_tile);
   launch_softstat_combine(sc.part, n_rows, ep.n_tiles, nullptr, entropy, lse, argmax, nullptr, nullptr, st);
   // one loop of the commit rule (a starts at 0, so a = lambda); per-row records go to the outputs
   launch_commit(B, 1, 1, L, B, tau_ent, tau_halt, sc.act1, sc.U, halt, sc.ro_map, entropy, argmax, nullptr, lam, lse,

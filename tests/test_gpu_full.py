@@ -175,7 +175,8 @@ def test_qwen3_8b_step_with_entropy_commits(gpu_lib):
     w = synth.workload("qwen3_8b", kv="synthetic", boost_lo=10.0, boost_hi=20.0, tau_ent=0.9)
     e, ores, _, dec = _check(w, [2, 6], name="qwen3_8b entropy commits")
     assert sum(int((r["commit_loop"] > 0).sum()) for r in ores) > 0
-    assert sum(d["compared"] for d in dec.values()) > 0
+    # at least one sequence with entropy commits had its whole commit schedule compared free-running
+    assert any(dec[r["seq"]]["diverged"] is None and (r["commit_loop"] > 0).any() for r in ores)
     e.close()
 
 
