@@ -20,6 +20,12 @@
 // chunk of a row.
 // With several key splits, partial (O, max, sum) go to a scratch buffer and k_attn_merge
 // combines them in a fixed order.
+// KH = 2 (key halves): two waves share each 16-row query sub-block, one taking keys 0..31 and
+// the other keys 32..63 of every tile (S subtiles 0-1 / 2-3, which are exactly the keys of P.V
+// products 0 / 1), each with its own online softmax; at the end the second wave hands (max, sum,
+// O) to the first through LDS.  Four waves then cover 32 query rows and stream every key tile of
+// the pair, so the four 32-row blocks of a 128-row pair need no key split and no merge launch:
+// they run side by side on one XCD and read each K/V tile from its L2.
 // F8: keys and values are stored in FP8 E4M3 (half the bytes).  The fp8 tiles stream into the
 // LDS ring unswizzled; once a stage has landed, the workgroup converts it (exactly: every E4M3
 // value is a bf16 value) into one bf16 working tile in the layout above, and the matrix-core
@@ -79,10 +85,13 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4 in, uint4& lo, uint4&
 }
 
 // NW waves per workgroup (4, or 8 for HD >= 64: two waves per SIMD sharing one K/V stream).
-template <int HD, int QW, int NS, int NW, bool F8>
+template <int HD, int QW, int NS, int NW, bool F8, int KH>
 __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs, int n_qblocks, int n_splits,
                                                        int tiles_per_split) {
-  constexpr int QB = NW * QW;
+  static_assert(KH == 1 || (KH == 2 && !F8), "key halves: bf16 K/V only");
+  constexpr int QB = NW / KH * QW;
+  constexpr int KS = 4 / KH;             // 16-key S subtiles of a tile per wave
+  constexpr int C2 = 2 / KH;             // 32-key P.V products of a tile per wave
   constexpr int NQ = QW / 16;
   constexpr int NH = HD / 16;
   constexpr int NC = HD / 32;
@@ -116,6 +125,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
   const int rows_q = G * p.rows_per_seq;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
+  const int wq = wid / KH, kh = wid % KH;  // query sub-block, key half
 
   // tile range of this block: prefix tiles 0 .. TP-1, then own-key tiles TP .. TP+TS-1
   const int TP = (p.n_cache + AKT - 1) / AKT;
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
   bool qok[NQ];
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
-    const int rho = qb * QB + wid * QW + nq * 16 + col;
+    const int rho = qb * QB + wq * QW + nq * 16 + col;
     qok[nq] = rho < rows_q;
     const int i = qok[nq] ? rho / G : 0, g = qok[nq] ? rho % G : 0;
     qpos[nq] = i;
@@ -275,19 +285,20 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
     // fragments are read one chunk ahead of its MFMAs, into the other register set, and retired by
     // an explicit LDS-counter wait (the compiler's own waits treat the direct-to-LDS loads as
     // unordered with these reads and would also wait for the reads just issued).
-    floatx4 s[4][NQ];
+    // (subtile j of this wave is S subtile kh * KS + j of the tile)
+    floatx4 s[KS][NQ];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int nq = 0; nq < NQ; ++nq) s[ks][nq] = (floatx4){0.f, 0.f, 0.f, 0.f};
-    auto read_k = [&](int c, bf16x8_t (&f)[4]) {
+    auto read_k = [&](int c, bf16x8_t (&f)[KS]) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int r = s_key(ks, col);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int r = s_key(kh * KS + ks, col);
         f[ks] = *(const bf16x8_t*)&sK[r * HD + (((c * 4 + quad) ^ kswz<HD>(r)) << 3)];
       }
     };
-    bf16x8_t kf[2][4];
+    bf16x8_t kf[2][KS];
     read_k(0, kf[0]);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -296,7 +307,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
       if (c + 1 < NC) read_k(c + 1, kf[(c + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq)
           s[ks][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c & 1][ks], qf[nq][c], s[ks][nq], 0, 0, 0);
@@ -304,16 +315,17 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
     }
     // the first V^T fragments are read while the softmax runs
     constexpr int HG = NH >= 2 ? 2 : 1;  // hd row blocks per V^T read group
-    auto read_v = [&](int g, bf16x8_t (&f)[HG][2]) {
+    auto read_v = [&](int g, bf16x8_t (&f)[HG][C2]) {
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) {
         const int r = (g * HG + hh) * 16 + col;
         const int sw = (r >> 1) & 7;
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) f[hh][c2] = *(const bf16x8_t*)&sV[r * AKT + (((c2 * 4 + quad) ^ sw) << 3)];
+        for (int c2 = 0; c2 < C2; ++c2)
+          f[hh][c2] = *(const bf16x8_t*)&sV[r * AKT + ((((kh * C2 + c2) * 4 + quad) ^ sw) << 3)];
       }
     };
-    bf16x8_t vf[2][HG][2];
+    bf16x8_t vf[2][HG][C2];
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
     read_v(0, vf[0]);
@@ -324,23 +336,23 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
     // last tile, or own keys under a causal mask); rows past the block (qok false) need none:
     // their query is zero, and their column is never written.
     const bool full = k0 + AKT <= klen && !(p.causal && !pre);
-    bf16x8_t pb[2][NQ];
+    bf16x8_t pb[C2][NQ];
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
       // raw scores; masked ones become -inf (exp2 of -inf is 0)
       float mx = -INFINITY;
       if (full) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
           for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[ks][nq][v]);
       } else {
         const int lim = (p.causal && !pre) ? qpos[nq] + p.causal_off : klen;  // last visible own key
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int kk = k0 + s_key(ks, quad * 4 + v);  // key within its segment
+            const int kk = k0 + s_key(kh * KS + ks, quad * 4 + v);  // key within its segment
             const bool ok = (kk < klen) & (kk <= lim);
             const float sc = ok ? s[ks][nq][v] : -INFINITY;
             s[ks][nq][v] = sc;
@@ -364,9 +376,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
       }
       const float mref = mrun[nq] == -INFINITY ? 0.f : mrun[nq];  // masked scores give exp2(-inf) = 0
       float sum = 0.f;
-      float pv[4][4];
+      float pv[KS][4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float e = __builtin_amdgcn_exp2f(fmaf(s[ks][nq][v], scale2, -mref));
@@ -375,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
         }
       lrun[nq] += sum;
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
+      for (int c2 = 0; c2 < C2; ++c2) {
         uint4 w;
         w.x = pack_bf16x2(pv[2 * c2][0], pv[2 * c2][1]);
         w.y = pack_bf16x2(pv[2 * c2][2], pv[2 * c2][3]);
@@ -396,7 +408,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh)
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < C2; ++c2)
 #pragma unroll
           for (int nq = 0; nq < NQ; ++nq)
             o[g * HG + hh][nq] =
@@ -411,11 +423,45 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnParams p, int n_pairs
     lrun[nq] += __shfl_xor(lrun[nq], 16, 64);
     lrun[nq] += __shfl_xor(lrun[nq], 32, 64);
   }
+  if constexpr (KH == 2) {
+    // Combine the two key halves of each query sub-block: wave kh = 1 leaves its (max, sum, O)
+    // in LDS, wave kh = 0 rescales both to the common max and adds.  The ring is free once every
+    // wave has passed the barrier (no loads are in flight after the last tile).
+    constexpr int PER = NH * NQ * 4 + 2 * NQ;  // floats per lane
+    float* xch = (float*)smem + (size_t)wq * PER * 64 + lane;
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int nq = 0; nq < NQ; ++nq) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) xch[((nq * NH + h) * 4 + v) * 64] = o[h][nq][v];
+        xch[(NH * NQ * 4 + 2 * nq) * 64] = mrun[nq];
+        xch[(NH * NQ * 4 + 2 * nq + 1) * 64] = lrun[nq];
+      }
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) {
+      const float m1 = xch[(NH * NQ * 4 + 2 * nq) * 64], l1 = xch[(NH * NQ * 4 + 2 * nq + 1) * 64];
+      const float M = fmaxf(mrun[nq], m1);
+      const float f0 = mrun[nq] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[nq] - M);
+      const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+      lrun[nq] = f0 * lrun[nq] + f1 * l1;
+      mrun[nq] = M;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[h][nq][v] = f0 * o[h][nq][v] + f1 * xch[((nq * NH + h) * 4 + v) * 64];
+    }
+  }
   // write: lane holds query column col of subtile nq, hd rows h*16 + 4*quad + v
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
     if (!qok[nq]) continue;
-    const int rho = qb * QB + wid * QW + nq * 16 + col;
+    const int rho = qb * QB + wq * QW + nq * 16 + col;
     const int i = rho / G, g = rho % G;
     if (n_splits == 1) {
       const float inv = lrun[nq] > 0.f ? 1.0f / lrun[nq] : 0.f;
@@ -503,16 +549,16 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int n_pairs, i
   }
 }
 
-template <int HD, int QW, int NW, bool F8>
+template <int HD, int QW, int NW, bool F8, int KH = 1>
 static void run_attn(const AttnParams& p, int n_pairs, int n_qblocks, int n_splits, int tps, int ns, hipStream_t st) {
   const int total = n_pairs * n_qblocks * n_splits;
   const int grid = ((total + 7) / 8) * 8;
   if (ns == 2)
-    k_attn_mfma<HD, QW, 2, NW, F8><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+    k_attn_mfma<HD, QW, 2, NW, F8, KH><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   else if (ns == 4)
-    k_attn_mfma<HD, QW, 4, NW, F8><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+    k_attn_mfma<HD, QW, 4, NW, F8, KH><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   else
-    k_attn_mfma<HD, QW, 3, NW, F8><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
+    k_attn_mfma<HD, QW, 3, NW, F8, KH><<<grid, NW * 64, 0, st>>>(p, n_pairs, n_qblocks, n_splits, tps);
   if (n_splits > 1) {
     const int rows_q = (p.Hq / p.Hkv) * p.rows_per_seq;
     const int waves = n_pairs * rows_q;
@@ -526,7 +572,7 @@ bool attn_mfma_supported(int hd) { return hd == 32 || hd == 64 || hd == 128; }
 // floats when max_splits > 1.  Key rows must be 16-byte aligned and V^T rows (c_vRow, s_vRow
 // elements) multiples of 64 elements; n_cache >= 1 or n_self >= 1.
 void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int force_splits, int force_qw,
-                      int force_ns, int force_nw) {
+                      int force_ns, int force_nw, int force_kh) {
   if (p.n_rows <= 0) return;
   const int n_seq = p.n_rows / p.rows_per_seq;
   const int n_pairs = n_seq * p.Hkv;
@@ -541,16 +587,25 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
   const bool long_kv = p.hd >= (p.kv8 ? 128 : 64) && rows_q >= 256 && n_tiles >= 64;
   // >= 128 query rows per pair: eight 16-row waves share each K/V stream (8B step: 2.12 -> 1.94 ms)
   const bool wide_q = p.hd >= (p.kv8 ? 128 : 64) && rows_q >= 128;
-  const int QW = (force_qw == 16 || force_qw == 32) ? force_qw : (long_kv && !p.kv8 ? 32 : 16);
-  const int NW = ((force_nw == 8 || (force_nw == 0 && (long_kv || wide_q))) && p.hd >= (p.kv8 ? 128 : 64)) ? 8 : 4;
-  const int QB = NW * QW;
+  // Key halves (four waves over 32 query rows, every key tile of the pair in one block, no key
+  // split or merge launch once the blocks fill the chip) on request only: at the 8B step they
+  // measured 1.77 ms of attention per step against 1.52 ms for the eight-wave blocks with key
+  // splits -- with one wave per SIMD the score products' accumulation chains stay exposed.
+  const bool kh2 = force_kh == 2 && !p.kv8 && (p.hd == 128 || p.hd == 64);
+  const int QW = kh2 ? 16 : (force_qw == 16 || force_qw == 32) ? force_qw : (long_kv && !p.kv8 ? 32 : 16);
+  const int NW = kh2 ? 4
+                     : ((force_nw == 8 || (force_nw == 0 && (long_kv || wide_q))) && p.hd >= (p.kv8 ? 128 : 64)) ? 8
+                                                                                                                   : 4;
+  const int QB = (kh2 ? NW / 2 : NW) * QW;
   const int n_qblocks = (rows_q + QB - 1) / QB;
   int splits = 1;
   if (!p.causal && p.part) {
     // long: enough splits for about one block per compute unit; else about two blocks per
-    // compute unit and at least two splits, at least 2 key tiles per split
+    // compute unit and at least two splits, at least 2 key tiles per split; key halves: no
+    // split once the blocks cover three quarters of the compute units
     const int blocks = n_pairs * n_qblocks;
-    const int want = long_kv ? max(1, (256 + blocks - 1) / blocks)
+    const int want = kh2 ? (blocks >= 192 ? 1 : (256 + blocks - 1) / blocks)
+                   : long_kv ? max(1, (256 + blocks - 1) / blocks)
                              : (NW == 8 ? max(2, (256 + blocks - 1) / blocks) : max(2, (512 + blocks - 1) / blocks));
     splits = min(min(want, max(1, n_tiles / 2)), max_splits);
     if (force_splits > 0) splits = min(force_splits, max_splits);
@@ -559,7 +614,12 @@ void launch_attn_mfma(const AttnParams& p, int max_splits, hipStream_t st, int f
   const int tps = (n_tiles + splits - 1) / splits;
   splits = (n_tiles + tps - 1) / tps;
   if (splits < 1) splits = 1;
-  const int ns = (force_ns >= 2 && force_ns <= 4) ? force_ns : 2;
+  const int ns = (force_ns >= 2 && force_ns <= 4) ? force_ns : (kh2 ? 4 : 2);
+  if (kh2) {
+    if (p.hd == 128) run_attn<128, 16, 4, false, 2>(p, n_pairs, n_qblocks, splits, tps, ns, st);
+    else run_attn<64, 16, 4, false, 2>(p, n_pairs, n_qblocks, splits, tps, ns, st);
+    return;
+  }
 #define GO(H, Q, W) run_attn<H, Q, W, false>(p, n_pairs, n_qblocks, splits, tps, ns, st)
 #define GO8(H, Q, W) run_attn<H, Q, W, true>(p, n_pairs, n_qblocks, splits, tps, ns, st)
   if (p.kv8) {  // fp8 keys and values (head sizes 64 and 128)

@@ -194,6 +194,7 @@ struct alodlm_ctx {
   int attn_force_qw = 0;       // diagnostics: ALODLM_ATTN_QW=16|32 fixes the query rows per wave
   int attn_force_ns = 0;       // diagnostics: ALODLM_ATTN_NS=2..4 fixes the LDS ring depth
   int attn_force_nw = 0;       // diagnostics: ALODLM_ATTN_NW=4|8 fixes the waves per workgroup
+  int attn_force_kh = 0;       // diagnostics: ALODLM_ATTN_KH=1|2 fixes the key halves per tile
   int proj_splits[3] = {0, 0, 0};  // diagnostics: ALODLM_PROJ_SPLITS=q,o,d fixes the QKV / O / down split-K
   int proj_tiles[4] = {-1, -1, -1, -1};  // diagnostics: ALODLM_PROJ_TILES=q,o,d,gu fixes their GEMM tiles
   int lm_tile = -1;            // diagnostics: ALODLM_LM_TILE=t fixes the LM-head readout's GEMM tile
@@ -323,7 +324,7 @@ void attention(alodlm_ctx* c, const AttnParams& p) {
     q.kv8 = kv8 ? 1 : 0;
     q.part = c->at<float>(c->plan.attn_part);
     launch_attn_mfma(q, c->plan.attn_splits, c->st, c->attn_force_splits, c->attn_force_qw, c->attn_force_ns,
-                     c->attn_force_nw);
+                     c->attn_force_nw, c->attn_force_kh);
     return;
   }
   launch_attn_generic(dt(c), p, c->st);
@@ -626,6 +627,7 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
   if (const char* v = getenv("ALODLM_ATTN_QW")) c->attn_force_qw = atoi(v);
   if (const char* v = getenv("ALODLM_ATTN_NS")) c->attn_force_ns = atoi(v);
   if (const char* v = getenv("ALODLM_ATTN_NW")) c->attn_force_nw = atoi(v);
+  if (const char* v = getenv("ALODLM_ATTN_KH")) c->attn_force_kh = atoi(v);
   if (const char* v = getenv("ALODLM_PROJ_SPLITS"))
     sscanf(v, "%d,%d,%d", &c->proj_splits[0], &c->proj_splits[1], &c->proj_splits[2]);
   if (const char* v = getenv("ALODLM_PROJ_TILES"))

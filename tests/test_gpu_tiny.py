@@ -312,3 +312,16 @@ def test_padded_and_dense_weight_rows_give_the_same_bits(gpu_lib):
     for k in ("tokens", "commit_loop", "loops", "entropy", "lam", "halt", "lse", "argmax", "hidden"):
         assert np.array_equal(getattr(a, k).view(np.uint8), getattr(b, k).view(np.uint8)), k
     check_step(w, ed, name="mid dense weight rows")
+
+
+@pytest.mark.parametrize("env", [{"ALODLM_ATTN_KH": "1"}, {"ALODLM_ATTN_KH": "2", "ALODLM_ATTN_SPLITS": "1"},
+                                 {"ALODLM_ATTN_KH": "2", "ALODLM_ATTN_NS": "2"}],
+                         ids=["eight_wave_key_splits", "key_halves_unsplit", "key_halves_two_stage"])
+def test_mid_bf16_attention_launch_layouts(gpu_lib, env, monkeypatch):
+    """The step attention's launch layouts on the mid shape (hd 128, 128 query rows per kv head,
+    ragged prefix): eight-wave blocks with key splits merged by a second launch; key halves (two
+    waves per query sub-block combined in LDS) with every key tile in one block; key halves with a
+    two-stage ring and key splits.  Each against the oracle."""
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    _check_step(_mid(batch=2, prefix=300), gpu_lib, name="mid attention %s" % ",".join("%s=%s" % kv for kv in env.items()))
