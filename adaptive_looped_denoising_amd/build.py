@@ -45,6 +45,44 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+ASAN_LIB = os.path.join(HERE, "libalodlm_asan.so")
+# host-side AddressSanitizer for the C ABI and the host runtime (argument checks, workspace planning,
+# tile choice): only the host half of runtime.cpp is instrumented (-Xarch_host), device code is not
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """The compiler's shared AddressSanitizer runtime (preloaded by the process that loads the library)."""
+    base = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(base)) if os.path.isdir(base) else []:
+        p = os.path.join(base, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    return ""
+
+
+def build_asan(verbose: bool = False) -> str:
+    """libalodlm_asan.so: runtime.cpp with host AddressSanitizer, the kernels' objects as built by build()."""
+    objs = [os.path.join(OBJDIR, s + ".o") for s in SOURCES if s != "runtime.cpp"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError("build() first: missing %s" % ", ".join(missing))
+    obj = os.path.join(OBJDIR, "runtime.asan.o")
+    cmd = [HIPCC] + FLAGS + ASAN_FLAGS + ["-c", os.path.join(CSRC, "runtime.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on runtime.cpp (asan):\n%s\n%s" % (r.stdout, r.stderr))
+    tmp = ASAN_LIB + ".tmp%d" % os.getpid()
+    r = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, obj] + objs,
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("asan link failed:\n%s\n%s" % (r.stdout, r.stderr))
+    os.replace(tmp, ASAN_LIB)
+    if verbose:
+        print("built", ASAN_LIB)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

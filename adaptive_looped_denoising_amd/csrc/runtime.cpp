@@ -248,9 +248,25 @@ struct alodlm_ctx {
     return code;
   }
   int hip_check(const char* what) {
+    if (!debug_first.empty()) {
+      const std::string m = "debug sync: " + debug_first;
+      debug_first.clear();
+      return fail(ALODLM_EHIP, m);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(ALODLM_EHIP, std::string(what) + ": " + hipGetErrorString(e));
     return ALODLM_OK;
+  }
+  // diagnostics: ALODLM_DEBUG_SYNC=1 synchronises the stream after every layer call and every
+  // readout / commit group and checks for a HIP error there, so that a failing launch is named
+  // by its group; the first failure is kept and returned by the entry point's next error check.
+  bool debug_sync = false;
+  std::string debug_first;
+  void dbg_point(const char* what, int index) {
+    if (!debug_sync || !debug_first.empty()) return;
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) debug_first = std::string(what) + " " + std::to_string(index) + ": " + hipGetErrorString(e);
   }
 };
 
@@ -519,6 +535,7 @@ int run_layer(alodlm_ctx* c, int li, const LayerCall& lc) {
                                 c->proj_tiles[2]);
   c->toc();
   c->layer_calls += 1;
+  c->dbg_point("layer", li);
   return down_splits;
 }
 
@@ -628,6 +645,7 @@ int alodlm_create(const alodlm_config* cfg, const alodlm_weights* w, void* works
   if (const char* v = getenv("ALODLM_ATTN_NS")) c->attn_force_ns = atoi(v);
   if (const char* v = getenv("ALODLM_ATTN_NW")) c->attn_force_nw = atoi(v);
   if (const char* v = getenv("ALODLM_ATTN_KH")) c->attn_force_kh = atoi(v);
+  if (const char* v = getenv("ALODLM_DEBUG_SYNC")) c->debug_sync = v[0] == '1';
   if (const char* v = getenv("ALODLM_PROJ_SPLITS"))
     sscanf(v, "%d,%d,%d", &c->proj_splits[0], &c->proj_splits[1], &c->proj_splits[2]);
   if (const char* v = getenv("ALODLM_PROJ_TILES"))
@@ -977,6 +995,7 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
     c->tic(ALODLM_K_LM_HEAD);
     readout_heads(c, c->at<void>(p.r), n_read, cnt + 1, bt, bv, smp ? &sp : nullptr);
     c->toc();
+    c->dbg_point("readout of loop", s);
     c->tic(ALODLM_K_CONTROL);
     launch_commit(nb, s, K, L, B, a->tau_ent, a->tau_halt, act[cur], U, av, ro_map, c->at<float>(p.H),
                   c->at<int32_t>(p.tok), smp ? c->at<int32_t>(p.stok) : nullptr, c->at<float>(p.lam),
@@ -986,6 +1005,7 @@ int alodlm_denoise_step(alodlm_ctx* c, const alodlm_step_args* a, alodlm_step_ou
     launch_build_lists(nb, L, B, 0, act[cur], stop, U, ncommit, act[cur ^ 1], src_slot, ro_rows, ro_map, cnt, st);
     launch_reset_compact(dt(c), nb, cnt, L, d, g.vocab, act[cur ^ 1], src_slot, U, o->tokens, h, c->w.embed, h_alt, st);
     c->toc();
+    c->dbg_point("commit and compaction of loop", s);
     float* t = h;
     h = h_alt;
     h_alt = t;
@@ -1118,11 +1138,13 @@ int readout_run(alodlm_ctx* c, const ReadoutScratch& sc, const void* rows, int32
   gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model + g.weight_row_pad, n_rows, g.vocab, g.d_model, nullptr,
        ep, 0, false, 0, c->lm_tile);
   launch_softstat_combine(sc.part, n_rows, ep.n_tiles, nullptr, entropy, lse, argmax, nullptr, nullptr, st);
+  c->dbg_point("readout of rows", n_rows);
   // one loop of the commit rule (a starts at 0, so a = lambda); per-row records go to the outputs
   launch_commit(B, 1, 1, L, B, tau_ent, tau_halt, sc.act1, sc.U, halt, sc.ro_map, entropy, argmax, nullptr, lam, lse,
                 tokens, commit_loop, sc.ncommit, sc.stop, sc.seq_loops, nullptr, nullptr, nullptr, nullptr, nullptr,
                 nullptr, nullptr, nullptr, nullptr, st);
   launch_embed_committed(dt(c), commit_loop, tokens, c->w.embed, n_rows, g.d_model, g.vocab, embed_out, st);
+  c->dbg_point("commit of rows", n_rows);
   return c->hip_check("readout launch");
 }
 

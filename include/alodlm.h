@@ -34,6 +34,12 @@
  *     any device work is enqueued, so an EINVAL call has no device effect.
  *   - All device work runs on the stream given to alodlm_create().  A context
  *     is not thread-safe; use one context per stream.
+ *   - Debugging: with ALODLM_DEBUG_SYNC=1 in the environment when the context
+ *     is created, the library synchronises its stream after every layer call
+ *     and every readout / commit group and checks for a HIP error there; the
+ *     first failure is returned (ALODLM_EHIP) by the entry point that ran it,
+ *     and alodlm_last_error() names the group ("layer 12: ...", "readout of
+ *     loop 2: ...").  Off by default (the step then synchronises once per loop).
  */
 #ifndef ALODLM_H
 #define ALODLM_H

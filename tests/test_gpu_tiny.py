@@ -325,3 +325,14 @@ def test_mid_bf16_attention_launch_layouts(gpu_lib, env, monkeypatch):
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     _check_step(_mid(batch=2, prefix=300), gpu_lib, name="mid attention %s" % ",".join("%s=%s" % kv for kv in env.items()))
+
+
+def test_debug_sync_flag_gives_the_same_step(gpu_lib, monkeypatch):
+    """ALODLM_DEBUG_SYNC=1 (stream synchronisation and a HIP error check after every layer call and
+    every readout / commit group) runs the same kernels: the same step bit for bit, and no error."""
+    w = _mid(batch=2, prefix=130)
+    a = _engine(w).step(records=True, hidden=True)
+    monkeypatch.setenv("ALODLM_DEBUG_SYNC", "1")
+    b = _engine(w).step(records=True, hidden=True)
+    for k in ("tokens", "commit_loop", "loops", "entropy", "lam", "halt", "lse", "argmax", "hidden"):
+        assert np.array_equal(getattr(a, k).view(np.uint8), getattr(b, k).view(np.uint8)), k
