@@ -1228,6 +1228,12 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
       *splits = 1;
       return 10;
     }
+    // a long reduction into few outputs (1.7B FFN down: 6144 -> 2048 at 32 rows): 64 x 64 tiles
+    // with split-K 8, 256 workgroups streaming the weight instead of 64 (15.7 -> 10.5 us)
+    if (K > 4096 && N <= 2048) {
+      *splits = 8;
+      return 12;
+    }
     *splits = 4;
     return N <= 4096 && K <= 4096 ? 12 : 10;
   }

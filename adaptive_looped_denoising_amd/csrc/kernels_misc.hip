@@ -645,6 +645,8 @@ void launch_rmsnorm(int dtype, const float* x, int n_rows, int d, const int32_t*
     RMS_GO(2);
   } else if (splits == 4) {
     RMS_GO(4);
+  } else if (splits == 8) {
+    RMS_GO(8);
   } else {
     RMS_GO(0);
   }

@@ -12,7 +12,7 @@ from tests.parity import log
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(32, 4096, 2048), (256, 6144, 4096), (200, 1024, 512), (1, 128, 64), (77, 640, 384), (2048, 1024, 4096),
-          (130, 4096, 12288)]
+          (130, 4096, 12288), (32, 2048, 6144)]
 
 
 def _bf16(shape, seed, scale=1.0):
