@@ -666,14 +666,16 @@ def readout_commit_group(r, W_lm, embed, exit_w, exit_b: float, tau_ent: float, 
     lam = exit_gate(r, exit_w, exit_b)
     a = lam.copy()                           # a = 0 + (1 - 0) * lambda
     commit = H <= tau_ent
+    # the stop test of the loop (Algorithm 1 (4)) averages a over the rows the entropy commits left
+    # unresolved; forced progress (5) comes after it
+    unresolved = ~commit
+    mean_a = float(a[unresolved].mean()) if unresolved.any() else float("nan")
     commit_loop = np.where(commit, 1, 0).astype(np.int64)
     forced = -1
     if not commit.any() and n:
         forced = int(np.argmin(H))
         commit_loop[forced] = -1
     committed = commit_loop != 0
-    unresolved = ~committed
-    mean_a = float(a[unresolved].mean()) if unresolved.any() else float("nan")
     emb = np.zeros((n, embed.shape[1]), dtype=F64)
     emb[committed] = _f64(embed[tok[committed]])
     return dict(H=H, tok=tok, lse=lse, gap=gap, lam=lam, a=a, commit_loop=commit_loop, forced=forced,

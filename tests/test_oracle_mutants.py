@@ -22,6 +22,13 @@ def _mutant(name, old, new):
 
 # (oracle function, text replaced, mistaken text, pins that must notice)
 MUTANTS = {
+    "group_mean_a_over_every_row": (
+        "readout_commit_group", "a[unresolved].mean()", "a.mean()", [pins.test_readout_group_halt_state]),
+    "group_mean_a_after_forced_progress": (
+        "readout_commit_group", "unresolved = ~commit", "unresolved = ~commit & (H > H.min())",
+        [pins.test_readout_group_halt_state]),
+    "group_halt_not_from_zero": (
+        "readout_commit_group", "a = lam.copy()", "a = 0.5 * lam", [pins.test_readout_group_halt_state]),
     "rope_turns_the_other_way": (
         "rope", "x1 * c - x2 * s, x2 * c + x1 * s", "x1 * c + x2 * s, x2 * c - x1 * s",
         [pins.test_rope_identity_norm_and_relative_position, pins.test_all_commit_reduces_to_one_fixed_depth_pass]),

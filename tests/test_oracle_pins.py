@@ -529,6 +529,39 @@ def test_readout_group_reduces_to_step_rule():
     assert out["forced"] == int(np.argmin(out["H"])) and (out["commit_loop"] != 0).sum() == 1
 
 
+def test_readout_group_halt_state():
+    """The readout group's halting state after its one loop (summary page, Algorithm 1 (4)): the
+    ExitGate logit of row i is set to logit(p_i) (w_g a unit vector, the row's first entry
+    ln(p/(1-p)), b_g 0), so lambda_i = p_i exactly; from a = 0, a_i = lambda_i; mean_a is the mean
+    of a over the rows the entropy commits left unresolved only, i.e. of the p_i of the rows that
+    did not commit."""
+    rng = np.random.default_rng(21)
+    V, d = 40, 6
+    Wl = rng.standard_normal((V, d))
+    E = rng.standard_normal((V, d))
+    p = np.array([0.2, 0.4, 0.6, 0.8, 0.9])
+    r = rng.standard_normal((5, d))
+    r[:, 0] = np.log(p / (1 - p))
+    wg = np.zeros(d)
+    wg[0] = 1.0
+    H = orc.readout_commit_group(r, Wl, E, wg, 0.0, tau_ent=-1.0, tau_halt=0.5)["H"]
+    order = np.argsort(H)
+    tau = 0.5 * (H[order[1]] + H[order[2]])     # exactly the two rows of lowest entropy commit
+    out = orc.readout_commit_group(r, Wl, E, wg, 0.0, tau_ent=tau, tau_halt=0.5)
+    np.testing.assert_allclose(out["lam"], p, rtol=1e-12)
+    np.testing.assert_allclose(out["a"], p, rtol=1e-12)
+    left = np.setdiff1d(np.arange(5), order[:2])
+    assert sorted(np.nonzero(out["commit_loop"] == 1)[0]) == sorted(order[:2]) and out["forced"] == -1
+    np.testing.assert_allclose(out["mean_a"], p[left].mean(), rtol=1e-12)
+    # nothing commits by entropy: the stop test (4) precedes forced progress (5), so every row is
+    # still in the mean
+    out = orc.readout_commit_group(r, Wl, E, wg, 0.0, tau_ent=-1.0, tau_halt=0.5)
+    assert out["forced"] == order[0]
+    np.testing.assert_allclose(out["mean_a"], p.mean(), rtol=1e-12)
+    # every row commits: no unresolved row, no mean
+    assert np.isnan(orc.readout_commit_group(r, Wl, E, wg, 0.0, tau_ent=1e9, tau_halt=0.5)["mean_a"])
+
+
 def test_bf16_rounding_matches_library_conversion():
     import torch
     rng = np.random.default_rng(9)
