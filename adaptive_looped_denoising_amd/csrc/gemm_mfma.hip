@@ -120,10 +120,10 @@ __device__ __forceinline__ void gemm_epilogue(floatx4 (&acc)[BM / WM / 16][BN / 
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
           const int n = cbase + b * 16;
-          z[b] = n < N ? acc[a][b][v] + (n == bt ? bv : 0.f) : -INFINITY;
+          z[b] = n < N ? acc[a][b][v] + (n + ep.col0 == bt ? bv : 0.f) : -INFINITY;
           if (z[b] > mx) {
             mx = z[b];
-            ix = n;
+            ix = n + ep.col0;
           }
         }
         SoftStat s = softstat_empty();
@@ -168,7 +168,7 @@ __device__ __forceinline__ void gemm_epilogue(floatx4 (&acc)[BM / WM / 16][BN / 
         }
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
-          uint32_t c0 = (uint32_t)((n0 + wn * TN * 16 + b * 16 + (lane & 12)) >> 2), c1 = rk, c2 = ep.smp.c2,
+          uint32_t c0 = (uint32_t)((ep.col0 + n0 + wn * TN * 16 + b * 16 + (lane & 12)) >> 2), c1 = rk, c2 = ep.smp.c2,
                    c3 = ep.smp.c3;
           philox4x32_10(c0, c1, c2, c3, ep.smp.k0, ep.smp.k1);
           float g[4];
@@ -188,10 +188,10 @@ __device__ __forceinline__ void gemm_epilogue(floatx4 (&acc)[BM / WM / 16][BN / 
           const int n = cbase + b * 16;  // ascending over b, so ties keep the lowest column
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float y = acc[a][b][v] + (n == btv[v] ? bvv[v] : 0.f) + g[v];
+            const float y = acc[a][b][v] + (n + ep.col0 == btv[v] ? bvv[v] : 0.f) + g[v];
             const bool tk = n < N && y > gg[v];
             gg[v] = tk ? y : gg[v];
-            gi[v] = tk ? n : gi[v];
+            gi[v] = tk ? n + ep.col0 : gi[v];
           }
         }
 #pragma unroll
@@ -1263,10 +1263,31 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   return 38;
 }
 
-int gemm_mfma_softstat_bn(int M, int force_tile) {
-  int sp;
-  if (force_tile >= 0 && force_tile < kNumTiles) return kTiles[force_tile].bn;
-  return kTiles[gemm_mfma_auto_tile(EPI_SOFTSTAT, M, 1, 1, &sp)].bn;
+// The LM-head readout's column ranges.  With one row tile of the wide 256 x 256 tile the
+// ceil(N / 256) column tiles run in rounds of one per compute unit; at N = 151936 that is 594
+// tiles, 2.3 rounds, the last one a third full.  When that last round would be at most half full
+// the columns of the whole rounds stay on the wide tile and the rest run as a second launch on
+// the 128 x 192 eight-wave tile, which spreads them over more workgroups (256 rows: 512 wide tiles
+// 320 us + the 20864-column rest 67 us, against 437-473 us in one launch, in a probe).
+void gemm_mfma_softstat_plan(int M, int N, int force_tile, SoftstatPlan* sp) {
+  int s;
+  const int tile = (force_tile >= 0 && force_tile < kNumTiles) ? force_tile : gemm_mfma_auto_tile(EPI_SOFTSTAT, M, N, 1, &s);
+  const int bn = kTiles[tile].bn;
+  sp->tile0 = tile;
+  sp->cols0 = N;
+  sp->tile1 = -1;
+  sp->tiles0 = (N + bn - 1) / bn;
+  sp->n_tiles = sp->tiles0;
+  constexpr int kCUs = 256, kRest = 47;
+  if (force_tile < 0 && kTiles[tile].bm >= M && kTiles[tile].bm == 256 && bn == 256) {
+    const int whole = sp->tiles0 / kCUs * kCUs;
+    if (whole > 0 && sp->tiles0 - whole > 0 && sp->tiles0 - whole <= kCUs / 2) {
+      sp->cols0 = whole * bn;
+      sp->tiles0 = whole;
+      sp->tile1 = kRest;
+      sp->n_tiles = whole + (N - sp->cols0 + kTiles[kRest].bn - 1) / kTiles[kRest].bn;
+    }
+  }
 }
 
 // Kernel and static template arguments of each tile (the names rocprofv3 reports are these with
@@ -1556,6 +1577,20 @@ extern "C" int alodlm_diag_gemm_choice(int32_t epi, int32_t M, int32_t N, int32_
   gemm_choose(epi, M, N, K, scratch_floats, 0, -1, &t, &sp);
   if (tile) *tile = t;
   if (splits) *splits = sp;
+  if (epi == EPI_SOFTSTAT) {  // the readout's column ranges (one or two launches)
+    SoftstatPlan rp;
+    gemm_mfma_softstat_plan(M, N, -1, &rp);
+    if (tile) *tile = rp.tile0;
+    if (name && name_len) {
+      if (rp.tile1 < 0)
+        snprintf(name, name_len, "%s<%s, %d, false>", kTileNames[rp.tile0].kernel, kTileNames[rp.tile0].args, epi);
+      else
+        snprintf(name, name_len, "%s<%s, %d, false> (columns 0..%d) + %s<%s, %d, false> (columns %d..%d)",
+                 kTileNames[rp.tile0].kernel, kTileNames[rp.tile0].args, epi, rp.cols0 - 1,
+                 kTileNames[rp.tile1].kernel, kTileNames[rp.tile1].args, epi, rp.cols0, N - 1);
+    }
+    return 0;
+  }
   if (name && name_len) {
     // the instantiation the dispatcher launches: split-K STORE / RESID run the plain store epilogue
     const int e = sp > 1 ? (epi == EPI_SWIGLU ? EPI_SWIGLU : EPI_STORE) : epi;

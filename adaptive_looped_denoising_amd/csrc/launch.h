@@ -34,6 +34,7 @@ struct GemmEpi {
   void* act = nullptr;
   int ld_act = 0;
   SampleParams smp;  // SOFTSTAT with smp.part: also the Gumbel-max draw of each row and tile
+  int col0 = 0;      // SOFTSTAT over a column range: vocabulary id of the launch's column 0
 };
 
 // Attention operands.  Query rows r = t * rows_per_seq + i of sequence slot t (cache sequence
@@ -124,7 +125,13 @@ void launch_embed_committed(int dtype, const int8_t* cl, const int32_t* tokens, 
 bool gemm_mfma_supported(int K, int lda, int ldb);
 // Column-tile width the matrix-core dispatcher uses for a SOFTSTAT (LM-head) GEMM of M rows:
 // the softmax statistics are kept per column tile.
-int gemm_mfma_softstat_bn(int M, int force_tile = -1);
+// Column ranges of an M-row LM-head readout over N columns on the matrix cores: columns
+// [0, cols0) on tile0 (tiles0 column tiles), then, if tile1 >= 0, columns [cols0, N) on tile1;
+// n_tiles = the per-row partial statistics of both (column-tile order).
+struct SoftstatPlan {
+  int tile0, cols0, tiles0, tile1, n_tiles;
+};
+void gemm_mfma_softstat_plan(int M, int N, int force_tile, SoftstatPlan* plan);
 // Returns the number of split-K partials left unreduced in `part` ([splits][M][N] fp32, plain
 // A.B^T sums) when defer_reduce is set and the GEMM was split (STORE / RESID only), else 1 (the
 // epilogue has been applied).

@@ -329,8 +329,33 @@ int gemm(alodlm_ctx* c, int epi, const void* A, int lda, const void* B, int ldb,
 // Column tiles of the LM-head softmax statistics for the path a readout of M rows takes.
 int lm_tiles(const alodlm_ctx* c, int M) {
   const int d = c->cfg.d_model;
-  const int bn = use_mfma(c, d, d, d) ? gemm_mfma_softstat_bn(M, c->lm_tile) : 64;
-  return (c->cfg.vocab + bn - 1) / bn;
+  if (!use_mfma(c, d, d, d + c->cfg.weight_row_pad)) return (c->cfg.vocab + 63) / 64;
+  SoftstatPlan sp;
+  gemm_mfma_softstat_plan(M, c->cfg.vocab, c->lm_tile, &sp);
+  return sp.n_tiles;
+}
+
+// The LM-head GEMM with the readout-statistics epilogue over the whole vocabulary for M rows
+// (rows >= *n_dev skipped): one launch, or on the matrix cores two column ranges
+// (gemm_mfma_softstat_plan) whose partials sit side by side in each row's ep.n_tiles entries.
+void lm_head_gemm(alodlm_ctx* c, const void* rows, int M, const int32_t* n_dev, const GemmEpi& ep) {
+  const alodlm_config& g = c->cfg;
+  const int d = g.d_model, ldw = d + g.weight_row_pad;
+  if (!use_mfma(c, d, d, ldw)) {
+    gemm(c, EPI_SOFTSTAT, rows, d, c->w.lm_head, ldw, M, g.vocab, d, n_dev, ep, 0, false, 0, c->lm_tile);
+    return;
+  }
+  SoftstatPlan sp;
+  gemm_mfma_softstat_plan(M, g.vocab, c->lm_tile, &sp);
+  gemm(c, EPI_SOFTSTAT, rows, d, c->w.lm_head, ldw, M, sp.cols0, d, n_dev, ep, 0, false, 0, sp.tile0);
+  if (sp.tile1 >= 0) {
+    GemmEpi e2 = ep;
+    e2.part = ep.part + sp.tiles0;
+    if (ep.smp.part) e2.smp.part = ep.smp.part + sp.tiles0;
+    e2.col0 = sp.cols0;
+    const void* w1 = (const char*)c->w.lm_head + (size_t)sp.cols0 * ldw * esize(g.dtype);
+    gemm(c, EPI_SOFTSTAT, rows, d, w1, ldw, M, g.vocab - sp.cols0, d, n_dev, e2, 0, false, 0, sp.tile1);
+  }
 }
 
 void attention(alodlm_ctx* c, const AttnParams& p) {
@@ -554,8 +579,7 @@ void readout_heads(alodlm_ctx* c, const void* rows, int n_upper, const int32_t* 
     ep.smp = *smp;
     ep.smp.part = c->at<GStat>(p.gpart);
   }
-  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model + g.weight_row_pad, n_upper, g.vocab, g.d_model, n_dev, ep,
-       0, false, 0, c->lm_tile);
+  lm_head_gemm(c, rows, n_upper, n_dev, ep);
   launch_softstat_combine(c->at<SoftStat>(p.part), n_upper, ep.n_tiles, n_dev, c->at<float>(p.H),
                           c->at<float>(p.lse), c->at<int32_t>(p.tok), smp ? ep.smp.part : nullptr,
                           smp ? c->at<int32_t>(p.stok) : nullptr, c->st);
@@ -1135,8 +1159,7 @@ int readout_run(alodlm_ctx* c, const ReadoutScratch& sc, const void* rows, int32
   ep.n_tiles = lm_tiles(c, n_rows);
   ep.btok = boost_tok;
   ep.bval = boost_val;
-  gemm(c, EPI_SOFTSTAT, rows, g.d_model, c->w.lm_head, g.d_model + g.weight_row_pad, n_rows, g.vocab, g.d_model, nullptr,
-       ep, 0, false, 0, c->lm_tile);
+  lm_head_gemm(c, rows, n_rows, nullptr, ep);
   launch_softstat_combine(sc.part, n_rows, ep.n_tiles, nullptr, entropy, lse, argmax, nullptr, nullptr, st);
   c->dbg_point("readout of rows", n_rows);
   // one loop of the commit rule (a starts at 0, so a = lambda); per-row records go to the outputs

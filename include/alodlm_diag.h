@@ -40,8 +40,11 @@ __attribute__((visibility("default"))) int alodlm_diag_gemm(int32_t epi, int32_t
 /* The matrix-core dispatcher's choice for a GEMM of M x N x K with epilogue epi (ALODLM_DIAG_*),
  * given scratch_floats of split-K scratch (the step has max_batch * max_block * max(2F, qkv) * 8):
  * tile index, split-K factor and the kernel instantiation's name as rocprofv3 reports it
- * (NUL-terminated, truncated to name_len).  Host only.  Returns 0, or -1 for a shape the matrix
- * cores do not take. */
+ * (NUL-terminated, truncated to name_len).  For the readout epilogue (epi 2) the LM head of the
+ * library's readouts: when its columns run as two launches (a 256-row readout over a vocabulary
+ * whose 256-column tiles leave a last round of the compute units at most half full), both
+ * instantiations with their column ranges, and *tile is the first.  Host only.  Returns 0, or -1
+ * for a shape the matrix cores do not take. */
 __attribute__((visibility("default"))) int alodlm_diag_gemm_choice(int32_t epi, int32_t M, int32_t N, int32_t K,
                                                                    size_t scratch_floats, int32_t* tile,
                                                                    int32_t* splits, char* name, size_t name_len);

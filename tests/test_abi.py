@@ -247,3 +247,18 @@ def test_weight_row_pad_range(pad, ok):
         with pytest.raises(B.AlodlmError) as e:
             B.workspace_bytes(_cfg(weight_row_pad=pad))
         assert e.value.code == B.EINVAL
+
+
+def test_readout_column_ranges():
+    """The LM-head readout's column split (host-side plan): a 256-row readout over the 8B vocabulary
+    runs the 512 whole rounds of 256-column wide tiles and the remaining 20864 columns on the
+    eight-wave tile; fewer rows, several row tiles or a vocabulary filling its last round stay in
+    one launch."""
+    V, d = 151936, 4096
+    t, _, name = B.gemm_choice(2, 256, V, d, 0)
+    assert t == 59 and "(columns 0..131071)" in name and "(columns 131072..151935)" in name, name
+    assert name.count("k_gemm_") == 2
+    for M, N in ((224, V), (129, V)):
+        assert "(columns 0..131071)" in B.gemm_choice(2, M, N, d, 0)[2]
+    for M, N in ((128, V), (300, V), (2048, V), (256, 256 * 512), (256, 256 * 512 + 256 * 200), (256, 4096)):
+        assert "columns" not in B.gemm_choice(2, M, N, d, 0)[2], (M, N)
