@@ -31,7 +31,7 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # flop per byte where the two bounds meet
 # HBM bytes per launch of the gate/up GEMM measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
 # (copy-calibrated), valid only for this kernel at this mean row count per launch
-GATE_UP_COUNTERS = dict(kernel="k_gemm_pipe<128, 192, 4, 2, 4, 3, false>", rows_per_launch=242.6, bytes=223.4e6,
+GATE_UP_COUNTERS = dict(kernel="k_gemm_pipe<128, 192, 4, 2, 4, 3, false>", rows_per_launch=242.6, bytes=223.3e6,
                         profile="profiles/gemm_gate_up_swiglu_qwen3_8b_hbm_traffic.md")
 CLASSES = ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention", "lm_head", "norm_rope")
 
