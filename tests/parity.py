@@ -3,8 +3,9 @@
 Tolerances.  The contract is the one stated for this step: hidden states and logits match
 row-wise within a relative 2e-2 in bf16 and 1e-4 in fp32 mode, entropies within 1e-2 nats, and
 committed tokens and the commit schedule match exactly except at decisions the oracle flags as
-near a boundary (|H - tau_ent| < 1e-2, top-2 logit gap < 1e-2; this build adds the halting mean
-|mean a - tau_halt| < 1e-2 and the forced commit's entropy gap < 1e-2 as flags of the same kind).
+near a boundary (|H - tau_ent| < 1e-2, top-2 logit gap < 1e-2; the halting mean
+|mean a - tau_halt| < 1e-2 and the forced commit's entropy gap < 1e-2 are flags of the same kind
+here).
 
 * fp32 mode, at every depth: those literal tolerances.
 * bf16 mode (the calibrated tier): the literal tolerance, or CAL_FACTOR times the drift of the
