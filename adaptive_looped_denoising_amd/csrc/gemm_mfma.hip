@@ -467,7 +467,10 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const bf16_t* __rest
 // weight stream bound the GEMM.  Eight waves hold 64 x (BN / 2) accumulator tiles each, so every
 // 16-byte fragment read from LDS feeds (TM * TN) / (TM + TN) MFMAs, about twice the reuse of the
 // 128-row tiles.  Stages are 32 deep in K (64-byte rows, four 16-byte chunks, chunk c of row r at
-// slot c ^ ((r >> 2) & 3): the 16 rows one fragment read touches cover all banks once), so
+// slot c ^ ((r >> 1) & 3): the LDS serves a 16-byte read eight lanes at a time over 128 bytes of
+// banks, i.e. two 64-byte rows, and the eight consecutive rows those lanes read (same chunk) then
+// land in eight distinct 16-byte bank groups -- swizzling by r >> 2 instead left rows r and r + 2
+// on the same banks: half of the LDS-active cycles were bank conflicts in rocprofv3), so
 // NS stages of a 256 x 256 tile fit in LDS with NS - 2 stages of load latency cover.  Each
 // stage's fragments are read into one of two register sets while the matrix cores work on the
 // other stage's; the reads are retired with explicit LDS-counter waits one stage later (the
@@ -507,12 +510,12 @@ __device__ __forceinline__ void gemm_wide_body(const bf16_t* __restrict__ A, int
   const int wm = wid / WN, wn = wid % WN;
 
   // load instruction j of this wave fills stage rows (wid * LPW + j) * 16 .. + 15; this lane's
-  // 16 bytes land at row rho, slot lane & 3, and hold global chunk (lane & 3) ^ ((rho >> 2) & 3)
+  // 16 bytes land at row rho, slot lane & 3, and hold global chunk (lane & 3) ^ ((rho >> 1) & 3)
   const bf16_t* src[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
     const int rho = (wid * LPW + j) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((rho >> 2) & 3);
+    const int c = (lane & 3) ^ ((rho >> 1) & 3);
     if (rho < BM) {
       const int gm = m0 + rho;
       src[j] = A + (size_t)(gm < Mr ? gm : 0) * lda + c * 8;
@@ -547,12 +550,12 @@ __device__ __forceinline__ void gemm_wide_body(const bf16_t* __restrict__ A, int
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
       const int r = wm * TM * 16 + a * 16 + col;
-      fa[a] = *(const bf16x8_t*)&st[r * WK + ((quad ^ ((r >> 2) & 3)) << 3)];
+      fa[a] = *(const bf16x8_t*)&st[r * WK + ((quad ^ ((r >> 1) & 3)) << 3)];
     }
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
       const int r = BM + wn * TN * 16 + b * 16 + col;
-      fb[b] = *(const bf16x8_t*)&st[r * WK + ((quad ^ ((r >> 2) & 3)) << 3)];
+      fb[b] = *(const bf16x8_t*)&st[r * WK + ((quad ^ ((r >> 1) & 3)) << 3)];
     }
   };
   auto mma = [&](bf16x8_t (&fa)[TM], bf16x8_t (&fb)[TN]) {
