@@ -1284,7 +1284,7 @@ void gemm_mfma_softstat_plan(int M, int N, int force_tile, SoftstatPlan* sp) {
   // rounds of one 512-thread wide-tile workgroup per compute unit (the library targets gfx950,
   // whose MI355X has 256 compute units); the rest runs on the 128 x 192 eight-wave tile
   constexpr int kCUs = 256, kRest = 47;
-  if (force_tile < 0 && kTiles[tile].bm >= M && kTiles[tile].bm == 256 && bn == 256) {
+  if (kTiles[tile].bm >= M && kTiles[tile].bm == 256 && bn == 256) {
     const int whole = sp->tiles0 / kCUs * kCUs;
     if (whole > 0 && sp->tiles0 - whole > 0 && sp->tiles0 - whole <= kCUs / 2) {
       sp->cols0 = whole * bn;
