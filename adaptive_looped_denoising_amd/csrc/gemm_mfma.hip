@@ -1224,10 +1224,21 @@ bool swiglu_single_pass_ok(int tile) { return ((kTiles[tile].bn / kTiles[tile].w
 // 32-row pipelined tile; more rows use the eight-wave tiles (two waves per SIMD hide each other's
 // LDS and barrier waits), with split-K up to 384 rows.
 // Returns the tile; *splits gets the split-K factor (0 = the generic rule).
+// FFN gate/up at up to 64 rows (weights streamed once, from HBM): the eight-wave 64 x 128 tile when
+// its N / 128 workgroups cover three quarters of the compute units, else the four-wave 64 x 64 tile
+// with twice the workgroups (weights rotated so none is cache-resident: 8B width 24576 x 4096 at
+// 32 / 48 rows 40.1 / 55.0 -> 39.7 / 40.2 us, 1.7B width 12288 x 2048 at 32 / 64 rows 16.9 / 18.6 ->
+// 13.8 / 14.7 us).
+static int swiglu_few_rows_tile(int N) { return N >= 192 * 128 ? 45 : 12; }
+
 int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   *splits = 0;
   if (M <= 48) {
-    if (epi == EPI_SWIGLU || epi == EPI_SOFTSTAT) {
+    if (epi == EPI_SWIGLU) {
+      *splits = 1;
+      return swiglu_few_rows_tile(N);
+    }
+    if (epi == EPI_SOFTSTAT) {
       *splits = 1;
       return 10;
     }
@@ -1247,7 +1258,7 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
     // weight tile read once: 256 rows 473 -> 424 us); 257..384 rows would take two wide row
     // tiles, three 128-row ones cost less (288 / 320 / 384 rows: 628 / 781 / 645 -> 553 / 614 / 559 us)
     if (epi == EPI_SOFTSTAT) return M <= 128 ? 47 : (M <= 256 ? 59 : 44);
-    if (epi == EPI_SWIGLU) return M <= 64 ? 45 : (M <= 128 ? 18 : 56);
+    if (epi == EPI_SWIGLU) return M <= 64 ? swiglu_few_rows_tile(N) : (M <= 128 ? 18 : 56);
     // projections (QKV, O, FFN down): split-K 4 over the eight-wave tiles
     *splits = 4;
     if (M <= 128) return (M <= 64 || N <= 4096) ? 45 : 18;

@@ -249,6 +249,17 @@ def test_weight_row_pad_range(pad, ok):
         assert e.value.code == B.EINVAL
 
 
+def test_swiglu_few_rows_tiles():
+    """FFN gate/up at up to 64 rows: the eight-wave 64 x 128 tile when its N / 128 workgroups cover
+    three quarters of the compute units (the 8B width), else the four-wave 64 x 64 tile (the 1.7B
+    width); single pass (the SwiGLU epilogue needs no split-K reduction)."""
+    for M in (1, 32, 48, 64):
+        t, sp, name = B.gemm_choice(3, M, 2 * 6144, 2048, 8 * M * 2 * 6144)
+        assert (t, sp) == (12, 1) and name.startswith("k_gemm_pipe<64, 64,"), (M, name)
+        t, sp, name = B.gemm_choice(3, M, 2 * 12288, 4096, 8 * M * 2 * 12288)
+        assert (t, sp) == (45, 1) and name.startswith("k_gemm_pipe<64, 128,"), (M, name)
+
+
 def test_readout_column_ranges():
     """The LM-head readout's column split (host-side plan): a 256-row readout over the 8B vocabulary
     runs the 512 whole rounds of 256-column wide tiles and the remaining 20864 columns on the
