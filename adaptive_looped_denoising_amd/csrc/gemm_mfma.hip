@@ -9,7 +9,9 @@
 //   k_gemm_ring2  separate activation / weight ring depths;
 //   k_gemm_ws     wave-specialised loads (half the waves fetch activations, half weights);
 //   k_gemm_wide   eight 64-row waves over 256-row tiles, 32-deep stages, each stage's fragments
-//                 read while the matrix cores work on the previous one (many rows).
+//                 read while the matrix cores work on the previous one; for many rows the
+//                 dispatcher now takes the pipelined 256 x 256 tile with two 64-deep stages,
+//                 which runs the same MFMAs in the same order and measured faster.
 // Tiles are numbered so that the blocks the dispatcher sends to one XCD (block ids congruent
 // mod 8) are consecutive tiles with the row tile varying fastest: the few row tiles that share
 // a weight column tile run on the same XCD at about the same time and find it in its L2.
@@ -464,7 +466,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const bf16_t* __rest
 }
 
 // Wide tiles for many rows (prefill, long-context steps), where the matrix cores rather than the
-// weight stream bound the GEMM.  Eight waves hold 64 x (BN / 2) accumulator tiles each, so every
+// weight stream bound the GEMM (kept in the tile table; the dispatcher prefers the pipelined
+// 256 x 256 tile, whose 64-deep stages bring each row's whole 128-byte line at once).  Eight waves hold 64 x (BN / 2) accumulator tiles each, so every
 // 16-byte fragment read from LDS feeds (TM * TN) / (TM + TN) MFMAs, about twice the reuse of the
 // 128-row tiles.  Stages are 32 deep in K (64-byte rows, four 16-byte chunks, chunk c of row r at
 // slot c ^ ((r >> 1) & 3): the LDS serves a 16-byte read eight lanes at a time over 128 bytes of
@@ -1188,7 +1191,6 @@ static void run_tile(int epi, bool split, dim3 grid, const bf16_t* A, int lda, c
 bool gemm_mfma_supported(int K, int lda, int ldb) { return K % GK == 0 && lda % 8 == 0 && ldb % 8 == 0 && K > 0; }
 
 
-// Tile shapes (BM, BN, waves along M x N).
 // Tile shapes: BM, BN and the number of waves along N.  The SwiGLU epilogue pairs gate and up
 // 16-column groups inside one wave, so a single-pass SwiGLU needs an even count of column
 // groups per wave (BN / WN / 16); tiles without it take SwiGLU only with split-K.
@@ -1214,9 +1216,12 @@ static const TileCfg kTiles[] = {
     {128, 192, 2}, {128, 192, 2}, {128, 192, 2}, {128, 128, 4}, {128, 128, 4}, {64, 128, 4}, {256, 128, 2},
     // eight waves, deeper LDS ring
     {128, 192, 2}, {128, 128, 4}, {128, 192, 4},
-    // wide tiles (many rows): eight 64-row waves, 32-deep stages, fragments prefetched
-    {256, 256, 2}, {256, 256, 2}, {256, 128, 2}, {128, 256, 4}, {256, 256, 2}};
-constexpr int kNumTiles = 64;
+    // wide tiles (many rows): eight 64-row waves, 32-deep stages, fragments prefetched (the
+    // dispatcher now takes tile 64 for these shapes)
+    {256, 256, 2}, {256, 256, 2}, {256, 128, 2}, {128, 256, 4}, {256, 256, 2},
+    // 256 x 256 over eight 64 x 128 waves, two 64-deep stages (the whole 128-byte line of each row)
+    {256, 256, 2}};
+constexpr int kNumTiles = 65;
 
 bool swiglu_single_pass_ok(int tile) { return ((kTiles[tile].bn / kTiles[tile].wn / 16) & 1) == 0; }
 
@@ -1254,10 +1259,10 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   if (M <= 64 && epi == EPI_SOFTSTAT) return 9;
   if (M <= 384) {
     *splits = 1;
-    // LM head: 128-row tiles up to 128 rows, then the 256 x 256 wide tile (one row tile, each
-    // weight tile read once: 256 rows 473 -> 424 us); 257..384 rows would take two wide row
-    // tiles, three 128-row ones cost less (288 / 320 / 384 rows: 628 / 781 / 645 -> 553 / 614 / 559 us)
-    if (epi == EPI_SOFTSTAT) return M <= 128 ? 47 : (M <= 256 ? 59 : 44);
+    // LM head: 128-row tiles up to 128 rows, then a 256 x 256 tile (one row tile, each weight
+    // tile read once: 256 rows 473 -> 424 us); 257..384 rows would take two 256-row tiles, three
+    // 128-row ones cost less (288 / 320 / 384 rows: 628 / 781 / 645 -> 553 / 614 / 559 us)
+    if (epi == EPI_SOFTSTAT) return M <= 128 ? 47 : (M <= 256 ? 64 : 44);
     if (epi == EPI_SWIGLU) return M <= 64 ? swiglu_few_rows_tile(N) : (M <= 128 ? 18 : 56);
     // projections (QKV, O, FFN down): split-K 4 over the eight-wave tiles
     *splits = 4;
@@ -1267,21 +1272,24 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   // more rows (long-context steps, prefill): single pass over the eight-wave tiles, measured at
   // 512 / 1024 / 2048 / 8192 rows on the 8B projections
   *splits = 1;
-  if (epi == EPI_SOFTSTAT) return 59;  // 2048 rows: 3.24 -> 2.50 ms
-  // wide eight-wave tiles where the matrix cores bound the GEMM: every projection at >= 4096
-  // rows (8192-row prefill: gate/up 1.84 -> 1.50 ms, down 0.94 -> 0.83), gate/up from 1536
-  if (M >= 4096) return 60;
-  if (M >= 1536) return epi == EPI_SWIGLU ? 60 : (epi == EPI_STORE ? 47 : 37);
+  if (epi == EPI_SOFTSTAT) return 64;  // 2048 rows: 3.24 -> 2.50 ms on the wide tile, 2.45 on tile 64
+  // 256 x 256 tiles where the matrix cores bound the GEMM: every projection at >= 4096 rows
+  // (8192-row prefill: gate/up 1.84 -> 1.50 ms on the wide tile), gate/up from 1536.  The
+  // pipelined 256 x 256 tile (64-deep stages, two of them) does the same MFMAs in the same order
+  // as the wide tile (32-deep stages, fragments read a stage ahead) and is faster at every shape
+  // measured: 8192 rows gate/up 1461 -> 1369 us, QKV 397 -> 365, down 808 -> 743.
+  if (M >= 4096) return 64;
+  if (M >= 1536) return epi == EPI_SWIGLU ? 64 : (epi == EPI_STORE ? 47 : 37);
   if (epi == EPI_SWIGLU) return M >= 768 ? 44 : 47;
   if (epi == EPI_STORE) return M >= 768 ? 47 : 38;
   return 38;
 }
 
-// The LM-head readout's column ranges.  With one row tile of the wide 256 x 256 tile the
+// The LM-head readout's column ranges.  With one row tile of a 256 x 256 tile the
 // ceil(N / 256) column tiles run in rounds of one per compute unit; at N = 151936 that is 594
 // tiles, 2.3 rounds, the last one a third full.  When that last round would be at most half full
-// the columns of the whole rounds stay on the wide tile and the rest run as a second launch on
-// the 128 x 192 eight-wave tile, which spreads them over more workgroups (256 rows: 512 wide tiles
+// the columns of the whole rounds stay on the 256 x 256 tile and the rest run as a second launch
+// on the 128 x 192 eight-wave tile, which spreads them over more workgroups (256 rows: 512 wide tiles
 // 320 us + the 20864-column rest 67 us, against 437-473 us in one launch, in a probe).
 void gemm_mfma_softstat_plan(int M, int N, int force_tile, SoftstatPlan* sp) {
   int s;
@@ -1292,7 +1300,7 @@ void gemm_mfma_softstat_plan(int M, int N, int force_tile, SoftstatPlan* sp) {
   sp->tile1 = -1;
   sp->tiles0 = (N + bn - 1) / bn;
   sp->n_tiles = sp->tiles0;
-  // rounds of one 512-thread wide-tile workgroup per compute unit (the library targets gfx950,
+  // rounds of one 512-thread 256 x 256 workgroup per compute unit (the library targets gfx950,
   // whose MI355X has 256 compute units); the rest runs on the 128 x 192 eight-wave tile
   constexpr int kCUs = 256, kRest = 47;
   if (kTiles[tile].bm >= M && kTiles[tile].bm == 256 && bn == 256) {
@@ -1377,6 +1385,7 @@ static const TileName kTileNames[kNumTiles] = {
     {"k_gemm_wide", "256, 128, 6"},
     {"k_gemm_wide", "128, 256, 6"},
     {"k_gemm_wide", "256, 256, 3"},
+    {"k_gemm_pipe", "256, 256, 4, 2, 2"},
 };
 
 // The tile and split-K the dispatcher takes for a shape (see launch_gemm_mfma).
@@ -1519,6 +1528,7 @@ int launch_gemm_mfma(int epi, const void* A, int lda, const void* B, int ldb, in
     case 62: WD(128, 256, 6); break;
     case 63: WD(256, 256, 3); break;
 #undef WD
+    case 64: run_pipe<256, 256, 4, 2, 2>(epi, split, grid, a, lda, b, ldb, M, N, K, k_split, mt, nt, splits, m_dev, e, F, st); break;
 
   }
 #undef T

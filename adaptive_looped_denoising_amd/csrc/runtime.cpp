@@ -197,7 +197,7 @@ struct alodlm_ctx {
   int attn_force_kh = 0;       // diagnostics: ALODLM_ATTN_KH=1|2 fixes the key halves per tile
   int proj_splits[3] = {0, 0, 0};  // diagnostics: ALODLM_PROJ_SPLITS=q,o,d fixes the QKV / O / down split-K
   int proj_tiles[4] = {-1, -1, -1, -1};  // diagnostics: ALODLM_PROJ_TILES=q,o,d,gu fixes their GEMM tiles
-  int lm_tile = -1;            // diagnostics: ALODLM_LM_TILE=t fixes the LM-head readout's GEMM tile (a 256 x 256 wide tile keeps the column ranges)
+  int lm_tile = -1;            // diagnostics: ALODLM_LM_TILE=t fixes the LM-head readout's GEMM tile (a 256 x 256 tile keeps the column ranges)
   // diagnostics: per-class kernel timing with event pairs on the context stream
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;

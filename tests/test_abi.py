@@ -262,12 +262,13 @@ def test_swiglu_few_rows_tiles():
 
 def test_readout_column_ranges():
     """The LM-head readout's column split (host-side plan): a 256-row readout over the 8B vocabulary
-    runs the 512 whole rounds of 256-column wide tiles and the remaining 20864 columns on the
+    runs the 512 whole rounds of 256 x 256 tiles and the remaining 20864 columns on the
     eight-wave tile; fewer rows, several row tiles or a vocabulary filling its last round stay in
     one launch."""
     V, d = 151936, 4096
     t, _, name = B.gemm_choice(2, 256, V, d, 0)
-    assert t == 59 and "(columns 0..131071)" in name and "(columns 131072..151935)" in name, name
+    assert t == 64 and "(columns 0..131071)" in name and "(columns 131072..151935)" in name, name
+    assert name.startswith("k_gemm_pipe<256, 256, 4, 2, 2, 2, false> (columns 0..131071)"), name
     assert name.count("k_gemm_") == 2
     for M, N in ((224, V), (129, V)):
         assert "(columns 0..131071)" in B.gemm_choice(2, M, N, d, 0)[2]

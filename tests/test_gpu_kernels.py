@@ -11,6 +11,7 @@ from tests.parity import log
 
 pytestmark = pytest.mark.gpu
 
+N_TILES = 65  # matrix-core tiles in the library's table (alodlm_diag_gemm force_tile 0 .. N_TILES - 1)
 SHAPES = [(32, 4096, 2048), (256, 6144, 4096), (200, 1024, 512), (1, 128, 64), (77, 640, 384), (2048, 1024, 4096),
           (130, 4096, 12288), (32, 2048, 6144)]
 
@@ -52,7 +53,7 @@ def test_gemm_store_and_resid(gpu_lib, M, N, K):
     assert err < 2e-5, err
 
 
-@pytest.mark.parametrize("tile", range(64))
+@pytest.mark.parametrize("tile", range(N_TILES))
 def test_gemm_every_tile(gpu_lib, tile):
     M, N, K = 300, 1024, 1024
     A, Bm = _bf16((M, K), 10), _bf16((N, K), 11, 0.02)
@@ -71,7 +72,7 @@ def test_gemm_every_tile(gpu_lib, tile):
     assert err.max() < 1.6e-2
 
 
-@pytest.mark.parametrize("tile", range(64))
+@pytest.mark.parametrize("tile", range(N_TILES))
 def test_softstat_every_tile(gpu_lib, tile):
     """LM-head readout statistics (entropy, log-sum-exp, argmax over the columns) of every tile,
     on a ragged shape, against float64 arithmetic on the same bf16 operands."""
@@ -123,7 +124,7 @@ def test_softstat_auto_tile_across_row_thresholds(gpu_lib, M):
     assert ((tok.cpu().numpy() == z.argmax(axis=1)) | (top2[:, 1] - top2[:, 0] < 1e-4)).all()
 
 
-@pytest.mark.parametrize("tile", list(range(64)) + ["generic"])
+@pytest.mark.parametrize("tile", list(range(N_TILES)) + ["generic"])
 def test_readout_sample_every_tile(gpu_lib, tile):
     """Gumbel-max draws of the LM-head kernel (every tile and the vector-ALU path), on a ragged
     shape, against argmax(z + g) with z in float64 on the same bf16 operands and g the oracle's own
