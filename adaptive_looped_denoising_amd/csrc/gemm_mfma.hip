@@ -1279,7 +1279,9 @@ int gemm_mfma_auto_tile(int epi, int M, int N, int K, int* splits) {
   // as the wide tile (32-deep stages, fragments read a stage ahead) and is faster at every shape
   // measured: 8192 rows gate/up 1461 -> 1369 us, QKV 397 -> 365, down 808 -> 743.
   if (M >= 4096) return 64;
-  if (M >= 1536) return epi == EPI_SWIGLU ? 64 : (epi == EPI_STORE ? 47 : 37);
+  // QKV (STORE) from 1792 rows too: the long-context step's QKV (1984..2048 rows) 19.3 -> 18.5 ms
+  // per step, the same tokens bit for bit
+  if (M >= 1536) return epi == EPI_SWIGLU ? 64 : (epi == EPI_STORE ? (M >= 1792 ? 64 : 47) : 37);
   if (epi == EPI_SWIGLU) return M >= 768 ? 44 : 47;
   if (epi == EPI_STORE) return M >= 768 ? 47 : 38;
   return 38;
