@@ -8,7 +8,9 @@ near a boundary (|H - tau_ent| < 1e-2, top-2 logit gap < 1e-2; the halting mean
 here).
 
 * fp32 mode, at every depth: those literal tolerances.
-* bf16 mode (the calibrated tier): the literal tolerance, or CAL_FACTOR times the drift of the
+* bf16 mode, readouts after at most LITERAL_BF16_DEPTH layer calls with bf16 keys and values:
+  the literal tolerances.
+* bf16 mode otherwise (the calibrated tier): the literal tolerance, or CAL_FACTOR times the drift of the
   oracle's own bf16 rounding-point mode from the exact oracle on the same input and the same
   decisions, whichever is larger; the near-decision flags widen the same way, from the drift of
   the quantity that decides (entropy, top-2 gap, halting mean).  Shallow runs stay at the
@@ -84,14 +86,23 @@ def _lse_rel(a, b):
     return np.abs(a - b) / np.maximum(np.abs(b), 1.0)
 
 
+# bf16 readouts after at most this many layer calls (with bf16 keys and values) are held to the
+# literal tolerances; deeper ones take the calibrated tier
+LITERAL_BF16_DEPTH = 10
+
+
 def calibrated(w: synth.Workload, depth: int) -> bool:
-    """Whether a readout after ``depth`` layer calls takes the calibrated tier: every bf16 run.  The
-    literal bf16 figures are its floor; above them only where the oracle's own bf16 drift says a
-    bf16 pipeline's rounding noise reaches that far (it does for single rows from about a dozen
-    layer calls on: the 1e-2-nat entropy figure is exceeded at 14 layer calls of a 512-wide model
-    with head size 64, and fp8 keys and values, whose E4M3 rounding keeps 3 fraction bits, exceed
-    it at any depth)."""
-    return w.dtype == "bf16"
+    """Whether a readout after ``depth`` layer calls takes the calibrated tier: bf16 runs deeper
+    than LITERAL_BF16_DEPTH layer calls, and every bf16 run whose keys and values are stored in
+    fp8.  The literal bf16 figures are the calibrated tier's floor; it goes above them only where
+    the oracle's own bf16 drift says a bf16 pipeline's rounding noise reaches that far (it does for
+    single rows from about a dozen layer calls on: the 1e-2-nat entropy figure is exceeded at 14
+    layer calls of a 512-wide model with head size 64, and fp8 keys and values, whose E4M3 rounding
+    keeps 3 fraction bits, exceed it at any depth).  Shallower bf16 readouts, at bf16 keys and
+    values, are held to the literal figures."""
+    if w.dtype != "bf16":
+        return False
+    return depth > LITERAL_BF16_DEPTH or getattr(w, "kv_dtype", "same") == "fp8"
 
 
 def tolerances(w: synth.Workload, exact: List[dict], rounded: Optional[List[dict]] = None) -> Callable:
