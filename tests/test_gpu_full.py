@@ -229,3 +229,15 @@ def test_qwen3_8b_long_context_step(gpu_lib):
     w = synth.workload("qwen3_8b_long")
     e, _, _, _ = _check(w, [5], name="qwen3_8b_long")
     e.close()
+
+
+def test_qwen3_8b_long_context_fp32_step(gpu_lib):
+    """fp32 mode at the long-context shape (8192 cached positions, a quarter of them cached at
+    depths 1..3 only, K_max 6, tau_halt 0.9) with entropy commits: the literal fp32 tolerances at
+    full depth (up to 166 layer calls), decisions position by position.  One sequence: the fp32
+    path's attention is the plain vector kernel."""
+    w = synth.workload("qwen3_8b_long", dtype="fp32", batch=1, boost_lo=10.0, boost_hi=20.0, tau_ent=0.9)
+    e, ores, _, dec = _check(w, [0], name="qwen3_8b_long fp32 entropy commits (batch 1)")
+    assert sum(int((r["commit_loop"] > 0).sum()) for r in ores) > 0
+    assert all(d["diverged"] is None for d in dec.values())
+    e.close()
