@@ -226,8 +226,18 @@ def test_qwen3_8b_step_is_deterministic(gpu_lib):
 
 # --------------------------------------------------------------------------- long context
 def test_qwen3_8b_long_context_step(gpu_lib):
+    """The long-context workload as benchmarked (batch 32, 8192 cached positions, K_max 6), one
+    sequence against the oracle; then the whole step twice, bit for bit (its GEMMs run single-pass
+    on the 256 x 256 tile and its attention without key splits: a different set of kernels from the
+    8B step's)."""
     w = synth.workload("qwen3_8b_long")
     e, _, _, _ = _check(w, [5], name="qwen3_8b_long")
+    a = e.step(records=True, hidden=True)
+    b = e.step(records=True, hidden=True)
+    for k in ("tokens", "commit_loop", "loops", "entropy", "lam", "halt", "lse", "argmax", "hidden"):
+        x, y = getattr(a, k), getattr(b, k)
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), k
+    log("long-context step twice: identical bits (%d commits, loops %s)" % (a.n_committed, a.loops.tolist()))
     e.close()
 
 
