@@ -203,6 +203,20 @@ def test_qwen3_8b_sampled_commits(gpu_lib):
     e.close()
 
 
+def test_qwen3_8b_fp32_sampled_commits(gpu_lib):
+    """Sampled commits in fp32 mode at the 8B dimensions (151936 Gumbel-max candidates per row,
+    10/16/10 layers): draws, commit schedule and tokens against the oracle's own generator at the
+    literal fp32 tolerances, no decision differing."""
+    w = synth.workload("qwen3_8b", kv="synthetic", dtype="fp32", boost_lo=10.0, boost_hi=20.0, tau_ent=0.9,
+                       batch=2)
+    e, ores, free, dec = _check(w, [0], sample=dict(seed=0x5EED0FF5, step=3),
+                                name="qwen3_8b fp32 sampled (batch 2)")
+    assert sum(int((r["commit_loop"] > 0).sum()) for r in ores) > 0
+    assert free.sampled is not None and (free.sampled[0] >= 0).sum() > 0
+    assert all(d["diverged"] is None for d in dec.values())
+    e.close()
+
+
 def test_qwen3_8b_fp8_kv_step(gpu_lib):
     """fp8 (E4M3) keys and values at the 8B shape over the synthetic cache."""
     w = synth.workload("qwen3_8b", kv="synthetic", kv_dtype="fp8")
