@@ -10,6 +10,7 @@ configuration the benchmark times, against the fp64 oracle:
 * determinism: the matrix-core step run twice gives the same bits.
 """
 import gc
+import os
 from dataclasses import replace
 
 import numpy as np
@@ -157,6 +158,18 @@ def test_qwen3_1p7b_pages_split_without_prelude_and_coda(gpu_lib):
 # --------------------------------------------------------------------------- 8B shape
 def test_qwen3_8b_prefill_first_positions(gpu_lib):
     _check_prefill_prefix(synth.workload("qwen3_8b"), 8, [0, 5])
+
+
+@pytest.mark.skipif(os.environ.get("ALODLM_LONG_TESTS") != "1",
+                    reason="about 150 s of oracle prefill on the host; run with ALODLM_LONG_TESTS=1")
+def test_qwen3_8b_step_on_prefill_cache(gpu_lib):
+    """The 8B-shape workload as benchmarked: the step over the depth-aware cache alodlm_prefill_kv
+    built from the 8 x 1024 prefix tokens, one sequence compared end to end (the oracle runs that
+    sequence's whole prefill, 84 layer calls over 1024 positions, exactly and at the bf16 rounding
+    points).  Opt-in: the oracle's two fp64 prefills of 1024 positions take about 150 s."""
+    w = synth.workload("qwen3_8b")
+    e, _, _, _ = _check(w, [0], prefill_cache=True, name="qwen3_8b prefill cache")
+    e.close()
 
 
 def test_qwen3_8b_step_sampled_sequences(gpu_lib):
